@@ -1,0 +1,252 @@
+/*
+ * ssd_oracle.c -- plain fp64 CPU oracle for the Mamba-2 selective state-space
+ * recurrence and for each staged call of the chunked (SSD) forward.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this library.  It shares no code with the HIP library
+ * and is never on the product path.
+ *
+ * What is computed (per batch row b and head h, group g = h / (H / G)):
+ *
+ *   S <- h0[b,h] (or 0)                                 P x N state
+ *   for t = 0 .. L-1:
+ *       a      = exp(dt[b,t,h] * A[h])                  discretised decay
+ *       S[p,n] = a * S[p,n] + dt[b,t,h] * x[b,t,h,p] * B[b,t,g,n]
+ *       y[b,t,h,p] = sum_n C[b,t,g,n] * S[p,n] + D[h] * x[b,t,h,p]
+ *   final[b,h] = S
+ *
+ * Sources: the discretisation abar = exp(delta * A) is written out in
+ * "3.3 Hardware-Aware algorithms and GPU memory hierarchy optimisation",
+ * section 2.1; the first-order recurrence h_t = abar_t h_{t-1} + bbar_t x_t and
+ * its output through C in the same chapter, sections 3 and 4.1.  Mamba-2 uses
+ * one scalar A per head and the input matrix bbar = dt * B (not the
+ * zero-order-hold form of section 2.1); the output is read after the update.
+ * The staged calls (in-chunk cumulative sum kept in log2 units, chunk states,
+ * chunk-order state passing, chunk output from the chunk-start state) follow
+ * the three-kernel description on the devotd.net page on the NVIDIA / Jane
+ * Street cuTile Mamba-2 forward kernels, section 2.  Each staged call here is
+ * written as the plain definition of its result (a token recurrence over the
+ * chunk), not as the chunked algebra.
+ *
+ * Layouts (row-major, contiguous): x, y (b,L,H,P); dt (b,L,H); A, D (H);
+ * B, C (b,L,G,N); h0, final, step state (b,H,P,N); per-chunk states
+ * (b,nC,H,P,N); dt_t and the log2 cumulative sum (b,H,nC,Q).
+ *
+ * Built with -O2 -ffp-contract=off and no fast-math; threads split the
+ * independent (b, h) slices.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define LOG2E_D 1.4426950408889634073599246810019
+
+int ssd_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+/* One token of the recurrence for one (b, h): S <- a*S + dt*x (outer) B, then
+ * y = C.S + D*x.  Pointers are already offset to this token and head. */
+static void token_update(int64_t P, int64_t N, double* S, double dt, double A,
+                         const double* x, const double* B, const double* C,
+                         double Dh, int has_D, double* y) {
+    double a = exp(dt * A);
+    for (int64_t p = 0; p < P; ++p) {
+        double u = dt * x[p];
+        double* row = S + p * N;
+        for (int64_t n = 0; n < N; ++n) row[n] = a * row[n] + u * B[n];
+    }
+    if (y == NULL) return;
+    for (int64_t p = 0; p < P; ++p) {
+        const double* row = S + p * N;
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) acc += C[n] * row[n];
+        y[p] = acc + (has_D ? Dh * x[p] : 0.0);
+    }
+}
+
+static int bad_dims(int64_t b, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G) {
+    return b < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || (H % G) != 0;
+}
+
+/*
+ * Full forward by the token recurrence.  Optional outputs (NULL to skip):
+ *   chunk_start  (b,nC,H,P,N): the state before token c*chunk, i.e. after
+ *                the first c*chunk tokens (h0 for c = 0);
+ *   chunk_local  (b,nC,H,P,N): the state the tokens of chunk c alone produce
+ *                from a zero start.
+ * Returns 0, or -1 on inconsistent arguments.
+ */
+int ssd_oracle_forward(int64_t b, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                       const double* x, const double* dt, const double* A,
+                       const double* B, const double* C, const double* D,
+                       const double* h0, double* y, double* final_state,
+                       int64_t chunk, double* chunk_start, double* chunk_local,
+                       int nthreads) {
+    if (bad_dims(b, L, H, P, N, G)) return -1;
+    if ((chunk_start || chunk_local) && chunk <= 0) return -1;
+    int64_t nC = chunk > 0 ? (L + chunk - 1) / chunk : 0;
+    int64_t hpg = H / G;
+    set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < b * H; ++bh) {
+        int64_t bb = bh / H, h = bh % H, g = h / hpg;
+        double* S = (double*)calloc((size_t)(P * N), sizeof(double));
+        if (!S) { err = 1; continue; }
+        if (h0) memcpy(S, h0 + bh * P * N, sizeof(double) * P * N);
+        for (int64_t t = 0; t < L; ++t) {
+            if (chunk_start && t % chunk == 0)
+                memcpy(chunk_start + ((bb * nC + t / chunk) * H + h) * P * N, S, sizeof(double) * P * N);
+            int64_t bt = bb * L + t;
+            token_update(P, N, S, dt[bt * H + h], A[h], x + (bt * H + h) * P,
+                         B + (bt * G + g) * N, C + (bt * G + g) * N,
+                         D ? D[h] : 0.0, D != NULL, y ? y + (bt * H + h) * P : NULL);
+        }
+        if (final_state) memcpy(final_state + bh * P * N, S, sizeof(double) * P * N);
+        if (chunk_local) {
+            for (int64_t c = 0; c < nC; ++c) {
+                memset(S, 0, sizeof(double) * P * N);
+                int64_t t1 = (c + 1) * chunk < L ? (c + 1) * chunk : L;
+                for (int64_t t = c * chunk; t < t1; ++t) {
+                    int64_t bt = bb * L + t;
+                    token_update(P, N, S, dt[bt * H + h], A[h], x + (bt * H + h) * P,
+                                 B + (bt * G + g) * N, C + (bt * G + g) * N, 0.0, 0, NULL);
+                }
+                memcpy(chunk_local + ((bb * nC + c) * H + h) * P * N, S, sizeof(double) * P * N);
+            }
+        }
+        free(S);
+    }
+    return err ? -2 : 0;
+}
+
+/*
+ * One decode step for every (b, h): the O(1) fixed-size state update of the
+ * "Compiler-First State Space Duality and Portable O(1) Autoregressive Caching
+ * for Inference" summary (Methodology, on-device O(1) caching).  state is
+ * (b,H,P,N), updated in place; x (b,H,P); dt (b,H); B, C (b,G,N); y (b,H,P).
+ */
+int ssd_oracle_step(int64_t b, int64_t H, int64_t P, int64_t N, int64_t G,
+                    double* state, const double* x, const double* dt, const double* A,
+                    const double* B, const double* C, const double* D, double* y,
+                    int nthreads) {
+    if (bad_dims(b, 1, H, P, N, G)) return -1;
+    int64_t hpg = H / G;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < b * H; ++bh) {
+        int64_t bb = bh / H, h = bh % H, g = h / hpg;
+        token_update(P, N, state + bh * P * N, dt[bh], A[h], x + bh * P,
+                     B + (bb * G + g) * N, C + (bb * G + g) * N,
+                     D ? D[h] : 0.0, D != NULL, y + bh * P);
+    }
+    return 0;
+}
+
+/*
+ * In-chunk cumulative sum (devotd.net cuTile page, section 2, first kernel):
+ * for chunk c and in-chunk position i, cs_log2 = log2(e) * sum_{k<=i} dt*A over
+ * the chunk's tokens; positions past L count as dt = 0.  dt_t receives dt
+ * itself (0 past L).  Both outputs are (b,H,nC,Q).
+ */
+int ssd_oracle_chunk_cumsum(int64_t b, int64_t L, int64_t H, int64_t Q,
+                            const double* dt, const double* A,
+                            double* dt_t, double* cs_log2) {
+    if (b < 0 || L < 0 || H <= 0 || Q <= 0) return -1;
+    int64_t nC = (L + Q - 1) / Q;
+    for (int64_t bb = 0; bb < b; ++bb)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t c = 0; c < nC; ++c) {
+                double run = 0.0;
+                for (int64_t i = 0; i < Q; ++i) {
+                    int64_t t = c * Q + i;
+                    double d = t < L ? dt[(bb * L + t) * H + h] : 0.0;
+                    run += d * A[h];
+                    int64_t o = ((bb * H + h) * nC + c) * Q + i;
+                    cs_log2[o] = run * LOG2E_D;
+                    if (dt_t) dt_t[o] = d;
+                }
+            }
+    return 0;
+}
+
+/*
+ * Chunk-order state passing (devotd.net cuTile page, section 2, second
+ * kernel; associativity of the recurrence, "3.3 Hardware-Aware ..." section
+ * 4.1): S_0 = h0 (or 0), chunk_start[c] = S_c, S_{c+1} = 2^{cs_log2[c,Q-1]} S_c
+ * + local[c], final = S_nC.  local and chunk_start are (b,nC,H,P,N) and may be
+ * the same buffer.
+ */
+int ssd_oracle_state_passing(int64_t b, int64_t nC, int64_t H, int64_t P, int64_t N, int64_t Q,
+                             const double* local, const double* cs_log2, const double* h0,
+                             double* chunk_start, double* final_state) {
+    if (b < 0 || nC < 0 || H <= 0 || P <= 0 || N <= 0 || Q <= 0) return -1;
+    int64_t PN = P * N;
+    double* S = (double*)malloc(sizeof(double) * (size_t)PN);
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)PN);
+    if (!S || !tmp) { free(S); free(tmp); return -2; }
+    for (int64_t bb = 0; bb < b; ++bb)
+        for (int64_t h = 0; h < H; ++h) {
+            for (int64_t e = 0; e < PN; ++e) S[e] = h0 ? h0[(bb * H + h) * PN + e] : 0.0;
+            for (int64_t c = 0; c < nC; ++c) {
+                int64_t o = ((bb * nC + c) * H + h) * PN;
+                double decay = exp2(cs_log2[((bb * H + h) * nC + c) * Q + (Q - 1)]);
+                memcpy(tmp, local + o, sizeof(double) * PN);
+                if (chunk_start) memcpy(chunk_start + o, S, sizeof(double) * PN);
+                for (int64_t e = 0; e < PN; ++e) S[e] = decay * S[e] + tmp[e];
+            }
+            if (final_state) memcpy(final_state + (bb * H + h) * PN, S, sizeof(double) * PN);
+        }
+    free(S);
+    free(tmp);
+    return 0;
+}
+
+/*
+ * Chunk output from the chunk-start state (devotd.net cuTile page, section 2,
+ * third kernel): for every chunk c, run the token recurrence over the chunk's
+ * tokens starting from chunk_start[c] and emit y.  chunk_start is
+ * (b,nC,H,P,N) with nC = ceil(L/Q).
+ */
+int ssd_oracle_chunk_scan(int64_t b, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q,
+                          const double* x, const double* dt, const double* A,
+                          const double* B, const double* C, const double* D,
+                          const double* chunk_start, double* y, int nthreads) {
+    if (bad_dims(b, L, H, P, N, G) || Q <= 0) return -1;
+    int64_t nC = (L + Q - 1) / Q, hpg = H / G;
+    set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t w = 0; w < b * nC * H; ++w) {
+        int64_t bb = w / (nC * H), c = (w / H) % nC, h = w % H, g = h / hpg;
+        double* S = (double*)malloc(sizeof(double) * (size_t)(P * N));
+        if (!S) { err = 1; continue; }
+        memcpy(S, chunk_start + w * P * N, sizeof(double) * P * N);
+        int64_t t1 = (c + 1) * Q < L ? (c + 1) * Q : L;
+        for (int64_t t = c * Q; t < t1; ++t) {
+            int64_t bt = bb * L + t;
+            token_update(P, N, S, dt[bt * H + h], A[h], x + (bt * H + h) * P,
+                         B + (bt * G + g) * N, C + (bt * G + g) * N,
+                         D ? D[h] : 0.0, D != NULL, y + (bt * H + h) * P);
+        }
+        free(S);
+    }
+    return err ? -2 : 0;
+}
