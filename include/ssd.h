@@ -1,0 +1,185 @@
+/*
+ * ssd.h -- C ABI of libssd, a gfx950 (MI355X) implementation of the Mamba-2
+ * state-space-duality (SSD) chunked forward scan and its O(1) decode step.
+ *
+ * What is computed.  For batch row b and head h (group g = h / (H/G)):
+ *     S_t = exp(dt_t * A_h) * S_{t-1} + dt_t * x_t (outer) B_t        (P x N)
+ *     y_t = C_t . S_t + D_h * x_t
+ * with S_{-1} = h0 (or 0).  The decay exp(delta*A) is the discretisation of
+ * "3.3 Hardware-Aware algorithms and GPU memory hierarchy optimisation",
+ * section 2.1; the recurrence and its output through C are its sections 3 and
+ * 4.1.  Mamba-2 uses one scalar A per head and the input term dt * B.
+ * The chunked method cuts the sequence into chunks of Q tokens and splits the
+ * work into an in-chunk cumulative sum of dt*A, chunk states, a chunk-order
+ * state pass and a fused in-chunk output -- the three kernels described on the
+ * devotd.net page on the NVIDIA / Jane Street cuTile Mamba-2 forward kernels,
+ * section 2 (the state kernel is split here into two calls).  The decode step
+ * is the fixed-size, on-device state update of "Compiler-First State Space
+ * Duality and Portable O(1) Autoregressive Caching for Inference",
+ * Methodology.
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers, contiguous, row-major, in the
+ *     layouts listed below.  `stream` is a hipStream_t passed as void* (NULL =
+ *     the null stream).  Calls only enqueue work; they never synchronise.
+ *   - The caller owns every buffer.  The library never allocates or frees
+ *     device memory and keeps no state between calls (a per-thread error
+ *     string aside), so it is re-entrant across threads and streams.
+ *   - Arguments are validated before anything is enqueued; a non-OK status
+ *     means nothing was launched, and ssd_last_error() describes why.
+ *     SSD_ERR_HIP is returned when a launch itself fails.  Faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ *   - io dtype (ssd_dims.io) is the element type of x, dt, B, C and y:
+ *     SSD_F32 (float) or SSD_BF16 (bfloat16).  A, D, h0, the final state, the
+ *     decode state and every intermediate are float32.
+ *
+ * Layouts (b = batch, L = seqlen, H = nheads, P = headdim, N = dstate,
+ * G = ngroups, Q = chunk, nC = ceil(L / Q)):
+ *     x, y              (b, L, H, P)        io dtype
+ *     dt                (b, L, H)           io dtype   (final positive step)
+ *     A, D              (H)                 float32    (A < 0 expected)
+ *     B, C              (b, L, G, N)        io dtype
+ *     h0, final_state   (b, H, P, N)        float32
+ *     dt_t, dA_cs_log2  (b, H, nC, Q)       float32
+ *     states            (b, nC, H, P, N)    float32
+ *     step: x, y (b, H, P); dt (b, H); B, C (b, G, N); state (b, H, P, N)
+ * Tokens at positions >= L inside the last chunk are treated as dt = 0,
+ * which leaves the state unchanged; their rows are never written.
+ *
+ * Supported sizes: P and N multiples of 16 with P <= 256 and N <= 1024;
+ * Q a multiple of 16 in [16, 512]; H divisible by G; b, L >= 0 (an empty
+ * batch or sequence is a valid no-op).  Other sizes return
+ * SSD_ERR_UNSUPPORTED.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,        /* a required pointer is NULL */
+    SSD_ERR_SHAPE = 2,       /* a dimension is negative/zero where it must not be, or H % G != 0 */
+    SSD_ERR_DTYPE = 3,       /* io is not SSD_F32 or SSD_BF16 */
+    SSD_ERR_UNSUPPORTED = 4, /* sizes outside the supported set (see above) */
+    SSD_ERR_WORKSPACE = 5,   /* workspace missing or smaller than ssd_forward_workspace_bytes() */
+    SSD_ERR_ALIAS = 6,       /* an output overlaps an input it may not overlap */
+    SSD_ERR_HIP = 7          /* a HIP launch failed; see ssd_last_error() */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef struct {
+    int64_t batch;    /* b */
+    int64_t seqlen;   /* L */
+    int64_t nheads;   /* H */
+    int64_t headdim;  /* P */
+    int64_t dstate;   /* N */
+    int64_t ngroups;  /* G: head h reads B, C of group h / (H / G) */
+    int64_t chunk;    /* Q; 0 = let ssd_forward choose (the staged calls need Q > 0) */
+    int32_t io;       /* ssd_dtype of x, dt, B, C, y */
+    int32_t reserved; /* must be 0 */
+} ssd_dims;
+
+/*
+ * In-chunk cumulative sum (cuTile page, section 2, first kernel and its
+ * listing): for chunk c and position i < Q,
+ *     dA_cs_log2[b,h,c,i] = log2(e) * sum_{k<=i} dt[b,cQ+k,h] * A[h]
+ *     dt_t[b,h,c,i]       = dt[b,cQ+i,h] as float32
+ * (log2 units, so later stages decay with exp2).  Positions past L read 0.
+ * dt_t and dA_cs_log2 must not overlap dt or A, nor each other.
+ */
+ssd_status ssd_chunk_cumsum(const ssd_dims* dims, const void* dt, const float* A,
+                            float* dt_t, float* dA_cs_log2, void* stream);
+
+/*
+ * Chunk-local states (cuTile page, section 2, first half of the state kernel):
+ * the state each chunk produces from a zero start,
+ *     states[b,c,h,p,n] = sum_{j<Q} 2^(l[Q-1] - l[j]) * dt_t[j] * x[b,cQ+j,h,p] * B[b,cQ+j,g,n]
+ * with l = dA_cs_log2[b,h,c,:].  states must not overlap any input.
+ */
+ssd_status ssd_chunk_state(const ssd_dims* dims, const void* x, const void* B,
+                           const float* dt_t, const float* dA_cs_log2,
+                           float* states, void* stream);
+
+/*
+ * Chunk-order state passing (cuTile page, section 2, second half of the state
+ * kernel: chunk order kept, independent state elements in parallel).  On
+ * entry states holds the chunk-local states; on return it holds the state
+ * BEFORE each chunk:
+ *     S_0 = h0 (or 0),  states[c] <- S_c,  S_{c+1} = 2^(l_c[Q-1]) S_c + local_c,
+ *     final_state = S_nC.
+ * h0 may be NULL.  final_state must not overlap states, h0 or dA_cs_log2.
+ */
+ssd_status ssd_state_passing(const ssd_dims* dims, float* states, const float* dA_cs_log2,
+                             const float* h0, float* final_state, void* stream);
+
+/*
+ * Chunk output from the chunk-start states (cuTile page, section 2, third
+ * kernel), for i < Q in chunk c:
+ *     y_i = 2^(l_i) C_i . S_c + sum_{j<=i} (C_i . B_j) 2^(l_i - l_j) dt_t[j] x_j + D_h x_i
+ * The in-chunk matrix stays in registers and LDS.  D may be NULL (no skip
+ * term).  y must not overlap any input.
+ */
+ssd_status ssd_chunk_scan(const ssd_dims* dims, const void* x, const void* B, const void* C,
+                          const float* dt_t, const float* dA_cs_log2,
+                          const float* chunk_start_states, const float* D,
+                          void* y, void* stream);
+
+/* Bytes of device workspace ssd_forward needs for these dims (0 on invalid dims). */
+size_t ssd_forward_workspace_bytes(const ssd_dims* dims);
+
+/*
+ * One-shot forward: y and the final state from (x, dt, A, B, C, D, h0), the
+ * four stages above composed (or fused) on `stream`.  dims->chunk = 0 lets
+ * the library pick the chunk size; the result does not depend on it beyond
+ * rounding.  D and h0 may be NULL.  workspace must hold at least
+ * ssd_forward_workspace_bytes(dims) bytes (256-byte aligned) and may not
+ * overlap anything else; its contents on entry are ignored.  y and
+ * final_state must not overlap the inputs.
+ */
+ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, const float* A,
+                       const void* B, const void* C, const float* D, const float* h0,
+                       void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * O(1) decode step for one token per (b, h), in place on state (dims->seqlen
+ * must be 1; dims->chunk is ignored):
+ *     S <- exp(dt A) S + dt x (outer) B;   y = C . S + D x   (after the update)
+ * y must not overlap the inputs or the state.  D may be NULL.
+ */
+ssd_status ssd_step(const ssd_dims* dims, float* state, const void* x, const void* dt,
+                    const float* A, const void* B, const void* C, const float* D,
+                    void* y, void* stream);
+
+/* Static text for a status code. */
+const char* ssd_status_string(ssd_status status);
+
+/* Detail for the last non-OK status returned on the calling thread ("" if none). */
+const char* ssd_last_error(void);
+
+/* SSD_ABI_VERSION of the loaded library. */
+int ssd_abi_version(void);
+
+/*
+ * The tiling ssd_forward would use for these dims: the chunk size, the
+ * P-tile and the number of heads per workgroup of its output kernel, and the
+ * number of chunks per segment of its carried-state pass (1 = staged).  Any
+ * pointer may be NULL.
+ */
+ssd_status ssd_query_config(const ssd_dims* dims, int* chunk, int* tile_p, int* heads_per_wg,
+                            int* chunks_per_segment);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

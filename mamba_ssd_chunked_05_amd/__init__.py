@@ -1,0 +1,303 @@
+"""Python binding of libssd, the gfx950 Mamba-2 SSD chunked forward and decode step.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libssd.so``; PyTorch supplies device memory and the current
+stream.  There is no CPU or PyTorch fallback -- if the library is not built,
+``load()`` raises.
+
+Calls (names follow the C ABI in ``include/ssd.h``):
+
+    forward(x, dt, A, B, C, D=None, h0=None, chunk=0)       -> (y, final_state)
+    step(state, x, dt, A, B, C, D=None)                    -> y   (state updated in place)
+    chunk_cumsum(dt, A, chunk)                             -> (dt_t, dA_cs_log2)
+    chunk_state(x, B, dt_t, dA_cs_log2, chunk)             -> states (chunk-local)
+    state_passing(states, dA_cs_log2, h0=None, chunk=...)  -> (states -> chunk-start, final_state)
+    chunk_scan(x, B, C, dt_t, dA_cs_log2, chunk_start, D=None, chunk=...) -> y
+
+Layouts: x, y (b, L, H, P); dt (b, L, H); A, D (H); B, C (b, L, G, N);
+h0, final and the decode state (b, H, P, N) float32; per-chunk (b, H, nC, Q)
+and (b, nC, H, P, N) float32.  x, dt, B, C share one dtype: bfloat16 or float32.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "SsdError", "load", "library_path", "forward", "forward_workspace_bytes", "step", "chunk_cumsum",
+    "chunk_state", "state_passing", "chunk_scan", "query_config", "abi_version", "Dims",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libssd.so")
+_lib = None
+
+SSD_OK, SSD_ERR_NULL, SSD_ERR_SHAPE, SSD_ERR_DTYPE, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_ALIAS, \
+    SSD_ERR_HIP = range(8)
+SSD_F32, SSD_BF16 = 0, 1
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        super().__init__(f"{func}: status {status} ({detail})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+        ("chunk", ctypes.c_int64), ("io", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libssd.so (built in-tree by ``build.py``); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libssd.so is not built ({_LIB_PATH}); run mamba_ssd_chunked_05_amd/build.py")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, dp = ctypes.c_void_p, ctypes.POINTER(Dims)
+    sig = {
+        "ssd_chunk_cumsum": [dp, vp, vp, vp, vp, vp],
+        "ssd_chunk_state": [dp, vp, vp, vp, vp, vp, vp],
+        "ssd_state_passing": [dp, vp, vp, vp, vp, vp],
+        "ssd_chunk_scan": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "ssd_forward": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "ssd_step": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "ssd_query_config": [dp] + [ctypes.POINTER(ctypes.c_int)] * 4,
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.ssd_forward_workspace_bytes.argtypes = [dp]
+    lib.ssd_forward_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssd_status_string.argtypes = [ctypes.c_int]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_last_error.argtypes = []
+    lib.ssd_last_error.restype = ctypes.c_char_p
+    lib.ssd_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(load().ssd_abi_version())
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+_IO = {torch.bfloat16: SSD_BF16, torch.float32: SSD_F32}
+
+
+def _io_code(t: torch.Tensor) -> int:
+    if t.dtype not in _IO:
+        raise TypeError(f"x/dt/B/C must be bfloat16 or float32, got {t.dtype}")
+    return _IO[t.dtype]
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.numel() and t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None or t.numel() == 0 else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(status: int, func: str):
+    if status != SSD_OK:
+        lib = load()
+        detail = lib.ssd_last_error().decode() or lib.ssd_status_string(status).decode()
+        if status == SSD_ERR_HIP:
+            raise SsdError(status, func, detail)
+        raise ValueError(f"{func}: {lib.ssd_status_string(status).decode()}: {detail}")
+
+
+def _dims(b, L, H, P, N, G, chunk, io) -> Dims:
+    return Dims(int(b), int(L), int(H), int(P), int(N), int(G), int(chunk), int(io), 0)
+
+
+def _fwd_dims(x, B, chunk):
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be (b, L, H, P) and B, C (b, L, G, N)")
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return _dims(b, L, H, P, N, G, chunk, _io_code(x))
+
+
+def _check_fwd_inputs(x, dt, A, B, C, D, h0):
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _dev(x, "x")
+    _dev(dt, "dt", x.dtype, (b, L, H))
+    _dev(A, "A", torch.float32, (H,))
+    _dev(B, "B", x.dtype, (b, L, G, N))
+    _dev(C, "C", x.dtype, (b, L, G, N))
+    _dev(D, "D", torch.float32, (H,))
+    _dev(h0, "h0", torch.float32, (b, H, P, N))
+
+
+# ---------------------------------------------------------------------------
+# the calls
+# ---------------------------------------------------------------------------
+
+
+def query_config(b, L, H, P, N, G=1, chunk=0, dtype=torch.bfloat16) -> dict:
+    lib = load()
+    d = _dims(b, L, H, P, N, G, chunk, _IO[dtype])
+    out = [ctypes.c_int(0) for _ in range(4)]
+    _check(lib.ssd_query_config(ctypes.byref(d), *[ctypes.byref(o) for o in out]), "ssd_query_config")
+    return dict(chunk=out[0].value, tile_p=out[1].value, heads_per_wg=out[2].value,
+                chunks_per_segment=out[3].value)
+
+
+def forward_workspace_bytes(x: torch.Tensor, B: torch.Tensor, chunk: int = 0) -> int:
+    lib = load()
+    d = _fwd_dims(x, B, chunk)
+    return int(lib.ssd_forward_workspace_bytes(ctypes.byref(d)))
+
+
+def forward(x, dt, A, B, C, D=None, h0=None, *, chunk: int = 0, y=None, final_state=None,
+            workspace=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One-shot SSD forward on the current stream; returns (y, final_state)."""
+    lib = load()
+    d = _fwd_dims(x, B, chunk)
+    _check_fwd_inputs(x, dt, A, B, C, D, h0)
+    b, L, H, P = x.shape
+    N = B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, x.shape)
+    if final_state is None:
+        final_state = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
+    _dev(final_state, "final_state", torch.float32, (b, H, P, N))
+    nbytes = int(lib.ssd_forward_workspace_bytes(ctypes.byref(d)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", torch.uint8)
+    st = lib.ssd_forward(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+                         _ptr(y), _ptr(final_state), _ptr(workspace), workspace.numel(), _stream(x))
+    _check(st, "ssd_forward")
+    return y, final_state
+
+
+def step(state, x, dt, A, B, C, D=None, *, y=None) -> torch.Tensor:
+    """One decode token per (b, h); ``state`` (b, H, P, N) float32 is updated in place."""
+    lib = load()
+    b, H, P, N = state.shape
+    G = B.shape[1]
+    _dev(state, "state", torch.float32)
+    _dev(x, "x", None, (b, H, P))
+    _dev(dt, "dt", x.dtype, (b, H))
+    _dev(A, "A", torch.float32, (H,))
+    _dev(B, "B", x.dtype, (b, G, N))
+    _dev(C, "C", x.dtype, (b, G, N))
+    _dev(D, "D", torch.float32, (H,))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, (b, H, P))
+    d = _dims(b, 1, H, P, N, G, 0, _io_code(x))
+    st = lib.ssd_step(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                      _ptr(y), _stream(x))
+    _check(st, "ssd_step")
+    return y
+
+
+def chunk_cumsum(dt, A, chunk: int):
+    lib = load()
+    b, L, H = dt.shape
+    _dev(dt, "dt")
+    _dev(A, "A", torch.float32, (H,))
+    nC = -(-L // chunk)
+    dt_t = torch.empty((b, H, nC, chunk), dtype=torch.float32, device=dt.device)
+    cs = torch.empty_like(dt_t)
+    d = _dims(b, L, H, 16, 16, 1, chunk, _io_code(dt))
+    _check(lib.ssd_chunk_cumsum(ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(dt_t), _ptr(cs), _stream(dt)),
+           "ssd_chunk_cumsum")
+    return dt_t, cs
+
+
+def chunk_state(x, B, dt_t, cs, chunk: int):
+    lib = load()
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    nC = -(-L // chunk)
+    _dev(x, "x")
+    _dev(B, "B", x.dtype, (b, L, G, N))
+    _dev(dt_t, "dt_t", torch.float32, (b, H, nC, chunk))
+    _dev(cs, "dA_cs_log2", torch.float32, (b, H, nC, chunk))
+    states = torch.empty((b, nC, H, P, N), dtype=torch.float32, device=x.device)
+    d = _dims(b, L, H, P, N, G, chunk, _io_code(x))
+    _check(lib.ssd_chunk_state(ctypes.byref(d), _ptr(x), _ptr(B), _ptr(dt_t), _ptr(cs), _ptr(states),
+                               _stream(x)), "ssd_chunk_state")
+    return states
+
+
+def state_passing(states, cs, h0=None, *, seqlen: int, chunk: int, io=torch.bfloat16, final_state=None):
+    """In place: chunk-local states -> chunk-start states.  Returns (states, final_state)."""
+    lib = load()
+    b, nC, H, P, N = states.shape
+    _dev(states, "states", torch.float32)
+    _dev(cs, "dA_cs_log2", torch.float32, (b, H, nC, chunk))
+    _dev(h0, "h0", torch.float32, (b, H, P, N))
+    if -(-seqlen // chunk) != nC:
+        raise ValueError("states has the wrong number of chunks for seqlen/chunk")
+    if final_state is None:
+        final_state = torch.empty((b, H, P, N), dtype=torch.float32, device=states.device)
+    _dev(final_state, "final_state", torch.float32, (b, H, P, N))
+    d = _dims(b, seqlen, H, P, N, 1, chunk, _IO[io])
+    _check(lib.ssd_state_passing(ctypes.byref(d), _ptr(states), _ptr(cs), _ptr(h0), _ptr(final_state),
+                                 _stream(states)), "ssd_state_passing")
+    return states, final_state
+
+
+def chunk_scan(x, B, C, dt_t, cs, chunk_start, D=None, *, chunk: int, y=None):
+    lib = load()
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    nC = -(-L // chunk)
+    _dev(x, "x")
+    _dev(B, "B", x.dtype, (b, L, G, N))
+    _dev(C, "C", x.dtype, (b, L, G, N))
+    _dev(dt_t, "dt_t", torch.float32, (b, H, nC, chunk))
+    _dev(cs, "dA_cs_log2", torch.float32, (b, H, nC, chunk))
+    _dev(chunk_start, "chunk_start_states", torch.float32, (b, nC, H, P, N))
+    _dev(D, "D", torch.float32, (H,))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, x.shape)
+    d = _dims(b, L, H, P, N, G, chunk, _io_code(x))
+    _check(lib.ssd_chunk_scan(ctypes.byref(d), _ptr(x), _ptr(B), _ptr(C), _ptr(dt_t), _ptr(cs),
+                              _ptr(chunk_start), _ptr(D), _ptr(y), _stream(x)), "ssd_chunk_scan")
+    return y

@@ -1,0 +1,365 @@
+// api.cpp -- the C ABI of libssd: argument validation, workspace layout,
+// tuning choice and launches.  Validation never touches the HIP runtime, so a
+// rejected call enqueues nothing (and works on a machine without a GPU).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/ssd.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ssd_status fail(ssd_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+ssd_status ok() {
+    g_last_error.clear();
+    return SSD_OK;
+}
+
+ssd_status hip_fail(hipError_t e, const char* where) {
+    return fail(SSD_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxGrid = 0x7fffffffLL;
+
+// ---------------------------------------------------------------------------
+// dims validation
+// ---------------------------------------------------------------------------
+enum class Need { kStaged, kForward, kStep };
+
+ssd_status check_dims(const ssd_dims* d, Need need, ssd::Shape* out) {
+    if (!d) return fail(SSD_ERR_NULL, "dims is NULL");
+    if (d->io != SSD_F32 && d->io != SSD_BF16) return fail(SSD_ERR_DTYPE, "io dtype %d is not SSD_F32/SSD_BF16", d->io);
+    if (d->reserved != 0) return fail(SSD_ERR_SHAPE, "dims.reserved must be 0");
+    if (d->batch < 0 || d->seqlen < 0) return fail(SSD_ERR_SHAPE, "batch and seqlen must be >= 0");
+    if (d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
+        return fail(SSD_ERR_SHAPE, "nheads, headdim, dstate and ngroups must be > 0");
+    if (d->nheads % d->ngroups != 0)
+        return fail(SSD_ERR_SHAPE, "nheads (%lld) is not a multiple of ngroups (%lld)", (long long)d->nheads,
+                    (long long)d->ngroups);
+    if (d->chunk < 0) return fail(SSD_ERR_SHAPE, "chunk must be >= 0");
+    if (d->headdim % 16 || d->headdim > 256)
+        return fail(SSD_ERR_UNSUPPORTED, "headdim %lld: need a multiple of 16 up to 256", (long long)d->headdim);
+    if (d->dstate % 16 || d->dstate > 1024)
+        return fail(SSD_ERR_UNSUPPORTED, "dstate %lld: need a multiple of 16 up to 1024", (long long)d->dstate);
+    ssd::Shape s{};
+    s.b = d->batch;
+    s.L = d->seqlen;
+    s.H = d->nheads;
+    s.P = d->headdim;
+    s.N = d->dstate;
+    s.G = d->ngroups;
+    s.io = d->io;
+    if (need == Need::kStep) {
+        if (d->seqlen != 1) return fail(SSD_ERR_SHAPE, "ssd_step needs seqlen == 1 (got %lld)", (long long)d->seqlen);
+        if (s.b * s.H > kMaxGrid) return fail(SSD_ERR_UNSUPPORTED, "batch * nheads too large");
+        s.Q = 1;
+        s.nC = 1;
+        *out = s;
+        return SSD_OK;
+    }
+    int64_t Q = d->chunk;
+    if (Q == 0) {
+        if (need == Need::kStaged) return fail(SSD_ERR_UNSUPPORTED, "the staged calls need an explicit chunk > 0");
+        Q = 256;  // tuned default of the staged forward
+    }
+    if (Q % 16 || Q < 16 || Q > 512)
+        return fail(SSD_ERR_UNSUPPORTED, "chunk %lld: need a multiple of 16 in [16, 512]", (long long)Q);
+    s.Q = Q;
+    s.nC = (s.L + Q - 1) / Q;
+    if (s.b * s.nC * s.H * s.N > kMaxGrid || s.H > 65535 || s.b > 65535)
+        return fail(SSD_ERR_UNSUPPORTED, "problem too large for one launch grid");
+    if (ssd::chunk_scan_lds_bytes(s) > 160 * 1024 || ssd::chunk_state_lds_bytes(s) > 160 * 1024)
+        return fail(SSD_ERR_UNSUPPORTED, "tile shapes exceed the 160 KiB LDS");
+    *out = s;
+    return SSD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// pointers and aliasing
+// ---------------------------------------------------------------------------
+struct Span {
+    const void* p;
+    size_t bytes;
+    const char* name;
+};
+
+bool overlap(const Span& a, const Span& b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    auto a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+ssd_status need_ptr(const Span& s) {
+    if (s.bytes > 0 && !s.p) return fail(SSD_ERR_NULL, "%s is NULL", s.name);
+    return SSD_OK;
+}
+
+ssd_status no_alias(const Span& out, const Span* ins, int n) {
+    for (int i = 0; i < n; ++i)
+        if (overlap(out, ins[i])) return fail(SSD_ERR_ALIAS, "%s overlaps %s", out.name, ins[i].name);
+    return SSD_OK;
+}
+
+#define SSD_TRY(expr)                       \
+    do {                                    \
+        ssd_status _st = (expr);            \
+        if (_st != SSD_OK) return _st;      \
+    } while (0)
+
+size_t esz(const ssd::Shape& s) { return s.io == SSD_BF16 ? 2 : 4; }
+
+struct Sizes {
+    size_t x, dt, bc, A, hstate, cs, states;
+};
+
+Sizes sizes(const ssd::Shape& s) {
+    Sizes z;
+    z.x = (size_t)(s.b * s.L * s.H * s.P) * esz(s);
+    z.dt = (size_t)(s.b * s.L * s.H) * esz(s);
+    z.bc = (size_t)(s.b * s.L * s.G * s.N) * esz(s);
+    z.A = (size_t)s.H * 4;
+    z.hstate = (size_t)(s.b * s.H * s.P * s.N) * 4;
+    z.cs = (size_t)(s.b * s.H * s.nC * s.Q) * 4;
+    z.states = (size_t)(s.b * s.nC * s.H * s.P * s.N) * 4;
+    return z;
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+struct FwdLayout {
+    size_t dt_t, cs, states, total;
+};
+
+FwdLayout fwd_layout(const ssd::Shape& s) {
+    Sizes z = sizes(s);
+    FwdLayout f;
+    f.dt_t = 0;
+    f.cs = align256(z.cs);
+    f.states = f.cs + align256(z.cs);
+    f.total = f.states + align256(z.states);
+    return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_status_string(ssd_status st) {
+    switch (st) {
+        case SSD_OK: return "ok";
+        case SSD_ERR_NULL: return "null pointer";
+        case SSD_ERR_SHAPE: return "invalid shape";
+        case SSD_ERR_DTYPE: return "invalid dtype";
+        case SSD_ERR_UNSUPPORTED: return "unsupported size";
+        case SSD_ERR_WORKSPACE: return "workspace too small";
+        case SSD_ERR_ALIAS: return "forbidden aliasing";
+        case SSD_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* ssd_last_error(void) { return g_last_error.c_str(); }
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+ssd_status ssd_query_config(const ssd_dims* dims, int* chunk, int* tile_p, int* heads_per_wg,
+                            int* chunks_per_segment) {
+    try {
+        ssd::Shape s;
+        SSD_TRY(check_dims(dims, Need::kForward, &s));
+        if (chunk) *chunk = (int)s.Q;
+        if (tile_p) *tile_p = (int)s.P;
+        if (heads_per_wg) *heads_per_wg = 1;
+        if (chunks_per_segment) *chunks_per_segment = 1;
+        return ok();
+    } catch (...) {
+        return fail(SSD_ERR_HIP, "internal error");
+    }
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_dims* dims, const void* dt, const float* A, float* dt_t, float* dA_cs_log2,
+                            void* stream) {
+    try {
+        ssd::Shape s;
+        SSD_TRY(check_dims(dims, Need::kStaged, &s));
+        Sizes z = sizes(s);
+        Span sdt{dt, z.dt, "dt"}, sA{A, z.A, "A"}, sdtt{dt_t, z.cs, "dt_t"}, scs{dA_cs_log2, z.cs, "dA_cs_log2"};
+        for (const Span& p : {sdt, sA, sdtt, scs}) SSD_TRY(need_ptr(p));
+        Span ins[] = {sdt, sA};
+        SSD_TRY(no_alias(sdtt, ins, 2));
+        SSD_TRY(no_alias(scs, ins, 2));
+        Span o1[] = {sdtt};
+        SSD_TRY(no_alias(scs, o1, 1));
+        hipError_t e = ssd::launch_chunk_cumsum(s, dt, A, dt_t, dA_cs_log2, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "ssd_chunk_cumsum");
+        return ok();
+    } catch (...) {
+        return fail(SSD_ERR_HIP, "internal error");
+    }
+}
+
+ssd_status ssd_chunk_state(const ssd_dims* dims, const void* x, const void* B, const float* dt_t,
+                           const float* dA_cs_log2, float* states, void* stream) {
+    try {
+        ssd::Shape s;
+        SSD_TRY(check_dims(dims, Need::kStaged, &s));
+        Sizes z = sizes(s);
+        Span sx{x, z.x, "x"}, sB{B, z.bc, "B"}, sdtt{dt_t, z.cs, "dt_t"}, scs{dA_cs_log2, z.cs, "dA_cs_log2"},
+            sst{states, z.states, "states"};
+        for (const Span& p : {sx, sB, sdtt, scs, sst}) SSD_TRY(need_ptr(p));
+        Span ins[] = {sx, sB, sdtt, scs};
+        SSD_TRY(no_alias(sst, ins, 4));
+        hipError_t e = ssd::launch_chunk_state(s, x, B, dt_t, dA_cs_log2, states, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "ssd_chunk_state");
+        return ok();
+    } catch (...) {
+        return fail(SSD_ERR_HIP, "internal error");
+    }
+}
+
+ssd_status ssd_state_passing(const ssd_dims* dims, float* states, const float* dA_cs_log2, const float* h0,
+                             float* final_state, void* stream) {
+    try {
+        ssd::Shape s;
+        SSD_TRY(check_dims(dims, Need::kStaged, &s));
+        Sizes z = sizes(s);
+        Span sst{states, z.states, "states"}, scs{dA_cs_log2, z.cs, "dA_cs_log2"}, sh0{h0, h0 ? z.hstate : 0, "h0"},
+            sfin{final_state, z.hstate, "final_state"};
+        for (const Span& p : {sst, scs, sfin}) SSD_TRY(need_ptr(p));
+        Span ins[] = {sst, scs, sh0};
+        SSD_TRY(no_alias(sfin, ins, 3));
+        Span ins2[] = {scs, sh0};
+        SSD_TRY(no_alias(sst, ins2, 2));
+        hipError_t e = ssd::launch_state_passing(s, states, dA_cs_log2, h0, final_state, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "ssd_state_passing");
+        return ok();
+    } catch (...) {
+        return fail(SSD_ERR_HIP, "internal error");
+    }
+}
+
+ssd_status ssd_chunk_scan(const ssd_dims* dims, const void* x, const void* B, const void* C, const float* dt_t,
+                          const float* dA_cs_log2, const float* chunk_start_states, const float* D, void* y,
+                          void* stream) {
+    try {
+        ssd::Shape s;
+        SSD_TRY(check_dims(dims, Need::kStaged, &s));
+        Sizes z = sizes(s);
+        Span sx{x, z.x, "x"}, sB{B, z.bc, "B"}, sC{C, z.bc, "C"}, sdtt{dt_t, z.cs, "dt_t"},
+            scs{dA_cs_log2, z.cs, "dA_cs_log2"}, sst{chunk_start_states, z.states, "chunk_start_states"},
+            sD{D, D ? z.A : 0, "D"}, sy{y, z.x, "y"};
+        for (const Span& p : {sx, sB, sC, sdtt, scs, sst, sy}) SSD_TRY(need_ptr(p));
+        Span ins[] = {sx, sB, sC, sdtt, scs, sst, sD};
+        SSD_TRY(no_alias(sy, ins, 7));
+        hipError_t e = ssd::launch_chunk_scan(s, x, B, C, dt_t, dA_cs_log2, chunk_start_states, D, y,
+                                              (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "ssd_chunk_scan");
+        return ok();
+    } catch (...) {
+        return fail(SSD_ERR_HIP, "internal error");
+    }
+}
+
+size_t ssd_forward_workspace_bytes(const ssd_dims* dims) {
+    try {
+        ssd::Shape s;
+        if (check_dims(dims, Need::kForward, &s) != SSD_OK) return 0;
+        return fwd_layout(s).total;
+    } catch (...) {
+        return 0;
+    }
+}
+
+ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, const float* A, const void* B,
+                       const void* C, const float* D, const float* h0, void* y, float* final_state,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        ssd::Shape s;
+        SSD_TRY(check_dims(dims, Need::kForward, &s));
+        Sizes z = sizes(s);
+        FwdLayout f = fwd_layout(s);
+        Span sx{x, z.x, "x"}, sdt{dt, z.dt, "dt"}, sA{A, z.A, "A"}, sB{B, z.bc, "B"}, sC{C, z.bc, "C"},
+            sD{D, D ? z.A : 0, "D"}, sh0{h0, h0 ? z.hstate : 0, "h0"}, sy{y, z.x, "y"},
+            sfin{final_state, z.hstate, "final_state"}, sws{workspace, f.total, "workspace"};
+        for (const Span& p : {sx, sdt, sA, sB, sC, sy, sfin}) SSD_TRY(need_ptr(p));
+        if (s.b > 0 && s.L > 0) {
+            if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", f.total);
+            if (workspace_bytes < f.total)
+                return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, f.total);
+            if (reinterpret_cast<uintptr_t>(workspace) % 256)
+                return fail(SSD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        }
+        Span ins[] = {sx, sdt, sA, sB, sC, sD, sh0};
+        SSD_TRY(no_alias(sy, ins, 7));
+        SSD_TRY(no_alias(sfin, ins, 7));
+        Span o1[] = {sy};
+        SSD_TRY(no_alias(sfin, o1, 1));
+        if (s.b > 0 && s.L > 0) {
+            Span all[] = {sx, sdt, sA, sB, sC, sD, sh0, sy, sfin};
+            SSD_TRY(no_alias(sws, all, 9));
+        }
+        hipStream_t st = (hipStream_t)stream;
+        if (s.b == 0) return ok();
+        char* ws = static_cast<char*>(workspace);
+        float* dt_t = reinterpret_cast<float*>(ws + f.dt_t);
+        float* cs = reinterpret_cast<float*>(ws + f.cs);
+        float* states = reinterpret_cast<float*>(ws + f.states);
+        hipError_t e;
+        if (s.nC > 0) {
+            e = ssd::launch_chunk_cumsum(s, dt, A, dt_t, cs, st);
+            if (e != hipSuccess) return hip_fail(e, "ssd_forward/cumsum");
+            e = ssd::launch_chunk_state(s, x, B, dt_t, cs, states, st);
+            if (e != hipSuccess) return hip_fail(e, "ssd_forward/chunk_state");
+        }
+        e = ssd::launch_state_passing(s, states, cs, h0, final_state, st);
+        if (e != hipSuccess) return hip_fail(e, "ssd_forward/state_passing");
+        if (s.nC > 0) {
+            e = ssd::launch_chunk_scan(s, x, B, C, dt_t, cs, states, D, y, st);
+            if (e != hipSuccess) return hip_fail(e, "ssd_forward/chunk_scan");
+        }
+        return ok();
+    } catch (...) {
+        return fail(SSD_ERR_HIP, "internal error");
+    }
+}
+
+ssd_status ssd_step(const ssd_dims* dims, float* state, const void* x, const void* dt, const float* A,
+                    const void* B, const void* C, const float* D, void* y, void* stream) {
+    try {
+        ssd::Shape s;
+        SSD_TRY(check_dims(dims, Need::kStep, &s));
+        const size_t e = esz(s);
+        Span sst{state, (size_t)(s.b * s.H * s.P * s.N) * 4, "state"}, sx{x, (size_t)(s.b * s.H * s.P) * e, "x"},
+            sdt{dt, (size_t)(s.b * s.H) * e, "dt"}, sA{A, (size_t)s.H * 4, "A"}, sB{B, (size_t)(s.b * s.G * s.N) * e, "B"},
+            sC{C, (size_t)(s.b * s.G * s.N) * e, "C"}, sD{D, D ? (size_t)s.H * 4 : 0, "D"},
+            sy{y, (size_t)(s.b * s.H * s.P) * e, "y"};
+        for (const Span& p : {sst, sx, sdt, sA, sB, sC, sy}) SSD_TRY(need_ptr(p));
+        Span ins[] = {sx, sdt, sA, sB, sC, sD};
+        SSD_TRY(no_alias(sst, ins, 6));
+        Span ins2[] = {sx, sdt, sA, sB, sC, sD, sst};
+        SSD_TRY(no_alias(sy, ins2, 7));
+        hipError_t he = ssd::launch_step(s, state, x, dt, A, B, C, D, y, (hipStream_t)stream);
+        if (he != hipSuccess) return hip_fail(he, "ssd_step");
+        return ok();
+    } catch (...) {
+        return fail(SSD_ERR_HIP, "internal error");
+    }
+}
+
+}  // extern "C"

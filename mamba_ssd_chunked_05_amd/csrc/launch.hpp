@@ -1,0 +1,30 @@
+// launch.hpp -- internal launchers behind the C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// Validated problem sizes; io = 0 (fp32) or 1 (bf16).
+struct Shape {
+    int64_t b, L, H, P, N, G, Q, nC;
+    int io;
+};
+
+hipError_t launch_chunk_cumsum(const Shape& s, const void* dt, const float* A, float* dt_t, float* cs,
+                               hipStream_t st);
+hipError_t launch_chunk_state(const Shape& s, const void* x, const void* B, const float* dt_t,
+                              const float* cs, float* states, hipStream_t st);
+hipError_t launch_state_passing(const Shape& s, float* states, const float* cs, const float* h0,
+                                float* final_state, hipStream_t st);
+hipError_t launch_chunk_scan(const Shape& s, const void* x, const void* B, const void* C, const float* dt_t,
+                             const float* cs, const float* start, const float* D, void* y, hipStream_t st);
+hipError_t launch_step(const Shape& s, float* state, const void* x, const void* dt, const float* A,
+                       const void* B, const void* C, const float* D, void* y, hipStream_t st);
+
+// LDS bytes the generic chunk kernels need; used by validation.
+size_t chunk_state_lds_bytes(const Shape& s);
+size_t chunk_scan_lds_bytes(const Shape& s);
+
+}  // namespace ssd
