@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSD chunked forward on one MI355X.
+
+One "step" is one ssd_forward over one batch of the 2.7B-shaped workload
+(b = 1, L = 64K tokens, H = 80 heads, P = 64, N = 128, one group, bf16 inputs,
+fp32 decay/accumulation), with every input already resident in HBM.  The timed
+region is exactly --steps forward calls bracketed by device synchronisation.
+
+The printed JSON line also carries
+  * roofline     -- the dominant kernel's algorithmic bytes (or flops) per launch
+                    over its average launch duration, timed with HIP events on the
+                    stream it runs on, against the MI355X peak;
+  * cpu_baseline -- the fp64 oracle timed on this host on a bounded sample;
+  * decode       -- 64 back-to-back ssd_step calls on the 2.7B decode shape.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
+METRIC = "SSD fwd tokens/s + % MFMA/HBM roofline (2.7B heads, L 1K–256K, N 64–512)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cfg2_64k", help="a forward workload name from synth.CONFIGS")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def fwd_flops_per_token(H, P, N, G, Q):
+    """Causal algorithmic FLOP per token at chunk Q: H((Q+1)P + 4NP) + G(Q+1)N."""
+    return H * ((Q + 1) * P + 4 * N * P) + G * (Q + 1) * N
+
+
+def fwd_bytes_per_token(H, P, N, G, s_io):
+    """Minimum HBM bytes per token: x and y, dt, and B and C once per group."""
+    return H * (P * 2 * s_io + s_io) + 2 * G * N * s_io
+
+
+def scan_bytes_per_token(H, P, N, G, Q, s_io):
+    """Algorithmic bytes of one chunk-scan launch per token: x, y, B, C, the two fp32 chunk vectors
+    and the fp32 chunk-start state (P*N*4 per chunk and head)."""
+    return H * (P * 2 * s_io + 8 + P * N * 4 / Q) + 2 * G * N * s_io
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the forward shards over batch, heads or sequence segments, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mamba_ssd_chunked_05_amd as ssd
+    from synth import CONFIGS, make_config_inputs, make_step_inputs, seed_for
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    ssd.load()
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS[args.workload]
+    b, L, H, P, N, G = cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"], cfg["ngroups"]
+    tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    s_io = 2 if cfg["dtype"] == "bf16" else 4
+
+    log(f"generating {args.workload}: b={b} L={L} H={H} P={P} N={N} G={G} {cfg['dtype']}")
+    t0 = time.time()
+    fi = make_config_inputs(args.workload)
+
+    def t(a, dtype=tdt):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dtype).to(dev)
+
+    x, dt, B, C = t(fi.x), t(fi.dt), t(fi.B), t(fi.C)
+    A, D = t(fi.A, torch.float32), t(fi.D, torch.float32)
+    log(f"inputs resident in HBM ({time.time() - t0:.1f}s)")
+
+    qcfg = ssd.query_config(b, L, H, P, N, G, 0, tdt)
+    Q = qcfg["chunk"]
+    y = torch.empty_like(x)
+    fin = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(ssd.forward_workspace_bytes(x, B, 0), 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        ssd.forward(x, dt, A, B, C, D, None, chunk=0, y=y, final_state=fin, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms = elapsed * 1e3 / args.steps
+    tokens = b * L
+    tok_s = tokens / (ms / 1e3)
+    flops = fwd_flops_per_token(H, P, N, G, cfg["chunk"]) * tokens
+    min_bytes = fwd_bytes_per_token(H, P, N, G, s_io) * tokens + b * H * P * N * 4
+    log(f"forward: {ms:.3f} ms/step, {tok_s / 1e6:.1f} M tok/s, {flops / (ms / 1e3) / 1e12:.1f} TFLOP/s algorithmic")
+
+    # ---- dominant kernel: the chunk scan, timed alone on the stream it runs on ------------
+    stream = torch.cuda.current_stream(dev)
+    dt_t, cs = ssd.chunk_cumsum(dt, A, Q)
+    states = ssd.chunk_state(x, B, dt_t, cs, Q)
+    ssd.state_passing(states, cs, None, seqlen=L, chunk=Q, io=tdt)
+    ys = torch.empty_like(x)
+    for _ in range(args.warmup):
+        ssd.chunk_scan(x, B, C, dt_t, cs, states, D, chunk=Q, y=ys)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        ssd.chunk_scan(x, B, C, dt_t, cs, states, D, chunk=Q, y=ys)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    scan_ms = ev0.elapsed_time(ev1) / args.steps
+    scan_bytes = scan_bytes_per_token(H, P, N, G, Q, s_io) * tokens
+    scan_gbs = scan_bytes / (scan_ms / 1e3) / 1e9
+    log(f"chunk_scan alone: {scan_ms:.3f} ms/launch, {scan_gbs:.0f} GB/s algorithmic")
+    del states, dt_t, cs, ys
+    torch.cuda.empty_cache()
+
+    result = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic (seeded; x~N(0,1), dt log-uniform [1e-3,0.1], A=-exp(U(0,ln16)), B,C~N(0,1)/sqrt(N), D~N(0,1))",
+        "config": {"workload": f"{args.workload}: SSD forward b={b} L={L} H={H} P={P} N={N} G={G} "
+                               f"{cfg['dtype']} (Mamba-2 2.7B heads)" if args.workload.startswith("cfg2")
+                   else f"{args.workload}: SSD forward b={b} L={L} H={H} P={P} N={N} G={G} {cfg['dtype']}",
+                   "chunk": Q, "global_batch": b, "seq_len": L, "parallelism": "single GPU"},
+        "throughput": {
+            "tflops_algorithmic": flops / (ms / 1e3) / 1e12,
+            "mfma_frac_algorithmic": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+            "gbs_min_bytes": min_bytes / (ms / 1e3) / 1e9,
+            "hbm_frac_min_bytes": min_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "flop_per_token": fwd_flops_per_token(H, P, N, G, cfg["chunk"]),
+            "min_bytes_per_token": fwd_bytes_per_token(H, P, N, G, s_io),
+        },
+        "roofline": {
+            "kernel": "chunk_scan_kernel<bf16>" if s_io == 2 else "chunk_scan_kernel<float>",
+            "bound": "hbm",
+            "achieved": scan_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": scan_gbs / PEAK_HBM_GBS,
+            "traffic": None,
+            "avg_launch_ms": scan_ms,
+            "algorithmic_bytes_per_launch": scan_bytes,
+        },
+    }
+
+    # ---- decode: 64 back-to-back ssd_step calls on the 2.7B decode shape ------------------------
+    if not args.no_decode:
+        c4 = CONFIGS["cfg4"]
+        si = make_step_inputs(c4["batch"], c4["nheads"], c4["headdim"], c4["dstate"], c4["ngroups"],
+                              steps=c4["steps"], dtype=c4["dtype"], seed=seed_for("cfg4"))
+        S = t(si.state0, torch.float32)
+        sx = [t(si.x[i]) for i in range(c4["steps"])]
+        sdt = [t(si.dt[i]) for i in range(c4["steps"])]
+        sB = [t(si.B[i]) for i in range(c4["steps"])]
+        sC = [t(si.C[i]) for i in range(c4["steps"])]
+        sA, sD = t(si.A, torch.float32), t(si.D, torch.float32)
+        yo = [torch.empty_like(sx[0]) for _ in range(c4["steps"])]
+        for i in range(8):
+            ssd.step(S, sx[i], sdt[i], sA, sB[i], sC[i], sD, y=yo[i])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(c4["steps"]):
+            ssd.step(S, sx[i], sdt[i], sA, sB[i], sC[i], sD, y=yo[i])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        step_ms = e0.elapsed_time(e1) / c4["steps"]
+        bb, hh, pp, nn, gg = c4["batch"], c4["nheads"], c4["headdim"], c4["dstate"], c4["ngroups"]
+        step_bytes = 2 * bb * hh * pp * nn * 4 + bb * hh * (pp * 2 * 2 + 2) + 2 * bb * gg * nn * 2
+        gbs = step_bytes / (step_ms / 1e3) / 1e9
+        result["decode"] = {
+            "workload": f"cfg4: ssd_step b={bb} H={hh} P={pp} N={nn} bf16 io, fp32 state, 64 steps",
+            "us_per_step": step_ms * 1e3,
+            "tokens_per_s": bb / (step_ms / 1e3),
+            "roofline": {"kernel": "step_kernel<bf16>", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": step_bytes},
+            "note": "the 168 MB state fits the 256 MB Infinity Cache, so back-to-back steps can exceed HBM rate",
+        }
+        log(f"decode: {step_ms * 1e3:.1f} us/step, {gbs:.0f} GB/s algorithmic")
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload ----------------
+    if not args.no_cpu_baseline:
+        import oracle
+
+        hs = list(range(min(args.cpu_heads, H)))
+        xs, dts = fi.x[:, :, hs], fi.dt[:, :, hs]
+        t1 = time.perf_counter()
+        oracle.forward(xs, dts, fi.A[hs], fi.B, fi.C, fi.D[hs], None)
+        cpu_s = time.perf_counter() - t1
+        frac = len(hs) / H
+        result["cpu_baseline"] = {
+            "value": tokens * frac / cpu_s,
+            "unit": "tokens/s",
+            "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{len(hs)} of {H} heads over all {L} tokens (b={b}); tokens/s scaled to all heads "
+                      f"({cpu_s:.1f} s, fp64 token recurrence, OpenMP over (b, h))",
+        }
+        log(f"cpu oracle: {cpu_s:.1f}s for {len(hs)} heads on {oracle.max_threads()} threads")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
