@@ -25,6 +25,7 @@ SOURCES = [
     "state_passing.hip",
     "chunk_scan.hip",
     "step.hip",
+    "fused.hip",
 ]
 
 

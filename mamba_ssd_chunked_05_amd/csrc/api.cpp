@@ -143,12 +143,22 @@ Sizes sizes(const ssd::Shape& s) {
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 struct FwdLayout {
+    bool fused;
     size_t dt_t, cs, states, total;
 };
 
-FwdLayout fwd_layout(const ssd::Shape& s) {
+// chunk == 0 asks for the library's choice: the fused path where it applies.
+bool use_fused(const ssd_dims* d, const ssd::Shape& s) { return d->chunk == 0 && ssd::fused_supported(s); }
+
+FwdLayout fwd_layout(const ssd_dims* d, const ssd::Shape& s) {
     Sizes z = sizes(s);
     FwdLayout f;
+    f.fused = use_fused(d, s);
+    if (f.fused) {
+        f.dt_t = f.cs = f.states = 0;
+        f.total = ssd::fused_workspace_bytes(s);
+        return f;
+    }
     f.dt_t = 0;
     f.cs = align256(z.cs);
     f.states = f.cs + align256(z.cs);
@@ -183,10 +193,11 @@ ssd_status ssd_query_config(const ssd_dims* dims, int* chunk, int* tile_p, int* 
     try {
         ssd::Shape s;
         SSD_TRY(check_dims(dims, Need::kForward, &s));
-        if (chunk) *chunk = (int)s.Q;
-        if (tile_p) *tile_p = (int)s.P;
+        const bool fused = use_fused(dims, s);
+        if (chunk) *chunk = fused ? 64 : (int)s.Q;
+        if (tile_p) *tile_p = 16;
         if (heads_per_wg) *heads_per_wg = 1;
-        if (chunks_per_segment) *chunks_per_segment = 1;
+        if (chunks_per_segment) *chunks_per_segment = fused ? ssd::fused_segment_len(s) / 64 : 1;
         return ok();
     } catch (...) {
         return fail(SSD_ERR_HIP, "internal error");
@@ -280,7 +291,7 @@ size_t ssd_forward_workspace_bytes(const ssd_dims* dims) {
     try {
         ssd::Shape s;
         if (check_dims(dims, Need::kForward, &s) != SSD_OK) return 0;
-        return fwd_layout(s).total;
+        return fwd_layout(dims, s).total;
     } catch (...) {
         return 0;
     }
@@ -293,7 +304,7 @@ ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, cons
         ssd::Shape s;
         SSD_TRY(check_dims(dims, Need::kForward, &s));
         Sizes z = sizes(s);
-        FwdLayout f = fwd_layout(s);
+        FwdLayout f = fwd_layout(dims, s);
         Span sx{x, z.x, "x"}, sdt{dt, z.dt, "dt"}, sA{A, z.A, "A"}, sB{B, z.bc, "B"}, sC{C, z.bc, "C"},
             sD{D, D ? z.A : 0, "D"}, sh0{h0, h0 ? z.hstate : 0, "h0"}, sy{y, z.x, "y"},
             sfin{final_state, z.hstate, "final_state"}, sws{workspace, f.total, "workspace"};
@@ -316,6 +327,11 @@ ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, cons
         }
         hipStream_t st = (hipStream_t)stream;
         if (s.b == 0) return ok();
+        if (f.fused) {
+            hipError_t e = ssd::launch_fused_forward(s, x, dt, A, B, C, D, h0, y, final_state, workspace, st);
+            if (e != hipSuccess) return hip_fail(e, "ssd_forward/fused");
+            return ok();
+        }
         char* ws = static_cast<char*>(workspace);
         float* dt_t = reinterpret_cast<float*>(ws + f.dt_t);
         float* cs = reinterpret_cast<float*>(ws + f.cs);

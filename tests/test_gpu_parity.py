@@ -212,3 +212,29 @@ def test_step_shapes(gpu_ssd, P, N, dtype):
     torch.cuda.synchronize()
     assert_close_y(np.stack(ys, axis=1), ref["y"], dtype)
     assert_close_state(host(S), ref["final"])
+
+
+# shapes that take the fused forward (chunk = 0, bf16, headdim 64, dstate 64/128): ragged tails,
+# several segments, G > 1, h0, long memory, sequences shorter than one 64-token chunk
+FUSED = [
+    (1, 1, 4, 64, 128, 1, "config"),
+    (1, 37, 3, 64, 64, 1, "config"),
+    (2, 700, 4, 64, 128, 2, "config"),
+    (1, 4096 + 77, 6, 64, 128, 3, "long_memory"),
+    (3, 1500, 8, 64, 64, 2, "long_memory"),
+    (1, 9000, 2, 64, 128, 1, "extreme"),
+    (1, 20000, 4, 64, 64, 1, "per_head_bias"),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: "b{}_L{}_H{}_P{}_N{}_G{}_{}".format(*c))
+def test_forward_fused(gpu_ssd, case):
+    b, L, H, P, N, G, mode = case
+    a_mode = "minus_one" if mode == "long_memory" else "config"
+    fi = make_forward_inputs(b, L, H, P, N, G, "bf16", 114, dt_mode=mode, a_mode=a_mode, h0_std=0.4)
+    cfg = gpu_ssd.query_config(b, L, H, P, N, G, 0, torch.bfloat16)
+    assert cfg["chunks_per_segment"] > 1 or L <= 256  # the fused path is the one taken
+    ref = oracle.forward(fi.x, fi.dt, fi.A, fi.B, fi.C, fi.D, fi.h0)
+    y, fin = _run_forward(gpu_ssd, fi, 0)
+    assert_close_y(y, ref["y"], "bf16")
+    assert_close_state(fin, ref["final"])
