@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--workload", default="cfg2_64k", help="a forward workload name from synth.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle's timed sample")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle's timed sample (0 = all)")
     return ap.parse_args()
 
 
@@ -123,25 +123,39 @@ def main():
     min_bytes = fwd_bytes_per_token(H, P, N, G, s_io) * tokens + b * H * P * N * 4
     log(f"forward: {ms:.3f} ms/step, {tok_s / 1e6:.1f} M tok/s, {flops / (ms / 1e3) / 1e12:.1f} TFLOP/s algorithmic")
 
-    # ---- dominant kernel: the chunk scan, timed alone on the stream it runs on ------------
+    # ---- the forward's stages, each timed alone on the stream it runs on ----------------------
+    # ssd_forward is exactly these four calls at chunk Q; the chunk scan dominates.
     stream = torch.cuda.current_stream(dev)
     dt_t, cs = ssd.chunk_cumsum(dt, A, Q)
     states = ssd.chunk_state(x, B, dt_t, cs, Q)
     ssd.state_passing(states, cs, None, seqlen=L, chunk=Q, io=tdt)
     ys = torch.empty_like(x)
-    for _ in range(args.warmup):
-        ssd.chunk_scan(x, B, C, dt_t, cs, states, D, chunk=Q, y=ys)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        ssd.chunk_scan(x, B, C, dt_t, cs, states, D, chunk=Q, y=ys)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    scan_ms = ev0.elapsed_time(ev1) / args.steps
+
+    def timed(fn, reps):
+        for _ in range(min(args.warmup, 3)):
+            fn()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    scan_ms = timed(lambda: ssd.chunk_scan(x, B, C, dt_t, cs, states, D, chunk=Q, y=ys), args.steps)
+    stage_ms = {
+        "chunk_cumsum": timed(lambda: ssd.chunk_cumsum(dt, A, Q), args.steps),
+        "chunk_state": timed(lambda: ssd.chunk_state(x, B, dt_t, cs, Q), args.steps),
+        "chunk_scan": scan_ms,
+    }
+    scratch = states.clone()
+    stage_ms["state_passing"] = timed(lambda: ssd.state_passing(scratch, cs, None, seqlen=L, chunk=Q, io=tdt),
+                                      args.steps)
     scan_bytes = scan_bytes_per_token(H, P, N, G, Q, s_io) * tokens
     scan_gbs = scan_bytes / (scan_ms / 1e3) / 1e9
+    log(f"stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
     log(f"chunk_scan alone: {scan_ms:.3f} ms/launch, {scan_gbs:.0f} GB/s algorithmic")
-    del states, dt_t, cs, ys
+    del states, dt_t, cs, ys, scratch
     torch.cuda.empty_cache()
 
     result = {
@@ -169,8 +183,9 @@ def main():
             "flop_per_token": fwd_flops_per_token(H, P, N, G, cfg["chunk"]),
             "min_bytes_per_token": fwd_bytes_per_token(H, P, N, G, s_io),
         },
+        "stage_ms": stage_ms,
         "roofline": {
-            "kernel": "chunk_scan_kernel<bf16>" if s_io == 2 else "chunk_scan_kernel<float>",
+            "kernel": "chunk_scan (ssd_chunk_scan at the forward's chunk size)",
             "bound": "hbm",
             "achieved": scan_gbs,
             "peak": PEAK_HBM_GBS,
@@ -220,7 +235,7 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
 
-        hs = list(range(min(args.cpu_heads, H)))
+        hs = list(range(min(args.cpu_heads, H) if args.cpu_heads > 0 else H))
         xs, dts = fi.x[:, :, hs], fi.dt[:, :, hs]
         t1 = time.perf_counter()
         oracle.forward(xs, dts, fi.A[hs], fi.B, fi.C, fi.D[hs], None)

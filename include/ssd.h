@@ -47,9 +47,10 @@
  * which leaves the state unchanged; their rows are never written.
  *
  * Supported sizes: P and N multiples of 16 with P <= 256 and N <= 1024;
- * Q a multiple of 16 in [16, 512]; H divisible by G; b, L >= 0 (an empty
- * batch or sequence is a valid no-op).  Other sizes return
- * SSD_ERR_UNSUPPORTED.
+ * Q a multiple of 16 in [16, 512] -- or a multiple of 64 up to 4096 for bf16
+ * with P = 64 and N in {64, 128}, the shapes served by the fast chunk
+ * kernels; H divisible by G; b, L >= 0 (an empty batch or sequence is a valid
+ * no-op).  Other sizes return SSD_ERR_UNSUPPORTED.
  */
 #ifndef SSD_H
 #define SSD_H
@@ -172,8 +173,8 @@ int ssd_abi_version(void);
 /*
  * The tiling ssd_forward would use for these dims: the chunk size, the
  * P-tile and the number of heads per workgroup of its output kernel, and the
- * number of chunks per segment of its carried-state pass (1 = staged).  Any
- * pointer may be NULL.
+ * number of 64-token sub-chunks its chunk kernels walk in registers per chunk
+ * (1 = the generic kernels, which do not sub-chunk).  Any pointer may be NULL.
  */
 ssd_status ssd_query_config(const ssd_dims* dims, int* chunk, int* tile_p, int* heads_per_wg,
                             int* chunks_per_segment);

@@ -40,7 +40,7 @@ constexpr int64_t kMaxGrid = 0x7fffffffLL;
 // ---------------------------------------------------------------------------
 // dims validation
 // ---------------------------------------------------------------------------
-enum class Need { kStaged, kForward, kStep };
+enum class Need { kStaged, kCumsum, kForward, kStep };
 
 ssd_status check_dims(const ssd_dims* d, Need need, ssd::Shape* out) {
     if (!d) return fail(SSD_ERR_NULL, "dims is NULL");
@@ -75,16 +75,21 @@ ssd_status check_dims(const ssd_dims* d, Need need, ssd::Shape* out) {
     }
     int64_t Q = d->chunk;
     if (Q == 0) {
-        if (need == Need::kStaged) return fail(SSD_ERR_UNSUPPORTED, "the staged calls need an explicit chunk > 0");
-        Q = 256;  // tuned default of the staged forward
+        if (need != Need::kForward) return fail(SSD_ERR_UNSUPPORTED, "the staged calls need an explicit chunk > 0");
+        // the forward's own choice: a large chunk on the fast path, else 256
+        s.Q = 64;
+        Q = ssd::fast_chunk_supported(s) ? ssd::fast_forward_chunk(s) : 256;
     }
-    if (Q % 16 || Q < 16 || Q > 512)
-        return fail(SSD_ERR_UNSUPPORTED, "chunk %lld: need a multiple of 16 in [16, 512]", (long long)Q);
     s.Q = Q;
+    // the cumulative sum has no headdim/dstate dependence: any chunk the other calls accept
+    const bool fast = Q % 64 == 0 && (need == Need::kCumsum || ssd::fast_chunk_supported(s));
+    if (Q % 16 || Q < 16 || Q > (fast ? 4096 : 512))
+        return fail(SSD_ERR_UNSUPPORTED, "chunk %lld: need a multiple of 16 in [16, 512] (multiple of 64 up to "
+                    "4096 for bf16 with headdim 64 and dstate 64/128)", (long long)Q);
     s.nC = (s.L + Q - 1) / Q;
     if (s.b * s.nC * s.H * s.N > kMaxGrid || s.H > 65535 || s.b > 65535)
         return fail(SSD_ERR_UNSUPPORTED, "problem too large for one launch grid");
-    if (ssd::chunk_scan_lds_bytes(s) > 160 * 1024 || ssd::chunk_state_lds_bytes(s) > 160 * 1024)
+    if (!fast && (ssd::chunk_scan_lds_bytes(s) > 160 * 1024 || ssd::chunk_state_lds_bytes(s) > 160 * 1024))
         return fail(SSD_ERR_UNSUPPORTED, "tile shapes exceed the 160 KiB LDS");
     *out = s;
     return SSD_OK;
@@ -143,22 +148,12 @@ Sizes sizes(const ssd::Shape& s) {
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 struct FwdLayout {
-    bool fused;
     size_t dt_t, cs, states, total;
 };
 
-// chunk == 0 asks for the library's choice: the fused path where it applies.
-bool use_fused(const ssd_dims* d, const ssd::Shape& s) { return d->chunk == 0 && ssd::fused_supported(s); }
-
-FwdLayout fwd_layout(const ssd_dims* d, const ssd::Shape& s) {
+FwdLayout fwd_layout(const ssd::Shape& s) {
     Sizes z = sizes(s);
     FwdLayout f;
-    f.fused = use_fused(d, s);
-    if (f.fused) {
-        f.dt_t = f.cs = f.states = 0;
-        f.total = ssd::fused_workspace_bytes(s);
-        return f;
-    }
     f.dt_t = 0;
     f.cs = align256(z.cs);
     f.states = f.cs + align256(z.cs);
@@ -193,11 +188,11 @@ ssd_status ssd_query_config(const ssd_dims* dims, int* chunk, int* tile_p, int* 
     try {
         ssd::Shape s;
         SSD_TRY(check_dims(dims, Need::kForward, &s));
-        const bool fused = use_fused(dims, s);
-        if (chunk) *chunk = fused ? 64 : (int)s.Q;
+        const bool fast = ssd::fast_chunk_supported(s);
+        if (chunk) *chunk = (int)s.Q;
         if (tile_p) *tile_p = 16;
-        if (heads_per_wg) *heads_per_wg = 1;
-        if (chunks_per_segment) *chunks_per_segment = fused ? ssd::fused_segment_len(s) / 64 : 1;
+        if (heads_per_wg) *heads_per_wg = fast ? ssd::fast_heads_per_wg(s) : 1;
+        if (chunks_per_segment) *chunks_per_segment = fast ? (int)(s.Q / 64) : 1;
         return ok();
     } catch (...) {
         return fail(SSD_ERR_HIP, "internal error");
@@ -208,7 +203,7 @@ ssd_status ssd_chunk_cumsum(const ssd_dims* dims, const void* dt, const float* A
                             void* stream) {
     try {
         ssd::Shape s;
-        SSD_TRY(check_dims(dims, Need::kStaged, &s));
+        SSD_TRY(check_dims(dims, Need::kCumsum, &s));
         Sizes z = sizes(s);
         Span sdt{dt, z.dt, "dt"}, sA{A, z.A, "A"}, sdtt{dt_t, z.cs, "dt_t"}, scs{dA_cs_log2, z.cs, "dA_cs_log2"};
         for (const Span& p : {sdt, sA, sdtt, scs}) SSD_TRY(need_ptr(p));
@@ -291,7 +286,7 @@ size_t ssd_forward_workspace_bytes(const ssd_dims* dims) {
     try {
         ssd::Shape s;
         if (check_dims(dims, Need::kForward, &s) != SSD_OK) return 0;
-        return fwd_layout(dims, s).total;
+        return fwd_layout(s).total;
     } catch (...) {
         return 0;
     }
@@ -304,7 +299,7 @@ ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, cons
         ssd::Shape s;
         SSD_TRY(check_dims(dims, Need::kForward, &s));
         Sizes z = sizes(s);
-        FwdLayout f = fwd_layout(dims, s);
+        FwdLayout f = fwd_layout(s);
         Span sx{x, z.x, "x"}, sdt{dt, z.dt, "dt"}, sA{A, z.A, "A"}, sB{B, z.bc, "B"}, sC{C, z.bc, "C"},
             sD{D, D ? z.A : 0, "D"}, sh0{h0, h0 ? z.hstate : 0, "h0"}, sy{y, z.x, "y"},
             sfin{final_state, z.hstate, "final_state"}, sws{workspace, f.total, "workspace"};
@@ -327,11 +322,6 @@ ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, cons
         }
         hipStream_t st = (hipStream_t)stream;
         if (s.b == 0) return ok();
-        if (f.fused) {
-            hipError_t e = ssd::launch_fused_forward(s, x, dt, A, B, C, D, h0, y, final_state, workspace, st);
-            if (e != hipSuccess) return hip_fail(e, "ssd_forward/fused");
-            return ok();
-        }
         char* ws = static_cast<char*>(workspace);
         float* dt_t = reinterpret_cast<float*>(ws + f.dt_t);
         float* cs = reinterpret_cast<float*>(ws + f.cs);

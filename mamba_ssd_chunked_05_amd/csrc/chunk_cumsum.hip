@@ -7,9 +7,10 @@
 // layout is (b, H, nC, Q) so the later stages read each chunk's values as one
 // contiguous run (the layout change of that page's section 3).
 //
-// One wavefront per (b, h, c): each lane owns ceil(Q/64) consecutive
-// positions, sums them serially, and a 6-step wavefront prefix over the lane
-// totals gives every lane its offset.  Bandwidth-trivial (< 3% of the bytes).
+// One wavefront per (b, h, c), walking the chunk in blocks of 512 positions:
+// each lane owns up to 8 consecutive positions of a block and sums them
+// serially, a 6-step wavefront prefix over the lane totals gives every lane its
+// offset, and the block total carries into the next block.  Bandwidth-trivial.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -26,38 +27,44 @@ __global__ void __launch_bounds__(256) chunk_cumsum_kernel(const T* __restrict__
     const int64_t c = (wid / H) % nC;
     const int64_t b = wid / ((int64_t)H * nC);
     const float a = A[h];
-    const int E = (Q + 63) / 64;  // positions per lane (Q <= 512 -> E <= 8)
-    float v[8], d[8];
-    float run = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        v[e] = 0.0f;
-        d[e] = 0.0f;
-        if (e < E) {
-            int i = lane * E + e;
-            int64_t t = c * Q + i;
-            if (i < Q && t < L) d[e] = to_f32(dt[(b * L + t) * H + h]);
-            run += d[e] * a;
-            v[e] = run;
-        }
-    }
-    // inclusive prefix of the lane totals across the wavefront
-    float incl = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        float up = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += up;
-    }
-    float excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.0f;
     const int64_t base = ((b * H + h) * nC + c) * Q;
+    float carry = 0.0f;  // sum over the chunk's earlier 512-token blocks
+    for (int q0 = 0; q0 < Q; q0 += 512) {
+        const int qb = Q - q0 < 512 ? Q - q0 : 512;
+        const int E = (qb + 63) / 64;  // positions per lane in this block (<= 8)
+        float v[8], d[8];
+        float run = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        int i = lane * E + e;
-        if (e < E && i < Q) {
-            cs[base + i] = (excl + v[e]) * kLog2e;
-            dt_t[base + i] = d[e];
+        for (int e = 0; e < 8; ++e) {
+            v[e] = 0.0f;
+            d[e] = 0.0f;
+            if (e < E) {
+                const int i = lane * E + e;
+                const int64_t t = c * Q + q0 + i;
+                if (i < qb && t < L) d[e] = to_f32(dt[(b * L + t) * H + h]);
+                run += d[e] * a;
+                v[e] = run;
+            }
         }
+        // inclusive prefix of the lane totals across the wavefront
+        float incl = run;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float up = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += up;
+        }
+        float excl = __shfl_up(incl, 1, 64);
+        if (lane == 0) excl = 0.0f;
+        excl += carry;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = lane * E + e;
+            if (e < E && i < qb) {
+                cs[base + q0 + i] = (excl + v[e]) * kLog2e;
+                dt_t[base + q0 + i] = d[e];
+            }
+        }
+        carry += __shfl(incl, 63, 64);
     }
 }
 

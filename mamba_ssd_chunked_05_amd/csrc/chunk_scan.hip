@@ -239,6 +239,7 @@ static hipError_t launch_sc(const Shape& s, const void* x, const void* B, const 
 
 hipError_t launch_chunk_scan(const Shape& s, const void* x, const void* B, const void* C, const float* dt_t,
                              const float* cs, const float* start, const float* D, void* y, hipStream_t st) {
+    if (fast_chunk_supported(s)) return launch_chunk_scan_fast(s, x, B, C, dt_t, cs, start, D, y, st);
     return s.io == 1 ? launch_sc<bf16>(s, x, B, C, dt_t, cs, start, D, y, st)
                      : launch_sc<float>(s, x, B, C, dt_t, cs, start, D, y, st);
 }

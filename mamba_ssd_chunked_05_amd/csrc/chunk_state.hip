@@ -160,6 +160,7 @@ static hipError_t launch_cs(const Shape& s, const void* x, const void* B, const 
 
 hipError_t launch_chunk_state(const Shape& s, const void* x, const void* B, const float* dt_t, const float* cs,
                               float* states, hipStream_t st) {
+    if (fast_chunk_supported(s)) return launch_chunk_state_fast(s, x, B, dt_t, cs, states, st);
     return s.io == 1 ? launch_cs<bf16>(s, x, B, dt_t, cs, states, st)
                      : launch_cs<float>(s, x, B, dt_t, cs, states, st);
 }

@@ -1,27 +1,41 @@
-// fused.hip -- the fused forward for bf16 inputs with headdim 64.
+// fused.hip -- fast chunk-state and chunk-scan kernels for bf16 inputs with
+// headdim 64 and dstate 64 or 128, for any chunk size Q that is a multiple of 64.
 //
-// The chunked method (devotd.net cuTile Mamba-2 page, sections 1-2) is
-// re-arranged around the associativity of the recurrence ("3.3 Hardware-Aware
-// algorithms ...", section 4.1) so that the per-chunk states never touch HBM:
+// They compute exactly the staged calls of the cuTile Mamba-2 page (devotd.net,
+// section 2): the chunk-local states, and the chunk output from the chunk-start
+// state.  Inside a chunk they walk 64-token sub-chunks in order, which is the
+// same recurrence regrouped once more ("3.3 Hardware-Aware algorithms ...",
+// section 4.1, associativity):
 //
-//   1. segment_state_kernel  -- one pass over x and B per (b, segment, h): the
-//      state the segment produces from a zero start (hi/lo bf16 MFMA, fp32
-//      accumulation, rescaled by each 128-token block's decay) and the
-//      segment's total log2 decay.
-//   2. state_passing_kernel  -- the chunk-order pass at segment granularity:
-//      segment-start states and the final state (fp32).
-//   3. fused_scan_kernel     -- per (b, segment, h): walk the segment in
-//      64-token chunks carrying the fp32 state in registers.  Per chunk:
-//          y   = 2^(l_i) C_i . S  +  sum_{j<=i} (C_i . B_j) 2^(l_i-l_j) dt_j x_j  +  D x_i
-//          S  <- 2^(l_63) S + sum_j 2^(l_63-l_j) dt_j B_j (outer) x_j
-//      Nothing but y leaves the kernel.
+//   chunk_state_fast_kernel  per (b, chunk, head pair): S <- 2^(l_63) S + B^T (w x)
+//                            per sub-chunk, from S = 0, with the scaled operand
+//                            split into hi + lo bf16 parts (fp32-level state).
+//   chunk_scan_fast_kernel   per (b, chunk, head pair): carry the fp32 state in
+//                            registers from the chunk-start state; per sub-chunk
+//                              y  = 2^(l_i) C_i . S + sum_{j<=i} (C_i . B_j) 2^(l_i-l_j) dt_j x_j + D x_i
+//                              S <- 2^(l_63) S + sum_j 2^(l_63-l_j) dt_j B_j (outer) x_j
+//                            with l relative to the sub-chunk start.  Only y is written.
 //
-// All contractions of the output kernel are computed transposed (Y^T = S C^T +
-// X^T M) so that every operand comes either straight from an accumulator (the
-// carried state, the decayed C.B^T tiles) or from a bank-conflict-free LDS
-// read; the state never round-trips through LDS.  Within a chunk the decay
-// factors are formed in fp32 with exp2 and the upper triangle is selected to
-// zero before it is used (static masking).
+// With a large chunk (a few thousand tokens) the per-chunk states are few, so
+// the forward's state traffic through HBM stays small while every kernel still
+// has thousands of independent work items.
+//
+// Layout choices (gfx950):
+//   * x, B and C sub-chunks sit in LDS in their natural row-major layout.
+//     Operands whose contraction runs over tokens (X^T, B^T) are fetched with the
+//     LDS transpose read (ds_read_b64_tr_b16: a 16-lane group reads a 4 x 16
+//     block and each lane receives one column); nothing is transposed in
+//     registers.
+//   * Row strides make the fragment reads bank-conflict-free: x rows of 80 bf16
+//     and B rows of N+16 bf16 (transpose reads of 8 rows land in 8 distinct
+//     8-bank groups), C rows of N+8 bf16 (row reads of 16 rows).
+//   * The output is computed transposed, Y^T = S C^T + X^T M, so the carried
+//     state feeds the MFMA straight from its accumulator registers, and the
+//     decayed C.B^T tiles are stored in LDS in fragment order.
+//   * Two heads share a workgroup: the B and C tiles, the C.B^T tiles and the C
+//     and B^T fragments are loaded once for both heads.
+//   * The decay is formed in fp32 with exp2; the upper triangle is selected to
+//     zero before use (static masking).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -29,29 +43,23 @@ namespace ssd {
 namespace fz {
 
 constexpr int P = 64;
-constexpr int QS = 64;          // tokens per chunk of the output kernel
-constexpr int XROW = QS + 8;    // bf16 row of X^T and B^T (144 bytes: conflict-free)
-constexpr int QA = 128;         // tokens per block of the segment-state kernel
-constexpr int AROW = QA + 8;
+constexpr int QS = 64;        // tokens per chunk
+constexpr int XS = P + 16;    // x row stride (bf16)
 
-typedef uint32_t u32;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// 8x8 transpose of bf16 held as 8 rows x uint4 (8 bf16 per row).
-__device__ __forceinline__ void transpose8(const uint4 (&v)[8], uint4 (&t)[8]) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        u32 w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint4& a = v[2 * k];
-            const uint4& b = v[2 * k + 1];
-            const int q = c >> 1;
-            const u32 av = q == 0 ? a.x : q == 1 ? a.y : q == 2 ? a.z : a.w;
-            const u32 bv = q == 0 ? b.x : q == 1 ? b.y : q == 2 ? b.z : b.w;
-            w[k] = (c & 1) ? ((av >> 16) | (bv & 0xffff0000u)) : ((av & 0xffffu) | (bv << 16));
-        }
-        t[c] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
+template <int N>
+struct Strides {
+    static constexpr int BS = N + 16;  // B rows: transpose reads
+    static constexpr int CS = N + 8;   // C rows: row reads
+};
+
+// Transpose read: rows [row0, row0+4) x columns [col0, col0+16) of a row-major
+// bf16 LDS tile with leading dimension ld; lane (16g + j) receives column
+// col0 + j, rows row0..row0+3 (row0 may differ between 16-lane groups).
+__device__ __forceinline__ bf16x4 tr_read(const bf16* tile, int row0, int col0, int ld, int l16) {
+    const bf16* p = tile + (row0 + (l16 >> 2)) * ld + col0 + 4 * (l16 & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
 __device__ __forceinline__ bf16x8 pack8(const bf16x4& a, const bf16x4& b) {
@@ -67,232 +75,326 @@ __device__ __forceinline__ bf16x4 cvt4(const f32x4& v) {
     return r;
 }
 
+__device__ __forceinline__ uint4 ld16(const bf16* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// ---------------------------------------------------------------------------
+// chunk staging shared by both kernels: x (HPW heads), B, C (optional), dt
+// ---------------------------------------------------------------------------
+template <int N, int HPW, bool WITH_C>
+struct ChunkRegs {
+    uint4 x[2 * HPW];
+    uint4 b[N / 32];
+    uint4 c[WITH_C ? N / 32 : 1];
+    float dt;   // dt_t of token (tid & 63) of head (tid >> 6), threads < 64 * HPW
+    float cs;   // chunk cumulative log2 decay of that token
+};
+
+// Per-thread staging offsets at token 0.  Chunk k of a thread is chunk
+// (tid + 256 k) of the tile, so every offset is a base plus a compile-time
+// multiple of k: x chunk k covers head k / 2, rows (tid / 8) + 32 (k % 2);
+// B / C chunk k covers row tid / (N / 8) + k * (256 / (N / 8)).
+template <int N, int HPW>
+struct ChunkAddr {
+    int64_t xo, bo, dto;   // global element offsets of this thread's first x, B/C rows; dt_t/cs element
+    int xr, br;            // first x / B row of this thread within the chunk
+    int xl, bl, cl;        // LDS element offsets of the first x / B / C chunk
+};
+
+template <int N>
+struct BRows {
+    static constexpr int RPI = 256 / (N / 8);  // B rows covered by one pass of 256 threads
+};
+
+template <int N, int HPW>
+__device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int64_t b, int64_t L, int H, int G, int h0, int g,
+                                           int64_t c, int64_t nC, int Q, int tid) {
+    constexpr int BS = Strides<N>::BS, CS = Strides<N>::CS;
+    const int xr = tid >> 3, xc = (tid & 7) * 8;
+    a.xr = xr;
+    a.xo = ((b * L + xr) * H + h0) * (int64_t)P + xc;
+    a.xl = xr * XS + xc;
+    const int br = tid / (N / 8), bc = (tid % (N / 8)) * 8;
+    a.br = br;
+    a.bo = ((b * L + br) * G + g) * (int64_t)N + bc;
+    a.bl = br * BS + bc;
+    a.cl = br * CS + bc;
+    const int hh = tid >> 6, r = tid & 63;
+    a.dto = ((b * H + h0 + (hh < HPW ? hh : 0)) * nC + c) * Q + r;
+}
+
+// Load the chunk starting at token tbase into registers (rows past L read as zero).
+template <int N, int HPW, bool WITH_C>
+__device__ __forceinline__ void chunk_load(ChunkRegs<N, HPW, WITH_C>& rg, const ChunkAddr<N, HPW>& a,
+                                           const bf16* __restrict__ x, const float* __restrict__ dt_t,
+                                           const float* __restrict__ cs, const bf16* __restrict__ B,
+                                           const bf16* __restrict__ C, int64_t tbase, int sub, int64_t L, int H,
+                                           int G, int tid) {
+    constexpr int RPI = BRows<N>::RPI;
+    if (tid < 64 * HPW) {  // dt_t and cs cover every position of the chunk (zero-padded past L)
+        rg.dt = dt_t[a.dto + QS * sub];
+        rg.cs = cs[a.dto + QS * sub];
+    }
+    const int64_t HP_ = (int64_t)H * P, GN = (int64_t)G * N;
+    const bf16* xb = x + a.xo + tbase * HP_;
+    const bf16* bb = B + a.bo + tbase * GN;
+    const bf16* cb = WITH_C ? C + a.bo + tbase * GN : nullptr;
+    if (tbase + QS <= L) {
+#pragma unroll
+        for (int k = 0; k < 2 * HPW; ++k) rg.x[k] = ld16(xb + (k & 1) * 32 * HP_ + (k >> 1) * P);
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) rg.b[k] = ld16(bb + k * RPI * GN);
+        if (WITH_C) {
+#pragma unroll
+            for (int k = 0; k < N / 32; ++k) rg.c[k] = ld16(cb + k * RPI * GN);
+        }
+    } else {
+        // ragged last chunk: clamp the row to the last valid one, then select zero
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        const int last = (int)(L - 1 - tbase);
+#pragma unroll
+        for (int k = 0; k < 2 * HPW; ++k) {
+            const int r = a.xr + (k & 1) * 32;
+            const bool ok = r <= last;
+            const uint4 v = ld16(xb + (int64_t)((ok ? r : last) - a.xr) * HP_ + (k >> 1) * P);
+            rg.x[k] = ok ? v : z;
+        }
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) {
+            const int r = a.br + k * RPI;
+            const bool ok = r <= last;
+            const int64_t off = (int64_t)((ok ? r : last) - a.br) * GN;
+            const uint4 v = ld16(bb + off);
+            rg.b[k] = ok ? v : z;
+            if (WITH_C) {
+                const uint4 u = ld16(cb + off);
+                rg.c[k] = ok ? u : z;
+            }
+        }
+    }
+}
+
+// registers -> LDS, and the in-chunk cumulative decay (one wavefront per head)
+// cs_prev: the chunk cumulative decay before this sub-chunk (0 for the first),
+// held by wavefront hh for head hh and advanced here.
+template <int N, int HPW, bool WITH_C>
+__device__ __forceinline__ void chunk_store(bf16* xs, bf16* bsm, bf16* csm, float* lw, float* dtw, float* ww,
+                                            float* alpha, const ChunkRegs<N, HPW, WITH_C>& rg,
+                                            const ChunkAddr<N, HPW>& a, float& cs_prev, int tid) {
+    constexpr int RPI = BRows<N>::RPI, BS = Strides<N>::BS, CS = Strides<N>::CS;
+#pragma unroll
+    for (int k = 0; k < 2 * HPW; ++k)
+        *reinterpret_cast<uint4*>(xs + a.xl + (k >> 1) * QS * XS + (k & 1) * 32 * XS) = rg.x[k];
+#pragma unroll
+    for (int k = 0; k < N / 32; ++k) {
+        *reinterpret_cast<uint4*>(bsm + a.bl + k * RPI * BS) = rg.b[k];
+        if (WITH_C) *reinterpret_cast<uint4*>(csm + a.cl + k * RPI * CS) = rg.c[k];
+    }
+    if (tid < 64 * HPW) {
+        const int hh = tid >> 6, lane = tid & 63;
+        const float d = rg.dt;
+        const float incl = rg.cs - cs_prev;  // cumulative log2 decay inside the sub-chunk
+        const float last = __shfl(incl, 63, 64);
+        cs_prev = __shfl(rg.cs, 63, 64);
+        lw[hh * QS + lane] = incl;
+        dtw[hh * QS + lane] = d;
+        ww[hh * QS + lane] = fast_exp2(last - incl) * d;
+        if (lane == 0) alpha[hh] = fast_exp2(last);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // fused output kernel
 // ---------------------------------------------------------------------------
-template <int N>
+template <int N, int HPW>
 struct ScanLds {
-    bf16 xt[P * XROW];            // X^T [p][j]
-    bf16 bt[N * XROW];            // B^T [n][j]
-    bf16 bn[QS * (N + 8)];        // B   [j][n]
-    bf16 cn[QS * (N + 8)];        // C   [i][n]
-    bf16 mb[16 * 64 * 4];         // decayed C.B^T tiles in fragment order [jt*4+it][lane][4]
-    float lw[QS];                 // in-chunk cumulative log2 decay
-    float dtw[QS];                // dt
-    float ww[QS];                 // 2^(l_63 - l_j) dt_j
-    float alpha[4];               // 2^(l_63)
+    bf16 xs[HPW * QS * XS];         // x [hh][j][p]
+    bf16 bs[QS * Strides<N>::BS];   // B [j][n]
+    bf16 cs[QS * Strides<N>::CS];   // C [i][n]
+    bf16 mb[HPW * 16 * 256];        // decayed C.B^T tiles, fragment order [hh][jt*4+it][lane][4]
+    float lw[HPW * QS];             // in-chunk cumulative log2 decay
+    float dtw[HPW * QS];            // dt
+    float ww[HPW * QS];             // 2^(l_63 - l_j) dt_j
+    float alpha[4];                 // 2^(l_63) per head
 };
 
-// (j-tile, i-tile) pairs of the causal 4x4 tile triangle, spread over 4 wavefronts
 __constant__ int8_t kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 __constant__ int8_t kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 
-template <int N>
-struct ScanPrefetch {
-    uint4 blk[8];   // an 8x8 block of x (threads 0..63) or of B (threads 64..64+N-1)
-    uint4 c[N / 32];
-    float dt;
-};
-
-template <int N>
-__device__ __forceinline__ void scan_load(ScanPrefetch<N>& pf, const bf16* __restrict__ x, const bf16* __restrict__ dt,
-                                          const bf16* __restrict__ B, const bf16* __restrict__ C, int64_t b,
-                                          int64_t L, int H, int G, int h, int g, int64_t tbase, int tid) {
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    if (tid < 64) {
-        const int rb = tid & 7, cb = tid >> 3;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int64_t t = tbase + 8 * rb + r;
-            pf.blk[r] = t < L ? *reinterpret_cast<const uint4*>(x + ((b * L + t) * H + h) * P + 8 * cb) : z;
-        }
-        const int64_t t = tbase + tid;
-        pf.dt = t < L ? to_f32(dt[(b * L + t) * H + h]) : 0.0f;
-    } else if (tid < 64 + N) {
-        const int k = tid - 64, rb = k & 7, cb = k >> 3;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int64_t t = tbase + 8 * rb + r;
-            pf.blk[r] = t < L ? *reinterpret_cast<const uint4*>(B + ((b * L + t) * G + g) * N + 8 * cb) : z;
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < N / 32; ++k) {
-        const int chunk = tid + 256 * k;
-        const int row = chunk / (N / 8), c8 = chunk % (N / 8);
-        const int64_t t = tbase + row;
-        pf.c[k] = t < L ? *reinterpret_cast<const uint4*>(C + ((b * L + t) * G + g) * N + 8 * c8) : z;
-    }
-}
-
-template <int N>
-__device__ __forceinline__ void scan_store(ScanLds<N>& sm, const ScanPrefetch<N>& pf, float a_log2, int tid) {
-    if (tid < 64) {
-        const int rb = tid & 7, cb = tid >> 3;
-        uint4 tr[8];
-        transpose8(pf.blk, tr);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(&sm.xt[(8 * cb + c) * XROW + 8 * rb]) = tr[c];
-        // in-chunk cumulative log2 decay: one token per lane of wavefront 0
-        const float d = pf.dt;
-        float incl = d * a_log2;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float up = __shfl_up(incl, off, 64);
-            if (tid >= off) incl += up;
-        }
-        const float last = __shfl(incl, 63, 64);
-        sm.lw[tid] = incl;
-        sm.dtw[tid] = d;
-        sm.ww[tid] = fast_exp2(last - incl) * d;
-        if (tid == 0) sm.alpha[0] = fast_exp2(last);
-    } else if (tid < 64 + N) {
-        const int k = tid - 64, rb = k & 7, cb = k >> 3;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) *reinterpret_cast<uint4*>(&sm.bn[(8 * rb + r) * (N + 8) + 8 * cb]) = pf.blk[r];
-        uint4 tr[8];
-        transpose8(pf.blk, tr);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(&sm.bt[(8 * cb + c) * XROW + 8 * rb]) = tr[c];
-    }
-#pragma unroll
-    for (int k = 0; k < N / 32; ++k) {
-        const int chunk = tid + 256 * k;
-        const int row = chunk / (N / 8), c8 = chunk % (N / 8);
-        *reinterpret_cast<uint4*>(&sm.cn[row * (N + 8) + 8 * c8]) = pf.c[k];
-    }
-}
-
-template <int N>
+template <int N, int HPW>
 __global__ void __launch_bounds__(256, 2)
-fused_scan_kernel(const bf16* __restrict__ x, const bf16* __restrict__ dt, const float* __restrict__ A,
-                  const bf16* __restrict__ B, const bf16* __restrict__ C, const float* __restrict__ D,
-                  const float* __restrict__ seg_start, bf16* __restrict__ y, int64_t L, int H, int G, int seg_len,
-                  int nSeg, uint32_t nitems) {
-    constexpr int NT = N / 16;  // state tiles per wavefront (n direction)
-    constexpr int NK = N / 32;  // K-steps over n
+chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, const bf16* __restrict__ C,
+                       const float* __restrict__ dt_t, const float* __restrict__ cs,
+                       const float* __restrict__ start, const float* __restrict__ D, bf16* __restrict__ y, int64_t L,
+                       int H, int G, int Q, int64_t nC, uint32_t nitems) {
+    constexpr int NT = N / 16, NK = N / 32;
+    constexpr int BS = Strides<N>::BS, CS = Strides<N>::CS;
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    ScanLds<N>& sm = *reinterpret_cast<ScanLds<N>*>(smem_raw);
+    ScanLds<N, HPW>& sm = *reinterpret_cast<ScanLds<N, HPW>*>(smem_raw);
 
+    const int HP = H / HPW;
     const uint32_t item = xcd_remap(blockIdx.x, nitems);
-    const int h = (int)(item % (uint32_t)H);
-    const int s = (int)((item / (uint32_t)H) % (uint32_t)nSeg);
-    const int64_t b = item / ((uint32_t)H * (uint32_t)nSeg);
-    const int g = h / (H / G);
+    const int hp = (int)(item % (uint32_t)HP);
+    const int64_t c = (item / (uint32_t)HP) % (uint32_t)nC;
+    const int64_t b = item / ((uint32_t)HP * (uint32_t)nC);
+    const int h0 = hp * HPW;
+    const int g = h0 / (H / G);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
-    const float a_log2 = A[h] * kLog2e;
-    const float Dh = D ? D[h] : 0.0f;
-    const int64_t t0 = (int64_t)s * seg_len;
-    const int64_t t_end = t0 + seg_len < L ? t0 + seg_len : L;
-    const int nsub = (int)((t_end - t0 + QS - 1) / QS);
-
-    // carried state, transposed: tile nt holds S[p = 16w + l16][n = 16nt + 4g4 + r]
-    f32x4 st[NT];
-    {
-        const float* S0 = seg_start + ((b * nSeg + s) * H + h) * (int64_t)P * N + (int64_t)(16 * w + l16) * N;
+    float Dh[HPW];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) st[nt] = *reinterpret_cast<const f32x4*>(S0 + 16 * nt + 4 * g4);
+    for (int hh = 0; hh < HPW; ++hh) Dh[hh] = D ? D[h0 + hh] : 0.0f;
+    const int64_t t0 = c * Q;
+    const int64_t t_end = t0 + Q < L ? t0 + Q : L;
+    const int nsub = (int)((t_end - t0 + QS - 1) / QS);
+    float cs_prev = 0.0f;
+
+    // carried state per head, transposed: st[hh][nt] holds S[p = 16w + l16][n = 16nt + 4g4 + r]
+    f32x4 st[HPW][NT];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+        const float* S0 =
+            start + ((b * nC + c) * H + h0 + hh) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 4 * g4;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st[hh][nt] = *reinterpret_cast<const f32x4*>(S0 + 16 * nt);
     }
     // tiles above the diagonal that pair with a diagonal tile in a 32-wide K step stay zero
-    for (int e = tid; e < 64 * 4; e += 256) {
-        sm.mb[(1 * 4 + 0) * 256 + e] = static_cast<bf16>(0.0f);
-        sm.mb[(3 * 4 + 2) * 256 + e] = static_cast<bf16>(0.0f);
+    for (int e = tid; e < HPW * 256; e += 256) {
+        const int hh = e >> 8, q = e & 255;
+        sm.mb[(hh * 16 + 1 * 4 + 0) * 256 + q] = static_cast<bf16>(0.0f);
+        sm.mb[(hh * 16 + 3 * 4 + 2) * 256 + q] = static_cast<bf16>(0.0f);
     }
 
-    ScanPrefetch<N> pf;
-    scan_load<N>(pf, x, dt, B, C, b, L, H, G, h, g, t0, tid);
+    ChunkAddr<N, HPW> ad;
+    chunk_addr<N, HPW>(ad, b, L, H, G, h0, g, c, nC, Q, tid);
+    ChunkRegs<N, HPW, true> rg;
+    chunk_load<N, HPW, true>(rg, ad, x, dt_t, cs, B, C, t0, 0, L, H, G, tid);
 
     for (int sc = 0; sc < nsub; ++sc) {
         const int64_t tbase = t0 + (int64_t)sc * QS;
-        __syncthreads();  // previous chunk's readers are done with the LDS tiles
-        scan_store<N>(sm, pf, a_log2, tid);
+        __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
+        chunk_store<N, HPW, true>(sm.xs, sm.bs, sm.cs, sm.lw, sm.dtw, sm.ww, sm.alpha, rg, ad, cs_prev, tid);
         __syncthreads();
-        if (sc + 1 < nsub) scan_load<N>(pf, x, dt, B, C, b, L, H, G, h, g, tbase + QS, tid);
+        if (sc + 1 < nsub) chunk_load<N, HPW, true>(rg, ad, x, dt_t, cs, B, C, tbase + QS, sc + 1, L, H, G, tid);
 
-        // ---- phase 1: decayed, masked C.B^T tiles -> LDS (fragment order) ------------------
+        // ---- phase 1: C.B^T tiles, decayed per head -> LDS in fragment order ----------------
         for (int tt = w; tt < 10; tt += 4) {
             const int jt = kTileJ[tt], it = kTileI[tt];
             f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NK; ++ks) {
                 Frag<bf16> a, bo;
-                frag_load8<bf16>(a, &sm.bn[(16 * jt + l16) * (N + 8) + 32 * ks + 8 * g4]);
-                frag_load8<bf16>(bo, &sm.cn[(16 * it + l16) * (N + 8) + 32 * ks + 8 * g4]);
+                frag_load8<bf16>(a, &sm.bs[(16 * jt + l16) * BS + 32 * ks + 8 * g4]);
+                frag_load8<bf16>(bo, &sm.cs[(16 * it + l16) * CS + 32 * ks + 8 * g4]);
                 mma(gacc, a, bo);
             }
             const int i = 16 * it + l16;
-            const float li = sm.lw[i];
-            f32x4 m;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * jt + 4 * g4 + r;
-                m[r] = j <= i ? gacc[r] * fast_exp2(li - sm.lw[j]) * sm.dtw[j] : 0.0f;
+            for (int hh = 0; hh < HPW; ++hh) {
+                const float li = sm.lw[hh * QS + i];
+                f32x4 m;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * jt + 4 * g4 + r;
+                    m[r] = j <= i ? gacc[r] * fast_exp2(li - sm.lw[hh * QS + j]) * sm.dtw[hh * QS + j] : 0.0f;
+                }
+                *reinterpret_cast<bf16x4*>(&sm.mb[((hh * 16 + jt * 4 + it) * 64 + lane) * 4]) = cvt4(m);
             }
-            *reinterpret_cast<bf16x4*>(&sm.mb[((jt * 4 + it) * 64 + lane) * 4]) = cvt4(m);
         }
         __syncthreads();
 
-        // ---- phase 2: Y^T[p-tile w] = 2^l_i (S C^T) + X^T M + D x ---------------------------
-        bf16x8 sa[NK];
+        // ---- phase 2: Y^T[p-tile w] = 2^l_i (S C^T) + X^T M + D x ------------------------------
+        bf16x8 sa[HPW][NK];
 #pragma unroll
-        for (int ks = 0; ks < NK; ++ks) sa[ks] = pack8(cvt4(st[2 * ks]), cvt4(st[2 * ks + 1]));
-        const bf16* xrow = &sm.xt[(16 * w + l16) * XROW];
+        for (int hh = 0; hh < HPW; ++hh) {
+#pragma unroll
+            for (int ks = 0; ks < NK; ++ks) sa[hh][ks] = pack8(cvt4(st[hh][2 * ks]), cvt4(st[hh][2 * ks + 1]));
+        }
+        const bool full = tbase + QS <= L;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int i = 16 * it + l16;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const bf16* crow = &sm.cn[i * (N + 8)];
+            f32x4 acc[HPW];
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh) acc[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const bf16* crow = &sm.cs[i * CS];
 #pragma unroll
             for (int ks = 0; ks < NK; ++ks) {
-                Frag<bf16> a, bo;
-                a.v = sa[ks];
+                Frag<bf16> bo;
                 bo.v = pack8(*reinterpret_cast<const bf16x4*>(crow + 32 * ks + 4 * g4),
                              *reinterpret_cast<const bf16x4*>(crow + 32 * ks + 16 + 4 * g4));
-                mma(acc, a, bo);
-            }
-            const float sc_i = fast_exp2(sm.lw[i]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= sc_i;
+                for (int hh = 0; hh < HPW; ++hh) {
+                    Frag<bf16> a;
+                    a.v = sa[hh][ks];
+                    mma(acc[hh], a, bo);
+                }
+            }
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh) {
+                const float sc_i = fast_exp2(sm.lw[hh * QS + i]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[hh][r] *= sc_i;
+            }
 #pragma unroll
             for (int js = 0; js <= it / 2; ++js) {
-                Frag<bf16> a, bo;
-                a.v = pack8(*reinterpret_cast<const bf16x4*>(xrow + 32 * js + 4 * g4),
-                            *reinterpret_cast<const bf16x4*>(xrow + 32 * js + 16 + 4 * g4));
-                bo.v = pack8(*reinterpret_cast<const bf16x4*>(&sm.mb[(((2 * js) * 4 + it) * 64 + lane) * 4]),
-                             *reinterpret_cast<const bf16x4*>(&sm.mb[(((2 * js + 1) * 4 + it) * 64 + lane) * 4]));
-                mma(acc, a, bo);
-            }
-            const int64_t t = tbase + i;
-            if (t < L) {
-                bf16x4 o;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int p = 16 * w + 4 * g4 + r;
-                    o[r] = static_cast<bf16>(acc[r] + Dh * static_cast<float>(sm.xt[p * XROW + i]));
+                for (int hh = 0; hh < HPW; ++hh) {
+                    const bf16* xt = &sm.xs[hh * QS * XS];
+                    Frag<bf16> a, bo;
+                    a.v = pack8(tr_read(xt, 32 * js + 4 * g4, 16 * w, XS, l16),
+                                tr_read(xt, 32 * js + 16 + 4 * g4, 16 * w, XS, l16));
+                    const bf16* mt = &sm.mb[hh * 16 * 256];
+                    bo.v = pack8(*reinterpret_cast<const bf16x4*>(&mt[(((2 * js) * 4 + it) * 64 + lane) * 4]),
+                                 *reinterpret_cast<const bf16x4*>(&mt[(((2 * js + 1) * 4 + it) * 64 + lane) * 4]));
+                    mma(acc[hh], a, bo);
                 }
-                *reinterpret_cast<bf16x4*>(y + ((b * L + t) * H + h) * P + 16 * w + 4 * g4) = o;
+            }
+            if (full || tbase + i < L) {
+#pragma unroll
+                for (int hh = 0; hh < HPW; ++hh) {
+                    const bf16x4 xv =
+                        *reinterpret_cast<const bf16x4*>(&sm.xs[hh * QS * XS + i * XS + 16 * w + 4 * g4]);
+                    bf16x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        o[r] = static_cast<bf16>(acc[hh][r] + Dh[hh] * static_cast<float>(xv[r]));
+                    *reinterpret_cast<bf16x4*>(y + ((b * L + tbase + i) * H + h0 + hh) * P + 16 * w + 4 * g4) = o;
+                }
             }
         }
 
-        // ---- phase 3: S <- 2^(l_63) S + B^T (w x) ----------------------------------------------
-        const float alpha = sm.alpha[0];
+        // ---- phase 3: S <- 2^(l_63) S + B^T (w x) ---------------------------------------------
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int hh = 0; hh < HPW; ++hh) {
+            const float alpha = sm.alpha[hh];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) st[nt][r] *= alpha;
+            for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[hh][nt][r] *= alpha;
+            }
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 xv = *reinterpret_cast<const bf16x8*>(xrow + 32 * ks + 8 * g4);
-            Frag<bf16> xw;
+            // token slots of this K step: 32ks + 4g4 + r (slots 0..3) and 32ks + 16 + 4g4 + r (slots 4..7)
+            Frag<bf16> xw[HPW];
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                xw.v[q] = static_cast<bf16>(static_cast<float>(xv[q]) * sm.ww[32 * ks + 8 * g4 + q]);
+            for (int hh = 0; hh < HPW; ++hh) {
+                const bf16* xt = &sm.xs[hh * QS * XS];
+                const bf16x4 lo4 = tr_read(xt, 32 * ks + 4 * g4, 16 * w, XS, l16);
+                const bf16x4 hi4 = tr_read(xt, 32 * ks + 16 + 4 * g4, 16 * w, XS, l16);
+                const float* wv = &sm.ww[hh * QS + 32 * ks + 4 * g4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    xw[hh].v[r] = static_cast<bf16>(static_cast<float>(lo4[r]) * wv[r]);
+                    xw[hh].v[4 + r] = static_cast<bf16>(static_cast<float>(hi4[r]) * wv[16 + r]);
+                }
+            }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 Frag<bf16> a;
-                frag_load8<bf16>(a, &sm.bt[(16 * nt + l16) * XROW + 32 * ks + 8 * g4]);
-                mma(st[nt], a, xw);
+                a.v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * nt, BS, l16),
+                            tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * nt, BS, l16));
+#pragma unroll
+                for (int hh = 0; hh < HPW; ++hh) mma(st[hh][nt], a, xw[hh]);
             }
         }
     }
@@ -301,191 +403,177 @@ fused_scan_kernel(const bf16* __restrict__ x, const bf16* __restrict__ dt, const
 // ---------------------------------------------------------------------------
 // segment-state kernel: the state each segment produces from zero (hi/lo)
 // ---------------------------------------------------------------------------
-template <int N>
+template <int N, int HPW>
 struct AggLds {
-    bf16 xt[P * AROW];   // X^T [p][j]
-    bf16 bt[N * AROW];   // B^T [n][j]
-    float ww[QA];
+    bf16 xs[HPW * QS * XS];
+    bf16 bs[QS * Strides<N>::BS];
+    float lw[HPW * QS];
+    float dtw[HPW * QS];
+    float ww[HPW * QS];
     float alpha[4];
 };
 
-template <int N>
+template <int N, int HPW>
 __global__ void __launch_bounds__(256, 2)
-segment_state_kernel(const bf16* __restrict__ x, const bf16* __restrict__ dt, const float* __restrict__ A,
-                     const bf16* __restrict__ B, float* __restrict__ agg, float* __restrict__ lam, int64_t L, int H,
-                     int G, int seg_len, int nSeg, uint32_t nitems) {
+chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, const float* __restrict__ dt_t,
+                        const float* __restrict__ cs, float* __restrict__ states, int64_t L, int H, int G, int Q,
+                        int64_t nC, uint32_t nitems) {
     constexpr int NT = N / 16;
+    constexpr int BS = Strides<N>::BS;
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    AggLds<N>& sm = *reinterpret_cast<AggLds<N>*>(smem_raw);
+    AggLds<N, HPW>& sm = *reinterpret_cast<AggLds<N, HPW>*>(smem_raw);
 
+    const int HP = H / HPW;
     const uint32_t item = xcd_remap(blockIdx.x, nitems);
-    const int h = (int)(item % (uint32_t)H);
-    const int s = (int)((item / (uint32_t)H) % (uint32_t)nSeg);
-    const int64_t b = item / ((uint32_t)H * (uint32_t)nSeg);
-    const int g = h / (H / G);
+    const int hp = (int)(item % (uint32_t)HP);
+    const int64_t c = (item / (uint32_t)HP) % (uint32_t)nC;
+    const int64_t b = item / ((uint32_t)HP * (uint32_t)nC);
+    const int h0 = hp * HPW;
+    const int g = h0 / (H / G);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
-    const float a_log2 = A[h] * kLog2e;
-    const int64_t t0 = (int64_t)s * seg_len;
-    const int64_t t_end = t0 + seg_len < L ? t0 + seg_len : L;
-    const int nsub = (int)((t_end - t0 + QA - 1) / QA);
-    const uint4 z = make_uint4(0, 0, 0, 0);
+    const int64_t t0 = c * Q;
+    const int64_t t_end = t0 + Q < L ? t0 + Q : L;
+    const int nsub = (int)((t_end - t0 + QS - 1) / QS);
+    float cs_prev = 0.0f;
 
-    f32x4 st[NT];
+    f32x4 st[HPW][NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) st[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float lam_sum = 0.0f;
+    for (int hh = 0; hh < HPW; ++hh) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st[hh][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    ChunkAddr<N, HPW> ad;
+    chunk_addr<N, HPW>(ad, b, L, H, G, h0, g, c, nC, Q, tid);
+    ChunkRegs<N, HPW, false> rg;
+    chunk_load<N, HPW, false>(rg, ad, x, dt_t, cs, B, nullptr, t0, 0, L, H, G, tid);
 
     for (int sc = 0; sc < nsub; ++sc) {
-        const int64_t tbase = t0 + (int64_t)sc * QA;
+        const int64_t tbase = t0 + (int64_t)sc * QS;
         __syncthreads();
-        // x^T: 16 x 8 blocks of 8x8 (threads 0..127); B^T: 16 x N/8 blocks
-        for (int blk = tid; blk < 16 * 8 + 16 * (N / 8); blk += 256) {
-            uint4 v[8], tr[8];
-            if (blk < 128) {
-                const int rb = blk & 15, cb = blk >> 4;
+        chunk_store<N, HPW, false>(sm.xs, sm.bs, nullptr, sm.lw, sm.dtw, sm.ww, sm.alpha, rg, ad, cs_prev, tid);
+        __syncthreads();
+        if (sc + 1 < nsub) chunk_load<N, HPW, false>(rg, ad, x, dt_t, cs, B, nullptr, tbase + QS, sc + 1, L, H, G, tid);
+
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int64_t t = tbase + 8 * rb + r;
-                    v[r] = t < L ? *reinterpret_cast<const uint4*>(x + ((b * L + t) * H + h) * P + 8 * cb) : z;
-                }
-                transpose8(v, tr);
+        for (int hh = 0; hh < HPW; ++hh) {
+            const float alpha = sm.alpha[hh];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(&sm.xt[(8 * cb + c) * AROW + 8 * rb]) = tr[c];
-            } else {
-                const int k = blk - 128, rb = k & 15, cb = k >> 4;
+            for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int64_t t = tbase + 8 * rb + r;
-                    v[r] = t < L ? *reinterpret_cast<const uint4*>(B + ((b * L + t) * G + g) * N + 8 * cb) : z;
-                }
-                transpose8(v, tr);
-#pragma unroll
-                for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(&sm.bt[(8 * cb + c) * AROW + 8 * rb]) = tr[c];
+                for (int r = 0; r < 4; ++r) st[hh][nt][r] *= alpha;
             }
         }
-        if (w == 0) {
-            // two consecutive tokens per lane
-            float d0 = 0.f, d1 = 0.f;
-            const int64_t ta = tbase + 2 * lane;
-            if (ta < L) d0 = to_f32(dt[(b * L + ta) * H + h]);
-            if (ta + 1 < L) d1 = to_f32(dt[(b * L + ta + 1) * H + h]);
-            const float v0 = d0 * a_log2, v1 = v0 + d1 * a_log2;
-            float incl = v1;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float up = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += up;
-            }
-            float excl = __shfl_up(incl, 1, 64);
-            if (lane == 0) excl = 0.0f;
-            const float last = __shfl(incl, 63, 64);
-            sm.ww[2 * lane] = fast_exp2(last - (excl + v0)) * d0;
-            sm.ww[2 * lane + 1] = fast_exp2(last - incl) * d1;
-            if (lane == 0) sm.alpha[0] = fast_exp2(last);
-            lam_sum += last;
-        }
-        __syncthreads();
-        const float alpha = sm.alpha[0];
+        for (int ks = 0; ks < 2; ++ks) {
+            Frag<bf16> xh[HPW], xl[HPW];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+            for (int hh = 0; hh < HPW; ++hh) {
+                const bf16* xt = &sm.xs[hh * QS * XS];
+                const bf16x4 lo4 = tr_read(xt, 32 * ks + 4 * g4, 16 * w, XS, l16);
+                const bf16x4 hi4 = tr_read(xt, 32 * ks + 16 + 4 * g4, 16 * w, XS, l16);
+                const float* wv = &sm.ww[hh * QS + 32 * ks + 4 * g4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) st[nt][r] *= alpha;
-        }
-        const bf16* xrow = &sm.xt[(16 * w + l16) * AROW];
-#pragma unroll
-        for (int ks = 0; ks < QA / 32; ++ks) {
-            const bf16x8 xv = *reinterpret_cast<const bf16x8*>(xrow + 32 * ks + 8 * g4);
-            Frag<bf16> hi, lo;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float v = static_cast<float>(xv[q]) * sm.ww[32 * ks + 8 * g4 + q];
-                const bf16 vh = static_cast<bf16>(v);
-                hi.v[q] = vh;
-                lo.v[q] = static_cast<bf16>(v - static_cast<float>(vh));
+                for (int r = 0; r < 4; ++r) {
+                    const float v0 = static_cast<float>(lo4[r]) * wv[r];
+                    const float v1 = static_cast<float>(hi4[r]) * wv[16 + r];
+                    const bf16 h0v = static_cast<bf16>(v0), h1v = static_cast<bf16>(v1);
+                    xh[hh].v[r] = h0v;
+                    xh[hh].v[4 + r] = h1v;
+                    xl[hh].v[r] = static_cast<bf16>(v0 - static_cast<float>(h0v));
+                    xl[hh].v[4 + r] = static_cast<bf16>(v1 - static_cast<float>(h1v));
+                }
             }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 Frag<bf16> a;
-                frag_load8<bf16>(a, &sm.bt[(16 * nt + l16) * AROW + 32 * ks + 8 * g4]);
-                mma(st[nt], a, hi);
-                mma(st[nt], a, lo);
+                a.v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * nt, BS, l16),
+                            tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * nt, BS, l16));
+#pragma unroll
+                for (int hh = 0; hh < HPW; ++hh) {
+                    mma(st[hh][nt], a, xh[hh]);
+                    mma(st[hh][nt], a, xl[hh]);
+                }
             }
         }
     }
-    // S[p][n]: lane holds p = 16w + l16, n = 16nt + 4g4 + r
-    float* out = agg + ((b * nSeg + s) * H + h) * (int64_t)P * N + (int64_t)(16 * w + l16) * N;
+    // a ragged last chunk ends at position Q-1 all the same: its padded tokens have dt = 0 and decay 1
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(out + 16 * nt + 4 * g4) = st[nt];
-    if (tid == 0) lam[(b * H + h) * nSeg + s] = lam_sum;
+    for (int hh = 0; hh < HPW; ++hh) {
+        float* out = states + ((b * nC + c) * H + h0 + hh) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 4 * g4;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(out + 16 * nt) = st[hh][nt];
+    }
 }
 
-template <int N>
-hipError_t launch_fused_n(const Shape& s, int seg_len, const void* x, const void* dt, const float* A, const void* B,
-                          const void* C, const float* D, const float* h0, void* y, float* final_state, float* agg,
-                          float* lam, hipStream_t st) {
-    const int nSeg = (int)((s.L + seg_len - 1) / seg_len);
-    const uint32_t nitems = (uint32_t)(s.b * nSeg * s.H);
-    hipError_t e;
-    if (nitems > 0) {
-        const size_t lds_a = sizeof(AggLds<N>);
-        e = hipFuncSetAttribute((const void*)segment_state_kernel<N>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds_a);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(segment_state_kernel<N>, dim3(nitems), dim3(256), lds_a, st, (const bf16*)x,
-                           (const bf16*)dt, A, (const bf16*)B, agg, lam, s.L, (int)s.H, (int)s.G, seg_len, nSeg,
-                           nitems);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    // segment-order pass: decay of segment k is 2^(lam[b,h,k]) (one value per "chunk")
-    Shape sp = s;
-    sp.nC = nSeg;
-    sp.Q = 1;
-    e = launch_state_passing(sp, agg, lam, h0, final_state, st);
+template <int N, int HPW>
+hipError_t launch_state_fast(const Shape& s, const bf16* x, const bf16* B, const float* dt_t, const float* cs,
+                             float* states, hipStream_t st) {
+    const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
+    if (nitems == 0) return hipSuccess;
+    const size_t lds = sizeof(AggLds<N, HPW>);
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_fast_kernel<N, HPW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    if (nitems > 0) {
-        const size_t lds_c = sizeof(ScanLds<N>);
-        e = hipFuncSetAttribute((const void*)fused_scan_kernel<N>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds_c);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(fused_scan_kernel<N>, dim3(nitems), dim3(256), lds_c, st, (const bf16*)x, (const bf16*)dt,
-                           A, (const bf16*)B, (const bf16*)C, D, agg, (bf16*)y, s.L, (int)s.H, (int)s.G, seg_len,
-                           nSeg, nitems);
-        e = hipGetLastError();
-    }
-    return e;
+    hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW>), dim3(nitems), dim3(256), lds, st, x, B, dt_t, cs, states,
+                       s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+    return hipGetLastError();
+}
+
+template <int N, int HPW>
+hipError_t launch_scan_fast(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const float* dt_t,
+                            const float* cs, const float* start, const float* D, bf16* y, hipStream_t st) {
+    const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
+    if (nitems == 0) return hipSuccess;
+    const size_t lds = sizeof(ScanLds<N, HPW>);
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_scan_fast_kernel<N, HPW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW>), dim3(nitems), dim3(256), lds, st, x, B, C, dt_t, cs, start,
+                       D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+    return hipGetLastError();
 }
 
 }  // namespace fz
 
-bool fused_supported(const Shape& s) { return s.io == 1 && s.P == 64 && (s.N == 64 || s.N == 128); }
-
-int fused_segment_len(const Shape& s) {
-    // enough (b, segment, head) items to fill 256 CUs a few times over; segments are whole chunks
-    const int64_t tokens_heads = s.b * s.L * s.H;
-    int64_t seg = 4096;
-    while (seg > 256 && tokens_heads / seg < 2048) seg /= 2;
-    return (int)seg;
+bool fast_chunk_supported(const Shape& s) {
+    return s.io == 1 && s.P == 64 && (s.N == 64 || s.N == 128) && s.Q % 64 == 0;
 }
 
-size_t fused_workspace_bytes(const Shape& s) {
-    const int64_t nSeg = (s.L + fused_segment_len(s) - 1) / fused_segment_len(s);
-    const size_t agg = (size_t)(s.b * nSeg * s.H * s.P * s.N) * 4;
-    const size_t lam = (size_t)(s.b * s.H * nSeg) * 4;
-    return (agg + 255) / 256 * 256 + (lam + 255) / 256 * 256;
+// heads per workgroup: two when both heads of every pair read the same group
+static int fast_hpw(const Shape& s) { return (s.H / s.G) % 2 == 0 ? 2 : 1; }
+
+int fast_heads_per_wg(const Shape& s) { return fast_hpw(s); }
+
+int fast_forward_chunk(const Shape& s) {
+    // the largest chunk (<= 4096 tokens) that still gives enough (b, chunk, head-pair) work items
+    const int64_t items_per_token = s.b * s.H / fast_hpw(s);
+    int64_t q = 4096;
+    while (q > 256 && items_per_token * s.L / q < 1024) q /= 2;
+    return (int)q;
 }
 
-hipError_t launch_fused_forward(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
-                                const void* C, const float* D, const float* h0, void* y, float* final_state,
-                                void* workspace, hipStream_t st) {
-    const int seg_len = fused_segment_len(s);
-    const int64_t nSeg = (s.L + seg_len - 1) / seg_len;
-    const size_t agg_bytes = (size_t)(s.b * nSeg * s.H * s.P * s.N) * 4;
-    float* agg = static_cast<float*>(workspace);
-    float* lam = reinterpret_cast<float*>(static_cast<char*>(workspace) + (agg_bytes + 255) / 256 * 256);
+hipError_t launch_chunk_state_fast(const Shape& s, const void* x, const void* B, const float* dt_t, const float* cs,
+                                   float* states, hipStream_t st) {
+    const bf16 *xb = (const bf16*)x, *bb = (const bf16*)B;
+    const bool pair = fast_hpw(s) == 2;
     if (s.N == 128)
-        return fz::launch_fused_n<128>(s, seg_len, x, dt, A, B, C, D, h0, y, final_state, agg, lam, st);
-    return fz::launch_fused_n<64>(s, seg_len, x, dt, A, B, C, D, h0, y, final_state, agg, lam, st);
+        return pair ? fz::launch_state_fast<128, 2>(s, xb, bb, dt_t, cs, states, st)
+                    : fz::launch_state_fast<128, 1>(s, xb, bb, dt_t, cs, states, st);
+    return pair ? fz::launch_state_fast<64, 2>(s, xb, bb, dt_t, cs, states, st)
+                : fz::launch_state_fast<64, 1>(s, xb, bb, dt_t, cs, states, st);
+}
+
+hipError_t launch_chunk_scan_fast(const Shape& s, const void* x, const void* B, const void* C, const float* dt_t,
+                                  const float* cs, const float* start, const float* D, void* y, hipStream_t st) {
+    const bf16 *xb = (const bf16*)x, *bb = (const bf16*)B, *cb = (const bf16*)C;
+    bf16* yb = (bf16*)y;
+    const bool pair = fast_hpw(s) == 2;
+    if (s.N == 128)
+        return pair ? fz::launch_scan_fast<128, 2>(s, xb, bb, cb, dt_t, cs, start, D, yb, st)
+                    : fz::launch_scan_fast<128, 1>(s, xb, bb, cb, dt_t, cs, start, D, yb, st);
+    return pair ? fz::launch_scan_fast<64, 2>(s, xb, bb, cb, dt_t, cs, start, D, yb, st)
+                : fz::launch_scan_fast<64, 1>(s, xb, bb, cb, dt_t, cs, start, D, yb, st);
 }
 
 }  // namespace ssd

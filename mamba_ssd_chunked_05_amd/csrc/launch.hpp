@@ -23,13 +23,14 @@ hipError_t launch_chunk_scan(const Shape& s, const void* x, const void* B, const
 hipError_t launch_step(const Shape& s, float* state, const void* x, const void* dt, const float* A,
                        const void* B, const void* C, const float* D, void* y, hipStream_t st);
 
-// Fused forward (bf16, headdim 64, dstate 64 or 128): segment states, segment pass, fused output.
-bool fused_supported(const Shape& s);
-int fused_segment_len(const Shape& s);
-size_t fused_workspace_bytes(const Shape& s);
-hipError_t launch_fused_forward(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
-                                const void* C, const float* D, const float* h0, void* y, float* final_state,
-                                void* workspace, hipStream_t st);
+// Fast chunk-state / chunk-scan kernels (bf16, headdim 64, dstate 64 or 128, chunk a multiple of 64).
+bool fast_chunk_supported(const Shape& s);
+int fast_forward_chunk(const Shape& s);   // chunk size the forward uses on the fast path
+int fast_heads_per_wg(const Shape& s);
+hipError_t launch_chunk_state_fast(const Shape& s, const void* x, const void* B, const float* dt_t, const float* cs,
+                                   float* states, hipStream_t st);
+hipError_t launch_chunk_scan_fast(const Shape& s, const void* x, const void* B, const void* C, const float* dt_t,
+                                  const float* cs, const float* start, const float* D, void* y, hipStream_t st);
 
 // LDS bytes the generic chunk kernels need; used by validation.
 size_t chunk_state_lds_bytes(const Shape& s);

@@ -72,7 +72,9 @@ def _forward(d, ws_bytes=1 << 40, **over):
     (_d(N=20), UNSUP),
     (_d(N=2048), UNSUP),
     (_d(Q=100), UNSUP),
-    (_d(Q=1024), UNSUP),
+    (_d(Q=8192), UNSUP),
+    (_d(Q=1024, N=256), UNSUP),
+    (_d(Q=1024, io=0), UNSUP),
     (_d(Q=-16), SHAPE),
 ])
 def test_forward_rejects_bad_dims(dims, code):
@@ -136,7 +138,7 @@ def test_workspace_and_config_are_host_only():
     d = _d(b=1, L=65536, H=80, P=64, N=128, Q=0)
     assert lib.ssd_forward_workspace_bytes(ctypes.byref(d)) > 0
     cfg = ssd.query_config(1, 65536, 80, 64, 128)
-    assert cfg["chunk"] in (64, 128, 256, 512)
+    assert cfg["chunk"] % 64 == 0 and 256 <= cfg["chunk"] <= 4096 and cfg["chunks_per_segment"] == cfg["chunk"] // 64
     with pytest.raises(ValueError):
         ssd.query_config(1, 64, 4, 24, 128)
 

@@ -27,6 +27,11 @@ CASES = [
     (1, 70, 1, 256, 64, 1, 16, "bf16"),
     (1, 200, 2, 16, 1024, 1, 48, "f32"),
     (1, 512, 2, 64, 32, 2, 512, "bf16"),
+    # fast chunk kernels (bf16, P = 64, N in {64, 128}, Q a multiple of 64, up to 4096)
+    (1, 3000, 4, 64, 128, 1, 1024, "bf16"),
+    (2, 1100, 6, 64, 64, 3, 512, "bf16"),
+    (1, 700, 3, 64, 128, 1, 192, "bf16"),
+    (1, 5000, 2, 64, 64, 1, 4096, "bf16"),
 ]
 
 
