@@ -154,6 +154,11 @@ struct FwdLayout {
 FwdLayout fwd_layout(const ssd::Shape& s) {
     Sizes z = sizes(s);
     FwdLayout f;
+    if (ssd::fast_chunk_supported(s)) {  // the fast forward keeps no per-position arrays
+        f.dt_t = f.cs = f.states = 0;
+        f.total = ssd::fast_forward_layout(s).total;
+        return f;
+    }
     f.dt_t = 0;
     f.cs = align256(z.cs);
     f.states = f.cs + align256(z.cs);
@@ -322,6 +327,14 @@ ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, cons
         }
         hipStream_t st = (hipStream_t)stream;
         if (s.b == 0) return ok();
+        if (ssd::fast_chunk_supported(s)) {
+            if (s.L == 0) {  // no tokens: the final state is h0 (or zero)
+                hipError_t e = ssd::launch_state_passing(s, nullptr, nullptr, h0, final_state, st);
+                return e == hipSuccess ? ok() : hip_fail(e, "ssd_forward/state_passing");
+            }
+            hipError_t e = ssd::launch_forward_fast(s, x, dt, A, B, C, D, h0, y, final_state, workspace, st);
+            return e == hipSuccess ? ok() : hip_fail(e, "ssd_forward (fast path)");
+        }
         char* ws = static_cast<char*>(workspace);
         float* dt_t = reinterpret_cast<float*>(ws + f.dt_t);
         float* cs = reinterpret_cast<float*>(ws + f.cs);

@@ -105,7 +105,7 @@ struct BRows {
     static constexpr int RPI = 256 / (N / 8);  // B rows covered by one pass of 256 threads
 };
 
-template <int N, int HPW>
+template <int N, int HPW, bool FWD>
 __device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int64_t b, int64_t L, int H, int G, int h0, int g,
                                            int64_t c, int64_t nC, int Q, int tid) {
     constexpr int BS = Strides<N>::BS, CS = Strides<N>::CS;
@@ -119,20 +119,32 @@ __device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int64_t b, int6
     a.bl = br * BS + bc;
     a.cl = br * CS + bc;
     const int hh = tid >> 6, r = tid & 63;
-    a.dto = ((b * H + h0 + (hh < HPW ? hh : 0)) * nC + c) * Q + r;
+    const int hd = h0 + (hh < HPW ? hh : 0);
+    if (FWD) {  // sub-chunk-local arrays (b, H, ceil(L/64), 64): position r of the chunk's first sub-chunk
+        const int64_t nsubT = (L + QS - 1) / QS;
+        a.dto = ((b * H + hd) * nsubT + c * (Q / QS)) * QS + r;
+    } else {    // chunk arrays (b, H, nC, Q): position r of the chunk
+        a.dto = ((b * H + hd) * nC + c) * Q + r;
+    }
 }
+
+// dt (fp32) and the cumulative log2 decay: over the chunk for the staged calls,
+// restarting at every 64-token sub-chunk in the forward.
+struct DtSrc {
+    const float* dt_t;
+    const float* cs;
+};
 
 // Load the chunk starting at token tbase into registers (rows past L read as zero).
 template <int N, int HPW, bool WITH_C>
 __device__ __forceinline__ void chunk_load(ChunkRegs<N, HPW, WITH_C>& rg, const ChunkAddr<N, HPW>& a,
-                                           const bf16* __restrict__ x, const float* __restrict__ dt_t,
-                                           const float* __restrict__ cs, const bf16* __restrict__ B,
+                                           const bf16* __restrict__ x, const DtSrc& ds, const bf16* __restrict__ B,
                                            const bf16* __restrict__ C, int64_t tbase, int sub, int64_t L, int H,
                                            int G, int tid) {
     constexpr int RPI = BRows<N>::RPI;
     if (tid < 64 * HPW) {  // dt_t and cs cover every position of the chunk (zero-padded past L)
-        rg.dt = dt_t[a.dto + QS * sub];
-        rg.cs = cs[a.dto + QS * sub];
+        rg.dt = ds.dt_t[a.dto + QS * sub];
+        rg.cs = ds.cs[a.dto + QS * sub];
     }
     const int64_t HP_ = (int64_t)H * P, GN = (int64_t)G * N;
     const bf16* xb = x + a.xo + tbase * HP_;
@@ -176,10 +188,12 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<N, HPW, WITH_C>& rg, const 
 // registers -> LDS, and the in-chunk cumulative decay (one wavefront per head)
 // cs_prev: the chunk cumulative decay before this sub-chunk (0 for the first),
 // held by wavefront hh for head hh and advanced here.
-template <int N, int HPW, bool WITH_C>
+// With FWD the decay arrays already restart at the sub-chunk.  tot accumulates
+// the sub-chunk totals (the chunk's total decay).
+template <int N, int HPW, bool WITH_C, bool FWD>
 __device__ __forceinline__ void chunk_store(bf16* xs, bf16* bsm, bf16* csm, float* lw, float* dtw, float* ww,
                                             float* alpha, const ChunkRegs<N, HPW, WITH_C>& rg,
-                                            const ChunkAddr<N, HPW>& a, float& cs_prev, int tid) {
+                                            const ChunkAddr<N, HPW>& a, float& cs_prev, float& tot, int tid) {
     constexpr int RPI = BRows<N>::RPI, BS = Strides<N>::BS, CS = Strides<N>::CS;
 #pragma unroll
     for (int k = 0; k < 2 * HPW; ++k)
@@ -192,9 +206,15 @@ __device__ __forceinline__ void chunk_store(bf16* xs, bf16* bsm, bf16* csm, floa
     if (tid < 64 * HPW) {
         const int hh = tid >> 6, lane = tid & 63;
         const float d = rg.dt;
-        const float incl = rg.cs - cs_prev;  // cumulative log2 decay inside the sub-chunk
+        float incl;  // cumulative log2 decay inside the sub-chunk
+        if (FWD) {
+            incl = rg.cs;
+        } else {
+            incl = rg.cs - cs_prev;
+            cs_prev = __shfl(rg.cs, 63, 64);
+        }
         const float last = __shfl(incl, 63, 64);
-        cs_prev = __shfl(rg.cs, 63, 64);
+        tot += last;
         lw[hh * QS + lane] = incl;
         dtw[hh * QS + lane] = d;
         ww[hh * QS + lane] = fast_exp2(last - incl) * d;
@@ -220,11 +240,11 @@ struct ScanLds {
 __constant__ int8_t kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 __constant__ int8_t kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 
-template <int N, int HPW>
+// FWD: the forward's variant, reading sub-chunk-local decay arrays (subchunk_decay_kernel).
+template <int N, int HPW, bool FWD>
 __global__ void __launch_bounds__(256, 2)
 chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, const bf16* __restrict__ C,
-                       const float* __restrict__ dt_t, const float* __restrict__ cs,
-                       const float* __restrict__ start, const float* __restrict__ D, bf16* __restrict__ y, int64_t L,
+                       DtSrc ds, const float* __restrict__ start, const float* __restrict__ D, bf16* __restrict__ y, int64_t L,
                        int H, int G, int Q, int64_t nC, uint32_t nitems) {
     constexpr int NT = N / 16, NK = N / 32;
     constexpr int BS = Strides<N>::BS, CS = Strides<N>::CS;
@@ -245,7 +265,7 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     const int64_t t0 = c * Q;
     const int64_t t_end = t0 + Q < L ? t0 + Q : L;
     const int nsub = (int)((t_end - t0 + QS - 1) / QS);
-    float cs_prev = 0.0f;
+    float cs_prev = 0.0f, tot = 0.0f;
 
     // carried state per head, transposed: st[hh][nt] holds S[p = 16w + l16][n = 16nt + 4g4 + r]
     f32x4 st[HPW][NT];
@@ -264,16 +284,16 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     }
 
     ChunkAddr<N, HPW> ad;
-    chunk_addr<N, HPW>(ad, b, L, H, G, h0, g, c, nC, Q, tid);
+    chunk_addr<N, HPW, FWD>(ad, b, L, H, G, h0, g, c, nC, Q, tid);
     ChunkRegs<N, HPW, true> rg;
-    chunk_load<N, HPW, true>(rg, ad, x, dt_t, cs, B, C, t0, 0, L, H, G, tid);
+    chunk_load<N, HPW, true>(rg, ad, x, ds, B, C, t0, 0, L, H, G, tid);
 
     for (int sc = 0; sc < nsub; ++sc) {
         const int64_t tbase = t0 + (int64_t)sc * QS;
         __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
-        chunk_store<N, HPW, true>(sm.xs, sm.bs, sm.cs, sm.lw, sm.dtw, sm.ww, sm.alpha, rg, ad, cs_prev, tid);
+        chunk_store<N, HPW, true, FWD>(sm.xs, sm.bs, sm.cs, sm.lw, sm.dtw, sm.ww, sm.alpha, rg, ad, cs_prev, tot, tid);
         __syncthreads();
-        if (sc + 1 < nsub) chunk_load<N, HPW, true>(rg, ad, x, dt_t, cs, B, C, tbase + QS, sc + 1, L, H, G, tid);
+        if (sc + 1 < nsub) chunk_load<N, HPW, true>(rg, ad, x, ds, B, C, tbase + QS, sc + 1, L, H, G, tid);
 
         // ---- phase 1: C.B^T tiles, decayed per head -> LDS in fragment order ----------------
         for (int tt = w; tt < 10; tt += 4) {
@@ -413,10 +433,11 @@ struct AggLds {
     float alpha[4];
 };
 
-template <int N, int HPW>
+// FWD: the forward's variant -- reads sub-chunk-local decay arrays and also
+// writes each chunk's total log2 decay to totals (b, H, nC).
+template <int N, int HPW, bool FWD>
 __global__ void __launch_bounds__(256, 2)
-chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, const float* __restrict__ dt_t,
-                        const float* __restrict__ cs, float* __restrict__ states, int64_t L, int H, int G, int Q,
+chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, DtSrc ds, float* __restrict__ states, float* __restrict__ totals, int64_t L, int H, int G, int Q,
                         int64_t nC, uint32_t nitems) {
     constexpr int NT = N / 16;
     constexpr int BS = Strides<N>::BS;
@@ -434,7 +455,7 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     const int64_t t0 = c * Q;
     const int64_t t_end = t0 + Q < L ? t0 + Q : L;
     const int nsub = (int)((t_end - t0 + QS - 1) / QS);
-    float cs_prev = 0.0f;
+    float cs_prev = 0.0f, tot = 0.0f;
 
     f32x4 st[HPW][NT];
 #pragma unroll
@@ -444,16 +465,18 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     }
 
     ChunkAddr<N, HPW> ad;
-    chunk_addr<N, HPW>(ad, b, L, H, G, h0, g, c, nC, Q, tid);
+    chunk_addr<N, HPW, FWD>(ad, b, L, H, G, h0, g, c, nC, Q, tid);
     ChunkRegs<N, HPW, false> rg;
-    chunk_load<N, HPW, false>(rg, ad, x, dt_t, cs, B, nullptr, t0, 0, L, H, G, tid);
+    chunk_load<N, HPW, false>(rg, ad, x, ds, B, nullptr, t0, 0, L, H, G, tid);
 
     for (int sc = 0; sc < nsub; ++sc) {
         const int64_t tbase = t0 + (int64_t)sc * QS;
         __syncthreads();
-        chunk_store<N, HPW, false>(sm.xs, sm.bs, nullptr, sm.lw, sm.dtw, sm.ww, sm.alpha, rg, ad, cs_prev, tid);
+        chunk_store<N, HPW, false, FWD>(sm.xs, sm.bs, nullptr, sm.lw, sm.dtw, sm.ww, sm.alpha, rg, ad, cs_prev, tot,
+                                        tid);
         __syncthreads();
-        if (sc + 1 < nsub) chunk_load<N, HPW, false>(rg, ad, x, dt_t, cs, B, nullptr, tbase + QS, sc + 1, L, H, G, tid);
+        if (sc + 1 < nsub)
+            chunk_load<N, HPW, false>(rg, ad, x, ds, B, nullptr, tbase + QS, sc + 1, L, H, G, tid);
 
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
@@ -504,35 +527,98 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(out + 16 * nt) = st[hh][nt];
     }
+    if (FWD && tid < 64 * HPW && lane == 0) totals[(b * H + h0 + w) * nC + c] = tot;
 }
 
-template <int N, int HPW>
-hipError_t launch_state_fast(const Shape& s, const bf16* x, const bf16* B, const float* dt_t, const float* cs,
-                             float* states, hipStream_t st) {
+// ---------------------------------------------------------------------------
+// the forward's decay arrays: for every 64-token sub-chunk and head,
+//   dtl[b,h,s,i] = dt[b, 64s+i, h],   lw[b,h,s,i] = log2(e) sum_{k<=i} dt[b,64s+k,h] A[h]
+// (the in-chunk cumulative sum with the chunk length set to 64).  One workgroup
+// per (b, s): the (64 x H) block of dt is contiguous, read coalesced through LDS
+// in blocks of 64 heads; each wavefront then scans one head at a time.
+// ---------------------------------------------------------------------------
+constexpr int kDecayHB = 64;  // heads per LDS block
+
+__global__ void __launch_bounds__(256) subchunk_decay_kernel(const bf16* __restrict__ dt, const float* __restrict__ A,
+                                                             float* __restrict__ dtl, float* __restrict__ lw,
+                                                             int64_t L, int H, uint32_t nitems) {
+    __shared__ float blk[QS][kDecayHB + 1];
+    const int64_t nsubT = (L + QS - 1) / QS;
+    const uint32_t item = xcd_remap(blockIdx.x, nitems);
+    const int64_t sub = item % (uint64_t)nsubT;
+    const int64_t b = item / (uint64_t)nsubT;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int64_t t0 = sub * QS;
+    for (int hb = 0; hb < H; hb += kDecayHB) {
+        const int nh = H - hb < kDecayHB ? H - hb : kDecayHB;
+        __syncthreads();
+        constexpr int KL = QS * kDecayHB / 256;
+        bf16 v[KL];  // all loads in flight before the first use
+#pragma unroll
+        for (int k = 0; k < KL; ++k) {
+            const int e = tid + 256 * k, t = e / kDecayHB, hh = e % kDecayHB;
+            const bool ok = hh < nh && t0 + t < L;  // load a valid element regardless, then select
+            v[k] = dt[ok ? (b * L + t0 + t) * H + hb + hh : 0];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < KL; ++k) {
+            const int e = tid + 256 * k, t = e / kDecayHB, hh = e % kDecayHB;
+            const bool ok = hh < nh && t0 + t < L;
+            blk[t][hh] = ok ? to_f32(v[k]) : 0.0f;
+        }
+        __syncthreads();
+        for (int hh = w; hh < nh; hh += 4) {
+            const int h = hb + hh;
+            const float d = blk[lane][hh];
+            float incl = d * A[h];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float up = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += up;
+            }
+            const int64_t o = ((b * H + h) * nsubT + sub) * QS + lane;
+            dtl[o] = d;
+            lw[o] = incl * kLog2e;
+        }
+    }
+}
+
+template <int N, int HPW, bool FWD>
+hipError_t launch_state_fast(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
+                             float* totals, hipStream_t st) {
     const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
     if (nitems == 0) return hipSuccess;
     const size_t lds = sizeof(AggLds<N, HPW>);
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_fast_kernel<N, HPW>,
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_fast_kernel<N, HPW, FWD>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW>), dim3(nitems), dim3(256), lds, st, x, B, dt_t, cs, states,
-                       s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+    hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, ds, states,
+                       totals, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
     return hipGetLastError();
 }
 
-template <int N, int HPW>
-hipError_t launch_scan_fast(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const float* dt_t,
-                            const float* cs, const float* start, const float* D, bf16* y, hipStream_t st) {
+template <int N, int HPW, bool FWD>
+hipError_t launch_scan_fast(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
+                            const float* start, const float* D, bf16* y, hipStream_t st) {
     const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
     if (nitems == 0) return hipSuccess;
     const size_t lds = sizeof(ScanLds<N, HPW>);
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_scan_fast_kernel<N, HPW>,
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_scan_fast_kernel<N, HPW, FWD>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW>), dim3(nitems), dim3(256), lds, st, x, B, C, dt_t, cs, start,
+    hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, C, ds, start,
                        D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
     return hipGetLastError();
 }
+
+// dispatch over (N, heads per workgroup)
+template <bool FWD>
+hipError_t state_dispatch(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
+                          float* totals, hipStream_t st);
+template <bool FWD>
+hipError_t scan_dispatch(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
+                         const float* start, const float* D, bf16* y, hipStream_t st);
 
 }  // namespace fz
 
@@ -553,27 +639,80 @@ int fast_forward_chunk(const Shape& s) {
     return (int)q;
 }
 
-hipError_t launch_chunk_state_fast(const Shape& s, const void* x, const void* B, const float* dt_t, const float* cs,
-                                   float* states, hipStream_t st) {
-    const bf16 *xb = (const bf16*)x, *bb = (const bf16*)B;
+namespace fz {
+
+template <bool FWD>
+hipError_t state_dispatch(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
+                          float* totals, hipStream_t st) {
     const bool pair = fast_hpw(s) == 2;
     if (s.N == 128)
-        return pair ? fz::launch_state_fast<128, 2>(s, xb, bb, dt_t, cs, states, st)
-                    : fz::launch_state_fast<128, 1>(s, xb, bb, dt_t, cs, states, st);
-    return pair ? fz::launch_state_fast<64, 2>(s, xb, bb, dt_t, cs, states, st)
-                : fz::launch_state_fast<64, 1>(s, xb, bb, dt_t, cs, states, st);
+        return pair ? launch_state_fast<128, 2, FWD>(s, x, B, ds, states, totals, st)
+                    : launch_state_fast<128, 1, FWD>(s, x, B, ds, states, totals, st);
+    return pair ? launch_state_fast<64, 2, FWD>(s, x, B, ds, states, totals, st)
+                : launch_state_fast<64, 1, FWD>(s, x, B, ds, states, totals, st);
+}
+
+template <bool FWD>
+hipError_t scan_dispatch(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
+                         const float* start, const float* D, bf16* y, hipStream_t st) {
+    const bool pair = fast_hpw(s) == 2;
+    if (s.N == 128)
+        return pair ? launch_scan_fast<128, 2, FWD>(s, x, B, C, ds, start, D, y, st)
+                    : launch_scan_fast<128, 1, FWD>(s, x, B, C, ds, start, D, y, st);
+    return pair ? launch_scan_fast<64, 2, FWD>(s, x, B, C, ds, start, D, y, st)
+                : launch_scan_fast<64, 1, FWD>(s, x, B, C, ds, start, D, y, st);
+}
+
+}  // namespace fz
+
+hipError_t launch_chunk_state_fast(const Shape& s, const void* x, const void* B, const float* dt_t, const float* cs,
+                                   float* states, hipStream_t st) {
+    const fz::DtSrc ds{dt_t, cs};
+    return fz::state_dispatch<false>(s, (const bf16*)x, (const bf16*)B, ds, states, nullptr, st);
 }
 
 hipError_t launch_chunk_scan_fast(const Shape& s, const void* x, const void* B, const void* C, const float* dt_t,
                                   const float* cs, const float* start, const float* D, void* y, hipStream_t st) {
+    const fz::DtSrc ds{dt_t, cs};
+    return fz::scan_dispatch<false>(s, (const bf16*)x, (const bf16*)B, (const bf16*)C, ds, start, D, (bf16*)y, st);
+}
+
+FastFwdLayout fast_forward_layout(const Shape& s) {
+    auto a256 = [](size_t v) { return (v + 255) / 256 * 256; };
+    FastFwdLayout f;
+    const size_t pos = (size_t)(s.b * s.H * ((s.L + fz::QS - 1) / fz::QS) * fz::QS) * 4;
+    f.dtl = 0;
+    f.lw = a256(pos);
+    f.states = f.lw + a256(pos);
+    f.totals = f.states + a256((size_t)(s.b * s.nC * s.H * s.P * s.N) * 4);
+    f.total = f.totals + a256((size_t)(s.b * s.H * s.nC) * 4);
+    return f;
+}
+
+hipError_t launch_forward_fast(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
+                               const void* C, const float* D, const float* h0, void* y, float* final_state,
+                               void* workspace, hipStream_t st) {
+    const FastFwdLayout f = fast_forward_layout(s);
+    char* ws = static_cast<char*>(workspace);
+    float* dtl = reinterpret_cast<float*>(ws + f.dtl);
+    float* lw = reinterpret_cast<float*>(ws + f.lw);
+    float* states = reinterpret_cast<float*>(ws + f.states);
+    float* totals = reinterpret_cast<float*>(ws + f.totals);
     const bf16 *xb = (const bf16*)x, *bb = (const bf16*)B, *cb = (const bf16*)C;
-    bf16* yb = (bf16*)y;
-    const bool pair = fast_hpw(s) == 2;
-    if (s.N == 128)
-        return pair ? fz::launch_scan_fast<128, 2>(s, xb, bb, cb, dt_t, cs, start, D, yb, st)
-                    : fz::launch_scan_fast<128, 1>(s, xb, bb, cb, dt_t, cs, start, D, yb, st);
-    return pair ? fz::launch_scan_fast<64, 2>(s, xb, bb, cb, dt_t, cs, start, D, yb, st)
-                : fz::launch_scan_fast<64, 1>(s, xb, bb, cb, dt_t, cs, start, D, yb, st);
+    const uint32_t ndec = (uint32_t)(s.b * ((s.L + fz::QS - 1) / fz::QS));
+    hipLaunchKernelGGL(fz::subchunk_decay_kernel, dim3(ndec), dim3(256), 0, st, (const bf16*)dt, A, dtl, lw, s.L,
+                       (int)s.H, ndec);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const fz::DtSrc ds{dtl, lw};
+    e = fz::state_dispatch<true>(s, xb, bb, ds, states, totals, st);
+    if (e != hipSuccess) return e;
+    // the pass reads one total per chunk: a chunk of "length 1" in its indexing
+    Shape s1 = s;
+    s1.Q = 1;
+    e = launch_state_passing(s1, states, totals, h0, final_state, st);
+    if (e != hipSuccess) return e;
+    return fz::scan_dispatch<true>(s, xb, bb, cb, ds, states, D, (bf16*)y, st);
 }
 
 }  // namespace ssd

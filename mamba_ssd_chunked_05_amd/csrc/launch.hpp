@@ -32,6 +32,19 @@ hipError_t launch_chunk_state_fast(const Shape& s, const void* x, const void* B,
 hipError_t launch_chunk_scan_fast(const Shape& s, const void* x, const void* B, const void* C, const float* dt_t,
                                   const float* cs, const float* start, const float* D, void* y, hipStream_t st);
 
+// The forward on the fast path: the decay arrays restart at every 64-token
+// sub-chunk (one coalesced pass over dt), the chunk states also yield each
+// chunk's total decay, the state pass runs over those totals, then the output
+// kernel.  Workspace byte offsets: dt and decay (b, H, ceil(L/64), 64), chunk
+// states (b, nC, H, P, N), chunk totals (b, H, nC), all fp32.
+struct FastFwdLayout {
+    size_t dtl, lw, states, totals, total;
+};
+FastFwdLayout fast_forward_layout(const Shape& s);
+hipError_t launch_forward_fast(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
+                               const void* C, const float* D, const float* h0, void* y, float* final_state,
+                               void* workspace, hipStream_t st);
+
 // LDS bytes the generic chunk kernels need; used by validation.
 size_t chunk_state_lds_bytes(const Shape& s);
 size_t chunk_scan_lds_bytes(const Shape& s);
