@@ -11,7 +11,8 @@ The printed JSON line also carries
                     over its average launch duration, timed with HIP events on the
                     stream it runs on, against the MI355X peak;
   * cpu_baseline -- the fp64 oracle timed on this host on a bounded sample;
-  * decode       -- 64 back-to-back ssd_step calls on the 2.7B decode shape.
+  * decode       -- 64 back-to-back ssd_step calls on the 2.7B decode shape, the same 64 steps
+                    replayed as one graph, and as one ssd_step_multi call (state kept on chip).
 """
 
 from __future__ import annotations
@@ -258,6 +259,35 @@ def main():
         bb, hh, pp, nn, gg = c4["batch"], c4["nheads"], c4["headdim"], c4["dstate"], c4["ngroups"]
         step_bytes = 2 * bb * hh * pp * nn * 4 + bb * hh * (pp * 2 * 2 + 2) + 2 * bb * gg * nn * 2
         gbs = step_bytes / (step_ms / 1e3) / 1e9
+        nst = c4["steps"]
+        # the same 64 steps as one CUDA/HIP graph of ssd_step launches (no host work between steps)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(nst):
+                ssd.step(S, sx[i], sdt[i], sA, sB[i], sC[i], sD, y=yo[i])
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(3):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / (3 * nst)
+        # ... and as one ssd_step_multi call over the pre-staged inputs, the state kept on chip
+        xm, dtm = torch.stack(sx, dim=1).contiguous(), torch.stack(sdt, dim=1).contiguous()
+        Bm, Cm = torch.stack(sB, dim=1).contiguous(), torch.stack(sC, dim=1).contiguous()
+        ym = torch.empty_like(xm)
+        for _ in range(2):
+            ssd.step_multi(S, xm, dtm, sA, Bm, Cm, sD, y=ym)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            ssd.step_multi(S, xm, dtm, sA, Bm, Cm, sD, y=ym)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        multi_ms = e0.elapsed_time(e1) / reps
+        multi_bytes = 2 * bb * hh * pp * nn * 4 + nst * (step_bytes - 2 * bb * hh * pp * nn * 4)
+        multi_gbs = multi_bytes / (multi_ms / 1e3) / 1e9
         result["decode"] = {
             "workload": f"cfg4: ssd_step b={bb} H={hh} P={pp} N={nn} bf16 io, fp32 state, 64 steps",
             "us_per_step": step_ms * 1e3,
@@ -265,8 +295,19 @@ def main():
             "roofline": {"kernel": "step_kernel<bf16>", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": step_bytes},
             "note": "the 168 MB state fits the 256 MB Infinity Cache, so back-to-back steps can exceed HBM rate",
+            "graph_us_per_step": graph_ms * 1e3,
+            "multi_step": {
+                "call": f"ssd_step_multi, {nst} pre-staged steps per call, state in registers across steps",
+                "us_per_call": multi_ms * 1e3,
+                "us_per_step": multi_ms * 1e3 / nst,
+                "tokens_per_s": bb * nst / (multi_ms / 1e3),
+                "roofline": {"kernel": "step_multi_kernel<bf16,4,32>", "bound": "hbm", "achieved": multi_gbs,
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": multi_gbs / PEAK_HBM_GBS,
+                             "algorithmic_bytes_per_launch": multi_bytes},
+            },
         }
-        log(f"decode: {step_ms * 1e3:.1f} us/step, {gbs:.0f} GB/s algorithmic")
+        log(f"decode: {step_ms * 1e3:.1f} us/step, {gbs:.0f} GB/s algorithmic; graph {graph_ms * 1e3:.1f} us/step; "
+            f"multi-step {multi_ms * 1e3 / nst:.2f} us/step ({multi_gbs:.0f} GB/s algorithmic)")
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload ----------------
     if not args.no_cpu_baseline:

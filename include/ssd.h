@@ -161,6 +161,28 @@ ssd_status ssd_step(const ssd_dims* dims, float* state, const void* x, const voi
                     const float* A, const void* B, const void* C, const float* D,
                     void* y, void* stream);
 
+/*
+ * K decode steps in one call, over inputs that are all on the device before
+ * the call (pre-staged: teacher forcing, scoring, speculative verification):
+ * the on-device multi-step decode loop of the "Compiler-First State Space
+ * Duality ..." page (Methodology; Results), with the state read from and
+ * written to HBM once per call instead of once per step.  K = dims->seqlen
+ * (K = 0 is a no-op); dims->chunk is ignored.  For k < K, in order:
+ *     S <- exp(dt_k A) S + dt_k x_k (outer) B_k;   y_k = C_k . S + D x_k
+ * Inputs use the forward's layouts with K as the sequence axis:
+ *     x, y (b, K, H, P);  dt (b, K, H);  B, C (b, K, G, N);  state (b, H, P, N)
+ * fp32, updated in place.  The result equals K calls of ssd_step on the
+ * slices [:, k] (up to summation order in y).  state, x, B, C and y must be
+ * 16-byte aligned (SSD_ERR_UNSUPPORTED otherwise); y must not overlap the
+ * inputs or the state; D may be NULL.  The state stays in registers across
+ * the K steps when P divides 256 and N / (256 / P) is 4, 8, 16, 32 or 64 (and
+ * a block of 16 steps fits 64 KiB of LDS); other shapes run one step kernel
+ * per token on `stream`, still without a host round trip.
+ */
+ssd_status ssd_step_multi(const ssd_dims* dims, float* state, const void* x, const void* dt,
+                          const float* A, const void* B, const void* C, const float* D,
+                          void* y, void* stream);
+
 /* Static text for a status code. */
 const char* ssd_status_string(ssd_status status);
 

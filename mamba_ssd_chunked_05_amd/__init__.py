@@ -75,6 +75,7 @@ def load():
         "ssd_chunk_scan": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_forward": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "ssd_step": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "ssd_step_multi": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_query_config": [dp] + [ctypes.POINTER(ctypes.c_int)] * 4,
     }
     for name, args in sig.items():
@@ -231,6 +232,30 @@ def step(state, x, dt, A, B, C, D=None, *, y=None) -> torch.Tensor:
     st = lib.ssd_step(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                       _ptr(y), _stream(x))
     _check(st, "ssd_step")
+    return y
+
+
+def step_multi(state, x, dt, A, B, C, D=None, *, y=None) -> torch.Tensor:
+    """K pre-staged decode steps: x (b, K, H, P), dt (b, K, H), B, C (b, K, G, N); ``state``
+    (b, H, P, N) float32 is updated in place; returns y (b, K, H, P)."""
+    lib = load()
+    b, H, P, N = state.shape
+    K = x.shape[1]
+    G = B.shape[2]
+    _dev(state, "state", torch.float32)
+    _dev(x, "x", None, (b, K, H, P))
+    _dev(dt, "dt", x.dtype, (b, K, H))
+    _dev(A, "A", torch.float32, (H,))
+    _dev(B, "B", x.dtype, (b, K, G, N))
+    _dev(C, "C", x.dtype, (b, K, G, N))
+    _dev(D, "D", torch.float32, (H,))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, (b, K, H, P))
+    d = _dims(b, K, H, P, N, G, 0, _io_code(x))
+    st = lib.ssd_step_multi(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                            _ptr(y), _stream(x))
+    _check(st, "ssd_step_multi")
     return y
 
 

@@ -40,7 +40,7 @@ constexpr int64_t kMaxGrid = 0x7fffffffLL;
 // ---------------------------------------------------------------------------
 // dims validation
 // ---------------------------------------------------------------------------
-enum class Need { kStaged, kCumsum, kForward, kStep };
+enum class Need { kStaged, kCumsum, kForward, kStep, kStepMulti };
 
 ssd_status check_dims(const ssd_dims* d, Need need, ssd::Shape* out) {
     if (!d) return fail(SSD_ERR_NULL, "dims is NULL");
@@ -65,8 +65,9 @@ ssd_status check_dims(const ssd_dims* d, Need need, ssd::Shape* out) {
     s.N = d->dstate;
     s.G = d->ngroups;
     s.io = d->io;
-    if (need == Need::kStep) {
-        if (d->seqlen != 1) return fail(SSD_ERR_SHAPE, "ssd_step needs seqlen == 1 (got %lld)", (long long)d->seqlen);
+    if (need == Need::kStep || need == Need::kStepMulti) {
+        if (need == Need::kStep && d->seqlen != 1)
+            return fail(SSD_ERR_SHAPE, "ssd_step needs seqlen == 1 (got %lld)", (long long)d->seqlen);
         if (s.b * s.H > kMaxGrid) return fail(SSD_ERR_UNSUPPORTED, "batch * nheads too large");
         s.Q = 1;
         s.nC = 1;
@@ -375,6 +376,34 @@ ssd_status ssd_step(const ssd_dims* dims, float* state, const void* x, const voi
         SSD_TRY(no_alias(sy, ins2, 7));
         hipError_t he = ssd::launch_step(s, state, x, dt, A, B, C, D, y, (hipStream_t)stream);
         if (he != hipSuccess) return hip_fail(he, "ssd_step");
+        return ok();
+    } catch (...) {
+        return fail(SSD_ERR_HIP, "internal error");
+    }
+}
+
+ssd_status ssd_step_multi(const ssd_dims* dims, float* state, const void* x, const void* dt, const float* A,
+                          const void* B, const void* C, const float* D, void* y, void* stream) {
+    try {
+        ssd::Shape s;
+        SSD_TRY(check_dims(dims, Need::kStepMulti, &s));
+        const size_t e = esz(s);
+        const size_t K = (size_t)s.L;
+        Span sst{state, (size_t)(s.b * s.H * s.P * s.N) * 4, "state"},
+            sx{x, (size_t)(s.b * s.H * s.P) * K * e, "x"}, sdt{dt, (size_t)(s.b * s.H) * K * e, "dt"},
+            sA{A, (size_t)s.H * 4, "A"}, sB{B, (size_t)(s.b * s.G * s.N) * K * e, "B"},
+            sC{C, (size_t)(s.b * s.G * s.N) * K * e, "C"}, sD{D, D ? (size_t)s.H * 4 : 0, "D"},
+            sy{y, (size_t)(s.b * s.H * s.P) * K * e, "y"};
+        for (const Span& p : {sst, sx, sdt, sA, sB, sC, sy}) SSD_TRY(need_ptr(p));
+        Span ins[] = {sx, sdt, sA, sB, sC, sD};
+        SSD_TRY(no_alias(sst, ins, 6));
+        Span ins2[] = {sx, sdt, sA, sB, sC, sD, sst};
+        SSD_TRY(no_alias(sy, ins2, 7));
+        for (const Span& p : {sst, sx, sB, sC, sy})
+            if (reinterpret_cast<uintptr_t>(p.p) % 16)
+                return fail(SSD_ERR_UNSUPPORTED, "%s must be 16-byte aligned", p.name);
+        hipError_t he = ssd::launch_step_multi(s, state, x, dt, A, B, C, D, y, (hipStream_t)stream);
+        if (he != hipSuccess) return hip_fail(he, "ssd_step_multi");
         return ok();
     } catch (...) {
         return fail(SSD_ERR_HIP, "internal error");

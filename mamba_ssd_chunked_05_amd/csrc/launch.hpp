@@ -22,6 +22,12 @@ hipError_t launch_chunk_scan(const Shape& s, const void* x, const void* B, const
                              const float* cs, const float* start, const float* D, void* y, hipStream_t st);
 hipError_t launch_step(const Shape& s, float* state, const void* x, const void* dt, const float* A,
                        const void* B, const void* C, const float* D, void* y, hipStream_t st);
+// K = s.L decode steps over pre-staged (b, K, ...) inputs; the state stays on chip
+// when N / 16 is 4, 8, 16, 32 or 64 and P * N <= 16384 (a 16 x 16 thread grid of
+// P/16 x N/16 register blocks), else one launch per step.
+bool step_multi_on_chip(const Shape& s);
+hipError_t launch_step_multi(const Shape& s, float* state, const void* x, const void* dt, const float* A,
+                             const void* B, const void* C, const float* D, void* y, hipStream_t st);
 
 // Fast chunk-state / chunk-scan kernels (bf16, headdim 64, dstate 64 or 128, chunk a multiple of 64).
 bool fast_chunk_supported(const Shape& s);

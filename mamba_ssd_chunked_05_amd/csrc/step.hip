@@ -16,12 +16,14 @@
 
 namespace ssd {
 
+// Batch strides (in elements) sx of x and y, sdt of dt and sbc of B and C let
+// the same kernel step one token of a (b, K, ...) multi-step layout.
 template <class T>
 __global__ void __launch_bounds__(256) step_kernel(float* __restrict__ state, const T* __restrict__ x,
                                                    const T* __restrict__ dt, const float* __restrict__ A,
                                                    const T* __restrict__ B, const T* __restrict__ C,
                                                    const float* __restrict__ D, T* __restrict__ y, int H, int P,
-                                                   int N, int G) {
+                                                   int N, int G, int64_t sx, int64_t sdt, int64_t sbc) {
     __shared__ float xs[256];
     __shared__ float ys[256];
     __shared__ float Bs[1024];
@@ -32,14 +34,14 @@ __global__ void __launch_bounds__(256) step_kernel(float* __restrict__ state, co
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63;
     for (int p = tid; p < P; p += 256) {
-        xs[p] = to_f32(x[bh * P + p]);
+        xs[p] = to_f32(x[b * sx + (int64_t)h * P + p]);
         ys[p] = 0.0f;
     }
     for (int n = tid; n < N; n += 256) {
-        Bs[n] = to_f32(B[(b * G + g) * N + n]);
-        Cs[n] = to_f32(C[(b * G + g) * N + n]);
+        Bs[n] = to_f32(B[b * sbc + (int64_t)g * N + n]);
+        Cs[n] = to_f32(C[b * sbc + (int64_t)g * N + n]);
     }
-    const float d = to_f32(dt[bh]);
+    const float d = to_f32(dt[b * sdt + h]);
     const float a = fast_exp2(kLog2e * (d * A[h]));
     __syncthreads();
 
@@ -79,22 +81,324 @@ __global__ void __launch_bounds__(256) step_kernel(float* __restrict__ state, co
     }
     __syncthreads();
     const float Dh = D ? D[h] : 0.0f;
-    for (int p = tid; p < P; p += 256) y[bh * P + p] = from_f32<T>(ys[p] + Dh * xs[p]);
+    for (int p = tid; p < P; p += 256) y[b * sx + (int64_t)h * P + p] = from_f32<T>(ys[p] + Dh * xs[p]);
 }
 
 hipError_t launch_step(const Shape& s, float* state, const void* x, const void* dt, const float* A, const void* B,
                        const void* C, const float* D, void* y, hipStream_t st) {
     const int64_t nbh = s.b * s.H;
     if (nbh == 0) return hipSuccess;
+    const int64_t sx = s.H * s.P, sdt = s.H, sbc = s.G * s.N;
     if (s.io == 1)
         hipLaunchKernelGGL(step_kernel<bf16>, dim3((unsigned)nbh), dim3(256), 0, st, state, (const bf16*)x,
                            (const bf16*)dt, A, (const bf16*)B, (const bf16*)C, D, (bf16*)y, (int)s.H, (int)s.P,
-                           (int)s.N, (int)s.G);
+                           (int)s.N, (int)s.G, sx, sdt, sbc);
     else
         hipLaunchKernelGGL(step_kernel<float>, dim3((unsigned)nbh), dim3(256), 0, st, state, (const float*)x,
                            (const float*)dt, A, (const float*)B, (const float*)C, D, (float*)y, (int)s.H, (int)s.P,
-                           (int)s.N, (int)s.G);
+                           (int)s.N, (int)s.G, sx, sdt, sbc);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// K decode steps over pre-staged inputs with the state held on chip
+// ---------------------------------------------------------------------------
+// The multi-step form of the same update (the on-device decode loop of the
+// "Compiler-First State Space Duality ..." page, Methodology and Results: the
+// state never leaves the device and no host round trip separates the steps).
+// Inputs of all K steps are already on the device in the forward's layouts,
+// x, y (b, K, H, P), dt (b, K, H), B, C (b, K, G, N); step k is token k.
+//
+// One workgroup per (b, h) holds the P x N fp32 state in registers for all K
+// steps.  The 256 threads form a 16 x 16 grid over (row block, column block):
+// thread t owns rows RT (t / 16) .. + RT - 1 and columns CT (t % 16) .. + CT - 1
+// (RT = P / 16, CT = N / 16), so a step reads CT values of B and of C and RT of
+// x from LDS for RT * CT state elements.  C . S is reduced over the 16 threads
+// of a row block -- sixteen consecutive lanes -- with DPP moves.  Each block of
+// KB steps stages x, dt, B, C in LDS (fp32) and leaves y in LDS, written out
+// coalesced after the block.  The state crosses HBM once per call.
+constexpr int kMultiKB = 16;  // steps per LDS block
+
+// One block of KB steps' inputs in registers: x (KB x P), B and C (KB x N) as
+// 16-byte pieces, thread t holding pieces t, t + 256, ...; loaded while the
+// previous block is computed, then stored to LDS as fp32.
+template <class T, int P, int N, int KB>
+struct MultiBlock {
+    static constexpr int V = 16 / sizeof(T);                 // elements per piece
+    static constexpr int NX = (KB * P / V + 255) / 256;      // x pieces per thread
+    static constexpr int NB = (KB * N / V + 255) / 256;      // B (and C) pieces per thread
+    uint4 xv[NX], bv[NB], cv[NB];
+    T draw;
+
+    __device__ __forceinline__ void load(const T* __restrict__ x, const T* __restrict__ dt,
+                                         const T* __restrict__ B, const T* __restrict__ C, int64_t b, int64_t K,
+                                         int64_t k0, int kb, int h, int g, int H, int G, int tid) {
+        // Rows past the block's kb steps load a valid row (the block's first) instead: the
+        // step loop never reads them, and no select makes the loads wait here.
+        const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N;
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int e = tid + 256 * i, r = e / (P / V), c = (e % (P / V)) * V;
+            xv[i] = *reinterpret_cast<const uint4*>(x + (b * K + k0 + (r < kb ? r : 0)) * HP + (int64_t)h * P + c);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int e = tid + 256 * i, r = e / (N / V), c = (e % (N / V)) * V;
+            const int64_t off = (b * K + k0 + (r < kb ? r : 0)) * GN + (int64_t)g * N + c;
+            bv[i] = *reinterpret_cast<const uint4*>(B + off);
+            cv[i] = *reinterpret_cast<const uint4*>(C + off);
+        }
+        draw = dt[(b * K + k0 + (tid < kb ? tid : 0)) * H + h];
+        __builtin_amdgcn_sched_barrier(0);  // nothing that uses the pieces moves up to here
+    }
+
+    // 16 bytes -> V floats, on 32-bit words (bf16 is the upper half of an fp32)
+    static __device__ __forceinline__ void unpack(const uint4& v, float* f) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (V == 8) {
+                f[2 * q] = __uint_as_float(w[q] << 16);
+                f[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+            } else {
+                f[q] = __uint_as_float(w[q]);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(float* xs, float* bs, float* cs, float* ds, int tid) const {
+        float f[V];
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int e = tid + 256 * i;
+            if (e < KB * P / V) {
+                unpack(xv[i], f);
+#pragma unroll
+                for (int q = 0; q < V; q += 4)
+                    *reinterpret_cast<float4*>(xs + e * V + q) = make_float4(f[q], f[q + 1], f[q + 2], f[q + 3]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int e = tid + 256 * i;
+            if (e < KB * N / V) {
+                unpack(bv[i], f);
+#pragma unroll
+                for (int q = 0; q < V; q += 4)
+                    *reinterpret_cast<float4*>(bs + e * V + q) = make_float4(f[q], f[q + 1], f[q + 2], f[q + 3]);
+                unpack(cv[i], f);
+#pragma unroll
+                for (int q = 0; q < V; q += 4)
+                    *reinterpret_cast<float4*>(cs + e * V + q) = make_float4(f[q], f[q + 1], f[q + 2], f[q + 3]);
+            }
+        }
+        if (tid < KB) ds[tid] = to_f32(draw);
+    }
+};
+
+// Sum over the 16 lanes of a DPP row, returned in every lane of the row:
+// quad_perm [1,0,3,2] and [2,3,0,1] sum each quad, row_half_mirror pairs the
+// two quads of each half row, row_mirror pairs the two half rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);  // row_half_mirror
+    v += dpp_mov<0x140>(v);  // row_mirror
+    return v;
+}
+
+template <class T, int RT, int CT>
+__global__ void __launch_bounds__(256) step_multi_kernel(float* __restrict__ state, const T* __restrict__ x,
+                                                         const T* __restrict__ dt, const float* __restrict__ A,
+                                                         const T* __restrict__ B, const T* __restrict__ C,
+                                                         const float* __restrict__ D, T* __restrict__ y, int64_t K,
+                                                         int H, int G) {
+    constexpr int P = 16 * RT, N = 16 * CT, KB = kMultiKB;
+    __shared__ __align__(16) float xs[KB * P];
+    __shared__ __align__(16) float bs[KB * N];
+    __shared__ __align__(16) float cs[KB * N];
+    __shared__ float ds[KB];
+    __shared__ float as[KB];  // exp(dt A) of each step of the block
+    __shared__ float ys[KB * P];
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / H;
+    const int h = (int)(bh % H);
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, cg = tid & 15, p0 = (tid >> 4) * RT, n0 = cg * CT;
+    float s[RT][CT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        const float* row = state + (bh * P + p0 + i) * (int64_t)N + n0;
+#pragma unroll
+        for (int j = 0; j < CT; j += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(row + j);
+            s[i][j] = v.x;
+            s[i][j + 1] = v.y;
+            s[i][j + 2] = v.z;
+            s[i][j + 3] = v.w;
+        }
+    }
+    const float al = A[h] * kLog2e;
+    const float Dh = D ? D[h] : 0.0f;
+    const int64_t HP = (int64_t)H * P;
+    MultiBlock<T, P, N, KB> blk;
+    blk.load(x, dt, B, C, b, K, 0, K < KB ? (int)K : KB, h, g, H, G, tid);
+    for (int64_t k0 = 0; k0 < K; k0 += KB) {
+        const int kb = K - k0 < KB ? (int)(K - k0) : KB;
+        __syncthreads();  // the previous block's y is written out; the LDS block is free
+        blk.store(xs, bs, cs, ds, tid);
+        if (tid < KB) as[tid] = fast_exp2(to_f32(blk.draw) * al);
+        __syncthreads();
+        if (k0 + KB < K) {  // the next block's inputs stream in while this one is computed
+            const int64_t k1 = k0 + KB;
+            blk.load(x, dt, B, C, b, K, k1, K - k1 < KB ? (int)(K - k1) : KB, h, g, H, G, tid);
+        }
+        // software pipeline: step kk + 1's B, C and x are read from LDS while step kk computes
+        float bv[CT], cv[CT], xv[RT];
+        auto fetch = [&](int kk, float* bq, float* cq, float* xq) {
+#pragma unroll
+            for (int j = 0; j < CT; j += 4) {
+                const float4 b4 = *reinterpret_cast<const float4*>(bs + kk * N + n0 + j);
+                const float4 c4 = *reinterpret_cast<const float4*>(cs + kk * N + n0 + j);
+                bq[j] = b4.x, bq[j + 1] = b4.y, bq[j + 2] = b4.z, bq[j + 3] = b4.w;
+                cq[j] = c4.x, cq[j + 1] = c4.y, cq[j + 2] = c4.z, cq[j + 3] = c4.w;
+            }
+#pragma unroll
+            for (int i = 0; i < RT; ++i) xq[i] = xs[kk * P + p0 + i];
+        };
+        fetch(0, bv, cv, xv);
+        for (int kk = 0; kk < kb; ++kk) {
+            const float d = ds[kk];
+            const float a = as[kk];
+            float bn[CT], cn[CT], xn[RT];
+            fetch(kk + 1 < kb ? kk + 1 : kk, bn, cn, xn);
+            // all rows' partial sums first (two chains per row), then the row reductions, so the
+            // independent chains interleave; lane cg of a row block keeps row p0 + cg
+            float sum[RT];
+#pragma unroll
+            for (int i = 0; i < RT; ++i) {
+                const float u = d * xv[i];
+                float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+                for (int j = 0; j < CT; j += 2) {
+                    s[i][j] = a * s[i][j] + u * bv[j];
+                    s[i][j + 1] = a * s[i][j + 1] + u * bv[j + 1];
+                    pa += cv[j] * s[i][j];
+                    pb += cv[j + 1] * s[i][j + 1];
+                }
+                sum[i] = pa + pb;
+            }
+#pragma unroll
+            for (int i = 0; i < RT; ++i) sum[i] = row16_sum(sum[i]);
+            float mine = sum[0], xm = xv[0];
+#pragma unroll
+            for (int i = 1; i < RT; ++i) {
+                mine = cg == i ? sum[i] : mine;
+                xm = cg == i ? xv[i] : xm;
+            }
+            if (cg < RT) ys[kk * P + p0 + cg] = mine + Dh * xm;
+#pragma unroll
+            for (int j = 0; j < CT; ++j) bv[j] = bn[j], cv[j] = cn[j];
+#pragma unroll
+            for (int i = 0; i < RT; ++i) xv[i] = xn[i];
+        }
+        __syncthreads();
+        for (int e = tid; e < kb * P; e += 256) {
+            const int kk = e / P, pp = e % P;
+            y[(b * K + k0 + kk) * HP + (int64_t)h * P + pp] = from_f32<T>(ys[e]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        float* row = state + (bh * P + p0 + i) * (int64_t)N + n0;
+#pragma unroll
+        for (int j = 0; j < CT; j += 4)
+            *reinterpret_cast<float4*>(row + j) = make_float4(s[i][j], s[i][j + 1], s[i][j + 2], s[i][j + 3]);
+    }
+}
+
+// static LDS of one block of steps (x, y: KB x P; B, C: KB x N; fp32) within 64 KiB,
+// and at most 64 state elements per thread
+constexpr bool multi_ok(int RT, int CT) {
+    return RT * CT <= 64 && 4 * kMultiKB * (2 * 16 * RT + 2 * 16 * CT) + 64 <= 65536;
+}
+
+template <class T, int RT, int CT>
+static hipError_t launch_multi(const Shape& s, float* state, const void* x, const void* dt, const float* A,
+                               const void* B, const void* C, const float* D, void* y, hipStream_t st) {
+    if constexpr (multi_ok(RT, CT)) {
+        hipLaunchKernelGGL((step_multi_kernel<T, RT, CT>), dim3((unsigned)(s.b * s.H)), dim3(256), 0, st, state,
+                           (const T*)x, (const T*)dt, A, (const T*)B, (const T*)C, D, (T*)y, s.L, (int)s.H,
+                           (int)s.G);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class T, int CT>
+static hipError_t multi_by_rt(const Shape& s, float* state, const void* x, const void* dt, const float* A,
+                              const void* B, const void* C, const float* D, void* y, hipStream_t st) {
+    switch (s.P / 16) {
+#define SSD_RT(r) \
+    case r: return launch_multi<T, r, CT>(s, state, x, dt, A, B, C, D, y, st);
+        SSD_RT(1) SSD_RT(2) SSD_RT(3) SSD_RT(4) SSD_RT(5) SSD_RT(6) SSD_RT(7) SSD_RT(8)
+        SSD_RT(9) SSD_RT(10) SSD_RT(11) SSD_RT(12) SSD_RT(13) SSD_RT(14) SSD_RT(15) SSD_RT(16)
+#undef SSD_RT
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class T>
+static hipError_t multi_by_ct(const Shape& s, float* state, const void* x, const void* dt, const float* A,
+                              const void* B, const void* C, const float* D, void* y, hipStream_t st) {
+    switch (s.N / 16) {
+        case 4: return multi_by_rt<T, 4>(s, state, x, dt, A, B, C, D, y, st);
+        case 8: return multi_by_rt<T, 8>(s, state, x, dt, A, B, C, D, y, st);
+        case 16: return multi_by_rt<T, 16>(s, state, x, dt, A, B, C, D, y, st);
+        case 32: return multi_by_rt<T, 32>(s, state, x, dt, A, B, C, D, y, st);
+        case 64: return multi_by_rt<T, 64>(s, state, x, dt, A, B, C, D, y, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+bool step_multi_on_chip(const Shape& s) {
+    const int rt = (int)(s.P / 16), ct = (int)(s.N / 16);
+    const bool ct_ok = ct == 4 || ct == 8 || ct == 16 || ct == 32 || ct == 64;
+    return s.P % 16 == 0 && s.N % 16 == 0 && rt >= 1 && rt <= 16 && ct_ok && multi_ok(rt, ct);
+}
+
+hipError_t launch_step_multi(const Shape& s, float* state, const void* x, const void* dt, const float* A,
+                             const void* B, const void* C, const float* D, void* y, hipStream_t st) {
+    const int64_t nbh = s.b * s.H;
+    if (nbh == 0 || s.L == 0) return hipSuccess;
+    if (step_multi_on_chip(s))
+        return s.io == 1 ? multi_by_ct<bf16>(s, state, x, dt, A, B, C, D, y, st)
+                         : multi_by_ct<float>(s, state, x, dt, A, B, C, D, y, st);
+    // other state shapes: one single-step launch per token, still without a host round trip
+    const size_t e = s.io == 1 ? 2 : 4;
+    const int64_t sx = s.L * s.H * s.P, sdt = s.L * s.H, sbc = s.L * s.G * s.N;
+    for (int64_t k = 0; k < s.L; ++k) {
+        const char* xk = static_cast<const char*>(x) + k * s.H * s.P * e;
+        const char* dk = static_cast<const char*>(dt) + k * s.H * e;
+        const char* bk = static_cast<const char*>(B) + k * s.G * s.N * e;
+        const char* ck = static_cast<const char*>(C) + k * s.G * s.N * e;
+        char* yk = static_cast<char*>(y) + k * s.H * s.P * e;
+        if (s.io == 1)
+            hipLaunchKernelGGL(step_kernel<bf16>, dim3((unsigned)nbh), dim3(256), 0, st, state, (const bf16*)xk,
+                               (const bf16*)dk, A, (const bf16*)bk, (const bf16*)ck, D, (bf16*)yk, (int)s.H,
+                               (int)s.P, (int)s.N, (int)s.G, sx, sdt, sbc);
+        else
+            hipLaunchKernelGGL(step_kernel<float>, dim3((unsigned)nbh), dim3(256), 0, st, state, (const float*)xk,
+                               (const float*)dk, A, (const float*)bk, (const float*)ck, D, (float*)yk, (int)s.H,
+                               (int)s.P, (int)s.N, (int)s.G, sx, sdt, sbc);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace ssd

@@ -27,7 +27,7 @@ def _declared():
 def test_header_symbols_exported():
     lib = ssd.load()
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
 
@@ -130,6 +130,24 @@ def test_step_validates():
     bad = list(args)
     bad[0] = None
     assert lib.ssd_step(ctypes.byref(d), *bad) == NULL
+
+
+def test_step_multi_validates():
+    lib = ssd.load()
+    args = [_p(0), _p(1 << 30), _p(2 << 30), _p(3 << 30), _p(4 << 30), _p(5 << 30), None, _p(6 << 30), None]
+    d = _d(L=8)
+    bad = list(args)
+    bad[7] = _p(64)  # y over the state
+    assert lib.ssd_step_multi(ctypes.byref(d), *bad) == ALIAS
+    bad = list(args)
+    bad[3] = None
+    assert lib.ssd_step_multi(ctypes.byref(d), *bad) == NULL
+    bad = list(args)
+    bad[1] = _p((1 << 30) + 8)  # x not 16-byte aligned
+    assert lib.ssd_step_multi(ctypes.byref(d), *bad) == UNSUP
+    assert lib.ssd_step_multi(ctypes.byref(_d(L=8, io=7)), *args) == DTYPE
+    # zero steps: a no-op that launches nothing
+    assert lib.ssd_step_multi(ctypes.byref(_d(L=0)), *args) == OK
 
 
 def test_workspace_and_config_are_host_only():
