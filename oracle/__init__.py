@@ -53,13 +53,15 @@ def _load():
         if not os.path.exists(_LIB_PATH):
             build(force=False)
         lib = ctypes.CDLL(_LIB_PATH)
-        lib.ssd_oracle_forward.argtypes = [_I64] * 6 + [_DP] * 9 + [_I64, _DP, _DP, ctypes.c_int]
-        lib.ssd_oracle_step.argtypes = [_I64] * 5 + [_DP] * 8 + [ctypes.c_int]
-        lib.ssd_oracle_chunk_cumsum.argtypes = [_I64] * 4 + [_DP] * 4
+        lib.ssd_oracle_forward.argtypes = [_I64] * 6 + [_DP] * 10 + [_I64, _DP, _DP, ctypes.c_int]
+        lib.ssd_oracle_step.argtypes = [_I64] * 5 + [_DP] * 9 + [ctypes.c_int]
+        lib.ssd_oracle_chunk_cumsum.argtypes = [_I64] * 4 + [_DP] * 5
+        lib.ssd_oracle_dt_frontend.argtypes = ([_I64] * 2 + [_DP] * 3 + [ctypes.c_int] * 3
+                                               + [ctypes.c_double] * 2 + [_DP] * 2)
         lib.ssd_oracle_state_passing.argtypes = [_I64] * 6 + [_DP] * 5
         lib.ssd_oracle_chunk_scan.argtypes = [_I64] * 7 + [_DP] * 8 + [ctypes.c_int]
         for f in ("ssd_oracle_forward", "ssd_oracle_step", "ssd_oracle_chunk_cumsum",
-                  "ssd_oracle_state_passing", "ssd_oracle_chunk_scan"):
+                  "ssd_oracle_state_passing", "ssd_oracle_chunk_scan", "ssd_oracle_dt_frontend"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -87,14 +89,33 @@ def _check(rc: int, name: str):
         raise ValueError(f"{name}: oracle rejected the arguments (rc={rc})")
 
 
-def forward(x, dt, A, B, C, D=None, h0=None, *, chunk: int = 0, chunk_states: bool = False,
+def dt_frontend(raw, A, bias=None, *, softplus: bool = False, zoh: bool = False, clamp=None):
+    """(dt_decay, dt_input) from a raw step (..., H): bias, softplus, clamp (lo, hi), and the
+    zero-order-hold input factor (exp(dt A) - 1) / A when ``zoh``."""
+    raw = np.asarray(raw, dtype=np.float64)
+    H = raw.shape[-1]
+    n = raw.size // H if H else 0
+    ra, pr = _in(raw)
+    Aa, pA = _in(A)
+    ba, pb = _in(bias)
+    dec, pd = _out(raw.shape)
+    inp, pi = _out(raw.shape)
+    lo, hi = (clamp if clamp is not None else (0.0, 0.0))
+    rc = _load().ssd_oracle_dt_frontend(n, H, pr, pA, pb, int(softplus), int(zoh), int(clamp is not None),
+                                        float(lo), float(hi), pd, pi)
+    _check(rc, "dt_frontend")
+    return dec, inp
+
+
+def forward(x, dt, A, B, C, D=None, h0=None, *, dt_in=None, chunk: int = 0, chunk_states: bool = False,
             threads: int = 0):
-    """Token recurrence.  Returns dict(y, final[, chunk_start, chunk_local])."""
+    """Token recurrence.  Returns dict(y, final[, chunk_start, chunk_local]).  ``dt`` is the decay
+    step; ``dt_in`` (default: dt) the step of the input term."""
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     keep = []
     ptrs = []
-    for a in (x, dt, A, B, C, D, h0):
+    for a in (x, dt, dt_in, A, B, C, D, h0):
         arr, p = _in(a)
         keep.append(arr)
         ptrs.append(p)
@@ -113,15 +134,16 @@ def forward(x, dt, A, B, C, D=None, h0=None, *, chunk: int = 0, chunk_states: bo
     return res
 
 
-def step(state, x, dt, A, B, C, D=None, *, threads: int = 0):
-    """One decode step.  ``state`` (b,H,P,N) float64 is updated in place; returns y (b,H,P)."""
+def step(state, x, dt, A, B, C, D=None, *, dt_in=None, threads: int = 0):
+    """One decode step.  ``state`` (b,H,P,N) float64 is updated in place; returns y (b,H,P).
+    ``dt`` is the decay step, ``dt_in`` (default: dt) the step of the input term."""
     if state.dtype != np.float64 or not state.flags.c_contiguous:
         raise TypeError("state must be a C-contiguous float64 array (updated in place)")
     b, H, P, N = state.shape
     G = B.shape[1]
     keep = []
     ptrs = []
-    for a in (x, dt, A, B, C, D):
+    for a in (x, dt, dt_in, A, B, C, D):
         arr, p = _in(a)
         keep.append(arr)
         ptrs.append(p)
@@ -131,15 +153,16 @@ def step(state, x, dt, A, B, C, D=None, *, threads: int = 0):
     return y
 
 
-def chunk_cumsum(dt, A, chunk: int):
-    """(dt_t, cs_log2), both (b,H,nC,Q)."""
+def chunk_cumsum(dt, A, chunk: int, *, dt_in=None):
+    """(dt_t, cs_log2), both (b,H,nC,Q); dt_t is the input step (``dt_in`` when given)."""
     b, L, H = dt.shape
     nC = -(-L // chunk)
     dta, pdt = _in(dt)
+    dia, pdi = _in(dt_in)
     Aa, pA = _in(A)
     dtt, pdtt = _out((b, H, nC, chunk))
     cs, pcs = _out((b, H, nC, chunk))
-    _check(_load().ssd_oracle_chunk_cumsum(b, L, H, chunk, pdt, pA, pdtt, pcs), "chunk_cumsum")
+    _check(_load().ssd_oracle_chunk_cumsum(b, L, H, chunk, pdt, pdi, pA, pdtt, pcs), "chunk_cumsum")
     return dtt, cs
 
 

@@ -28,6 +28,13 @@
  * written as the plain definition of its result (a token recurrence over the
  * chunk), not as the chunked algebra.
  *
+ * Optional dt front-end (ssd_oracle_dt_frontend): a per-head bias, softplus
+ * and a clamp turn a raw dt into the step; the zero-order-hold (ZOH) input
+ * matrix of "3.3 Hardware-Aware ..." section 2.1 replaces dt in the input term
+ * by (exp(dt A) - 1) / A (for scalar A the ZOH B-bar is that factor times B).
+ * Every recurrence below therefore takes the decay step dt and, optionally, a
+ * separate input step dt_in (NULL: the input term uses dt).
+ *
  * Layouts (row-major, contiguous): x, y (b,L,H,P); dt (b,L,H); A, D (H);
  * B, C (b,L,G,N); h0, final, step state (b,H,P,N); per-chunk states
  * (b,nC,H,P,N); dt_t and the log2 cumulative sum (b,H,nC,Q).
@@ -61,14 +68,16 @@ static void set_threads(int nthreads) {
 #endif
 }
 
-/* One token of the recurrence for one (b, h): S <- a*S + dt*x (outer) B, then
- * y = C.S + D*x.  Pointers are already offset to this token and head. */
-static void token_update(int64_t P, int64_t N, double* S, double dt, double A,
+/* One token of the recurrence for one (b, h): S <- a*S + dtu*x (outer) B with
+ * a = exp(dt*A), then y = C.S + D*x.  dt is the decay step and dtu the input
+ * step (equal unless a front-end says otherwise).  Pointers are already offset
+ * to this token and head. */
+static void token_update(int64_t P, int64_t N, double* S, double dt, double dtu, double A,
                          const double* x, const double* B, const double* C,
                          double Dh, int has_D, double* y) {
     double a = exp(dt * A);
     for (int64_t p = 0; p < P; ++p) {
-        double u = dt * x[p];
+        double u = dtu * x[p];
         double* row = S + p * N;
         for (int64_t n = 0; n < N; ++n) row[n] = a * row[n] + u * B[n];
     }
@@ -94,7 +103,7 @@ static int bad_dims(int64_t b, int64_t L, int64_t H, int64_t P, int64_t N, int64
  * Returns 0, or -1 on inconsistent arguments.
  */
 int ssd_oracle_forward(int64_t b, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
-                       const double* x, const double* dt, const double* A,
+                       const double* x, const double* dt, const double* dt_in, const double* A,
                        const double* B, const double* C, const double* D,
                        const double* h0, double* y, double* final_state,
                        int64_t chunk, double* chunk_start, double* chunk_local,
@@ -115,8 +124,8 @@ int ssd_oracle_forward(int64_t b, int64_t L, int64_t H, int64_t P, int64_t N, in
             if (chunk_start && t % chunk == 0)
                 memcpy(chunk_start + ((bb * nC + t / chunk) * H + h) * P * N, S, sizeof(double) * P * N);
             int64_t bt = bb * L + t;
-            token_update(P, N, S, dt[bt * H + h], A[h], x + (bt * H + h) * P,
-                         B + (bt * G + g) * N, C + (bt * G + g) * N,
+            token_update(P, N, S, dt[bt * H + h], (dt_in ? dt_in : dt)[bt * H + h], A[h],
+                         x + (bt * H + h) * P, B + (bt * G + g) * N, C + (bt * G + g) * N,
                          D ? D[h] : 0.0, D != NULL, y ? y + (bt * H + h) * P : NULL);
         }
         if (final_state) memcpy(final_state + bh * P * N, S, sizeof(double) * P * N);
@@ -126,8 +135,9 @@ int ssd_oracle_forward(int64_t b, int64_t L, int64_t H, int64_t P, int64_t N, in
                 int64_t t1 = (c + 1) * chunk < L ? (c + 1) * chunk : L;
                 for (int64_t t = c * chunk; t < t1; ++t) {
                     int64_t bt = bb * L + t;
-                    token_update(P, N, S, dt[bt * H + h], A[h], x + (bt * H + h) * P,
-                                 B + (bt * G + g) * N, C + (bt * G + g) * N, 0.0, 0, NULL);
+                    token_update(P, N, S, dt[bt * H + h], (dt_in ? dt_in : dt)[bt * H + h], A[h],
+                                 x + (bt * H + h) * P, B + (bt * G + g) * N, C + (bt * G + g) * N, 0.0, 0,
+                                 NULL);
                 }
                 memcpy(chunk_local + ((bb * nC + c) * H + h) * P * N, S, sizeof(double) * P * N);
             }
@@ -144,7 +154,7 @@ int ssd_oracle_forward(int64_t b, int64_t L, int64_t H, int64_t P, int64_t N, in
  * (b,H,P,N), updated in place; x (b,H,P); dt (b,H); B, C (b,G,N); y (b,H,P).
  */
 int ssd_oracle_step(int64_t b, int64_t H, int64_t P, int64_t N, int64_t G,
-                    double* state, const double* x, const double* dt, const double* A,
+                    double* state, const double* x, const double* dt, const double* dt_in, const double* A,
                     const double* B, const double* C, const double* D, double* y,
                     int nthreads) {
     if (bad_dims(b, 1, H, P, N, G)) return -1;
@@ -153,7 +163,7 @@ int ssd_oracle_step(int64_t b, int64_t H, int64_t P, int64_t N, int64_t G,
 #pragma omp parallel for schedule(static)
     for (int64_t bh = 0; bh < b * H; ++bh) {
         int64_t bb = bh / H, h = bh % H, g = h / hpg;
-        token_update(P, N, state + bh * P * N, dt[bh], A[h], x + bh * P,
+        token_update(P, N, state + bh * P * N, dt[bh], (dt_in ? dt_in : dt)[bh], A[h], x + bh * P,
                      B + (bb * G + g) * N, C + (bb * G + g) * N,
                      D ? D[h] : 0.0, D != NULL, y + bh * P);
     }
@@ -161,13 +171,44 @@ int ssd_oracle_step(int64_t b, int64_t H, int64_t P, int64_t N, int64_t G,
 }
 
 /*
+ * dt front-end, elementwise over n rows of H heads (row-major (n, H)):
+ *   d = raw + bias[h]                       (bias may be NULL)
+ *   d = softplus(d) = log(1 + exp(d))       if softplus
+ *   d = min(max(d, lo), hi)                 if clamp
+ *   dt_decay = d
+ *   dt_input = (exp(d A) - 1) / A           if zoh (A != 0; d when A == 0)
+ *            = d                            otherwise
+ * The ZOH factor is the scalar-A form of the zero-order-hold B-bar of
+ * "3.3 Hardware-Aware ..." section 2.1: integrating S' = A S + B x over a step
+ * of length d with x held constant gives exp(dA) S + (exp(dA) - 1)/A B x.
+ */
+int ssd_oracle_dt_frontend(int64_t n, int64_t H, const double* raw, const double* A, const double* bias,
+                           int softplus, int zoh, int clamp, double lo, double hi,
+                           double* dt_decay, double* dt_input) {
+    if (n < 0 || H <= 0) return -1;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t h = 0; h < H; ++h) {
+            double d = raw[r * H + h];
+            if (bias) d = d + bias[h];
+            if (softplus) d = d > 0.0 ? d + log1p(exp(-d)) : log1p(exp(d));
+            if (clamp) d = d < lo ? lo : (d > hi ? hi : d);
+            dt_decay[r * H + h] = d;
+            double in = d;
+            if (zoh && A[h] != 0.0) in = expm1(d * A[h]) / A[h];
+            dt_input[r * H + h] = in;
+        }
+    return 0;
+}
+
+/*
  * In-chunk cumulative sum (devotd.net cuTile page, section 2, first kernel):
  * for chunk c and in-chunk position i, cs_log2 = log2(e) * sum_{k<=i} dt*A over
- * the chunk's tokens; positions past L count as dt = 0.  dt_t receives dt
- * itself (0 past L).  Both outputs are (b,H,nC,Q).
+ * the chunk's tokens; positions past L count as dt = 0.  dt_t receives the
+ * input step: dt itself, or dt_in when given (0 past L).  Both outputs are
+ * (b,H,nC,Q).
  */
 int ssd_oracle_chunk_cumsum(int64_t b, int64_t L, int64_t H, int64_t Q,
-                            const double* dt, const double* A,
+                            const double* dt, const double* dt_in, const double* A,
                             double* dt_t, double* cs_log2) {
     if (b < 0 || L < 0 || H <= 0 || Q <= 0) return -1;
     int64_t nC = (L + Q - 1) / Q;
@@ -181,7 +222,7 @@ int ssd_oracle_chunk_cumsum(int64_t b, int64_t L, int64_t H, int64_t Q,
                     run += d * A[h];
                     int64_t o = ((bb * H + h) * nC + c) * Q + i;
                     cs_log2[o] = run * LOG2E_D;
-                    if (dt_t) dt_t[o] = d;
+                    if (dt_t) dt_t[o] = t < L && dt_in ? dt_in[(bb * L + t) * H + h] : d;
                 }
             }
     return 0;
@@ -242,7 +283,7 @@ int ssd_oracle_chunk_scan(int64_t b, int64_t L, int64_t H, int64_t P, int64_t N,
         int64_t t1 = (c + 1) * Q < L ? (c + 1) * Q : L;
         for (int64_t t = c * Q; t < t1; ++t) {
             int64_t bt = bb * L + t;
-            token_update(P, N, S, dt[bt * H + h], A[h], x + (bt * H + h) * P,
+            token_update(P, N, S, dt[bt * H + h], dt[bt * H + h], A[h], x + (bt * H + h) * P,
                          B + (bt * G + g) * N, C + (bt * G + g) * N,
                          D ? D[h] : 0.0, D != NULL, y + (bt * H + h) * P);
         }

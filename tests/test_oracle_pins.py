@@ -275,11 +275,100 @@ def pin_groups():
         assert _rel(rg["final"], r["final"][:, hs]) < TIGHT
 
 
+# ---------------------------------------------------------------------------
+# dt front-end: bias + softplus + clamp, and the zero-order-hold input factor
+# ---------------------------------------------------------------------------
+
+
+def pin_frontend_softplus():
+    """softplus(raw + bias) equals NumPy's logaddexp(0, .) (a library routine), including large
+    positive and negative arguments; the clamp bounds it; without ZOH the input step is the step."""
+    rng = np.random.default_rng(40)
+    raw = np.concatenate([rng.normal(0.0, 3.0, (50, 4)), np.array([[-60.0, -20.0, 20.0, 60.0]])])
+    bias = rng.normal(0.0, 1.0, 4)
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), 4))
+    dec, inp = oracle.dt_frontend(raw, A, bias, softplus=True)
+    want = np.logaddexp(0.0, raw + bias)
+    assert np.max(np.abs(dec - want) / want) < 1e-14
+    assert np.array_equal(inp, dec)
+    dec_c, _ = oracle.dt_frontend(raw, A, bias, softplus=True, clamp=(1e-3, 0.1))
+    assert dec_c.min() >= 1e-3 and dec_c.max() <= 0.1
+    inside = (want > 1e-3) & (want < 0.1)
+    assert inside.any() and np.array_equal(dec_c[inside], dec[inside])
+    dec_n, _ = oracle.dt_frontend(raw, A)  # no bias, no softplus: the raw step itself
+    assert np.array_equal(dec_n, raw)
+
+
+def pin_zoh_factor_matrix_exponential():
+    """The ZOH input factor is the top-right entry of expm([[A, 1], [0, 0]] d) (the augmented-matrix
+    construction of a zero-order hold), computed by scipy.linalg.expm; small steps tend to d."""
+    from scipy.linalg import expm
+
+    rng = np.random.default_rng(41)
+    d = np.exp(rng.uniform(math.log(1e-4), math.log(2.0), (6, 5)))
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), 5))
+    dec, inp = oracle.dt_frontend(d, A, zoh=True)
+    assert np.array_equal(dec, d)
+    for r in range(d.shape[0]):
+        for h in range(d.shape[1]):
+            m = expm(np.array([[A[h], 1.0], [0.0, 0.0]]) * d[r, h])
+            assert abs(inp[r, h] - m[0, 1]) <= 1e-12 * abs(m[0, 1])
+    tiny = np.full((1, 5), 1e-9)
+    _, inp_t = oracle.dt_frontend(tiny, A, zoh=True)
+    assert np.max(np.abs(inp_t / tiny - 1.0)) < 1e-7
+
+
+def pin_zoh_forward_solves_the_ode():
+    """With the ZOH input step the recurrence is the exact solution of S' = A S + B x with x, B held
+    over each token's interval: one state (P = N = 1) integrated by scipy's solve_ivp."""
+    from scipy.integrate import solve_ivp
+
+    rng = np.random.default_rng(42)
+    L = 12
+    A = np.array([-3.0])
+    d = np.exp(rng.uniform(math.log(1e-2), math.log(0.5), (1, L, 1)))
+    x = rng.normal(size=(1, L, 1, 1))
+    B = rng.normal(size=(1, L, 1, 1))
+    C = rng.normal(size=(1, L, 1, 1))
+    h0 = np.array([[[[0.7]]]])
+    dec, inp = oracle.dt_frontend(d, A, zoh=True)
+    r = oracle.forward(x, dec, A, B, C, None, h0, dt_in=inp)
+    s = 0.7
+    for t in range(L):
+        sol = solve_ivp(lambda _, v: A[0] * v + B[0, t, 0, 0] * x[0, t, 0, 0], (0.0, d[0, t, 0]), [s],
+                        rtol=1e-12, atol=1e-14)
+        s = sol.y[0, -1]
+        assert abs(r["y"][0, t, 0, 0] - C[0, t, 0, 0] * s) < 1e-9
+    assert abs(r["final"][0, 0, 0, 0] - s) < 1e-9
+
+
+def pin_input_step_only_scales_the_input():
+    """A separate input step leaves the decay alone: with x = 0 the result ignores dt_in, and with
+    h0 = 0 scaling dt_in by k scales y and the final state by k (linearity in the input term)."""
+    fi = _small(seed=43)
+    r1 = _fwd(fi)
+    r2 = _fwd(fi, dt_in=fi.dt * 2.0)
+    fi0 = _small(seed=43)
+    fi0.x[:] = 0.0
+    assert _rel(_fwd(fi0, dt_in=fi0.dt * 5.0)["final"], _fwd(fi0)["final"]) < TIGHT
+    fih = _small(seed=43, h0=False)
+    ra, rb = _fwd(fih), _fwd(fih, dt_in=fih.dt * 3.0)
+    assert _rel(rb["final"], 3.0 * ra["final"]) < TIGHT
+    d_x = (fih.D[None, None, :, None] * fih.x)
+    assert _rel(rb["y"] - d_x, 3.0 * (ra["y"] - d_x)) < TIGHT
+    assert _rel(r1["final"], r2["final"]) > 1e-3  # it does change the result
+    dtt, cs = oracle.chunk_cumsum(fi.dt, fi.A, 16, dt_in=fi.dt * 2.0)
+    dtt0, cs0 = oracle.chunk_cumsum(fi.dt, fi.A, 16)
+    assert np.array_equal(cs, cs0) and np.array_equal(dtt, 2.0 * dtt0)
+
+
 PINS = [
     pin_decay_closed_form, pin_geometric_series, pin_lti_convolution, pin_single_token,
     pin_materialized_and_quadratic, pin_chunk_decomposition, pin_staged_calls,
     pin_cumsum_worked_example, pin_dt_zero, pin_split_resume, pin_step_equals_forward,
     pin_step_inputs_roundtrip, pin_linearity, pin_head_permutation, pin_groups,
+    pin_frontend_softplus, pin_zoh_factor_matrix_exponential, pin_zoh_forward_solves_the_ode,
+    pin_input_step_only_scales_the_input,
 ]
 
 
@@ -302,7 +391,7 @@ def test_zero_length_sequence():
 
 MUTANTS = {
     "decay_sign": ("double a = exp(dt * A);", "double a = exp(-dt * A);"),
-    "input_without_dt": ("double u = dt * x[p];", "double u = x[p];"),
+    "input_without_dt": ("double u = dtu * x[p];", "double u = x[p];"),
     "B_for_C_in_update": ("row[n] = a * row[n] + u * B[n];", "row[n] = a * row[n] + u * C[n];"),
     "dropped_D": ("y[p] = acc + (has_D ? Dh * x[p] : 0.0);", "y[p] = acc;"),
     "output_before_decay": ("double a = exp(dt * A);", "double a = 1.0;"),
@@ -317,6 +406,13 @@ MUTANTS = {
         "for (int64_t e = 0; e < PN; ++e) S[e] = decay * S[e] + tmp[e];\n                if (chunk_start) memcpy(chunk_start + o, S, sizeof(double) * PN);",
     ),
     "chunk_start_off_by_one": ("if (chunk_start && t % chunk == 0)", "if (chunk_start && t % chunk == 1)"),
+    "frontend_bias_dropped": ("if (bias) d = d + bias[h];", ""),
+    "softplus_branch": ("d = d > 0.0 ? d + log1p(exp(-d)) : log1p(exp(d));",
+                        "d = d > 0.0 ? log1p(exp(-d)) : log1p(exp(d));"),
+    "zoh_without_division": ("in = expm1(d * A[h]) / A[h];", "in = expm1(d * A[h]);"),
+    "decay_from_input_step": ("double a = exp(dt * A);", "double a = exp(dtu * A);"),
+    "cumsum_ignores_input_step": ("if (dt_t) dt_t[o] = t < L && dt_in ? dt_in[(bb * L + t) * H + h] : d;",
+                                  "if (dt_t) dt_t[o] = d;"),
 }
 
 
