@@ -90,6 +90,31 @@ typedef struct {
 } ssd_dims;
 
 /*
+ * Optional dt front-end of the *_ex calls, applied wherever the kernels read
+ * dt (the plain calls behave as if it were all zero: dt is the final step).
+ * For head h, with d the raw dt:
+ *     d <- d + dt_bias[h]                    (dt_bias: (H) float32, or NULL)
+ *     d <- log(1 + exp(d))                   if softplus
+ *     d <- min(max(d, dt_min), dt_max)       if clamp
+ * d is then the decay step (exp(d A)).  The input term uses d, or with zoh
+ * the zero-order-hold factor (exp(d A) - 1) / A (d where A == 0): the
+ * scalar-A form of the ZOH discretisation B-bar in "3.3 Hardware-Aware
+ * algorithms and GPU memory hierarchy optimisation", section 2.1.  In
+ * ssd_chunk_cumsum_ex, dt_t receives that input step and dA_cs_log2 sums the
+ * decay steps, so ssd_chunk_state and ssd_chunk_scan need no change.
+ * reserved must be 0; clamp needs finite dt_min <= dt_max (SSD_ERR_SHAPE
+ * otherwise); dt_bias must not overlap any output.
+ */
+typedef struct {
+    const float* dt_bias; /* (H) float32 device pointer, or NULL */
+    int32_t softplus;     /* nonzero: d <- softplus(d) */
+    int32_t zoh;          /* nonzero: zero-order-hold input step (exp(d A) - 1) / A */
+    int32_t clamp;        /* nonzero: d <- min(max(d, dt_min), dt_max) after the softplus */
+    int32_t reserved;     /* must be 0 */
+    float dt_min, dt_max;
+} ssd_dt_frontend;
+
+/*
  * In-chunk cumulative sum (cuTile page, section 2, first kernel and its
  * listing): for chunk c and position i < Q,
  *     dA_cs_log2[b,h,c,i] = log2(e) * sum_{k<=i} dt[b,cQ+k,h] * A[h]
@@ -134,6 +159,10 @@ ssd_status ssd_chunk_scan(const ssd_dims* dims, const void* x, const void* B, co
                           const float* chunk_start_states, const float* D,
                           void* y, void* stream);
 
+/* ssd_chunk_cumsum with the dt front-end above (fe may be NULL). */
+ssd_status ssd_chunk_cumsum_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, const void* dt,
+                               const float* A, float* dt_t, float* dA_cs_log2, void* stream);
+
 /* Bytes of device workspace ssd_forward needs for these dims (0 on invalid dims). */
 size_t ssd_forward_workspace_bytes(const ssd_dims* dims);
 
@@ -151,6 +180,12 @@ ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, cons
                        void* y, float* final_state, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* ssd_forward with the dt front-end above (fe may be NULL); same workspace. */
+ssd_status ssd_forward_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, const void* x, const void* dt,
+                          const float* A, const void* B, const void* C, const float* D,
+                          const float* h0, void* y, float* final_state, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /*
  * O(1) decode step for one token per (b, h), in place on state (dims->seqlen
  * must be 1; dims->chunk is ignored):
@@ -160,6 +195,11 @@ ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, cons
 ssd_status ssd_step(const ssd_dims* dims, float* state, const void* x, const void* dt,
                     const float* A, const void* B, const void* C, const float* D,
                     void* y, void* stream);
+
+/* ssd_step with the dt front-end above (fe may be NULL). */
+ssd_status ssd_step_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, float* state, const void* x,
+                       const void* dt, const float* A, const void* B, const void* C, const float* D,
+                       void* y, void* stream);
 
 /*
  * K decode steps in one call, over inputs that are all on the device before
@@ -182,6 +222,11 @@ ssd_status ssd_step(const ssd_dims* dims, float* state, const void* x, const voi
 ssd_status ssd_step_multi(const ssd_dims* dims, float* state, const void* x, const void* dt,
                           const float* A, const void* B, const void* C, const float* D,
                           void* y, void* stream);
+
+/* ssd_step_multi with the dt front-end above (fe may be NULL). */
+ssd_status ssd_step_multi_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, float* state,
+                             const void* x, const void* dt, const float* A, const void* B,
+                             const void* C, const float* D, void* y, void* stream);
 
 /* Static text for a status code. */
 const char* ssd_status_string(ssd_status status);

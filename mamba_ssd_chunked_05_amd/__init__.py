@@ -28,8 +28,9 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "SsdError", "load", "library_path", "forward", "forward_workspace_bytes", "step", "chunk_cumsum",
-    "chunk_state", "state_passing", "chunk_scan", "query_config", "abi_version", "Dims",
+    "SsdError", "load", "library_path", "forward", "forward_workspace_bytes", "step", "step_multi", "chunk_cumsum",
+    "chunk_state", "state_passing", "chunk_scan", "query_config", "abi_version", "Dims", "DtFrontend",
+    "Frontend",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +56,33 @@ class Dims(ctypes.Structure):
     ]
 
 
+class DtFrontend(ctypes.Structure):
+    _fields_ = [
+        ("dt_bias", ctypes.c_void_p), ("softplus", ctypes.c_int32), ("zoh", ctypes.c_int32),
+        ("clamp", ctypes.c_int32), ("reserved", ctypes.c_int32), ("dt_min", ctypes.c_float),
+        ("dt_max", ctypes.c_float),
+    ]
+
+
+class Frontend:
+    """The dt front-end of the *_ex calls: ``dt_bias`` (H) float32 GPU tensor or None, ``softplus``,
+    ``zoh`` (zero-order-hold input step) and ``clamp`` = (dt_min, dt_max) or None."""
+
+    def __init__(self, dt_bias: Optional[torch.Tensor] = None, softplus: bool = False, zoh: bool = False,
+                 clamp: Optional[Tuple[float, float]] = None):
+        self.dt_bias, self.softplus, self.zoh, self.clamp = dt_bias, softplus, zoh, clamp
+
+    def _c(self, H: int) -> DtFrontend:
+        _dev(self.dt_bias, "dt_bias", torch.float32, (H,))
+        lo, hi = self.clamp if self.clamp is not None else (0.0, 0.0)
+        return DtFrontend(_ptr(self.dt_bias), int(bool(self.softplus)), int(bool(self.zoh)),
+                          int(self.clamp is not None), 0, float(lo), float(hi))
+
+
+def _fe(frontend: Optional[Frontend], H: int):
+    return None if frontend is None else ctypes.byref(frontend._c(H))
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -67,7 +95,7 @@ def load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"libssd.so is not built ({_LIB_PATH}); run mamba_ssd_chunked_05_amd/build.py")
     lib = ctypes.CDLL(_LIB_PATH)
-    vp, dp = ctypes.c_void_p, ctypes.POINTER(Dims)
+    vp, dp, fp = ctypes.c_void_p, ctypes.POINTER(Dims), ctypes.POINTER(DtFrontend)
     sig = {
         "ssd_chunk_cumsum": [dp, vp, vp, vp, vp, vp],
         "ssd_chunk_state": [dp, vp, vp, vp, vp, vp, vp],
@@ -76,6 +104,10 @@ def load():
         "ssd_forward": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "ssd_step": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_step_multi": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "ssd_chunk_cumsum_ex": [dp, fp, vp, vp, vp, vp, vp],
+        "ssd_forward_ex": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "ssd_step_ex": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "ssd_step_multi_ex": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_query_config": [dp] + [ctypes.POINTER(ctypes.c_int)] * 4,
     }
     for name, args in sig.items():
@@ -190,8 +222,9 @@ def forward_workspace_bytes(x: torch.Tensor, B: torch.Tensor, chunk: int = 0) ->
 
 
 def forward(x, dt, A, B, C, D=None, h0=None, *, chunk: int = 0, y=None, final_state=None,
-            workspace=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """One-shot SSD forward on the current stream; returns (y, final_state)."""
+            workspace=None, frontend: Optional[Frontend] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One-shot SSD forward on the current stream; returns (y, final_state).  ``frontend`` (optional)
+    turns the raw dt into the step (bias, softplus, clamp, zero-order-hold input step)."""
     lib = load()
     d = _fwd_dims(x, B, chunk)
     _check_fwd_inputs(x, dt, A, B, C, D, h0)
@@ -207,13 +240,14 @@ def forward(x, dt, A, B, C, D=None, h0=None, *, chunk: int = 0, y=None, final_st
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
     _dev(workspace, "workspace", torch.uint8)
-    st = lib.ssd_forward(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
-                         _ptr(y), _ptr(final_state), _ptr(workspace), workspace.numel(), _stream(x))
+    st = lib.ssd_forward_ex(ctypes.byref(d), _fe(frontend, H), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                            _ptr(D), _ptr(h0), _ptr(y), _ptr(final_state), _ptr(workspace), workspace.numel(),
+                            _stream(x))
     _check(st, "ssd_forward")
     return y, final_state
 
 
-def step(state, x, dt, A, B, C, D=None, *, y=None) -> torch.Tensor:
+def step(state, x, dt, A, B, C, D=None, *, y=None, frontend: Optional[Frontend] = None) -> torch.Tensor:
     """One decode token per (b, h); ``state`` (b, H, P, N) float32 is updated in place."""
     lib = load()
     b, H, P, N = state.shape
@@ -229,13 +263,13 @@ def step(state, x, dt, A, B, C, D=None, *, y=None) -> torch.Tensor:
         y = torch.empty_like(x)
     _dev(y, "y", x.dtype, (b, H, P))
     d = _dims(b, 1, H, P, N, G, 0, _io_code(x))
-    st = lib.ssd_step(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                      _ptr(y), _stream(x))
+    st = lib.ssd_step_ex(ctypes.byref(d), _fe(frontend, H), _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                         _ptr(C), _ptr(D), _ptr(y), _stream(x))
     _check(st, "ssd_step")
     return y
 
 
-def step_multi(state, x, dt, A, B, C, D=None, *, y=None) -> torch.Tensor:
+def step_multi(state, x, dt, A, B, C, D=None, *, y=None, frontend: Optional[Frontend] = None) -> torch.Tensor:
     """K pre-staged decode steps: x (b, K, H, P), dt (b, K, H), B, C (b, K, G, N); ``state``
     (b, H, P, N) float32 is updated in place; returns y (b, K, H, P)."""
     lib = load()
@@ -253,13 +287,13 @@ def step_multi(state, x, dt, A, B, C, D=None, *, y=None) -> torch.Tensor:
         y = torch.empty_like(x)
     _dev(y, "y", x.dtype, (b, K, H, P))
     d = _dims(b, K, H, P, N, G, 0, _io_code(x))
-    st = lib.ssd_step_multi(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                            _ptr(y), _stream(x))
+    st = lib.ssd_step_multi_ex(ctypes.byref(d), _fe(frontend, H), _ptr(state), _ptr(x), _ptr(dt), _ptr(A),
+                               _ptr(B), _ptr(C), _ptr(D), _ptr(y), _stream(x))
     _check(st, "ssd_step_multi")
     return y
 
 
-def chunk_cumsum(dt, A, chunk: int):
+def chunk_cumsum(dt, A, chunk: int, *, frontend: Optional[Frontend] = None):
     lib = load()
     b, L, H = dt.shape
     _dev(dt, "dt")
@@ -268,8 +302,8 @@ def chunk_cumsum(dt, A, chunk: int):
     dt_t = torch.empty((b, H, nC, chunk), dtype=torch.float32, device=dt.device)
     cs = torch.empty_like(dt_t)
     d = _dims(b, L, H, 16, 16, 1, chunk, _io_code(dt))
-    _check(lib.ssd_chunk_cumsum(ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(dt_t), _ptr(cs), _stream(dt)),
-           "ssd_chunk_cumsum")
+    _check(lib.ssd_chunk_cumsum_ex(ctypes.byref(d), _fe(frontend, H), _ptr(dt), _ptr(A), _ptr(dt_t), _ptr(cs),
+                                   _stream(dt)), "ssd_chunk_cumsum")
     return dt_t, cs
 
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -122,6 +123,19 @@ ssd_status no_alias(const Span& out, const Span* ins, int n) {
     return SSD_OK;
 }
 
+// the dt front-end of the *_ex calls (NULL: the raw dt is the step)
+ssd_status front_end(const ssd_dt_frontend* f, int64_t H, ssd::DtFront* out, Span* sbias) {
+    *out = ssd::DtFront{nullptr, 0, 0, 0, 0.0f, 0.0f};
+    *sbias = Span{nullptr, 0, "dt_bias"};
+    if (!f) return SSD_OK;
+    if (f->reserved != 0) return fail(SSD_ERR_SHAPE, "ssd_dt_frontend.reserved must be 0");
+    if (f->clamp && !(std::isfinite(f->dt_min) && std::isfinite(f->dt_max) && f->dt_min <= f->dt_max))
+        return fail(SSD_ERR_SHAPE, "the dt clamp needs finite dt_min <= dt_max");
+    *out = ssd::DtFront{f->dt_bias, f->softplus != 0, f->zoh != 0, f->clamp != 0, f->dt_min, f->dt_max};
+    *sbias = Span{f->dt_bias, f->dt_bias ? (size_t)H * 4 : 0, "dt_bias"};
+    return SSD_OK;
+}
+
 #define SSD_TRY(expr)                       \
     do {                                    \
         ssd_status _st = (expr);            \
@@ -205,25 +219,33 @@ ssd_status ssd_query_config(const ssd_dims* dims, int* chunk, int* tile_p, int* 
     }
 }
 
-ssd_status ssd_chunk_cumsum(const ssd_dims* dims, const void* dt, const float* A, float* dt_t, float* dA_cs_log2,
-                            void* stream) {
+ssd_status ssd_chunk_cumsum_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, const void* dt, const float* A,
+                               float* dt_t, float* dA_cs_log2, void* stream) {
     try {
         ssd::Shape s;
         SSD_TRY(check_dims(dims, Need::kCumsum, &s));
         Sizes z = sizes(s);
+        ssd::DtFront f;
+        Span sbias;
+        SSD_TRY(front_end(fe, s.H, &f, &sbias));
         Span sdt{dt, z.dt, "dt"}, sA{A, z.A, "A"}, sdtt{dt_t, z.cs, "dt_t"}, scs{dA_cs_log2, z.cs, "dA_cs_log2"};
         for (const Span& p : {sdt, sA, sdtt, scs}) SSD_TRY(need_ptr(p));
-        Span ins[] = {sdt, sA};
-        SSD_TRY(no_alias(sdtt, ins, 2));
-        SSD_TRY(no_alias(scs, ins, 2));
+        Span ins[] = {sdt, sA, sbias};
+        SSD_TRY(no_alias(sdtt, ins, 3));
+        SSD_TRY(no_alias(scs, ins, 3));
         Span o1[] = {sdtt};
         SSD_TRY(no_alias(scs, o1, 1));
-        hipError_t e = ssd::launch_chunk_cumsum(s, dt, A, dt_t, dA_cs_log2, (hipStream_t)stream);
+        hipError_t e = ssd::launch_chunk_cumsum(s, f, dt, A, dt_t, dA_cs_log2, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "ssd_chunk_cumsum");
         return ok();
     } catch (...) {
         return fail(SSD_ERR_HIP, "internal error");
     }
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_dims* dims, const void* dt, const float* A, float* dt_t, float* dA_cs_log2,
+                            void* stream) {
+    return ssd_chunk_cumsum_ex(dims, nullptr, dt, A, dt_t, dA_cs_log2, stream);
 }
 
 ssd_status ssd_chunk_state(const ssd_dims* dims, const void* x, const void* B, const float* dt_t,
@@ -298,14 +320,17 @@ size_t ssd_forward_workspace_bytes(const ssd_dims* dims) {
     }
 }
 
-ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, const float* A, const void* B,
-                       const void* C, const float* D, const float* h0, void* y, float* final_state,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+ssd_status ssd_forward_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, const void* x, const void* dt,
+                          const float* A, const void* B, const void* C, const float* D, const float* h0, void* y,
+                          float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
     try {
         ssd::Shape s;
         SSD_TRY(check_dims(dims, Need::kForward, &s));
         Sizes z = sizes(s);
         FwdLayout f = fwd_layout(s);
+        ssd::DtFront dfe;
+        Span sbias;
+        SSD_TRY(front_end(fe, s.H, &dfe, &sbias));
         Span sx{x, z.x, "x"}, sdt{dt, z.dt, "dt"}, sA{A, z.A, "A"}, sB{B, z.bc, "B"}, sC{C, z.bc, "C"},
             sD{D, D ? z.A : 0, "D"}, sh0{h0, h0 ? z.hstate : 0, "h0"}, sy{y, z.x, "y"},
             sfin{final_state, z.hstate, "final_state"}, sws{workspace, f.total, "workspace"};
@@ -317,14 +342,14 @@ ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, cons
             if (reinterpret_cast<uintptr_t>(workspace) % 256)
                 return fail(SSD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
         }
-        Span ins[] = {sx, sdt, sA, sB, sC, sD, sh0};
-        SSD_TRY(no_alias(sy, ins, 7));
-        SSD_TRY(no_alias(sfin, ins, 7));
+        Span ins[] = {sx, sdt, sA, sB, sC, sD, sh0, sbias};
+        SSD_TRY(no_alias(sy, ins, 8));
+        SSD_TRY(no_alias(sfin, ins, 8));
         Span o1[] = {sy};
         SSD_TRY(no_alias(sfin, o1, 1));
         if (s.b > 0 && s.L > 0) {
-            Span all[] = {sx, sdt, sA, sB, sC, sD, sh0, sy, sfin};
-            SSD_TRY(no_alias(sws, all, 9));
+            Span all[] = {sx, sdt, sA, sB, sC, sD, sh0, sy, sfin, sbias};
+            SSD_TRY(no_alias(sws, all, 10));
         }
         hipStream_t st = (hipStream_t)stream;
         if (s.b == 0) return ok();
@@ -333,7 +358,7 @@ ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, cons
                 hipError_t e = ssd::launch_state_passing(s, nullptr, nullptr, h0, final_state, st);
                 return e == hipSuccess ? ok() : hip_fail(e, "ssd_forward/state_passing");
             }
-            hipError_t e = ssd::launch_forward_fast(s, x, dt, A, B, C, D, h0, y, final_state, workspace, st);
+            hipError_t e = ssd::launch_forward_fast(s, dfe, x, dt, A, B, C, D, h0, y, final_state, workspace, st);
             return e == hipSuccess ? ok() : hip_fail(e, "ssd_forward (fast path)");
         }
         char* ws = static_cast<char*>(workspace);
@@ -342,7 +367,7 @@ ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, cons
         float* states = reinterpret_cast<float*>(ws + f.states);
         hipError_t e;
         if (s.nC > 0) {
-            e = ssd::launch_chunk_cumsum(s, dt, A, dt_t, cs, st);
+            e = ssd::launch_chunk_cumsum(s, dfe, dt, A, dt_t, cs, st);
             if (e != hipSuccess) return hip_fail(e, "ssd_forward/cumsum");
             e = ssd::launch_chunk_state(s, x, B, dt_t, cs, states, st);
             if (e != hipSuccess) return hip_fail(e, "ssd_forward/chunk_state");
@@ -359,22 +384,31 @@ ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, cons
     }
 }
 
-ssd_status ssd_step(const ssd_dims* dims, float* state, const void* x, const void* dt, const float* A,
-                    const void* B, const void* C, const float* D, void* y, void* stream) {
+ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, const float* A, const void* B,
+                       const void* C, const float* D, const float* h0, void* y, float* final_state,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    return ssd_forward_ex(dims, nullptr, x, dt, A, B, C, D, h0, y, final_state, workspace, workspace_bytes, stream);
+}
+
+ssd_status ssd_step_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, float* state, const void* x, const void* dt,
+                       const float* A, const void* B, const void* C, const float* D, void* y, void* stream) {
     try {
         ssd::Shape s;
         SSD_TRY(check_dims(dims, Need::kStep, &s));
+        ssd::DtFront dfe;
+        Span sbias;
+        SSD_TRY(front_end(fe, s.H, &dfe, &sbias));
         const size_t e = esz(s);
         Span sst{state, (size_t)(s.b * s.H * s.P * s.N) * 4, "state"}, sx{x, (size_t)(s.b * s.H * s.P) * e, "x"},
             sdt{dt, (size_t)(s.b * s.H) * e, "dt"}, sA{A, (size_t)s.H * 4, "A"}, sB{B, (size_t)(s.b * s.G * s.N) * e, "B"},
             sC{C, (size_t)(s.b * s.G * s.N) * e, "C"}, sD{D, D ? (size_t)s.H * 4 : 0, "D"},
             sy{y, (size_t)(s.b * s.H * s.P) * e, "y"};
         for (const Span& p : {sst, sx, sdt, sA, sB, sC, sy}) SSD_TRY(need_ptr(p));
-        Span ins[] = {sx, sdt, sA, sB, sC, sD};
-        SSD_TRY(no_alias(sst, ins, 6));
-        Span ins2[] = {sx, sdt, sA, sB, sC, sD, sst};
-        SSD_TRY(no_alias(sy, ins2, 7));
-        hipError_t he = ssd::launch_step(s, state, x, dt, A, B, C, D, y, (hipStream_t)stream);
+        Span ins[] = {sx, sdt, sA, sB, sC, sD, sbias};
+        SSD_TRY(no_alias(sst, ins, 7));
+        Span ins2[] = {sx, sdt, sA, sB, sC, sD, sst, sbias};
+        SSD_TRY(no_alias(sy, ins2, 8));
+        hipError_t he = ssd::launch_step(s, dfe, state, x, dt, A, B, C, D, y, (hipStream_t)stream);
         if (he != hipSuccess) return hip_fail(he, "ssd_step");
         return ok();
     } catch (...) {
@@ -382,11 +416,20 @@ ssd_status ssd_step(const ssd_dims* dims, float* state, const void* x, const voi
     }
 }
 
-ssd_status ssd_step_multi(const ssd_dims* dims, float* state, const void* x, const void* dt, const float* A,
-                          const void* B, const void* C, const float* D, void* y, void* stream) {
+ssd_status ssd_step(const ssd_dims* dims, float* state, const void* x, const void* dt, const float* A,
+                    const void* B, const void* C, const float* D, void* y, void* stream) {
+    return ssd_step_ex(dims, nullptr, state, x, dt, A, B, C, D, y, stream);
+}
+
+ssd_status ssd_step_multi_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, float* state, const void* x,
+                             const void* dt, const float* A, const void* B, const void* C, const float* D, void* y,
+                             void* stream) {
     try {
         ssd::Shape s;
         SSD_TRY(check_dims(dims, Need::kStepMulti, &s));
+        ssd::DtFront dfe;
+        Span sbias;
+        SSD_TRY(front_end(fe, s.H, &dfe, &sbias));
         const size_t e = esz(s);
         const size_t K = (size_t)s.L;
         Span sst{state, (size_t)(s.b * s.H * s.P * s.N) * 4, "state"},
@@ -395,19 +438,24 @@ ssd_status ssd_step_multi(const ssd_dims* dims, float* state, const void* x, con
             sC{C, (size_t)(s.b * s.G * s.N) * K * e, "C"}, sD{D, D ? (size_t)s.H * 4 : 0, "D"},
             sy{y, (size_t)(s.b * s.H * s.P) * K * e, "y"};
         for (const Span& p : {sst, sx, sdt, sA, sB, sC, sy}) SSD_TRY(need_ptr(p));
-        Span ins[] = {sx, sdt, sA, sB, sC, sD};
-        SSD_TRY(no_alias(sst, ins, 6));
-        Span ins2[] = {sx, sdt, sA, sB, sC, sD, sst};
-        SSD_TRY(no_alias(sy, ins2, 7));
+        Span ins[] = {sx, sdt, sA, sB, sC, sD, sbias};
+        SSD_TRY(no_alias(sst, ins, 7));
+        Span ins2[] = {sx, sdt, sA, sB, sC, sD, sst, sbias};
+        SSD_TRY(no_alias(sy, ins2, 8));
         for (const Span& p : {sst, sx, sB, sC, sy})
             if (reinterpret_cast<uintptr_t>(p.p) % 16)
                 return fail(SSD_ERR_UNSUPPORTED, "%s must be 16-byte aligned", p.name);
-        hipError_t he = ssd::launch_step_multi(s, state, x, dt, A, B, C, D, y, (hipStream_t)stream);
+        hipError_t he = ssd::launch_step_multi(s, dfe, state, x, dt, A, B, C, D, y, (hipStream_t)stream);
         if (he != hipSuccess) return hip_fail(he, "ssd_step_multi");
         return ok();
     } catch (...) {
         return fail(SSD_ERR_HIP, "internal error");
     }
+}
+
+ssd_status ssd_step_multi(const ssd_dims* dims, float* state, const void* x, const void* dt, const float* A,
+                          const void* B, const void* C, const float* D, void* y, void* stream) {
+    return ssd_step_multi_ex(dims, nullptr, state, x, dt, A, B, C, D, y, stream);
 }
 
 }  // extern "C"

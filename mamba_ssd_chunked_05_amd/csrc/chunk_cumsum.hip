@@ -17,9 +17,10 @@
 namespace ssd {
 
 template <class T>
-__global__ void __launch_bounds__(256) chunk_cumsum_kernel(const T* __restrict__ dt, const float* __restrict__ A,
-                                                           float* __restrict__ dt_t, float* __restrict__ cs,
-                                                           int64_t L, int H, int Q, int64_t nC, int64_t nwaves) {
+__global__ void __launch_bounds__(256) chunk_cumsum_kernel(DtFront fe, const T* __restrict__ dt,
+                                                           const float* __restrict__ A, float* __restrict__ dt_t,
+                                                           float* __restrict__ cs, int64_t L, int H, int Q, int64_t nC,
+                                                           int64_t nwaves) {
     const int lane = threadIdx.x & 63;
     const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (wid >= nwaves) return;
@@ -32,7 +33,7 @@ __global__ void __launch_bounds__(256) chunk_cumsum_kernel(const T* __restrict__
     for (int q0 = 0; q0 < Q; q0 += 512) {
         const int qb = Q - q0 < 512 ? Q - q0 : 512;
         const int E = (qb + 63) / 64;  // positions per lane in this block (<= 8)
-        float v[8], d[8];
+        float v[8], d[8];  // cumulative decay, input step
         float run = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -41,8 +42,9 @@ __global__ void __launch_bounds__(256) chunk_cumsum_kernel(const T* __restrict__
             if (e < E) {
                 const int i = lane * E + e;
                 const int64_t t = c * Q + q0 + i;
-                if (i < qb && t < L) d[e] = to_f32(dt[(b * L + t) * H + h]);
-                run += d[e] * a;
+                float dec = 0.0f;
+                if (i < qb && t < L) dt_front(fe, h, a, to_f32(dt[(b * L + t) * H + h]), dec, d[e]);
+                run += dec * a;
                 v[e] = run;
             }
         }
@@ -68,16 +70,16 @@ __global__ void __launch_bounds__(256) chunk_cumsum_kernel(const T* __restrict__
     }
 }
 
-hipError_t launch_chunk_cumsum(const Shape& s, const void* dt, const float* A, float* dt_t, float* cs,
-                               hipStream_t st) {
+hipError_t launch_chunk_cumsum(const Shape& s, const DtFront& fe, const void* dt, const float* A, float* dt_t,
+                               float* cs, hipStream_t st) {
     const int64_t nwaves = s.b * s.H * s.nC;
     if (nwaves == 0) return hipSuccess;
     dim3 grid((unsigned)((nwaves + 3) / 4)), block(256);
     if (s.io == 1)
-        hipLaunchKernelGGL(chunk_cumsum_kernel<bf16>, grid, block, 0, st, (const bf16*)dt, A, dt_t, cs, s.L,
+        hipLaunchKernelGGL(chunk_cumsum_kernel<bf16>, grid, block, 0, st, fe, (const bf16*)dt, A, dt_t, cs, s.L,
                            (int)s.H, (int)s.Q, s.nC, nwaves);
     else
-        hipLaunchKernelGGL(chunk_cumsum_kernel<float>, grid, block, 0, st, (const float*)dt, A, dt_t, cs, s.L,
+        hipLaunchKernelGGL(chunk_cumsum_kernel<float>, grid, block, 0, st, fe, (const float*)dt, A, dt_t, cs, s.L,
                            (int)s.H, (int)s.Q, s.nC, nwaves);
     return hipGetLastError();
 }

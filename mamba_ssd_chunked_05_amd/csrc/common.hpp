@@ -38,6 +38,19 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf1
 // hardware 2^x (v_exp_f32); exact limits: 2^-inf = 0, large negative -> 0
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// The dt front-end for head h with decay rate a_h: the decay step dec and the
+// input step inp from the raw value.  softplus(d) = log(1 + e^d), evaluated as
+// d + log1p(e^-d) for d > 0; the zero-order-hold input step is expm1(d a) / a.
+template <class FE>
+__device__ __forceinline__ void dt_front(const FE& fe, int h, float a_h, float raw, float& dec, float& inp) {
+    float d = raw;
+    if (fe.bias) d += fe.bias[h];
+    if (fe.softplus) d = d > 0.0f ? d + log1pf(expf(-d)) : log1pf(expf(d));
+    if (fe.clamp) d = fminf(fmaxf(d, fe.lo), fe.hi);
+    dec = d;
+    inp = fe.zoh && a_h != 0.0f ? expm1f(d * a_h) / a_h : d;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA fragments: 8 operand values per lane
 // ---------------------------------------------------------------------------

@@ -533,16 +533,19 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
 // ---------------------------------------------------------------------------
 // the forward's decay arrays: for every 64-token sub-chunk and head,
 //   dtl[b,h,s,i] = dt[b, 64s+i, h],   lw[b,h,s,i] = log2(e) sum_{k<=i} dt[b,64s+k,h] A[h]
+// (dt after the front-end: the input step in dtl, the decay step in lw)
 // (the in-chunk cumulative sum with the chunk length set to 64).  One workgroup
 // per (b, s): the (64 x H) block of dt is contiguous, read coalesced through LDS
 // in blocks of 64 heads; each wavefront then scans one head at a time.
 // ---------------------------------------------------------------------------
 constexpr int kDecayHB = 64;  // heads per LDS block
 
-__global__ void __launch_bounds__(256) subchunk_decay_kernel(const bf16* __restrict__ dt, const float* __restrict__ A,
-                                                             float* __restrict__ dtl, float* __restrict__ lw,
-                                                             int64_t L, int H, uint32_t nitems) {
+__global__ void __launch_bounds__(256) subchunk_decay_kernel(DtFront fe, const bf16* __restrict__ dt,
+                                                             const float* __restrict__ A, float* __restrict__ dtl,
+                                                             float* __restrict__ lw, int64_t L, int H,
+                                                             uint32_t nitems) {
     __shared__ float blk[QS][kDecayHB + 1];
+    __shared__ bool vok[QS][kDecayHB + 1];  // position inside the sequence
     const int64_t nsubT = (L + QS - 1) / QS;
     const uint32_t item = xcd_remap(blockIdx.x, nitems);
     const int64_t sub = item % (uint64_t)nsubT;
@@ -566,12 +569,15 @@ __global__ void __launch_bounds__(256) subchunk_decay_kernel(const bf16* __restr
             const int e = tid + 256 * k, t = e / kDecayHB, hh = e % kDecayHB;
             const bool ok = hh < nh && t0 + t < L;
             blk[t][hh] = ok ? to_f32(v[k]) : 0.0f;
+            vok[t][hh] = ok;
         }
         __syncthreads();
         for (int hh = w; hh < nh; hh += 4) {
             const int h = hb + hh;
-            const float d = blk[lane][hh];
-            float incl = d * A[h];
+            const float ah = A[h];
+            float dec = 0.0f, d = 0.0f;  // decay and input steps; zero past L
+            if (vok[lane][hh]) dt_front(fe, h, ah, blk[lane][hh], dec, d);
+            float incl = dec * ah;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float up = __shfl_up(incl, off, 64);
@@ -689,7 +695,8 @@ FastFwdLayout fast_forward_layout(const Shape& s) {
     return f;
 }
 
-hipError_t launch_forward_fast(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
+hipError_t launch_forward_fast(const Shape& s, const DtFront& fe, const void* x, const void* dt, const float* A,
+                               const void* B,
                                const void* C, const float* D, const float* h0, void* y, float* final_state,
                                void* workspace, hipStream_t st) {
     const FastFwdLayout f = fast_forward_layout(s);
@@ -700,8 +707,8 @@ hipError_t launch_forward_fast(const Shape& s, const void* x, const void* dt, co
     float* totals = reinterpret_cast<float*>(ws + f.totals);
     const bf16 *xb = (const bf16*)x, *bb = (const bf16*)B, *cb = (const bf16*)C;
     const uint32_t ndec = (uint32_t)(s.b * ((s.L + fz::QS - 1) / fz::QS));
-    hipLaunchKernelGGL(fz::subchunk_decay_kernel, dim3(ndec), dim3(256), 0, st, (const bf16*)dt, A, dtl, lw, s.L,
-                       (int)s.H, ndec);
+    hipLaunchKernelGGL(fz::subchunk_decay_kernel, dim3(ndec), dim3(256), 0, st, fe, (const bf16*)dt, A, dtl, lw,
+                       s.L, (int)s.H, ndec);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const fz::DtSrc ds{dtl, lw};

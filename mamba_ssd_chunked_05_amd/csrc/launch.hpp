@@ -12,22 +12,31 @@ struct Shape {
     int io;
 };
 
-hipError_t launch_chunk_cumsum(const Shape& s, const void* dt, const float* A, float* dt_t, float* cs,
-                               hipStream_t st);
+// dt front-end, applied where dt is read: d = raw (+ bias[h]); softplus; clamp to
+// [lo, hi]; the decay uses d and the input term d, or (exp(d A) - 1) / A with zoh.
+// All zero = the raw dt is the step.
+struct DtFront {
+    const float* bias;
+    int softplus, zoh, clamp;
+    float lo, hi;
+};
+
+hipError_t launch_chunk_cumsum(const Shape& s, const DtFront& fe, const void* dt, const float* A, float* dt_t,
+                               float* cs, hipStream_t st);
 hipError_t launch_chunk_state(const Shape& s, const void* x, const void* B, const float* dt_t,
                               const float* cs, float* states, hipStream_t st);
 hipError_t launch_state_passing(const Shape& s, float* states, const float* cs, const float* h0,
                                 float* final_state, hipStream_t st);
 hipError_t launch_chunk_scan(const Shape& s, const void* x, const void* B, const void* C, const float* dt_t,
                              const float* cs, const float* start, const float* D, void* y, hipStream_t st);
-hipError_t launch_step(const Shape& s, float* state, const void* x, const void* dt, const float* A,
+hipError_t launch_step(const Shape& s, const DtFront& fe, float* state, const void* x, const void* dt, const float* A,
                        const void* B, const void* C, const float* D, void* y, hipStream_t st);
 // K = s.L decode steps over pre-staged (b, K, ...) inputs; the state stays on chip
 // when N / 16 is 4, 8, 16, 32 or 64 and P * N <= 16384 (a 16 x 16 thread grid of
 // P/16 x N/16 register blocks), else one launch per step.
 bool step_multi_on_chip(const Shape& s);
-hipError_t launch_step_multi(const Shape& s, float* state, const void* x, const void* dt, const float* A,
-                             const void* B, const void* C, const float* D, void* y, hipStream_t st);
+hipError_t launch_step_multi(const Shape& s, const DtFront& fe, float* state, const void* x, const void* dt,
+                             const float* A, const void* B, const void* C, const float* D, void* y, hipStream_t st);
 
 // Fast chunk-state / chunk-scan kernels (bf16, headdim 64, dstate 64 or 128, chunk a multiple of 64).
 bool fast_chunk_supported(const Shape& s);
@@ -47,7 +56,8 @@ struct FastFwdLayout {
     size_t dtl, lw, states, totals, total;
 };
 FastFwdLayout fast_forward_layout(const Shape& s);
-hipError_t launch_forward_fast(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
+hipError_t launch_forward_fast(const Shape& s, const DtFront& fe, const void* x, const void* dt, const float* A,
+                               const void* B,
                                const void* C, const float* D, const float* h0, void* y, float* final_state,
                                void* workspace, hipStream_t st);
 

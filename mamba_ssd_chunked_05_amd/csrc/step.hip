@@ -19,7 +19,7 @@ namespace ssd {
 // Batch strides (in elements) sx of x and y, sdt of dt and sbc of B and C let
 // the same kernel step one token of a (b, K, ...) multi-step layout.
 template <class T>
-__global__ void __launch_bounds__(256) step_kernel(float* __restrict__ state, const T* __restrict__ x,
+__global__ void __launch_bounds__(256) step_kernel(DtFront fe, float* __restrict__ state, const T* __restrict__ x,
                                                    const T* __restrict__ dt, const float* __restrict__ A,
                                                    const T* __restrict__ B, const T* __restrict__ C,
                                                    const float* __restrict__ D, T* __restrict__ y, int H, int P,
@@ -41,8 +41,9 @@ __global__ void __launch_bounds__(256) step_kernel(float* __restrict__ state, co
         Bs[n] = to_f32(B[b * sbc + (int64_t)g * N + n]);
         Cs[n] = to_f32(C[b * sbc + (int64_t)g * N + n]);
     }
-    const float d = to_f32(dt[b * sdt + h]);
-    const float a = fast_exp2(kLog2e * (d * A[h]));
+    float dec, d;  // decay and input steps
+    dt_front(fe, h, A[h], to_f32(dt[b * sdt + h]), dec, d);
+    const float a = fast_exp2(kLog2e * (dec * A[h]));
     __syncthreads();
 
     const int n4 = N / 4;
@@ -84,17 +85,17 @@ __global__ void __launch_bounds__(256) step_kernel(float* __restrict__ state, co
     for (int p = tid; p < P; p += 256) y[b * sx + (int64_t)h * P + p] = from_f32<T>(ys[p] + Dh * xs[p]);
 }
 
-hipError_t launch_step(const Shape& s, float* state, const void* x, const void* dt, const float* A, const void* B,
-                       const void* C, const float* D, void* y, hipStream_t st) {
+hipError_t launch_step(const Shape& s, const DtFront& fe, float* state, const void* x, const void* dt, const float* A,
+                       const void* B, const void* C, const float* D, void* y, hipStream_t st) {
     const int64_t nbh = s.b * s.H;
     if (nbh == 0) return hipSuccess;
     const int64_t sx = s.H * s.P, sdt = s.H, sbc = s.G * s.N;
     if (s.io == 1)
-        hipLaunchKernelGGL(step_kernel<bf16>, dim3((unsigned)nbh), dim3(256), 0, st, state, (const bf16*)x,
+        hipLaunchKernelGGL(step_kernel<bf16>, dim3((unsigned)nbh), dim3(256), 0, st, fe, state, (const bf16*)x,
                            (const bf16*)dt, A, (const bf16*)B, (const bf16*)C, D, (bf16*)y, (int)s.H, (int)s.P,
                            (int)s.N, (int)s.G, sx, sdt, sbc);
     else
-        hipLaunchKernelGGL(step_kernel<float>, dim3((unsigned)nbh), dim3(256), 0, st, state, (const float*)x,
+        hipLaunchKernelGGL(step_kernel<float>, dim3((unsigned)nbh), dim3(256), 0, st, fe, state, (const float*)x,
                            (const float*)dt, A, (const float*)B, (const float*)C, D, (float*)y, (int)s.H, (int)s.P,
                            (int)s.N, (int)s.G, sx, sdt, sbc);
     return hipGetLastError();
@@ -166,7 +167,7 @@ struct MultiBlock {
         }
     }
 
-    __device__ __forceinline__ void store(float* xs, float* bs, float* cs, float* ds, int tid) const {
+    __device__ __forceinline__ void store(float* xs, float* bs, float* cs, int tid) const {
         float f[V];
 #pragma unroll
         for (int i = 0; i < NX; ++i) {
@@ -192,7 +193,6 @@ struct MultiBlock {
                     *reinterpret_cast<float4*>(cs + e * V + q) = make_float4(f[q], f[q + 1], f[q + 2], f[q + 3]);
             }
         }
-        if (tid < KB) ds[tid] = to_f32(draw);
     }
 };
 
@@ -212,7 +212,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 template <class T, int RT, int CT>
-__global__ void __launch_bounds__(256) step_multi_kernel(float* __restrict__ state, const T* __restrict__ x,
+__global__ void __launch_bounds__(256) step_multi_kernel(DtFront fe, float* __restrict__ state, const T* __restrict__ x,
                                                          const T* __restrict__ dt, const float* __restrict__ A,
                                                          const T* __restrict__ B, const T* __restrict__ C,
                                                          const float* __restrict__ D, T* __restrict__ y, int64_t K,
@@ -250,8 +250,13 @@ __global__ void __launch_bounds__(256) step_multi_kernel(float* __restrict__ sta
     for (int64_t k0 = 0; k0 < K; k0 += KB) {
         const int kb = K - k0 < KB ? (int)(K - k0) : KB;
         __syncthreads();  // the previous block's y is written out; the LDS block is free
-        blk.store(xs, bs, cs, ds, tid);
-        if (tid < KB) as[tid] = fast_exp2(to_f32(blk.draw) * al);
+        blk.store(xs, bs, cs, tid);
+        if (tid < KB) {  // the step's decay and input step
+            float dec, din;
+            dt_front(fe, h, A[h], to_f32(blk.draw), dec, din);
+            ds[tid] = din;
+            as[tid] = fast_exp2(dec * al);
+        }
         __syncthreads();
         if (k0 + KB < K) {  // the next block's inputs stream in while this one is computed
             const int64_t k1 = k0 + KB;
@@ -328,10 +333,10 @@ constexpr bool multi_ok(int RT, int CT) {
 }
 
 template <class T, int RT, int CT>
-static hipError_t launch_multi(const Shape& s, float* state, const void* x, const void* dt, const float* A,
+static hipError_t launch_multi(const Shape& s, const DtFront& fe, float* state, const void* x, const void* dt, const float* A,
                                const void* B, const void* C, const float* D, void* y, hipStream_t st) {
     if constexpr (multi_ok(RT, CT)) {
-        hipLaunchKernelGGL((step_multi_kernel<T, RT, CT>), dim3((unsigned)(s.b * s.H)), dim3(256), 0, st, state,
+        hipLaunchKernelGGL((step_multi_kernel<T, RT, CT>), dim3((unsigned)(s.b * s.H)), dim3(256), 0, st, fe, state,
                            (const T*)x, (const T*)dt, A, (const T*)B, (const T*)C, D, (T*)y, s.L, (int)s.H,
                            (int)s.G);
         return hipGetLastError();
@@ -340,11 +345,11 @@ static hipError_t launch_multi(const Shape& s, float* state, const void* x, cons
 }
 
 template <class T, int CT>
-static hipError_t multi_by_rt(const Shape& s, float* state, const void* x, const void* dt, const float* A,
+static hipError_t multi_by_rt(const Shape& s, const DtFront& fe, float* state, const void* x, const void* dt, const float* A,
                               const void* B, const void* C, const float* D, void* y, hipStream_t st) {
     switch (s.P / 16) {
 #define SSD_RT(r) \
-    case r: return launch_multi<T, r, CT>(s, state, x, dt, A, B, C, D, y, st);
+    case r: return launch_multi<T, r, CT>(s, fe, state, x, dt, A, B, C, D, y, st);
         SSD_RT(1) SSD_RT(2) SSD_RT(3) SSD_RT(4) SSD_RT(5) SSD_RT(6) SSD_RT(7) SSD_RT(8)
         SSD_RT(9) SSD_RT(10) SSD_RT(11) SSD_RT(12) SSD_RT(13) SSD_RT(14) SSD_RT(15) SSD_RT(16)
 #undef SSD_RT
@@ -353,14 +358,14 @@ static hipError_t multi_by_rt(const Shape& s, float* state, const void* x, const
 }
 
 template <class T>
-static hipError_t multi_by_ct(const Shape& s, float* state, const void* x, const void* dt, const float* A,
+static hipError_t multi_by_ct(const Shape& s, const DtFront& fe, float* state, const void* x, const void* dt, const float* A,
                               const void* B, const void* C, const float* D, void* y, hipStream_t st) {
     switch (s.N / 16) {
-        case 4: return multi_by_rt<T, 4>(s, state, x, dt, A, B, C, D, y, st);
-        case 8: return multi_by_rt<T, 8>(s, state, x, dt, A, B, C, D, y, st);
-        case 16: return multi_by_rt<T, 16>(s, state, x, dt, A, B, C, D, y, st);
-        case 32: return multi_by_rt<T, 32>(s, state, x, dt, A, B, C, D, y, st);
-        case 64: return multi_by_rt<T, 64>(s, state, x, dt, A, B, C, D, y, st);
+        case 4: return multi_by_rt<T, 4>(s, fe, state, x, dt, A, B, C, D, y, st);
+        case 8: return multi_by_rt<T, 8>(s, fe, state, x, dt, A, B, C, D, y, st);
+        case 16: return multi_by_rt<T, 16>(s, fe, state, x, dt, A, B, C, D, y, st);
+        case 32: return multi_by_rt<T, 32>(s, fe, state, x, dt, A, B, C, D, y, st);
+        case 64: return multi_by_rt<T, 64>(s, fe, state, x, dt, A, B, C, D, y, st);
     }
     return hipErrorInvalidValue;
 }
@@ -371,13 +376,13 @@ bool step_multi_on_chip(const Shape& s) {
     return s.P % 16 == 0 && s.N % 16 == 0 && rt >= 1 && rt <= 16 && ct_ok && multi_ok(rt, ct);
 }
 
-hipError_t launch_step_multi(const Shape& s, float* state, const void* x, const void* dt, const float* A,
+hipError_t launch_step_multi(const Shape& s, const DtFront& fe, float* state, const void* x, const void* dt, const float* A,
                              const void* B, const void* C, const float* D, void* y, hipStream_t st) {
     const int64_t nbh = s.b * s.H;
     if (nbh == 0 || s.L == 0) return hipSuccess;
     if (step_multi_on_chip(s))
-        return s.io == 1 ? multi_by_ct<bf16>(s, state, x, dt, A, B, C, D, y, st)
-                         : multi_by_ct<float>(s, state, x, dt, A, B, C, D, y, st);
+        return s.io == 1 ? multi_by_ct<bf16>(s, fe, state, x, dt, A, B, C, D, y, st)
+                         : multi_by_ct<float>(s, fe, state, x, dt, A, B, C, D, y, st);
     // other state shapes: one single-step launch per token, still without a host round trip
     const size_t e = s.io == 1 ? 2 : 4;
     const int64_t sx = s.L * s.H * s.P, sdt = s.L * s.H, sbc = s.L * s.G * s.N;
@@ -388,11 +393,11 @@ hipError_t launch_step_multi(const Shape& s, float* state, const void* x, const 
         const char* ck = static_cast<const char*>(C) + k * s.G * s.N * e;
         char* yk = static_cast<char*>(y) + k * s.H * s.P * e;
         if (s.io == 1)
-            hipLaunchKernelGGL(step_kernel<bf16>, dim3((unsigned)nbh), dim3(256), 0, st, state, (const bf16*)xk,
+            hipLaunchKernelGGL(step_kernel<bf16>, dim3((unsigned)nbh), dim3(256), 0, st, fe, state, (const bf16*)xk,
                                (const bf16*)dk, A, (const bf16*)bk, (const bf16*)ck, D, (bf16*)yk, (int)s.H,
                                (int)s.P, (int)s.N, (int)s.G, sx, sdt, sbc);
         else
-            hipLaunchKernelGGL(step_kernel<float>, dim3((unsigned)nbh), dim3(256), 0, st, state, (const float*)xk,
+            hipLaunchKernelGGL(step_kernel<float>, dim3((unsigned)nbh), dim3(256), 0, st, fe, state, (const float*)xk,
                                (const float*)dk, A, (const float*)bk, (const float*)ck, D, (float*)yk, (int)s.H,
                                (int)s.P, (int)s.N, (int)s.G, sx, sdt, sbc);
         const hipError_t err = hipGetLastError();

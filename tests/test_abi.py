@@ -27,7 +27,7 @@ def _declared():
 def test_header_symbols_exported():
     lib = ssd.load()
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
 
@@ -148,6 +148,32 @@ def test_step_multi_validates():
     assert lib.ssd_step_multi(ctypes.byref(_d(L=8, io=7)), *args) == DTYPE
     # zero steps: a no-op that launches nothing
     assert lib.ssd_step_multi(ctypes.byref(_d(L=0)), *args) == OK
+
+
+def test_frontend_validates():
+    lib = ssd.load()
+    from mamba_ssd_chunked_05_amd import DtFrontend
+    d = _d(L=512, Q=256)
+    args = [_p(0), _p(1 << 30), _p(2 << 30), _p(3 << 30), None]
+    bad = DtFrontend(None, 1, 0, 0, 1, 0.0, 0.0)  # reserved != 0
+    assert lib.ssd_chunk_cumsum_ex(ctypes.byref(d), ctypes.byref(bad), *args) == SHAPE
+    bad = DtFrontend(None, 1, 0, 1, 0, 0.5, 0.1)  # dt_min > dt_max
+    assert lib.ssd_chunk_cumsum_ex(ctypes.byref(d), ctypes.byref(bad), *args) == SHAPE
+    bad = DtFrontend(None, 1, 0, 1, 0, float("nan"), 0.1)
+    assert lib.ssd_chunk_cumsum_ex(ctypes.byref(d), ctypes.byref(bad), *args) == SHAPE
+    over = DtFrontend(FAKE + (2 << 30), 1, 1, 0, 0, 0.0, 0.0)  # dt_bias over the dt_t output
+    assert lib.ssd_chunk_cumsum_ex(ctypes.byref(d), ctypes.byref(over), *args) == ALIAS
+    step_args = [_p(0), _p(1 << 30), _p(2 << 30), _p(3 << 30), _p(4 << 30), _p(5 << 30), None, _p(6 << 30), None]
+    over = DtFrontend(FAKE + (6 << 30) + 16, 1, 0, 0, 0, 0.0, 0.0)  # dt_bias over y
+    assert lib.ssd_step_ex(ctypes.byref(_d(L=1)), ctypes.byref(over), *step_args) == ALIAS
+    assert lib.ssd_step_multi_ex(ctypes.byref(_d(L=4)), ctypes.byref(over), *step_args) == ALIAS
+    assert _forward_ex(d, DtFrontend(None, 0, 0, 1, 0, 1.0, 0.5)) == SHAPE
+
+
+def _forward_ex(d, fe):
+    lib = ssd.load()
+    return lib.ssd_forward_ex(ctypes.byref(d), ctypes.byref(fe), _p(0), _p(1 << 30), _p(2 << 30), _p(3 << 30),
+                              _p(4 << 30), _p(5 << 30), None, _p(6 << 30), _p(7 << 30), _p(8 << 30), 1 << 40, None)
 
 
 def test_workspace_and_config_are_host_only():
