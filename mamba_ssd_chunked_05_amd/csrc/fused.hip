@@ -89,14 +89,16 @@ struct ChunkRegs {
     float cs;   // chunk cumulative log2 decay of that token
 };
 
-// Per-thread staging offsets at token 0.  Chunk k of a thread is chunk
-// (tid + 256 k) of the tile, so every offset is a base plus a compile-time
-// multiple of k: x chunk k covers head k / 2, rows (tid / 8) + 32 (k % 2);
-// B / C chunk k covers row tid / (N / 8) + k * (256 / (N / 8)).
+// Per-thread staging offsets within one sub-chunk tile, in elements from the
+// tile's first element (32-bit: a tile spans 64 tokens).  Chunk k of a thread
+// is chunk (tid + 256 k) of the tile: x chunk k covers head k / 2, rows
+// (tid / 8) + 32 (k % 2); B / C chunk k covers row tid / (N / 8) + k * RPI.
+// The tile bases themselves are wavefront-uniform pointers (TileBase), so each
+// load is a scalar base plus this vector offset plus a uniform constant.
 template <int N, int HPW>
 struct ChunkAddr {
-    int64_t xo, bo, dto;   // global element offsets of this thread's first x, B/C rows; dt_t/cs element
-    int xr, br;            // first x / B row of this thread within the chunk
+    uint32_t xo, bo, dto;  // this thread's first x element, B/C element, dt/cs element
+    int xr, br;            // first x / B row of this thread within the sub-chunk
     int xl, bl, cl;        // LDS element offsets of the first x / B / C chunk
 };
 
@@ -105,29 +107,6 @@ struct BRows {
     static constexpr int RPI = 256 / (N / 8);  // B rows covered by one pass of 256 threads
 };
 
-template <int N, int HPW, bool FWD>
-__device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int64_t b, int64_t L, int H, int G, int h0, int g,
-                                           int64_t c, int64_t nC, int Q, int tid) {
-    constexpr int BS = Strides<N>::BS, CS = Strides<N>::CS;
-    const int xr = tid >> 3, xc = (tid & 7) * 8;
-    a.xr = xr;
-    a.xo = ((b * L + xr) * H + h0) * (int64_t)P + xc;
-    a.xl = xr * XS + xc;
-    const int br = tid / (N / 8), bc = (tid % (N / 8)) * 8;
-    a.br = br;
-    a.bo = ((b * L + br) * G + g) * (int64_t)N + bc;
-    a.bl = br * BS + bc;
-    a.cl = br * CS + bc;
-    const int hh = tid >> 6, r = tid & 63;
-    const int hd = h0 + (hh < HPW ? hh : 0);
-    if (FWD) {  // sub-chunk-local arrays (b, H, ceil(L/64), 64): position r of the chunk's first sub-chunk
-        const int64_t nsubT = (L + QS - 1) / QS;
-        a.dto = ((b * H + hd) * nsubT + c * (Q / QS)) * QS + r;
-    } else {    // chunk arrays (b, H, nC, Q): position r of the chunk
-        a.dto = ((b * H + hd) * nC + c) * Q + r;
-    }
-}
-
 // dt (fp32) and the cumulative log2 decay: over the chunk for the staged calls,
 // restarting at every 64-token sub-chunk in the forward.
 struct DtSrc {
@@ -135,50 +114,83 @@ struct DtSrc {
     const float* cs;
 };
 
-// Load the chunk starting at token tbase into registers (rows past L read as zero).
+// wavefront-uniform bases of one sub-chunk's tiles
+struct TileBase {
+    const bf16 *x, *b, *c;
+    const float *dt, *cs;
+};
+
+// dt_head: distance between consecutive heads in the dt/cs arrays
+template <int N, int HPW>
+__device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int H, int G, int64_t dt_head, int tid) {
+    constexpr int BS = Strides<N>::BS, CS = Strides<N>::CS;
+    const int xr = tid >> 3, xc = (tid & 7) * 8;
+    a.xr = xr;
+    a.xo = (uint32_t)(xr * H * P + xc);
+    a.xl = xr * XS + xc;
+    const int br = tid / (N / 8), bc = (tid % (N / 8)) * 8;
+    a.br = br;
+    a.bo = (uint32_t)(br * G * N + bc);
+    a.bl = br * BS + bc;
+    a.cl = br * CS + bc;
+    const int hh = tid >> 6, r = tid & 63;
+    a.dto = (uint32_t)((hh < HPW ? hh : 0) * dt_head + r);
+}
+
+// The tiles of the sub-chunk starting at token tbase of batch row b (heads h0.., group g);
+// dt0 / cs0 point at this chunk's first position of head h0 and sub is the sub-chunk index.
+template <bool WITH_C>
+__device__ __forceinline__ TileBase tile_base(const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
+                                              int64_t dt0, int64_t b, int64_t L, int H, int G, int N, int h0, int g,
+                                              int64_t tbase, int sub) {
+    TileBase t;
+    t.x = x + ((b * L + tbase) * H + h0) * (int64_t)P;
+    t.b = B + ((b * L + tbase) * G + g) * (int64_t)N;
+    t.c = WITH_C ? C + ((b * L + tbase) * G + g) * (int64_t)N : nullptr;
+    t.dt = ds.dt_t + dt0 + (int64_t)QS * sub;
+    t.cs = ds.cs + dt0 + (int64_t)QS * sub;
+    return t;
+}
+
+// Load one sub-chunk into registers; rows past L read as zero (last = index of the
+// last valid row, used when the sub-chunk is ragged).
 template <int N, int HPW, bool WITH_C>
 __device__ __forceinline__ void chunk_load(ChunkRegs<N, HPW, WITH_C>& rg, const ChunkAddr<N, HPW>& a,
-                                           const bf16* __restrict__ x, const DtSrc& ds, const bf16* __restrict__ B,
-                                           const bf16* __restrict__ C, int64_t tbase, int sub, int64_t L, int H,
-                                           int G, int tid) {
+                                           const TileBase& t, bool full, int last, int H, int G, int tid) {
     constexpr int RPI = BRows<N>::RPI;
     if (tid < 64 * HPW) {  // dt_t and cs cover every position of the chunk (zero-padded past L)
-        rg.dt = ds.dt_t[a.dto + QS * sub];
-        rg.cs = ds.cs[a.dto + QS * sub];
+        rg.dt = t.dt[a.dto];
+        rg.cs = t.cs[a.dto];
     }
-    const int64_t HP_ = (int64_t)H * P, GN = (int64_t)G * N;
-    const bf16* xb = x + a.xo + tbase * HP_;
-    const bf16* bb = B + a.bo + tbase * GN;
-    const bf16* cb = WITH_C ? C + a.bo + tbase * GN : nullptr;
-    if (tbase + QS <= L) {
+    const uint32_t HP_ = (uint32_t)(H * P), GN = (uint32_t)(G * N);
+    if (full) {
 #pragma unroll
-        for (int k = 0; k < 2 * HPW; ++k) rg.x[k] = ld16(xb + (k & 1) * 32 * HP_ + (k >> 1) * P);
+        for (int k = 0; k < 2 * HPW; ++k) rg.x[k] = ld16(t.x + a.xo + ((k & 1) * 32 * HP_ + (k >> 1) * P));
 #pragma unroll
-        for (int k = 0; k < N / 32; ++k) rg.b[k] = ld16(bb + k * RPI * GN);
+        for (int k = 0; k < N / 32; ++k) rg.b[k] = ld16(t.b + a.bo + k * RPI * GN);
         if (WITH_C) {
 #pragma unroll
-            for (int k = 0; k < N / 32; ++k) rg.c[k] = ld16(cb + k * RPI * GN);
+            for (int k = 0; k < N / 32; ++k) rg.c[k] = ld16(t.c + a.bo + k * RPI * GN);
         }
     } else {
-        // ragged last chunk: clamp the row to the last valid one, then select zero
+        // ragged last sub-chunk: clamp the row to the last valid one, then select zero
         const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        const int last = (int)(L - 1 - tbase);
 #pragma unroll
         for (int k = 0; k < 2 * HPW; ++k) {
             const int r = a.xr + (k & 1) * 32;
             const bool ok = r <= last;
-            const uint4 v = ld16(xb + (int64_t)((ok ? r : last) - a.xr) * HP_ + (k >> 1) * P);
+            const uint4 v = ld16(t.x + (a.xo + (uint32_t)((ok ? r : last) - a.xr) * HP_ + (k >> 1) * P));
             rg.x[k] = ok ? v : z;
         }
 #pragma unroll
         for (int k = 0; k < N / 32; ++k) {
             const int r = a.br + k * RPI;
             const bool ok = r <= last;
-            const int64_t off = (int64_t)((ok ? r : last) - a.br) * GN;
-            const uint4 v = ld16(bb + off);
+            const uint32_t off = a.bo + (uint32_t)((ok ? r : last) - a.br) * GN;
+            const uint4 v = ld16(t.b + off);
             rg.b[k] = ok ? v : z;
             if (WITH_C) {
-                const uint4 u = ld16(cb + off);
+                const uint4 u = ld16(t.c + off);
                 rg.c[k] = ok ? u : z;
             }
         }
@@ -237,8 +249,6 @@ struct ScanLds {
     float alpha[4];                 // 2^(l_63) per head
 };
 
-__constant__ int8_t kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-__constant__ int8_t kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 
 // FWD: the forward's variant, reading sub-chunk-local decay arrays (subchunk_decay_kernel).
 template <int N, int HPW, bool FWD>
@@ -283,21 +293,33 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
         sm.mb[(hh * 16 + 3 * 4 + 2) * 256 + q] = static_cast<bf16>(0.0f);
     }
 
+    const int64_t nsubT = (L + QS - 1) / QS;
+    const int64_t dt_head = FWD ? nsubT * QS : nC * Q;  // dt/cs distance between heads
+    const int64_t dt0 = FWD ? ((b * H + h0) * nsubT + c * (Q / QS)) * QS : ((b * H + h0) * nC + c) * Q;
     ChunkAddr<N, HPW> ad;
-    chunk_addr<N, HPW, FWD>(ad, b, L, H, G, h0, g, c, nC, Q, tid);
+    chunk_addr<N, HPW>(ad, H, G, dt_head, tid);
     ChunkRegs<N, HPW, true> rg;
-    chunk_load<N, HPW, true>(rg, ad, x, ds, B, C, t0, 0, L, H, G, tid);
+    chunk_load<N, HPW, true>(rg, ad, tile_base<true>(x, B, C, ds, dt0, b, L, H, G, N, h0, g, t0, 0), t0 + QS <= L,
+                             (int)(L - 1 - t0), H, G, tid);
+    // this thread's output element offset within a sub-chunk's y tile (row l16, columns 16w + 4g4 ..)
+    const uint32_t yo = (uint32_t)(l16 * H * P + 16 * w + 4 * g4);
 
     for (int sc = 0; sc < nsub; ++sc) {
         const int64_t tbase = t0 + (int64_t)sc * QS;
         __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
         chunk_store<N, HPW, true, FWD>(sm.xs, sm.bs, sm.cs, sm.lw, sm.dtw, sm.ww, sm.alpha, rg, ad, cs_prev, tot, tid);
         __syncthreads();
-        if (sc + 1 < nsub) chunk_load<N, HPW, true>(rg, ad, x, ds, B, C, tbase + QS, sc + 1, L, H, G, tid);
+        if (sc + 1 < nsub) {
+            const int64_t t1 = tbase + QS;
+            chunk_load<N, HPW, true>(rg, ad, tile_base<true>(x, B, C, ds, dt0, b, L, H, G, N, h0, g, t1, sc + 1),
+                                     t1 + QS <= L, (int)(L - 1 - t1), H, G, tid);
+        }
 
         // ---- phase 1: C.B^T tiles, decayed per head -> LDS in fragment order ----------------
         for (int tt = w; tt < 10; tt += 4) {
-            const int jt = kTileJ[tt], it = kTileI[tt];
+            // tile tt = it (it + 1) / 2 + jt of the lower triangle, from arithmetic (no table lookup)
+            const int it = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+            const int jt = tt - it * (it + 1) / 2;
             f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NK; ++ks) {
@@ -306,15 +328,19 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
                 frag_load8<bf16>(bo, &sm.cs[(16 * it + l16) * CS + 32 * ks + 8 * g4]);
                 mma(gacc, a, bo);
             }
-            const int i = 16 * it + l16;
+            const int i = 16 * it + l16, j0 = 16 * jt + 4 * g4;
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
+                // every operand is read and every product formed, then the upper triangle is
+                // selected to zero (the exponent is capped at 0 so no lane forms an infinity)
                 const float li = sm.lw[hh * QS + i];
+                const f32x4 lj = *reinterpret_cast<const f32x4*>(&sm.lw[hh * QS + j0]);
+                const f32x4 dj = *reinterpret_cast<const f32x4*>(&sm.dtw[hh * QS + j0]);
                 f32x4 m;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * jt + 4 * g4 + r;
-                    m[r] = j <= i ? gacc[r] * fast_exp2(li - sm.lw[hh * QS + j]) * sm.dtw[hh * QS + j] : 0.0f;
+                    const float v = gacc[r] * fast_exp2(fminf(li - lj[r], 0.0f)) * dj[r];
+                    m[r] = j0 + r <= i ? v : 0.0f;
                 }
                 *reinterpret_cast<bf16x4*>(&sm.mb[((hh * 16 + jt * 4 + it) * 64 + lane) * 4]) = cvt4(m);
             }
@@ -377,7 +403,8 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         o[r] = static_cast<bf16>(acc[hh][r] + Dh[hh] * static_cast<float>(xv[r]));
-                    *reinterpret_cast<bf16x4*>(y + ((b * L + tbase + i) * H + h0 + hh) * P + 16 * w + 4 * g4) = o;
+                    *reinterpret_cast<bf16x4*>(y + ((b * L + tbase) * H + h0) * (int64_t)P +
+                                               (yo + (uint32_t)((16 * it * H + hh) * P))) = o;
                 }
             }
         }
@@ -464,10 +491,14 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
         for (int nt = 0; nt < NT; ++nt) st[hh][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    const int64_t nsubT = (L + QS - 1) / QS;
+    const int64_t dt_head = FWD ? nsubT * QS : nC * Q;  // dt/cs distance between heads
+    const int64_t dt0 = FWD ? ((b * H + h0) * nsubT + c * (Q / QS)) * QS : ((b * H + h0) * nC + c) * Q;
     ChunkAddr<N, HPW> ad;
-    chunk_addr<N, HPW, FWD>(ad, b, L, H, G, h0, g, c, nC, Q, tid);
+    chunk_addr<N, HPW>(ad, H, G, dt_head, tid);
     ChunkRegs<N, HPW, false> rg;
-    chunk_load<N, HPW, false>(rg, ad, x, ds, B, nullptr, t0, 0, L, H, G, tid);
+    chunk_load<N, HPW, false>(rg, ad, tile_base<false>(x, B, nullptr, ds, dt0, b, L, H, G, N, h0, g, t0, 0),
+                              t0 + QS <= L, (int)(L - 1 - t0), H, G, tid);
 
     for (int sc = 0; sc < nsub; ++sc) {
         const int64_t tbase = t0 + (int64_t)sc * QS;
@@ -475,8 +506,12 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
         chunk_store<N, HPW, false, FWD>(sm.xs, sm.bs, nullptr, sm.lw, sm.dtw, sm.ww, sm.alpha, rg, ad, cs_prev, tot,
                                         tid);
         __syncthreads();
-        if (sc + 1 < nsub)
-            chunk_load<N, HPW, false>(rg, ad, x, ds, B, nullptr, tbase + QS, sc + 1, L, H, G, tid);
+        if (sc + 1 < nsub) {
+            const int64_t t1 = tbase + QS;
+            chunk_load<N, HPW, false>(rg, ad,
+                                      tile_base<false>(x, B, nullptr, ds, dt0, b, L, H, G, N, h0, g, t1, sc + 1),
+                                      t1 + QS <= L, (int)(L - 1 - t1), H, G, tid);
+        }
 
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
