@@ -202,9 +202,15 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<N, HPW, WITH_C>& rg, const 
 // held by wavefront hh for head hh and advanced here.
 // With FWD the decay arrays already restart at the sub-chunk.  tot accumulates
 // the sub-chunk totals (the chunk's total decay).
+//
+// ec (optional, [hh][4][64]): for the off-diagonal 16 x 16 tiles of the in-chunk
+// matrix, 2^(l_i - l_j) dt_j = ec[0][i] * ec[it][j] with row-block start r = 16 it:
+//   ec[0][i]  = 2^(l_i - l_(16 (i / 16)))      (<= 1: i at or after its block start)
+//   ec[it][j] = 2^(l_(16 it) - l_j) dt_j       (<= dt_j for j < 16 it, the only ones used)
+// so those tiles need no exponential; the diagonal tiles form 2^(l_i - l_j) directly.
 template <int N, int HPW, bool WITH_C, bool FWD>
 __device__ __forceinline__ void chunk_store(bf16* xs, bf16* bsm, bf16* csm, float* lw, float* dtw, float* ww,
-                                            float* alpha, const ChunkRegs<N, HPW, WITH_C>& rg,
+                                            float* ec, float* alpha, const ChunkRegs<N, HPW, WITH_C>& rg,
                                             const ChunkAddr<N, HPW>& a, float& cs_prev, float& tot, int tid) {
     constexpr int RPI = BRows<N>::RPI, BS = Strides<N>::BS, CS = Strides<N>::CS;
 #pragma unroll
@@ -230,6 +236,12 @@ __device__ __forceinline__ void chunk_store(bf16* xs, bf16* bsm, bf16* csm, floa
         lw[hh * QS + lane] = incl;
         dtw[hh * QS + lane] = d;
         ww[hh * QS + lane] = fast_exp2(last - incl) * d;
+        if (ec) {
+            ec[(hh * 4) * QS + lane] = fast_exp2(incl - __shfl(incl, lane & ~15, 64));
+#pragma unroll
+            for (int it = 1; it < 4; ++it)
+                ec[(hh * 4 + it) * QS + lane] = fast_exp2(fminf(__shfl(incl, 16 * it, 64) - incl, 0.0f)) * d;
+        }
         if (lane == 0) alpha[hh] = fast_exp2(last);
     }
 }
@@ -246,6 +258,7 @@ struct ScanLds {
     float lw[HPW * QS];             // in-chunk cumulative log2 decay
     float dtw[HPW * QS];            // dt
     float ww[HPW * QS];             // 2^(l_63 - l_j) dt_j
+    float ec[HPW * 4 * QS];         // separable decay factors of the off-diagonal tiles (chunk_store)
     float alpha[4];                 // 2^(l_63) per head
 };
 
@@ -307,7 +320,8 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     for (int sc = 0; sc < nsub; ++sc) {
         const int64_t tbase = t0 + (int64_t)sc * QS;
         __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
-        chunk_store<N, HPW, true, FWD>(sm.xs, sm.bs, sm.cs, sm.lw, sm.dtw, sm.ww, sm.alpha, rg, ad, cs_prev, tot, tid);
+        chunk_store<N, HPW, true, FWD>(sm.xs, sm.bs, sm.cs, sm.lw, sm.dtw, sm.ww, sm.ec, sm.alpha, rg, ad, cs_prev,
+                                       tot, tid);
         __syncthreads();
         if (sc + 1 < nsub) {
             const int64_t t1 = tbase + QS;
@@ -331,23 +345,31 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
             const int i = 16 * it + l16, j0 = 16 * jt + 4 * g4;
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
-                // every operand is read and every product formed, then the upper triangle is
-                // selected to zero (the exponent is capped at 0 so no lane forms an infinity)
-                const float li = sm.lw[hh * QS + i];
-                const f32x4 lj = *reinterpret_cast<const f32x4*>(&sm.lw[hh * QS + j0]);
-                const f32x4 dj = *reinterpret_cast<const f32x4*>(&sm.dtw[hh * QS + j0]);
                 f32x4 m;
+                if (jt == it) {
+                    // diagonal tile: every operand is read and every product formed, then the upper
+                    // triangle is selected to zero (the exponent is capped at 0 so no lane forms an
+                    // infinity); D_h joins the diagonal, so X^T M also yields the skip term D x
+                    const float li = sm.lw[hh * QS + i];
+                    const f32x4 lj = *reinterpret_cast<const f32x4*>(&sm.lw[hh * QS + j0]);
+                    const f32x4 dj = *reinterpret_cast<const f32x4*>(&sm.dtw[hh * QS + j0]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v = gacc[r] * fast_exp2(fminf(li - lj[r], 0.0f)) * dj[r];
-                    m[r] = j0 + r <= i ? v : 0.0f;
+                    for (int r = 0; r < 4; ++r) {
+                        const float v = gacc[r] * fast_exp2(fminf(li - lj[r], 0.0f)) * dj[r];
+                        m[r] = (j0 + r <= i ? v : 0.0f) + (j0 + r == i ? Dh[hh] : 0.0f);
+                    }
+                } else {  // below the diagonal: the separable factors of chunk_store
+                    const float er = sm.ec[(hh * 4) * QS + i];
+                    const f32x4 ej = *reinterpret_cast<const f32x4*>(&sm.ec[(hh * 4 + it) * QS + j0]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m[r] = gacc[r] * er * ej[r];
                 }
                 *reinterpret_cast<bf16x4*>(&sm.mb[((hh * 16 + jt * 4 + it) * 64 + lane) * 4]) = cvt4(m);
             }
         }
         __syncthreads();
 
-        // ---- phase 2: Y^T[p-tile w] = 2^l_i (S C^T) + X^T M + D x ------------------------------
+        // ---- phase 2: Y^T[p-tile w] = 2^l_i (S C^T) + X^T M  (M carries D on its diagonal) -------
         bf16x8 sa[HPW][NK];
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
@@ -397,12 +419,9 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
             if (full || tbase + i < L) {
 #pragma unroll
                 for (int hh = 0; hh < HPW; ++hh) {
-                    const bf16x4 xv =
-                        *reinterpret_cast<const bf16x4*>(&sm.xs[hh * QS * XS + i * XS + 16 * w + 4 * g4]);
                     bf16x4 o;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        o[r] = static_cast<bf16>(acc[hh][r] + Dh[hh] * static_cast<float>(xv[r]));
+                    for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(acc[hh][r]);
                     *reinterpret_cast<bf16x4*>(y + ((b * L + tbase) * H + h0) * (int64_t)P +
                                                (yo + (uint32_t)((16 * it * H + hh) * P))) = o;
                 }
@@ -503,8 +522,8 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     for (int sc = 0; sc < nsub; ++sc) {
         const int64_t tbase = t0 + (int64_t)sc * QS;
         __syncthreads();
-        chunk_store<N, HPW, false, FWD>(sm.xs, sm.bs, nullptr, sm.lw, sm.dtw, sm.ww, sm.alpha, rg, ad, cs_prev, tot,
-                                        tid);
+        chunk_store<N, HPW, false, FWD>(sm.xs, sm.bs, nullptr, sm.lw, sm.dtw, sm.ww, nullptr, sm.alpha, rg, ad,
+                                        cs_prev, tot, tid);
         __syncthreads();
         if (sc + 1 < nsub) {
             const int64_t t1 = tbase + QS;
