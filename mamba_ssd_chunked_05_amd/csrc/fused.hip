@@ -454,13 +454,16 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
                     xw[hh].v[4 + r] = static_cast<bf16>(static_cast<float>(hi4[r]) * wv[16 + r]);
                 }
             }
+            Frag<bf16> a[NT];  // every B^T fragment of this K step in flight before the products
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                a[nt].v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * nt, BS, l16),
+                                tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * nt, BS, l16));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                Frag<bf16> a;
-                a.v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * nt, BS, l16),
-                            tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * nt, BS, l16));
 #pragma unroll
-                for (int hh = 0; hh < HPW; ++hh) mma(st[hh][nt], a, xw[hh]);
+                for (int hh = 0; hh < HPW; ++hh) mma(st[hh][nt], a[nt], xw[hh]);
             }
         }
     }
@@ -561,15 +564,18 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
                     xl[hh].v[4 + r] = static_cast<bf16>(v1 - static_cast<float>(h1v));
                 }
             }
+            Frag<bf16> a[NT];  // every B^T fragment of this K step in flight before the products
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                a[nt].v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * nt, BS, l16),
+                                tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * nt, BS, l16));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                Frag<bf16> a;
-                a.v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * nt, BS, l16),
-                            tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * nt, BS, l16));
 #pragma unroll
                 for (int hh = 0; hh < HPW; ++hh) {
-                    mma(st[hh][nt], a, xh[hh]);
-                    mma(st[hh][nt], a, xl[hh]);
+                    mma(st[hh][nt], a[nt], xh[hh]);
+                    mma(st[hh][nt], a[nt], xl[hh]);
                 }
             }
         }
