@@ -376,6 +376,19 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
 #pragma unroll
             for (int ks = 0; ks < NK; ++ks) sa[hh][ks] = pack8(cvt4(st[hh][2 * ks]), cvt4(st[hh][2 * ks + 1]));
         }
+        // X^T fragments of this wavefront's p-tile over token slots 32ks + 4g4 + r and
+        // 32ks + 16 + 4g4 + r: read once, used by the in-chunk product here and, scaled, by the
+        // state update of phase 3
+        Frag<bf16> xf[2][HPW];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh) {
+                const bf16* xt = &sm.xs[hh * QS * XS];
+                xf[ks][hh].v = pack8(tr_read(xt, 32 * ks + 4 * g4, 16 * w, XS, l16),
+                                     tr_read(xt, 32 * ks + 16 + 4 * g4, 16 * w, XS, l16));
+            }
+        }
         const bool full = tbase + QS <= L;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -406,14 +419,11 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
             for (int js = 0; js <= it / 2; ++js) {
 #pragma unroll
                 for (int hh = 0; hh < HPW; ++hh) {
-                    const bf16* xt = &sm.xs[hh * QS * XS];
-                    Frag<bf16> a, bo;
-                    a.v = pack8(tr_read(xt, 32 * js + 4 * g4, 16 * w, XS, l16),
-                                tr_read(xt, 32 * js + 16 + 4 * g4, 16 * w, XS, l16));
+                    Frag<bf16> bo;
                     const bf16* mt = &sm.mb[hh * 16 * 256];
                     bo.v = pack8(*reinterpret_cast<const bf16x4*>(&mt[(((2 * js) * 4 + it) * 64 + lane) * 4]),
                                  *reinterpret_cast<const bf16x4*>(&mt[(((2 * js + 1) * 4 + it) * 64 + lane) * 4]));
-                    mma(acc[hh], a, bo);
+                    mma(acc[hh], xf[js][hh], bo);
                 }
             }
             if (full || tbase + i < L) {
@@ -444,14 +454,11 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
             Frag<bf16> xw[HPW];
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
-                const bf16* xt = &sm.xs[hh * QS * XS];
-                const bf16x4 lo4 = tr_read(xt, 32 * ks + 4 * g4, 16 * w, XS, l16);
-                const bf16x4 hi4 = tr_read(xt, 32 * ks + 16 + 4 * g4, 16 * w, XS, l16);
                 const float* wv = &sm.ww[hh * QS + 32 * ks + 4 * g4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    xw[hh].v[r] = static_cast<bf16>(static_cast<float>(lo4[r]) * wv[r]);
-                    xw[hh].v[4 + r] = static_cast<bf16>(static_cast<float>(hi4[r]) * wv[16 + r]);
+                    xw[hh].v[r] = static_cast<bf16>(static_cast<float>(xf[ks][hh].v[r]) * wv[r]);
+                    xw[hh].v[4 + r] = static_cast<bf16>(static_cast<float>(xf[ks][hh].v[4 + r]) * wv[16 + r]);
                 }
             }
             Frag<bf16> a[NT];  // every B^T fragment of this K step in flight before the products
