@@ -48,7 +48,7 @@
  *
  * Supported sizes: P and N multiples of 16 with P <= 256 and N <= 1024;
  * Q a multiple of 16 in [16, 512] -- or a multiple of 64 up to 4096 for bf16
- * with P = 64 and N in {64, 128}, the shapes served by the fast chunk
+ * with P = 64 and N in {64, 128, 256, 512}, the shapes served by the fast chunk
  * kernels; H divisible by G; b, L >= 0 (an empty batch or sequence is a valid
  * no-op).  Other sizes return SSD_ERR_UNSUPPORTED.
  */

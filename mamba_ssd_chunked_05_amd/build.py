@@ -26,6 +26,7 @@ SOURCES = [
     "chunk_scan.hip",
     "step.hip",
     "fused.hip",
+    "wide.hip",
 ]
 
 

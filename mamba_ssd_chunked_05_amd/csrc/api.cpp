@@ -87,7 +87,7 @@ ssd_status check_dims(const ssd_dims* d, Need need, ssd::Shape* out) {
     const bool fast = Q % 64 == 0 && (need == Need::kCumsum || ssd::fast_chunk_supported(s));
     if (Q % 16 || Q < 16 || Q > (fast ? 4096 : 512))
         return fail(SSD_ERR_UNSUPPORTED, "chunk %lld: need a multiple of 16 in [16, 512] (multiple of 64 up to "
-                    "4096 for bf16 with headdim 64 and dstate 64/128)", (long long)Q);
+                    "4096 for bf16 with headdim 64 and dstate 64/128/256/512)", (long long)Q);
     s.nC = (s.L + Q - 1) / Q;
     if (s.b * s.nC * s.H * s.N > kMaxGrid || s.H > 65535 || s.b > 65535)
         return fail(SSD_ERR_UNSUPPORTED, "problem too large for one launch grid");

@@ -38,44 +38,10 @@
 //     zero before use (static masking).
 #include "common.hpp"
 #include "launch.hpp"
+#include "tiles.hpp"
 
 namespace ssd {
 namespace fz {
-
-constexpr int P = 64;
-constexpr int QS = 64;        // tokens per chunk
-constexpr int XS = P + 16;    // x row stride (bf16)
-
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-template <int N>
-struct Strides {
-    static constexpr int BS = N + 16;  // B rows: transpose reads
-    static constexpr int CS = N + 8;   // C rows: row reads
-};
-
-// Transpose read: rows [row0, row0+4) x columns [col0, col0+16) of a row-major
-// bf16 LDS tile with leading dimension ld; lane (16g + j) receives column
-// col0 + j, rows row0..row0+3 (row0 may differ between 16-lane groups).
-__device__ __forceinline__ bf16x4 tr_read(const bf16* tile, int row0, int col0, int ld, int l16) {
-    const bf16* p = tile + (row0 + (l16 >> 2)) * ld + col0 + 4 * (l16 & 3);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-}
-
-__device__ __forceinline__ bf16x8 pack8(const bf16x4& a, const bf16x4& b) {
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-__device__ __forceinline__ bf16x4 cvt4(const f32x4& v) {
-    bf16x4 r;
-    r[0] = static_cast<bf16>(v[0]);
-    r[1] = static_cast<bf16>(v[1]);
-    r[2] = static_cast<bf16>(v[2]);
-    r[3] = static_cast<bf16>(v[3]);
-    return r;
-}
-
-__device__ __forceinline__ uint4 ld16(const bf16* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // ---------------------------------------------------------------------------
 // chunk staging shared by both kernels: x (HPW heads), B, C (optional), dt
@@ -107,12 +73,6 @@ struct BRows {
     static constexpr int RPI = 256 / (N / 8);  // B rows covered by one pass of 256 threads
 };
 
-// dt (fp32) and the cumulative log2 decay: over the chunk for the staged calls,
-// restarting at every 64-token sub-chunk in the forward.
-struct DtSrc {
-    const float* dt_t;
-    const float* cs;
-};
 
 // wavefront-uniform bases of one sub-chunk's tiles
 struct TileBase {
@@ -685,6 +645,14 @@ hipError_t launch_scan_fast(const Shape& s, const bf16* x, const bf16* B, const 
     return hipGetLastError();
 }
 
+// wide-state kernels (dstate 256 and 512, one head per workgroup), wide.hip
+template <bool FWD>
+hipError_t state_wide(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states, float* totals,
+                      hipStream_t st);
+template <bool FWD>
+hipError_t scan_wide(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
+                     const float* start, const float* D, bf16* y, hipStream_t st);
+
 // dispatch over (N, heads per workgroup)
 template <bool FWD>
 hipError_t state_dispatch(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
@@ -696,11 +664,12 @@ hipError_t scan_dispatch(const Shape& s, const bf16* x, const bf16* B, const bf1
 }  // namespace fz
 
 bool fast_chunk_supported(const Shape& s) {
-    return s.io == 1 && s.P == 64 && (s.N == 64 || s.N == 128) && s.Q % 64 == 0;
+    return s.io == 1 && s.P == 64 && (s.N == 64 || s.N == 128 || s.N == 256 || s.N == 512) && s.Q % 64 == 0;
 }
 
-// heads per workgroup: two when both heads of every pair read the same group
-static int fast_hpw(const Shape& s) { return (s.H / s.G) % 2 == 0 ? 2 : 1; }
+// heads per workgroup: two when both heads of every pair read the same group (dstate <= 128;
+// the wide-state kernels in wide.hip take one head per workgroup)
+static int fast_hpw(const Shape& s) { return s.N <= 128 && (s.H / s.G) % 2 == 0 ? 2 : 1; }
 
 int fast_heads_per_wg(const Shape& s) { return fast_hpw(s); }
 
@@ -717,6 +686,7 @@ namespace fz {
 template <bool FWD>
 hipError_t state_dispatch(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
                           float* totals, hipStream_t st) {
+    if (s.N >= 256) return state_wide<FWD>(s, x, B, ds, states, totals, st);
     const bool pair = fast_hpw(s) == 2;
     if (s.N == 128)
         return pair ? launch_state_fast<128, 2, FWD>(s, x, B, ds, states, totals, st)
@@ -728,6 +698,7 @@ hipError_t state_dispatch(const Shape& s, const bf16* x, const bf16* B, const Dt
 template <bool FWD>
 hipError_t scan_dispatch(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
                          const float* start, const float* D, bf16* y, hipStream_t st) {
+    if (s.N >= 256) return scan_wide<FWD>(s, x, B, C, ds, start, D, y, st);
     const bool pair = fast_hpw(s) == 2;
     if (s.N == 128)
         return pair ? launch_scan_fast<128, 2, FWD>(s, x, B, C, ds, start, D, y, st)

@@ -1,0 +1,501 @@
+// wide.hip -- chunk-state and chunk-scan kernels for a wide state: bf16 inputs,
+// headdim 64, dstate 256 or 512, any chunk that is a multiple of 64.
+//
+// They compute the same staged calls as fused.hip (the chunk-local states and
+// the chunk output from the chunk-start state, cuTile page on devotd.net,
+// section 2), with the same 64-token sub-chunk walk: per sub-chunk
+//   y  = 2^(l_i) C_i . S + sum_{j<=i} (C_i . B_j) 2^(l_i-l_j) dt_j x_j + D x_i
+//   S <- 2^(l_63) S + sum_j 2^(l_63-l_j) dt_j B_j (outer) x_j.
+// Every term is a sum over the state index n ("3.3 Hardware-Aware ...",
+// section 4.1: the output through C is linear in the state), so a sub-chunk is
+// processed in blocks of 128 state columns: the B and C tiles of one block sit
+// in LDS at a time (the LDS footprint of dstate 128), the products over n
+// accumulate across blocks in registers, and the state update of a block runs
+// right after that block's part of C . S has read the old state.
+//
+// One head per workgroup, four wavefronts; wavefront w carries the fp32 state
+// rows p = 16w .. 16w + 15 for all N columns in registers (N/4 values per lane).
+// Staging of the next block (or the next sub-chunk) runs one step ahead in
+// registers.  Layout and fragment conventions are those of fused.hip.
+#include "common.hpp"
+#include "launch.hpp"
+#include "tiles.hpp"
+
+namespace ssd {
+namespace fz {
+
+constexpr int WB = 128;       // state columns per LDS block
+constexpr int WBS = WB + 16;  // B block row stride (bf16): transpose reads
+constexpr int WCS = WB + 8;   // C block row stride (bf16): row reads
+
+// one head's sub-chunk staging: x (2 pieces), one B/C block (4 + 4 pieces), dt and cs
+struct WideRegs {
+    uint4 x[2];
+    uint4 b[4];
+    uint4 c[4];
+    float dt, cs;
+};
+
+// Per-thread piece coordinates.  x: rows tid / 8 (+ 32), columns 8 (tid % 8);
+// B / C block: rows tid / 16 (+ 16 k), columns 8 (tid % 16) of the block.
+struct WideAddr {
+    int xr, xc, br, bc;
+};
+
+struct WideSrc {
+    const bf16 *x, *B, *C;
+    DtSrc ds;
+    int64_t b, L, dt0;  // dt0: this chunk's first dt/cs element of the head
+    int H, G, N, h, g;
+};
+
+// rows past the sequence end read a valid row and are selected to zero (per word: a select of
+// the whole vector is lowered through private memory)
+__device__ __forceinline__ uint4 ld_row(const bf16* base, int64_t row_stride, int r, int last, int c) {
+    const bool ok = r <= last;
+    const uint4 v = ld16(base + (int64_t)(ok ? r : last) * row_stride + c);
+    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
+// x, dt and cs of sub-chunk `sub` starting at token tbase
+__device__ __forceinline__ void wide_load_x(WideRegs& rg, const WideAddr& a, const WideSrc& s, int64_t tbase, int sub,
+                                            int tid) {
+    const int last = (int)(s.L - 1 - tbase);
+    const bf16* xb = s.x + ((s.b * s.L + tbase) * s.H + s.h) * (int64_t)P;
+    const int64_t HP_ = (int64_t)s.H * P;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) rg.x[k] = ld_row(xb, HP_, a.xr + 32 * k, last, a.xc);
+    if (tid < 64) {
+        rg.dt = s.ds.dt_t[s.dt0 + (int64_t)QS * sub + tid];
+        rg.cs = s.ds.cs[s.dt0 + (int64_t)QS * sub + tid];
+    }
+}
+
+// block nb (columns 128 nb ..) of B (and C) for the sub-chunk starting at tbase
+template <bool WITH_C>
+__device__ __forceinline__ void wide_load_bc(WideRegs& rg, const WideAddr& a, const WideSrc& s, int64_t tbase, int nb) {
+    const int last = (int)(s.L - 1 - tbase);
+    const int64_t GN = (int64_t)s.G * s.N, off = ((s.b * s.L + tbase) * s.G + s.g) * (int64_t)s.N + WB * nb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        rg.b[k] = ld_row(s.B + off, GN, a.br + 16 * k, last, a.bc);
+        if (WITH_C) rg.c[k] = ld_row(s.C + off, GN, a.br + 16 * k, last, a.bc);
+    }
+}
+
+template <bool WITH_C>
+__device__ __forceinline__ void wide_store_bc(bf16* bsb, bf16* csb, const WideRegs& rg, const WideAddr& a) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        *reinterpret_cast<uint4*>(bsb + (a.br + 16 * k) * WBS + a.bc) = rg.b[k];
+        if (WITH_C) *reinterpret_cast<uint4*>(csb + (a.br + 16 * k) * WCS + a.bc) = rg.c[k];
+    }
+}
+
+// x to LDS and the decay vectors of the sub-chunk (wavefront 0); see chunk_store in fused.hip
+template <bool FWD>
+__device__ __forceinline__ void wide_store_x(bf16* xs, float* lw, float* dtw, float* ww, float* ec, float* alpha,
+                                             const WideRegs& rg, const WideAddr& a, float& cs_prev, float& tot,
+                                             int tid) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4*>(xs + (a.xr + 32 * k) * XS + a.xc) = rg.x[k];
+    if (tid < 64) {
+        const int lane = tid;
+        const float d = rg.dt;
+        float incl;
+        if (FWD) {
+            incl = rg.cs;
+        } else {
+            incl = rg.cs - cs_prev;
+            cs_prev = __shfl(rg.cs, 63, 64);
+        }
+        const float last = __shfl(incl, 63, 64);
+        tot += last;
+        lw[lane] = incl;
+        dtw[lane] = d;
+        ww[lane] = fast_exp2(last - incl) * d;
+        if (ec) {
+            ec[lane] = fast_exp2(incl - __shfl(incl, lane & ~15, 64));
+#pragma unroll
+            for (int it = 1; it < 4; ++it) ec[it * QS + lane] = fast_exp2(fminf(__shfl(incl, 16 * it, 64) - incl, 0.0f)) * d;
+        }
+        if (lane == 0) alpha[0] = fast_exp2(last);
+    }
+}
+
+__device__ __forceinline__ void wide_addr(WideAddr& a, int tid) {
+    a.xr = tid >> 3;
+    a.xc = (tid & 7) * 8;
+    a.br = tid >> 4;
+    a.bc = (tid & 15) * 8;
+}
+
+// ---------------------------------------------------------------------------
+// chunk output
+// ---------------------------------------------------------------------------
+struct WideScanLds {
+    bf16 xs[QS * XS];
+    bf16 bs[QS * WBS];
+    bf16 cs[QS * WCS];
+    bf16 mb[16 * 256];  // decayed C.B^T tiles in fragment order [jt*4+it][lane][4]
+    float lw[QS], dtw[QS], ww[QS];
+    float ec[4 * QS];
+    float alpha[4];
+};
+
+// dstate 512 keeps 128 state values per lane: one wavefront per SIMD, all registers
+template <int N, bool FWD>
+__global__ void __launch_bounds__(256, N >= 512 ? 1 : 2)
+chunk_scan_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, const bf16* __restrict__ C,
+                       DtSrc ds, const float* __restrict__ start, const float* __restrict__ D, bf16* __restrict__ y,
+                       int64_t L, int H, int G, int Q, int64_t nC, uint32_t nitems) {
+    constexpr int NBLK = N / WB, NT = N / 16;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    WideScanLds& sm = *reinterpret_cast<WideScanLds*>(smem_raw);
+
+    const uint32_t item = xcd_remap(blockIdx.x, nitems);
+    const int h = (int)(item % (uint32_t)H);
+    const int64_t c = (item / (uint32_t)H) % (uint32_t)nC;
+    const int64_t b = item / ((uint32_t)H * (uint32_t)nC);
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+    const float Dh = D ? D[h] : 0.0f;
+    const int64_t t0 = c * Q;
+    const int64_t t_end = t0 + Q < L ? t0 + Q : L;
+    const int nsub = (int)((t_end - t0 + QS - 1) / QS);
+    const int64_t nsubT = (L + QS - 1) / QS;
+    float cs_prev = 0.0f, tot = 0.0f;
+
+    // carried state, transposed: st[nt] holds S[p = 16w + l16][n = 16nt + 4g4 + r]
+    f32x4 st[NT];
+    {
+        const float* S0 = start + ((b * nC + c) * H + h) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 4 * g4;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st[nt] = *reinterpret_cast<const f32x4*>(S0 + 16 * nt);
+    }
+    // tiles above the diagonal that pair with a diagonal tile in a 32-wide K step stay zero
+    sm.mb[(1 * 4 + 0) * 256 + tid] = static_cast<bf16>(0.0f);
+    sm.mb[(3 * 4 + 2) * 256 + tid] = static_cast<bf16>(0.0f);
+
+    WideSrc src;
+    src.x = x, src.B = B, src.C = C, src.ds = ds, src.b = b, src.L = L, src.H = H, src.G = G, src.N = N, src.h = h,
+    src.g = g;
+    src.dt0 = FWD ? ((b * H + h) * nsubT + c * (Q / QS)) * QS : ((b * H + h) * nC + c) * Q;
+    WideAddr ad;
+    wide_addr(ad, tid);
+    WideRegs rg;
+    wide_load_x(rg, ad, src, t0, 0, tid);
+    wide_load_bc<true>(rg, ad, src, t0, 0);
+
+    for (int sc = 0; sc < nsub; ++sc) {
+        const int64_t tbase = t0 + (int64_t)sc * QS;
+        const bool more = sc + 1 < nsub;
+        __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
+        wide_store_x<FWD>(sm.xs, sm.lw, sm.dtw, sm.ww, sm.ec, sm.alpha, rg, ad, cs_prev, tot, tid);
+        wide_store_bc<true>(sm.bs, sm.cs, rg, ad);
+        __syncthreads();
+        if (more) wide_load_x(rg, ad, src, tbase + QS, sc + 1, tid);
+        if (NBLK > 1)
+            wide_load_bc<true>(rg, ad, src, tbase, 1);
+        else if (more)
+            wide_load_bc<true>(rg, ad, src, tbase + QS, 0);
+
+        // decay-scaled X^T fragments (token slots 32ks + 4g4 + r, 32ks + 16 + 4g4 + r)
+        Frag<bf16> xw[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            Frag<bf16> xf;
+            xf.v = pack8(tr_read(sm.xs, 32 * ks + 4 * g4, 16 * w, XS, l16),
+                         tr_read(sm.xs, 32 * ks + 16 + 4 * g4, 16 * w, XS, l16));
+            const float* wv = &sm.ww[32 * ks + 4 * g4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                xw[ks].v[r] = static_cast<bf16>(static_cast<float>(xf.v[r]) * wv[r]);
+                xw[ks].v[4 + r] = static_cast<bf16>(static_cast<float>(xf.v[4 + r]) * wv[16 + r]);
+            }
+        }
+        const float alpha = sm.alpha[0];
+        f32x4 acc[4], gacc[3];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 3; ++q) gacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+        for (int nb = 0; nb < NBLK; ++nb) {
+            if (nb > 0) {
+                __syncthreads();  // every wavefront is done with the previous block
+                wide_store_bc<true>(sm.bs, sm.cs, rg, ad);
+                __syncthreads();
+                if (nb + 1 < NBLK)
+                    wide_load_bc<true>(rg, ad, src, tbase, nb + 1);
+                else if (more)
+                    wide_load_bc<true>(rg, ad, src, tbase + QS, 0);
+            }
+            // C.B^T over this block's 128 columns for this wavefront's tiles w, w + 4 (, w + 8)
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const int tt = w + 4 * q;
+                if (tt < 10) {
+                    const int it = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+                    const int jt = tt - it * (it + 1) / 2;
+#pragma unroll
+                    for (int ks = 0; ks < WB / 32; ++ks) {
+                        Frag<bf16> a, bo;
+                        frag_load8<bf16>(a, &sm.bs[(16 * jt + l16) * WBS + 32 * ks + 8 * g4]);
+                        frag_load8<bf16>(bo, &sm.cs[(16 * it + l16) * WCS + 32 * ks + 8 * g4]);
+                        mma(gacc[q], a, bo);
+                    }
+                }
+            }
+            // S C^T over this block, from the state before this sub-chunk's update
+#pragma unroll
+            for (int ks = 0; ks < WB / 32; ++ks) {
+                Frag<bf16> sa;
+                sa.v = pack8(cvt4(st[nb * (WB / 16) + 2 * ks]), cvt4(st[nb * (WB / 16) + 2 * ks + 1]));
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const bf16* crow = &sm.cs[(16 * it + l16) * WCS + 32 * ks];
+                    Frag<bf16> bo;
+                    bo.v = pack8(*reinterpret_cast<const bf16x4*>(crow + 4 * g4),
+                                 *reinterpret_cast<const bf16x4*>(crow + 16 + 4 * g4));
+                    mma(acc[it], sa, bo);
+                }
+            }
+            // S <- 2^(l_63) S + B^T (w x) on this block's columns
+#pragma unroll
+            for (int nt = 0; nt < WB / 16; ++nt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[nb * (WB / 16) + nt][r] *= alpha;
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int nt = 0; nt < WB / 16; ++nt) {
+                    Frag<bf16> a;
+                    a.v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * nt, WBS, l16),
+                                tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * nt, WBS, l16));
+                    mma(st[nb * (WB / 16) + nt], a, xw[ks]);
+                }
+            }
+        }
+
+        // decayed C.B^T tiles -> LDS (D_h on the diagonal, so X^T M also yields D x)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const int tt = w + 4 * q;
+            if (tt < 10) {
+                const int it = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+                const int jt = tt - it * (it + 1) / 2;
+                const int i = 16 * it + l16, j0 = 16 * jt + 4 * g4;
+                f32x4 m;
+                if (jt == it) {
+                    const float li = sm.lw[i];
+                    const f32x4 lj = *reinterpret_cast<const f32x4*>(&sm.lw[j0]);
+                    const f32x4 dj = *reinterpret_cast<const f32x4*>(&sm.dtw[j0]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float v = gacc[q][r] * fast_exp2(fminf(li - lj[r], 0.0f)) * dj[r];
+                        m[r] = (j0 + r <= i ? v : 0.0f) + (j0 + r == i ? Dh : 0.0f);
+                    }
+                } else {
+                    const float er = sm.ec[i];
+                    const f32x4 ej = *reinterpret_cast<const f32x4*>(&sm.ec[it * QS + j0]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m[r] = gacc[q][r] * er * ej[r];
+                }
+                *reinterpret_cast<bf16x4*>(&sm.mb[((jt * 4 + it) * 64 + lane) * 4]) = cvt4(m);
+            }
+        }
+        __syncthreads();
+
+        // Y^T[p-tile w] = 2^l_i (S C^T) + X^T M
+        const bool full = tbase + QS <= L;
+        bf16* yb = y + ((b * L + tbase) * H + h) * (int64_t)P + 16 * w + 4 * g4;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int i = 16 * it + l16;
+            const float sc_i = fast_exp2(sm.lw[i]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[it][r] *= sc_i;
+#pragma unroll
+            for (int js = 0; js <= it / 2; ++js) {
+                Frag<bf16> a, bo;
+                a.v = pack8(tr_read(sm.xs, 32 * js + 4 * g4, 16 * w, XS, l16),
+                            tr_read(sm.xs, 32 * js + 16 + 4 * g4, 16 * w, XS, l16));
+                bo.v = pack8(*reinterpret_cast<const bf16x4*>(&sm.mb[(((2 * js) * 4 + it) * 64 + lane) * 4]),
+                             *reinterpret_cast<const bf16x4*>(&sm.mb[(((2 * js + 1) * 4 + it) * 64 + lane) * 4]));
+                mma(acc[it], a, bo);
+            }
+            if (full || tbase + i < L) {
+                bf16x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(acc[it][r]);
+                *reinterpret_cast<bf16x4*>(yb + (int64_t)i * H * P) = o;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// chunk-local states (hi + lo split of the decay-scaled operand, as in fused.hip)
+// ---------------------------------------------------------------------------
+struct WideAggLds {
+    bf16 xs[QS * XS];
+    bf16 bs[QS * WBS];
+    float lw[QS], dtw[QS], ww[QS];
+    float alpha[4];
+};
+
+template <int N, bool FWD>
+__global__ void __launch_bounds__(256, 2)
+chunk_state_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, DtSrc ds, float* __restrict__ states,
+                        float* __restrict__ totals, int64_t L, int H, int G, int Q, int64_t nC, uint32_t nitems) {
+    constexpr int NBLK = N / WB, NT = N / 16;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    WideAggLds& sm = *reinterpret_cast<WideAggLds*>(smem_raw);
+
+    const uint32_t item = xcd_remap(blockIdx.x, nitems);
+    const int h = (int)(item % (uint32_t)H);
+    const int64_t c = (item / (uint32_t)H) % (uint32_t)nC;
+    const int64_t b = item / ((uint32_t)H * (uint32_t)nC);
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+    const int64_t t0 = c * Q;
+    const int64_t t_end = t0 + Q < L ? t0 + Q : L;
+    const int nsub = (int)((t_end - t0 + QS - 1) / QS);
+    const int64_t nsubT = (L + QS - 1) / QS;
+    float cs_prev = 0.0f, tot = 0.0f;
+
+    f32x4 st[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) st[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    WideSrc src;
+    src.x = x, src.B = B, src.C = nullptr, src.ds = ds, src.b = b, src.L = L, src.H = H, src.G = G, src.N = N,
+    src.h = h, src.g = g;
+    src.dt0 = FWD ? ((b * H + h) * nsubT + c * (Q / QS)) * QS : ((b * H + h) * nC + c) * Q;
+    WideAddr ad;
+    wide_addr(ad, tid);
+    WideRegs rg;
+    wide_load_x(rg, ad, src, t0, 0, tid);
+    wide_load_bc<false>(rg, ad, src, t0, 0);
+
+    for (int sc = 0; sc < nsub; ++sc) {
+        const int64_t tbase = t0 + (int64_t)sc * QS;
+        const bool more = sc + 1 < nsub;
+        __syncthreads();
+        wide_store_x<FWD>(sm.xs, sm.lw, sm.dtw, sm.ww, nullptr, sm.alpha, rg, ad, cs_prev, tot, tid);
+        wide_store_bc<false>(sm.bs, nullptr, rg, ad);
+        __syncthreads();
+        if (more) wide_load_x(rg, ad, src, tbase + QS, sc + 1, tid);
+        if (NBLK > 1)
+            wide_load_bc<false>(rg, ad, src, tbase, 1);
+        else if (more)
+            wide_load_bc<false>(rg, ad, src, tbase + QS, 0);
+
+        Frag<bf16> xh[2], xl[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x4 lo4 = tr_read(sm.xs, 32 * ks + 4 * g4, 16 * w, XS, l16);
+            const bf16x4 hi4 = tr_read(sm.xs, 32 * ks + 16 + 4 * g4, 16 * w, XS, l16);
+            const float* wv = &sm.ww[32 * ks + 4 * g4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v0 = static_cast<float>(lo4[r]) * wv[r];
+                const float v1 = static_cast<float>(hi4[r]) * wv[16 + r];
+                const bf16 h0v = static_cast<bf16>(v0), h1v = static_cast<bf16>(v1);
+                xh[ks].v[r] = h0v;
+                xh[ks].v[4 + r] = h1v;
+                xl[ks].v[r] = static_cast<bf16>(v0 - static_cast<float>(h0v));
+                xl[ks].v[4 + r] = static_cast<bf16>(v1 - static_cast<float>(h1v));
+            }
+        }
+        const float alpha = sm.alpha[0];
+#pragma unroll
+        for (int nb = 0; nb < NBLK; ++nb) {
+            if (nb > 0) {
+                __syncthreads();
+                wide_store_bc<false>(sm.bs, nullptr, rg, ad);
+                __syncthreads();
+                if (nb + 1 < NBLK)
+                    wide_load_bc<false>(rg, ad, src, tbase, nb + 1);
+                else if (more)
+                    wide_load_bc<false>(rg, ad, src, tbase + QS, 0);
+            }
+#pragma unroll
+            for (int nt = 0; nt < WB / 16; ++nt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[nb * (WB / 16) + nt][r] *= alpha;
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int nt = 0; nt < WB / 16; ++nt) {
+                    Frag<bf16> a;
+                    a.v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * nt, WBS, l16),
+                                tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * nt, WBS, l16));
+                    mma(st[nb * (WB / 16) + nt], a, xh[ks]);
+                    mma(st[nb * (WB / 16) + nt], a, xl[ks]);
+                }
+            }
+        }
+    }
+    // a ragged last chunk ends at position Q-1 all the same: its padded tokens have dt = 0 and decay 1
+    float* out = states + ((b * nC + c) * H + h) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 4 * g4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(out + 16 * nt) = st[nt];
+    if (FWD && tid == 0) totals[(b * H + h) * nC + c] = tot;
+}
+
+template <int N, bool FWD>
+hipError_t launch_state_wide(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
+                             float* totals, hipStream_t st) {
+    const uint32_t nitems = (uint32_t)(s.b * s.nC * s.H);
+    if (nitems == 0) return hipSuccess;
+    const size_t lds = sizeof(WideAggLds);
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_wide_kernel<N, FWD>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_state_wide_kernel<N, FWD>), dim3(nitems), dim3(256), lds, st, x, B, ds, states, totals,
+                       s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+    return hipGetLastError();
+}
+
+template <int N, bool FWD>
+hipError_t launch_scan_wide(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
+                            const float* start, const float* D, bf16* y, hipStream_t st) {
+    const uint32_t nitems = (uint32_t)(s.b * s.nC * s.H);
+    if (nitems == 0) return hipSuccess;
+    const size_t lds = sizeof(WideScanLds);
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_scan_wide_kernel<N, FWD>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_scan_wide_kernel<N, FWD>), dim3(nitems), dim3(256), lds, st, x, B, C, ds, start, D, y,
+                       s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+    return hipGetLastError();
+}
+
+template <bool FWD>
+hipError_t state_wide(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states, float* totals,
+                      hipStream_t st) {
+    return s.N == 512 ? launch_state_wide<512, FWD>(s, x, B, ds, states, totals, st)
+                      : launch_state_wide<256, FWD>(s, x, B, ds, states, totals, st);
+}
+
+template <bool FWD>
+hipError_t scan_wide(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
+                     const float* start, const float* D, bf16* y, hipStream_t st) {
+    return s.N == 512 ? launch_scan_wide<512, FWD>(s, x, B, C, ds, start, D, y, st)
+                      : launch_scan_wide<256, FWD>(s, x, B, C, ds, start, D, y, st);
+}
+
+template hipError_t state_wide<false>(const Shape&, const bf16*, const bf16*, const DtSrc&, float*, float*,
+                                      hipStream_t);
+template hipError_t state_wide<true>(const Shape&, const bf16*, const bf16*, const DtSrc&, float*, float*,
+                                     hipStream_t);
+template hipError_t scan_wide<false>(const Shape&, const bf16*, const bf16*, const bf16*, const DtSrc&, const float*,
+                                     const float*, bf16*, hipStream_t);
+template hipError_t scan_wide<true>(const Shape&, const bf16*, const bf16*, const bf16*, const DtSrc&, const float*,
+                                    const float*, bf16*, hipStream_t);
+
+}  // namespace fz
+}  // namespace ssd

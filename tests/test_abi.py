@@ -73,7 +73,7 @@ def _forward(d, ws_bytes=1 << 40, **over):
     (_d(N=2048), UNSUP),
     (_d(Q=100), UNSUP),
     (_d(Q=8192), UNSUP),
-    (_d(Q=1024, N=256), UNSUP),
+    (_d(Q=1024, N=192), UNSUP),
     (_d(Q=1024, io=0), UNSUP),
     (_d(Q=-16), SHAPE),
 ])

@@ -27,11 +27,15 @@ CASES = [
     (1, 70, 1, 256, 64, 1, 16, "bf16"),
     (1, 200, 2, 16, 1024, 1, 48, "f32"),
     (1, 512, 2, 64, 32, 2, 512, "bf16"),
-    # fast chunk kernels (bf16, P = 64, N in {64, 128}, Q a multiple of 64, up to 4096)
+    # fast chunk kernels (bf16, P = 64, N in {64, 128, 256, 512}, Q a multiple of 64, up to 4096)
     (1, 3000, 4, 64, 128, 1, 1024, "bf16"),
     (2, 1100, 6, 64, 64, 3, 512, "bf16"),
     (1, 700, 3, 64, 128, 1, 192, "bf16"),
     (1, 5000, 2, 64, 64, 1, 4096, "bf16"),
+    # wide-state fast kernels (dstate 256 / 512, one head per workgroup, 128-column blocks)
+    (1, 700, 2, 64, 256, 1, 192, "bf16"),
+    (2, 450, 4, 64, 512, 2, 256, "bf16"),
+    (1, 1300, 3, 64, 256, 3, 1024, "bf16"),
 ]
 
 
@@ -219,7 +223,7 @@ def test_step_shapes(gpu_ssd, P, N, dtype):
     assert_close_state(host(S), ref["final"])
 
 
-# shapes that take the fused forward (chunk = 0, bf16, headdim 64, dstate 64/128): ragged tails,
+# shapes that take the fused forward (chunk = 0, bf16, headdim 64, dstate 64 to 512): ragged tails,
 # several segments, G > 1, h0, long memory, sequences shorter than one 64-token chunk
 FUSED = [
     (1, 1, 4, 64, 128, 1, "config"),
@@ -229,6 +233,9 @@ FUSED = [
     (3, 1500, 8, 64, 64, 2, "long_memory"),
     (1, 9000, 2, 64, 128, 1, "extreme"),
     (1, 20000, 4, 64, 64, 1, "per_head_bias"),
+    (1, 1000, 4, 64, 256, 1, "long_memory"),
+    (2, 333, 2, 64, 512, 2, "config"),
+    (1, 3000, 2, 64, 512, 1, "extreme"),
 ]
 
 
