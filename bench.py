@@ -68,15 +68,27 @@ def scan_bytes_per_token(H, P, N, G, Q, s_io):
     return H * (P * 2 * s_io + 8 + P * N * 4 / Q) + 2 * G * N * s_io
 
 
-def measured_traffic(kernel_source: str, summary: str):
+def kernel_sources_sha(paths) -> str:
+    """sha256 over the concatenated kernel sources (the .hip file and the headers it includes)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+SCAN_SOURCES = [os.path.join(ROOT, "mamba_ssd_chunked_05_amd", "csrc", f) for f in ("fused.hip", "tiles.hpp", "common.hpp")]
+
+
+def measured_traffic(kernel_sources, summary: str):
     """HBM bytes per launch from a committed counter summary, or None if the kernel changed since.
 
     The summary records FETCH_SIZE and WRITE_SIZE per dispatch, already scaled by the factors a
     plain device copy of known size gives for the same counters, and the sha256 of the kernel
-    source they were taken on.
+    sources they were taken on.
     """
-    import hashlib
-
     try:
         fields = {}
         with open(summary) as f:
@@ -84,9 +96,7 @@ def measured_traffic(kernel_source: str, summary: str):
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     fields[k.strip()] = v.strip()
-        with open(kernel_source, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if fields.get("source_sha256") != sha:
+        if fields.get("source_sha256") != kernel_sources_sha(kernel_sources):
             return None
         return float(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -228,7 +238,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": scan_gbs / PEAK_HBM_GBS,
-            "traffic": measured_traffic(os.path.join(ROOT, "mamba_ssd_chunked_05_amd", "csrc", "fused.hip"),
+            "traffic": measured_traffic(SCAN_SOURCES,
                                         os.path.join(ROOT, "profiles", f"chunk_scan_{args.workload}_traffic.txt")),
             "avg_launch_ms": scan_ms,
             "algorithmic_bytes_per_launch": scan_bytes,
