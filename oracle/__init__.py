@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the Mamba-2 SSD forward scan and its decode step.
+"""fp64 CPU oracle for the Mamba-2 SSD forward scan, its decode step and the Mamba-1 selective scan.
 
 TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no
@@ -60,8 +60,10 @@ def _load():
                                                + [ctypes.c_double] * 2 + [_DP] * 2)
         lib.ssd_oracle_state_passing.argtypes = [_I64] * 6 + [_DP] * 5
         lib.ssd_oracle_chunk_scan.argtypes = [_I64] * 7 + [_DP] * 8 + [ctypes.c_int]
+        lib.ssd_oracle_selective_scan.argtypes = [_I64] * 5 + [_DP] * 9 + [ctypes.c_int] * 2
         for f in ("ssd_oracle_forward", "ssd_oracle_step", "ssd_oracle_chunk_cumsum",
-                  "ssd_oracle_state_passing", "ssd_oracle_chunk_scan", "ssd_oracle_dt_frontend"):
+                  "ssd_oracle_state_passing", "ssd_oracle_chunk_scan", "ssd_oracle_dt_frontend",
+                  "ssd_oracle_selective_scan"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -193,3 +195,22 @@ def chunk_scan(x, dt, A, B, C, chunk_start, D=None, *, chunk: int, threads: int 
     rc = _load().ssd_oracle_chunk_scan(b, L, H, P, N, G, chunk, *ptrs, py, threads)
     _check(rc, "chunk_scan")
     return y
+
+
+def selective_scan(x, delta, A, B, C, D=None, h0=None, *, zoh: bool = True, threads: int = 0):
+    """Mamba-1 selective scan by the token recurrence.  x, delta (b,L,Dc); A (Dc,N); B, C (b,L,G,N);
+    D (Dc,) or None; h0 (b,Dc,N) or None.  ``delta`` is the step after any front-end; ``zoh`` picks
+    the zero-order-hold input matrix (else delta * B).  Returns dict(y, final)."""
+    b, L, Dc = x.shape
+    G, N = B.shape[2], B.shape[3]
+    keep = []
+    ptrs = []
+    for a in (x, delta, A, B, C, D, h0):
+        arr, p = _in(a)
+        keep.append(arr)
+        ptrs.append(p)
+    y, py = _out((b, L, Dc))
+    fin, pf = _out((b, Dc, N))
+    rc = _load().ssd_oracle_selective_scan(b, L, Dc, N, G, *ptrs, py, pf, int(zoh), threads)
+    _check(rc, "selective_scan")
+    return {"y": y, "final": fin}

@@ -291,3 +291,60 @@ int ssd_oracle_chunk_scan(int64_t b, int64_t L, int64_t H, int64_t P, int64_t N,
     }
     return err ? -2 : 0;
 }
+
+/*
+ * Mamba-1 selective scan (the per-channel selective SSM of "3.3 Hardware-Aware
+ * algorithms and GPU memory hierarchy optimisation", sections 2.1 and 3): for
+ * every batch row b and channel d (group g = d / (Dc / G)), with a diagonal
+ * state of N entries and a per-entry A[d,n]:
+ *
+ *   h <- h0[b,d] (or 0)
+ *   for t = 0 .. L-1:
+ *       abar[n] = exp(delta[b,t,d] * A[d,n])
+ *       bbar[n] = (exp(delta A[d,n]) - 1) / A[d,n] * B[b,t,g,n]   zero-order hold (zoh != 0;
+ *                                                                 delta * B when A[d,n] == 0)
+ *               = delta[b,t,d] * B[b,t,g,n]                        otherwise
+ *       h[n] = abar[n] * h[n] + bbar[n] * x[b,t,d]
+ *       y[b,t,d] = sum_n C[b,t,g,n] * h[n] + Dskip[d] * x[b,t,d]
+ *   final[b,d] = h
+ *
+ * delta is the step after any front-end (bias, softplus, clamp).  Layouts:
+ * x, delta, y (b,L,Dc); A (Dc,N); B, C (b,L,G,N); Dskip (Dc); h0, final
+ * (b,Dc,N).  Threads split the independent (b, d) rows.
+ */
+int ssd_oracle_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, int64_t G,
+                              const double* x, const double* delta, const double* A,
+                              const double* B, const double* C, const double* Dskip,
+                              const double* h0, double* y, double* final_state, int zoh,
+                              int nthreads) {
+    if (b < 0 || L < 0 || Dc <= 0 || N <= 0 || G <= 0 || (Dc % G) != 0) return -1;
+    int64_t cpg = Dc / G;
+    set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bd = 0; bd < b * Dc; ++bd) {
+        int64_t bb = bd / Dc, d = bd % Dc, g = d / cpg;
+        double* h = (double*)calloc((size_t)N, sizeof(double));
+        if (!h) { err = 1; continue; }
+        if (h0) memcpy(h, h0 + bd * N, sizeof(double) * N);
+        const double* Ad = A + d * N;
+        for (int64_t t = 0; t < L; ++t) {
+            int64_t bt = bb * L + t;
+            double dl = delta[bt * Dc + d], xv = x[bt * Dc + d];
+            const double* Bt = B + (bt * G + g) * N;
+            const double* Ct = C + (bt * G + g) * N;
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double abar = exp(dl * Ad[n]);
+                double bbar = dl * Bt[n];
+                if (zoh && Ad[n] != 0.0) bbar = expm1(dl * Ad[n]) / Ad[n] * Bt[n];
+                h[n] = abar * h[n] + bbar * xv;
+                acc += Ct[n] * h[n];
+            }
+            if (y) y[bt * Dc + d] = acc + (Dskip ? Dskip[d] * xv : 0.0);
+        }
+        if (final_state) memcpy(final_state + bd * N, h, sizeof(double) * N);
+        free(h);
+    }
+    return err ? -2 : 0;
+}

@@ -7,12 +7,16 @@ oracle and the HIP library can be fed from it without sharing method code.
 
 from .gen import (  # noqa: F401
     CONFIGS,
+    SELECTIVE_CONFIGS,
+    SelectiveInputs,
     StepInputs,
     ForwardInputs,
     bf16_round,
     config_shapes,
     make_config_inputs,
     make_forward_inputs,
+    make_selective_config_inputs,
+    make_selective_inputs,
     make_step_inputs,
     round_to,
     seed_for,

@@ -1,4 +1,5 @@
-"""Seeded input generators for the Mamba-2 SSD forward scan and its decode step.
+"""Seeded input generators for the Mamba-2 SSD forward scan, its decode step and the
+Mamba-1 selective scan.
 
 Value distributions follow the workload description of the SSD benchmark
 configurations (tiny fp32 case, 130M-shaped, 2.7B-shaped, long-context state
@@ -13,6 +14,11 @@ sweep, decode step):
 * B, C ~ N(0, 1) / sqrt(N)
 * D ~ N(0, 1)
 * h0 = 0 for the prefill configurations; the decode state ~ N(0, 0.1^2)
+
+The Mamba-1 selective scan takes the same recipes per channel: x ~ N(0, 1), the
+step delta log-uniform on [1e-3, 0.1] (through the same softplus construction),
+B, C ~ N(0, 1) / sqrt(N), D ~ N(0, 1), and A[d, n] = -exp(U(log 1, log 16))
+drawn independently for every (channel, state) entry.
 
 Everything is drawn in float64 from ``numpy.random.default_rng(seed)`` (PCG64)
 and then rounded (round-to-nearest-even) to the storage dtype of the device
@@ -244,3 +250,75 @@ def make_step_inputs(
         C=round_to(np.stack(Cs), dtype),
         dtype=dtype,
     )
+
+
+# ---------------------------------------------------------------------------
+# Mamba-1 selective scan
+# ---------------------------------------------------------------------------
+
+#: Selective-scan workload: the 2.7B-shaped width (80 heads x 64 = 5120 channels) at the longest
+#: 2.7B sequence length, with Mamba-1's per-channel diagonal state of 16 entries.
+SELECTIVE_CONFIGS: Dict[str, dict] = {
+    "mamba1_5120ch_64k": dict(batch=1, seqlen=64 * K, channels=5120, dstate=16, ngroups=1, dtype="bf16"),
+}
+
+
+@dataclasses.dataclass
+class SelectiveInputs:
+    x: np.ndarray  # (b, L, Dc)
+    delta: np.ndarray  # (b, L, Dc): the step after the front-end
+    A: np.ndarray  # (Dc, N)
+    B: np.ndarray  # (b, L, G, N)
+    C: np.ndarray  # (b, L, G, N)
+    D: Optional[np.ndarray]  # (Dc,) or None
+    h0: Optional[np.ndarray]  # (b, Dc, N) or None
+    dtype: str
+
+    @property
+    def dims(self):
+        b, L, Dc = self.x.shape
+        G, N = self.B.shape[2], self.B.shape[3]
+        return b, L, Dc, N, G
+
+
+def make_selective_inputs(
+    batch: int,
+    seqlen: int,
+    channels: int,
+    dstate: int,
+    ngroups: int = 1,
+    dtype: str = "bf16",
+    seed: int = 0,
+    *,
+    dt_mode: str = "config",
+    with_D: bool = True,
+    h0_std: float = 0.0,
+) -> SelectiveInputs:
+    """Draw one selective-scan problem (delta modes as for the SSD step)."""
+    if channels % ngroups:
+        raise ValueError("channels must be a multiple of ngroups")
+    rng = np.random.default_rng(seed)
+    b, L, Dc, N, G = batch, seqlen, channels, dstate, ngroups
+    x = rng.standard_normal((b, L, Dc))
+    delta = _draw_dt(rng, (b, L, Dc), dt_mode, Dc)
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), size=(Dc, N)))
+    Bm = rng.standard_normal((b, L, G, N)) / math.sqrt(N)
+    Cm = rng.standard_normal((b, L, G, N)) / math.sqrt(N)
+    D = rng.standard_normal((Dc,)) if with_D else None
+    h0 = rng.standard_normal((b, Dc, N)) * h0_std if h0_std > 0 else None
+    return SelectiveInputs(
+        x=round_to(x, dtype),
+        delta=round_to(delta, dtype),
+        A=round_to(A, "f32"),
+        B=round_to(Bm, dtype),
+        C=round_to(Cm, dtype),
+        D=None if D is None else round_to(D, "f32"),
+        h0=None if h0 is None else round_to(h0, "f32"),
+        dtype=dtype,
+    )
+
+
+def make_selective_config_inputs(name: str, seed: int = 5) -> SelectiveInputs:
+    cfg = SELECTIVE_CONFIGS[name]
+    return make_selective_inputs(cfg["batch"], cfg["seqlen"], cfg["channels"], cfg["dstate"], cfg["ngroups"],
+                                 cfg["dtype"], seed)
