@@ -228,6 +228,45 @@ ssd_status ssd_step_multi_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, fl
                              const void* x, const void* dt, const float* A, const void* B,
                              const void* C, const float* D, void* y, void* stream);
 
+/*
+ * Mamba-1 selective scan: a per-channel diagonal state with a per-entry decay
+ * rate, discretised, scanned and read out through C in one fused call ("3.3
+ * Hardware-Aware algorithms and GPU memory hierarchy optimisation": section
+ * 2.1 for the discretisation abar = exp(delta A) and the zero-order-hold
+ * bbar, section 3 for the fused load / discretise / scan / output steps,
+ * section 4.1 for the associativity that lets the sequence run in segments).
+ * For every batch row b and channel d (group g = d / (Dc / G)), n < N:
+ *     h[n] <- h0[b, d, n] (or 0)
+ *     for t < L:  e = exp(delta[b,t,d] A[d,n])
+ *                 h[n] <- e h[n] + f x[b,t,d] B[b,t,g,n],
+ *                        f = (e - 1) / A[d,n]  (zero-order hold; delta where A[d,n] == 0)
+ *                        f = delta[b,t,d]      (without zoh)
+ *                 y[b,t,d] = sum_n C[b,t,g,n] h[n] + D[d] x[b,t,d]
+ *     final_state[b, d] = h
+ * dims: batch = b, seqlen = L, nheads = the channel count Dc, headdim = 1,
+ * dstate = N, ngroups = G, io = dtype of x, delta, B, C and y; chunk = the
+ * length of the sequence segments the call scans in parallel (0: the
+ * library's choice; otherwise a multiple of 64).  The result does not depend
+ * on the segment length beyond rounding.
+ * fe (may be NULL): the step front-end of ssd_dt_frontend, per channel
+ * (dt_bias has Dc entries): delta <- clamp(softplus(delta + bias)); zoh
+ * selects the zero-order-hold input (else delta B).  A NULL fe means the raw
+ * delta is the step and the input is delta B.
+ * Layouts (row-major, contiguous): x, delta, y (b, L, Dc); A (Dc, N) and D (Dc)
+ * float32; B, C (b, L, G, N); h0, final_state (b, Dc, N) float32.  D and h0
+ * may be NULL.  x, delta, B, C and y must be 16-byte aligned.
+ * Supported: N in {16, 32, 48, 64} and Dc / G a multiple of 16
+ * (SSD_ERR_UNSUPPORTED otherwise).
+ * workspace: ssd_selective_scan_workspace_bytes(dims) bytes, 256-byte aligned
+ * (NULL allowed when that is 0: a single segment).  y and final_state must not
+ * overlap the inputs, each other or the workspace.
+ */
+size_t ssd_selective_scan_workspace_bytes(const ssd_dims* dims);
+ssd_status ssd_selective_scan(const ssd_dims* dims, const ssd_dt_frontend* fe, const void* x,
+                              const void* delta, const float* A, const void* B, const void* C,
+                              const float* D, const float* h0, void* y, float* final_state,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* ssd_status_string(ssd_status status);
 

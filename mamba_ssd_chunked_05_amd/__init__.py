@@ -109,6 +109,7 @@ def load():
         "ssd_step_ex": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_step_multi_ex": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_query_config": [dp] + [ctypes.POINTER(ctypes.c_int)] * 4,
+        "ssd_selective_scan": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -116,6 +117,8 @@ def load():
         fn.restype = ctypes.c_int
     lib.ssd_forward_workspace_bytes.argtypes = [dp]
     lib.ssd_forward_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssd_selective_scan_workspace_bytes.argtypes = [dp]
+    lib.ssd_selective_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssd_status_string.argtypes = [ctypes.c_int]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_last_error.argtypes = []
@@ -291,6 +294,49 @@ def step_multi(state, x, dt, A, B, C, D=None, *, y=None, frontend: Optional[Fron
                                _ptr(B), _ptr(C), _ptr(D), _ptr(y), _stream(x))
     _check(st, "ssd_step_multi")
     return y
+
+
+def selective_scan_workspace_bytes(b, L, Dc, N, G=1, *, chunk: int = 0, dtype=torch.bfloat16) -> int:
+    d = _dims(b, L, Dc, 1, N, G, chunk, _IO[dtype])
+    return int(load().ssd_selective_scan_workspace_bytes(ctypes.byref(d)))
+
+
+def selective_scan(x, delta, A, B, C, D=None, h0=None, *, chunk: int = 0, y=None, final_state=None,
+                   workspace=None, frontend: Optional[Frontend] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Mamba-1 selective scan on the current stream: x, delta (b, L, Dc); A (Dc, N) float32; B, C
+    (b, L, G, N); D (Dc,) and h0 (b, Dc, N) float32 or None.  ``frontend`` turns the raw delta into
+    the step (per-channel bias, softplus, clamp) and its ``zoh`` flag selects the zero-order-hold
+    input; without it the input is delta * B.  ``chunk`` is the segment length (0: the library's
+    choice).  Returns (y, final_state)."""
+    lib = load()
+    if x.dim() != 3 or B.dim() != 4:
+        raise ValueError("x must be (b, L, Dc) and B, C (b, L, G, N)")
+    b, L, Dc = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = _io_code(x)
+    _dev(x, "x")
+    _dev(delta, "delta", x.dtype, (b, L, Dc))
+    _dev(A, "A", torch.float32, (Dc, N))
+    _dev(B, "B", x.dtype, (b, L, G, N))
+    _dev(C, "C", x.dtype, (b, L, G, N))
+    _dev(D, "D", torch.float32, (Dc,))
+    _dev(h0, "h0", torch.float32, (b, Dc, N))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, (b, L, Dc))
+    if final_state is None:
+        final_state = torch.empty((b, Dc, N), dtype=torch.float32, device=x.device)
+    _dev(final_state, "final_state", torch.float32, (b, Dc, N))
+    d = _dims(b, L, Dc, 1, N, G, chunk, io)
+    nbytes = int(lib.ssd_selective_scan_workspace_bytes(ctypes.byref(d)))
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", torch.uint8)
+    st = lib.ssd_selective_scan(ctypes.byref(d), _fe(frontend, Dc), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(final_state), _ptr(workspace),
+                                0 if workspace is None else workspace.numel(), _stream(x))
+    _check(st, "ssd_selective_scan")
+    return y, final_state
 
 
 def chunk_cumsum(dt, A, chunk: int, *, frontend: Optional[Frontend] = None):

@@ -27,6 +27,7 @@ SOURCES = [
     "step.hip",
     "fused.hip",
     "wide.hip",
+    "selective.hip",
 ]
 
 

@@ -458,4 +458,88 @@ ssd_status ssd_step_multi(const ssd_dims* dims, float* state, const void* x, con
     return ssd_step_multi_ex(dims, nullptr, state, x, dt, A, B, C, D, y, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Mamba-1 selective scan
+// ---------------------------------------------------------------------------
+static ssd_status check_selective(const ssd_dims* d, ssd::SelectiveLayout* lay) {
+    if (!d) return fail(SSD_ERR_NULL, "dims is NULL");
+    if (d->io != SSD_F32 && d->io != SSD_BF16) return fail(SSD_ERR_DTYPE, "io dtype %d is not SSD_F32/SSD_BF16", d->io);
+    if (d->reserved != 0) return fail(SSD_ERR_SHAPE, "dims.reserved must be 0");
+    if (d->batch < 0 || d->seqlen < 0) return fail(SSD_ERR_SHAPE, "batch and seqlen must be >= 0");
+    if (d->nheads <= 0 || d->dstate <= 0 || d->ngroups <= 0)
+        return fail(SSD_ERR_SHAPE, "nheads (channels), dstate and ngroups must be > 0");
+    if (d->headdim != 1) return fail(SSD_ERR_SHAPE, "the selective scan needs headdim == 1 (got %lld)",
+                                     (long long)d->headdim);
+    if (d->nheads % d->ngroups != 0)
+        return fail(SSD_ERR_SHAPE, "channels (%lld) is not a multiple of ngroups (%lld)", (long long)d->nheads,
+                    (long long)d->ngroups);
+    if (d->chunk < 0) return fail(SSD_ERR_SHAPE, "chunk must be >= 0");
+    if (d->chunk % 64) return fail(SSD_ERR_UNSUPPORTED, "segment length %lld: need 0 or a multiple of 64",
+                                   (long long)d->chunk);
+    if (!ssd::selective_supported(d->nheads, d->dstate, d->ngroups))
+        return fail(SSD_ERR_UNSUPPORTED, "dstate %lld, channels per group %lld: need dstate in {16, 32, 48, 64} and "
+                    "a multiple of 16 channels per group", (long long)d->dstate,
+                    (long long)(d->nheads / d->ngroups));
+    if (d->batch > 65535 || d->batch * (d->nheads / 16) * ((d->seqlen + 63) / 64 + 1) > kMaxGrid)
+        return fail(SSD_ERR_UNSUPPORTED, "problem too large for one launch grid");
+    *lay = ssd::selective_layout(d->batch, d->seqlen, d->nheads, d->dstate, d->chunk);
+    return SSD_OK;
+}
+
+size_t ssd_selective_scan_workspace_bytes(const ssd_dims* dims) {
+    try {
+        ssd::SelectiveLayout f;
+        if (check_selective(dims, &f) != SSD_OK) return 0;
+        return f.total;
+    } catch (...) {
+        return 0;
+    }
+}
+
+ssd_status ssd_selective_scan(const ssd_dims* dims, const ssd_dt_frontend* fe, const void* x, const void* delta,
+                              const float* A, const void* B, const void* C, const float* D, const float* h0,
+                              void* y, float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        ssd::SelectiveLayout f;
+        SSD_TRY(check_selective(dims, &f));
+        const int64_t b = dims->batch, L = dims->seqlen, Dc = dims->nheads, N = dims->dstate, G = dims->ngroups;
+        ssd::DtFront dfe;
+        Span sbias;
+        SSD_TRY(front_end(fe, Dc, &dfe, &sbias));
+        const size_t e = dims->io == SSD_BF16 ? 2 : 4;
+        Span sx{x, (size_t)(b * L * Dc) * e, "x"}, sdl{delta, (size_t)(b * L * Dc) * e, "delta"},
+            sA{A, (size_t)(Dc * N) * 4, "A"}, sB{B, (size_t)(b * L * G * N) * e, "B"},
+            sC{C, (size_t)(b * L * G * N) * e, "C"}, sD{D, D ? (size_t)Dc * 4 : 0, "D"},
+            sh0{h0, h0 ? (size_t)(b * Dc * N) * 4 : 0, "h0"}, sy{y, (size_t)(b * L * Dc) * e, "y"},
+            sfin{final_state, (size_t)(b * Dc * N) * 4, "final_state"}, sws{workspace, f.total, "workspace"};
+        for (const Span& p : {sx, sdl, sA, sB, sC, sy, sfin}) SSD_TRY(need_ptr(p));
+        if (b > 0 && L > 0 && f.total > 0) {
+            if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", f.total);
+            if (workspace_bytes < f.total)
+                return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, f.total);
+            if (reinterpret_cast<uintptr_t>(workspace) % 256)
+                return fail(SSD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        }
+        Span ins[] = {sx, sdl, sA, sB, sC, sD, sh0, sbias};
+        SSD_TRY(no_alias(sy, ins, 8));
+        SSD_TRY(no_alias(sfin, ins, 8));
+        Span o1[] = {sy};
+        SSD_TRY(no_alias(sfin, o1, 1));
+        if (b > 0 && L > 0 && f.total > 0) {
+            Span all[] = {sx, sdl, sA, sB, sC, sD, sh0, sy, sfin, sbias};
+            SSD_TRY(no_alias(sws, all, 10));
+        }
+        for (const Span& p : {sx, sdl, sB, sC, sy})
+            if (reinterpret_cast<uintptr_t>(p.p) % 16)
+                return fail(SSD_ERR_UNSUPPORTED, "%s must be 16-byte aligned", p.name);
+        hipError_t he = ssd::launch_selective_scan(b, L, Dc, N, G, dims->io == SSD_BF16 ? 1 : 0, dfe, x, delta, A,
+                                                   B, C, D, h0, y, final_state, dims->chunk, workspace,
+                                                   (hipStream_t)stream);
+        if (he != hipSuccess) return hip_fail(he, "ssd_selective_scan");
+        return ok();
+    } catch (...) {
+        return fail(SSD_ERR_HIP, "internal error");
+    }
+}
+
 }  // extern "C"

@@ -61,6 +61,23 @@ hipError_t launch_forward_fast(const Shape& s, const DtFront& fe, const void* x,
                                const void* C, const float* D, const float* h0, void* y, float* final_state,
                                void* workspace, hipStream_t st);
 
+// Mamba-1 selective scan (selective.hip): x, delta, y (b, L, Dc); A (Dc, N); B, C
+// (b, L, G, N); D (Dc); h0, final (b, Dc, N).  Supported: N in {16, 32, 48, 64}
+// and Dc / G a multiple of 16.  The sequence runs in nseg segments of seg_len
+// tokens (a multiple of 64); with more than one segment the workspace holds the
+// segment states (b, nseg - 1, Dc, N) and step sums (b, nseg - 1, Dc), fp32.
+struct SelectiveLayout {
+    int64_t seg_len;
+    int nseg;
+    size_t states, sums, total;
+};
+bool selective_supported(int64_t Dc, int64_t N, int64_t G);
+SelectiveLayout selective_layout(int64_t b, int64_t L, int64_t Dc, int64_t N, int64_t seg_len);
+hipError_t launch_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, int64_t G, int io, const DtFront& fe,
+                                 const void* x, const void* delta, const float* A, const void* B, const void* C,
+                                 const float* D, const float* h0, void* y, float* final_state, int64_t seg_len,
+                                 void* workspace, hipStream_t st);
+
 // LDS bytes the generic chunk kernels need; used by validation.
 size_t chunk_state_lds_bytes(const Shape& s);
 size_t chunk_scan_lds_bytes(const Shape& s);

@@ -27,7 +27,7 @@ def _declared():
 def test_header_symbols_exported():
     lib = ssd.load()
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
 
@@ -195,3 +195,57 @@ def test_product_never_imports_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "ssd_oracle" not in text, f
+
+
+def _sel(d, fe=None, ws=None, ws_bytes=0, **over):
+    lib = ssd.load()
+    p = dict(x=_p(0), delta=_p(1 << 30), A=_p(2 << 30), B=_p(3 << 30), C=_p(4 << 30), D=None, h0=None,
+             y=_p(6 << 30), fin=_p(7 << 30))
+    p.update(over)
+    return lib.ssd_selective_scan(ctypes.byref(d) if d is not None else None, fe, p["x"], p["delta"], p["A"],
+                                  p["B"], p["C"], p["D"], p["h0"], p["y"], p["fin"], ws, ws_bytes, None)
+
+
+def _sd(b=1, L=4096, Dc=64, N=16, G=1, chunk=0, io=1, P=1):
+    return Dims(b, L, Dc, P, N, G, chunk, io, 0)
+
+
+@pytest.mark.parametrize("dims,code", [
+    (None, NULL),
+    (_sd(io=5), DTYPE),
+    (_sd(P=2), SHAPE),
+    (_sd(Dc=0), SHAPE),
+    (_sd(Dc=48, G=5), SHAPE),
+    (_sd(N=8), UNSUP),
+    (_sd(N=128), UNSUP),
+    (_sd(Dc=40), UNSUP),
+    (_sd(Dc=64, G=8), UNSUP),
+    (_sd(chunk=100), UNSUP),
+    (_sd(chunk=-64), SHAPE),
+])
+def test_selective_rejects_bad_dims(dims, code):
+    assert _sel(dims) == code
+
+
+def test_selective_validates_pointers_and_workspace():
+    lib = ssd.load()
+    d = _sd(L=4096, chunk=1024)
+    need = lib.ssd_selective_scan_workspace_bytes(ctypes.byref(d))
+    assert need > 0  # four segments: three carried states
+    assert lib.ssd_selective_scan_workspace_bytes(ctypes.byref(_sd(L=4096, chunk=4096))) == 0
+    assert _sel(d) == WS  # NULL workspace
+    ws = _p(8 << 30)
+    assert _sel(d, ws=ws, ws_bytes=need - 1) == WS
+    assert _sel(d, ws=_p((8 << 30) + 16), ws_bytes=need) == WS  # not 256-byte aligned
+    assert _sel(d, ws=ws, ws_bytes=need, delta=None) == NULL
+    assert _sel(d, ws=ws, ws_bytes=need, y=_p(64)) == ALIAS  # y over x
+    assert _sel(d, ws=ws, ws_bytes=need, fin=_p((6 << 30) + 64)) == ALIAS  # final state over y
+    assert _sel(d, ws=_p(0), ws_bytes=need) == ALIAS  # workspace over x
+    assert _sel(d, ws=ws, ws_bytes=need, B=_p((3 << 30) + 8)) == UNSUP  # B not 16-byte aligned
+    from mamba_ssd_chunked_05_amd import DtFrontend
+    bad = DtFrontend(None, 1, 1, 1, 0, 0.2, 0.1)
+    assert _sel(d, fe=ctypes.byref(bad), ws=ws, ws_bytes=need) == SHAPE
+    over = DtFrontend(FAKE + (6 << 30), 1, 1, 0, 0, 0.0, 0.0)  # bias over y
+    assert _sel(d, fe=ctypes.byref(over), ws=ws, ws_bytes=need) == ALIAS
+    # empty batch: a no-op
+    assert _sel(_sd(b=0)) == OK
