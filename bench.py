@@ -12,7 +12,10 @@ The printed JSON line also carries
                     stream it runs on, against the MI355X peak;
   * cpu_baseline -- the fp64 oracle timed on this host on a bounded sample;
   * decode       -- 64 back-to-back ssd_step calls on the 2.7B decode shape, the same 64 steps
-                    replayed as one graph, and as one ssd_step_multi call (state kept on chip).
+                    replayed as one graph, and as one ssd_step_multi call (state kept on chip);
+  * selective_scan -- the Mamba-1 selective scan (ssd_selective_scan) on the same width
+                    (5120 channels, N = 16, 64K tokens, zero-order hold), with its own ALU
+                    roofline and oracle baseline.
 """
 
 from __future__ import annotations
@@ -31,6 +34,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
+# fp32 VALU issue rate without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, in G lane-ops/s
+PEAK_VALU_GOPS = 256 * 4 * 16 * 2.4
+# lane operations of one selective-scan element update (token, channel, state entry) in its
+# cheapest form: delta*A, exp2, B*x, add, fma (state), C/A scale, fma (output)
+SEL_OPS_PER_ELEMENT = 7
 METRIC = "SSD fwd tokens/s + % MFMA/HBM roofline (2.7B heads, L 1K–256K, N 64–512)"
 
 
@@ -42,6 +50,7 @@ def parse():
     ap.add_argument("--workload", default="cfg2_64k", help="a forward workload name from synth.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-selective", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle's timed sample (0 = all)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this many MiB (hardware-counter calibration)")
@@ -318,6 +327,63 @@ def main():
         }
         log(f"decode: {step_ms * 1e3:.1f} us/step, {gbs:.0f} GB/s algorithmic; graph {graph_ms * 1e3:.1f} us/step; "
             f"multi-step {multi_ms * 1e3 / nst:.2f} us/step ({multi_gbs:.0f} GB/s algorithmic)")
+
+    # ---- Mamba-1 selective scan on the same width ------------------------------------------------
+    if not args.no_selective:
+        from synth import SELECTIVE_CONFIGS, make_selective_config_inputs
+
+        sname = "mamba1_5120ch_64k"
+        sc = SELECTIVE_CONFIGS[sname]
+        t0 = time.time()
+        si = make_selective_config_inputs(sname)
+        sdt_ = torch.bfloat16 if sc["dtype"] == "bf16" else torch.float32
+        ux, ud, uB, uC = t(si.x, sdt_), t(si.delta, sdt_), t(si.B, sdt_), t(si.C, sdt_)
+        uA, uD = t(si.A, torch.float32), t(si.D, torch.float32)
+        log(f"selective workload resident ({time.time() - t0:.1f}s)")
+        sb, sL, sDc = ux.shape
+        sN = uB.shape[-1]
+        fe = ssd.Frontend(zoh=True)
+        uy = torch.empty_like(ux)
+        ufin = torch.empty((sb, sDc, sN), dtype=torch.float32, device=dev)
+        uws_n = ssd.selective_scan_workspace_bytes(sb, sL, sDc, sN, uB.shape[2], dtype=sdt_)
+        uws = torch.empty(max(uws_n, 1), dtype=torch.uint8, device=dev)
+
+        def sel():
+            ssd.selective_scan(ux, ud, uA, uB, uC, uD, None, y=uy, final_state=ufin, workspace=uws, frontend=fe)
+
+        sel_ms = timed(sel, args.steps)
+        elems = sb * sL * sDc * sN
+        gops = elems * SEL_OPS_PER_ELEMENT / (sel_ms / 1e3) / 1e9
+        sel_bytes = sb * sL * sDc * 3 * (2 if sc["dtype"] == "bf16" else 4) + 2 * sb * sL * uB.shape[2] * sN * 2
+        result["selective_scan"] = {
+            "workload": f"{sname}: Mamba-1 selective scan b={sb} L={sL} channels={sDc} N={sN} G={uB.shape[2]} "
+                        f"{sc['dtype']} io, fp32 state, zero-order hold",
+            "ms_per_call": sel_ms,
+            "tokens_per_s": sb * sL / (sel_ms / 1e3),
+            "element_updates_per_s": elems / (sel_ms / 1e3),
+            "hbm_gbs_min_bytes": sel_bytes / (sel_ms / 1e3) / 1e9,
+            "roofline": {"kernel": "ssd_selective_scan (whole call: first pass, carry, output pass)",
+                         "bound": "alu", "achieved": gops, "peak": PEAK_VALU_GOPS, "unit": "Gop/s",
+                         "frac": gops / PEAK_VALU_GOPS, "ops_per_element": SEL_OPS_PER_ELEMENT,
+                         "traffic": None},
+        }
+        log(f"selective scan: {sel_ms:.3f} ms/call, {elems / (sel_ms / 1e3) / 1e12:.2f} T element updates/s, "
+            f"{gops / PEAK_VALU_GOPS:.2f} of the VALU issue rate")
+        if not args.no_cpu_baseline:
+            import oracle
+
+            ch = list(range(0, sDc, max(1, sDc // 256)))[:256]
+            t1 = time.perf_counter()
+            oracle.selective_scan(si.x[:, :, ch], si.delta[:, :, ch], si.A[ch], si.B, si.C, si.D[ch], None, zoh=True)
+            cpu_s = time.perf_counter() - t1
+            result["selective_scan"]["cpu_baseline"] = {
+                "value": sb * sL * len(ch) / sDc / cpu_s, "unit": "tokens/s", "cores": oracle.max_threads(),
+                "kind": "oracle",
+                "sample": f"{len(ch)} of {sDc} channels over all {sL} tokens; tokens/s scaled to all channels "
+                          f"({cpu_s:.1f} s, fp64 recurrence, OpenMP over (b, channel))",
+            }
+        del si, ux, ud, uB, uC, uy, uws
+        torch.cuda.empty_cache()
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload ----------------
     if not args.no_cpu_baseline:

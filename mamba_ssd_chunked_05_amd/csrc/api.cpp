@@ -482,7 +482,7 @@ static ssd_status check_selective(const ssd_dims* d, ssd::SelectiveLayout* lay) 
                     (long long)(d->nheads / d->ngroups));
     if (d->batch > 65535 || d->batch * (d->nheads / 16) * ((d->seqlen + 63) / 64 + 1) > kMaxGrid)
         return fail(SSD_ERR_UNSUPPORTED, "problem too large for one launch grid");
-    *lay = ssd::selective_layout(d->batch, d->seqlen, d->nheads, d->dstate, d->chunk);
+    *lay = ssd::selective_layout(d->batch, d->seqlen, d->nheads, d->dstate, d->ngroups, d->chunk);
     return SSD_OK;
 }
 

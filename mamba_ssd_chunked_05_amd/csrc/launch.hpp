@@ -72,7 +72,7 @@ struct SelectiveLayout {
     size_t states, sums, total;
 };
 bool selective_supported(int64_t Dc, int64_t N, int64_t G);
-SelectiveLayout selective_layout(int64_t b, int64_t L, int64_t Dc, int64_t N, int64_t seg_len);
+SelectiveLayout selective_layout(int64_t b, int64_t L, int64_t Dc, int64_t N, int64_t G, int64_t seg_len);
 hipError_t launch_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, int64_t G, int io, const DtFront& fe,
                                  const void* x, const void* delta, const float* A, const void* B, const void* C,
                                  const float* D, const float* h0, void* y, float* final_state, int64_t seg_len,

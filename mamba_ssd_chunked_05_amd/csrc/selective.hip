@@ -358,6 +358,254 @@ __global__ void __launch_bounds__(256) selective_carry_kernel(const float* A, co
     if (final_state) final_state[i] = hv;
 }
 
+// ---------------------------------------------------------------------------
+// dstate 16: one lane per channel, the whole state of the channel in its
+// registers, so the sum over n stays in the lane.  One wavefront per
+// workgroup (64 channels of one group); per tile the wavefront stages x and
+// the step transposed to [channel][token] and the B, C rows to [token][n] in
+// LDS (fp32), and every lane reads B and C rows as broadcasts.
+//
+// With the zero-order hold and no zero entry in A, the lane keeps g = A h:
+//   g <- e g + (e - 1) B x = e (g + B x) - B x,   y = sum_n (C / A) g,
+// three operations per entry and token for the update.  A wavefront whose
+// channels have a zero entry of A keeps h and the (e - 1) / A factor with its
+// limit delta.
+// ---------------------------------------------------------------------------
+constexpr int LN = 16;   // dstate of the lane kernel
+constexpr int LCW = 64;  // channels per workgroup (one wavefront)
+
+template <class T>
+struct LaneCfg {
+    static constexpr int TT = 16;                         // tokens per tile
+    static constexpr int XS = TT + 4;                     // [channel][token] stride (conflict-free 16-byte reads)
+    static constexpr int E = Io<T>::per16;
+    static constexpr int KX = TT * LCW / E / 64;  // x (and step) pieces per lane
+    static constexpr int NB = TT * LN / E;        // B (and C) pieces per tile
+    static constexpr int KB = (NB + 63) / 64;
+    static_assert(KX >= 1 && TT * LCW % (E * 64) == 0, "lane kernel tile split");
+};
+
+template <class T>
+struct LaneLds {
+    float xs[LCW * LaneCfg<T>::XS];
+    float ds[LCW * LaneCfg<T>::XS];
+    float bs[LaneCfg<T>::TT * LN];
+    float cs[LaneCfg<T>::TT * LN];
+};
+
+template <class T>
+struct LaneStage {
+    uint4 x[LaneCfg<T>::KX], d[LaneCfg<T>::KX];
+    uint4 b[LaneCfg<T>::KB], c[LaneCfg<T>::KB];
+};
+
+template <class T, bool OUT>
+__device__ __forceinline__ void lane_load(LaneStage<T>& st, const Args& a, int64_t b, int64_t t0, int last, int c0,
+                                          int g, int lane) {
+    using CF = LaneCfg<T>;
+    constexpr int PR = LCW / CF::E;  // pieces per x row
+    const T* xg = static_cast<const T*>(a.x);
+    const T* dg = static_cast<const T*>(a.delta);
+#pragma unroll
+    for (int k = 0; k < CF::KX; ++k) {
+        const int i = lane + 64 * k, r = i / PR, col = (i % PR) * CF::E;
+        const int64_t o = (b * a.L + t0 + (r <= last ? r : last)) * a.Dc + c0 + col;
+        st.x[k] = *reinterpret_cast<const uint4*>(xg + o);
+        st.d[k] = *reinterpret_cast<const uint4*>(dg + o);
+    }
+    constexpr int PB = LN / CF::E;
+#pragma unroll
+    for (int k = 0; k < CF::KB; ++k) {
+        const int i = lane + 64 * k;
+        if (i < CF::NB) {
+            const int r = i / PB, col = (i % PB) * CF::E;
+            const int64_t o = ((b * a.L + t0 + (r <= last ? r : last)) * a.G + g) * LN + col;
+            st.b[k] = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.B) + o);
+            if (OUT) st.c[k] = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.C) + o);
+        }
+    }
+}
+
+template <class T, bool OUT>
+__device__ __forceinline__ void lane_store(LaneLds<T>& sm, const LaneStage<T>& st, const Args& a, int last, int c0,
+                                           int lane) {
+    using CF = LaneCfg<T>;
+    constexpr int PR = LCW / CF::E;
+#pragma unroll
+    for (int k = 0; k < CF::KX; ++k) {
+        const int i = lane + 64 * k, r = i / PR, col = (i % PR) * CF::E;
+        const bool ok = r <= last;
+        float v[CF::E], w[CF::E];
+        Io<T>::unpack(st.x[k], v);
+        Io<T>::unpack(st.d[k], w);
+#pragma unroll
+        for (int e = 0; e < CF::E; ++e) {
+            float dec, inp;
+            dt_front(a.fe, c0 + col + e, 0.0f, w[e], dec, inp);
+            sm.xs[(col + e) * CF::XS + r] = ok ? v[e] : 0.0f;
+            sm.ds[(col + e) * CF::XS + r] = ok ? dec : 0.0f;  // padding tokens: zero step
+        }
+    }
+    constexpr int PB = LN / CF::E;
+#pragma unroll
+    for (int k = 0; k < CF::KB; ++k) {
+        const int i = lane + 64 * k;
+        if (i < CF::NB) {
+            const int r = i / PB, col = (i % PB) * CF::E;
+            const bool ok = r <= last;
+            float v[CF::E];
+            Io<T>::unpack(st.b[k], v);
+#pragma unroll
+            for (int e = 0; e < CF::E; ++e) sm.bs[r * LN + col + e] = ok ? v[e] : 0.0f;
+            if (OUT) {
+                Io<T>::unpack(st.c[k], v);
+#pragma unroll
+                for (int e = 0; e < CF::E; ++e) sm.cs[r * LN + col + e] = ok ? v[e] : 0.0f;
+            }
+        }
+    }
+}
+
+// the token walk of one segment; GF: the state is kept as g = A h (zero-order hold, A has no zero)
+template <class T, bool ZOH, bool OUT, bool GF>
+__device__ __forceinline__ void lane_walk(LaneLds<T>& sm, const Args& a, float (&h)[LN], const float (&a2)[LN],
+                                          const float (&ia)[LN], float& dsum, int64_t b,
+                                          int64_t s0, int64_t s1, int c0, int g, int lane, float Dd) {
+    using CF = LaneCfg<T>;
+    constexpr int TT = CF::TT;
+    const int c = c0 + lane;
+    T* yg = static_cast<T*>(a.y);
+    LaneStage<T> st;
+    int last = (int)(s1 - s0 - 1 < TT - 1 ? s1 - s0 - 1 : TT - 1);
+    lane_load<T, OUT>(st, a, b, s0, last, c0, g, lane);
+    for (int64_t t0 = s0; t0 < s1; t0 += TT) {
+        last = (int)(s1 - t0 - 1 < TT - 1 ? s1 - t0 - 1 : TT - 1);
+        __syncthreads();
+        lane_store<T, OUT>(sm, st, a, last, c0, lane);
+        __syncthreads();
+        if (t0 + TT < s1) {
+            const int nl = (int)(s1 - t0 - TT - 1 < TT - 1 ? s1 - t0 - TT - 1 : TT - 1);
+            lane_load<T, OUT>(st, a, b, t0 + TT, nl, c0, g, lane);
+        }
+#pragma unroll 1
+        for (int t4 = 0; t4 < TT; t4 += 4) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.ds[lane * CF::XS + t4]);
+            const f32x4 x4 = *reinterpret_cast<const f32x4*>(&sm.xs[lane * CF::XS + t4]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = t4 + r;
+                const float dl = d4[r], xv = x4[r];
+                if (!OUT) dsum += dl;
+                float bv[LN], cv[LN];
+#pragma unroll
+                for (int q = 0; q < LN / 4; ++q) {
+                    const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.bs[t * LN + 4 * q]);
+                    bv[4 * q] = bq[0], bv[4 * q + 1] = bq[1], bv[4 * q + 2] = bq[2], bv[4 * q + 3] = bq[3];
+                    if (OUT) {
+                        const f32x4 cq = *reinterpret_cast<const f32x4*>(&sm.cs[t * LN + 4 * q]);
+                        cv[4 * q] = cq[0], cv[4 * q + 1] = cq[1], cv[4 * q + 2] = cq[2], cv[4 * q + 3] = cq[3];
+                    }
+                }
+                const float dx = dl * xv;
+                float acc = 0.0f;
+#pragma unroll
+                for (int n = 0; n < LN; ++n) {
+                    const float e = fast_exp2(dl * a2[n]);
+                    if (GF) {
+                        const float bx = bv[n] * xv;
+                        h[n] = fmaf(e, h[n] + bx, -bx);
+                        if (OUT) acc = fmaf(cv[n] * ia[n], h[n], acc);
+                    } else {
+                        float u;
+                        if (ZOH) {
+                            const float f = ia[n] != 0.0f ? fmaf(e, ia[n], -ia[n]) : dl;  // limit delta at A = 0
+                            u = f * (bv[n] * xv);
+                        } else {
+                            u = dx * bv[n];
+                        }
+                        h[n] = fmaf(e, h[n], u);
+                        if (OUT) acc = fmaf(cv[n], h[n], acc);
+                    }
+                }
+                if (OUT && t <= last) yg[(b * a.L + t0 + t) * a.Dc + c] = from_f32<T>(fmaf(Dd, xv, acc));
+            }
+        }
+    }
+}
+
+template <class T, bool ZOH, bool OUT>
+__global__ void __launch_bounds__(64) selective_lane_kernel(Args a, uint32_t nitems) {
+    __shared__ __align__(16) LaneLds<T> sm;
+    const int nblk = a.Dc / LCW;
+    const int nsegk = OUT ? a.nseg : a.nseg - 1;
+    const uint32_t item = xcd_remap(blockIdx.x, nitems);
+    const int cblk = (int)(item % (uint32_t)nblk);
+    const int seg = (int)((item / (uint32_t)nblk) % (uint32_t)nsegk);
+    const int64_t b = item / ((uint32_t)nblk * (uint32_t)nsegk);
+    const int lane = threadIdx.x;
+    const int c0 = cblk * LCW, c = c0 + lane;
+    const int g = c0 / (a.Dc / a.G);
+    const int64_t s0 = (int64_t)seg * a.Lseg;
+    const int64_t s1 = s0 + a.Lseg < a.L ? s0 + a.Lseg : a.L;
+
+    float a2[LN], ia[LN], h[LN];
+    bool zero = false;
+#pragma unroll
+    for (int n = 0; n < LN; ++n) {
+        const float Av = a.A[(int64_t)c * LN + n];
+        a2[n] = Av * kLog2e;
+        ia[n] = Av != 0.0f ? 1.0f / Av : 0.0f;
+        zero |= Av == 0.0f;
+    }
+    const int64_t sidx = ((b * (a.nseg - 1) + seg) * a.Dc + c) * (int64_t)LN;
+#pragma unroll
+    for (int n = 0; n < LN; ++n) {
+        float v = 0.0f;
+        if (OUT) {
+            if (seg == 0)
+                v = a.h0 ? a.h0[(b * a.Dc + c) * (int64_t)LN + n] : 0.0f;
+            else
+                v = a.seg_states[sidx - (int64_t)a.Dc * LN + n];
+        }
+        h[n] = v;
+    }
+    const float Dd = (OUT && a.D) ? a.D[c] : 0.0f;
+    float dsum = 0.0f;
+    const bool gf = ZOH && !__any(zero);  // wavefront-uniform
+    if (gf) {
+#pragma unroll
+        for (int n = 0; n < LN; ++n) h[n] *= a.A[(int64_t)c * LN + n];
+        lane_walk<T, ZOH, OUT, ZOH>(sm, a, h, a2, ia, dsum, b, s0, s1, c0, g, lane, Dd);
+#pragma unroll
+        for (int n = 0; n < LN; ++n) h[n] *= ia[n];
+    } else {
+        lane_walk<T, ZOH, OUT, false>(sm, a, h, a2, ia, dsum, b, s0, s1, c0, g, lane, Dd);
+    }
+    if (OUT) {
+        if (seg == a.nseg - 1) {
+#pragma unroll
+            for (int q = 0; q < LN / 4; ++q)
+                *reinterpret_cast<f32x4*>(&a.final_state[(b * a.Dc + c) * (int64_t)LN + 4 * q]) =
+                    f32x4{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < LN / 4; ++q)
+            *reinterpret_cast<f32x4*>(&a.seg_states[sidx + 4 * q]) =
+                f32x4{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
+        a.seg_sums[(b * (a.nseg - 1) + seg) * a.Dc + c] = dsum;
+    }
+}
+
+template <class T, bool ZOH, bool OUT>
+hipError_t launch_lane_pass(const Args& a, int64_t b, hipStream_t st) {
+    const int nsegk = OUT ? a.nseg : a.nseg - 1;
+    const uint32_t nitems = (uint32_t)(b * (a.Dc / LCW) * nsegk);
+    if (nitems == 0) return hipSuccess;
+    hipLaunchKernelGGL((selective_lane_kernel<T, ZOH, OUT>), dim3(nitems), dim3(64), 0, st, a, nitems);
+    return hipGetLastError();
+}
+
 template <class T, int N, bool ZOH, bool OUT>
 hipError_t launch_pass(const Args& a, int64_t b, hipStream_t st) {
     const int nsegk = OUT ? a.nseg : a.nseg - 1;
@@ -369,9 +617,9 @@ hipError_t launch_pass(const Args& a, int64_t b, hipStream_t st) {
 }
 
 template <class T, int N, bool ZOH>
-hipError_t run(const Args& a, int64_t b, hipStream_t st) {
+hipError_t run(const Args& a, int64_t b, bool lane, hipStream_t st) {
     if (a.nseg > 1) {
-        hipError_t e = launch_pass<T, N, ZOH, false>(a, b, st);
+        hipError_t e = lane ? launch_lane_pass<T, ZOH, false>(a, b, st) : launch_pass<T, N, ZOH, false>(a, b, st);
         if (e != hipSuccess) return e;
         const int64_t n = b * a.Dc * (int64_t)N;
         hipLaunchKernelGGL(selective_carry_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, a.A, a.h0,
@@ -379,16 +627,16 @@ hipError_t run(const Args& a, int64_t b, hipStream_t st) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    return launch_pass<T, N, ZOH, true>(a, b, st);
+    return lane ? launch_lane_pass<T, ZOH, true>(a, b, st) : launch_pass<T, N, ZOH, true>(a, b, st);
 }
 
 template <class T, bool ZOH>
-hipError_t by_n(const Args& a, int64_t b, int N, hipStream_t st) {
+hipError_t by_n(const Args& a, int64_t b, int N, bool lane, hipStream_t st) {
     switch (N) {
-        case 16: return run<T, 16, ZOH>(a, b, st);
-        case 32: return run<T, 32, ZOH>(a, b, st);
-        case 48: return run<T, 48, ZOH>(a, b, st);
-        case 64: return run<T, 64, ZOH>(a, b, st);
+        case 16: return run<T, 16, ZOH>(a, b, lane, st);
+        case 32: return run<T, 32, ZOH>(a, b, false, st);
+        case 48: return run<T, 48, ZOH>(a, b, false, st);
+        case 64: return run<T, 64, ZOH>(a, b, false, st);
     }
     return hipErrorInvalidValue;
 }
@@ -399,16 +647,22 @@ bool selective_supported(int64_t Dc, int64_t N, int64_t G) {
     return (N == 16 || N == 32 || N == 48 || N == 64) && G > 0 && Dc % G == 0 && (Dc / G) % sel::CB == 0;
 }
 
-SelectiveLayout selective_layout(int64_t b, int64_t L, int64_t Dc, int64_t N, int64_t seg_len) {
+// dstate 16 with 64 channels per group runs one lane per channel
+static bool lane_kernel(int64_t Dc, int64_t N, int64_t G) { return N == sel::LN && (Dc / G) % sel::LCW == 0; }
+
+SelectiveLayout selective_layout(int64_t b, int64_t L, int64_t Dc, int64_t N, int64_t G, int64_t seg_len) {
     SelectiveLayout f{};
     int64_t Lseg;
     if (seg_len > 0) {
         Lseg = seg_len;
     } else {
-        // enough segments for about four wavefronts per SIMD (1024 SIMDs), none shorter than 512 tokens
-        const int64_t waves = b * (Dc / sel::CB) * 4;
+        // segments enough for about eight wavefronts per SIMD (1024 SIMDs), none shorter than 256
+        // tokens (one-lane-per-channel kernel) or 512 tokens (sixteen lanes per channel)
+        const bool ln = lane_kernel(Dc, N, G);
+        const int64_t waves = ln ? b * (Dc / sel::LCW) : b * (Dc / sel::CB) * 4;
+        const int64_t target = ln ? 8192 : 4096, shortest = ln ? 256 : 512;
         int64_t nseg = 1;
-        while (waves * nseg < 4096 && L / (2 * nseg) >= 512) nseg *= 2;
+        while (waves * nseg < target && L / (2 * nseg) >= shortest) nseg *= 2;
         Lseg = (L + nseg - 1) / nseg;
         Lseg = (Lseg + sel::TT - 1) / sel::TT * sel::TT;
     }
@@ -427,7 +681,7 @@ hipError_t launch_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, in
                                  const void* x, const void* delta, const float* A, const void* B, const void* C,
                                  const float* D, const float* h0, void* y, float* final_state, int64_t seg_len,
                                  void* workspace, hipStream_t st) {
-    const SelectiveLayout f = selective_layout(b, L, Dc, N, seg_len);
+    const SelectiveLayout f = selective_layout(b, L, Dc, N, G, seg_len);
     if (b == 0) return hipSuccess;
     if (L == 0) {  // the final state is the start state
         const int64_t n = b * Dc * N;
@@ -440,9 +694,10 @@ hipError_t launch_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, in
                 f.nseg > 1 ? reinterpret_cast<float*>(ws + f.states) : nullptr,
                 f.nseg > 1 ? reinterpret_cast<float*>(ws + f.sums) : nullptr,
                 y, final_state, fe, L, f.seg_len, (int)Dc, (int)G, f.nseg};
-    const bool zoh = fe.zoh != 0;
-    if (io == 1) return zoh ? sel::by_n<bf16, true>(a, b, (int)N, st) : sel::by_n<bf16, false>(a, b, (int)N, st);
-    return zoh ? sel::by_n<float, true>(a, b, (int)N, st) : sel::by_n<float, false>(a, b, (int)N, st);
+    const bool zoh = fe.zoh != 0, lane = lane_kernel(Dc, N, G);
+    if (io == 1)
+        return zoh ? sel::by_n<bf16, true>(a, b, (int)N, lane, st) : sel::by_n<bf16, false>(a, b, (int)N, lane, st);
+    return zoh ? sel::by_n<float, true>(a, b, (int)N, lane, st) : sel::by_n<float, false>(a, b, (int)N, lane, st);
 }
 
 }  // namespace ssd
