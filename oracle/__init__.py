@@ -61,9 +61,10 @@ def _load():
         lib.ssd_oracle_state_passing.argtypes = [_I64] * 6 + [_DP] * 5
         lib.ssd_oracle_chunk_scan.argtypes = [_I64] * 7 + [_DP] * 8 + [ctypes.c_int]
         lib.ssd_oracle_selective_scan.argtypes = [_I64] * 5 + [_DP] * 9 + [ctypes.c_int] * 2
+        lib.ssd_oracle_backward.argtypes = [_I64] * 6 + [_DP] * 16 + [ctypes.c_int]
         for f in ("ssd_oracle_forward", "ssd_oracle_step", "ssd_oracle_chunk_cumsum",
                   "ssd_oracle_state_passing", "ssd_oracle_chunk_scan", "ssd_oracle_dt_frontend",
-                  "ssd_oracle_selective_scan"):
+                  "ssd_oracle_selective_scan", "ssd_oracle_backward"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -214,3 +215,26 @@ def selective_scan(x, delta, A, B, C, D=None, h0=None, *, zoh: bool = True, thre
     rc = _load().ssd_oracle_selective_scan(b, L, Dc, N, G, *ptrs, py, pf, int(zoh), threads)
     _check(rc, "selective_scan")
     return {"y": y, "final": fin}
+
+
+def backward(x, dt, A, B, C, D, h0, dy, dfinal=None, *, threads: int = 0):
+    """Gradients of the SSD forward (plain input step dt) for output gradient dy (b,L,H,P) and final-state
+    gradient dfinal (b,H,P,N) or None.  Returns dict(dx, ddt, dA, dB, dC, dD, dh0); dD is None when D is."""
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    keep = []
+    ptrs = []
+    for a in (x, dt, A, B, C, D, h0, dy, dfinal):
+        arr, p = _in(a)
+        keep.append(arr)
+        ptrs.append(p)
+    dx, pdx = _out((b, L, H, P))
+    ddt, pddt = _out((b, L, H))
+    dA, pdA = _out((H,))
+    dB, pdB = _out((b, L, G, N))
+    dC, pdC = _out((b, L, G, N))
+    dD, pdD = _out((H,)) if D is not None else (None, None)
+    dh0, pdh0 = _out((b, H, P, N))
+    rc = _load().ssd_oracle_backward(b, L, H, P, N, G, *ptrs, pdx, pddt, pdA, pdB, pdC, pdD, pdh0, threads)
+    _check(rc, "backward")
+    return {"dx": dx, "ddt": ddt, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dh0": dh0}

@@ -348,3 +348,148 @@ int ssd_oracle_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, int64
     }
     return err ? -2 : 0;
 }
+
+/*
+ * Backward pass of the SSD recurrence (reverse-mode derivative of the token
+ * recurrence ssd_oracle_forward computes, plain input step dt, no front-end):
+ * given dy (b,L,H,P) and the gradient of the final state dfinal (b,H,P,N, may
+ * be NULL = 0), returns dx (b,L,H,P), ddt (b,L,H), dA (H), dB, dC (b,L,G,N),
+ * dD (H, may be NULL) and dh0 (b,H,P,N, may be NULL).  The training use and
+ * the recomputation of forward states instead of storing them follow
+ * "3.3 Hardware-Aware ..." section 6.
+ *
+ * With G_t the gradient with respect to the state after token t, in reverse
+ * token order (a_t = exp(dt_t A), S_{-1} = h0):
+ *   G <- dfinal (or 0)
+ *   for t = L-1 .. 0:
+ *       G      += dy_t (outer) C_t                 (y_t = C_t . S_t + D x_t)
+ *       dC_t   += S_t^T dy_t                       (summed over the heads of the group)
+ *       dx_t    = dt_t G B_t + D dy_t
+ *       dB_t   += dt_t G^T x_t                     (summed over the heads of the group)
+ *       ddt_t   = sum_{p,n} G (x_t (outer) B_t + A a_t S_{t-1})
+ *       dA     += sum_{p,n} G dt_t a_t S_{t-1}
+ *       dD     += dy_t . x_t
+ *       G      <- a_t G                            (gradient w.r.t. S_{t-1})
+ *   dh0 = G
+ * The states S_t are recomputed from checkpoints every 64 tokens.  Per-head
+ * dB, dC contributions go to a (b,L,H,N) scratch and are summed over heads.
+ */
+#define BWD_BLOCK 64
+int ssd_oracle_backward(int64_t b, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                        const double* x, const double* dt, const double* A, const double* B,
+                        const double* C, const double* D, const double* h0, const double* dy,
+                        const double* dfinal, double* dx, double* ddt, double* dA, double* dB,
+                        double* dC, double* dD, double* dh0, int nthreads) {
+    if (bad_dims(b, L, H, P, N, G)) return -1;
+    int64_t hpg = H / G, PN = P * N, nblk = (L + BWD_BLOCK - 1) / BWD_BLOCK;
+    double* dBh = (double*)calloc((size_t)(b * L * H * N) + 1, sizeof(double));
+    double* dCh = (double*)calloc((size_t)(b * L * H * N) + 1, sizeof(double));
+    double* dAbh = (double*)calloc((size_t)(b * H) + 1, sizeof(double));
+    double* dDbh = (double*)calloc((size_t)(b * H) + 1, sizeof(double));
+    if (!dBh || !dCh || !dAbh || !dDbh) { free(dBh); free(dCh); free(dAbh); free(dDbh); return -2; }
+    set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < b * H; ++bh) {
+        int64_t bb = bh / H, h = bh % H, g = h / hpg;
+        double* ck = (double*)malloc(sizeof(double) * (size_t)((nblk + 1) * PN));
+        double* blk = (double*)malloc(sizeof(double) * (size_t)((BWD_BLOCK + 1) * PN));
+        double* Gs = (double*)malloc(sizeof(double) * (size_t)PN);
+        if (!ck || !blk || !Gs) { err = 1; free(ck); free(blk); free(Gs); continue; }
+        /* forward: checkpoint the state before every block */
+        double* S = blk;
+        for (int64_t e = 0; e < PN; ++e) S[e] = h0 ? h0[bh * PN + e] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            if (t % BWD_BLOCK == 0) memcpy(ck + (t / BWD_BLOCK) * PN, S, sizeof(double) * PN);
+            int64_t bt = bb * L + t;
+            token_update(P, N, S, dt[bt * H + h], dt[bt * H + h], A[h], x + (bt * H + h) * P,
+                         B + (bt * G + g) * N, C + (bt * G + g) * N, 0.0, 0, NULL);
+        }
+        /* backward over the blocks, last first */
+        for (int64_t e = 0; e < PN; ++e) Gs[e] = dfinal ? dfinal[bh * PN + e] : 0.0;
+        double dAacc = 0.0, dDacc = 0.0;
+        for (int64_t k = nblk - 1; k >= 0; --k) {
+            int64_t t0 = k * BWD_BLOCK, t1 = (t0 + BWD_BLOCK < L) ? t0 + BWD_BLOCK : L;
+            /* blk[i] = state before token t0 + i; blk[t1 - t0] = state after the block */
+            memcpy(blk, ck + k * PN, sizeof(double) * PN);
+            for (int64_t t = t0; t < t1; ++t) {
+                int64_t bt = bb * L + t;
+                double* nxt = blk + (t - t0 + 1) * PN;
+                memcpy(nxt, blk + (t - t0) * PN, sizeof(double) * PN);
+                token_update(P, N, nxt, dt[bt * H + h], dt[bt * H + h], A[h], x + (bt * H + h) * P,
+                             B + (bt * G + g) * N, C + (bt * G + g) * N, 0.0, 0, NULL);
+            }
+            for (int64_t t = t1 - 1; t >= t0; --t) {
+                int64_t bt = bb * L + t;
+                const double* xt = x + (bt * H + h) * P;
+                const double* dyt = dy + (bt * H + h) * P;
+                const double* Bt = B + (bt * G + g) * N;
+                const double* Ct = C + (bt * G + g) * N;
+                const double* Sprev = blk + (t - t0) * PN;
+                const double* Scur = blk + (t - t0 + 1) * PN;
+                double d = dt[bt * H + h], a = exp(d * A[h]);
+                for (int64_t p = 0; p < P; ++p)
+                    for (int64_t n = 0; n < N; ++n) Gs[p * N + n] += dyt[p] * Ct[n];
+                double* dCt = dCh + (bt * H + h) * N;
+                double* dBt = dBh + (bt * H + h) * N;
+                for (int64_t n = 0; n < N; ++n) {
+                    double sc = 0.0, sb = 0.0;
+                    for (int64_t p = 0; p < P; ++p) {
+                        sc += Scur[p * N + n] * dyt[p];
+                        sb += Gs[p * N + n] * xt[p];
+                    }
+                    dCt[n] = sc;
+                    dBt[n] = d * sb;
+                }
+                double dd = 0.0, gs = 0.0;
+                for (int64_t p = 0; p < P; ++p) {
+                    double gb = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        gb += Gs[p * N + n] * Bt[n];
+                        gs += Gs[p * N + n] * Sprev[p * N + n];
+                    }
+                    dx[(bt * H + h) * P + p] = d * gb + (D ? D[h] * dyt[p] : 0.0);
+                    dd += gb * xt[p];
+                    dDacc += dyt[p] * xt[p];
+                }
+                ddt[bt * H + h] = dd + A[h] * a * gs;
+                dAacc += d * a * gs;
+                for (int64_t e = 0; e < PN; ++e) Gs[e] *= a;
+            }
+        }
+        if (dh0) memcpy(dh0 + bh * PN, Gs, sizeof(double) * PN);
+        dAbh[bh] = dAacc;
+        dDbh[bh] = dDacc;
+        free(ck);
+        free(blk);
+        free(Gs);
+    }
+    if (!err) {
+        for (int64_t h = 0; h < H; ++h) {
+            double sa = 0.0, sd = 0.0;
+            for (int64_t bb = 0; bb < b; ++bb) {
+                sa += dAbh[bb * H + h];
+                sd += dDbh[bb * H + h];
+            }
+            dA[h] = sa;
+            if (dD) dD[h] = sd;
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t bt = 0; bt < b * L; ++bt)
+            for (int64_t g = 0; g < G; ++g)
+                for (int64_t n = 0; n < N; ++n) {
+                    double sb = 0.0, sc = 0.0;
+                    for (int64_t h = g * hpg; h < (g + 1) * hpg; ++h) {
+                        sb += dBh[(bt * H + h) * N + n];
+                        sc += dCh[(bt * H + h) * N + n];
+                    }
+                    dB[(bt * G + g) * N + n] = sb;
+                    dC[(bt * G + g) * N + n] = sc;
+                }
+    }
+    free(dBh);
+    free(dCh);
+    free(dAbh);
+    free(dDbh);
+    return err ? -2 : 0;
+}
