@@ -229,6 +229,32 @@ ssd_status ssd_step_multi_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, fl
                              const void* C, const float* D, void* y, void* stream);
 
 /*
+ * Backward pass of ssd_forward (plain input step dt, no front-end): the
+ * gradients of a loss through y and the final state, for training ("3.3
+ * Hardware-Aware algorithms and GPU memory hierarchy optimisation", section 6:
+ * the forward's states are recomputed, not stored).  Given dy (the gradient
+ * of y, layout of x) and dfinal (of the final state, (b, H, P, N) fp32, or
+ * NULL for zero), it writes
+ *     dx (b, L, H, P), ddt (b, L, H), dB, dC (b, L, G, N)   in the io dtype
+ *     dA (H), dD (H), dh0 (b, H, P, N)                       float32
+ * dB and dC sum over the heads of each group; dA and dD over batch rows and
+ * tokens.  D, h0 and dfinal may be NULL (then D = 0, h0 = 0, dfinal = 0); dD
+ * and dh0 may be NULL (not written).  dims->chunk is the chunk of the
+ * internal scans: 0 for the library's choice, else a multiple of 16 up to 512
+ * whose fp32 tiles fit LDS.  Supported: dstate <= 256 besides the forward's
+ * limits (SSD_ERR_UNSUPPORTED otherwise).  workspace:
+ * ssd_backward_workspace_bytes(dims) bytes, 256-byte aligned (about
+ * 4 (5 P + 4 N) bytes per token-head); no output may overlap an input,
+ * another output or the workspace.
+ */
+size_t ssd_backward_workspace_bytes(const ssd_dims* dims);
+ssd_status ssd_backward(const ssd_dims* dims, const void* x, const void* dt, const float* A,
+                        const void* B, const void* C, const float* D, const float* h0,
+                        const void* dy, const float* dfinal, void* dx, void* ddt, float* dA,
+                        void* dB, void* dC, float* dD, float* dh0, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
  * Mamba-1 selective scan: a per-channel diagonal state with a per-entry decay
  * rate, discretised, scanned and read out through C in one fused call ("3.3
  * Hardware-Aware algorithms and GPU memory hierarchy optimisation": section

@@ -110,6 +110,7 @@ def load():
         "ssd_step_multi_ex": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_query_config": [dp] + [ctypes.POINTER(ctypes.c_int)] * 4,
         "ssd_selective_scan": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "ssd_backward": [dp] + [vp] * 17 + [ctypes.c_size_t, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -117,6 +118,8 @@ def load():
         fn.restype = ctypes.c_int
     lib.ssd_forward_workspace_bytes.argtypes = [dp]
     lib.ssd_forward_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssd_backward_workspace_bytes.argtypes = [dp]
+    lib.ssd_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.ssd_selective_scan_workspace_bytes.argtypes = [dp]
     lib.ssd_selective_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssd_status_string.argtypes = [ctypes.c_int]
@@ -294,6 +297,41 @@ def step_multi(state, x, dt, A, B, C, D=None, *, y=None, frontend: Optional[Fron
                                _ptr(B), _ptr(C), _ptr(D), _ptr(y), _stream(x))
     _check(st, "ssd_step_multi")
     return y
+
+
+def backward_workspace_bytes(x: torch.Tensor, B: torch.Tensor, chunk: int = 0) -> int:
+    d = _fwd_dims(x, B, chunk)
+    return int(load().ssd_backward_workspace_bytes(ctypes.byref(d)))
+
+
+def backward(x, dt, A, B, C, D=None, h0=None, dy=None, dfinal=None, *, chunk: int = 0, workspace=None) -> dict:
+    """Gradients of ssd_forward (plain dt) for output gradient ``dy`` (layout of x) and final-state gradient
+    ``dfinal`` (b, H, P, N) float32 or None.  Returns dict(dx, ddt, dA, dB, dC, dD, dh0): dx, ddt, dB, dC in
+    the io dtype, dA, dD, dh0 float32 (dD None when D is None)."""
+    lib = load()
+    d = _fwd_dims(x, B, chunk)
+    _check_fwd_inputs(x, dt, A, B, C, D, h0)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _dev(dy, "dy", x.dtype, x.shape)
+    _dev(dfinal, "dfinal", torch.float32, (b, H, P, N))
+    out = {
+        "dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dA": torch.empty((H,), dtype=torch.float32,
+                                                                                 device=x.device),
+        "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+        "dD": None if D is None else torch.empty((H,), dtype=torch.float32, device=x.device),
+        "dh0": torch.empty((b, H, P, N), dtype=torch.float32, device=x.device),
+    }
+    nbytes = int(lib.ssd_backward_workspace_bytes(ctypes.byref(d)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", torch.uint8)
+    st = lib.ssd_backward(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(dy),
+                          _ptr(dfinal), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                          _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(workspace), workspace.numel(),
+                          _stream(x))
+    _check(st, "ssd_backward")
+    return out
 
 
 def selective_scan_workspace_bytes(b, L, Dc, N, G=1, *, chunk: int = 0, dtype=torch.bfloat16) -> int:

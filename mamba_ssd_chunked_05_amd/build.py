@@ -28,6 +28,7 @@ SOURCES = [
     "fused.hip",
     "wide.hip",
     "selective.hip",
+    "backward.hip",
 ]
 
 

@@ -459,6 +459,104 @@ ssd_status ssd_step_multi(const ssd_dims* dims, float* state, const void* x, con
 }
 
 // ---------------------------------------------------------------------------
+// backward pass
+// ---------------------------------------------------------------------------
+// The backward runs three fp32 scans on the generic chunk kernels: the adjoint (headdim P, dstate N)
+// and two transposed ones (headdim N, dstate P, one group per head).  The chunk must suit both.
+static bool backward_chunk_ok(const ssd::Shape& s, int64_t Q) {
+    if (Q % 16 || Q < 16 || Q > 512) return false;
+    ssd::Shape a = s, t = s;
+    a.io = t.io = 0;
+    a.Q = t.Q = Q;
+    t.P = s.N;
+    t.N = s.P;
+    t.G = s.H;
+    for (const ssd::Shape& x : {a, t})
+        if (ssd::chunk_scan_lds_bytes(x) > 160 * 1024 || ssd::chunk_state_lds_bytes(x) > 160 * 1024) return false;
+    return true;
+}
+
+static ssd_status check_backward(const ssd_dims* d, ssd::Shape* out) {
+    if (!d) return fail(SSD_ERR_NULL, "dims is NULL");
+    ssd_dims d2 = *d;
+    if (d2.chunk == 0) d2.chunk = 64;  // validated below with the backward's own choice
+    ssd::Shape s;
+    SSD_TRY(check_dims(&d2, Need::kStaged, &s));
+    if (s.N > 256)
+        return fail(SSD_ERR_UNSUPPORTED, "dstate %lld: the backward needs dstate <= 256", (long long)s.N);
+    int64_t Q = d->chunk;
+    if (Q == 0) {
+        for (int64_t cand : {256, 128, 64})
+            if (backward_chunk_ok(s, cand)) {
+                Q = cand;
+                break;
+            }
+        if (Q == 0) return fail(SSD_ERR_UNSUPPORTED, "no chunk size fits the backward's tiles in LDS");
+    } else if (!backward_chunk_ok(s, Q)) {
+        return fail(SSD_ERR_UNSUPPORTED, "chunk %lld: the backward needs a multiple of 16 up to 512 whose fp32 "
+                    "tiles fit the 160 KiB LDS", (long long)Q);
+    }
+    s.Q = Q;
+    s.nC = (s.L + Q - 1) / Q;
+    if (s.b * s.L * s.H > kMaxGrid * 4 || s.b * s.nC * s.H * s.N > kMaxGrid)
+        return fail(SSD_ERR_UNSUPPORTED, "problem too large for one launch grid");
+    *out = s;
+    return SSD_OK;
+}
+
+size_t ssd_backward_workspace_bytes(const ssd_dims* dims) {
+    try {
+        ssd::Shape s;
+        if (check_backward(dims, &s) != SSD_OK) return 0;
+        return ssd::backward_layout(s).total;
+    } catch (...) {
+        return 0;
+    }
+}
+
+ssd_status ssd_backward(const ssd_dims* dims, const void* x, const void* dt, const float* A, const void* B,
+                        const void* C, const float* D, const float* h0, const void* dy, const float* dfinal,
+                        void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    try {
+        ssd::Shape s;
+        SSD_TRY(check_backward(dims, &s));
+        Sizes z = sizes(s);
+        const size_t need = ssd::backward_layout(s).total;
+        Span sx{x, z.x, "x"}, sdt{dt, z.dt, "dt"}, sA{A, z.A, "A"}, sB{B, z.bc, "B"}, sC{C, z.bc, "C"},
+            sD{D, D ? z.A : 0, "D"}, sh0{h0, h0 ? z.hstate : 0, "h0"}, sdy{dy, z.x, "dy"},
+            sdf{dfinal, dfinal ? z.hstate : 0, "dfinal"}, sdx{dx, z.x, "dx"}, sddt{ddt, z.dt, "ddt"},
+            sdA{dA, z.A, "dA"}, sdB{dB, z.bc, "dB"}, sdC{dC, z.bc, "dC"}, sdD{dD, dD ? z.A : 0, "dD"},
+            sdh0{dh0, dh0 ? z.hstate : 0, "dh0"}, sws{workspace, need, "workspace"};
+        for (const Span& p : {sx, sdt, sA, sB, sC, sdy, sdx, sddt, sdA, sdB, sdC}) SSD_TRY(need_ptr(p));
+        if (s.b > 0 && s.L > 0) {
+            if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+            if (workspace_bytes < need)
+                return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, need);
+            if (reinterpret_cast<uintptr_t>(workspace) % 256)
+                return fail(SSD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        }
+        Span ins[] = {sx, sdt, sA, sB, sC, sD, sh0, sdy, sdf};
+        Span outs[] = {sdx, sddt, sdA, sdB, sdC, sdD, sdh0};
+        for (const Span& o : outs) {
+            SSD_TRY(no_alias(o, ins, 9));
+            for (const Span& o2 : outs)
+                if (&o2 != &o && overlap(o, o2)) return fail(SSD_ERR_ALIAS, "%s overlaps %s", o.name, o2.name);
+        }
+        if (s.b > 0 && s.L > 0) {
+            Span all[] = {sx, sdt, sA, sB, sC, sD, sh0, sdy, sdf, sdx, sddt, sdA, sdB, sdC, sdD, sdh0};
+            SSD_TRY(no_alias(sws, all, 16));
+        }
+        hipError_t e = ssd::launch_backward(s, x, dt, A, B, C, D, h0, dy, dfinal, dx, ddt, dA, dB, dC, dD, dh0,
+                                            workspace, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "ssd_backward");
+        return ok();
+    } catch (...) {
+        return fail(SSD_ERR_HIP, "internal error");
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Mamba-1 selective scan
 // ---------------------------------------------------------------------------
 static ssd_status check_selective(const ssd_dims* d, ssd::SelectiveLayout* lay) {

@@ -1,0 +1,402 @@
+// backward.hip -- gradients of the SSD forward (plain input step dt).
+//
+// Training needs the backward pass, and the forward's intermediate states are
+// recomputed rather than stored ("3.3 Hardware-Aware algorithms and GPU memory
+// hierarchy optimisation", section 6).  The pass is built on one identity: the
+// adjoint of the recurrence S_t = a_t S_{t-1} + dt_t x_t (outer) B_t with
+// y_t = C_t . S_t is the same kind of recurrence run backwards in time,
+//   G_t = a_{t+1} G_{t+1} + dy_t (outer) C_t,   G_{L-1} includes dfinal,
+// so three chunked scans of the forward's own kernels give everything:
+//   (b) G in reversed time, read out through B:   u_t = G_t B_t          -> dx
+//   (c) G^T in reversed time, read out through x: v_t = G_t^T x_t        -> dB, ddt
+//   (d) S^T forwards, read out through dy:        w_t = S_t^T dy_t       -> dC, ddt
+// (the transposed scans swap the roles of headdim and dstate, with one B/C
+// "group" per head).  The decay gradients follow from the log-decay
+// lambda_t = A sum_{k<=t} dt_k, on which the loss depends only through
+// differences: d lambda_t = C_t . w_t - dt_t x_t^T G_t B_t (+ <dfinal, S_L-1>
+// at the last token), then
+//   ddt_k = x_k^T G_k B_k + A sum_{t>=k} d lambda_t,  dA = sum_k dt_k sum_{t>=k} d lambda_t.
+// The scans run in fp32 (the generic chunk kernels with fp32 MFMA) on
+// converted, reversed or per-head copies of the inputs that this file builds.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssd {
+namespace bwd {
+
+// out[b, t, j, k] (fp32) = in[b, rev ? L-1-t : t, j / rep, k]; four consecutive k per thread
+template <class T>
+__global__ void __launch_bounds__(256) copy_kernel(const T* __restrict__ in, float* __restrict__ out, int64_t b,
+                                                   int64_t L, int J, int K, int rep, int rev, int64_t n4) {
+    const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i4 >= n4) return;
+    const int64_t e = i4 * 4;
+    const int k = (int)(e % K);
+    const int j = (int)((e / K) % J);
+    const int64_t t = (e / ((int64_t)K * J)) % L;
+    const int64_t bb = e / ((int64_t)K * J * L);
+    const int64_t ts = rev ? L - 1 - t : t;
+    const int64_t src = ((bb * L + ts) * (J / rep) + j / rep) * K + k;
+    float4 o;
+    o.x = to_f32(in[src]);
+    o.y = to_f32(in[src + 1]);
+    o.z = to_f32(in[src + 2]);
+    o.w = to_f32(in[src + 3]);
+    *reinterpret_cast<float4*>(out + e) = o;
+}
+
+// decay steps of the reversed scans: d'[b, tau, h] = dt[b, L - tau, h] for tau >= 1, 0 at tau = 0;
+// and the forward steps as fp32
+template <class T>
+__global__ void __launch_bounds__(256) steps_kernel(const T* __restrict__ dt, float* __restrict__ drev,
+                                                    float* __restrict__ dfwd, int64_t L, int H, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int h = (int)(i % H);
+    const int64_t tau = (i / H) % L;
+    const int64_t bb = i / ((int64_t)H * L);
+    dfwd[i] = to_f32(dt[i]);
+    drev[i] = tau == 0 ? 0.0f : to_f32(dt[(bb * L + (L - tau)) * H + h]);
+}
+
+// (b, H, P, N) -> (b, H, N, P), fp32; a NULL source gives zeros
+__global__ void __launch_bounds__(256) transpose_kernel(const float* __restrict__ in, float* __restrict__ out,
+                                                        int P, int N, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int p = (int)(i % P);
+    const int nn = (int)((i / P) % N);
+    const int64_t bh = i / ((int64_t)P * N);
+    out[i] = in ? in[(bh * P + p) * N + nn] : 0.0f;
+}
+
+// the reversed scans' input step is 1 (0 past the sequence end): overwrite dt_t of the chunk cumsum
+__global__ void __launch_bounds__(256) ones_kernel(float* __restrict__ dt_t, int64_t L, int Q, int64_t nC, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t pos = i % ((int64_t)nC * Q);  // (c, i) of one (b, h)
+    dt_t[i] = pos < L ? 1.0f : 0.0f;
+}
+
+// per (b, t, h): dx, q_t = x^T G B = v_t . B_t, and d lambda_t = C_t . w_t - dt_t q_t
+template <class T>
+__global__ void __launch_bounds__(256) head_kernel(const T* __restrict__ dy, const T* __restrict__ x,
+                                                   const T* __restrict__ dt,
+                                                   const T* __restrict__ B, const T* __restrict__ C,
+                                                   const float* __restrict__ D, const float* __restrict__ u_r,
+                                                   const float* __restrict__ v_r, const float* __restrict__ w,
+                                                   T* __restrict__ dx, float* __restrict__ q, float* __restrict__ dlam,
+                                                   float* __restrict__ dxy, int64_t L, int H, int P, int N, int G,
+                                                   int64_t nitems) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= nitems) return;
+    const int h = (int)(item % H);
+    const int64_t t = (item / H) % L;
+    const int64_t bb = item / ((int64_t)H * L);
+    const int g = h / (H / G);
+    const int64_t bt = bb * L + t, btr = bb * L + (L - 1 - t);
+    const float d = to_f32(dt[bt * H + h]);
+    const float Dh = D ? D[h] : 0.0f;
+    float sxy = 0.0f;
+    for (int p = lane; p < P; p += 64) {
+        const float u = u_r[(btr * H + h) * P + p];
+        const float gy = to_f32(dy[(bt * H + h) * P + p]);
+        dx[(bt * H + h) * P + p] = from_f32<T>(fmaf(d, u, Dh * gy));
+        sxy = fmaf(gy, to_f32(x[(bt * H + h) * P + p]), sxy);
+    }
+    float sq = 0.0f, sw = 0.0f;
+    for (int n = lane; n < N; n += 64) {
+        sq += v_r[(btr * H + h) * N + n] * to_f32(B[(bt * G + g) * N + n]);
+        sw += w[(bt * H + h) * N + n] * to_f32(C[(bt * G + g) * N + n]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        sq += __shfl_xor(sq, off, 64);
+        sw += __shfl_xor(sw, off, 64);
+        sxy += __shfl_xor(sxy, off, 64);
+    }
+    if (lane == 0) {
+        q[(bb * H + h) * L + t] = sq;
+        dlam[(bb * H + h) * L + t] = sw - d * sq;
+        dxy[(bb * H + h) * L + t] = sxy;
+    }
+}
+
+// per (b, t, g, n): dB = sum over the group's heads of dt v, dC = sum of w
+template <class T>
+__global__ void __launch_bounds__(256) group_kernel(const T* __restrict__ dt, const float* __restrict__ v_r,
+                                                    const float* __restrict__ w, T* __restrict__ dB, T* __restrict__ dC,
+                                                    int64_t L, int H, int N, int G, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int nn = (int)(i % N);
+    const int g = (int)((i / N) % G);
+    const int64_t t = (i / ((int64_t)N * G)) % L;
+    const int64_t bb = i / ((int64_t)N * G * L);
+    const int hpg = H / G;
+    const int64_t bt = bb * L + t, btr = bb * L + (L - 1 - t);
+    float sb = 0.0f, sc = 0.0f;
+    for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+        sb = fmaf(to_f32(dt[bt * H + h]), v_r[(btr * H + h) * N + nn], sb);
+        sc += w[(bt * H + h) * N + nn];
+    }
+    dB[i] = from_f32<T>(sb);
+    dC[i] = from_f32<T>(sc);
+}
+
+// per (b, h): the final-state term, suffix sums R_k = sum_{t>=k} d lambda_t (fp64), ddt, and the
+// (b, h) parts of dA = sum_k dt_k R_k and dD = sum_t dy_t . x_t
+template <class T>
+__global__ void __launch_bounds__(256) suffix_kernel(const float* __restrict__ dlam, const float* __restrict__ q,
+                                                     const float* __restrict__ dxy, const T* __restrict__ dt,
+                                                     const float* __restrict__ A,
+                                                     const float* __restrict__ dfinal, const float* __restrict__ finT,
+                                                     T* __restrict__ ddt, double* __restrict__ dA_part,
+                                                     double* __restrict__ dD_part, int64_t L, int H, int P, int N) {
+    __shared__ double red[256];
+    const int tid = threadIdx.x;
+    const int h = blockIdx.x;
+    const int64_t bb = blockIdx.y;
+    const int64_t bh = bb * H + h;
+    const float Ah = A[h];
+    // <dfinal, S_{L-1}>: the loss's dependence on the last log-decay through the final state
+    double fterm = 0.0;
+    if (dfinal) {
+        const int64_t PN = (int64_t)P * N;
+        for (int64_t e = tid; e < PN; e += 256) {
+            const int p = (int)(e / N), n = (int)(e % N);
+            fterm += (double)dfinal[bh * PN + e] * (double)finT[(bh * N + n) * P + p];
+        }
+    }
+    red[tid] = fterm;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) red[tid] += red[tid + s];
+        __syncthreads();
+    }
+    fterm = red[0];
+    __syncthreads();
+    // thread tid owns tokens [t0, t1)
+    const int64_t per = (L + 255) / 256;
+    const int64_t t0 = tid * per < L ? tid * per : L, t1 = t0 + per < L ? t0 + per : L;
+    const float* dl = dlam + bh * L;
+    double loc = 0.0;
+    for (int64_t t = t0; t < t1; ++t) loc += (double)dl[t] + (t == L - 1 ? fterm : 0.0);
+    // exclusive suffix over the threads after this one
+    red[tid] = loc;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const double add = tid + off < 256 ? red[tid + off] : 0.0;
+        __syncthreads();
+        red[tid] += add;
+        __syncthreads();
+    }
+    double R = red[tid] - loc;  // sum over later threads' tokens
+    double da = 0.0, dd = 0.0;
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+        R += (double)dl[t] + (t == L - 1 ? fterm : 0.0);
+        const float d = to_f32(dt[(bb * L + t) * H + h]);
+        ddt[(bb * L + t) * H + h] = from_f32<T>((float)((double)Ah * R + (double)q[bh * L + t]));
+        da += (double)d * R;
+        dd += (double)dxy[bh * L + t];
+    }
+    __syncthreads();
+    red[tid] = da;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) red[tid] += red[tid + s];
+        __syncthreads();
+    }
+    if (tid == 0) dA_part[bh] = red[0];
+    __syncthreads();
+    red[tid] = dd;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) red[tid] += red[tid + s];
+        __syncthreads();
+    }
+    if (tid == 0) dD_part[bh] = red[0];
+}
+
+// dA[h], dD[h]: sums over the batch rows
+__global__ void __launch_bounds__(256) reduce_kernel(const double* __restrict__ dA_part, const double* __restrict__ dD_part,
+                                                     float* __restrict__ dA, float* __restrict__ dD, int64_t b, int H) {
+    const int h = blockIdx.x * 256 + threadIdx.x;
+    if (h >= H) return;
+    double sa = 0.0, sd = 0.0;
+    for (int64_t bb = 0; bb < b; ++bb) {
+        sa += dA_part[bb * H + h];
+        sd += dD_part[bb * H + h];
+    }
+    dA[h] = (float)sa;
+    if (dD) dD[h] = (float)sd;
+}
+
+// dh0 = a_0 G_0 (G_0: the reversed adjoint scan's final state); with no tokens, dh0 = dfinal
+template <class T>
+__global__ void __launch_bounds__(256) dh0_kernel(const float* __restrict__ G0, const T* __restrict__ dt,
+                                                  const float* __restrict__ A, const float* __restrict__ dfinal,
+                                                  float* __restrict__ dh0, int64_t L, int H, int64_t PN, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t bh = i / PN;
+    const int h = (int)(bh % H);
+    const int64_t bb = bh / H;
+    if (L == 0) {
+        dh0[i] = dfinal ? dfinal[i] : 0.0f;
+        return;
+    }
+    dh0[i] = fast_exp2(to_f32(dt[(bb * L) * H + h]) * A[h] * kLog2e) * G0[i];
+}
+
+inline dim3 grid1(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
+
+template <class T>
+hipError_t copy(const void* in, float* out, int64_t b, int64_t L, int J, int K, int rep, bool rev, hipStream_t st) {
+    const int64_t n4 = b * L * J * (int64_t)K / 4;
+    if (n4 == 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_kernel<T>, grid1(n4), dim3(256), 0, st, static_cast<const T*>(in), out, b, L, J, K, rep,
+                       rev ? 1 : 0, n4);
+    return hipGetLastError();
+}
+
+// one chunked scan (cumsum arrays given): chunk states, state pass from h0, chunk output
+hipError_t scan(const Shape& s, const float* xin, const float* Bin, const float* Cin, const float* dt_t,
+                const float* cs, float* states, const float* h0, float* fin, float* y, hipStream_t st) {
+    hipError_t e = launch_chunk_state(s, xin, Bin, dt_t, cs, states, st);
+    if (e != hipSuccess) return e;
+    e = launch_state_passing(s, states, cs, h0, fin, st);
+    if (e != hipSuccess) return e;
+    return launch_chunk_scan(s, xin, Bin, Cin, dt_t, cs, states, nullptr, y, st);
+}
+
+template <class T>
+hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const void* dt, const float* A,
+               const void* B, const void* C, const float* D, const float* h0, const void* dy, const float* dfinal,
+               void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0, char* ws, hipStream_t st) {
+    const int64_t b = s.b, L = s.L;
+    const int H = (int)s.H, P = (int)s.P, N = (int)s.N, G = (int)s.G;
+    auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+    float *xr = F(f.xr), *xf = F(f.xf), *dyr = F(f.dyr), *dyf = F(f.dyf), *Cr = F(f.Cr), *Br = F(f.Br);
+    float *Crh = F(f.Crh), *Bh = F(f.Bh), *drev = F(f.drev), *dfwd = F(f.dfwd), *dt_t = F(f.dt_t), *cs = F(f.cs);
+    float *states = F(f.states), *u_r = F(f.u_r), *v_r = F(f.v_r), *w = F(f.w), *G0 = F(f.G0), *dfT = F(f.dfT);
+    float *h0T = F(f.h0T), *finT = F(f.finT), *fscr = F(f.fscr), *q = F(f.q), *dlam = F(f.dlam), *dxy = F(f.dxy);
+    double *dA_part = reinterpret_cast<double*>(ws + f.dA_part), *dD_part = reinterpret_cast<double*>(ws + f.dD_part);
+    const int64_t PN = (int64_t)P * N;
+    hipError_t e;
+#define BWD_CHECK(expr)             \
+    do {                            \
+        e = (expr);                 \
+        if (e != hipSuccess) return e; \
+    } while (0)
+    if (L == 0 || b == 0) {
+        // no tokens or no rows: zero gradients of the parameters (a sum over nothing), dh0 = dfinal
+        hipLaunchKernelGGL(reduce_kernel, grid1(H), dim3(256), 0, st, (const double*)nullptr, (const double*)nullptr,
+                           dA, dD, (int64_t)0, H);
+        BWD_CHECK(hipGetLastError());
+        if (dh0 && b > 0) {
+            hipLaunchKernelGGL(dh0_kernel<T>, grid1(b * H * PN), dim3(256), 0, st, (const float*)nullptr,
+                               static_cast<const T*>(dt), A, dfinal, dh0, (int64_t)0, H, PN, b * H * PN);
+            BWD_CHECK(hipGetLastError());
+        }
+        return hipSuccess;
+    }
+    // converted, reversed and per-head copies
+    BWD_CHECK(copy<T>(x, xr, b, L, H, P, 1, true, st));
+    BWD_CHECK(copy<T>(x, xf, b, L, H, P, 1, false, st));
+    BWD_CHECK(copy<T>(dy, dyr, b, L, H, P, 1, true, st));
+    BWD_CHECK(copy<T>(dy, dyf, b, L, H, P, 1, false, st));
+    BWD_CHECK(copy<T>(C, Cr, b, L, G, N, 1, true, st));
+    BWD_CHECK(copy<T>(B, Br, b, L, G, N, 1, true, st));
+    BWD_CHECK(copy<T>(C, Crh, b, L, H, N, H / G, true, st));
+    BWD_CHECK(copy<T>(B, Bh, b, L, H, N, H / G, false, st));
+    hipLaunchKernelGGL(steps_kernel<T>, grid1(b * L * H), dim3(256), 0, st, static_cast<const T*>(dt), drev, dfwd, L,
+                       H, b * L * H);
+    BWD_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(transpose_kernel, grid1(b * H * PN), dim3(256), 0, st, dfinal, dfT, P, N, b * H * PN);
+    BWD_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(transpose_kernel, grid1(b * H * PN), dim3(256), 0, st, h0, h0T, P, N, b * H * PN);
+    BWD_CHECK(hipGetLastError());
+
+    const DtFront none{nullptr, 0, 0, 0, 0.0f, 0.0f};
+    Shape sb = s;  // the adjoint scan: headdim P, dstate N, G groups, fp32
+    sb.io = 0;
+    Shape sT = s;  // the transposed scans: headdim N, dstate P, one group per head
+    sT.io = 0;
+    sT.P = N;
+    sT.N = P;
+    sT.G = H;
+    // reversed scans (b) and (c): decay steps d', input step 1
+    BWD_CHECK(launch_chunk_cumsum(sb, none, drev, A, dt_t, cs, st));
+    hipLaunchKernelGGL(ones_kernel, grid1(b * H * s.nC * s.Q), dim3(256), 0, st, dt_t, L, (int)s.Q, s.nC,
+                       b * H * s.nC * s.Q);
+    BWD_CHECK(hipGetLastError());
+    BWD_CHECK(scan(sb, dyr, Cr, Br, dt_t, cs, states, dfinal, G0, u_r, st));
+    BWD_CHECK(scan(sT, Crh, dyr, xr, dt_t, cs, states, dfT, fscr, v_r, st));
+    // forward transposed scan (d): decay and input step dt
+    BWD_CHECK(launch_chunk_cumsum(sb, none, dfwd, A, dt_t, cs, st));
+    BWD_CHECK(scan(sT, Bh, xf, dyf, dt_t, cs, states, h0 ? h0T : nullptr, finT, w, st));
+
+    // combine
+    const int64_t nh = b * L * H;
+    hipLaunchKernelGGL(head_kernel<T>, dim3((unsigned)((nh + 3) / 4)), dim3(256), 0, st, static_cast<const T*>(dy),
+                       static_cast<const T*>(x), static_cast<const T*>(dt), static_cast<const T*>(B),
+                       static_cast<const T*>(C), D, u_r, v_r, w, static_cast<T*>(dx), q, dlam, dxy, L, H, P, N, G, nh);
+    BWD_CHECK(hipGetLastError());
+    const int64_t ng = b * L * G * (int64_t)N;
+    hipLaunchKernelGGL(group_kernel<T>, grid1(ng), dim3(256), 0, st, static_cast<const T*>(dt), v_r, w,
+                       static_cast<T*>(dB), static_cast<T*>(dC), L, H, N, G, ng);
+    BWD_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(suffix_kernel<T>, dim3((unsigned)H, (unsigned)b), dim3(256), 0, st, dlam, q, dxy,
+                       static_cast<const T*>(dt), A, dfinal, finT, static_cast<T*>(ddt), dA_part, dD_part, L, H, P,
+                       N);
+    BWD_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(reduce_kernel, grid1(H), dim3(256), 0, st, dA_part, dD_part, dA, dD, b, H);
+    BWD_CHECK(hipGetLastError());
+    if (dh0) {
+        hipLaunchKernelGGL(dh0_kernel<T>, grid1(b * H * PN), dim3(256), 0, st, G0, static_cast<const T*>(dt), A,
+                           dfinal, dh0, L, H, PN, b * H * PN);
+        BWD_CHECK(hipGetLastError());
+    }
+#undef BWD_CHECK
+    return hipSuccess;
+}
+
+}  // namespace bwd
+
+BackwardLayout backward_layout(const Shape& s) {
+    auto a256 = [](size_t v) { return (v + 255) / 256 * 256; };
+    BackwardLayout f{};
+    const size_t BLHP = (size_t)(s.b * s.L * s.H * s.P) * 4, BLHN = (size_t)(s.b * s.L * s.H * s.N) * 4;
+    const size_t BLGN = (size_t)(s.b * s.L * s.G * s.N) * 4, BLH = (size_t)(s.b * s.L * s.H) * 4;
+    const size_t CS = (size_t)(s.b * s.H * s.nC * s.Q) * 4, ST = (size_t)(s.b * s.nC * s.H * s.P * s.N) * 4;
+    const size_t HS = (size_t)(s.b * s.H * s.P * s.N) * 4, BH8 = (size_t)(s.b * s.H) * 8;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += a256(bytes);
+        return at;
+    };
+    f.xr = take(BLHP), f.xf = take(BLHP), f.dyr = take(BLHP), f.dyf = take(BLHP);
+    f.Cr = take(BLGN), f.Br = take(BLGN), f.Crh = take(BLHN), f.Bh = take(BLHN);
+    f.drev = take(BLH), f.dfwd = take(BLH), f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST);
+    f.u_r = take(BLHP), f.v_r = take(BLHN), f.w = take(BLHN);
+    f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS), f.fscr = take(HS);
+    f.q = take(BLH), f.dlam = take(BLH), f.dxy = take(BLH), f.dA_part = take(BH8), f.dD_part = take(BH8);
+    f.total = o;
+    return f;
+}
+
+hipError_t launch_backward(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
+                           const void* C, const float* D, const float* h0, const void* dy, const float* dfinal,
+                           void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0, void* workspace,
+                           hipStream_t st) {
+    const BackwardLayout f = backward_layout(s);
+    char* ws = static_cast<char*>(workspace);
+    if (s.io == 1)
+        return bwd::run<bf16>(s, f, x, dt, A, B, C, D, h0, dy, dfinal, dx, ddt, dA, dB, dC, dD, dh0, ws, st);
+    return bwd::run<float>(s, f, x, dt, A, B, C, D, h0, dy, dfinal, dx, ddt, dA, dB, dC, dD, dh0, ws, st);
+}
+
+}  // namespace ssd

@@ -78,6 +78,18 @@ hipError_t launch_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, in
                                  const float* D, const float* h0, void* y, float* final_state, int64_t seg_len,
                                  void* workspace, hipStream_t st);
 
+// Backward pass (backward.hip): three fp32 chunked scans on converted copies of the
+// inputs.  Byte offsets of the workspace pieces (all 256-byte aligned).
+struct BackwardLayout {
+    size_t xr, xf, dyr, dyf, Cr, Br, Crh, Bh, drev, dfwd, dt_t, cs, states, u_r, v_r, w, G0, dfT, h0T, finT, fscr,
+        q, dlam, dxy, dA_part, dD_part, total;
+};
+BackwardLayout backward_layout(const Shape& s);
+hipError_t launch_backward(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
+                           const void* C, const float* D, const float* h0, const void* dy, const float* dfinal,
+                           void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0, void* workspace,
+                           hipStream_t st);
+
 // LDS bytes the generic chunk kernels need; used by validation.
 size_t chunk_state_lds_bytes(const Shape& s);
 size_t chunk_scan_lds_bytes(const Shape& s);

@@ -350,10 +350,23 @@ __global__ void __launch_bounds__(256) selective_carry_kernel(const float* A, co
     const int c = (int)((i / N) % Dc), n = (int)(i % N);
     const float a2 = A[(int64_t)c * N + n] * kLog2e;
     float hv = h0 ? h0[i] : 0.0f;
-    for (int s = 0; s + 1 < nseg; ++s) {
-        const int64_t o = ((bb * (nseg - 1) + s) * Dc + c) * (int64_t)N + n;
-        hv = fmaf(fast_exp2(a2 * seg_sums[(bb * (nseg - 1) + s) * Dc + c]), hv, seg_states[o]);
-        seg_states[o] = hv;
+    // eight segments' loads in flight per step of the chain
+    constexpr int K = 8;
+    for (int s0 = 0; s0 + 1 < nseg; s0 += K) {
+        float loc[K], dec[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int s = s0 + k < nseg - 1 ? s0 + k : nseg - 2;
+            loc[k] = seg_states[((bb * (nseg - 1) + s) * Dc + c) * (int64_t)N + n];
+            dec[k] = seg_sums[(bb * (nseg - 1) + s) * Dc + c];
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (s0 + k < nseg - 1) {
+                hv = fmaf(fast_exp2(a2 * dec[k]), hv, loc[k]);
+                seg_states[((bb * (nseg - 1) + s0 + k) * Dc + c) * (int64_t)N + n] = hv;
+            }
+        }
     }
     if (final_state) final_state[i] = hv;
 }

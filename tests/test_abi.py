@@ -27,7 +27,7 @@ def _declared():
 def test_header_symbols_exported():
     lib = ssd.load()
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
 
@@ -249,3 +249,44 @@ def test_selective_validates_pointers_and_workspace():
     assert _sel(d, fe=ctypes.byref(over), ws=ws, ws_bytes=need) == ALIAS
     # empty batch: a no-op
     assert _sel(_sd(b=0)) == OK
+
+
+def _bwd(d, ws=None, ws_bytes=0, **over):
+    lib = ssd.load()
+    p = dict(x=_p(0), dt=_p(1 << 30), A=_p(2 << 30), B=_p(3 << 30), C=_p(4 << 30), D=None, h0=None, dy=_p(5 << 30),
+             dfinal=None, dx=_p(6 << 30), ddt=_p(7 << 30), dA=_p(8 << 30), dB=_p(9 << 30), dC=_p(10 << 30), dD=None,
+             dh0=None)
+    p.update(over)
+    return lib.ssd_backward(ctypes.byref(d) if d is not None else None, p["x"], p["dt"], p["A"], p["B"], p["C"],
+                            p["D"], p["h0"], p["dy"], p["dfinal"], p["dx"], p["ddt"], p["dA"], p["dB"], p["dC"],
+                            p["dD"], p["dh0"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("dims,code", [
+    (None, NULL),
+    (_d(io=3), DTYPE),
+    (_d(H=6, G=4), SHAPE),
+    (_d(N=512), UNSUP),  # the transposed scans take dstate as their headdim
+    (_d(Q=1024), UNSUP),
+    (_d(Q=24), UNSUP),
+])
+def test_backward_rejects_bad_dims(dims, code):
+    assert _bwd(dims) == code
+
+
+def test_backward_validates_pointers_and_workspace():
+    lib = ssd.load()
+    d = _d(L=512, Q=0)
+    need = lib.ssd_backward_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    ws = _p(16 << 30)
+    assert _bwd(d) == WS
+    assert _bwd(d, ws=ws, ws_bytes=need - 1) == WS
+    assert _bwd(d, ws=_p((16 << 30) + 64), ws_bytes=need) == WS
+    assert _bwd(d, ws=ws, ws_bytes=need, dy=None) == NULL
+    assert _bwd(d, ws=ws, ws_bytes=need, dA=None) == NULL
+    assert _bwd(d, ws=ws, ws_bytes=need, dx=_p(64)) == ALIAS  # dx over x
+    assert _bwd(d, ws=ws, ws_bytes=need, dB=_p((6 << 30) + 64)) == ALIAS  # dB over dx
+    assert _bwd(d, ws=_p(5 << 30), ws_bytes=need) == ALIAS  # workspace over dy
+    # no rows: nothing to validate against the workspace
+    assert lib.ssd_backward_workspace_bytes(ctypes.byref(_d(b=0))) >= 0

@@ -1,0 +1,120 @@
+"""GPU parity of the backward pass (ssd_backward) against the fp64 backward oracle.
+
+Every gradient (dx, ddt, dA, dB, dC, dD, dh0) is compared with the oracle on the same
+seeded inputs, at sizes that span several chunks with ragged tails, groups, both io
+dtypes, with and without h0, D and a final-state gradient.  The 2.7B-shaped workload
+is checked at full size on sampled heads (every gradient that belongs to one head).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mamba_ssd_chunked_05_amd as ssd_mod
+import oracle
+from synth import make_config_inputs, make_forward_inputs
+from tests.gpu_util import Y_TOL, assert_close_state, dev, host, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+# (b, L, H, P, N, G, dtype, chunk, with_h0_and_dfinal)
+CASES = [
+    (1, 100, 2, 16, 16, 1, "f32", 0, True),
+    (2, 300, 4, 32, 64, 2, "f32", 64, True),
+    (1, 517, 4, 64, 128, 1, "bf16", 0, True),
+    (2, 257, 6, 64, 64, 3, "bf16", 128, False),
+    (1, 1, 2, 16, 32, 1, "f32", 0, True),
+    (1, 1000, 2, 64, 128, 1, "f32", 256, True),
+]
+
+
+def _ids(c):
+    return "b{}_L{}_H{}_P{}_N{}_G{}_{}_Q{}_{}".format(*c[:8], "h0" if c[8] else "noh0")
+
+
+def _grads(seed, case, dt_mode="config", with_D=True):
+    b, L, H, P, N, G, dtype, chunk, full = case
+    fi = make_forward_inputs(b, L, H, P, N, G, dtype, seed, dt_mode=dt_mode, with_D=with_D,
+                             h0_std=0.4 if full else 0.0)
+    rng = np.random.default_rng(seed + 7)
+    from synth import round_to
+
+    dy = round_to(rng.standard_normal(fi.x.shape), dtype)
+    dfinal = round_to(rng.standard_normal((b, H, P, N)), "f32") if full else None
+    ref = oracle.backward(fi.x, fi.dt, fi.A, fi.B, fi.C, fi.D, fi.h0, dy, dfinal)
+    got = ssd_mod.backward(dev(fi.x, dtype), dev(fi.dt, dtype), dev(fi.A), dev(fi.B, dtype), dev(fi.C, dtype),
+                           dev(fi.D), dev(fi.h0), dev(dy, dtype), dev(dfinal), chunk=chunk)
+    torch.cuda.synchronize()
+    return ref, {k: (None if v is None else host(v)) for k, v in got.items()}
+
+
+def _check(ref, got, dtype, names=("dx", "ddt", "dB", "dC", "dA", "dD"), tol_dA=None):
+    for k in names:
+        if ref[k] is None:
+            continue
+        tol = tol_dA if (k == "dA" and tol_dA is not None) else Y_TOL[dtype]
+        assert np.all(np.isfinite(got[k])), f"{k}: non-finite values"
+        e = rel_l2(got[k], ref[k])
+        assert e <= tol, f"{k}: rel L2 {e:.3e} > {tol:.0e}"
+    assert_close_state(got["dh0"], ref["dh0"], "dh0")
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_backward(gpu_ssd, case):
+    ref, got = _grads(300, case)
+    _check(ref, got, case[6])
+
+
+@pytest.mark.parametrize("mode", ["long_memory", "extreme", "zero"])
+def test_backward_stress(gpu_ssd, mode):
+    """Long memory (the adjoint crosses every chunk), huge steps (decay underflow), zero steps.
+
+    With steps up to 2 the in-chunk log2 decay reaches |l| ~ 64 * 2 * 16 * log2(e) ~ 3000, whose fp32
+    ulp (2.4e-4) makes every decay factor of the fp32 scans relative-accurate to ~1.7e-4 only.  dA is
+    the sum over tokens of dt_k (Z_k - dt_k q_k), two terms that nearly cancel when the decay is strong,
+    so that error reaches dA at ~1e-2 relative; the other gradients stay at the fp32 bar."""
+    ref, got = _grads(301, (1, 700, 4, 32, 32, 1, "f32", 64, True), dt_mode=mode)
+    _check(ref, got, "f32", tol_dA=2e-2 if mode == "extreme" else None)
+
+
+def test_backward_without_D(gpu_ssd):
+    ref, got = _grads(302, (2, 200, 4, 16, 32, 2, "f32", 64, True), with_D=False)
+    assert got["dD"] is None
+    _check(ref, got, "f32")
+
+
+def test_backward_empty(gpu_ssd):
+    """L = 0: dh0 = dfinal and zero parameter gradients."""
+    fi = make_forward_inputs(2, 1, 2, 16, 16, 1, "f32", 303, h0_std=0.3)
+    dfinal = np.random.default_rng(3).standard_normal((2, 2, 16, 16)).astype(np.float32).astype(np.float64)
+    got = ssd_mod.backward(dev(fi.x[:, :0]), dev(fi.dt[:, :0]), dev(fi.A), dev(fi.B[:, :0]), dev(fi.C[:, :0]),
+                           dev(fi.D), dev(fi.h0), dev(fi.x[:, :0]), dev(dfinal))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got["dh0"]), dfinal)
+    assert np.all(host(got["dA"]) == 0) and np.all(host(got["dD"]) == 0)
+
+
+def test_backward_workload_sampled(gpu_ssd):
+    """The 2.7B-shaped workload (64K tokens, 80 heads) at full size; the oracle recomputes the
+    per-head gradients (dx, ddt, dA, dD, dh0) of sampled heads over the whole sequence."""
+    fi = make_config_inputs("cfg2_64k")
+    rng = np.random.default_rng(304)
+    from synth import round_to
+
+    dy = round_to(rng.standard_normal(fi.x.shape), "bf16")
+    b, L, H, P, N, G = fi.dims
+    dfinal = round_to(rng.standard_normal((b, H, P, N)), "f32")
+    got = ssd_mod.backward(dev(fi.x, "bf16"), dev(fi.dt, "bf16"), dev(fi.A), dev(fi.B, "bf16"), dev(fi.C, "bf16"),
+                           dev(fi.D), None, dev(dy, "bf16"), dev(dfinal))
+    torch.cuda.synchronize()
+    got = {k: (None if v is None else host(v)) for k, v in got.items()}
+    heads = [0, 47, 79]
+    ref = oracle.backward(fi.x[:, :, heads], fi.dt[:, :, heads], fi.A[heads], fi.B, fi.C, fi.D[heads], None,
+                          dy[:, :, heads], dfinal[:, heads])
+    for k, sl in (("dx", np.s_[:, :, heads]), ("ddt", np.s_[:, :, heads]), ("dA", np.s_[heads]),
+                  ("dD", np.s_[heads])):
+        e = rel_l2(got[k][sl], ref[k])
+        assert e <= Y_TOL["bf16"], f"{k}: rel L2 {e:.3e}"
+    assert_close_state(got["dh0"][:, heads], ref["dh0"], "dh0")
