@@ -13,6 +13,7 @@ The printed JSON line also carries
   * cpu_baseline -- the fp64 oracle timed on this host on a bounded sample;
   * decode       -- 64 back-to-back ssd_step calls on the 2.7B decode shape, the same 64 steps
                     replayed as one graph, and as one ssd_step_multi call (state kept on chip);
+  * backward     -- ssd_backward (all gradients) on the same 2.7B workload;
   * selective_scan -- the Mamba-1 selective scan (ssd_selective_scan) on the same width
                     (5120 channels, N = 16, 64K tokens, zero-order hold), with its own ALU
                     roofline and oracle baseline.
@@ -34,6 +35,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3  # dense fp32 MFMA (the backward's scans run in fp32)
+# backward FLOP per token-head in its recurrence form: state recompute (3PN), adjoint update (3PN) and
+# the four contractions G.B, G^T.x, S^T.dy and <G, S> (2PN each)
+BWD_FLOP_PER_TOKEN_HEAD_PN = 14
 # fp32 VALU issue rate without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, in G lane-ops/s
 PEAK_VALU_GOPS = 256 * 4 * 16 * 2.4
 # lane operations of one selective-scan element update (token, channel, state entry) in its
@@ -51,6 +56,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-selective", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle's timed sample (0 = all)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this many MiB (hardware-counter calibration)")
@@ -327,6 +333,35 @@ def main():
         }
         log(f"decode: {step_ms * 1e3:.1f} us/step, {gbs:.0f} GB/s algorithmic; graph {graph_ms * 1e3:.1f} us/step; "
             f"multi-step {multi_ms * 1e3 / nst:.2f} us/step ({multi_gbs:.0f} GB/s algorithmic)")
+
+    # ---- backward pass on the same workload --------------------------------------------------------
+    if not args.no_backward:
+        gen = torch.Generator(device=dev).manual_seed(11)
+        gdy = torch.randn(x.shape, generator=gen, device=dev, dtype=torch.float32).to(tdt)
+        gdf = torch.randn((b, H, P, N), generator=gen, device=dev, dtype=torch.float32)
+        bws = torch.empty(max(ssd.backward_workspace_bytes(x, B, 0), 1), dtype=torch.uint8, device=dev)
+
+        def bwd():
+            ssd.backward(x, dt, A, B, C, D, None, gdy, gdf, workspace=bws)
+
+        bwd_ms = timed(bwd, max(3, args.steps // 4))
+        bflop = BWD_FLOP_PER_TOKEN_HEAD_PN * P * N * tokens * H
+        btf = bflop / (bwd_ms / 1e3) / 1e12
+        result["backward"] = {
+            "workload": f"{args.workload}: ssd_backward b={b} L={L} H={H} P={P} N={N} G={G} {cfg['dtype']} io, "
+                        f"every gradient (dx, ddt, dA, dB, dC, dD, dh0), final-state gradient given",
+            "ms_per_call": bwd_ms,
+            "tokens_per_s": tokens / (bwd_ms / 1e3),
+            "workspace_bytes": int(bws.numel()),
+            "roofline": {"kernel": "ssd_backward (whole call: three fp32 chunked scans and the combine kernels)",
+                         "bound": "mfma", "achieved": btf, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                         "frac": btf / PEAK_FP32_MFMA_TFLOPS,
+                         "flop_per_token_head": BWD_FLOP_PER_TOKEN_HEAD_PN * P * N},
+        }
+        log(f"backward: {bwd_ms:.3f} ms/call, {tokens / (bwd_ms / 1e3) / 1e6:.1f} M tok/s, {btf:.1f} TFLOP/s "
+            f"(recurrence-form count) against the fp32 MFMA peak")
+        del gdy, gdf, bws
+        torch.cuda.empty_cache()
 
     # ---- Mamba-1 selective scan on the same width ------------------------------------------------
     if not args.no_selective:

@@ -484,6 +484,8 @@ static ssd_status check_backward(const ssd_dims* d, ssd::Shape* out) {
     SSD_TRY(check_dims(&d2, Need::kStaged, &s));
     if (s.N > 256)
         return fail(SSD_ERR_UNSUPPORTED, "dstate %lld: the backward needs dstate <= 256", (long long)s.N);
+    if ((2 * s.G * s.N + s.H) * 4 > 64 * 1024)
+        return fail(SSD_ERR_UNSUPPORTED, "the backward stages B and C of all groups of a token in 64 KiB of LDS");
     int64_t Q = d->chunk;
     if (Q == 0) {
         for (int64_t cand : {256, 128, 64})

@@ -24,9 +24,9 @@
 namespace ssd {
 namespace bwd {
 
-// out[b, t, j, k] (fp32) = in[b, rev ? L-1-t : t, j / rep, k]; four consecutive k per thread
-template <class T>
-__global__ void __launch_bounds__(256) copy_kernel(const T* __restrict__ in, float* __restrict__ out, int64_t b,
+// out[b, t, j, k] = in[b, rev ? L-1-t : t, j / rep, k] (fp32 or bf16 out); four consecutive k per thread
+template <class T, class O>
+__global__ void __launch_bounds__(256) copy_kernel(const T* __restrict__ in, O* __restrict__ out, int64_t b,
                                                    int64_t L, int J, int K, int rep, int rev, int64_t n4) {
     const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i4 >= n4) return;
@@ -37,12 +37,8 @@ __global__ void __launch_bounds__(256) copy_kernel(const T* __restrict__ in, flo
     const int64_t bb = e / ((int64_t)K * J * L);
     const int64_t ts = rev ? L - 1 - t : t;
     const int64_t src = ((bb * L + ts) * (J / rep) + j / rep) * K + k;
-    float4 o;
-    o.x = to_f32(in[src]);
-    o.y = to_f32(in[src + 1]);
-    o.z = to_f32(in[src + 2]);
-    o.w = to_f32(in[src + 3]);
-    *reinterpret_cast<float4*>(out + e) = o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[e + r] = from_f32<O>(to_f32(in[src + r]));
 }
 
 // decay steps of the reversed scans: d'[b, tau, h] = dt[b, L - tau, h] for tau >= 1, 0 at tau = 0;
@@ -78,71 +74,69 @@ __global__ void __launch_bounds__(256) ones_kernel(float* __restrict__ dt_t, int
     dt_t[i] = pos < L ? 1.0f : 0.0f;
 }
 
-// per (b, t, h): dx, q_t = x^T G B = v_t . B_t, and d lambda_t = C_t . w_t - dt_t q_t
-template <class T>
-__global__ void __launch_bounds__(256) head_kernel(const T* __restrict__ dy, const T* __restrict__ x,
-                                                   const T* __restrict__ dt,
-                                                   const T* __restrict__ B, const T* __restrict__ C,
-                                                   const float* __restrict__ D, const float* __restrict__ u_r,
-                                                   const float* __restrict__ v_r, const float* __restrict__ w,
-                                                   T* __restrict__ dx, float* __restrict__ q, float* __restrict__ dlam,
-                                                   float* __restrict__ dxy, int64_t L, int H, int P, int N, int G,
-                                                   int64_t nitems) {
-    const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= nitems) return;
-    const int h = (int)(item % H);
-    const int64_t t = (item / H) % L;
-    const int64_t bb = item / ((int64_t)H * L);
-    const int g = h / (H / G);
-    const int64_t bt = bb * L + t, btr = bb * L + (L - 1 - t);
-    const float d = to_f32(dt[bt * H + h]);
-    const float Dh = D ? D[h] : 0.0f;
-    float sxy = 0.0f;
-    for (int p = lane; p < P; p += 64) {
-        const float u = u_r[(btr * H + h) * P + p];
-        const float gy = to_f32(dy[(bt * H + h) * P + p]);
-        dx[(bt * H + h) * P + p] = from_f32<T>(fmaf(d, u, Dh * gy));
-        sxy = fmaf(gy, to_f32(x[(bt * H + h) * P + p]), sxy);
-    }
-    float sq = 0.0f, sw = 0.0f;
-    for (int n = lane; n < N; n += 64) {
-        sq += v_r[(btr * H + h) * N + n] * to_f32(B[(bt * G + g) * N + n]);
-        sw += w[(bt * H + h) * N + n] * to_f32(C[(bt * G + g) * N + n]);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        sq += __shfl_xor(sq, off, 64);
-        sw += __shfl_xor(sw, off, 64);
-        sxy += __shfl_xor(sxy, off, 64);
-    }
-    if (lane == 0) {
-        q[(bb * H + h) * L + t] = sq;
-        dlam[(bb * H + h) * L + t] = sw - d * sq;
-        dxy[(bb * H + h) * L + t] = sxy;
-    }
-}
-
-// per (b, t, g, n): dB = sum over the group's heads of dt v, dC = sum of w
-template <class T>
-__global__ void __launch_bounds__(256) group_kernel(const T* __restrict__ dt, const float* __restrict__ v_r,
-                                                    const float* __restrict__ w, T* __restrict__ dB, T* __restrict__ dC,
-                                                    int64_t L, int H, int N, int G, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    const int nn = (int)(i % N);
-    const int g = (int)((i / N) % G);
-    const int64_t t = (i / ((int64_t)N * G)) % L;
-    const int64_t bb = i / ((int64_t)N * G * L);
+// One workgroup per (b, t), all heads: dx = dt u + D dy; per head q = v . B (= x^T G B), d lambda =
+// C . w - dt q and dy . x; per group dB = sum_h dt v and dC = sum_h w.  Each head's rows of u, v, w
+// are read by one wavefront (lanes over p and n); the group sums re-read them from cache.
+template <class T, class U>
+__global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, const T* __restrict__ x,
+                                                      const T* __restrict__ dt, const T* __restrict__ B,
+                                                      const T* __restrict__ C, const float* __restrict__ D,
+                                                      const U* __restrict__ u_r, const float* __restrict__ v_r,
+                                                      const float* __restrict__ w, T* __restrict__ dx,
+                                                      T* __restrict__ dB, T* __restrict__ dC, float* __restrict__ q,
+                                                      float* __restrict__ dlam, float* __restrict__ dxy, int64_t L,
+                                                      int H, int P, int N, int G) {
+    extern __shared__ float lds[];
+    float* sB = lds;           // [G][N]
+    float* sC = sB + G * N;    // [G][N]
+    float* sdt = sC + G * N;   // [H]
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t bt = blockIdx.x;  // b * L + t
+    const int64_t bb = bt / L, t = bt % L;
+    const int64_t btr = bb * L + (L - 1 - t);
     const int hpg = H / G;
-    const int64_t bt = bb * L + t, btr = bb * L + (L - 1 - t);
-    float sb = 0.0f, sc = 0.0f;
-    for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
-        sb = fmaf(to_f32(dt[bt * H + h]), v_r[(btr * H + h) * N + nn], sb);
-        sc += w[(bt * H + h) * N + nn];
+    for (int e = tid; e < G * N; e += 256) {
+        sB[e] = to_f32(B[bt * G * N + e]);
+        sC[e] = to_f32(C[bt * G * N + e]);
     }
-    dB[i] = from_f32<T>(sb);
-    dC[i] = from_f32<T>(sc);
+    for (int h = tid; h < H; h += 256) sdt[h] = to_f32(dt[bt * H + h]);
+    __syncthreads();
+    for (int h = wv; h < H; h += 4) {
+        const int g = h / hpg;
+        const float d = sdt[h], Dh = D ? D[h] : 0.0f;
+        float sxy = 0.0f, sq = 0.0f, sw = 0.0f;
+        for (int p = lane; p < P; p += 64) {
+            const int64_t o = (bt * H + h) * P + p;
+            const float gy = to_f32(dy[o]);
+            dx[o] = from_f32<T>(fmaf(d, to_f32(u_r[(btr * H + h) * P + p]), Dh * gy));
+            sxy = fmaf(gy, to_f32(x[o]), sxy);
+        }
+        for (int n = lane; n < N; n += 64) {
+            sq = fmaf(v_r[(btr * H + h) * N + n], sB[g * N + n], sq);
+            sw = fmaf(w[(bt * H + h) * N + n], sC[g * N + n], sw);
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            sq += __shfl_xor(sq, off, 64);
+            sw += __shfl_xor(sw, off, 64);
+            sxy += __shfl_xor(sxy, off, 64);
+        }
+        if (lane == 0) {
+            q[(bb * H + h) * L + t] = sq;
+            dlam[(bb * H + h) * L + t] = sw - d * sq;
+            dxy[(bb * H + h) * L + t] = sxy;
+        }
+    }
+    for (int e = tid; e < G * N; e += 256) {
+        const int g = e / N, n = e % N;
+        float sb = 0.0f, sc = 0.0f;
+        for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+            sb = fmaf(sdt[h], v_r[(btr * H + h) * N + n], sb);
+            sc += w[(bt * H + h) * N + n];
+        }
+        dB[bt * G * N + e] = from_f32<T>(sb);
+        dC[bt * G * N + e] = from_f32<T>(sc);
+    }
 }
 
 // per (b, h): the final-state term, suffix sums R_k = sum_{t>=k} d lambda_t (fp64), ddt, and the
@@ -252,18 +246,18 @@ __global__ void __launch_bounds__(256) dh0_kernel(const float* __restrict__ G0, 
 
 inline dim3 grid1(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
 
-template <class T>
-hipError_t copy(const void* in, float* out, int64_t b, int64_t L, int J, int K, int rep, bool rev, hipStream_t st) {
+template <class T, class O = float>
+hipError_t copy(const void* in, O* out, int64_t b, int64_t L, int J, int K, int rep, bool rev, hipStream_t st) {
     const int64_t n4 = b * L * J * (int64_t)K / 4;
     if (n4 == 0) return hipSuccess;
-    hipLaunchKernelGGL(copy_kernel<T>, grid1(n4), dim3(256), 0, st, static_cast<const T*>(in), out, b, L, J, K, rep,
+    hipLaunchKernelGGL((copy_kernel<T, O>), grid1(n4), dim3(256), 0, st, static_cast<const T*>(in), out, b, L, J, K, rep,
                        rev ? 1 : 0, n4);
     return hipGetLastError();
 }
 
 // one chunked scan (cumsum arrays given): chunk states, state pass from h0, chunk output
-hipError_t scan(const Shape& s, const float* xin, const float* Bin, const float* Cin, const float* dt_t,
-                const float* cs, float* states, const float* h0, float* fin, float* y, hipStream_t st) {
+hipError_t scan(const Shape& s, const void* xin, const void* Bin, const void* Cin, const float* dt_t,
+                const float* cs, float* states, const float* h0, float* fin, void* y, hipStream_t st) {
     hipError_t e = launch_chunk_state(s, xin, Bin, dt_t, cs, states, st);
     if (e != hipSuccess) return e;
     e = launch_state_passing(s, states, cs, h0, fin, st);
@@ -332,21 +326,38 @@ hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const voi
     hipLaunchKernelGGL(ones_kernel, grid1(b * H * s.nC * s.Q), dim3(256), 0, st, dt_t, L, (int)s.Q, s.nC,
                        b * H * s.nC * s.Q);
     BWD_CHECK(hipGetLastError());
-    BWD_CHECK(scan(sb, dyr, Cr, Br, dt_t, cs, states, dfinal, G0, u_r, st));
+    // (b) on the bf16 chunk kernels when the shape allows: only dx (bf16 accuracy) and the final
+    // adjoint (fp32, hi + lo split chunk states) come from it; the decay gradients use (c) and (d)
+    Shape s16 = s;
+    s16.io = 1;
+    const bool fastb = sizeof(T) == 2 && fast_chunk_supported(s16);
+    bf16 *dyr16 = reinterpret_cast<bf16*>(ws + f.dyr16), *Cr16 = reinterpret_cast<bf16*>(ws + f.Cr16);
+    bf16 *Br16 = reinterpret_cast<bf16*>(ws + f.Br16), *u16 = reinterpret_cast<bf16*>(ws + f.u16);
+    if (fastb) {
+        BWD_CHECK((copy<T, bf16>(dy, dyr16, b, L, H, P, 1, true, st)));
+        BWD_CHECK((copy<T, bf16>(C, Cr16, b, L, G, N, 1, true, st)));
+        BWD_CHECK((copy<T, bf16>(B, Br16, b, L, G, N, 1, true, st)));
+        BWD_CHECK(scan(s16, dyr16, Cr16, Br16, dt_t, cs, states, dfinal, G0, u16, st));
+    } else {
+        BWD_CHECK(scan(sb, dyr, Cr, Br, dt_t, cs, states, dfinal, G0, u_r, st));
+    }
     BWD_CHECK(scan(sT, Crh, dyr, xr, dt_t, cs, states, dfT, fscr, v_r, st));
     // forward transposed scan (d): decay and input step dt
     BWD_CHECK(launch_chunk_cumsum(sb, none, dfwd, A, dt_t, cs, st));
     BWD_CHECK(scan(sT, Bh, xf, dyf, dt_t, cs, states, h0 ? h0T : nullptr, finT, w, st));
 
     // combine
-    const int64_t nh = b * L * H;
-    hipLaunchKernelGGL(head_kernel<T>, dim3((unsigned)((nh + 3) / 4)), dim3(256), 0, st, static_cast<const T*>(dy),
-                       static_cast<const T*>(x), static_cast<const T*>(dt), static_cast<const T*>(B),
-                       static_cast<const T*>(C), D, u_r, v_r, w, static_cast<T*>(dx), q, dlam, dxy, L, H, P, N, G, nh);
-    BWD_CHECK(hipGetLastError());
-    const int64_t ng = b * L * G * (int64_t)N;
-    hipLaunchKernelGGL(group_kernel<T>, grid1(ng), dim3(256), 0, st, static_cast<const T*>(dt), v_r, w,
-                       static_cast<T*>(dB), static_cast<T*>(dC), L, H, N, G, ng);
+    const size_t clds = (size_t)(2 * G * N + H) * 4;
+    if (fastb)
+        hipLaunchKernelGGL((combine_kernel<T, bf16>), dim3((unsigned)(b * L)), dim3(256), clds, st,
+                           static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
+                           static_cast<const T*>(B), static_cast<const T*>(C), D, u16, v_r, w, static_cast<T*>(dx),
+                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, H, P, N, G);
+    else
+        hipLaunchKernelGGL((combine_kernel<T, float>), dim3((unsigned)(b * L)), dim3(256), clds, st,
+                           static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
+                           static_cast<const T*>(B), static_cast<const T*>(C), D, u_r, v_r, w, static_cast<T*>(dx),
+                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, H, P, N, G);
     BWD_CHECK(hipGetLastError());
     hipLaunchKernelGGL(suffix_kernel<T>, dim3((unsigned)H, (unsigned)b), dim3(256), 0, st, dlam, q, dxy,
                        static_cast<const T*>(dt), A, dfinal, finT, static_cast<T*>(ddt), dA_part, dD_part, L, H, P,
@@ -382,6 +393,7 @@ BackwardLayout backward_layout(const Shape& s) {
     f.Cr = take(BLGN), f.Br = take(BLGN), f.Crh = take(BLHN), f.Bh = take(BLHN);
     f.drev = take(BLH), f.dfwd = take(BLH), f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST);
     f.u_r = take(BLHP), f.v_r = take(BLHN), f.w = take(BLHN);
+    f.dyr16 = take(BLHP / 2), f.Cr16 = take(BLGN / 2), f.Br16 = take(BLGN / 2), f.u16 = take(BLHP / 2);
     f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS), f.fscr = take(HS);
     f.q = take(BLH), f.dlam = take(BLH), f.dxy = take(BLH), f.dA_part = take(BH8), f.dD_part = take(BH8);
     f.total = o;

@@ -81,8 +81,8 @@ hipError_t launch_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, in
 // Backward pass (backward.hip): three fp32 chunked scans on converted copies of the
 // inputs.  Byte offsets of the workspace pieces (all 256-byte aligned).
 struct BackwardLayout {
-    size_t xr, xf, dyr, dyf, Cr, Br, Crh, Bh, drev, dfwd, dt_t, cs, states, u_r, v_r, w, G0, dfT, h0T, finT, fscr,
-        q, dlam, dxy, dA_part, dD_part, total;
+    size_t xr, xf, dyr, dyf, Cr, Br, Crh, Bh, drev, dfwd, dt_t, cs, states, u_r, v_r, w, dyr16, Cr16, Br16, u16,
+        G0, dfT, h0T, finT, fscr, q, dlam, dxy, dA_part, dD_part, total;
 };
 BackwardLayout backward_layout(const Shape& s);
 hipError_t launch_backward(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
