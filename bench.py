@@ -47,6 +47,41 @@ SEL_OPS_PER_ELEMENT = 7
 METRIC = "SSD fwd tokens/s + % MFMA/HBM roofline (2.7B heads, L 1K–256K, N 64–512)"
 
 
+def backward_section(ssd, torch, dev, timed, args, cfg, x, dt, A, B, C, D, tokens):
+    """Time ssd_backward (every gradient) on the forward's workload; returns the bench object."""
+    b, L, H, P = x.shape
+    N, G = B.shape[3], B.shape[2]
+    tdt = x.dtype
+    gen = torch.Generator(device=dev).manual_seed(11)
+    gdy = torch.randn(x.shape, generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    gdf = torch.randn((b, H, P, N), generator=gen, device=dev, dtype=torch.float32)
+    bws = torch.empty(max(ssd.backward_workspace_bytes(x, B, 0), 1), dtype=torch.uint8, device=dev)
+
+    def bwd():
+        ssd.backward(x, dt, A, B, C, D, None, gdy, gdf, workspace=bws)
+
+    bwd_ms = timed(bwd, max(3, args.steps // 4))
+    bflop = BWD_FLOP_PER_TOKEN_HEAD_PN * P * N * tokens * H
+    btf = bflop / (bwd_ms / 1e3) / 1e12
+    out = {
+        "workload": f"{args.workload}: ssd_backward b={b} L={L} H={H} P={P} N={N} G={G} {cfg['dtype']} io, "
+                    f"every gradient (dx, ddt, dA, dB, dC, dD, dh0), final-state gradient given",
+        "ms_per_call": bwd_ms,
+        "tokens_per_s": tokens / (bwd_ms / 1e3),
+        "workspace_bytes": int(bws.numel()),
+        "roofline": {"kernel": "ssd_backward (whole call: three chunked scans, fp32 where the decay gradients "
+                               "need it, and the combine kernels)",
+                     "bound": "mfma", "achieved": btf, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": btf / PEAK_FP32_MFMA_TFLOPS,
+                     "flop_per_token_head": BWD_FLOP_PER_TOKEN_HEAD_PN * P * N},
+    }
+    log(f"backward: {bwd_ms:.3f} ms/call, {tokens / (bwd_ms / 1e3) / 1e6:.1f} M tok/s, {btf:.1f} TFLOP/s "
+        f"(recurrence-form count) against the fp32 MFMA peak")
+    del gdy, gdf, bws
+    torch.cuda.empty_cache()
+    return out
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -57,6 +92,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-selective", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only ssd_backward on the workload (kernel-trace profiling); prints its object")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle's timed sample (0 = all)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this many MiB (hardware-counter calibration)")
@@ -151,6 +188,23 @@ def main():
     x, dt, B, C = t(fi.x), t(fi.dt), t(fi.B), t(fi.C)
     A, D = t(fi.A, torch.float32), t(fi.D, torch.float32)
     log(f"inputs resident in HBM ({time.time() - t0:.1f}s)")
+    if args.backward_only:
+        stream0 = torch.cuda.current_stream(dev)
+
+        def timed0(fn, reps):
+            for _ in range(min(args.warmup, 3)):
+                fn()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream0)
+            for _ in range(reps):
+                fn()
+            ev1.record(stream0)
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / reps
+
+        print(json.dumps({"backward": backward_section(ssd, torch, dev, timed0, args, cfg, x, dt, A, B, C, D, b * L)}),
+              flush=True)
+        return
     if args.calib_copy:
         nbytes = args.calib_copy << 20
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -336,32 +390,7 @@ def main():
 
     # ---- backward pass on the same workload --------------------------------------------------------
     if not args.no_backward:
-        gen = torch.Generator(device=dev).manual_seed(11)
-        gdy = torch.randn(x.shape, generator=gen, device=dev, dtype=torch.float32).to(tdt)
-        gdf = torch.randn((b, H, P, N), generator=gen, device=dev, dtype=torch.float32)
-        bws = torch.empty(max(ssd.backward_workspace_bytes(x, B, 0), 1), dtype=torch.uint8, device=dev)
-
-        def bwd():
-            ssd.backward(x, dt, A, B, C, D, None, gdy, gdf, workspace=bws)
-
-        bwd_ms = timed(bwd, max(3, args.steps // 4))
-        bflop = BWD_FLOP_PER_TOKEN_HEAD_PN * P * N * tokens * H
-        btf = bflop / (bwd_ms / 1e3) / 1e12
-        result["backward"] = {
-            "workload": f"{args.workload}: ssd_backward b={b} L={L} H={H} P={P} N={N} G={G} {cfg['dtype']} io, "
-                        f"every gradient (dx, ddt, dA, dB, dC, dD, dh0), final-state gradient given",
-            "ms_per_call": bwd_ms,
-            "tokens_per_s": tokens / (bwd_ms / 1e3),
-            "workspace_bytes": int(bws.numel()),
-            "roofline": {"kernel": "ssd_backward (whole call: three fp32 chunked scans and the combine kernels)",
-                         "bound": "mfma", "achieved": btf, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                         "frac": btf / PEAK_FP32_MFMA_TFLOPS,
-                         "flop_per_token_head": BWD_FLOP_PER_TOKEN_HEAD_PN * P * N},
-        }
-        log(f"backward: {bwd_ms:.3f} ms/call, {tokens / (bwd_ms / 1e3) / 1e6:.1f} M tok/s, {btf:.1f} TFLOP/s "
-            f"(recurrence-form count) against the fp32 MFMA peak")
-        del gdy, gdf, bws
-        torch.cuda.empty_cache()
+        result["backward"] = backward_section(ssd, torch, dev, timed, args, cfg, x, dt, A, B, C, D, tokens)
 
     # ---- Mamba-1 selective scan on the same width ------------------------------------------------
     if not args.no_selective:
