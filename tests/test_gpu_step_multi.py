@@ -45,6 +45,21 @@ def test_step_multi_matches_oracle(gpu_ssd, case):
     assert_close_state(host(S), ref["final"])
 
 
+@pytest.mark.parametrize("mode", ["long_memory", "extreme", "per_head_bias", "zero"])
+def test_step_multi_dt_modes(gpu_ssd, mode):
+    """Tiny steps (long memory), huge steps (decay underflow within a block of steps), spread steps and
+    zero steps, against the oracle."""
+    b, K, H, P, N, G = 2, 40, 4, 64, 128, 1
+    a_mode = "minus_one" if mode == "long_memory" else "config"
+    fi = make_forward_inputs(b, K, H, P, N, G, "f32", 133, dt_mode=mode, a_mode=a_mode, h0_std=0.5)
+    ref = oracle.forward(fi.x, fi.dt, fi.A, fi.B, fi.C, fi.D, fi.h0)
+    S = dev(fi.h0)
+    y = gpu_ssd.step_multi(S, dev(fi.x), dev(fi.dt), dev(fi.A), dev(fi.B), dev(fi.C), dev(fi.D))
+    torch.cuda.synchronize()
+    assert_close_y(host(y), ref["y"], "f32")
+    assert_close_state(host(S), ref["final"])
+
+
 def test_step_multi_equals_single_steps(gpu_ssd):
     """One K-step call and K ssd_step calls on the slices [:, k] give the same state and outputs."""
     b, K, H, P, N, G = 2, 24, 4, 64, 128, 1
