@@ -488,7 +488,7 @@ static ssd_status check_backward(const ssd_dims* d, ssd::Shape* out) {
         return fail(SSD_ERR_UNSUPPORTED, "the backward stages B and C of all groups of a token in 64 KiB of LDS");
     int64_t Q = d->chunk;
     if (Q == 0) {
-        for (int64_t cand : {256, 128, 64})
+        for (int64_t cand : {128, 256, 64})  // 128: fewest in-chunk flops per chunk state (measured)
             if (backward_chunk_ok(s, cand)) {
                 Q = cand;
                 break;
