@@ -244,8 +244,8 @@ ssd_status ssd_step_multi_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, fl
  * whose fp32 tiles fit LDS.  Supported: dstate <= 256 besides the forward's
  * limits (SSD_ERR_UNSUPPORTED otherwise).  workspace:
  * ssd_backward_workspace_bytes(dims) bytes, 256-byte aligned (about
- * 4 (5 P + 4 N) bytes per token-head); no output may overlap an input,
- * another output or the workspace.
+ * (2 s + 4) P + 8 N + 4 P N / chunk bytes per token-head, s = the io element
+ * size); no output may overlap an input, another output or the workspace.
  */
 size_t ssd_backward_workspace_bytes(const ssd_dims* dims);
 ssd_status ssd_backward(const ssd_dims* dims, const void* x, const void* dt, const float* A,

@@ -16,8 +16,11 @@
 // differences: d lambda_t = C_t . w_t - dt_t x_t^T G_t B_t (+ <dfinal, S_L-1>
 // at the last token), then
 //   ddt_k = x_k^T G_k B_k + A sum_{t>=k} d lambda_t,  dA = sum_k dt_k sum_{t>=k} d lambda_t.
-// The scans run in fp32 (the generic chunk kernels with fp32 MFMA) on
-// converted, reversed or per-head copies of the inputs that this file builds.
+// The scans run in fp32 (the generic chunk kernels with fp32 MFMA); they read
+// the inputs in place in forward time, and time-reversed copies (in the input
+// dtype) that this file builds for the reversed scans.  The transposed scans'
+// x-role input is B or C of the head's group, read through the kernels' x-head
+// map rather than copied per head.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -265,6 +268,17 @@ hipError_t scan(const Shape& s, const void* xin, const void* Bin, const void* Ci
     return launch_chunk_scan(s, xin, Bin, Cin, dt_t, cs, states, nullptr, y, st);
 }
 
+// the same on the generic kernels with fp32 compute, inputs of dtype in_io, x-head map xrep
+hipError_t scan_in(const Shape& s, int in_io, int xrep, const void* xin, const void* Bin, const void* Cin,
+                   const float* dt_t, const float* cs, float* states, const float* h0, float* fin, void* y,
+                   hipStream_t st) {
+    hipError_t e = launch_chunk_state_in(s, in_io, xrep, xin, Bin, dt_t, cs, states, st);
+    if (e != hipSuccess) return e;
+    e = launch_state_passing(s, states, cs, h0, fin, st);
+    if (e != hipSuccess) return e;
+    return launch_chunk_scan_in(s, in_io, xrep, xin, Bin, Cin, dt_t, cs, states, nullptr, y, st);
+}
+
 template <class T>
 hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const void* dt, const float* A,
                const void* B, const void* C, const float* D, const float* h0, const void* dy, const float* dfinal,
@@ -272,12 +286,14 @@ hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const voi
     const int64_t b = s.b, L = s.L;
     const int H = (int)s.H, P = (int)s.P, N = (int)s.N, G = (int)s.G;
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-    float *xr = F(f.xr), *xf = F(f.xf), *dyr = F(f.dyr), *dyf = F(f.dyf), *Cr = F(f.Cr), *Br = F(f.Br);
-    float *Crh = F(f.Crh), *Bh = F(f.Bh), *drev = F(f.drev), *dfwd = F(f.dfwd), *dt_t = F(f.dt_t), *cs = F(f.cs);
+    T *xr = reinterpret_cast<T*>(ws + f.xr), *dyr = reinterpret_cast<T*>(ws + f.dyr);
+    T *Cr = reinterpret_cast<T*>(ws + f.Cr), *Br = reinterpret_cast<T*>(ws + f.Br);
+    float *drev = F(f.drev), *dfwd = F(f.dfwd), *dt_t = F(f.dt_t), *cs = F(f.cs);
     float *states = F(f.states), *u_r = F(f.u_r), *v_r = F(f.v_r), *w = F(f.w), *G0 = F(f.G0), *dfT = F(f.dfT);
     float *h0T = F(f.h0T), *finT = F(f.finT), *fscr = F(f.fscr), *q = F(f.q), *dlam = F(f.dlam), *dxy = F(f.dxy);
     double *dA_part = reinterpret_cast<double*>(ws + f.dA_part), *dD_part = reinterpret_cast<double*>(ws + f.dD_part);
     const int64_t PN = (int64_t)P * N;
+    const int io = sizeof(T) == 2 ? 1 : 0;
     hipError_t e;
 #define BWD_CHECK(expr)             \
     do {                            \
@@ -296,15 +312,11 @@ hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const voi
         }
         return hipSuccess;
     }
-    // converted, reversed and per-head copies
-    BWD_CHECK(copy<T>(x, xr, b, L, H, P, 1, true, st));
-    BWD_CHECK(copy<T>(x, xf, b, L, H, P, 1, false, st));
-    BWD_CHECK(copy<T>(dy, dyr, b, L, H, P, 1, true, st));
-    BWD_CHECK(copy<T>(dy, dyf, b, L, H, P, 1, false, st));
-    BWD_CHECK(copy<T>(C, Cr, b, L, G, N, 1, true, st));
-    BWD_CHECK(copy<T>(B, Br, b, L, G, N, 1, true, st));
-    BWD_CHECK(copy<T>(C, Crh, b, L, H, N, H / G, true, st));
-    BWD_CHECK(copy<T>(B, Bh, b, L, H, N, H / G, false, st));
+    // time-reversed copies for the reversed scans, in the input dtype
+    BWD_CHECK((copy<T, T>(x, xr, b, L, H, P, 1, true, st)));
+    BWD_CHECK((copy<T, T>(dy, dyr, b, L, H, P, 1, true, st)));
+    BWD_CHECK((copy<T, T>(C, Cr, b, L, G, N, 1, true, st)));
+    BWD_CHECK((copy<T, T>(B, Br, b, L, G, N, 1, true, st)));
     hipLaunchKernelGGL(steps_kernel<T>, grid1(b * L * H), dim3(256), 0, st, static_cast<const T*>(dt), drev, dfwd, L,
                        H, b * L * H);
     BWD_CHECK(hipGetLastError());
@@ -314,13 +326,14 @@ hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const voi
     BWD_CHECK(hipGetLastError());
 
     const DtFront none{nullptr, 0, 0, 0, 0.0f, 0.0f};
-    Shape sb = s;  // the adjoint scan: headdim P, dstate N, G groups, fp32
+    Shape sb = s;  // the adjoint scan: headdim P, dstate N, G groups, fp32 compute
     sb.io = 0;
-    Shape sT = s;  // the transposed scans: headdim N, dstate P, one group per head
+    Shape sT = s;  // the transposed scans: headdim N, dstate P, one group per head, fp32 compute
     sT.io = 0;
     sT.P = N;
     sT.N = P;
     sT.G = H;
+    const int hpg = H / G;  // the transposed scans' x-role (B or C) is shared by the heads of a group
     // reversed scans (b) and (c): decay steps d', input step 1
     BWD_CHECK(launch_chunk_cumsum(sb, none, drev, A, dt_t, cs, st));
     hipLaunchKernelGGL(ones_kernel, grid1(b * H * s.nC * s.Q), dim3(256), 0, st, dt_t, L, (int)s.Q, s.nC,
@@ -330,28 +343,24 @@ hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const voi
     // adjoint (fp32, hi + lo split chunk states) come from it; the decay gradients use (c) and (d)
     Shape s16 = s;
     s16.io = 1;
-    const bool fastb = sizeof(T) == 2 && fast_chunk_supported(s16);
-    bf16 *dyr16 = reinterpret_cast<bf16*>(ws + f.dyr16), *Cr16 = reinterpret_cast<bf16*>(ws + f.Cr16);
-    bf16 *Br16 = reinterpret_cast<bf16*>(ws + f.Br16), *u16 = reinterpret_cast<bf16*>(ws + f.u16);
-    if (fastb) {
-        BWD_CHECK((copy<T, bf16>(dy, dyr16, b, L, H, P, 1, true, st)));
-        BWD_CHECK((copy<T, bf16>(C, Cr16, b, L, G, N, 1, true, st)));
-        BWD_CHECK((copy<T, bf16>(B, Br16, b, L, G, N, 1, true, st)));
-        BWD_CHECK(scan(s16, dyr16, Cr16, Br16, dt_t, cs, states, dfinal, G0, u16, st));
-    } else {
-        BWD_CHECK(scan(sb, dyr, Cr, Br, dt_t, cs, states, dfinal, G0, u_r, st));
-    }
-    BWD_CHECK(scan(sT, Crh, dyr, xr, dt_t, cs, states, dfT, fscr, v_r, st));
-    // forward transposed scan (d): decay and input step dt
+    const bool fastb = io == 1 && fast_chunk_supported(s16);
+    if (fastb)
+        BWD_CHECK(scan(s16, dyr, Cr, Br, dt_t, cs, states, dfinal, G0, u_r, st));
+    else
+        BWD_CHECK(scan_in(sb, io, 1, dyr, Cr, Br, dt_t, cs, states, dfinal, G0, u_r, st));
+    // (c): x-role C of the head's group, B-role dy, read out through x (all reversed)
+    BWD_CHECK(scan_in(sT, io, hpg, Cr, dyr, xr, dt_t, cs, states, dfT, fscr, v_r, st));
+    // forward transposed scan (d): decay and input step dt; x-role B, B-role x, read out through dy
     BWD_CHECK(launch_chunk_cumsum(sb, none, dfwd, A, dt_t, cs, st));
-    BWD_CHECK(scan(sT, Bh, xf, dyf, dt_t, cs, states, h0 ? h0T : nullptr, finT, w, st));
+    BWD_CHECK(scan_in(sT, io, hpg, B, x, dy, dt_t, cs, states, h0 ? h0T : nullptr, finT, w, st));
 
     // combine
     const size_t clds = (size_t)(2 * G * N + H) * 4;
     if (fastb)
         hipLaunchKernelGGL((combine_kernel<T, bf16>), dim3((unsigned)(b * L)), dim3(256), clds, st,
                            static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
-                           static_cast<const T*>(B), static_cast<const T*>(C), D, u16, v_r, w, static_cast<T*>(dx),
+                           static_cast<const T*>(B), static_cast<const T*>(C), D, reinterpret_cast<const bf16*>(u_r),
+                           v_r, w, static_cast<T*>(dx),
                            static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, H, P, N, G);
     else
         hipLaunchKernelGGL((combine_kernel<T, float>), dim3((unsigned)(b * L)), dim3(256), clds, st,
@@ -379,8 +388,9 @@ hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const voi
 BackwardLayout backward_layout(const Shape& s) {
     auto a256 = [](size_t v) { return (v + 255) / 256 * 256; };
     BackwardLayout f{};
+    const size_t sz = s.io == 1 ? 2 : 4;  // the reversed copies keep the input dtype
     const size_t BLHP = (size_t)(s.b * s.L * s.H * s.P) * 4, BLHN = (size_t)(s.b * s.L * s.H * s.N) * 4;
-    const size_t BLGN = (size_t)(s.b * s.L * s.G * s.N) * 4, BLH = (size_t)(s.b * s.L * s.H) * 4;
+    const size_t BLGN = (size_t)(s.b * s.L * s.G * s.N), BLH = (size_t)(s.b * s.L * s.H) * 4;
     const size_t CS = (size_t)(s.b * s.H * s.nC * s.Q) * 4, ST = (size_t)(s.b * s.nC * s.H * s.P * s.N) * 4;
     const size_t HS = (size_t)(s.b * s.H * s.P * s.N) * 4, BH8 = (size_t)(s.b * s.H) * 8;
     size_t o = 0;
@@ -389,11 +399,9 @@ BackwardLayout backward_layout(const Shape& s) {
         o += a256(bytes);
         return at;
     };
-    f.xr = take(BLHP), f.xf = take(BLHP), f.dyr = take(BLHP), f.dyf = take(BLHP);
-    f.Cr = take(BLGN), f.Br = take(BLGN), f.Crh = take(BLHN), f.Bh = take(BLHN);
+    f.xr = take(BLHP / 4 * sz), f.dyr = take(BLHP / 4 * sz), f.Cr = take(BLGN * sz), f.Br = take(BLGN * sz);
     f.drev = take(BLH), f.dfwd = take(BLH), f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST);
     f.u_r = take(BLHP), f.v_r = take(BLHN), f.w = take(BLHN);
-    f.dyr16 = take(BLHP / 2), f.Cr16 = take(BLGN / 2), f.Br16 = take(BLGN / 2), f.u16 = take(BLHP / 2);
     f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS), f.fscr = take(HS);
     f.q = take(BLH), f.dlam = take(BLH), f.dxy = take(BLH), f.dA_part = take(BH8), f.dD_part = take(BH8);
     f.total = o;

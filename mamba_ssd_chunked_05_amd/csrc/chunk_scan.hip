@@ -15,7 +15,8 @@
 // Workgroup = 4 wavefronts for one (b, c, h).  The chunk is walked in 64-row
 // query blocks (one 16-row tile per wavefront) and 64-row key blocks up to the
 // diagonal; C, B and S are staged in LDS in 64-wide slices of N, so every N up
-// to 1024 fits.
+// to 1024 fits.  The inputs may be bf16 under fp32 compute (I), and heads may
+// share their x rows: head h reads x head h / xrep.
 #include <type_traits>
 
 #include "common.hpp"
@@ -37,8 +38,8 @@ static inline size_t sc_lds_bytes(int P, int Q) {
 }
 
 // Stage rows [r0, r0 + kScBlk) x cols [n0, n0 + ns) of a (b, L, G, N) tensor into LDS (zero padded).
-template <class T>
-__device__ __forceinline__ void stage_rows(T* dst, const T* __restrict__ src, int64_t b, int64_t L, int G, int g,
+template <class T, class I>
+__device__ __forceinline__ void stage_rows(T* dst, const I* __restrict__ src, int64_t b, int64_t L, int G, int g,
                                            int N, int64_t cq, int Q, int r0, int n0, int ns, int kpad, int tid) {
     const int n8n = kpad / 8;
     for (int task = tid; task < kScBlk * n8n; task += 256) {
@@ -52,14 +53,14 @@ __device__ __forceinline__ void stage_rows(T* dst, const T* __restrict__ src, in
     }
 }
 
-template <class T>
-__global__ void __launch_bounds__(256) chunk_scan_kernel(const T* __restrict__ x, const T* __restrict__ B,
-                                                         const T* __restrict__ C, const float* __restrict__ dt_t,
+template <class T, class I>
+__global__ void __launch_bounds__(256) chunk_scan_kernel(const I* __restrict__ x, const I* __restrict__ B,
+                                                         const I* __restrict__ C, const float* __restrict__ dt_t,
                                                          const float* __restrict__ cs,
                                                          const float* __restrict__ start,
                                                          const float* __restrict__ D, T* __restrict__ y, int64_t L,
                                                          int H, int P, int N, int G, int Q, int64_t nC,
-                                                         uint32_t nitems) {
+                                                         int xrep, uint32_t nitems) {
     extern __shared__ __align__(16) unsigned char smem[];
     float* lw = reinterpret_cast<float*>(smem);
     float* dw = lw + Q;
@@ -72,6 +73,7 @@ __global__ void __launch_bounds__(256) chunk_scan_kernel(const T* __restrict__ x
     const int64_t c = (item / H) % nC;
     const int64_t b = item / ((uint32_t)H * (uint32_t)nC);
     const int g = h / (H / G);
+    const int Hx = H / xrep, hx = h / xrep;  // x rows of this head
     const int64_t cq = c * Q;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
     const int tp = P / 16;
@@ -95,7 +97,7 @@ __global__ void __launch_bounds__(256) chunk_scan_kernel(const T* __restrict__ x
         for (int n0 = 0; n0 < N; n0 += kScNs) {
             const int ns = min(kScNs, N - n0), kpad = (ns + 31) / 32 * 32;
             __syncthreads();
-            stage_rows<T>(Cs, C, b, L, G, g, N, cq, Q, I0, n0, ns, kpad, tid);
+            stage_rows<T, I>(Cs, C, b, L, G, g, N, cq, Q, I0, n0, ns, kpad, tid);
             const int n8n = kpad / 8;
             for (int task = tid; task < P * n8n; task += 256) {
                 const int p = task / n8n, n8 = (task % n8n) * 8;
@@ -138,8 +140,8 @@ __global__ void __launch_bounds__(256) chunk_scan_kernel(const T* __restrict__ x
             for (int n0 = 0; n0 < N; n0 += kScNs) {
                 const int ns = min(kScNs, N - n0), kpad = (ns + 31) / 32 * 32;
                 __syncthreads();
-                stage_rows<T>(Cs, C, b, L, G, g, N, cq, Q, I0, n0, ns, kpad, tid);
-                stage_rows<T>(Bs, B, b, L, G, g, N, cq, Q, J0, n0, ns, kpad, tid);
+                stage_rows<T, I>(Cs, C, b, L, G, g, N, cq, Q, I0, n0, ns, kpad, tid);
+                stage_rows<T, I>(Bs, B, b, L, G, g, N, cq, Q, J0, n0, ns, kpad, tid);
                 __syncthreads();
                 if (act) {
                     for (int ks = 0; ks < kpad; ks += 32) {
@@ -162,7 +164,7 @@ __global__ void __launch_bounds__(256) chunk_scan_kernel(const T* __restrict__ x
                 const int j = J0 + jj;
                 const int64_t t = cq + j;
                 float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                if (j < Q && t < L) load8_f32(x + ((b * L + t) * H + h) * P + p8, v);
+                if (j < Q && t < L) load8_f32(x + ((b * L + t) * Hx + hx) * P + p8, v);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) Xs[(p8 + q) * kScRow + jj] = from_f32<T>(v[q]);
             }
@@ -203,12 +205,13 @@ __global__ void __launch_bounds__(256) chunk_scan_kernel(const T* __restrict__ x
                 const int64_t t = cq + i;
                 if (t < L) {
                     const int64_t row = ((b * L + t) * H + h) * (int64_t)P;
+                    const int64_t xrow = ((b * L + t) * Hx + hx) * (int64_t)P;
 #pragma unroll
                     for (int pt = 0; pt < kScMaxP; ++pt) {
                         if (pt < tp) {
                             const int p = pt * 16 + l16;
                             float v = yacc[pt][r];
-                            if (D) v += Dh * to_f32(x[row + p]);
+                            if (D) v += Dh * to_f32(x[xrow + p]);
                             y[row + p] = from_f32<T>(v);
                         }
                     }
@@ -222,26 +225,34 @@ size_t chunk_scan_lds_bytes(const Shape& s) {
     return s.io == 1 ? sc_lds_bytes<bf16>((int)s.P, (int)s.Q) : sc_lds_bytes<float>((int)s.P, (int)s.Q);
 }
 
-template <class T>
-static hipError_t launch_sc(const Shape& s, const void* x, const void* B, const void* C, const float* dt_t,
+template <class T, class I>
+static hipError_t launch_sc(const Shape& s, int xrep, const void* x, const void* B, const void* C, const float* dt_t,
                             const float* cs, const float* start, const float* D, void* y, hipStream_t st) {
     const uint32_t nitems = (uint32_t)(s.b * s.nC * s.H);
     if (nitems == 0) return hipSuccess;
     const size_t lds = sc_lds_bytes<T>((int)s.P, (int)s.Q);
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_scan_kernel<T>,
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_scan_kernel<T, I>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_scan_kernel<T>, dim3(nitems), dim3(256), lds, st, (const T*)x, (const T*)B,
-                       (const T*)C, dt_t, cs, start, D, (T*)y, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G,
-                       (int)s.Q, s.nC, nitems);
+    hipLaunchKernelGGL((chunk_scan_kernel<T, I>), dim3(nitems), dim3(256), lds, st, (const I*)x, (const I*)B,
+                       (const I*)C, dt_t, cs, start, D, (T*)y, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G,
+                       (int)s.Q, s.nC, xrep, nitems);
     return hipGetLastError();
+}
+
+hipError_t launch_chunk_scan_in(const Shape& s, int in_io, int xrep, const void* x, const void* B, const void* C,
+                                const float* dt_t, const float* cs, const float* start, const float* D, void* y,
+                                hipStream_t st) {
+    if (s.io == 1)
+        return in_io == 1 ? launch_sc<bf16, bf16>(s, xrep, x, B, C, dt_t, cs, start, D, y, st) : hipErrorInvalidValue;
+    return in_io == 1 ? launch_sc<float, bf16>(s, xrep, x, B, C, dt_t, cs, start, D, y, st)
+                      : launch_sc<float, float>(s, xrep, x, B, C, dt_t, cs, start, D, y, st);
 }
 
 hipError_t launch_chunk_scan(const Shape& s, const void* x, const void* B, const void* C, const float* dt_t,
                              const float* cs, const float* start, const float* D, void* y, hipStream_t st) {
     if (fast_chunk_supported(s)) return launch_chunk_scan_fast(s, x, B, C, dt_t, cs, start, D, y, st);
-    return s.io == 1 ? launch_sc<bf16>(s, x, B, C, dt_t, cs, start, D, y, st)
-                     : launch_sc<float>(s, x, B, C, dt_t, cs, start, D, y, st);
+    return launch_chunk_scan_in(s, s.io, 1, x, B, C, dt_t, cs, start, D, y, st);
 }
 
 }  // namespace ssd

@@ -11,8 +11,9 @@
 // LDS read along the token axis.  For bf16 inputs the scaled operand w_j x_j
 // is split into hi + lo bf16 parts and both are multiplied by the exact bf16
 // B: the chunk state then carries ~2^-17 relative error instead of the ~2^-9
-// of one bf16 rounding, which the final state needs.  fp32 inputs use fp32
-// MFMA (16x16x4) and need no split.
+// of one bf16 rounding, which the final state needs.  fp32 compute uses fp32
+// MFMA (16x16x4) and needs no split; its inputs may be fp32 or bf16 (I).
+// Heads may share their x rows: head h reads x head h / xrep (xrep = 1: its own).
 #include <type_traits>
 
 #include "common.hpp"
@@ -38,12 +39,12 @@ static inline size_t cs_lds_bytes(int P, int Q, int NB) {
     return w + (kSplit ? 2 : 1) * (size_t)P * kCsRow * sizeof(T) + (size_t)NB * kCsRow * sizeof(T);
 }
 
-template <class T>
-__global__ void __launch_bounds__(256) chunk_state_kernel(const T* __restrict__ x, const T* __restrict__ B,
+template <class T, class I>
+__global__ void __launch_bounds__(256) chunk_state_kernel(const I* __restrict__ x, const I* __restrict__ B,
                                                           const float* __restrict__ dt_t,
                                                           const float* __restrict__ cs, float* __restrict__ states,
                                                           int64_t L, int H, int P, int N, int G, int Q, int64_t nC,
-                                                          int NB, uint32_t nitems) {
+                                                          int NB, int xrep, uint32_t nitems) {
     constexpr bool kSplit = std::is_same<T, bf16>::value;
     extern __shared__ __align__(16) unsigned char smem[];
     float* w = reinterpret_cast<float*>(smem);
@@ -58,6 +59,7 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(const T* __restrict__ 
     const int64_t c = (item / ((uint32_t)H * nblocks)) % nC;
     const int64_t b = item / ((uint32_t)H * nblocks * (uint32_t)nC);
     const int g = h / (H / G);
+    const int Hx = H / xrep, hx = h / xrep;  // x rows of this head
     const int64_t cq = c * Q;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
@@ -82,7 +84,7 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(const T* __restrict__ 
             float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             const int64_t t = cq + j0 + jj;
             if (jj < klen && t < L) {
-                load8_f32(x + ((b * L + t) * H + h) * P + p8, v);
+                load8_f32(x + ((b * L + t) * Hx + hx) * P + p8, v);
                 const float wj = w[j0 + jj];
 #pragma unroll
                 for (int q = 0; q < 8; ++q) v[q] *= wj;
@@ -143,26 +145,32 @@ size_t chunk_state_lds_bytes(const Shape& s) {
     return s.io == 1 ? cs_lds_bytes<bf16>((int)s.P, (int)s.Q, NB) : cs_lds_bytes<float>((int)s.P, (int)s.Q, NB);
 }
 
-template <class T>
-static hipError_t launch_cs(const Shape& s, const void* x, const void* B, const float* dt_t, const float* cs,
+template <class T, class I>
+static hipError_t launch_cs(const Shape& s, int xrep, const void* x, const void* B, const float* dt_t, const float* cs,
                             float* states, hipStream_t st) {
     const int NB = cs_nblock((int)s.P, (int)s.N);
     const uint32_t nitems = (uint32_t)(s.b * s.nC * s.H * (s.N / NB));
     if (nitems == 0) return hipSuccess;
     const size_t lds = cs_lds_bytes<T>((int)s.P, (int)s.Q, NB);
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_kernel<T>,
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_kernel<T, I>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_state_kernel<T>, dim3(nitems), dim3(256), lds, st, (const T*)x, (const T*)B, dt_t, cs,
-                       states, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q, s.nC, NB, nitems);
+    hipLaunchKernelGGL((chunk_state_kernel<T, I>), dim3(nitems), dim3(256), lds, st, (const I*)x, (const I*)B, dt_t,
+                       cs, states, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q, s.nC, NB, xrep, nitems);
     return hipGetLastError();
+}
+
+hipError_t launch_chunk_state_in(const Shape& s, int in_io, int xrep, const void* x, const void* B,
+                                 const float* dt_t, const float* cs, float* states, hipStream_t st) {
+    if (s.io == 1) return in_io == 1 ? launch_cs<bf16, bf16>(s, xrep, x, B, dt_t, cs, states, st) : hipErrorInvalidValue;
+    return in_io == 1 ? launch_cs<float, bf16>(s, xrep, x, B, dt_t, cs, states, st)
+                      : launch_cs<float, float>(s, xrep, x, B, dt_t, cs, states, st);
 }
 
 hipError_t launch_chunk_state(const Shape& s, const void* x, const void* B, const float* dt_t, const float* cs,
                               float* states, hipStream_t st) {
     if (fast_chunk_supported(s)) return launch_chunk_state_fast(s, x, B, dt_t, cs, states, st);
-    return s.io == 1 ? launch_cs<bf16>(s, x, B, dt_t, cs, states, st)
-                     : launch_cs<float>(s, x, B, dt_t, cs, states, st);
+    return launch_chunk_state_in(s, s.io, 1, x, B, dt_t, cs, states, st);
 }
 
 }  // namespace ssd

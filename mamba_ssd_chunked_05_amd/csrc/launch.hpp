@@ -29,6 +29,13 @@ hipError_t launch_state_passing(const Shape& s, float* states, const float* cs, 
                                 float* final_state, hipStream_t st);
 hipError_t launch_chunk_scan(const Shape& s, const void* x, const void* B, const void* C, const float* dt_t,
                              const float* cs, const float* start, const float* D, void* y, hipStream_t st);
+// The generic chunk kernels alone, with inputs x, B, C in dtype in_io (0 fp32, 1 bf16; bf16
+// compute needs bf16 inputs), computing in s.io, and head h reading x head h / xrep.
+hipError_t launch_chunk_state_in(const Shape& s, int in_io, int xrep, const void* x, const void* B,
+                                 const float* dt_t, const float* cs, float* states, hipStream_t st);
+hipError_t launch_chunk_scan_in(const Shape& s, int in_io, int xrep, const void* x, const void* B, const void* C,
+                                const float* dt_t, const float* cs, const float* start, const float* D, void* y,
+                                hipStream_t st);
 hipError_t launch_step(const Shape& s, const DtFront& fe, float* state, const void* x, const void* dt, const float* A,
                        const void* B, const void* C, const float* D, void* y, hipStream_t st);
 // K = s.L decode steps over pre-staged (b, K, ...) inputs; the state stays on chip
@@ -81,8 +88,8 @@ hipError_t launch_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, in
 // Backward pass (backward.hip): three fp32 chunked scans on converted copies of the
 // inputs.  Byte offsets of the workspace pieces (all 256-byte aligned).
 struct BackwardLayout {
-    size_t xr, xf, dyr, dyf, Cr, Br, Crh, Bh, drev, dfwd, dt_t, cs, states, u_r, v_r, w, dyr16, Cr16, Br16, u16,
-        G0, dfT, h0T, finT, fscr, q, dlam, dxy, dA_part, dD_part, total;
+    size_t xr, dyr, Cr, Br, drev, dfwd, dt_t, cs, states, u_r, v_r, w, G0, dfT, h0T, finT, fscr, q, dlam, dxy,
+        dA_part, dD_part, total;
 };
 BackwardLayout backward_layout(const Shape& s);
 hipError_t launch_backward(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
