@@ -78,9 +78,12 @@ __global__ void __launch_bounds__(256) ones_kernel(float* __restrict__ dt_t, int
 }
 
 // One workgroup per (b, t), all heads: dx = dt u + D dy; per head q = v . B (= x^T G B), d lambda =
-// C . w - dt q and dy . x; per group dB = sum_h dt v and dC = sum_h w.  Each head's rows of u, v, w
-// are read by one wavefront (lanes over p and n); the group sums re-read them from cache.
-template <class T, class U>
+// C . w - dt q and dy . x; per group dB = sum_h dt v and dC = sum_h w.  Wavefront wv takes heads
+// wv, wv + 4, ... (lanes over p and n) and reads each element of u, v, w once: the group sums
+// accumulate in registers while the heads stay in one group (heads are grouped in contiguous
+// ranges, so a wavefront meets each group once) and are flushed to a per-wavefront LDS slice.
+// Without SLICES (LDS too small for them) the group sums re-read v and w in a second pass.
+template <class T, class U, bool SLICES>
 __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, const T* __restrict__ x,
                                                       const T* __restrict__ dt, const T* __restrict__ B,
                                                       const T* __restrict__ C, const float* __restrict__ D,
@@ -90,9 +93,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
                                                       float* __restrict__ dlam, float* __restrict__ dxy, int64_t L,
                                                       int H, int P, int N, int G) {
     extern __shared__ float lds[];
-    float* sB = lds;           // [G][N]
-    float* sC = sB + G * N;    // [G][N]
-    float* sdt = sC + G * N;   // [H]
+    float* sB = lds;                // [G][N]
+    float* sC = sB + G * N;         // [G][N]
+    float* sdt = sC + G * N;        // [H]
+    float* pB = sdt + H;            // [4][G][N] per-wavefront partial dB
+    float* pC = pB + 4 * G * N;     // [4][G][N] per-wavefront partial dC
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bt = blockIdx.x;  // b * L + t
     const int64_t bb = bt / L, t = bt % L;
@@ -102,10 +107,33 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
         sB[e] = to_f32(B[bt * G * N + e]);
         sC[e] = to_f32(C[bt * G * N + e]);
     }
+    if (SLICES)
+        for (int e = tid; e < 8 * G * N; e += 256) pB[e] = 0.0f;  // pB and pC
     for (int h = tid; h < H; h += 256) sdt[h] = to_f32(dt[bt * H + h]);
     __syncthreads();
+    constexpr int kMaxNL = 4;  // n = lane + 64 k, N <= 256
+    float ab[kMaxNL], ac[kMaxNL];
+#pragma unroll
+    for (int k = 0; k < kMaxNL; ++k) ab[k] = ac[k] = 0.0f;
+    int gcur = wv < H ? wv / hpg : 0;
+    auto flush = [&](int g) {
+        if (!SLICES) return;
+#pragma unroll
+        for (int k = 0; k < kMaxNL; ++k) {
+            const int n = lane + 64 * k;
+            if (n < N) {
+                pB[(wv * G + g) * N + n] = ab[k];
+                pC[(wv * G + g) * N + n] = ac[k];
+            }
+            ab[k] = ac[k] = 0.0f;
+        }
+    };
     for (int h = wv; h < H; h += 4) {
         const int g = h / hpg;
+        if (g != gcur) {
+            flush(gcur);
+            gcur = g;
+        }
         const float d = sdt[h], Dh = D ? D[h] : 0.0f;
         float sxy = 0.0f, sq = 0.0f, sw = 0.0f;
         for (int p = lane; p < P; p += 64) {
@@ -114,9 +142,18 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
             dx[o] = from_f32<T>(fmaf(d, to_f32(u_r[(btr * H + h) * P + p]), Dh * gy));
             sxy = fmaf(gy, to_f32(x[o]), sxy);
         }
-        for (int n = lane; n < N; n += 64) {
-            sq = fmaf(v_r[(btr * H + h) * N + n], sB[g * N + n], sq);
-            sw = fmaf(w[(bt * H + h) * N + n], sC[g * N + n], sw);
+#pragma unroll
+        for (int k = 0; k < kMaxNL; ++k) {
+            const int n = lane + 64 * k;
+            if (n < N) {
+                const float vv = v_r[(btr * H + h) * N + n], ww = w[(bt * H + h) * N + n];
+                sq = fmaf(vv, sB[g * N + n], sq);
+                sw = fmaf(ww, sC[g * N + n], sw);
+                if (SLICES) {
+                    ab[k] = fmaf(d, vv, ab[k]);
+                    ac[k] += ww;
+                }
+            }
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
@@ -130,16 +167,51 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
             dxy[(bb * H + h) * L + t] = sxy;
         }
     }
+    if (wv < H) flush(gcur);
+    __syncthreads();
     for (int e = tid; e < G * N; e += 256) {
-        const int g = e / N, n = e % N;
         float sb = 0.0f, sc = 0.0f;
-        for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
-            sb = fmaf(sdt[h], v_r[(btr * H + h) * N + n], sb);
-            sc += w[(bt * H + h) * N + n];
+        if (SLICES) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                sb += pB[k * G * N + e];
+                sc += pC[k * G * N + e];
+            }
+        } else {
+            const int g = e / N, n = e % N;
+            for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+                sb = fmaf(sdt[h], v_r[(btr * H + h) * N + n], sb);
+                sc += w[(bt * H + h) * N + n];
+            }
         }
         dB[bt * G * N + e] = from_f32<T>(sb);
         dC[bt * G * N + e] = from_f32<T>(sc);
     }
+}
+
+// the combine kernel with LDS slices for the group sums when they fit, else the two-pass form
+template <class T, class U>
+hipError_t launch_combine(const void* dy, const void* x, const void* dt, const void* B, const void* C,
+                          const float* D, const U* u_r, const float* v_r, const float* w, void* dx, void* dB,
+                          void* dC, float* q, float* dlam, float* dxy, int64_t b, int64_t L, int H, int P, int N,
+                          int G, hipStream_t st) {
+    const size_t base = (size_t)(2 * G * N + H) * 4, sliced = base + (size_t)8 * G * N * 4;
+    const bool slices = sliced <= 160 * 1024;
+    const size_t lds = slices ? sliced : base;
+    const void* fn = slices ? (const void*)combine_kernel<T, U, true> : (const void*)combine_kernel<T, U, false>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    if (slices)
+        hipLaunchKernelGGL((combine_kernel<T, U, true>), dim3((unsigned)(b * L)), dim3(256), lds, st,
+                           static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
+                           static_cast<const T*>(B), static_cast<const T*>(C), D, u_r, v_r, w, static_cast<T*>(dx),
+                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, H, P, N, G);
+    else
+        hipLaunchKernelGGL((combine_kernel<T, U, false>), dim3((unsigned)(b * L)), dim3(256), lds, st,
+                           static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
+                           static_cast<const T*>(B), static_cast<const T*>(C), D, u_r, v_r, w, static_cast<T*>(dx),
+                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, H, P, N, G);
+    return hipGetLastError();
 }
 
 // per (b, h): the final-state term, suffix sums R_k = sum_{t>=k} d lambda_t (fp64), ddt, and the
@@ -355,19 +427,12 @@ hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const voi
     BWD_CHECK(scan_in(sT, io, hpg, B, x, dy, dt_t, cs, states, h0 ? h0T : nullptr, finT, w, st));
 
     // combine
-    const size_t clds = (size_t)(2 * G * N + H) * 4;
     if (fastb)
-        hipLaunchKernelGGL((combine_kernel<T, bf16>), dim3((unsigned)(b * L)), dim3(256), clds, st,
-                           static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
-                           static_cast<const T*>(B), static_cast<const T*>(C), D, reinterpret_cast<const bf16*>(u_r),
-                           v_r, w, static_cast<T*>(dx),
-                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, H, P, N, G);
+        BWD_CHECK((launch_combine<T, bf16>(dy, x, dt, B, C, D, reinterpret_cast<const bf16*>(u_r), v_r, w, dx, dB, dC, q,
+                                           dlam, dxy, b, L, H, P, N, G, st)));
     else
-        hipLaunchKernelGGL((combine_kernel<T, float>), dim3((unsigned)(b * L)), dim3(256), clds, st,
-                           static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
-                           static_cast<const T*>(B), static_cast<const T*>(C), D, u_r, v_r, w, static_cast<T*>(dx),
-                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, H, P, N, G);
-    BWD_CHECK(hipGetLastError());
+        BWD_CHECK((launch_combine<T, float>(dy, x, dt, B, C, D, u_r, v_r, w, dx, dB, dC, q, dlam, dxy, b, L, H, P, N, G,
+                                            st)));
     hipLaunchKernelGGL(suffix_kernel<T>, dim3((unsigned)H, (unsigned)b), dim3(256), 0, st, dlam, q, dxy,
                        static_cast<const T*>(dt), A, dfinal, finT, static_cast<T*>(ddt), dA_part, dD_part, L, H, P,
                        N);

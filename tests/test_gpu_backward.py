@@ -27,6 +27,8 @@ CASES = [
     (2, 257, 6, 64, 64, 3, "bf16", 128, False),
     (1, 1, 2, 16, 32, 1, "f32", 0, True),
     (1, 1000, 2, 64, 128, 1, "f32", 256, True),
+    (1, 150, 4, 16, 32, 4, "f32", 64, True),      # one head per group
+    (1, 130, 16, 16, 256, 16, "bf16", 64, True),  # group sums too wide for the LDS slices: two-pass combine
 ]
 
 
