@@ -149,6 +149,21 @@ def _draw_dt(rng: np.random.Generator, shape, mode: str, nheads: int) -> np.ndar
         return np.exp(rng.uniform(math.log(1e-3), math.log(2.0), size=shape))
     if mode == "zero":
         return np.zeros(shape)
+    if mode == "bursts":
+        # the workload's steps with bursts of very large ones (0.5 to 2, 20 to 90 tokens long, at
+        # random offsets along the sequence axis), so that slowly and very quickly decaying stretches
+        # alternate within one sequence
+        dt = _draw_dt(rng, shape, "config", nheads)
+        L = shape[1]
+        flat = dt.reshape(shape[0], L, -1)
+        for bi in range(shape[0]):
+            for c in range(flat.shape[2]):
+                t = int(rng.integers(0, 64))
+                while t < L:
+                    n = int(rng.integers(20, 91))
+                    flat[bi, t:t + n, c] = rng.uniform(0.5, 2.0, size=min(n, L - t))
+                    t += n + int(rng.integers(30, 400))
+        return flat.reshape(shape)
     raise ValueError(f"unknown dt mode {mode!r}")
 
 

@@ -119,10 +119,11 @@ def test_forward(gpu_ssd, case):
     assert_close_state(fin, ref["final"])
 
 
-@pytest.mark.parametrize("mode", ["long_memory", "extreme", "per_head_bias", "zero"])
+@pytest.mark.parametrize("mode", ["long_memory", "extreme", "per_head_bias", "zero", "bursts"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_forward_stress(gpu_ssd, mode, dtype):
-    """Long memory (chunk passing matters), extreme decay (underflow), wide dt spread, dt = 0."""
+    """Long memory (chunk passing matters), extreme decay (underflow), wide dt spread, dt = 0, and bursts
+    of very large steps between ordinary ones (the chunk kernels switch their state-scale mode)."""
     a_mode = "minus_one" if mode == "long_memory" else "config"
     fi = make_forward_inputs(1, 1100, 4, 64, 128, 1, dtype, 105, dt_mode=mode, a_mode=a_mode, h0_std=0.5)
     ref = oracle.forward(fi.x, fi.dt, fi.A, fi.B, fi.C, fi.D, fi.h0)
@@ -236,6 +237,9 @@ FUSED = [
     (1, 1000, 4, 64, 256, 1, "long_memory"),
     (2, 333, 2, 64, 512, 2, "config"),
     (1, 3000, 2, 64, 512, 1, "extreme"),
+    (1, 6000, 4, 64, 128, 1, "bursts"),
+    (2, 2500, 2, 64, 64, 1, "bursts"),
+    (1, 3000, 2, 64, 256, 1, "bursts"),
 ]
 
 
