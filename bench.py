@@ -98,6 +98,9 @@ def parse():
     ap.add_argument("--backward-only", action="store_true",
                     help="time only ssd_backward on the workload (kernel-trace profiling); prints its object")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle's timed sample (0 = all)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time ssd_forward on every forward workload (tiny, 130M, 2.7B at 1K-64K, the long-context "
+                         "state-size grid) and print one JSON line with all of them; nothing else runs")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this many MiB (hardware-counter calibration)")
     return ap.parse_args()
@@ -105,6 +108,19 @@ def parse():
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cold_ms(torch, stream, fn, reps, flush):
+    """Median time of fn alone when the 256 MB Infinity Cache holds none of its data: a 512 MiB
+    buffer is written before every rep (outside the event pair)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (e0, e1) in enumerate(evs):
+        flush.fill_(float(i))
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
 
 
 def fwd_flops_per_token(H, P, N, G, Q):
@@ -158,6 +174,86 @@ def measured_traffic(kernel_sources, summary: str):
         return None
 
 
+def device_inputs(torch, dev, cfg, seed):
+    """The workload's inputs drawn on the device (the recipe of the synthetic inputs, in torch's
+    generator instead of NumPy's: the sweep times shapes far too large to draw on the host)."""
+    b, L, H, P, N, G = cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"], cfg["ngroups"]
+    tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    f32 = dict(device=dev, dtype=torch.float32, generator=gen)
+    x = torch.randn((b, L, H, P), **f32).to(tdt)
+    # dt log-uniform on [1e-3, 0.1], A = -exp(U(0, ln 16)), B, C ~ N(0, 1/N), D ~ N(0, 1)
+    dt = torch.exp(torch.empty((b, L, H), device=dev, dtype=torch.float32)
+                   .uniform_(math.log(1e-3), math.log(0.1), generator=gen)).to(tdt)
+    A = -torch.exp(torch.empty(H, device=dev, dtype=torch.float32).uniform_(0.0, math.log(16.0), generator=gen))
+    Bm = (torch.randn((b, L, G, N), **f32) / math.sqrt(N)).to(tdt)
+    Cm = (torch.randn((b, L, G, N), **f32) / math.sqrt(N)).to(tdt)
+    D = torch.randn(H, **f32)
+    return x, dt, A, Bm, Cm, D
+
+
+def sweep(args, torch, ssd, dev):
+    """ssd_forward on every forward workload, warm and cold, each with its roofline fraction."""
+    from synth import CONFIGS, seed_for
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    out = []
+    names = [n for n in CONFIGS if n != "cfg4"]
+    for name in names:
+        cfg = CONFIGS[name]
+        b, L, H, P, N, G = (cfg[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups"))
+        s_io = 2 if cfg["dtype"] == "bf16" else 4
+        x, dt, A, Bm, Cm, D = device_inputs(torch, dev, cfg, seed_for(name))
+        y = torch.empty_like(x)
+        fin = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(ssd.forward_workspace_bytes(x, Bm, 0), 1), dtype=torch.uint8, device=dev)
+
+        def fwd():
+            ssd.forward(x, dt, A, Bm, Cm, D, None, chunk=0, y=y, final_state=fin, workspace=ws)
+
+        for _ in range(10):
+            fwd()
+        torch.cuda.synchronize()
+        # enough reps for about half a second, at least 10
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reps = max(10, min(2000, int(500.0 / max(e0.elapsed_time(e1), 1e-3))))
+        e0.record(stream)
+        for _ in range(reps):
+            fwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        cold = cold_ms(torch, stream, fwd, 10, flush)
+        tokens = b * L
+        flop = fwd_flops_per_token(H, P, N, G, cfg["chunk"]) * tokens
+        nbytes = fwd_bytes_per_token(H, P, N, G, s_io) * tokens + b * H * P * N * 4
+        peak_flop = (PEAK_BF16_TFLOPS if s_io == 2 else PEAK_FP32_MFMA_TFLOPS) * 1e12
+        ceiling = min(peak_flop, flop / nbytes * PEAK_HBM_GBS * 1e9)  # flop/s the roofline allows
+        rate = flop / (ms / 1e3)
+        out.append({
+            "workload": name, "shape": dict(b=b, L=L, H=H, P=P, N=N, G=G, dtype=cfg["dtype"]),
+            "chunk": ssd.query_config(b, L, H, P, N, G, 0, x.dtype)["chunk"],
+            "ms": ms, "cold_ms": cold, "tokens_per_s": tokens / (ms / 1e3),
+            "tflops_algorithmic": rate / 1e12, "mfma_frac": rate / peak_flop,
+            "gbs_min_bytes": nbytes / (ms / 1e3) / 1e9, "hbm_frac": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "intensity_flop_per_byte": flop / nbytes,
+            "bound": "mfma" if ceiling >= peak_flop else "hbm",
+            "roofline_frac": rate / ceiling,
+        })
+        log(f"{name}: {ms:.3f} ms (cold {cold:.3f}), {tokens / (ms / 1e3) / 1e6:.1f} M tok/s, "
+            f"{rate / 1e12:.1f} TFLOP/s, roofline {rate / ceiling:.3f} ({out[-1]['bound']})")
+        del x, dt, A, Bm, Cm, D, y, fin, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": out, "method": "ssd_forward (chunk chosen by the library), inputs drawn on the "
+                      "device with the synthetic recipe; warm: mean over about 0.5 s of back-to-back calls; cold: "
+                      "median of 10 calls each after a 512 MiB cache-evicting write; FLOP at the workload's "
+                      "chunk of 256 (causal), bytes = x, y, dt, B, C once plus the final state"}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -176,6 +272,9 @@ def main():
         sys.exit(2)
     ssd.load()
     dev = torch.device("cuda:0")
+    if args.sweep:
+        sweep(args, torch, ssd, dev)
+        return
     cfg = CONFIGS[args.workload]
     b, L, H, P, N, G = cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"], cfg["ngroups"]
     tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
@@ -262,6 +361,13 @@ def main():
         return ev0.elapsed_time(ev1) / reps
 
     scan_ms = timed(lambda: ssd.chunk_scan(x, B, C, dt_t, cs, states, D, chunk=Q, y=ys), args.steps)
+    # the same calls with a cold Infinity Cache (a 512 MiB write before each rep)
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    cold = {"method": "a 512 MiB buffer written before every rep (evicts the 256 MB Infinity Cache); "
+                      "median over the reps, each rep timed alone with HIP events on the call's stream"}
+    cold["forward_ms"] = cold_ms(torch, stream, step, 10, flush)
+    cold["chunk_scan_ms"] = cold_ms(torch, stream, lambda: ssd.chunk_scan(x, B, C, dt_t, cs, states, D, chunk=Q,
+                                                                          y=ys), 10, flush)
     stage_ms = {
         "chunk_cumsum": timed(lambda: ssd.chunk_cumsum(dt, A, Q), args.steps),
         "chunk_state": timed(lambda: ssd.chunk_state(x, B, dt_t, cs, Q), args.steps),
@@ -274,6 +380,9 @@ def main():
     scan_gbs = scan_bytes / (scan_ms / 1e3) / 1e9
     log(f"stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
     log(f"chunk_scan alone: {scan_ms:.3f} ms/launch, {scan_gbs:.0f} GB/s algorithmic")
+    cold["forward_tokens_per_s"] = tokens / (cold["forward_ms"] / 1e3)
+    cold["chunk_scan_frac_hbm"] = scan_bytes / (cold["chunk_scan_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS
+    log(f"cold cache: forward {cold['forward_ms']:.3f} ms, chunk_scan {cold['chunk_scan_ms']:.3f} ms")
     del states, dt_t, cs, ys, scratch
     torch.cuda.empty_cache()
 
@@ -303,6 +412,7 @@ def main():
             "min_bytes_per_token": fwd_bytes_per_token(H, P, N, G, s_io),
         },
         "stage_ms": stage_ms,
+        "cold": cold,
         "roofline": {
             "kernel": "chunk_scan (ssd_chunk_scan at the forward's chunk size)",
             "bound": "hbm",
@@ -369,6 +479,16 @@ def main():
         torch.cuda.synchronize()
         multi_ms = e0.elapsed_time(e1) / reps
         multi_bytes = 2 * bb * hh * pp * nn * 4 + nst * (step_bytes - 2 * bb * hh * pp * nn * 4)
+        # one step with a cold Infinity Cache: the state streams from HBM
+        ic = [0]
+
+        def one_step():
+            i = ic[0] % nst
+            ic[0] += 1
+            ssd.step(S, sx[i], sdt[i], sA, sB[i], sC[i], sD, y=yo[i])
+
+        cold_step_ms = cold_ms(torch, stream, one_step, 32, flush)
+        cold_gbs = step_bytes / (cold_step_ms / 1e3) / 1e9
         multi_gbs = multi_bytes / (multi_ms / 1e3) / 1e9
         result["decode"] = {
             "workload": f"cfg4: ssd_step b={bb} H={hh} P={pp} N={nn} bf16 io, fp32 state, 64 steps",
@@ -376,7 +496,10 @@ def main():
             "tokens_per_s": bb / (step_ms / 1e3),
             "roofline": {"kernel": "step_kernel<bf16>", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": step_bytes},
-            "note": "the 168 MB state fits the 256 MB Infinity Cache, so back-to-back steps can exceed HBM rate",
+            "note": "the 168 MB state fits the 256 MB Infinity Cache, so back-to-back steps can exceed HBM rate; "
+                    "the cold object times single steps after a 512 MiB cache-evicting write",
+            "cold": {"us_per_step": cold_step_ms * 1e3, "achieved_gbs": cold_gbs,
+                     "frac": cold_gbs / PEAK_HBM_GBS},
             "graph_us_per_step": graph_ms * 1e3,
             "multi_step": {
                 "call": f"ssd_step_multi, {nst} pre-staged steps per call, state in registers across steps",
@@ -388,6 +511,7 @@ def main():
                              "algorithmic_bytes_per_launch": multi_bytes},
             },
         }
+        log(f"decode cold: {cold_step_ms * 1e3:.1f} us/step, {cold_gbs:.0f} GB/s algorithmic")
         log(f"decode: {step_ms * 1e3:.1f} us/step, {gbs:.0f} GB/s algorithmic; graph {graph_ms * 1e3:.1f} us/step; "
             f"multi-step {multi_ms * 1e3 / nst:.2f} us/step ({multi_gbs:.0f} GB/s algorithmic)")
 

@@ -112,17 +112,42 @@ __device__ __forceinline__ TileBase tile_base(const bf16* x, const bf16* B, cons
     return t;
 }
 
+__device__ __forceinline__ uint4 ldb16(const void* base, uint32_t off) {
+    return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
+}
+
 // Load one sub-chunk into registers; rows past L read as zero (last = index of the
 // last valid row, used when the sub-chunk is ragged).
 template <int N, int HPW, bool WITH_C>
 __device__ __forceinline__ void chunk_load(ChunkRegs<N, HPW, WITH_C>& rg, const ChunkAddr<N, HPW>& a,
                                            const TileBase& t, bool full, int last, int H, int G, int tid) {
     constexpr int RPI = BRows<N>::RPI;
+    const uint32_t HP_ = (uint32_t)(H * P), GN = (uint32_t)(G * N);
+    if (N >= 128 && full) {
+        // byte offsets from the scalar tile bases, made opaque per call: every load stays a scalar
+        // base plus one 32-bit vector offset instead of a 64-bit per-lane pointer that the compiler
+        // would carry (and spill) across the sub-chunk loop (measured: 1.2-1.5% faster at dstate
+        // 128, 2-3% slower at dstate 64, which keeps the element-offset form below)
+        uint32_t xo = a.xo * 2u, bo = a.bo * 2u, dto = a.dto * 4u;
+        asm volatile("" : "+v"(xo), "+v"(bo), "+v"(dto));
+        if (tid < 64 * HPW) {
+            rg.dt = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(t.dt) + dto);
+            rg.cs = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(t.cs) + dto);
+        }
+#pragma unroll
+        for (int k = 0; k < 2 * HPW; ++k) rg.x[k] = ldb16(t.x, xo + ((k & 1) * 32 * HP_ + (k >> 1) * P) * 2u);
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) rg.b[k] = ldb16(t.b, bo + k * RPI * GN * 2u);
+        if (WITH_C) {
+#pragma unroll
+            for (int k = 0; k < N / 32; ++k) rg.c[k] = ldb16(t.c, bo + k * RPI * GN * 2u);
+        }
+        return;
+    }
     if (tid < 64 * HPW) {  // dt_t and cs cover every position of the chunk (zero-padded past L)
         rg.dt = t.dt[a.dto];
         rg.cs = t.cs[a.dto];
     }
-    const uint32_t HP_ = (uint32_t)(H * P), GN = (uint32_t)(G * N);
     if (full) {
 #pragma unroll
         for (int k = 0; k < 2 * HPW; ++k) rg.x[k] = ld16(t.x + a.xo + ((k & 1) * 32 * HP_ + (k >> 1) * P));
@@ -207,94 +232,6 @@ __device__ __forceinline__ void chunk_store(bf16* xs, bf16* bsm, bf16* csm, floa
 }
 
 // ---------------------------------------------------------------------------
-// scaled carried state
-//
-// The chunk kernels carry the state as S = 2^k * St (k <= 0, one exponent per
-// head) instead of decaying it every sub-chunk.  With l_j the sub-chunk's
-// cumulative log2 decay and a = l_63 its total, the update
-//   S' = 2^a S + sum_j 2^(a - l_j) dt_j x_j (outer) B_j
-// is, in the scaled form (k' = k + a),
-//   St' = St + sum_j 2^(-l_j - k) dt_j x_j (outer) B_j,
-// and every output of the sub-chunk shares the factor 2^(l_i + k):
-//   y_i = 2^(l_i + k) [ C_i . St + sum_{j<=i} (C_i . B_j) 2^(-l_j - k) dt_j x_j
-//                       + 2^(-l_i - k) D x_i ],
-// so the in-chunk matrix needs one multiply per element and the state no
-// per-sub-chunk decay.  The weights 2^(-l_j - k) stay below 2^kScaleMax: when a
-// sub-chunk would pass it the state is renormalised first (St *= 2^k, k = 0),
-// and a sub-chunk that alone decays by more than 2^kScaleMax takes the direct
-// form (true decays, St = S afterwards).  The regrouping is exact (associativity,
-// "3.3 Hardware-Aware algorithms ...", section 4.1); only powers of two move.
-// ---------------------------------------------------------------------------
-constexpr float kScaleMax = 64.0f;
-enum ScaleMode { kScaled = 0, kRenorm = 1, kDirect = 2 };
-
-// Per head (wavefront hh, lane = token): the decay vectors of one sub-chunk for the
-// output kernel, the sub-chunk's scale mode and the state multiplier, and the advance
-// of k (kexp, held by the head's wavefront).
-//   lw[j]   = l_j + k_s   (k_s: the state's exponent while this sub-chunk is read)
-//   ww[j]   = 2^(-l_j - k_s) dt_j (scaled modes) or 2^(a - l_j) dt_j (direct)
-//   dfac[j] = D 2^(-l_j - k_s) (scaled modes) or D (direct): the diagonal skip term
-//   ec      = separable off-diagonal factors, written in the direct mode only
-//   smul    = 2^k before the sub-chunk (renormalise) or 2^(k + a) after it (direct)
-template <int HPW, bool FWD>
-__device__ __forceinline__ void scan_decay_store(float* lw, float* dtw, float* ww, float* dfac, float* ec,
-                                                 float* smul, int* mode, float dtv, float csv, float Dm,
-                                                 float& cs_prev, float& kexp, int tid) {
-    const int hh = tid >> 6, lane = tid & 63;
-    float incl;  // cumulative log2 decay inside the sub-chunk
-    if (FWD) {
-        incl = csv;
-    } else {
-        incl = csv - cs_prev;
-        cs_prev = __shfl(csv, 63, 64);
-    }
-    const float a = __shfl(incl, 63, 64);
-    const float k0 = kexp;
-    int md;
-    float ks, mul;
-    if (-a > kScaleMax) {
-        md = kDirect, ks = k0, mul = fast_exp2(k0 + a), kexp = 0.0f;
-    } else if (-a - k0 > kScaleMax) {
-        md = kRenorm, ks = 0.0f, mul = fast_exp2(k0), kexp = a;
-    } else {
-        md = kScaled, ks = k0, mul = 1.0f, kexp = k0 + a;
-    }
-    lw[hh * QS + lane] = incl + ks;
-    dtw[hh * QS + lane] = dtv;
-    if (md == kDirect) {
-        ww[hh * QS + lane] = fast_exp2(a - incl) * dtv;
-        dfac[hh * QS + lane] = Dm;
-        ec[(hh * 4) * QS + lane] = fast_exp2(incl - __shfl(incl, lane & ~15, 64));
-#pragma unroll
-        for (int it = 1; it < 4; ++it)
-            ec[(hh * 4 + it) * QS + lane] = fast_exp2(fminf(__shfl(incl, 16 * it, 64) - incl, 0.0f)) * dtv;
-    } else {
-        const float e = fast_exp2(-incl - ks);
-        ww[hh * QS + lane] = e * dtv;
-        dfac[hh * QS + lane] = e * Dm;
-    }
-    if (lane == 0) {
-        smul[hh] = mul;
-        mode[hh] = md;
-    }
-}
-
-// x, B and (optionally) C of one sub-chunk: registers -> LDS
-template <int N, int HPW, bool WITH_C>
-__device__ __forceinline__ void tiles_store(bf16* xs, bf16* bsm, bf16* csm, const ChunkRegs<N, HPW, WITH_C>& rg,
-                                            const ChunkAddr<N, HPW>& a) {
-    constexpr int RPI = BRows<N>::RPI, BS = Strides<N>::BS, CS = Strides<N>::CS;
-#pragma unroll
-    for (int k = 0; k < 2 * HPW; ++k)
-        *reinterpret_cast<uint4*>(xs + a.xl + (k >> 1) * QS * XS + (k & 1) * 32 * XS) = rg.x[k];
-#pragma unroll
-    for (int k = 0; k < N / 32; ++k) {
-        *reinterpret_cast<uint4*>(bsm + a.bl + k * RPI * BS) = rg.b[k];
-        if (WITH_C) *reinterpret_cast<uint4*>(csm + a.cl + k * RPI * CS) = rg.c[k];
-    }
-}
-
-// ---------------------------------------------------------------------------
 // fused output kernel
 // ---------------------------------------------------------------------------
 template <int N, int HPW>
@@ -303,13 +240,11 @@ struct ScanLds {
     bf16 bs[QS * Strides<N>::BS];   // B [j][n]
     bf16 cs[QS * Strides<N>::CS];   // C [i][n]
     bf16 mb[HPW * 16 * 256];        // decayed C.B^T tiles, fragment order [hh][jt*4+it][lane][4]
-    float lw[HPW * QS];             // in-chunk cumulative log2 decay plus the state's scale exponent
+    float lw[HPW * QS];             // in-chunk cumulative log2 decay
     float dtw[HPW * QS];            // dt
-    float ww[HPW * QS];             // weight of token j in the state update and the scaled in-chunk matrix
-    float dfac[HPW * QS];           // the skip term D on the in-chunk matrix's diagonal
-    float ec[HPW * 4 * QS];         // separable decay factors of the off-diagonal tiles (direct mode)
-    float smul[4];                  // state multiplier per head (scan_decay_store)
-    int mode[4];                    // scale mode per head
+    float ww[HPW * QS];             // 2^(l_63 - l_j) dt_j
+    float ec[HPW * 4 * QS];         // separable decay factors of the off-diagonal tiles (chunk_store)
+    float alpha[4];                 // 2^(l_63) per head
 };
 
 
@@ -332,15 +267,16 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     const int h0 = hp * HPW;
     const int g = h0 / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, held in a scalar register
-    // D of head (tid >> 6), read by the wavefront that forms that head's decay vectors
-    const float Dm = D && tid < 64 * HPW ? D[h0 + (tid >> 6)] : 0.0f;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, in a scalar register
+    float Dh[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) Dh[hh] = D ? D[h0 + hh] : 0.0f;
     const int64_t t0 = c * Q;
     const int64_t t_end = t0 + Q < L ? t0 + Q : L;
     const int nsub = (int)((t_end - t0 + QS - 1) / QS);
-    float cs_prev = 0.0f, kexp = 0.0f;
+    float cs_prev = 0.0f, tot = 0.0f;
 
-    // carried state per head (scaled by 2^kexp, see scan_decay_store), transposed: st[hh][nt] holds S[p = 16w + l16][n = 16nt + 4g4 + r]
+    // carried state per head, transposed: st[hh][nt] holds S[p = 16w + l16][n = 16nt + 4g4 + r]
     f32x4 st[HPW][NT];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -370,14 +306,9 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     for (int sc = 0; sc < nsub; ++sc) {
         const int64_t tbase = t0 + (int64_t)sc * QS;
         __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
-        tiles_store<N, HPW, true>(sm.xs, sm.bs, sm.cs, rg, ad);
-        if (tid < 64 * HPW)
-            scan_decay_store<HPW, FWD>(sm.lw, sm.dtw, sm.ww, sm.dfac, sm.ec, sm.smul, sm.mode, rg.dt, rg.cs, Dm,
-                                       cs_prev, kexp, tid);
+        chunk_store<N, HPW, true, FWD>(sm.xs, sm.bs, sm.cs, sm.lw, sm.dtw, sm.ww, sm.ec, sm.alpha, rg, ad, cs_prev,
+                                       tot, tid);
         __syncthreads();
-        int md[HPW];  // this sub-chunk's scale mode per head (wavefront-uniform)
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) md[hh] = __builtin_amdgcn_readfirstlane(sm.mode[hh]);
         if (sc + 1 < nsub) {
             const int64_t t1 = tbase + QS;
             chunk_load<N, HPW, true>(rg, ad, tile_base<true>(x, B, C, ds, dt0, b, L, H, G, N, h0, g, t1, sc + 1),
@@ -401,33 +332,19 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
                 f32x4 m;
-                // D_h joins the diagonal (as dfac), so X^T M also yields the skip term D x
-                if (md[hh] != kDirect) {
-                    // scaled modes: token j's weight 2^(-l_j - k) dt_j; the output's 2^(l_i + k) comes later
-                    const f32x4 wj = *reinterpret_cast<const f32x4*>(&sm.ww[hh * QS + j0]);
-                    if (jt == it) {  // diagonal tile: the upper triangle is selected to zero
-                        const float di = sm.dfac[hh * QS + i];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            m[r] = (j0 + r <= i ? gacc[r] * wj[r] : 0.0f) + (j0 + r == i ? di : 0.0f);
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) m[r] = gacc[r] * wj[r];
-                    }
-                } else if (jt == it) {
-                    // direct mode, diagonal tile: every operand is read and every product formed, then
-                    // the upper triangle is selected to zero (the exponent is capped at 0 so no lane
-                    // forms an infinity)
+                if (jt == it) {
+                    // diagonal tile: every operand is read and every product formed, then the upper
+                    // triangle is selected to zero (the exponent is capped at 0 so no lane forms an
+                    // infinity); D_h joins the diagonal, so X^T M also yields the skip term D x
                     const float li = sm.lw[hh * QS + i];
-                    const float di = sm.dfac[hh * QS + i];
                     const f32x4 lj = *reinterpret_cast<const f32x4*>(&sm.lw[hh * QS + j0]);
                     const f32x4 dj = *reinterpret_cast<const f32x4*>(&sm.dtw[hh * QS + j0]);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float v = gacc[r] * fast_exp2(fminf(li - lj[r], 0.0f)) * dj[r];
-                        m[r] = (j0 + r <= i ? v : 0.0f) + (j0 + r == i ? di : 0.0f);
+                        m[r] = (j0 + r <= i ? v : 0.0f) + (j0 + r == i ? Dh[hh] : 0.0f);
                     }
-                } else {  // direct mode, below the diagonal: the separable factors
+                } else {  // below the diagonal: the separable factors of chunk_store
                     const float er = sm.ec[(hh * 4) * QS + i];
                     const f32x4 ej = *reinterpret_cast<const f32x4*>(&sm.ec[(hh * 4 + it) * QS + j0]);
 #pragma unroll
@@ -438,19 +355,7 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
         }
         __syncthreads();
 
-        // ---- phase 2: Y^T[p-tile w] = 2^(l_i + k) (St C^T + X^T M)  (scaled modes), or
-        //      2^(l_i + k) (St C^T) + X^T M (direct mode); M carries D on its diagonal ----------------
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-            if (md[hh] == kRenorm) {
-                const float mul = sm.smul[hh];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) st[hh][nt][r] *= mul;
-                }
-            }
-        }
+        // ---- phase 2: Y^T[p-tile w] = 2^l_i (S C^T) + X^T M  (M carries D on its diagonal) -------
         bf16x8 sa[HPW][NK];
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
@@ -490,14 +395,11 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
                     mma(acc[hh], a, bo);
                 }
             }
-            float sc_i[HPW];
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
-                sc_i[hh] = fast_exp2(sm.lw[hh * QS + i]);
-                if (md[hh] == kDirect) {
+                const float sc_i = fast_exp2(sm.lw[hh * QS + i]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[hh][r] *= sc_i[hh];
-                }
+                for (int r = 0; r < 4; ++r) acc[hh][r] *= sc_i;
             }
 #pragma unroll
             for (int js = 0; js <= it / 2; ++js) {
@@ -510,35 +412,31 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
                     mma(acc[hh], xf[js][hh], bo);
                 }
             }
-#pragma unroll
-            for (int hh = 0; hh < HPW; ++hh) {
-                if (md[hh] != kDirect) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[hh][r] *= sc_i[hh];
-                }
-            }
             if (full || tbase + i < L) {
 #pragma unroll
                 for (int hh = 0; hh < HPW; ++hh) {
                     bf16x4 o;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(acc[hh][r]);
-                    *reinterpret_cast<bf16x4*>(y + ((b * L + tbase) * H + h0) * (int64_t)P +
-                                               (yo + (uint32_t)((16 * it * H + hh) * P))) = o;
+                    // 32-bit byte offset from a scalar base (dstate 128; see chunk_load)
+                    if (N >= 128)
+                        *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(y + ((b * L + tbase) * H + h0) * (int64_t)P) +
+                                                   (yo + (uint32_t)((16 * it * H + hh) * P)) * 2u) = o;
+                    else
+                        *reinterpret_cast<bf16x4*>(y + ((b * L + tbase) * H + h0) * (int64_t)P +
+                                                   (yo + (uint32_t)((16 * it * H + hh) * P))) = o;
                 }
             }
         }
 
-        // ---- phase 3: St <- St + B^T (w x)  (scaled modes), S <- 2^(k + a) St + B^T (w x) (direct) --
+        // ---- phase 3: S <- 2^(l_63) S + B^T (w x) ---------------------------------------------
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
-            if (md[hh] == kDirect) {
-                const float mul = sm.smul[hh];
+            const float alpha = sm.alpha[hh];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
+            for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) st[hh][nt][r] *= mul;
-                }
+                for (int r = 0; r < 4; ++r) st[hh][nt][r] *= alpha;
             }
         }
 #pragma unroll
@@ -601,7 +499,7 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     const int h0 = hp * HPW;
     const int g = h0 / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, held in a scalar register
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, in a scalar register
     const int64_t t0 = c * Q;
     const int64_t t_end = t0 + Q < L ? t0 + Q : L;
     const int nsub = (int)((t_end - t0 + QS - 1) / QS);
