@@ -53,3 +53,19 @@ def test_step_generator():
 def test_seeds_follow_the_rule():
     assert synth.seed_for("cfg0") == 0 and synth.seed_for("cfg4") == 4
     assert synth.seed_for("cfg3_256k_n512") == 3000 + 10 * 18 + 9
+
+
+def test_bursts_mode():
+    """Runs of very large steps (0.5 to 2) between the workload's log-uniform ones, per sequence."""
+    a = synth.make_forward_inputs(2, 3000, 3, 8, 8, 1, "f32", 9, dt_mode="bursts")
+    b = synth.make_forward_inputs(2, 3000, 3, 8, 8, 1, "f32", 9, dt_mode="bursts")
+    assert np.array_equal(a.dt, b.dt)
+    big = a.dt >= 0.5
+    assert a.dt.min() >= 1e-3 * (1 - 1e-6) and a.dt.max() <= 2.0
+    assert np.all((a.dt[~big] <= 0.1 * (1 + 1e-6)))
+    # every (batch row, head) sequence holds bursts, and bursts are runs (not isolated tokens)
+    assert big.any(axis=1).all()
+    frac = big.mean()
+    assert 0.05 < frac < 0.5
+    starts = big[:, 1:] & ~big[:, :-1]
+    assert big.sum() / max(starts.sum(), 1) >= 15
