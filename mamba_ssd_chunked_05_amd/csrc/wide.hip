@@ -13,8 +13,11 @@
 // accumulate across blocks in registers, and the state update of a block runs
 // right after that block's part of C . S has read the old state.
 //
-// One head per workgroup, four wavefronts; wavefront w carries the fp32 state
-// rows p = 16w .. 16w + 15 for all N columns in registers (N/4 values per lane).
+// One head per workgroup.  chunk_state_wide_kernel and chunk_scan_wide_kernel
+// (dstate 256) run four wavefronts; wavefront w carries the fp32 state rows
+// p = 16w .. 16w + 15 for all N columns in registers (N/4 values per lane).
+// chunk_scan_wide8_kernel (dstate 512) runs eight, each with one p-tile and
+// one half of the state columns.
 // Staging of the next block (or the next sub-chunk) runs one step ahead in
 // registers.  Layout and fragment conventions are those of fused.hip.
 #include "common.hpp"
@@ -92,22 +95,19 @@ __device__ __forceinline__ void wide_store_bc(bf16* bsb, bf16* csb, const WideRe
     }
 }
 
-// x to LDS and the decay vectors of the sub-chunk (wavefront 0); see chunk_store in fused.hip
+// the decay vectors of the sub-chunk (wavefront 0, lane = token); see chunk_store in fused.hip
 template <bool FWD>
-__device__ __forceinline__ void wide_store_x(bf16* xs, float* lw, float* dtw, float* ww, float* ec, float* alpha,
-                                             const WideRegs& rg, const WideAddr& a, float& cs_prev, float& tot,
-                                             int tid) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4*>(xs + (a.xr + 32 * k) * XS + a.xc) = rg.x[k];
-    if (tid < 64) {
+__device__ __forceinline__ void wide_decay_store(float* lw, float* dtw, float* ww, float* ec, float* alpha, float dtv,
+                                                 float csv, float& cs_prev, float& tot, int tid) {
+    {
         const int lane = tid;
-        const float d = rg.dt;
+        const float d = dtv;
         float incl;
         if (FWD) {
-            incl = rg.cs;
+            incl = csv;
         } else {
-            incl = rg.cs - cs_prev;
-            cs_prev = __shfl(rg.cs, 63, 64);
+            incl = csv - cs_prev;
+            cs_prev = __shfl(csv, 63, 64);
         }
         const float last = __shfl(incl, 63, 64);
         tot += last;
@@ -121,6 +121,16 @@ __device__ __forceinline__ void wide_store_x(bf16* xs, float* lw, float* dtw, fl
         }
         if (lane == 0) alpha[0] = fast_exp2(last);
     }
+}
+
+// x to LDS and the decay vectors of the sub-chunk (wavefront 0)
+template <bool FWD>
+__device__ __forceinline__ void wide_store_x(bf16* xs, float* lw, float* dtw, float* ww, float* ec, float* alpha,
+                                             const WideRegs& rg, const WideAddr& a, float& cs_prev, float& tot,
+                                             int tid) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4*>(xs + (a.xr + 32 * k) * XS + a.xc) = rg.x[k];
+    if (tid < 64) wide_decay_store<FWD>(lw, dtw, ww, ec, alpha, rg.dt, rg.cs, cs_prev, tot, tid);
 }
 
 __device__ __forceinline__ void wide_addr(WideAddr& a, int tid) {
@@ -338,6 +348,292 @@ chunk_scan_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
 }
 
 // ---------------------------------------------------------------------------
+// chunk output with the state split over n: eight wavefronts, wavefront w owns
+// p-tile w % 4 and state half w / 4 (columns (w / 4) N/2 ..).  Each pass stages
+// one 128-column block of B and C for each half, so every B and C fragment is
+// read only by the wavefronts of its half; the C.B^T tiles accumulate over both
+// blocks of every pass.  The two halves' partial outputs C.S are exchanged
+// through LDS at the end of the sub-chunk: half 0 finishes token tiles 0-1,
+// half 1 token tiles 2-3.  Half the state per wavefront lets dstate 512 run two
+// wavefronts per SIMD instead of one.
+// ---------------------------------------------------------------------------
+struct Wide8Lds {
+    bf16 xs[QS * XS];
+    bf16 bs[2][QS * WBS];  // per half: the pass's B block; reused for the partial-output exchange
+    bf16 cs[2][QS * WCS];
+    bf16 mb[16 * 256];
+    float lw[QS], dtw[QS], ww[QS];
+    float ec[4 * QS];
+    float alpha[4];
+};
+
+struct Wide8Regs {
+    uint4 x;
+    uint4 b[4];
+    uint4 c[4];
+    float dt, cs;
+};
+
+// x of the sub-chunk at tbase (row tid / 8, columns 8 (tid % 8)), and its dt and cs (threads < 64)
+__device__ __forceinline__ void wide8_load_x(Wide8Regs& rg, const WideSrc& s, int64_t tbase, int sub, int tid) {
+    const int last = (int)(s.L - 1 - tbase);
+    const bf16* xb = s.x + ((s.b * s.L + tbase) * s.H + s.h) * (int64_t)P;
+    rg.x = ld_row(xb, (int64_t)s.H * P, tid >> 3, last, (tid & 7) * 8);
+    if (tid < 64) {
+        rg.dt = s.ds.dt_t[s.dt0 + (int64_t)QS * sub + tid];
+        rg.cs = s.ds.cs[s.dt0 + (int64_t)QS * sub + tid];
+    }
+}
+
+// pass q's two blocks of B and C: half tid / 256 takes columns (tid / 256) N/2 + 128 q ..,
+// rows (tid % 256) / 16 + 16 k, columns 8 (tid % 16) of the block
+__device__ __forceinline__ void wide8_load_bc(Wide8Regs& rg, const WideSrc& s, int64_t tbase, int q, int tid) {
+    const int last = (int)(s.L - 1 - tbase);
+    const int half = tid >> 8, r0 = (tid & 255) >> 4, cc = (tid & 15) * 8;
+    const int64_t GN = (int64_t)s.G * s.N;
+    const int64_t off = ((s.b * s.L + tbase) * s.G + s.g) * (int64_t)s.N + half * (s.N / 2) + WB * q;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        rg.b[k] = ld_row(s.B + off, GN, r0 + 16 * k, last, cc);
+        rg.c[k] = ld_row(s.C + off, GN, r0 + 16 * k, last, cc);
+    }
+}
+
+__device__ __forceinline__ void wide8_store_bc(Wide8Lds& sm, const Wide8Regs& rg, int tid) {
+    const int half = tid >> 8, r0 = (tid & 255) >> 4, cc = (tid & 15) * 8;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        *reinterpret_cast<uint4*>(&sm.bs[half][(r0 + 16 * k) * WBS + cc]) = rg.b[k];
+        *reinterpret_cast<uint4*>(&sm.cs[half][(r0 + 16 * k) * WCS + cc]) = rg.c[k];
+    }
+}
+
+// token tiles IT0, IT0 + 1 of the output: add the other half's partial C.S, scale by 2^l_i, add X^T M, store
+template <int IT0>
+__device__ __forceinline__ void wide8_finish(f32x4* acc, const Wide8Lds& sm, const float* px, int partner, int pt,
+                                             int lane, int g4, int l16, bf16* yb, int64_t HP_, bool full,
+                                             int64_t rows_left) {
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+        const int it = IT0 + o;
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(&px[((partner * 2 + o) * 64 + lane) * 4]);
+        const int i = 16 * it + l16;
+        const float sc_i = fast_exp2(sm.lw[i]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[it][r] = (acc[it][r] + pv[r]) * sc_i;
+#pragma unroll
+        for (int js = 0; js <= it / 2; ++js) {
+            Frag<bf16> a, bo;
+            a.v = pack8(tr_read(sm.xs, 32 * js + 4 * g4, 16 * pt, XS, l16),
+                        tr_read(sm.xs, 32 * js + 16 + 4 * g4, 16 * pt, XS, l16));
+            bo.v = pack8(*reinterpret_cast<const bf16x4*>(&sm.mb[(((2 * js) * 4 + it) * 64 + lane) * 4]),
+                         *reinterpret_cast<const bf16x4*>(&sm.mb[(((2 * js + 1) * 4 + it) * 64 + lane) * 4]));
+            mma(acc[it], a, bo);
+        }
+        if (full || i < rows_left) {
+            bf16x4 ov;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ov[r] = static_cast<bf16>(acc[it][r]);
+            *reinterpret_cast<bf16x4*>(yb + (int64_t)i * HP_) = ov;
+        }
+    }
+}
+
+template <int N, bool FWD>
+__global__ void __launch_bounds__(512, 2)
+chunk_scan_wide8_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, const bf16* __restrict__ C,
+                        DtSrc ds, const float* __restrict__ start, const float* __restrict__ D,
+                        bf16* __restrict__ y, int64_t L, int H, int G, int Q, int64_t nC, uint32_t nitems) {
+    constexpr int NH = N / 2, NP = NH / WB, NTH = NH / 16;  // state half, passes, state tiles per wavefront
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Wide8Lds& sm = *reinterpret_cast<Wide8Lds*>(smem_raw);
+
+    const uint32_t item = xcd_remap(blockIdx.x, nitems);
+    const int h = (int)(item % (uint32_t)H);
+    const int64_t c = (item / (uint32_t)H) % (uint32_t)nC;
+    const int64_t b = item / ((uint32_t)H * (uint32_t)nC);
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+    const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pt = w8 & 3, nh = w8 >> 2;  // p-tile and state half of this wavefront
+    const float Dh = D ? D[h] : 0.0f;
+    const int64_t t0 = c * Q;
+    const int64_t t_end = t0 + Q < L ? t0 + Q : L;
+    const int nsub = (int)((t_end - t0 + QS - 1) / QS);
+    const int64_t nsubT = (L + QS - 1) / QS;
+    float cs_prev = 0.0f, tot = 0.0f;
+
+    // st[nt] holds S[p = 16 pt + l16][n = nh N/2 + 16 nt + 4 g4 + r]
+    f32x4 st[NTH];
+    {
+        const float* S0 = start + ((b * nC + c) * H + h) * (int64_t)P * N + (int64_t)(16 * pt + l16) * N + nh * NH +
+                          4 * g4;
+#pragma unroll
+        for (int nt = 0; nt < NTH; ++nt) st[nt] = *reinterpret_cast<const f32x4*>(S0 + 16 * nt);
+    }
+    if (tid < 256) {
+        sm.mb[(1 * 4 + 0) * 256 + tid] = static_cast<bf16>(0.0f);
+        sm.mb[(3 * 4 + 2) * 256 + tid] = static_cast<bf16>(0.0f);
+    }
+
+    WideSrc src;
+    src.x = x, src.B = B, src.C = C, src.ds = ds, src.b = b, src.L = L, src.H = H, src.G = G, src.N = N, src.h = h,
+    src.g = g;
+    src.dt0 = FWD ? ((b * H + h) * nsubT + c * (Q / QS)) * QS : ((b * H + h) * nC + c) * Q;
+    Wide8Regs rg;
+    wide8_load_x(rg, src, t0, 0, tid);
+    wide8_load_bc(rg, src, t0, 0, tid);
+    const int64_t HP_ = (int64_t)H * P;
+    const float* px = reinterpret_cast<const float*>(&sm.bs[0][0]);  // partial-output exchange area
+
+    for (int sc = 0; sc < nsub; ++sc) {
+        const int64_t tbase = t0 + (int64_t)sc * QS;
+        const bool more = sc + 1 < nsub;
+        __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
+        *reinterpret_cast<uint4*>(&sm.xs[(tid >> 3) * XS + (tid & 7) * 8]) = rg.x;
+        if (tid < 64) wide_decay_store<FWD>(sm.lw, sm.dtw, sm.ww, sm.ec, sm.alpha, rg.dt, rg.cs, cs_prev, tot, tid);
+        wide8_store_bc(sm, rg, tid);
+        __syncthreads();
+        if (more) wide8_load_x(rg, src, tbase + QS, sc + 1, tid);
+        if (NP > 1)
+            wide8_load_bc(rg, src, tbase, 1, tid);
+        else if (more)
+            wide8_load_bc(rg, src, tbase + QS, 0, tid);
+
+        Frag<bf16> xw[2];  // decay-scaled X^T fragments of p-tile pt
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            Frag<bf16> xf;
+            xf.v = pack8(tr_read(sm.xs, 32 * ks + 4 * g4, 16 * pt, XS, l16),
+                         tr_read(sm.xs, 32 * ks + 16 + 4 * g4, 16 * pt, XS, l16));
+            const float* wv = &sm.ww[32 * ks + 4 * g4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                xw[ks].v[r] = static_cast<bf16>(static_cast<float>(xf.v[r]) * wv[r]);
+                xw[ks].v[4 + r] = static_cast<bf16>(static_cast<float>(xf.v[4 + r]) * wv[16 + r]);
+            }
+        }
+        const float alpha = sm.alpha[0];
+        f32x4 acc[4], gacc[2];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        gacc[0] = gacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            if (q > 0) {
+                __syncthreads();  // every wavefront is done with the previous pass's blocks
+                wide8_store_bc(sm, rg, tid);
+                __syncthreads();
+                if (q + 1 < NP)
+                    wide8_load_bc(rg, src, tbase, q + 1, tid);
+                else if (more)
+                    wide8_load_bc(rg, src, tbase + QS, 0, tid);
+            }
+            // C.B^T tiles w8 and w8 + 8 (of the ten in the lower triangle) over both blocks
+#pragma unroll
+            for (int o = 0; o < 2; ++o) {
+                const int tt = w8 + 8 * o;
+                if (tt < 10) {
+                    const int it = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+                    const int jt = tt - it * (it + 1) / 2;
+#pragma unroll
+                    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+                        for (int ks = 0; ks < WB / 32; ++ks) {
+                            Frag<bf16> a, bo;
+                            frag_load8<bf16>(a, &sm.bs[hb][(16 * jt + l16) * WBS + 32 * ks + 8 * g4]);
+                            frag_load8<bf16>(bo, &sm.cs[hb][(16 * it + l16) * WCS + 32 * ks + 8 * g4]);
+                            mma(gacc[o], a, bo);
+                        }
+                    }
+                }
+            }
+            // partial S C^T over this wavefront's block, from the state before the update
+            const bf16* csb = sm.cs[nh];
+#pragma unroll
+            for (int ks = 0; ks < WB / 32; ++ks) {
+                Frag<bf16> sa;
+                sa.v = pack8(cvt4(st[q * (WB / 16) + 2 * ks]), cvt4(st[q * (WB / 16) + 2 * ks + 1]));
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const bf16* crow = &csb[(16 * it + l16) * WCS + 32 * ks];
+                    Frag<bf16> bo;
+                    bo.v = pack8(*reinterpret_cast<const bf16x4*>(crow + 4 * g4),
+                                 *reinterpret_cast<const bf16x4*>(crow + 16 + 4 * g4));
+                    mma(acc[it], sa, bo);
+                }
+            }
+            // S <- 2^(l_63) S + B^T (w x) on this block's columns
+#pragma unroll
+            for (int nt = 0; nt < WB / 16; ++nt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[q * (WB / 16) + nt][r] *= alpha;
+            }
+            const bf16* bsb = sm.bs[nh];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int nt = 0; nt < WB / 16; ++nt) {
+                    Frag<bf16> a;
+                    a.v = pack8(tr_read(bsb, 32 * ks + 4 * g4, 16 * nt, WBS, l16),
+                                tr_read(bsb, 32 * ks + 16 + 4 * g4, 16 * nt, WBS, l16));
+                    mma(st[q * (WB / 16) + nt], a, xw[ks]);
+                }
+            }
+        }
+        __syncthreads();  // the blocks are free: their space takes the partial outputs
+
+        // send the token tiles the other half finishes (half 0 finishes 0-1, half 1 finishes 2-3)
+        float* pxw = reinterpret_cast<float*>(&sm.bs[0][0]);
+        if (nh == 0) {
+            *reinterpret_cast<f32x4*>(&pxw[((w8 * 2 + 0) * 64 + lane) * 4]) = acc[2];
+            *reinterpret_cast<f32x4*>(&pxw[((w8 * 2 + 1) * 64 + lane) * 4]) = acc[3];
+        } else {
+            *reinterpret_cast<f32x4*>(&pxw[((w8 * 2 + 0) * 64 + lane) * 4]) = acc[0];
+            *reinterpret_cast<f32x4*>(&pxw[((w8 * 2 + 1) * 64 + lane) * 4]) = acc[1];
+        }
+        // decayed C.B^T tiles -> LDS (D_h on the diagonal, so X^T M also yields D x)
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+            const int tt = w8 + 8 * o;
+            if (tt < 10) {
+                const int it = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+                const int jt = tt - it * (it + 1) / 2;
+                const int i = 16 * it + l16, j0 = 16 * jt + 4 * g4;
+                f32x4 m;
+                if (jt == it) {
+                    const float li = sm.lw[i];
+                    const f32x4 lj = *reinterpret_cast<const f32x4*>(&sm.lw[j0]);
+                    const f32x4 dj = *reinterpret_cast<const f32x4*>(&sm.dtw[j0]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float v = gacc[o][r] * fast_exp2(fminf(li - lj[r], 0.0f)) * dj[r];
+                        m[r] = (j0 + r <= i ? v : 0.0f) + (j0 + r == i ? Dh : 0.0f);
+                    }
+                } else {
+                    const float er = sm.ec[i];
+                    const f32x4 ej = *reinterpret_cast<const f32x4*>(&sm.ec[it * QS + j0]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m[r] = gacc[o][r] * er * ej[r];
+                }
+                *reinterpret_cast<bf16x4*>(&sm.mb[((jt * 4 + it) * 64 + lane) * 4]) = cvt4(m);
+            }
+        }
+        __syncthreads();
+
+        // Y^T[p-tile pt] of the token tiles this half finishes
+        const bool full = tbase + QS <= L;
+        bf16* yb = y + ((b * L + tbase) * H + h) * (int64_t)P + 16 * pt + 4 * g4;
+        const int partner = w8 ^ 4;  // same p-tile, other half
+        if (nh == 0)
+            wide8_finish<0>(acc, sm, px, partner, pt, lane, g4, l16, yb, HP_, full, L - tbase);
+        else
+            wide8_finish<2>(acc, sm, px, partner, pt, lane, g4, l16, yb, HP_, full, L - tbase);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // chunk-local states (hi + lo split of the decay-scaled operand, as in fused.hip)
 // ---------------------------------------------------------------------------
 struct WideAggLds {
@@ -466,6 +762,18 @@ hipError_t launch_scan_wide(const Shape& s, const bf16* x, const bf16* B, const 
                             const float* start, const float* D, bf16* y, hipStream_t st) {
     const uint32_t nitems = (uint32_t)(s.b * s.nC * s.H);
     if (nitems == 0) return hipSuccess;
+    // dstate 512: the split-state kernel (two wavefronts per SIMD instead of one; measured 5.80 against
+    // 6.79 ms for the 256K-token forward).  dstate 256 keeps the four-wavefront kernel, which already
+    // runs two workgroups per CU (the split one measured 3.04 against 2.65 ms there).
+    if (N >= 512) {
+        const size_t lds8 = sizeof(Wide8Lds);
+        hipError_t e = hipFuncSetAttribute((const void*)chunk_scan_wide8_kernel<N, FWD>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds8);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((chunk_scan_wide8_kernel<N, FWD>), dim3(nitems), dim3(512), lds8, st, x, B, C, ds, start,
+                           D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+        return hipGetLastError();
+    }
     const size_t lds = sizeof(WideScanLds);
     hipError_t e = hipFuncSetAttribute((const void*)chunk_scan_wide_kernel<N, FWD>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
