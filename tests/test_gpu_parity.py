@@ -254,3 +254,29 @@ def test_forward_fused(gpu_ssd, case):
     y, fin = _run_forward(gpu_ssd, fi, 0)
     assert_close_y(y, ref["y"], "bf16")
     assert_close_state(fin, ref["final"])
+
+
+def test_forward_many_chunks(gpu_ssd):
+    """20000 tokens at the workload's decay rates: dozens of chunks, most of them attenuated far below
+    fp32 range by the sequence end; outputs and final state stay within the tolerances."""
+    fi = make_forward_inputs(1, 20000, 4, 64, 128, 1, "bf16", 131, h0_std=0.3)
+    cfg = gpu_ssd.query_config(1, 20000, 4, 64, 128, 1, 0, torch.bfloat16)
+    assert 20000 / cfg["chunk"] > 30
+    ref = oracle.forward(fi.x, fi.dt, fi.A, fi.B, fi.C, fi.D, fi.h0)
+    y, fin = _run_forward(gpu_ssd, fi, 0)
+    assert_close_y(y, ref["y"], "bf16")
+    assert_close_state(fin, ref["final"])
+
+
+def test_forward_final_state_made_of_old_chunks(gpu_ssd):
+    """x = 0 over the last 2000 tokens: the final state is only the older chunks' states, attenuated
+    by about 2^-62 (A = -1, log-uniform steps); it still meets its bound relative to its own size,
+    which any loss of precision in those older chunk states would break."""
+    fi = make_forward_inputs(1, 4096, 4, 64, 128, 1, "bf16", 132, a_mode="minus_one", h0_std=0.3)
+    fi.x[:, -2000:] = 0.0
+    decay_log2 = -(fi.dt[0, -2000:, :].astype(np.float64).sum(axis=0)) * np.log2(np.e)
+    assert np.all(decay_log2 < -40) and np.all(decay_log2 > -100)
+    ref = oracle.forward(fi.x, fi.dt, fi.A, fi.B, fi.C, fi.D, fi.h0)
+    y, fin = _run_forward(gpu_ssd, fi, 0)
+    assert_close_y(y, ref["y"], "bf16")
+    assert_close_state(fin, ref["final"])
