@@ -706,11 +706,30 @@ static int fast_hpw(const Shape& s) { return s.N <= 128 && (s.H / s.G) % 2 == 0 
 int fast_heads_per_wg(const Shape& s) { return fast_hpw(s); }
 
 int fast_forward_chunk(const Shape& s) {
-    // the largest chunk (<= 4096 tokens) that still gives enough (b, chunk, head-pair) work items
+    // the largest power of two (<= 4096 tokens) that still gives enough (b, chunk, head-pair) work items
     const int64_t items_per_token = s.b * s.H / fast_hpw(s);
-    int64_t q = 4096;
-    while (q > 256 && items_per_token * s.L / q < 1024) q /= 2;
-    return (int)q;
+    int64_t q0 = 4096;
+    while (q0 > 256 && items_per_token * s.L / q0 < 1024) q0 /= 2;
+    // dstate <= 128, enough work to fill the chip: refine over the multiples of 64 in [q0/2, 2 q0] by
+    // the workgroup rounds of the two chunk kernels (two resident per CU on the 256 CUs of gfx950).
+    // A round costs one chunk length of sub-chunk steps; a last round with at most one workgroup per
+    // CU runs about 1.6x faster per workgroup (measured); each chunk adds a state round trip through
+    // HBM, worth about 8 tokens.  At 2.7B/64K this picks 2624 (1000 workgroups, two full rounds)
+    // over 2048 (1280, two and a half rounds): 0.794 against 0.811 ms.
+    constexpr int64_t kSlots = 2 * 256;
+    constexpr double kLoneSpeed = 1.0 / 1.6, kChunkCost = 8.0;
+    if (s.N > 128 || items_per_token * ((s.L + q0 - 1) / q0) < kSlots) return (int)q0;
+    int64_t best = q0;
+    double best_cost = 0.0;
+    for (int64_t q = (q0 / 2 + 63) / 64 * 64; q <= 2 * q0 && q <= 4096; q += 64) {
+        if (q < 256) continue;
+        const int64_t nC = (s.L + q - 1) / q, items = items_per_token * nC;
+        const int64_t full = items / kSlots, rest = items % kSlots;
+        const double rounds = (double)full + (rest == 0 ? 0.0 : (rest <= kSlots / 2 ? kLoneSpeed : 1.0));
+        const double cost = rounds * (double)(q < s.L ? q : s.L) + kChunkCost * (double)nC;
+        if (best_cost == 0.0 || cost < best_cost) best_cost = cost, best = q;
+    }
+    return (int)best;
 }
 
 namespace fz {
