@@ -187,6 +187,23 @@ def test_workspace_and_config_are_host_only():
         ssd.query_config(1, 64, 4, 24, 128)
 
 
+@pytest.mark.parametrize("shape, chunk", [
+    ((1, 65536, 80, 64, 128), 2624),   # 2.7B, 64K: 1000 workgroups, two full rounds (2048 gave 2.5)
+    ((1, 4096, 80, 64, 128), 384),     # 2.7B, 4K
+    ((1, 16384, 80, 64, 128), 512),    # 2.7B, 16K: the power-of-two anchor stays
+    ((1, 1024, 80, 64, 128), 256),     # too little work to refine
+    ((4, 2048, 24, 64, 128), 256),     # 130M shape
+    ((1, 65536, 32, 64, 64), 2048),    # long-context grid, N = 64 and 128
+    ((1, 65536, 32, 64, 128), 2048),
+    ((1, 262144, 32, 64, 128), 4096),
+    ((1, 262144, 32, 64, 512), 4096),  # the wide kernels keep the anchor
+])
+def test_forward_chunk_rule(shape, chunk):
+    """The forward's chunk choice at the measured workloads (the values the sweep was taken at)."""
+    cfg = ssd.query_config(*shape)
+    assert cfg["chunk"] == chunk
+
+
 def test_product_never_imports_oracle():
     pkg = os.path.join(ROOT, "mamba_ssd_chunked_05_amd")
     for dirpath, _, files in os.walk(pkg):
