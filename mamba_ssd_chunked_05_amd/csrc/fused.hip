@@ -710,19 +710,23 @@ int fast_forward_chunk(const Shape& s) {
     const int64_t items_per_token = s.b * s.H / fast_hpw(s);
     int64_t q0 = 4096;
     while (q0 > 256 && items_per_token * s.L / q0 < 1024) q0 /= 2;
-    // dstate <= 128, enough work to fill the chip: refine over the multiples of 64 in [q0/2, 2 q0] by
+    // dstate <= 128: refine over the multiples of 64 in [q0/2, 2 q0] by
     // the workgroup rounds of the two chunk kernels (two resident per CU on the 256 CUs of gfx950).
     // A round costs one chunk length of sub-chunk steps; a last round with at most one workgroup per
     // CU runs about 1.6x faster per workgroup (measured); each chunk adds a state round trip through
     // HBM, worth about 8 tokens.  At 2.7B/64K this picks 2624 (1000 workgroups, two full rounds)
     // over 2048 (1280, two and a half rounds): 0.794 against 0.811 ms.
+    // Below one round of workgroups only smaller chunks are tried (more workgroups in flight): at
+    // 2.7B/1K this picks 192 over 256 (0.050 against 0.054 ms); below a quarter round the anchor stays.
     constexpr int64_t kSlots = 2 * 256;
     constexpr double kLoneSpeed = 1.0 / 1.6, kChunkCost = 8.0;
-    if (s.N > 128 || items_per_token * ((s.L + q0 - 1) / q0) < kSlots) return (int)q0;
+    const int64_t items0 = items_per_token * ((s.L + q0 - 1) / q0);
+    if (s.N > 128 || items0 < kSlots / 4) return (int)q0;
+    const int64_t qmax = items0 >= kSlots ? 2 * q0 : q0;
     int64_t best = q0;
     double best_cost = 0.0;
-    for (int64_t q = (q0 / 2 + 63) / 64 * 64; q <= 2 * q0 && q <= 4096; q += 64) {
-        if (q < 256) continue;
+    for (int64_t q = (q0 / 2 + 63) / 64 * 64; q <= qmax && q <= 4096; q += 64) {
+        if (q < 128) continue;
         const int64_t nC = (s.L + q - 1) / q, items = items_per_token * nC;
         const int64_t full = items / kSlots, rest = items % kSlots;
         const double rounds = (double)full + (rest == 0 ? 0.0 : (rest <= kSlots / 2 ? kLoneSpeed : 1.0));

@@ -191,7 +191,8 @@ def test_workspace_and_config_are_host_only():
     ((1, 65536, 80, 64, 128), 2624),   # 2.7B, 64K: 1000 workgroups, two full rounds (2048 gave 2.5)
     ((1, 4096, 80, 64, 128), 384),     # 2.7B, 4K
     ((1, 16384, 80, 64, 128), 512),    # 2.7B, 16K: the power-of-two anchor stays
-    ((1, 1024, 80, 64, 128), 256),     # too little work to refine
+    ((1, 1024, 80, 64, 128), 192),     # 2.7B, 1K: under one round, a smaller chunk (more workgroups)
+    ((1, 20000, 4, 64, 128), 256),     # few heads: the anchor
     ((4, 2048, 24, 64, 128), 256),     # 130M shape
     ((1, 65536, 32, 64, 64), 2048),    # long-context grid, N = 64 and 128
     ((1, 65536, 32, 64, 128), 2048),
