@@ -765,7 +765,7 @@ hipError_t launch_scan_wide(const Shape& s, const bf16* x, const bf16* B, const 
     // dstate 512: the split-state kernel (two wavefronts per SIMD instead of one; measured 5.80 against
     // 6.79 ms for the 256K-token forward).  dstate 256 keeps the four-wavefront kernel, which already
     // runs two workgroups per CU (the split one measured 3.04 against 2.65 ms there).
-    if (N >= 512) {
+    if constexpr (N >= 512) {
         const size_t lds8 = sizeof(Wide8Lds);
         hipError_t e = hipFuncSetAttribute((const void*)chunk_scan_wide8_kernel<N, FWD>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds8);
