@@ -335,11 +335,21 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms = elapsed * 1e3 / args.steps
+    # per-call spread, after the timed region: each call bracketed by its own HIP events
+    stream_f = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(30)]
+    for e0, e1 in evs:
+        e0.record(stream_f)
+        step()
+        e1.record(stream_f)
+    torch.cuda.synchronize()
+    per_call = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     tokens = b * L
     tok_s = tokens / (ms / 1e3)
     flops = fwd_flops_per_token(H, P, N, G, cfg["chunk"]) * tokens
     min_bytes = fwd_bytes_per_token(H, P, N, G, s_io) * tokens + b * H * P * N * 4
-    log(f"forward: {ms:.3f} ms/step, {tok_s / 1e6:.1f} M tok/s, {flops / (ms / 1e3) / 1e12:.1f} TFLOP/s algorithmic")
+    log(f"forward: {ms:.3f} ms/step, {tok_s / 1e6:.1f} M tok/s, {flops / (ms / 1e3) / 1e12:.1f} TFLOP/s algorithmic; "
+        f"per call median {per_call[len(per_call) // 2]:.3f}, min {per_call[0]:.3f} ms")
 
     # ---- the forward's stages, each timed alone on the stream it runs on ----------------------
     # ssd_forward is exactly these four calls at chunk Q; the chunk scan dominates.
@@ -411,6 +421,8 @@ def main():
             "flop_per_token": fwd_flops_per_token(H, P, N, G, cfg["chunk"]),
             "min_bytes_per_token": fwd_bytes_per_token(H, P, N, G, s_io),
         },
+        "forward_ms_per_call": {"median": per_call[len(per_call) // 2], "min": per_call[0], "max": per_call[-1],
+                                "calls": len(per_call)},
         "stage_ms": stage_ms,
         "cold": cold,
         "roofline": {
