@@ -140,7 +140,7 @@ def test_forward_without_D_and_h0(gpu_ssd):
     assert_close_state(fin, ref["final"])
 
 
-@pytest.mark.parametrize("Q", [64, 128, 256, 512, 0])
+@pytest.mark.parametrize("Q", [64, 128, 192, 256, 512, 2624, 0])
 def test_forward_chunk_independent(gpu_ssd, Q):
     """The result does not depend on the chunk size (Q = 0: the library's choice)."""
     fi = make_forward_inputs(1, 1500, 4, 64, 128, 1, "bf16", 107, dt_mode="long_memory", a_mode="minus_one",
@@ -278,5 +278,17 @@ def test_forward_final_state_made_of_old_chunks(gpu_ssd):
     assert np.all(decay_log2 < -40) and np.all(decay_log2 > -100)
     ref = oracle.forward(fi.x, fi.dt, fi.A, fi.B, fi.C, fi.D, fi.h0)
     y, fin = _run_forward(gpu_ssd, fi, 0)
+    assert_close_y(y, ref["y"], "bf16")
+    assert_close_state(fin, ref["final"])
+
+
+@pytest.mark.parametrize("Q", [192, 2624])
+def test_forward_non_power_of_two_chunks(gpu_ssd, Q):
+    """Chunk sizes the library's rule picks (multiples of 64 that are not powers of two) over several
+    chunks and a ragged tail (6000 = 2 x 2624 + 752), with long memory so the state pass matters."""
+    fi = make_forward_inputs(1, 6000, 4, 64, 128, 1, "bf16", 133, dt_mode="long_memory", a_mode="minus_one",
+                             h0_std=0.2)
+    ref = oracle.forward(fi.x, fi.dt, fi.A, fi.B, fi.C, fi.D, fi.h0)
+    y, fin = _run_forward(gpu_ssd, fi, Q)
     assert_close_y(y, ref["y"], "bf16")
     assert_close_state(fin, ref["final"])
