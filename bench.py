@@ -45,6 +45,8 @@ PEAK_VALU_GOPS = 256 * 4 * 16 * 2.4
 # lane operations of one selective-scan element update (token, channel, state entry) in its
 # cheapest form: delta*A, exp2, B*x, add, fma (state), C/A scale, fma (output)
 SEL_OPS_PER_ELEMENT = 7
+# fp32 lane operations per state element and decode step: decay multiply, input fma, output fma
+STEP_OPS = 3
 METRIC = "SSD fwd tokens/s + % MFMA/HBM roofline (2.7B heads, L 1K–256K, N 64–512)"
 
 
@@ -106,6 +108,18 @@ def parse():
     return ap.parse_args()
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu's "Model name", read from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -133,12 +147,6 @@ def fwd_bytes_per_token(H, P, N, G, s_io):
     return H * (P * 2 * s_io + s_io) + 2 * G * N * s_io
 
 
-def scan_bytes_per_token(H, P, N, G, Q, s_io):
-    """Algorithmic bytes of one chunk-scan launch per token: x, y, B, C, the two fp32 chunk vectors
-    and the fp32 chunk-start state (P*N*4 per chunk and head)."""
-    return H * (P * 2 * s_io + 8 + P * N * 4 / Q) + 2 * G * N * s_io
-
-
 def kernel_sources_sha(paths) -> str:
     """sha256 over the concatenated kernel sources (the .hip file and the headers it includes)."""
     import hashlib
@@ -150,7 +158,11 @@ def kernel_sources_sha(paths) -> str:
     return h.hexdigest()
 
 
-SCAN_SOURCES = [os.path.join(ROOT, "mamba_ssd_chunked_05_amd", "csrc", f) for f in ("fused.hip", "tiles.hpp", "common.hpp")]
+# the kernels one ssd_forward call launches at dstate <= 128, in order
+FWD_LAUNCHES = ["subchunk_decay_kernel", "chunk_state_fast_kernel", "state_passing_kernel", "chunk_scan_fast_kernel"]
+# the sources of every kernel the forward launches at the 2.7B shape (dstate 128)
+FWD_SOURCES = [os.path.join(ROOT, "mamba_ssd_chunked_05_amd", "csrc", f)
+               for f in ("fused.hip", "state_passing.hip", "tiles.hpp", "common.hpp")]
 
 
 def measured_traffic(kernel_sources, summary: str):
@@ -326,17 +338,21 @@ def main():
     def step():
         ssd.forward(x, dt, A, B, C, D, None, chunk=0, y=y, final_state=fin, workspace=ws)
 
+    stream_f = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
+    ev_a.record(stream_f)  # the forward's kernels all run on this stream
     for _ in range(args.steps):
         step()
+    ev_b.record(stream_f)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms = elapsed * 1e3 / args.steps
+    ev_ms = ev_a.elapsed_time(ev_b) / args.steps  # HIP events over the timed region, per forward
     # per-call spread, after the timed region: each call bracketed by its own HIP events
-    stream_f = torch.cuda.current_stream(dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(30)]
     for e0, e1 in evs:
         e0.record(stream_f)
@@ -371,13 +387,11 @@ def main():
         return ev0.elapsed_time(ev1) / reps
 
     scan_ms = timed(lambda: ssd.chunk_scan(x, B, C, dt_t, cs, states, D, chunk=Q, y=ys), args.steps)
-    # the same calls with a cold Infinity Cache (a 512 MiB write before each rep)
+    # the forward with a cold Infinity Cache (a 512 MiB write before each rep)
     flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
     cold = {"method": "a 512 MiB buffer written before every rep (evicts the 256 MB Infinity Cache); "
                       "median over the reps, each rep timed alone with HIP events on the call's stream"}
     cold["forward_ms"] = cold_ms(torch, stream, step, 10, flush)
-    cold["chunk_scan_ms"] = cold_ms(torch, stream, lambda: ssd.chunk_scan(x, B, C, dt_t, cs, states, D, chunk=Q,
-                                                                          y=ys), 10, flush)
     stage_ms = {
         "chunk_cumsum": timed(lambda: ssd.chunk_cumsum(dt, A, Q), args.steps),
         "chunk_state": timed(lambda: ssd.chunk_state(x, B, dt_t, cs, Q), args.steps),
@@ -386,13 +400,10 @@ def main():
     scratch = states.clone()
     stage_ms["state_passing"] = timed(lambda: ssd.state_passing(scratch, cs, None, seqlen=L, chunk=Q, io=tdt),
                                       args.steps)
-    scan_bytes = scan_bytes_per_token(H, P, N, G, Q, s_io) * tokens
-    scan_gbs = scan_bytes / (scan_ms / 1e3) / 1e9
-    log(f"stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
-    log(f"chunk_scan alone: {scan_ms:.3f} ms/launch, {scan_gbs:.0f} GB/s algorithmic")
+    log(f"staged calls at the forward's chunk, each alone (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
     cold["forward_tokens_per_s"] = tokens / (cold["forward_ms"] / 1e3)
-    cold["chunk_scan_frac_hbm"] = scan_bytes / (cold["chunk_scan_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS
-    log(f"cold cache: forward {cold['forward_ms']:.3f} ms, chunk_scan {cold['chunk_scan_ms']:.3f} ms")
+    cold["forward_hbm_frac_min_bytes"] = min_bytes / (cold["forward_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS
+    log(f"cold cache: forward {cold['forward_ms']:.3f} ms")
     del states, dt_t, cs, ys, scratch
     torch.cuda.empty_cache()
 
@@ -426,16 +437,20 @@ def main():
         "stage_ms": stage_ms,
         "cold": cold,
         "roofline": {
-            "kernel": "chunk_scan (ssd_chunk_scan at the forward's chunk size)",
+            "kernel": "ssd_forward (the whole call)",
+            "launches": FWD_LAUNCHES,
             "bound": "hbm",
-            "achieved": scan_gbs,
+            "achieved": min_bytes / (ev_ms / 1e3) / 1e9,
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": scan_gbs / PEAK_HBM_GBS,
-            "traffic": measured_traffic(SCAN_SOURCES,
-                                        os.path.join(ROOT, "profiles", f"chunk_scan_{args.workload}_traffic.txt")),
-            "avg_launch_ms": scan_ms,
-            "algorithmic_bytes_per_launch": scan_bytes,
+            "frac": min_bytes / (ev_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "traffic": measured_traffic(FWD_SOURCES,
+                                        os.path.join(ROOT, "profiles", f"forward_{args.workload}_traffic.txt")),
+            "avg_launch_ms": ev_ms,
+            "algorithmic_bytes_per_launch": min_bytes,
+            "algorithmic_bytes": "x, y, dt, B, C once each plus the fp32 final state: "
+                                 "H(P(s_x+s_y)+s_dt) + 2GN s_bc bytes per token, + b H P N 4",
+            "mfma_frac_algorithmic": flops / (ev_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         },
     }
 
@@ -502,6 +517,7 @@ def main():
         cold_step_ms = cold_ms(torch, stream, one_step, 32, flush)
         cold_gbs = step_bytes / (cold_step_ms / 1e3) / 1e9
         multi_gbs = multi_bytes / (multi_ms / 1e3) / 1e9
+        multi_gops = STEP_OPS * bb * hh * pp * nn * nst / (multi_ms / 1e3) / 1e9
         result["decode"] = {
             "workload": f"cfg4: ssd_step b={bb} H={hh} P={pp} N={nn} bf16 io, fp32 state, 64 steps",
             "us_per_step": step_ms * 1e3,
@@ -518,9 +534,11 @@ def main():
                 "us_per_call": multi_ms * 1e3,
                 "us_per_step": multi_ms * 1e3 / nst,
                 "tokens_per_s": bb * nst / (multi_ms / 1e3),
-                "roofline": {"kernel": "step_multi_kernel<bf16,4,32>", "bound": "hbm", "achieved": multi_gbs,
-                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": multi_gbs / PEAK_HBM_GBS,
-                             "algorithmic_bytes_per_launch": multi_bytes},
+                "hbm_gbs_algorithmic": multi_gbs,
+                "roofline": {"kernel": "step_multi_kernel (state in registers across the steps)", "bound": "alu",
+                             "achieved": multi_gops, "peak": PEAK_VALU_GOPS, "unit": "Gop/s",
+                             "frac": multi_gops / PEAK_VALU_GOPS, "ops_per_state_element_step": STEP_OPS,
+                             "traffic": None},
             },
         }
         log(f"decode cold: {cold_step_ms * 1e3:.1f} us/step, {cold_gbs:.0f} GB/s algorithmic")
@@ -607,6 +625,21 @@ def main():
                       f"({cpu_s:.1f} s, fp64 token recurrence, OpenMP over (b, h))",
         }
         log(f"cpu oracle: {cpu_s:.1f}s for {len(hs)} heads on {oracle.max_threads()} threads")
+        result["cpu_baseline"]["model"] = cpu_model()
+        # one thread: the tiny and 130M workloads whole, and one head of this workload
+        one = {}
+        for name in ("cfg0", "cfg1"):
+            f1 = make_config_inputs(name)
+            t1 = time.perf_counter()
+            oracle.forward(f1.x, f1.dt, f1.A, f1.B, f1.C, f1.D, f1.h0, threads=1)
+            one[name] = {"tokens_per_s": f1.x.shape[0] * f1.x.shape[1] / (time.perf_counter() - t1),
+                         "seconds": time.perf_counter() - t1}
+        t1 = time.perf_counter()
+        oracle.forward(fi.x[:, :, :1], fi.dt[:, :, :1], fi.A[:1], fi.B, fi.C, fi.D[:1], None, threads=1)
+        one_s = time.perf_counter() - t1
+        one[f"{args.workload}_1_head"] = {"token_heads_per_s": tokens / one_s, "seconds": one_s}
+        result["cpu_baseline"]["one_thread"] = one
+        log(f"cpu oracle, one thread: " + ", ".join(f"{k} {v['seconds']:.2f}s" for k, v in one.items()))
 
     print(json.dumps(result), flush=True)
 

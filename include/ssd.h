@@ -29,6 +29,10 @@
  *     means nothing was launched, and ssd_last_error() describes why.
  *     SSD_ERR_HIP is returned when a launch itself fails.  Faults inside a
  *     kernel surface at the caller's next synchronisation.
+ *   - x, B, C, y, h0, final_state, states and the decode state must be
+ *     16-byte aligned (the kernels move them in 16-byte vectors); a
+ *     misaligned pointer returns SSD_ERR_UNSUPPORTED.  dt, A, D and the
+ *     per-position float32 arrays have no alignment rule beyond their type.
  *   - io dtype (ssd_dims.io) is the element type of x, dt, B, C and y:
  *     SSD_F32 (float) or SSD_BF16 (bfloat16).  A, D, h0, the final state, the
  *     decode state and every intermediate are float32.

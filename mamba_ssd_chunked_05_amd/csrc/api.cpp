@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 
 #include "../../include/ssd.h"
@@ -114,6 +115,14 @@ bool overlap(const Span& a, const Span& b) {
 
 ssd_status need_ptr(const Span& s) {
     if (s.bytes > 0 && !s.p) return fail(SSD_ERR_NULL, "%s is NULL", s.name);
+    return SSD_OK;
+}
+
+// The kernels read and write the io and state arrays with 16-byte vector accesses.
+ssd_status need_align16(std::initializer_list<Span> spans) {
+    for (const Span& p : spans)
+        if (p.p && reinterpret_cast<uintptr_t>(p.p) % 16)
+            return fail(SSD_ERR_UNSUPPORTED, "%s must be 16-byte aligned", p.name);
     return SSD_OK;
 }
 
@@ -257,6 +266,7 @@ ssd_status ssd_chunk_state(const ssd_dims* dims, const void* x, const void* B, c
         Span sx{x, z.x, "x"}, sB{B, z.bc, "B"}, sdtt{dt_t, z.cs, "dt_t"}, scs{dA_cs_log2, z.cs, "dA_cs_log2"},
             sst{states, z.states, "states"};
         for (const Span& p : {sx, sB, sdtt, scs, sst}) SSD_TRY(need_ptr(p));
+        SSD_TRY(need_align16({sx, sB, sst}));
         Span ins[] = {sx, sB, sdtt, scs};
         SSD_TRY(no_alias(sst, ins, 4));
         hipError_t e = ssd::launch_chunk_state(s, x, B, dt_t, dA_cs_log2, states, (hipStream_t)stream);
@@ -276,6 +286,7 @@ ssd_status ssd_state_passing(const ssd_dims* dims, float* states, const float* d
         Span sst{states, z.states, "states"}, scs{dA_cs_log2, z.cs, "dA_cs_log2"}, sh0{h0, h0 ? z.hstate : 0, "h0"},
             sfin{final_state, z.hstate, "final_state"};
         for (const Span& p : {sst, scs, sfin}) SSD_TRY(need_ptr(p));
+        SSD_TRY(need_align16({sst, sh0, sfin}));
         Span ins[] = {sst, scs, sh0};
         SSD_TRY(no_alias(sfin, ins, 3));
         Span ins2[] = {scs, sh0};
@@ -299,6 +310,7 @@ ssd_status ssd_chunk_scan(const ssd_dims* dims, const void* x, const void* B, co
             scs{dA_cs_log2, z.cs, "dA_cs_log2"}, sst{chunk_start_states, z.states, "chunk_start_states"},
             sD{D, D ? z.A : 0, "D"}, sy{y, z.x, "y"};
         for (const Span& p : {sx, sB, sC, sdtt, scs, sst, sy}) SSD_TRY(need_ptr(p));
+        SSD_TRY(need_align16({sx, sB, sC, sst, sy}));
         Span ins[] = {sx, sB, sC, sdtt, scs, sst, sD};
         SSD_TRY(no_alias(sy, ins, 7));
         hipError_t e = ssd::launch_chunk_scan(s, x, B, C, dt_t, dA_cs_log2, chunk_start_states, D, y,
@@ -335,6 +347,7 @@ ssd_status ssd_forward_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, const
             sD{D, D ? z.A : 0, "D"}, sh0{h0, h0 ? z.hstate : 0, "h0"}, sy{y, z.x, "y"},
             sfin{final_state, z.hstate, "final_state"}, sws{workspace, f.total, "workspace"};
         for (const Span& p : {sx, sdt, sA, sB, sC, sy, sfin}) SSD_TRY(need_ptr(p));
+        SSD_TRY(need_align16({sx, sB, sC, sy, sh0, sfin}));
         if (s.b > 0 && s.L > 0) {
             if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", f.total);
             if (workspace_bytes < f.total)
@@ -404,6 +417,7 @@ ssd_status ssd_step_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, float* s
             sC{C, (size_t)(s.b * s.G * s.N) * e, "C"}, sD{D, D ? (size_t)s.H * 4 : 0, "D"},
             sy{y, (size_t)(s.b * s.H * s.P) * e, "y"};
         for (const Span& p : {sst, sx, sdt, sA, sB, sC, sy}) SSD_TRY(need_ptr(p));
+        SSD_TRY(need_align16({sst, sx, sB, sC, sy}));
         Span ins[] = {sx, sdt, sA, sB, sC, sD, sbias};
         SSD_TRY(no_alias(sst, ins, 7));
         Span ins2[] = {sx, sdt, sA, sB, sC, sD, sst, sbias};
@@ -442,9 +456,7 @@ ssd_status ssd_step_multi_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, fl
         SSD_TRY(no_alias(sst, ins, 7));
         Span ins2[] = {sx, sdt, sA, sB, sC, sD, sst, sbias};
         SSD_TRY(no_alias(sy, ins2, 8));
-        for (const Span& p : {sst, sx, sB, sC, sy})
-            if (reinterpret_cast<uintptr_t>(p.p) % 16)
-                return fail(SSD_ERR_UNSUPPORTED, "%s must be 16-byte aligned", p.name);
+        SSD_TRY(need_align16({sst, sx, sB, sC, sy}));
         hipError_t he = ssd::launch_step_multi(s, dfe, state, x, dt, A, B, C, D, y, (hipStream_t)stream);
         if (he != hipSuccess) return hip_fail(he, "ssd_step_multi");
         return ok();

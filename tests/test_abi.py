@@ -97,9 +97,38 @@ def test_forward_rejects_null_and_workspace():
 
 def test_forward_rejects_aliasing():
     d = _d()
-    assert _forward(d, y=_p(100)) == ALIAS  # y inside x
+    assert _forward(d, y=_p(96)) == ALIAS  # y inside x
     assert _forward(d, fin=_p(6 << 30)) == ALIAS  # final == y
     assert _forward(d, ws=_p(0)) == ALIAS  # workspace over x
+
+
+@pytest.mark.parametrize("name", ["x", "B", "C", "y", "fin", "h0"])
+def test_forward_rejects_misaligned(name):
+    """x, B, C, y, h0 and the final state move in 16-byte vectors: misaligned pointers are rejected."""
+    base = dict(x=0, B=3 << 30, C=4 << 30, y=6 << 30, fin=7 << 30, h0=9 << 30)
+    over = {name: _p(base[name] + 8)}
+    if name != "h0":
+        over["h0"] = _p(9 << 30)
+    assert _forward(_d(), **over) == UNSUP
+    assert b"16-byte" in ssd.load().ssd_last_error()
+    # the same call with every pointer aligned passes validation up to the (fake) workspace check
+    assert _forward(_d(), h0=_p(9 << 30), ws_bytes=1) == WS
+
+
+def test_step_and_staged_reject_misaligned():
+    lib = ssd.load()
+    d = _d(L=1)
+    args = [_p(0), _p(1 << 30), _p(2 << 30), _p(3 << 30), _p(4 << 30), _p(5 << 30), None, _p(6 << 30), None]
+    for i in (0, 1, 4, 5, 7):  # state, x, B, C, y
+        bad = list(args)
+        bad[i] = _p(((i + 10) << 30) + 8)
+        assert lib.ssd_step(ctypes.byref(d), *bad) == UNSUP, i
+    d = _d()
+    assert lib.ssd_chunk_state(ctypes.byref(d), _p(8), _p(1 << 30), _p(2 << 30), _p(3 << 30), _p(4 << 30),
+                               None) == UNSUP
+    assert lib.ssd_state_passing(ctypes.byref(d), _p(0), _p(1 << 30), None, _p((2 << 30) + 4), None) == UNSUP
+    assert lib.ssd_chunk_scan(ctypes.byref(d), _p(0), _p(1 << 30), _p((2 << 30) + 8), _p(3 << 30), _p(4 << 30),
+                              _p(5 << 30), None, _p(6 << 30), None) == UNSUP
 
 
 def test_staged_calls_validate():
@@ -125,7 +154,7 @@ def test_step_validates():
     assert lib.ssd_step(ctypes.byref(d), *args) == SHAPE
     d = _d(L=1)
     bad = list(args)
-    bad[7] = _p(8)  # y over the state
+    bad[7] = _p(16)  # y over the state
     assert lib.ssd_step(ctypes.byref(d), *bad) == ALIAS
     bad = list(args)
     bad[0] = None

@@ -1,10 +1,12 @@
 """The five benchmark workloads at full size, through ssd_forward / ssd_step, against the oracle.
 
-Small workloads are compared element by element over every output.  For the
-long sequences the GPU runs the whole problem in the launch configuration the
-benchmark times (chunk = 0, the library's choice), and the oracle recomputes a
-sample of heads over the full sequence -- heads are independent, so each
-sampled head's y and final state are exact references.
+Every workload is compared over every head and every token: the GPU runs the
+whole problem in the launch configuration the benchmark times (chunk = 0, the
+library's choice) and the fp64 oracle recomputes all of it.  y is checked by
+its global relative L2 error, per (b, t, h) row and per element
+(tests/gpu_util.py); the final state element-wise against its RMS.  The largest
+point (256K tokens x 32 heads x headdim 64) holds about 4.3 GB per fp64 copy of
+x or y on the host, well inside the GPU host's memory, so no head is sampled.
 """
 
 from __future__ import annotations
@@ -20,23 +22,17 @@ from tests.gpu_util import assert_close_state, assert_close_y, dev, host
 pytestmark = pytest.mark.gpu
 
 
-def _forward_parity(gpu_ssd, name, heads=None, chunk=0):
+def _forward_parity(gpu_ssd, name, chunk=0):
     fi = make_config_inputs(name)
-    cfg = CONFIGS[name]
-    q = chunk if chunk else 0
+    print(f"{name}: inputs drawn", flush=True)
     y, fin = gpu_ssd.forward(dev(fi.x, fi.dtype), dev(fi.dt, fi.dtype), dev(fi.A), dev(fi.B, fi.dtype),
-                             dev(fi.C, fi.dtype), dev(fi.D), dev(fi.h0), chunk=q)
+                             dev(fi.C, fi.dtype), dev(fi.D), dev(fi.h0), chunk=chunk)
     torch.cuda.synchronize()
-    if heads is None:
-        ref = oracle.forward(fi.x, fi.dt, fi.A, fi.B, fi.C, fi.D, fi.h0)
-        yg, fg = host(y), host(fin)
-    else:
-        hs = list(heads)
-        assert cfg["ngroups"] == 1
-        ref = oracle.forward(fi.x[:, :, hs], fi.dt[:, :, hs], fi.A[hs], fi.B, fi.C, fi.D[hs], None)
-        yg = y[:, :, hs].float().cpu().numpy().astype(np.float64)
-        fg = fin[:, hs].cpu().numpy().astype(np.float64)
-    ey = assert_close_y(yg, ref["y"], fi.dtype)
+    yg, fg = host(y), host(fin)
+    del y, fin
+    ref = oracle.forward(fi.x, fi.dt, fi.A, fi.B, fi.C, fi.D, fi.h0)
+    del fi
+    ey = assert_close_y(yg, ref["y"], CONFIGS[name]["dtype"], f"{name} y")
     es = assert_close_state(fg, ref["final"])
     print(f"{name}: rel L2(y) = {ey:.3e}, max|dS|/RMS = {es:.3e}")
 
@@ -56,14 +52,13 @@ def test_cfg2_27b_full(gpu_ssd, name):
     _forward_parity(gpu_ssd, name)
 
 
-def test_cfg2_27b_64k_sampled(gpu_ssd):
-    _forward_parity(gpu_ssd, "cfg2_64k", heads=[0, 13, 27, 40, 66, 79])
+def test_cfg2_27b_64k_all_heads(gpu_ssd):
+    _forward_parity(gpu_ssd, "cfg2_64k")
 
 
 @pytest.mark.parametrize("name", [n for n in CONFIGS if n.startswith("cfg3_")])
-def test_cfg3_long_context_sampled(gpu_ssd, name):
-    heads = [0, 31] if CONFIGS[name]["seqlen"] > 65536 else [0, 11, 31]
-    _forward_parity(gpu_ssd, name, heads=heads)
+def test_cfg3_long_context_all_heads(gpu_ssd, name):
+    _forward_parity(gpu_ssd, name)
 
 
 def test_cfg4_decode_64_steps(gpu_ssd):
@@ -82,7 +77,6 @@ def test_cfg4_decode_64_steps(gpu_ssd):
         ys_ref.append(oracle.step(S_ref, si.x[t], si.dt[t], si.A, si.B[t], si.C[t], si.D))
         ys.append(host(y))
         torch.cuda.synchronize()
-        if t % 8 == 7 or t == cfg["steps"] - 1:
-            worst_state = max(worst_state, assert_close_state(host(S), S_ref, f"state after step {t + 1}"))
+        worst_state = max(worst_state, assert_close_state(host(S), S_ref, f"state after step {t + 1}"))
     ey = assert_close_y(np.stack(ys), np.stack(ys_ref), "bf16", "y over 64 steps")
     print(f"cfg4: rel L2(y, 64 steps) = {ey:.3e}, worst max|dS|/RMS = {worst_state:.3e}")
