@@ -191,6 +191,23 @@ ssd_status ssd_forward_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, const
                           size_t workspace_bytes, void* stream);
 
 /*
+ * ssd_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The forward's intermediates go to a static device
+ * scratch of 128 MiB that the library holds on each GPU it runs on until the
+ * process ends; this call allocates nothing and frees nothing.  Shapes whose
+ * ssd_forward_workspace_bytes() exceeds 128 MiB return SSD_ERR_WORKSPACE
+ * (the 2.7B-shaped forward at 64K tokens needs about 108 MB).  All other
+ * arguments, validation and results are those of ssd_forward.  Every call on
+ * one GPU shares that GPU's scratch: calls that may overlap in time on one GPU
+ * (different streams, or different host threads) race and must be ordered by
+ * the caller.  The first call on a device looks up the scratch's address.
+ */
+ssd_status ssd_forward_noalloc(const ssd_dims* dims, const void* x, const void* dt, const float* A,
+                               const void* B, const void* C, const float* D, const float* h0,
+                               void* y, float* final_state, void* stream);
+
+/*
  * O(1) decode step for one token per (b, h), in place on state (dims->seqlen
  * must be 1; dims->chunk is ignored):
  *     S <- exp(dt A) S + dt x (outer) B;   y = C . S + D x   (after the update)

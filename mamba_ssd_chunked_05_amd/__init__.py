@@ -28,7 +28,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "SsdError", "load", "library_path", "forward", "forward_workspace_bytes", "step", "step_multi", "chunk_cumsum",
+    "SsdError", "load", "library_path", "forward", "forward_noalloc", "forward_workspace_bytes", "step", "step_multi",
+    "chunk_cumsum",
     "chunk_state", "state_passing", "chunk_scan", "query_config", "abi_version", "Dims", "DtFrontend",
     "Frontend",
 ]
@@ -106,6 +107,7 @@ def load():
         "ssd_step_multi": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_chunk_cumsum_ex": [dp, fp, vp, vp, vp, vp, vp],
         "ssd_forward_ex": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "ssd_forward_noalloc": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_step_ex": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_step_multi_ex": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_query_config": [dp] + [ctypes.POINTER(ctypes.c_int)] * 4,
@@ -250,6 +252,27 @@ def forward(x, dt, A, B, C, D=None, h0=None, *, chunk: int = 0, y=None, final_st
                             _ptr(D), _ptr(h0), _ptr(y), _ptr(final_state), _ptr(workspace), workspace.numel(),
                             _stream(x))
     _check(st, "ssd_forward")
+    return y, final_state
+
+
+def forward_noalloc(x, dt, A, B, C, D=None, h0=None, *, chunk: int = 0, y=None,
+                    final_state=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """ssd_forward_noalloc: the forward with the library's static device scratch instead of a workspace.
+    Pass ``y`` and ``final_state`` to keep the call free of any allocation."""
+    lib = load()
+    d = _fwd_dims(x, B, chunk)
+    _check_fwd_inputs(x, dt, A, B, C, D, h0)
+    b, L, H, P = x.shape
+    N = B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype, x.shape)
+    if final_state is None:
+        final_state = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
+    _dev(final_state, "final_state", torch.float32, (b, H, P, N))
+    st = lib.ssd_forward_noalloc(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+                                 _ptr(y), _ptr(final_state), _stream(x))
+    _check(st, "ssd_forward_noalloc")
     return y, final_state
 
 

@@ -332,9 +332,16 @@ size_t ssd_forward_workspace_bytes(const ssd_dims* dims) {
     }
 }
 
-ssd_status ssd_forward_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, const void* x, const void* dt,
+}  // extern "C"
+
+namespace {
+
+// ssd_forward_ex, or with use_static the same forward on the library's static scratch
+// (ssd_forward_noalloc): every argument is validated before the first HIP call.
+ssd_status forward_common(const ssd_dims* dims, const ssd_dt_frontend* fe, const void* x, const void* dt,
                           const float* A, const void* B, const void* C, const float* D, const float* h0, void* y,
-                          float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+                          float* final_state, void* workspace, size_t workspace_bytes, bool use_static,
+                          void* stream) {
     try {
         ssd::Shape s;
         SSD_TRY(check_dims(dims, Need::kForward, &s));
@@ -348,7 +355,10 @@ ssd_status ssd_forward_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, const
             sfin{final_state, z.hstate, "final_state"}, sws{workspace, f.total, "workspace"};
         for (const Span& p : {sx, sdt, sA, sB, sC, sy, sfin}) SSD_TRY(need_ptr(p));
         SSD_TRY(need_align16({sx, sB, sC, sy, sh0, sfin}));
-        if (s.b > 0 && s.L > 0) {
+        if (use_static && f.total > ssd::kStaticScratchBytes)
+            return fail(SSD_ERR_WORKSPACE, "ssd_forward_noalloc: this shape needs %zu bytes of scratch, above the "
+                        "%zu-byte static scratch (use ssd_forward with a workspace)", f.total, ssd::kStaticScratchBytes);
+        if (!use_static && s.b > 0 && s.L > 0) {
             if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", f.total);
             if (workspace_bytes < f.total)
                 return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, f.total);
@@ -360,12 +370,16 @@ ssd_status ssd_forward_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, const
         SSD_TRY(no_alias(sfin, ins, 8));
         Span o1[] = {sy};
         SSD_TRY(no_alias(sfin, o1, 1));
-        if (s.b > 0 && s.L > 0) {
+        if (!use_static && s.b > 0 && s.L > 0) {
             Span all[] = {sx, sdt, sA, sB, sC, sD, sh0, sy, sfin, sbias};
             SSD_TRY(no_alias(sws, all, 10));
         }
         hipStream_t st = (hipStream_t)stream;
         if (s.b == 0) return ok();
+        if (use_static && s.L > 0) {  // validation is complete: the first HIP call of this entry point
+            hipError_t e = ssd::static_scratch(&workspace);
+            if (e != hipSuccess) return hip_fail(e, "ssd_forward_noalloc (static scratch address)");
+        }
         if (ssd::fast_chunk_supported(s)) {
             if (s.L == 0) {  // no tokens: the final state is h0 (or zero)
                 hipError_t e = ssd::launch_state_passing(s, nullptr, nullptr, h0, final_state, st);
@@ -395,6 +409,23 @@ ssd_status ssd_forward_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, const
     } catch (...) {
         return fail(SSD_ERR_HIP, "internal error");
     }
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_forward_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, const void* x, const void* dt,
+                          const float* A, const void* B, const void* C, const float* D, const float* h0, void* y,
+                          float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    return forward_common(dims, fe, x, dt, A, B, C, D, h0, y, final_state, workspace, workspace_bytes, false, stream);
+}
+
+ssd_status ssd_forward_noalloc(const ssd_dims* dims, const void* x, const void* dt, const float* A, const void* B,
+                               const void* C, const float* D, const float* h0, void* y, float* final_state,
+                               void* stream) {
+    return forward_common(dims, nullptr, x, dt, A, B, C, D, h0, y, final_state, nullptr, ssd::kStaticScratchBytes,
+                          true, stream);
 }
 
 ssd_status ssd_forward(const ssd_dims* dims, const void* x, const void* dt, const float* A, const void* B,

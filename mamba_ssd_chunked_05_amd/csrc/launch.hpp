@@ -97,6 +97,12 @@ hipError_t launch_backward(const Shape& s, const void* x, const void* dt, const 
                            void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0, void* workspace,
                            hipStream_t st);
 
+// The static device scratch of ssd_forward_noalloc (noalloc.hip): its size, and its
+// device address on the current device (taken with hipGetSymbolAddress on the first
+// call per device, then cached).
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
+hipError_t static_scratch(void** ptr);
+
 // LDS bytes the generic chunk kernels need; used by validation.
 size_t chunk_state_lds_bytes(const Shape& s);
 size_t chunk_scan_lds_bytes(const Shape& s);

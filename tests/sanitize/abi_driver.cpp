@@ -60,6 +60,14 @@ int main() {
     expect(ssd_forward(&d, P(0), P(GB), F(2 * GB), P(3 * GB), P(4 * GB), nullptr, nullptr, P(96), F(7 * GB),
                        P(8 * GB), need, nullptr),
            SSD_ERR_ALIAS, "forward y over x");
+    // the allocation-free forward: same validation, and a shape above its static scratch is refused
+    ssd_dims big = dims(1, 262144, 80, 64, 128, 1, 0, SSD_BF16);
+    expect(ssd_forward_noalloc(&big, P(0), P(GB), F(2 * GB), P(3 * GB), P(4 * GB), nullptr, nullptr, P(6 * GB),
+                               F(7 * GB), nullptr),
+           SSD_ERR_WORKSPACE, "noalloc oversize");
+    expect(ssd_forward_noalloc(&d, nullptr, P(GB), F(2 * GB), P(3 * GB), P(4 * GB), nullptr, nullptr, P(6 * GB),
+                               F(7 * GB), nullptr),
+           SSD_ERR_NULL, "noalloc x NULL");
     // staged calls
     expect(ssd_chunk_state(&d, P(0), nullptr, F(2 * GB), F(3 * GB), F(4 * GB), nullptr), SSD_ERR_NULL,
            "chunk_state B NULL");

@@ -27,7 +27,7 @@ def _declared():
 def test_header_symbols_exported():
     lib = ssd.load()
     names = _declared()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
 
@@ -129,6 +129,28 @@ def test_step_and_staged_reject_misaligned():
     assert lib.ssd_state_passing(ctypes.byref(d), _p(0), _p(1 << 30), None, _p((2 << 30) + 4), None) == UNSUP
     assert lib.ssd_chunk_scan(ctypes.byref(d), _p(0), _p(1 << 30), _p((2 << 30) + 8), _p(3 << 30), _p(4 << 30),
                               _p(5 << 30), None, _p(6 << 30), None) == UNSUP
+
+
+def test_forward_noalloc_validates():
+    """The allocation-free forward validates like ssd_forward and refuses shapes whose
+    intermediates exceed its 128 MiB static scratch, before any HIP call."""
+    lib = ssd.load()
+
+    def call(d, **over):
+        p = dict(x=_p(0), dt=_p(1 << 30), A=_p(2 << 30), B=_p(3 << 30), C=_p(4 << 30), D=None, h0=None,
+                 y=_p(6 << 30), fin=_p(7 << 30))
+        p.update(over)
+        return lib.ssd_forward_noalloc(ctypes.byref(d) if d is not None else None, p["x"], p["dt"], p["A"], p["B"],
+                                       p["C"], p["D"], p["h0"], p["y"], p["fin"], None)
+
+    assert call(None) == NULL
+    assert call(_d(H=6, G=4)) == SHAPE
+    assert call(_d(), x=None) == NULL
+    assert call(_d(), x=_p(8)) == UNSUP
+    big = _d(L=262144, H=80, Q=0)  # 2.7B heads at 256K tokens: about 170 MB of intermediates
+    assert lib.ssd_forward_workspace_bytes(ctypes.byref(big)) > 128 << 20
+    assert call(big) == WS
+    assert b"static scratch" in lib.ssd_last_error()
 
 
 def test_staged_calls_validate():
