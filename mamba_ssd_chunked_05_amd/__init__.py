@@ -108,6 +108,7 @@ def load():
         "ssd_chunk_cumsum_ex": [dp, fp, vp, vp, vp, vp, vp],
         "ssd_forward_ex": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "ssd_forward_noalloc": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "ssd_bench_rmw_stream": [vp, ctypes.c_size_t, ctypes.c_float, ctypes.c_float, vp],
         "ssd_step_ex": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_step_multi_ex": [dp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "ssd_query_config": [dp] + [ctypes.POINTER(ctypes.c_int)] * 4,
@@ -274,6 +275,13 @@ def forward_noalloc(x, dt, A, B, C, D=None, h0=None, *, chunk: int = 0, y=None,
                                  _ptr(y), _ptr(final_state), _stream(x))
     _check(st, "ssd_forward_noalloc")
     return y, final_state
+
+
+def bench_rmw_stream(buf: torch.Tensor, a: float = 1.0, b: float = 0.0) -> None:
+    """Measurement helper (ssd_bench.h): buf <- a * buf + b in place, float32, on the current stream."""
+    lib = load()
+    _dev(buf, "buf", torch.float32)
+    _check(lib.ssd_bench_rmw_stream(_ptr(buf), buf.numel(), a, b, _stream(buf)), "ssd_bench_rmw_stream")
 
 
 def step(state, x, dt, A, B, C, D=None, *, y=None, frontend: Optional[Frontend] = None) -> torch.Tensor:

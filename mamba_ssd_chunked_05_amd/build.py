@@ -30,6 +30,7 @@ SOURCES = [
     "selective.hip",
     "backward.hip",
     "noalloc.hip",
+    "calib.hip",
 ]
 
 

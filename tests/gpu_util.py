@@ -9,7 +9,9 @@ y is accepted on three levels, all of which must hold:
   satisfies ||d_row|| <= rel * ||ref_row|| + floor * rms_row, where rms_row is
   the root mean square of the reference row norms of the same head (the same
   index of the second-to-last axis);
-* per element: |d| <= rel * |ref| + floor * rms, rms over the same head's reference.
+* per element: |d| <= rel * |ref| + floor * rms, rms the larger of the same head's
+  reference RMS and that of the element's own row (a row may sit far above its
+  head's average, e.g. early tokens carrying a large initial state).
 
 For bf16 outputs the relative parts start from 2^-8, the largest relative
 error of rounding one value to bfloat16 (8 significant bits, nearest-even),
@@ -101,7 +103,9 @@ def local_errors(got, ref, dtype: str):
         d = gb - rb
         row_ratio = np.sqrt(np.sum(d * d, axis=2)) / (rrel * np.sqrt(np.sum(rb * rb, axis=2))
                                                       + rfloor * rms_row[None, :] + 1e-300)
-        el_ratio = np.abs(d) / (erel * np.abs(rb) + efloor * rms_el[None, :, None] + 1e-300)
+        row_rms = np.sqrt(np.mean(rb * rb, axis=2))
+        el_scale = np.maximum(rms_el[None, :], row_rms)[:, :, None]
+        el_ratio = np.abs(d) / (erel * np.abs(rb) + efloor * el_scale + 1e-300)
         k = int(np.argmax(row_ratio))
         if row_ratio.flat[k] > worst_row or at_row < 0:
             worst_row, at_row = float(row_ratio.flat[k]), i * G + k

@@ -32,6 +32,20 @@ def test_header_symbols_exported():
         assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
 
 
+def test_bench_helper_exported_and_validates():
+    """The measurement helper of ssd_bench.h is exported and validates before launching."""
+    lib = ssd.load()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "ssd_bench.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["ssd_bench_rmw_stream"]
+    for n in names:
+        assert hasattr(lib, n)
+    assert lib.ssd_bench_rmw_stream(None, 16, 1.0, 0.0, None) == NULL
+    assert lib.ssd_bench_rmw_stream(_p(8), 16, 1.0, 0.0, None) == UNSUP
+    assert lib.ssd_bench_rmw_stream(_p(0), 6, 1.0, 0.0, None) == UNSUP
+    assert lib.ssd_bench_rmw_stream(None, 0, 1.0, 0.0, None) == OK
+
+
 def test_abi_version_and_strings():
     lib = ssd.load()
     assert ssd.abi_version() == 1
