@@ -43,6 +43,7 @@ struct WideRegs {
 // B / C block: rows tid / 16 (+ 16 k), columns 8 (tid % 16) of the block.
 struct WideAddr {
     int xr, xc, br, bc;
+    uint32_t xo, bo;  // byte offsets of the first x piece and of the B / C piece within their tiles
 };
 
 struct WideSrc {
@@ -52,22 +53,30 @@ struct WideSrc {
     int H, G, N, h, g;
 };
 
-// rows past the sequence end read a valid row and are selected to zero (per word: a select of
-// the whole vector is lowered through private memory)
-__device__ __forceinline__ uint4 ld_row(const bf16* base, int64_t row_stride, int r, int last, int c) {
-    const bool ok = r <= last;
-    const uint4 v = ld16(base + (int64_t)(ok ? r : last) * row_stride + c);
-    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+// Sub-chunk tiles are read through buffer resources: a resource starts at the tile's first element and
+// its size ends with the last row inside the sequence, so the hardware's range check returns zero for
+// rows past the end (whole 16-byte pieces: a row is in range entirely or not at all) and no load
+// reaches past it.  Each load is then a wavefront-uniform resource plus one 32-bit per-thread byte
+// offset, with no per-element select.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* base, int64_t row_stride, int64_t rows,
+                                                           int row_len) {
+    const int64_t n = rows < QS ? rows : QS;
+    const int bytes = n > 0 ? (int)(((n - 1) * row_stride + row_len) * 2) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ldbuf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // x, dt and cs of sub-chunk `sub` starting at token tbase
 __device__ __forceinline__ void wide_load_x(WideRegs& rg, const WideAddr& a, const WideSrc& s, int64_t tbase, int sub,
                                             int tid) {
-    const int last = (int)(s.L - 1 - tbase);
-    const bf16* xb = s.x + ((s.b * s.L + tbase) * s.H + s.h) * (int64_t)P;
     const int64_t HP_ = (int64_t)s.H * P;
+    const auto r = tile_rsrc(s.x + ((s.b * s.L + tbase) * s.H + s.h) * (int64_t)P, HP_, s.L - tbase, P);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) rg.x[k] = ld_row(xb, HP_, a.xr + 32 * k, last, a.xc);
+    for (int k = 0; k < 2; ++k) rg.x[k] = ldbuf(r, a.xo + (uint32_t)(32 * k * HP_ * 2));
     if (tid < 64) {
         rg.dt = s.ds.dt_t[s.dt0 + (int64_t)QS * sub + tid];
         rg.cs = s.ds.cs[s.dt0 + (int64_t)QS * sub + tid];
@@ -77,12 +86,14 @@ __device__ __forceinline__ void wide_load_x(WideRegs& rg, const WideAddr& a, con
 // block nb (columns 128 nb ..) of B (and C) for the sub-chunk starting at tbase
 template <bool WITH_C>
 __device__ __forceinline__ void wide_load_bc(WideRegs& rg, const WideAddr& a, const WideSrc& s, int64_t tbase, int nb) {
-    const int last = (int)(s.L - 1 - tbase);
-    const int64_t GN = (int64_t)s.G * s.N, off = ((s.b * s.L + tbase) * s.G + s.g) * (int64_t)s.N + WB * nb;
+    const int64_t GN = (int64_t)s.G * s.N, off = ((s.b * s.L + tbase) * s.G + s.g) * (int64_t)s.N;
+    const auto rb = tile_rsrc(s.B + off, GN, s.L - tbase, s.N);
+    const auto rc = tile_rsrc(WITH_C ? s.C + off : s.B + off, GN, s.L - tbase, s.N);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        rg.b[k] = ld_row(s.B + off, GN, a.br + 16 * k, last, a.bc);
-        if (WITH_C) rg.c[k] = ld_row(s.C + off, GN, a.br + 16 * k, last, a.bc);
+        const uint32_t o = a.bo + (uint32_t)((16 * k * GN + WB * nb) * 2);
+        rg.b[k] = ldbuf(rb, o);
+        if (WITH_C) rg.c[k] = ldbuf(rc, o);
     }
 }
 
@@ -133,11 +144,13 @@ __device__ __forceinline__ void wide_store_x(bf16* xs, float* lw, float* dtw, fl
     if (tid < 64) wide_decay_store<FWD>(lw, dtw, ww, ec, alpha, rg.dt, rg.cs, cs_prev, tot, tid);
 }
 
-__device__ __forceinline__ void wide_addr(WideAddr& a, int tid) {
+__device__ __forceinline__ void wide_addr(WideAddr& a, const WideSrc& s, int tid) {
     a.xr = tid >> 3;
     a.xc = (tid & 7) * 8;
     a.br = tid >> 4;
     a.bc = (tid & 15) * 8;
+    a.xo = (uint32_t)((a.xr * (int64_t)s.H * P + a.xc) * 2);
+    a.bo = (uint32_t)((a.br * (int64_t)s.G * s.N + a.bc) * 2);
 }
 
 // ---------------------------------------------------------------------------
@@ -192,7 +205,7 @@ chunk_scan_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     src.g = g;
     src.dt0 = FWD ? ((b * H + h) * nsubT + c * (Q / QS)) * QS : ((b * H + h) * nC + c) * Q;
     WideAddr ad;
-    wide_addr(ad, tid);
+    wide_addr(ad, src, tid);
     WideRegs rg;
     wide_load_x(rg, ad, src, t0, 0, tid);
     wide_load_bc<true>(rg, ad, src, t0, 0);
@@ -374,11 +387,12 @@ struct Wide8Regs {
     float dt, cs;
 };
 
-// x of the sub-chunk at tbase (row tid / 8, columns 8 (tid % 8)), and its dt and cs (threads < 64)
-__device__ __forceinline__ void wide8_load_x(Wide8Regs& rg, const WideSrc& s, int64_t tbase, int sub, int tid) {
-    const int last = (int)(s.L - 1 - tbase);
-    const bf16* xb = s.x + ((s.b * s.L + tbase) * s.H + s.h) * (int64_t)P;
-    rg.x = ld_row(xb, (int64_t)s.H * P, tid >> 3, last, (tid & 7) * 8);
+// x of the sub-chunk at tbase (row tid / 8, columns 8 (tid % 8); byte offset xo), and its dt and cs
+// (threads < 64)
+__device__ __forceinline__ void wide8_load_x(Wide8Regs& rg, const WideSrc& s, int64_t tbase, int sub, int tid,
+                                             uint32_t xo) {
+    const auto r = tile_rsrc(s.x + ((s.b * s.L + tbase) * s.H + s.h) * (int64_t)P, (int64_t)s.H * P, s.L - tbase, P);
+    rg.x = ldbuf(r, xo);
     if (tid < 64) {
         rg.dt = s.ds.dt_t[s.dt0 + (int64_t)QS * sub + tid];
         rg.cs = s.ds.cs[s.dt0 + (int64_t)QS * sub + tid];
@@ -386,16 +400,16 @@ __device__ __forceinline__ void wide8_load_x(Wide8Regs& rg, const WideSrc& s, in
 }
 
 // pass q's two blocks of B and C: half tid / 256 takes columns (tid / 256) N/2 + 128 q ..,
-// rows (tid % 256) / 16 + 16 k, columns 8 (tid % 16) of the block
-__device__ __forceinline__ void wide8_load_bc(Wide8Regs& rg, const WideSrc& s, int64_t tbase, int q, int tid) {
-    const int last = (int)(s.L - 1 - tbase);
-    const int half = tid >> 8, r0 = (tid & 255) >> 4, cc = (tid & 15) * 8;
-    const int64_t GN = (int64_t)s.G * s.N;
-    const int64_t off = ((s.b * s.L + tbase) * s.G + s.g) * (int64_t)s.N + half * (s.N / 2) + WB * q;
+// rows (tid % 256) / 16 + 16 k, columns 8 (tid % 16) of the block (byte offset bo for k = q = 0)
+__device__ __forceinline__ void wide8_load_bc(Wide8Regs& rg, const WideSrc& s, int64_t tbase, int q, uint32_t bo) {
+    const int64_t GN = (int64_t)s.G * s.N, off = ((s.b * s.L + tbase) * s.G + s.g) * (int64_t)s.N;
+    const auto rb = tile_rsrc(s.B + off, GN, s.L - tbase, s.N);
+    const auto rc = tile_rsrc(s.C + off, GN, s.L - tbase, s.N);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        rg.b[k] = ld_row(s.B + off, GN, r0 + 16 * k, last, cc);
-        rg.c[k] = ld_row(s.C + off, GN, r0 + 16 * k, last, cc);
+        const uint32_t o = bo + (uint32_t)((16 * k * GN + WB * q) * 2);
+        rg.b[k] = ldbuf(rb, o);
+        rg.c[k] = ldbuf(rc, o);
     }
 }
 
@@ -480,9 +494,11 @@ chunk_scan_wide8_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     src.x = x, src.B = B, src.C = C, src.ds = ds, src.b = b, src.L = L, src.H = H, src.G = G, src.N = N, src.h = h,
     src.g = g;
     src.dt0 = FWD ? ((b * H + h) * nsubT + c * (Q / QS)) * QS : ((b * H + h) * nC + c) * Q;
+    const uint32_t xo = (uint32_t)(((tid >> 3) * (int64_t)H * P + (tid & 7) * 8) * 2);
+    const uint32_t bo = (uint32_t)((((tid & 255) >> 4) * (int64_t)G * N + (tid >> 8) * (N / 2) + (tid & 15) * 8) * 2);
     Wide8Regs rg;
-    wide8_load_x(rg, src, t0, 0, tid);
-    wide8_load_bc(rg, src, t0, 0, tid);
+    wide8_load_x(rg, src, t0, 0, tid, xo);
+    wide8_load_bc(rg, src, t0, 0, bo);
     const int64_t HP_ = (int64_t)H * P;
     const float* px = reinterpret_cast<const float*>(&sm.bs[0][0]);  // partial-output exchange area
 
@@ -494,11 +510,11 @@ chunk_scan_wide8_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
         if (tid < 64) wide_decay_store<FWD>(sm.lw, sm.dtw, sm.ww, sm.ec, sm.alpha, rg.dt, rg.cs, cs_prev, tot, tid);
         wide8_store_bc(sm, rg, tid);
         __syncthreads();
-        if (more) wide8_load_x(rg, src, tbase + QS, sc + 1, tid);
+        if (more) wide8_load_x(rg, src, tbase + QS, sc + 1, tid, xo);
         if (NP > 1)
-            wide8_load_bc(rg, src, tbase, 1, tid);
+            wide8_load_bc(rg, src, tbase, 1, bo);
         else if (more)
-            wide8_load_bc(rg, src, tbase + QS, 0, tid);
+            wide8_load_bc(rg, src, tbase + QS, 0, bo);
 
         Frag<bf16> xw[2];  // decay-scaled X^T fragments of p-tile pt
 #pragma unroll
@@ -526,9 +542,9 @@ chunk_scan_wide8_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
                 wide8_store_bc(sm, rg, tid);
                 __syncthreads();
                 if (q + 1 < NP)
-                    wide8_load_bc(rg, src, tbase, q + 1, tid);
+                    wide8_load_bc(rg, src, tbase, q + 1, bo);
                 else if (more)
-                    wide8_load_bc(rg, src, tbase + QS, 0, tid);
+                    wide8_load_bc(rg, src, tbase + QS, 0, bo);
             }
             // C.B^T tiles w8 and w8 + 8 (of the ten in the lower triangle) over both blocks
 #pragma unroll
@@ -672,7 +688,7 @@ chunk_state_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     src.h = h, src.g = g;
     src.dt0 = FWD ? ((b * H + h) * nsubT + c * (Q / QS)) * QS : ((b * H + h) * nC + c) * Q;
     WideAddr ad;
-    wide_addr(ad, tid);
+    wide_addr(ad, src, tid);
     WideRegs rg;
     wide_load_x(rg, ad, src, t0, 0, tid);
     wide_load_bc<false>(rg, ad, src, t0, 0);
