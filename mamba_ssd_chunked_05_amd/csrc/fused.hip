@@ -55,16 +55,14 @@ struct ChunkRegs {
     float cs;   // chunk cumulative log2 decay of that token
 };
 
-// Per-thread staging offsets within one sub-chunk tile, in elements from the
-// tile's first element (32-bit: a tile spans 64 tokens).  Chunk k of a thread
-// is chunk (tid + 256 k) of the tile: x chunk k covers head k / 2, rows
-// (tid / 8) + 32 (k % 2); B / C chunk k covers row tid / (N / 8) + k * RPI.
-// The tile bases themselves are wavefront-uniform pointers (TileBase), so each
-// load is a scalar base plus this vector offset plus a uniform constant.
+// Per-thread staging offsets within one sub-chunk tile, in bytes from the tile's first element (32-bit: a
+// tile spans 64 tokens).  Chunk k of a thread is chunk (tid + 256 k) of the tile: x chunk k covers head
+// k / 2, rows (tid / 8) + 32 (k % 2); B / C chunk k covers row tid / (N / 8) + k * RPI.  The tiles are
+// read through wavefront-uniform buffer resources, so each load is a resource plus this offset plus a
+// uniform constant.
 template <int N, int HPW>
 struct ChunkAddr {
-    uint32_t xo, bo, dto;  // this thread's first x element, B/C element, dt/cs element
-    int xr, br;            // first x / B row of this thread within the sub-chunk
+    uint32_t xo, bo, dto;  // byte offsets of this thread's first x and B/C piece; dt/cs element
     int xl, bl, cl;        // LDS element offsets of the first x / B / C chunk
 };
 
@@ -85,12 +83,10 @@ template <int N, int HPW>
 __device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int H, int G, int64_t dt_head, int tid) {
     constexpr int BS = Strides<N>::BS, CS = Strides<N>::CS;
     const int xr = tid >> 3, xc = (tid & 7) * 8;
-    a.xr = xr;
-    a.xo = (uint32_t)(xr * H * P + xc);
+    a.xo = (uint32_t)(xr * H * P + xc) * 2u;
     a.xl = xr * XS + xc;
     const int br = tid / (N / 8), bc = (tid % (N / 8)) * 8;
-    a.br = br;
-    a.bo = (uint32_t)(br * G * N + bc);
+    a.bo = (uint32_t)(br * G * N + bc) * 2u;
     a.bl = br * BS + bc;
     a.cl = br * CS + bc;
     const int hh = tid >> 6, r = tid & 63;
@@ -112,73 +108,26 @@ __device__ __forceinline__ TileBase tile_base(const bf16* x, const bf16* B, cons
     return t;
 }
 
-__device__ __forceinline__ uint4 ldb16(const void* base, uint32_t off) {
-    return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
-}
-
-// Load one sub-chunk into registers; rows past L read as zero (last = index of the
-// last valid row, used when the sub-chunk is ragged).
+// Load one sub-chunk into registers; rows past the sequence end read as zero (rows = L - tile start).
 template <int N, int HPW, bool WITH_C>
 __device__ __forceinline__ void chunk_load(ChunkRegs<N, HPW, WITH_C>& rg, const ChunkAddr<N, HPW>& a,
-                                           const TileBase& t, bool full, int last, int H, int G, int tid) {
+                                           const TileBase& t, int64_t rows, int H, int G, int tid) {
     constexpr int RPI = BRows<N>::RPI;
     const uint32_t HP_ = (uint32_t)(H * P), GN = (uint32_t)(G * N);
-    if (N >= 128 && full) {
-        // byte offsets from the scalar tile bases, made opaque per call: every load stays a scalar
-        // base plus one 32-bit vector offset instead of a 64-bit per-lane pointer that the compiler
-        // would carry (and spill) across the sub-chunk loop (measured: 1.2-1.5% faster at dstate
-        // 128, 2-3% slower at dstate 64, which keeps the element-offset form below)
-        uint32_t xo = a.xo * 2u, bo = a.bo * 2u, dto = a.dto * 4u;
-        asm volatile("" : "+v"(xo), "+v"(bo), "+v"(dto));
-        if (tid < 64 * HPW) {
-            rg.dt = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(t.dt) + dto);
-            rg.cs = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(t.cs) + dto);
-        }
-#pragma unroll
-        for (int k = 0; k < 2 * HPW; ++k) rg.x[k] = ldb16(t.x, xo + ((k & 1) * 32 * HP_ + (k >> 1) * P) * 2u);
-#pragma unroll
-        for (int k = 0; k < N / 32; ++k) rg.b[k] = ldb16(t.b, bo + k * RPI * GN * 2u);
-        if (WITH_C) {
-#pragma unroll
-            for (int k = 0; k < N / 32; ++k) rg.c[k] = ldb16(t.c, bo + k * RPI * GN * 2u);
-        }
-        return;
-    }
     if (tid < 64 * HPW) {  // dt_t and cs cover every position of the chunk (zero-padded past L)
         rg.dt = t.dt[a.dto];
         rg.cs = t.cs[a.dto];
     }
-    if (full) {
+    const auto rx = tile_rsrc(t.x, HP_, rows, HPW * P);
+    const auto rb = tile_rsrc(t.b, GN, rows, N);
 #pragma unroll
-        for (int k = 0; k < 2 * HPW; ++k) rg.x[k] = ld16(t.x + a.xo + ((k & 1) * 32 * HP_ + (k >> 1) * P));
+    for (int k = 0; k < 2 * HPW; ++k) rg.x[k] = ldbuf(rx, a.xo + ((k & 1) * 32 * HP_ + (k >> 1) * P) * 2u);
 #pragma unroll
-        for (int k = 0; k < N / 32; ++k) rg.b[k] = ld16(t.b + a.bo + k * RPI * GN);
-        if (WITH_C) {
+    for (int k = 0; k < N / 32; ++k) rg.b[k] = ldbuf(rb, a.bo + k * RPI * GN * 2u);
+    if (WITH_C) {
+        const auto rc = tile_rsrc(t.c, GN, rows, N);
 #pragma unroll
-            for (int k = 0; k < N / 32; ++k) rg.c[k] = ld16(t.c + a.bo + k * RPI * GN);
-        }
-    } else {
-        // ragged last sub-chunk: clamp the row to the last valid one, then select zero
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-        for (int k = 0; k < 2 * HPW; ++k) {
-            const int r = a.xr + (k & 1) * 32;
-            const bool ok = r <= last;
-            const uint4 v = ld16(t.x + (a.xo + (uint32_t)((ok ? r : last) - a.xr) * HP_ + (k >> 1) * P));
-            rg.x[k] = ok ? v : z;
-        }
-#pragma unroll
-        for (int k = 0; k < N / 32; ++k) {
-            const int r = a.br + k * RPI;
-            const bool ok = r <= last;
-            const uint32_t off = a.bo + (uint32_t)((ok ? r : last) - a.br) * GN;
-            const uint4 v = ld16(t.b + off);
-            rg.b[k] = ok ? v : z;
-            if (WITH_C) {
-                const uint4 u = ld16(t.c + off);
-                rg.c[k] = ok ? u : z;
-            }
-        }
+        for (int k = 0; k < N / 32; ++k) rg.c[k] = ldbuf(rc, a.bo + k * RPI * GN * 2u);
     }
 }
 
@@ -298,8 +247,8 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     ChunkAddr<N, HPW> ad;
     chunk_addr<N, HPW>(ad, H, G, dt_head, tid);
     ChunkRegs<N, HPW, true> rg;
-    chunk_load<N, HPW, true>(rg, ad, tile_base<true>(x, B, C, ds, dt0, b, L, H, G, N, h0, g, t0, 0), t0 + QS <= L,
-                             (int)(L - 1 - t0), H, G, tid);
+    chunk_load<N, HPW, true>(rg, ad, tile_base<true>(x, B, C, ds, dt0, b, L, H, G, N, h0, g, t0, 0), L - t0, H, G,
+                             tid);
     // this thread's output element offset within a sub-chunk's y tile (row l16, columns 16w + 4g4 ..)
     const uint32_t yo = (uint32_t)(l16 * H * P + 16 * w + 4 * g4);
 
@@ -312,7 +261,7 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
         if (sc + 1 < nsub) {
             const int64_t t1 = tbase + QS;
             chunk_load<N, HPW, true>(rg, ad, tile_base<true>(x, B, C, ds, dt0, b, L, H, G, N, h0, g, t1, sc + 1),
-                                     t1 + QS <= L, (int)(L - 1 - t1), H, G, tid);
+                                     L - t1, H, G, tid);
         }
 
         // ---- phase 1: C.B^T tiles, decayed per head -> LDS in fragment order ----------------
@@ -418,7 +367,8 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
                     bf16x4 o;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(acc[hh][r]);
-                    // 32-bit byte offset from a scalar base (dstate 128; see chunk_load)
+                    // a 32-bit byte offset from a scalar base at dstate 128 (measured 1.2-1.5% faster there and
+                    // 2-3% slower at dstate 64 than the element offset)
                     if (N >= 128)
                         *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(y + ((b * L + tbase) * H + h0) * (int64_t)P) +
                                                    (yo + (uint32_t)((16 * it * H + hh) * P)) * 2u) = o;
@@ -518,8 +468,8 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     ChunkAddr<N, HPW> ad;
     chunk_addr<N, HPW>(ad, H, G, dt_head, tid);
     ChunkRegs<N, HPW, false> rg;
-    chunk_load<N, HPW, false>(rg, ad, tile_base<false>(x, B, nullptr, ds, dt0, b, L, H, G, N, h0, g, t0, 0),
-                              t0 + QS <= L, (int)(L - 1 - t0), H, G, tid);
+    chunk_load<N, HPW, false>(rg, ad, tile_base<false>(x, B, nullptr, ds, dt0, b, L, H, G, N, h0, g, t0, 0), L - t0,
+                              H, G, tid);
 
     for (int sc = 0; sc < nsub; ++sc) {
         const int64_t tbase = t0 + (int64_t)sc * QS;
@@ -531,7 +481,7 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
             const int64_t t1 = tbase + QS;
             chunk_load<N, HPW, false>(rg, ad,
                                       tile_base<false>(x, B, nullptr, ds, dt0, b, L, H, G, N, h0, g, t1, sc + 1),
-                                      t1 + QS <= L, (int)(L - 1 - t1), H, G, tid);
+                                      L - t1, H, G, tid);
         }
 
 #pragma unroll

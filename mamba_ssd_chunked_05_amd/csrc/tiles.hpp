@@ -42,6 +42,23 @@ __device__ __forceinline__ bf16x4 cvt4(const f32x4& v) {
 
 __device__ __forceinline__ uint4 ld16(const bf16* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Sub-chunk tiles are read through buffer resources: a resource starts at the tile's first element and
+// its size ends with the last row inside the sequence (row_len elements of the last row), so the
+// hardware's range check returns zero for rows past the end (whole 16-byte pieces: a row is in range
+// entirely or not at all) and no load reaches past it.  Each load is then a wavefront-uniform resource
+// plus one 32-bit per-thread byte offset, with no per-element select.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* base, int64_t row_stride, int64_t rows,
+                                                           int row_len) {
+    const int64_t n = rows < QS ? rows : QS;
+    const int bytes = n > 0 ? (int)(((n - 1) * row_stride + row_len) * 2) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ldbuf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // dt (fp32) and the cumulative log2 decay: over the chunk for the staged calls,
 // restarting at every 64-token sub-chunk in the forward.
 struct DtSrc {

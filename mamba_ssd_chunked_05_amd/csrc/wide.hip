@@ -53,23 +53,6 @@ struct WideSrc {
     int H, G, N, h, g;
 };
 
-// Sub-chunk tiles are read through buffer resources: a resource starts at the tile's first element and
-// its size ends with the last row inside the sequence, so the hardware's range check returns zero for
-// rows past the end (whole 16-byte pieces: a row is in range entirely or not at all) and no load
-// reaches past it.  Each load is then a wavefront-uniform resource plus one 32-bit per-thread byte
-// offset, with no per-element select.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* base, int64_t row_stride, int64_t rows,
-                                                           int row_len) {
-    const int64_t n = rows < QS ? rows : QS;
-    const int bytes = n > 0 ? (int)(((n - 1) * row_stride + row_len) * 2) : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 ldbuf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 // x, dt and cs of sub-chunk `sub` starting at token tbase
 __device__ __forceinline__ void wide_load_x(WideRegs& rg, const WideAddr& a, const WideSrc& s, int64_t tbase, int sub,
                                             int tid) {
