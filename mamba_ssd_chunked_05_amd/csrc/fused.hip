@@ -3,12 +3,13 @@
 //
 // They compute exactly the staged calls of the cuTile Mamba-2 page (devotd.net,
 // section 2): the chunk-local states, and the chunk output from the chunk-start
-// state.  Inside a chunk they walk 64-token sub-chunks in order, which is the
-// same recurrence regrouped once more ("3.3 Hardware-Aware algorithms ...",
-// section 4.1, associativity):
+// state.  Inside a chunk they walk 64-token sub-chunks, which is the same
+// recurrence regrouped once more ("3.3 Hardware-Aware algorithms ...", section
+// 4.1, associativity):
 //
-//   chunk_state_fast_kernel  per (b, chunk, head pair): S <- 2^(l_63) S + B^T (w x)
-//                            per sub-chunk, from S = 0, with the scaled operand
+//   chunk_state_fast_kernel  per (b, chunk, head pair): S = sum_j B_j (outer) (w_j x_j)
+//                            over the chunk's tokens with w_j = 2^(l_end - l_j) dt_j,
+//                            sub-chunks walked from the last, with the scaled operand
 //                            split into hi + lo bf16 parts (fp32-level state).
 //   chunk_scan_fast_kernel   per (b, chunk, head pair): carry the fp32 state in
 //                            registers from the chunk-start state; per sub-chunk
@@ -418,24 +419,55 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
 }
 
 // ---------------------------------------------------------------------------
-// segment-state kernel: the state each segment produces from zero (hi/lo)
+// chunk-state kernel: the state each chunk produces from zero (hi/lo)
 // ---------------------------------------------------------------------------
 template <int N, int HPW>
 struct AggLds {
     bf16 xs[HPW * QS * XS];
     bf16 bs[QS * Strides<N>::BS];
-    float lw[HPW * QS];
-    float dtw[HPW * QS];
-    float ww[HPW * QS];
-    float alpha[4];
+    float ww[HPW * QS];  // 2^(l_end - l_j) dt_j: token j's weight in the chunk's end state
 };
 
-// FWD: the forward's variant -- reads sub-chunk-local decay arrays and also
-// writes each chunk's total log2 decay to totals (b, H, nC).
+// registers -> LDS for the chunk-state kernel, and each token's weight in the state at the chunk's
+// end (one wavefront per head).  FWD: the decay arrays restart at every sub-chunk, the sub-chunks are
+// walked from the last, `after` holds the log2 decay from this sub-chunk's end to the chunk's end and
+// tot accumulates the chunk's total.  Otherwise cs is cumulative over the chunk and cs_end is its
+// value at the chunk's last position (flat past the sequence end, where dt is zero).
+template <int N, int HPW, bool FWD>
+__device__ __forceinline__ void state_store(bf16* xs, bf16* bsm, float* ww, const ChunkRegs<N, HPW, false>& rg,
+                                            const ChunkAddr<N, HPW>& a, float& after, float cs_end, float& tot,
+                                            int tid) {
+    constexpr int RPI = BRows<N>::RPI, BS = Strides<N>::BS;
+#pragma unroll
+    for (int k = 0; k < 2 * HPW; ++k)
+        *reinterpret_cast<uint4*>(xs + a.xl + (k >> 1) * QS * XS + (k & 1) * 32 * XS) = rg.x[k];
+#pragma unroll
+    for (int k = 0; k < N / 32; ++k) *reinterpret_cast<uint4*>(bsm + a.bl + k * RPI * BS) = rg.b[k];
+    if (tid < 64 * HPW) {
+        float e;  // log2 decay from this token to the chunk's end
+        if (FWD) {
+            const float last = __shfl(rg.cs, 63, 64);
+            e = after + (last - rg.cs);
+            after += last;
+            tot += last;
+        } else {
+            e = cs_end - rg.cs;
+        }
+        ww[(tid >> 6) * QS + (tid & 63)] = fast_exp2(e) * rg.dt;
+    }
+}
+
+// Every token's contribution reaches the chunk's end through one weight, 2^(l_end - l_j) dt_j, so
+// the state is a plain sum over the chunk's tokens: S = sum_j B_j (outer) (w_j x_j), accumulated in
+// the MFMA registers with no per-sub-chunk decay of the partial state.  The sub-chunks are walked from
+// the last to the first, which makes each sub-chunk's distance to the chunk's end known when its
+// weights are formed.
+// FWD: the forward's variant -- reads sub-chunk-local decay arrays and also writes each chunk's total
+// log2 decay to totals (b, H, nC).
 template <int N, int HPW, bool FWD>
 __global__ void __launch_bounds__(256, 2)
-chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, DtSrc ds, float* __restrict__ states, float* __restrict__ totals, int64_t L, int H, int G, int Q,
-                        int64_t nC, uint32_t nitems) {
+chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, DtSrc ds, float* __restrict__ states,
+                        float* __restrict__ totals, int64_t L, int H, int G, int Q, int64_t nC, uint32_t nitems) {
     constexpr int NT = N / 16;
     constexpr int BS = Strides<N>::BS;
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -453,7 +485,6 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     const int64_t t0 = c * Q;
     const int64_t t_end = t0 + Q < L ? t0 + Q : L;
     const int nsub = (int)((t_end - t0 + QS - 1) / QS);
-    float cs_prev = 0.0f, tot = 0.0f;
 
     f32x4 st[HPW][NT];
 #pragma unroll
@@ -465,34 +496,28 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     const int64_t nsubT = (L + QS - 1) / QS;
     const int64_t dt_head = FWD ? nsubT * QS : nC * Q;  // dt/cs distance between heads
     const int64_t dt0 = FWD ? ((b * H + h0) * nsubT + c * (Q / QS)) * QS : ((b * H + h0) * nC + c) * Q;
+    float after = 0.0f, tot = 0.0f, cs_end = 0.0f;
+    if (!FWD && tid < 64 * HPW) cs_end = ds.cs[dt0 + (int64_t)(tid >> 6) * dt_head + (Q - 1)];
     ChunkAddr<N, HPW> ad;
     chunk_addr<N, HPW>(ad, H, G, dt_head, tid);
     ChunkRegs<N, HPW, false> rg;
-    chunk_load<N, HPW, false>(rg, ad, tile_base<false>(x, B, nullptr, ds, dt0, b, L, H, G, N, h0, g, t0, 0), L - t0,
-                              H, G, tid);
+    {
+        const int64_t tl = t0 + (int64_t)(nsub - 1) * QS;
+        chunk_load<N, HPW, false>(rg, ad, tile_base<false>(x, B, nullptr, ds, dt0, b, L, H, G, N, h0, g, tl, nsub - 1),
+                                  L - tl, H, G, tid);
+    }
 
-    for (int sc = 0; sc < nsub; ++sc) {
-        const int64_t tbase = t0 + (int64_t)sc * QS;
+    for (int sc = nsub - 1; sc >= 0; --sc) {
         __syncthreads();
-        chunk_store<N, HPW, false, FWD>(sm.xs, sm.bs, nullptr, sm.lw, sm.dtw, sm.ww, nullptr, sm.alpha, rg, ad,
-                                        cs_prev, tot, tid);
+        state_store<N, HPW, FWD>(sm.xs, sm.bs, sm.ww, rg, ad, after, cs_end, tot, tid);
         __syncthreads();
-        if (sc + 1 < nsub) {
-            const int64_t t1 = tbase + QS;
+        if (sc > 0) {
+            const int64_t t1 = t0 + (int64_t)(sc - 1) * QS;
             chunk_load<N, HPW, false>(rg, ad,
-                                      tile_base<false>(x, B, nullptr, ds, dt0, b, L, H, G, N, h0, g, t1, sc + 1),
+                                      tile_base<false>(x, B, nullptr, ds, dt0, b, L, H, G, N, h0, g, t1, sc - 1),
                                       L - t1, H, G, tid);
         }
 
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-            const float alpha = sm.alpha[hh];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) st[hh][nt][r] *= alpha;
-            }
-        }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             Frag<bf16> xh[HPW], xl[HPW];
