@@ -633,14 +633,38 @@ chunk_scan_wide8_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
 }
 
 // ---------------------------------------------------------------------------
-// chunk-local states (hi + lo split of the decay-scaled operand, as in fused.hip)
+// chunk-local states (hi + lo split of the scaled operand, as in fused.hip): every token's contribution
+// reaches the chunk's end through one weight 2^(l_end - l_j) dt_j, so the state is a plain sum over the
+// chunk's tokens with no per-sub-chunk decay of the partial state; the sub-chunks are walked from the
+// last, which makes each one's distance to the chunk's end known when its weights are formed
 // ---------------------------------------------------------------------------
 struct WideAggLds {
     bf16 xs[QS * XS];
     bf16 bs[QS * WBS];
-    float lw[QS], dtw[QS], ww[QS];
-    float alpha[4];
+    float ww[QS];  // 2^(l_end - l_j) dt_j
 };
+
+// x to LDS and the sub-chunk's weights (wavefront 0, lane = token).  FWD: the decay arrays restart at
+// every sub-chunk and `after` holds the log2 decay from this sub-chunk's end to the chunk's end; tot
+// accumulates the chunk's total.  Otherwise cs is cumulative over the chunk, cs_end its last value.
+template <bool FWD>
+__device__ __forceinline__ void wide_state_store_x(bf16* xs, float* ww, const WideRegs& rg, const WideAddr& a,
+                                                   float& after, float cs_end, float& tot, int tid) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4*>(xs + (a.xr + 32 * k) * XS + a.xc) = rg.x[k];
+    if (tid < 64) {
+        float e;  // log2 decay from this token to the chunk's end
+        if (FWD) {
+            const float last = __shfl(rg.cs, 63, 64);
+            e = after + (last - rg.cs);
+            after += last;
+            tot += last;
+        } else {
+            e = cs_end - rg.cs;
+        }
+        ww[tid] = fast_exp2(e) * rg.dt;
+    }
+}
 
 template <int N, bool FWD>
 __global__ void __launch_bounds__(256, 2)
@@ -660,7 +684,6 @@ chunk_state_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     const int64_t t_end = t0 + Q < L ? t0 + Q : L;
     const int nsub = (int)((t_end - t0 + QS - 1) / QS);
     const int64_t nsubT = (L + QS - 1) / QS;
-    float cs_prev = 0.0f, tot = 0.0f;
 
     f32x4 st[NT];
 #pragma unroll
@@ -670,24 +693,29 @@ chunk_state_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     src.x = x, src.B = B, src.C = nullptr, src.ds = ds, src.b = b, src.L = L, src.H = H, src.G = G, src.N = N,
     src.h = h, src.g = g;
     src.dt0 = FWD ? ((b * H + h) * nsubT + c * (Q / QS)) * QS : ((b * H + h) * nC + c) * Q;
+    float after = 0.0f, tot = 0.0f, cs_end = 0.0f;
+    if (!FWD && tid < 64) cs_end = ds.cs[src.dt0 + (Q - 1)];
     WideAddr ad;
     wide_addr(ad, src, tid);
     WideRegs rg;
-    wide_load_x(rg, ad, src, t0, 0, tid);
-    wide_load_bc<false>(rg, ad, src, t0, 0);
+    {
+        const int64_t tl = t0 + (int64_t)(nsub - 1) * QS;
+        wide_load_x(rg, ad, src, tl, nsub - 1, tid);
+        wide_load_bc<false>(rg, ad, src, tl, 0);
+    }
 
-    for (int sc = 0; sc < nsub; ++sc) {
+    for (int sc = nsub - 1; sc >= 0; --sc) {
         const int64_t tbase = t0 + (int64_t)sc * QS;
-        const bool more = sc + 1 < nsub;
+        const bool more = sc > 0;
         __syncthreads();
-        wide_store_x<FWD>(sm.xs, sm.lw, sm.dtw, sm.ww, nullptr, sm.alpha, rg, ad, cs_prev, tot, tid);
+        wide_state_store_x<FWD>(sm.xs, sm.ww, rg, ad, after, cs_end, tot, tid);
         wide_store_bc<false>(sm.bs, nullptr, rg, ad);
         __syncthreads();
-        if (more) wide_load_x(rg, ad, src, tbase + QS, sc + 1, tid);
+        if (more) wide_load_x(rg, ad, src, tbase - QS, sc - 1, tid);
         if (NBLK > 1)
             wide_load_bc<false>(rg, ad, src, tbase, 1);
         else if (more)
-            wide_load_bc<false>(rg, ad, src, tbase + QS, 0);
+            wide_load_bc<false>(rg, ad, src, tbase - QS, 0);
 
         Frag<bf16> xh[2], xl[2];
 #pragma unroll
@@ -706,7 +734,6 @@ chunk_state_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
                 xl[ks].v[4 + r] = static_cast<bf16>(v1 - static_cast<float>(h1v));
             }
         }
-        const float alpha = sm.alpha[0];
 #pragma unroll
         for (int nb = 0; nb < NBLK; ++nb) {
             if (nb > 0) {
@@ -716,12 +743,7 @@ chunk_state_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
                 if (nb + 1 < NBLK)
                     wide_load_bc<false>(rg, ad, src, tbase, nb + 1);
                 else if (more)
-                    wide_load_bc<false>(rg, ad, src, tbase + QS, 0);
-            }
-#pragma unroll
-            for (int nt = 0; nt < WB / 16; ++nt) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) st[nb * (WB / 16) + nt][r] *= alpha;
+                    wide_load_bc<false>(rg, ad, src, tbase - QS, 0);
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
