@@ -540,7 +540,7 @@ def main():
             "workload": f"cfg4: ssd_step b={bb} H={hh} P={pp} N={nn} bf16 io, fp32 state, 64 steps",
             "us_per_step": step_ms * 1e3,
             "tokens_per_s": bb / (step_ms / 1e3),
-            "roofline": {"kernel": "step_kernel<bf16>", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+            "roofline": {"kernel": "step_lane_kernel<bf16> (dstate 128: 32 lanes per state row)", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": step_bytes},
             "note": "the 168 MB state fits the 256 MB Infinity Cache, so back-to-back steps can exceed HBM rate; "
                     "the cold object times single steps after a 512 MiB cache-evicting write",
