@@ -141,8 +141,9 @@ __device__ __forceinline__ float dpp_add(float v) {
 // cross-lane shuffles between rows.
 template <int N4>
 __device__ __forceinline__ float group_sum(float v) {
-    if (N4 >= 2) v = dpp_add<0xB1>(v);  // quad_perm [1, 0, 3, 2]: lane ^ 1
-    if (N4 >= 4) v = dpp_add<0x4E>(v);  // quad_perm [2, 3, 0, 1]: lane ^ 2
+    static_assert(N4 >= 4 && N4 <= 64 && (N4 & (N4 - 1)) == 0, "groups of 4 to 64 lanes");
+    v = dpp_add<0xB1>(v);  // quad_perm [1, 0, 3, 2]: lane ^ 1
+    v = dpp_add<0x4E>(v);  // quad_perm [2, 3, 0, 1]: lane ^ 2
     if (N4 == 8) v += __shfl_xor(v, 4, 64);
     if (N4 >= 16) {
         v = dpp_add<0x124>(v);  // row_ror 4
@@ -153,12 +154,13 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-// The same update for dstate N = 4 N4 with N4 a power of two up to 64.  Thread t owns the four state
-// columns n = 4 (t % N4) .. + 3 of rows t / N4 + k (256 / N4), k < kStepK, of the block, so it needs
-// only its own four values of B and of C and the x of its rows, loaded straight into registers; each
-// row lies in N4 consecutive lanes of one wavefront, which reduce its C . S with cross-lane shuffles.
-// No LDS and no barrier.  The few small loads go out first and the state loads right after them, so
-// the update of row k waits only for its own state piece (the load counter retires in issue order).
+// The same update for dstate N = 4 N4 with N4 a power of two from 4 to 64 (dstate 16 to 256).
+// Thread t owns the four state columns n = 4 (t % N4) .. + 3 of rows t / N4 + k (256 / N4), k < kStepK,
+// of the block, so it needs only its own four values of B and of C and the x of its rows, loaded
+// straight into registers; each row lies in N4 consecutive lanes of one wavefront, which reduce its
+// C . S with cross-lane moves.  No LDS and no barrier.  The few small loads go out first and the state
+// loads right after them, so the update of row k waits only for its own state piece (the load counter
+// retires in issue order).
 template <class T, int N4>
 __global__ void __launch_bounds__(256) step_lane_kernel(DtFront fe, float* __restrict__ state,
                                                         const T* __restrict__ x, const T* __restrict__ dt,
@@ -215,7 +217,7 @@ __global__ void __launch_bounds__(256) step_lane_kernel(DtFront fe, float* __res
 
 static bool step_lane_ok(const Shape& s) {
     const int64_t n4 = s.N / 4;
-    return s.N % 4 == 0 && n4 >= 1 && n4 <= 64 && (n4 & (n4 - 1)) == 0;
+    return s.N % 4 == 0 && n4 >= 4 && n4 <= 64 && (n4 & (n4 - 1)) == 0;
 }
 
 template <class T>
@@ -232,8 +234,6 @@ static void launch_step_lane(const Shape& s, const DtFront& fe, float* state, co
         hipLaunchKernelGGL((step_lane_kernel<T, n4>), grid, block, 0, st, fe, state, xt, dtt, A, Bt, Ct, D, yt, H, \
                            P, G, RB, sx, sdt, sbc);                                                               \
         break;
-        SSD_STEP_LANE(1)
-        SSD_STEP_LANE(2)
         SSD_STEP_LANE(4)
         SSD_STEP_LANE(8)
         SSD_STEP_LANE(16)

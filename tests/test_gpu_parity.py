@@ -217,10 +217,16 @@ def test_step_matches_forward(gpu_ssd):
     assert_close_state(host(S), ref["final"])
 
 
-@pytest.mark.parametrize("P,N,dtype", [(16, 16, "f32"), (64, 48, "bf16"), (32, 512, "bf16"), (256, 1024, "f32"),
-                                       (128, 256, "bf16")])
-def test_step_shapes(gpu_ssd, P, N, dtype):
-    fi = make_forward_inputs(3, 3, 5, P, N, 1, dtype, 113, h0_std=0.2)
+# dstate 4 N4 with N4 a power of two up to 64 takes the lane kernel (whole rows per workgroup: 4096 / N,
+# at most P); the others the LDS-staged one.  Headdims that are not a multiple of the rows per workgroup
+# leave a partial last block (48 = 32 + 16 at N = 128, 80 = 64 + 16 at N = 64, 144 = 128 + 16 at N = 32),
+# and 48 rows at N = 16 are fewer than one pass of 256 threads covers (64).
+@pytest.mark.parametrize("P,N,dtype,G", [(16, 16, "f32", 1), (64, 48, "bf16", 1), (32, 512, "bf16", 1),
+                                         (256, 1024, "f32", 1), (128, 256, "bf16", 1), (48, 128, "bf16", 1),
+                                         (80, 64, "f32", 1), (112, 256, "bf16", 2), (48, 16, "f32", 2),
+                                         (144, 32, "bf16", 2), (64, 32, "bf16", 1)])
+def test_step_shapes(gpu_ssd, P, N, dtype, G):
+    fi = make_forward_inputs(3, 3, 4 if G == 2 else 5, P, N, G, dtype, 113, h0_std=0.2)
     ref = oracle.forward(fi.x, fi.dt, fi.A, fi.B, fi.C, fi.D, fi.h0)
     S = dev(fi.h0)
     ys = [host(gpu_ssd.step(S, dev(fi.x[:, t], dtype), dev(fi.dt[:, t], dtype), dev(fi.A), dev(fi.B[:, t], dtype),
