@@ -29,6 +29,7 @@ SOURCES = [
     "wide.hip",
     "selective.hip",
     "backward.hip",
+    "decay_grad.hip",
     "noalloc.hip",
     "calib.hip",
 ]

@@ -27,35 +27,46 @@
 namespace ssd {
 namespace bwd {
 
-// out[b, t, j, k] = in[b, rev ? L-1-t : t, j / rep, k] (fp32 or bf16 out); four consecutive k per thread
+// out[b, pad + t, j, k] = in[b, rev ? L-1-t : t, j / rep, k] and zero for the first pad rows (fp32 or bf16
+// out, L + pad rows); four consecutive k per thread
 template <class T, class O>
 __global__ void __launch_bounds__(256) copy_kernel(const T* __restrict__ in, O* __restrict__ out, int64_t b,
-                                                   int64_t L, int J, int K, int rep, int rev, int64_t n4) {
+                                                   int64_t L, int J, int K, int rep, int rev, int64_t pad,
+                                                   int64_t n4) {
     const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i4 >= n4) return;
-    const int64_t e = i4 * 4;
+    const int64_t e = i4 * 4, Lo = L + pad;
     const int k = (int)(e % K);
     const int j = (int)((e / K) % J);
-    const int64_t t = (e / ((int64_t)K * J)) % L;
-    const int64_t bb = e / ((int64_t)K * J * L);
+    const int64_t to = (e / ((int64_t)K * J)) % Lo;
+    const int64_t bb = e / ((int64_t)K * J * Lo);
+    if (to < pad) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[e + r] = from_f32<O>(0.0f);
+        return;
+    }
+    const int64_t t = to - pad;
     const int64_t ts = rev ? L - 1 - t : t;
     const int64_t src = ((bb * L + ts) * (J / rep) + j / rep) * K + k;
 #pragma unroll
     for (int r = 0; r < 4; ++r) out[e + r] = from_f32<O>(to_f32(in[src + r]));
 }
 
-// decay steps of the reversed scans: d'[b, tau, h] = dt[b, L - tau, h] for tau >= 1, 0 at tau = 0;
-// and the forward steps as fp32
+// decay steps of the reversed scans, behind pad rows of zero: d'[b, pad + tau, h] = dt[b, L - tau, h] for
+// tau >= 1, 0 at tau = 0 (L + pad rows); and the forward steps as fp32 (L rows)
 template <class T>
 __global__ void __launch_bounds__(256) steps_kernel(const T* __restrict__ dt, float* __restrict__ drev,
-                                                    float* __restrict__ dfwd, int64_t L, int H, int64_t n) {
+                                                    float* __restrict__ dfwd, int64_t L, int64_t pad, int H,
+                                                    int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
+    const int64_t Lo = L + pad;
     const int h = (int)(i % H);
-    const int64_t tau = (i / H) % L;
-    const int64_t bb = i / ((int64_t)H * L);
-    dfwd[i] = to_f32(dt[i]);
-    drev[i] = tau == 0 ? 0.0f : to_f32(dt[(bb * L + (L - tau)) * H + h]);
+    const int64_t to = (i / H) % Lo;
+    const int64_t bb = i / ((int64_t)H * Lo);
+    const int64_t tau = to - pad;
+    drev[i] = tau <= 0 ? 0.0f : to_f32(dt[(bb * L + (L - tau)) * H + h]);
+    if (to < L) dfwd[(bb * L + to) * H + h] = to_f32(dt[(bb * L + to) * H + h]);
 }
 
 // (b, H, P, N) -> (b, H, N, P), fp32; a NULL source gives zeros
@@ -77,21 +88,33 @@ __global__ void __launch_bounds__(256) ones_kernel(float* __restrict__ dt_t, int
     dt_t[i] = pos < L ? 1.0f : 0.0f;
 }
 
+// out[i, 2h + k] = in[i, h] (k = 0, 1): per-head values for the two half-heads of every head
+__global__ void __launch_bounds__(256) dup_kernel(const float* __restrict__ in, float* __restrict__ out, int H,
+                                                  int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t r = i / (2 * H);
+    const int h2 = (int)(i % (2 * H));
+    out[i] = in[r * H + (h2 >> 1)];
+}
+
 // One workgroup per (b, t), all heads: dx = dt u + D dy; per head q = v . B (= x^T G B), d lambda =
 // C . w - dt q and dy . x; per group dB = sum_h dt v and dC = sum_h w.  Wavefront wv takes heads
 // wv, wv + 4, ... (lanes over p and n) and reads each element of u, v, w once: the group sums
 // accumulate in registers while the heads stay in one group (heads are grouped in contiguous
 // ranges, so a wavefront meets each group once) and are flushed to a per-wavefront LDS slice.
 // Without SLICES (LDS too small for them) the group sums re-read v and w in a second pass.
-template <class T, class U, bool SLICES>
+// u_r and v_r have Lr rows per batch row (time-reversed, behind Lr - L rows of padding); dlam may be
+// NULL (the chunk-local decay gradient does not use it).
+template <class T, class U, class V, bool SLICES>
 __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, const T* __restrict__ x,
                                                       const T* __restrict__ dt, const T* __restrict__ B,
                                                       const T* __restrict__ C, const float* __restrict__ D,
-                                                      const U* __restrict__ u_r, const float* __restrict__ v_r,
-                                                      const float* __restrict__ w, T* __restrict__ dx,
+                                                      const U* __restrict__ u_r, const V* __restrict__ v_r,
+                                                      const V* __restrict__ w, T* __restrict__ dx,
                                                       T* __restrict__ dB, T* __restrict__ dC, float* __restrict__ q,
                                                       float* __restrict__ dlam, float* __restrict__ dxy, int64_t L,
-                                                      int H, int P, int N, int G) {
+                                                      int64_t Lr, int H, int P, int N, int G) {
     extern __shared__ float lds[];
     float* sB = lds;                // [G][N]
     float* sC = sB + G * N;         // [G][N]
@@ -101,7 +124,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bt = blockIdx.x;  // b * L + t
     const int64_t bb = bt / L, t = bt % L;
-    const int64_t btr = bb * L + (L - 1 - t);
+    const int64_t btr = bb * Lr + (Lr - 1 - t);
     const int hpg = H / G;
     for (int e = tid; e < G * N; e += 256) {
         sB[e] = to_f32(B[bt * G * N + e]);
@@ -146,7 +169,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
         for (int k = 0; k < kMaxNL; ++k) {
             const int n = lane + 64 * k;
             if (n < N) {
-                const float vv = v_r[(btr * H + h) * N + n], ww = w[(bt * H + h) * N + n];
+                const float vv = to_f32(v_r[(btr * H + h) * N + n]), ww = to_f32(w[(bt * H + h) * N + n]);
                 sq = fmaf(vv, sB[g * N + n], sq);
                 sw = fmaf(ww, sC[g * N + n], sw);
                 if (SLICES) {
@@ -163,7 +186,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
         }
         if (lane == 0) {
             q[(bb * H + h) * L + t] = sq;
-            dlam[(bb * H + h) * L + t] = sw - d * sq;
+            if (dlam) dlam[(bb * H + h) * L + t] = sw - d * sq;
             dxy[(bb * H + h) * L + t] = sxy;
         }
     }
@@ -180,8 +203,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
         } else {
             const int g = e / N, n = e % N;
             for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
-                sb = fmaf(sdt[h], v_r[(btr * H + h) * N + n], sb);
-                sc += w[(bt * H + h) * N + n];
+                sb = fmaf(sdt[h], to_f32(v_r[(btr * H + h) * N + n]), sb);
+                sc += to_f32(w[(bt * H + h) * N + n]);
             }
         }
         dB[bt * G * N + e] = from_f32<T>(sb);
@@ -190,27 +213,28 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
 }
 
 // the combine kernel with LDS slices for the group sums when they fit, else the two-pass form
-template <class T, class U>
+template <class T, class U, class V>
 hipError_t launch_combine(const void* dy, const void* x, const void* dt, const void* B, const void* C,
-                          const float* D, const U* u_r, const float* v_r, const float* w, void* dx, void* dB,
-                          void* dC, float* q, float* dlam, float* dxy, int64_t b, int64_t L, int H, int P, int N,
-                          int G, hipStream_t st) {
+                          const float* D, const U* u_r, const V* v_r, const V* w, void* dx, void* dB,
+                          void* dC, float* q, float* dlam, float* dxy, int64_t b, int64_t L, int64_t Lr, int H, int P,
+                          int N, int G, hipStream_t st) {
     const size_t base = (size_t)(2 * G * N + H) * 4, sliced = base + (size_t)8 * G * N * 4;
     const bool slices = sliced <= 160 * 1024;
     const size_t lds = slices ? sliced : base;
-    const void* fn = slices ? (const void*)combine_kernel<T, U, true> : (const void*)combine_kernel<T, U, false>;
+    const void* fn =
+        slices ? (const void*)combine_kernel<T, U, V, true> : (const void*)combine_kernel<T, U, V, false>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     if (slices)
-        hipLaunchKernelGGL((combine_kernel<T, U, true>), dim3((unsigned)(b * L)), dim3(256), lds, st,
+        hipLaunchKernelGGL((combine_kernel<T, U, V, true>), dim3((unsigned)(b * L)), dim3(256), lds, st,
                            static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
                            static_cast<const T*>(B), static_cast<const T*>(C), D, u_r, v_r, w, static_cast<T*>(dx),
-                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, H, P, N, G);
+                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, Lr, H, P, N, G);
     else
-        hipLaunchKernelGGL((combine_kernel<T, U, false>), dim3((unsigned)(b * L)), dim3(256), lds, st,
+        hipLaunchKernelGGL((combine_kernel<T, U, V, false>), dim3((unsigned)(b * L)), dim3(256), lds, st,
                            static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
                            static_cast<const T*>(B), static_cast<const T*>(C), D, u_r, v_r, w, static_cast<T*>(dx),
-                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, H, P, N, G);
+                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, Lr, H, P, N, G);
     return hipGetLastError();
 }
 
@@ -303,6 +327,41 @@ __global__ void __launch_bounds__(256) reduce_kernel(const double* __restrict__ 
 }
 
 // dh0 = a_0 G_0 (G_0: the reversed adjoint scan's final state); with no tokens, dh0 = dfinal
+// The chunk-local decay gradient's last step, one workgroup per (b, h): ddt = q + A R per token, and the
+// partial sums dA = sum dt R, dD = sum dy . x (fp64).
+template <class T>
+__global__ void __launch_bounds__(256) finish_kernel(const float* __restrict__ q, const float* __restrict__ R,
+                                                     const float* __restrict__ dxy, const T* __restrict__ dt,
+                                                     const float* __restrict__ A, T* __restrict__ ddt,
+                                                     double* __restrict__ dA_part, double* __restrict__ dD_part,
+                                                     int64_t L, int H) {
+    __shared__ double red[2][256];
+    const int tid = threadIdx.x, h = blockIdx.x;
+    const int64_t bb = blockIdx.y, bh = bb * H + h;
+    const double Ah = A[h];
+    double da = 0.0, dd = 0.0;
+    for (int64_t t = tid; t < L; t += 256) {
+        const double r = R[bh * L + t];
+        ddt[(bb * L + t) * H + h] = from_f32<T>((float)(Ah * r + (double)q[bh * L + t]));
+        da += (double)to_f32(dt[(bb * L + t) * H + h]) * r;
+        dd += (double)dxy[bh * L + t];
+    }
+    red[0][tid] = da;
+    red[1][tid] = dd;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) {
+            red[0][tid] += red[0][tid + s];
+            red[1][tid] += red[1][tid + s];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        dA_part[bh] = red[0][0];
+        dD_part[bh] = red[1][0];
+    }
+}
+
 template <class T>
 __global__ void __launch_bounds__(256) dh0_kernel(const float* __restrict__ G0, const T* __restrict__ dt,
                                                   const float* __restrict__ A, const float* __restrict__ dfinal,
@@ -322,11 +381,12 @@ __global__ void __launch_bounds__(256) dh0_kernel(const float* __restrict__ G0, 
 inline dim3 grid1(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
 
 template <class T, class O = float>
-hipError_t copy(const void* in, O* out, int64_t b, int64_t L, int J, int K, int rep, bool rev, hipStream_t st) {
-    const int64_t n4 = b * L * J * (int64_t)K / 4;
+hipError_t copy(const void* in, O* out, int64_t b, int64_t L, int J, int K, int rep, bool rev, int64_t pad,
+                hipStream_t st) {
+    const int64_t n4 = b * (L + pad) * J * (int64_t)K / 4;
     if (n4 == 0) return hipSuccess;
     hipLaunchKernelGGL((copy_kernel<T, O>), grid1(n4), dim3(256), 0, st, static_cast<const T*>(in), out, b, L, J, K, rep,
-                       rev ? 1 : 0, n4);
+                       rev ? 1 : 0, pad, n4);
     return hipGetLastError();
 }
 
@@ -349,6 +409,136 @@ hipError_t scan_in(const Shape& s, int in_io, int xrep, const void* xin, const v
     e = launch_state_passing(s, states, cs, h0, fin, st);
     if (e != hipSuccess) return e;
     return launch_chunk_scan_in(s, in_io, xrep, xin, Bin, Cin, dt_t, cs, states, nullptr, y, st);
+}
+
+// The backward with the decay gradient formed chunk by chunk (decay_grad.hip), for bf16 io with headdim
+// 64 and dstate 64 or 128.  The decay gradient then needs no long suffix sum, so the transposed scans
+// (c) and (d), which only feed dB, dC and q, run in bf16 compute.  The reversed copies are front-padded
+// to whole chunks, so that every reversed chunk is a forward chunk read backwards and the adjoint
+// scan's chunk-start states are the adjoints entering the forward chunks.
+hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, const void* dt, const float* A,
+                     const void* B, const void* C, const float* D, const float* h0, const void* dy,
+                     const float* dfinal, void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0,
+                     char* ws, hipStream_t st) {
+    using T = bf16;
+    const int64_t b = s.b, L = s.L, Lr = f.Lr, pad = f.Lr - s.L;
+    const int H = (int)s.H, P = (int)s.P, N = (int)s.N, G = (int)s.G;
+    auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+    T *xr = reinterpret_cast<T*>(ws + f.xr), *dyr = reinterpret_cast<T*>(ws + f.dyr);
+    T *Cr = reinterpret_cast<T*>(ws + f.Cr), *Br = reinterpret_cast<T*>(ws + f.Br);
+    float *drev = F(f.drev), *dfwd = F(f.dfwd), *dt_t = F(f.dt_t), *cs = F(f.cs);
+    float *states = F(f.states), *states_b = F(f.states_b), *R = F(f.R), *G0 = F(f.G0), *dfT = F(f.dfT);
+    float *h0T = F(f.h0T), *finT = F(f.finT), *fscr = F(f.fscr), *q = F(f.q), *dxy = F(f.dxy);
+    T *u_r = reinterpret_cast<T*>(ws + f.u_r), *v_r = reinterpret_cast<T*>(ws + f.v_r), *w = reinterpret_cast<T*>(ws + f.w);
+    double *dA_part = reinterpret_cast<double*>(ws + f.dA_part), *dD_part = reinterpret_cast<double*>(ws + f.dD_part);
+    const int64_t PN = (int64_t)P * N;
+    hipError_t e;
+#define BWD_CHECK(expr)                \
+    do {                               \
+        e = (expr);                    \
+        if (e != hipSuccess) return e; \
+    } while (0)
+    BWD_CHECK((copy<T, T>(x, xr, b, L, H, P, 1, true, pad, st)));
+    BWD_CHECK((copy<T, T>(dy, dyr, b, L, H, P, 1, true, pad, st)));
+    BWD_CHECK((copy<T, T>(C, Cr, b, L, G, N, 1, true, pad, st)));
+    BWD_CHECK((copy<T, T>(B, Br, b, L, G, N, 1, true, pad, st)));
+    hipLaunchKernelGGL(steps_kernel<T>, grid1(b * Lr * H), dim3(256), 0, st, static_cast<const T*>(dt), drev, dfwd, L,
+                       pad, H, b * Lr * H);
+    BWD_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(transpose_kernel, grid1(b * H * PN), dim3(256), 0, st, dfinal, dfT, P, N, b * H * PN);
+    BWD_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(transpose_kernel, grid1(b * H * PN), dim3(256), 0, st, h0, h0T, P, N, b * H * PN);
+    BWD_CHECK(hipGetLastError());
+
+    const DtFront none{nullptr, 0, 0, 0, 0.0f, 0.0f};
+    Shape sf = s;  // the forward direction: decay arrays from fp32 steps, bf16 chunk kernels
+    sf.io = 0;
+    Shape s16 = s;
+    Shape sr = s;  // the reversed direction over Lr tokens (nC chunks, as forwards)
+    sr.L = Lr;
+    sr.io = 0;
+    Shape sr16 = sr;
+    sr16.io = 1;
+    Shape sT16 = s;  // the transposed scans: headdim N, dstate P, one group per head, bf16 compute
+    sT16.P = N;
+    sT16.N = P;
+    sT16.G = H;
+    const int hpg = H / G;
+    // reversed direction: decay steps d', input step 1
+    BWD_CHECK(launch_chunk_cumsum(sr, none, drev, A, dt_t, cs, st));
+    hipLaunchKernelGGL(ones_kernel, grid1(b * H * s.nC * s.Q), dim3(256), 0, st, dt_t, Lr, (int)s.Q, s.nC,
+                       b * H * s.nC * s.Q);
+    BWD_CHECK(hipGetLastError());
+    // (b) the adjoint: u (dx), its final value G0 (dh0) and the chunk-start adjoints kept in states_b
+    BWD_CHECK(scan(sr16, dyr, Cr, Br, dt_t, cs, states_b, dfinal, G0, u_r, st));
+    // (c) G^T read out through x: v (dB, q), on the fast chunk kernels as nh H heads of headdim 64 (nh = N / 64:
+    // at dstate 128 each head splits into two half-heads, the two halves of the state's N rows, which form
+    // one head pair) whose x is (that half of) B or C of the head's group
+    const int nh = N / 64;
+    const XMap xm{nh * G, nh * hpg, nh};
+    Shape sh = sT16;
+    sh.H = nh * H;
+    sh.P = 64;
+    sh.N = P;
+    sh.G = H;
+    sh.L = Lr;
+    sh.Q = f.Qt;
+    sh.nC = (Lr + f.Qt - 1) / f.Qt;
+    Shape shf = sh;  // their decay arrays come from fp32 steps
+    shf.io = 0;
+    float *d2 = F(f.d2), *A2 = F(f.A2), *dt2 = F(f.dt2), *cs2 = F(f.cs2);
+    const float* Ah = A;  // A and the steps per (half-)head
+    const float* drh = drev;
+    if (nh == 2) {
+        hipLaunchKernelGGL(dup_kernel, grid1(2 * H), dim3(256), 0, st, A, A2, H, (int64_t)2 * H);
+        BWD_CHECK(hipGetLastError());
+        hipLaunchKernelGGL(dup_kernel, grid1(b * Lr * 2 * H), dim3(256), 0, st, drev, d2, H, b * Lr * 2 * H);
+        BWD_CHECK(hipGetLastError());
+        Ah = A2;
+        drh = d2;
+    }
+    BWD_CHECK(launch_chunk_cumsum(shf, none, drh, Ah, dt2, cs2, st));
+    hipLaunchKernelGGL(ones_kernel, grid1(b * sh.H * sh.nC * sh.Q), dim3(256), 0, st, dt2, Lr, (int)sh.Q, sh.nC,
+                       b * sh.H * sh.nC * sh.Q);
+    BWD_CHECK(hipGetLastError());
+    BWD_CHECK(launch_chunk_state_fast(sh, Cr, dyr, dt2, cs2, states, st, &xm));
+    BWD_CHECK(launch_state_passing(sh, states, cs2, dfT, fscr, st));
+    BWD_CHECK(launch_chunk_scan_fast(sh, Cr, dyr, xr, dt2, cs2, states, nullptr, v_r, st, &xm));
+    // forward direction: the chunk-start states S0 (hi/lo chunk states, fp32 pass), then the decay gradient
+    BWD_CHECK(launch_chunk_cumsum(sf, none, dfwd, A, dt_t, cs, st));
+    BWD_CHECK(launch_chunk_state(s16, x, B, dt_t, cs, states, st));
+    BWD_CHECK(launch_state_passing(s16, states, cs, h0, fscr, st));
+    BWD_CHECK(launch_decay_grad(s16, x, dy, B, C, cs, dt_t, states, states_b, R, st));
+    // (d) S^T read out through dy: w (dC), as half-heads like (c), forwards in time
+    sh.L = L;
+    sh.nC = (L + f.Qt - 1) / f.Qt;
+    shf = sh;
+    shf.io = 0;
+    const float* dfh = dfwd;
+    if (nh == 2) {
+        hipLaunchKernelGGL(dup_kernel, grid1(b * L * 2 * H), dim3(256), 0, st, dfwd, d2, H, b * L * 2 * H);
+        BWD_CHECK(hipGetLastError());
+        dfh = d2;
+    }
+    BWD_CHECK(launch_chunk_cumsum(shf, none, dfh, Ah, dt2, cs2, st));
+    BWD_CHECK(launch_chunk_state_fast(sh, B, x, dt2, cs2, states, st, &xm));
+    BWD_CHECK(launch_state_passing(sh, states, cs2, h0 ? h0T : nullptr, finT, st));
+    BWD_CHECK(launch_chunk_scan_fast(sh, B, x, dy, dt2, cs2, states, nullptr, w, st, &xm));
+
+    BWD_CHECK((launch_combine<T, bf16, bf16>(dy, x, dt, B, C, D, u_r, v_r, w, dx, dB, dC, q, nullptr, dxy, b, L, Lr, H,
+                                             P, N, G, st)));
+    hipLaunchKernelGGL(finish_kernel<T>, dim3((unsigned)H, (unsigned)b), dim3(256), 0, st, q, R, dxy,
+                       static_cast<const T*>(dt), A, static_cast<T*>(ddt), dA_part, dD_part, L, H);
+    BWD_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(reduce_kernel, grid1(H), dim3(256), 0, st, dA_part, dD_part, dA, dD, b, H);
+    BWD_CHECK(hipGetLastError());
+    if (dh0) {
+        hipLaunchKernelGGL(dh0_kernel<T>, grid1(b * H * PN), dim3(256), 0, st, G0, static_cast<const T*>(dt), A,
+                           dfinal, dh0, L, H, PN, b * H * PN);
+        BWD_CHECK(hipGetLastError());
+    }
+#undef BWD_CHECK
+    return hipSuccess;
 }
 
 template <class T>
@@ -385,12 +575,12 @@ hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const voi
         return hipSuccess;
     }
     // time-reversed copies for the reversed scans, in the input dtype
-    BWD_CHECK((copy<T, T>(x, xr, b, L, H, P, 1, true, st)));
-    BWD_CHECK((copy<T, T>(dy, dyr, b, L, H, P, 1, true, st)));
-    BWD_CHECK((copy<T, T>(C, Cr, b, L, G, N, 1, true, st)));
-    BWD_CHECK((copy<T, T>(B, Br, b, L, G, N, 1, true, st)));
+    BWD_CHECK((copy<T, T>(x, xr, b, L, H, P, 1, true, 0, st)));
+    BWD_CHECK((copy<T, T>(dy, dyr, b, L, H, P, 1, true, 0, st)));
+    BWD_CHECK((copy<T, T>(C, Cr, b, L, G, N, 1, true, 0, st)));
+    BWD_CHECK((copy<T, T>(B, Br, b, L, G, N, 1, true, 0, st)));
     hipLaunchKernelGGL(steps_kernel<T>, grid1(b * L * H), dim3(256), 0, st, static_cast<const T*>(dt), drev, dfwd, L,
-                       H, b * L * H);
+                       (int64_t)0, H, b * L * H);
     BWD_CHECK(hipGetLastError());
     hipLaunchKernelGGL(transpose_kernel, grid1(b * H * PN), dim3(256), 0, st, dfinal, dfT, P, N, b * H * PN);
     BWD_CHECK(hipGetLastError());
@@ -428,11 +618,11 @@ hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const voi
 
     // combine
     if (fastb)
-        BWD_CHECK((launch_combine<T, bf16>(dy, x, dt, B, C, D, reinterpret_cast<const bf16*>(u_r), v_r, w, dx, dB, dC, q,
-                                           dlam, dxy, b, L, H, P, N, G, st)));
+        BWD_CHECK((launch_combine<T, bf16, float>(dy, x, dt, B, C, D, reinterpret_cast<const bf16*>(u_r), v_r, w, dx, dB,
+                                                  dC, q, dlam, dxy, b, L, L, H, P, N, G, st)));
     else
-        BWD_CHECK((launch_combine<T, float>(dy, x, dt, B, C, D, u_r, v_r, w, dx, dB, dC, q, dlam, dxy, b, L, H, P, N, G,
-                                            st)));
+        BWD_CHECK((launch_combine<T, float, float>(dy, x, dt, B, C, D, u_r, v_r, w, dx, dB, dC, q, dlam, dxy, b, L, L, H,
+                                                   P, N, G, st)));
     hipLaunchKernelGGL(suffix_kernel<T>, dim3((unsigned)H, (unsigned)b), dim3(256), 0, st, dlam, q, dxy,
                        static_cast<const T*>(dt), A, dfinal, finT, static_cast<T*>(ddt), dA_part, dD_part, L, H, P,
                        N);
@@ -450,25 +640,51 @@ hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const voi
 
 }  // namespace bwd
 
+// Chunk of the transposed scans of the local flow, run as (N / 64) H heads of headdim and dstate 64: the
+// forward's rule for that shape, at least the backward's chunk (so their states fit the space of its
+// chunk states).
+static int64_t transposed_chunk(const Shape& s) {
+    Shape h = s;
+    h.H = s.N / 64 * s.H;
+    h.P = 64;
+    h.N = 64;
+    h.G = s.H;
+    const int64_t q = fast_forward_chunk(h);
+    return q < s.Q ? s.Q : q;
+}
+
 BackwardLayout backward_layout(const Shape& s) {
     auto a256 = [](size_t v) { return (v + 255) / 256 * 256; };
     BackwardLayout f{};
+    f.local = decay_grad_supported(s);
+    f.Lr = f.local ? s.nC * s.Q : s.L;  // the reversed copies: front-padded to whole chunks when local
     const size_t sz = s.io == 1 ? 2 : 4;  // the reversed copies keep the input dtype
     const size_t BLHP = (size_t)(s.b * s.L * s.H * s.P) * 4, BLHN = (size_t)(s.b * s.L * s.H * s.N) * 4;
-    const size_t BLGN = (size_t)(s.b * s.L * s.G * s.N), BLH = (size_t)(s.b * s.L * s.H) * 4;
+    const size_t RLHP = (size_t)(s.b * f.Lr * s.H * s.P) * 4, RLHN = (size_t)(s.b * f.Lr * s.H * s.N) * 4;
+    const size_t RLGN = (size_t)(s.b * f.Lr * s.G * s.N), BLH = (size_t)(s.b * s.L * s.H) * 4;
+    const size_t RLH = (size_t)(s.b * f.Lr * s.H) * 4;
     const size_t CS = (size_t)(s.b * s.H * s.nC * s.Q) * 4, ST = (size_t)(s.b * s.nC * s.H * s.P * s.N) * 4;
     const size_t HS = (size_t)(s.b * s.H * s.P * s.N) * 4, BH8 = (size_t)(s.b * s.H) * 8;
+    (void)BLHP;
     size_t o = 0;
     auto take = [&](size_t bytes) {
         const size_t at = o;
         o += a256(bytes);
         return at;
     };
-    f.xr = take(BLHP / 4 * sz), f.dyr = take(BLHP / 4 * sz), f.Cr = take(BLGN * sz), f.Br = take(BLGN * sz);
-    f.drev = take(BLH), f.dfwd = take(BLH), f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST);
-    f.u_r = take(BLHP), f.v_r = take(BLHN), f.w = take(BLHN);
+    f.xr = take(RLHP / 4 * sz), f.dyr = take(RLHP / 4 * sz), f.Cr = take(RLGN * sz), f.Br = take(RLGN * sz);
+    f.drev = take(RLH), f.dfwd = take(BLH), f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST);
+    f.u_r = take(RLHP), f.v_r = take(RLHN), f.w = take(BLHN);
     f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS), f.fscr = take(HS);
-    f.q = take(BLH), f.dlam = take(BLH), f.dxy = take(BLH), f.dA_part = take(BH8), f.dD_part = take(BH8);
+    f.q = take(BLH), f.dlam = take(f.local ? 0 : BLH), f.dxy = take(BLH), f.dA_part = take(BH8), f.dD_part = take(BH8);
+    f.states_b = take(f.local ? ST : 0), f.R = take(f.local ? BLH : 0);
+    // the half-head transposed scans (local flow): per half-head steps, A, and chunk cumsum arrays at their chunk
+    f.Qt = f.local ? transposed_chunk(s) : 0;
+    const int64_t nct = f.local ? (f.Lr + f.Qt - 1) / f.Qt : 0;
+    const int64_t nhh = s.N / 64 * s.H;  // heads of the transposed scans
+    f.d2 = take(f.local ? (size_t)(s.b * f.Lr * nhh) * 4 : 0), f.A2 = take(f.local ? (size_t)nhh * 4 : 0);
+    f.dt2 = take(f.local ? (size_t)(s.b * nhh * nct * f.Qt) * 4 : 0);
+    f.cs2 = take(f.local ? (size_t)(s.b * nhh * nct * f.Qt) * 4 : 0);
     f.total = o;
     return f;
 }
@@ -479,6 +695,8 @@ hipError_t launch_backward(const Shape& s, const void* x, const void* dt, const 
                            hipStream_t st) {
     const BackwardLayout f = backward_layout(s);
     char* ws = static_cast<char*>(workspace);
+    if (s.io == 1 && f.local && s.b > 0 && s.L > 0)
+        return bwd::run_local(s, f, x, dt, A, B, C, D, h0, dy, dfinal, dx, ddt, dA, dB, dC, dD, dh0, ws, st);
     if (s.io == 1)
         return bwd::run<bf16>(s, f, x, dt, A, B, C, D, h0, dy, dfinal, dx, ddt, dA, dB, dC, dD, dh0, ws, st);
     return bwd::run<float>(s, f, x, dt, A, B, C, D, h0, dy, dfinal, dx, ddt, dA, dB, dC, dD, dh0, ws, st);

@@ -1,0 +1,307 @@
+// decay_grad.hip -- the backward's decay gradient, chunk by chunk.
+//
+// The loss depends on the log-decay only through differences, so its gradient
+// at token k is R_k = sum_{t>=k} dlambda_t, and the identity
+//     R_k = a_k <G_k, S_{k-1}>                (a_k = 2^(dt_k A log2 e))
+// with S the forward state and G the adjoint ("3.3 Hardware-Aware algorithms
+// and GPU memory hierarchy optimisation", section 6: the backward recomputes
+// states instead of storing them) turns that long suffix sum, whose terms
+// nearly cancel over the whole sequence, into a sum of chunk-local terms.  With
+// S0 the forward state entering chunk [c0, c1], Gam the adjoint entering it from
+// the next chunk (a_{c1+1} G_{c1+1}; dfinal for the last chunk) and l the
+// in-chunk cumulative log2 decay:
+//   T1   = 2^(l_c1) <Gam, S0>                                   (one per chunk)
+//   T2_k = sum_{t>=k} 2^(l_t) dy_t . (S0 C_t)                    (suffix sum)
+//   T3_k = sum_{j<k} dt_j 2^(l_c1 - l_j) x_j . (Gam B_j)         (prefix sum)
+//   T4_k = sum_{t>=k>j} M_tj,  M_tj = (dy_t . x_j)(C_t . B_j) 2^(l_t - l_j) dt_j
+//   R_k  = T1 + T2_k + T3_k + T4_k
+// (substituting both chunk-local expansions into a_k <G_k, S_{k-1}>; the
+// decays combine as a_k 2^(l_{k-1}) = 2^(l_k)).  T4 follows from the column and
+// row sums of the strictly lower triangle of M: T4_{k+1} = T4_k + colsum_k -
+// rowsum_k.  Each term is accurate relative to itself, so the decay gradient
+// no longer needs fp32 scans: dy . x and C . B are exact bf16 products with
+// fp32 accumulation, and S0 and Gam enter the MFMA split into hi + lo bf16.
+//
+// One workgroup (four wavefronts) per (b, chunk, head); headdim 64, dstate 64
+// or 128, chunk 64 or 128.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssd {
+namespace dg {
+
+constexpr int P = 64;
+constexpr int QMAX = 128;
+constexpr int XS = P + 16;  // x / dy row stride (bf16): 16-byte fragment reads of 16 rows
+
+struct Lds {
+    bf16 xs[QMAX * XS];
+    bf16 ys[QMAX * XS];   // dy
+    float lw[QMAX];       // in-chunk cumulative log2 decay (flat past the sequence end)
+    float dtw[QMAX];      // dt (zero past the sequence end)
+    float rowsum[QMAX];
+    float colsum[QMAX];
+    float s2[QMAX];       // dy_t . (S0 C_t), before the factor 2^(l_t)
+    float s3[QMAX];       // x_j . (Gam B_j), before dt_j 2^(l_c1 - l_j)
+    float red[4];
+};
+
+// a buffer resource over rows [0, rows) of a row-major bf16 tile (row_stride elements apart, row_len
+// elements read per row); rows past it read zero
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* base, int64_t row_stride, int rows,
+                                                           int row_len) {
+    const int bytes = rows > 0 ? (int)(((int64_t)(rows - 1) * row_stride + row_len) * 2) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ldr(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// 8 fp32 values -> hi and lo bf16 fragments
+__device__ __forceinline__ void split8(const float4& a, const float4& b, Frag<bf16>& hi, Frag<bf16>& lo) {
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const bf16 h = static_cast<bf16>(v[s]);
+        hi.v[s] = h;
+        lo.v[s] = static_cast<bf16>(v[s] - static_cast<float>(h));
+    }
+}
+
+// R (b, H, L) fp32.  cs / dtv: the forward chunk cumsum arrays (b, H, nC, Q) (log2 units; dt, zero past
+// L); S0: forward chunk-start states (b, nC, H, P, N); Gst: the reversed adjoint scan's chunk-start
+// states (b, nC, H, P, N) in reversed chunk order, so forward chunk c reads reversed chunk nC - 1 - c:
+// the adjoint G_{c1+1} of the token after the chunk (dfinal for the last chunk), which enters decayed
+// by that token's factor 2^(cs of the next chunk's first position).
+//
+// Wavefront w holds rows 16 w .. 16 w + 15 of S0 and of Gam in registers (hi + lo bf16 fragments, read
+// once), so it forms the state terms for those 16 of the P output columns over every token of the
+// chunk; the four wavefronts' parts meet in LDS.  x and dy of the head sit in LDS; B and C, shared by
+// the heads of a group, are read as MFMA fragments straight from the cache.
+template <int N>
+__global__ void __launch_bounds__(256) decay_grad_kernel(const bf16* __restrict__ x, const bf16* __restrict__ dy,
+                                                         const bf16* __restrict__ B, const bf16* __restrict__ C,
+                                                         const float* __restrict__ cs,
+                                                         const float* __restrict__ dtv,
+                                                         const float* __restrict__ S0,
+                                                         const float* __restrict__ Gst, float* __restrict__ R,
+                                                         int64_t L, int H, int G, int Q, int64_t nC,
+                                                         uint32_t nitems) {
+    constexpr int NK = N / 32;
+    __shared__ Lds sm;
+    const uint32_t item = xcd_remap(blockIdx.x, nitems);
+    const int h = (int)(item % (uint32_t)H);
+    const int64_t c = (item / (uint32_t)H) % (uint32_t)nC;
+    const int64_t b = item / ((uint32_t)H * (uint32_t)nC);
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int QT = Q / 16;
+    const int64_t c0 = c * Q;
+    const int valid = (int)(L - c0 < Q ? L - c0 : Q);  // tokens of this chunk inside the sequence
+
+    // ---- loads: x and dy pieces (zero past the sequence end), this wavefront's state rows -----------
+    const int64_t HP = (int64_t)H * P;
+    const auto rx = rows_rsrc(x + ((b * L + c0) * H + h) * (int64_t)P, HP, valid, P);
+    const auto ry = rows_rsrc(dy + ((b * L + c0) * H + h) * (int64_t)P, HP, valid, P);
+    constexpr int KX = QMAX * (P / 8) / 256;  // x (and dy) pieces per thread at the largest chunk
+    uint4 vx[KX], vy[KX];
+    const int xr0 = tid >> 3, xc = (tid & 7) * 8;
+#pragma unroll
+    for (int k = 0; k < KX; ++k) {
+        const uint32_t off = (uint32_t)(((int64_t)(xr0 + 32 * k) * HP + xc) * 2);
+        vx[k] = ldr(rx, off);
+        vy[k] = ldr(ry, off);
+    }
+    const float* S0c = S0 + ((b * nC + c) * H + h) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 8 * g4;
+    const float* Gc = Gst + ((b * nC + (nC - 1 - c)) * H + h) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 8 * g4;
+    float4 sa[NK][2], ga[NK][2];
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+        sa[ks][0] = *reinterpret_cast<const float4*>(S0c + 32 * ks);
+        sa[ks][1] = *reinterpret_cast<const float4*>(S0c + 32 * ks + 4);
+        ga[ks][0] = *reinterpret_cast<const float4*>(Gc + 32 * ks);
+        ga[ks][1] = *reinterpret_cast<const float4*>(Gc + 32 * ks + 4);
+    }
+    const int64_t base = ((b * H + h) * nC + c) * Q;
+    if (tid < Q) {
+        sm.lw[tid] = cs[base + tid];
+        sm.dtw[tid] = dtv[base + tid];
+        sm.rowsum[tid] = 0.0f;
+        sm.colsum[tid] = 0.0f;
+        sm.s2[tid] = 0.0f;
+        sm.s3[tid] = 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < KX; ++k) {
+        if (xr0 + 32 * k < Q) {
+            *reinterpret_cast<uint4*>(&sm.xs[(xr0 + 32 * k) * XS + xc]) = vx[k];
+            *reinterpret_cast<uint4*>(&sm.ys[(xr0 + 32 * k) * XS + xc]) = vy[k];
+        }
+    }
+    // T1 part over this lane's state values, and the hi / lo fragments
+    float dot = 0.0f;
+    Frag<bf16> sh[NK], sl[NK], gh[NK], gl[NK];
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const float4 u = sa[ks][q], v = ga[ks][q];
+            dot = fmaf(u.x, v.x, fmaf(u.y, v.y, fmaf(u.z, v.z, fmaf(u.w, v.w, dot))));
+        }
+        split8(sa[ks][0], sa[ks][1], sh[ks], sl[ks]);
+        split8(ga[ks][0], ga[ks][1], gh[ks], gl[ks]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+    if (lane == 0) sm.red[w] = dot;
+    __syncthreads();
+
+    // B and C rows of this chunk (group g), read as fragments from the cache; rows past the end read zero
+    const int64_t GN = (int64_t)G * N;
+    const auto rb = rows_rsrc(B + ((b * L + c0) * G + g) * (int64_t)N, GN, valid, N);
+    const auto rc = rows_rsrc(C + ((b * L + c0) * G + g) * (int64_t)N, GN, valid, N);
+    auto frag_bc = [&](__amdgpu_buffer_rsrc_t r, int row, int ks) {
+        Frag<bf16> f;
+        const uint4 v = ldr(r, (uint32_t)(((int64_t)row * GN + 32 * ks + 8 * g4) * 2));
+        f.v = __builtin_bit_cast(bf16x8, v);
+        return f;
+    };
+
+    // ---- T2 and T3 for this wavefront's 16 output columns p = 16 w + l16, every token tile -------------
+    for (int it = 0; it < QT; ++it) {
+        Frag<bf16> cf[NK], bf[NK];
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+            cf[ks] = frag_bc(rc, 16 * it + l16, ks);
+            bf[ks] = frag_bc(rb, 16 * it + l16, ks);
+        }
+        f32x4 a2 = {0.f, 0.f, 0.f, 0.f}, a3 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+            mma(a2, cf[ks], sh[ks]);
+            mma(a2, cf[ks], sl[ks]);
+            mma(a3, bf[ks], gh[ks]);
+            mma(a3, bf[ks], gl[ks]);
+        }
+        // a2[r] = (S0 C_t)_p, a3[r] = (Gam B_t)_p for t = 16 it + 4 g4 + r, p = 16 w + l16
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * it + 4 * g4 + r;
+            const float v2 = sum16(static_cast<float>(sm.ys[t * XS + 16 * w + l16]) * a2[r]);
+            const float v3 = sum16(static_cast<float>(sm.xs[t * XS + 16 * w + l16]) * a3[r]);
+            if (l16 == 0) {
+                atomicAdd(&sm.s2[t], v2);
+                atomicAdd(&sm.s3[t], v3);
+            }
+        }
+    }
+
+    // ---- T4: the strictly lower triangle of M, tile by tile, into row and column sums -------------
+    const int ntiles = QT * (QT + 1) / 2;
+    for (int tt = w; tt < ntiles; tt += 4) {
+        int it = 0;
+        while ((it + 1) * (it + 2) / 2 <= tt) ++it;
+        const int jt = tt - it * (it + 1) / 2;
+        Frag<bf16> cf[NK], bf[NK];
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+            cf[ks] = frag_bc(rc, 16 * it + l16, ks);
+            bf[ks] = frag_bc(rb, 16 * jt + l16, ks);
+        }
+        f32x4 ad = {0.f, 0.f, 0.f, 0.f}, ac = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < P / 32; ++ks) {
+            Frag<bf16> a, bo;
+            frag_load8<bf16>(a, &sm.ys[(16 * it + l16) * XS + 32 * ks + 8 * g4]);
+            frag_load8<bf16>(bo, &sm.xs[(16 * jt + l16) * XS + 32 * ks + 8 * g4]);
+            mma(ad, a, bo);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) mma(ac, cf[ks], bf[ks]);
+        const int j = 16 * jt + l16;
+        const float lj = sm.lw[j], dj = sm.dtw[j];
+        float colp = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * it + 4 * g4 + r;
+            // j < t only; the exponent is capped at 0 so no masked lane forms an infinity
+            const float m = j < t ? ad[r] * ac[r] * fast_exp2(fminf(sm.lw[t] - lj, 0.0f)) * dj : 0.0f;
+            colp += m;
+            const float rs = sum16(m);
+            if (l16 == 0) atomicAdd(&sm.rowsum[t], rs);
+        }
+        colp += __shfl_xor(colp, 16, 64);
+        colp += __shfl_xor(colp, 32, 64);
+        if (g4 == 0) atomicAdd(&sm.colsum[j], colp);
+    }
+    __syncthreads();
+
+    // ---- R_k = T1 + T2_k + T3_k + T4_k: one wavefront, two positions per lane ---------------------
+    if (w == 0) {
+        const float lend = sm.lw[Q - 1];
+        // the adjoint enters decayed by the next token's factor (none after the sequence's end)
+        const float gam = c + 1 < nC ? fast_exp2(cs[((b * H + h) * nC + c + 1) * Q]) : 1.0f;
+        const float T1 = fast_exp2(lend) * gam * (sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]);
+        float a2[2], a3[2], a4[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int k = 2 * lane + q;
+            const bool in = k < Q;
+            a2[q] = in ? fast_exp2(sm.lw[k]) * sm.s2[k] : 0.0f;
+            a3[q] = in ? sm.dtw[k] * fast_exp2(lend - sm.lw[k]) * gam * sm.s3[k] : 0.0f;
+            a4[q] = in ? sm.colsum[k] - sm.rowsum[k] : 0.0f;
+        }
+        // inclusive prefix sums over k of the pair sums, then per position
+        float p2 = a2[0] + a2[1], p3 = a3[0] + a3[1], p4 = a4[0] + a4[1];
+        float tot2 = p2;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float u2 = __shfl_up(p2, off, 64), u3 = __shfl_up(p3, off, 64), u4 = __shfl_up(p4, off, 64);
+            if (lane >= off) p2 += u2, p3 += u3, p4 += u4;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) tot2 += __shfl_xor(tot2, off, 64);
+        // exclusive prefix before this lane's pair
+        const float e2 = p2 - (a2[0] + a2[1]), e3 = p3 - (a3[0] + a3[1]), e4 = p4 - (a4[0] + a4[1]);
+        float* Rh = R + (b * H + h) * L + c0;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int k = 2 * lane + q;
+            // T2_k: suffix from k = total - prefix before k; T3_k, T4_k: prefix before k
+            const float pre2 = e2 + (q ? a2[0] : 0.0f), pre3 = e3 + (q ? a3[0] : 0.0f), pre4 = e4 + (q ? a4[0] : 0.0f);
+            if (k < valid) Rh[k] = T1 + (tot2 - pre2) + pre3 + pre4;
+        }
+    }
+}
+
+}  // namespace dg
+
+bool decay_grad_supported(const Shape& s) {
+    return s.io == 1 && s.P == 64 && (s.N == 64 || s.N == 128) && (s.Q == 64 || s.Q == dg::QMAX);
+}
+
+hipError_t launch_decay_grad(const Shape& s, const void* x, const void* dy, const void* B, const void* C,
+                             const float* cs, const float* dtv, const float* S0, const float* Gst, float* R,
+                             hipStream_t st) {
+    const uint32_t nitems = (uint32_t)(s.b * s.nC * s.H);
+    if (nitems == 0) return hipSuccess;
+    const bf16 *xb = (const bf16*)x, *yb = (const bf16*)dy, *bb = (const bf16*)B, *cb = (const bf16*)C;
+    if (s.N == 128)
+        hipLaunchKernelGGL(dg::decay_grad_kernel<128>, dim3(nitems), dim3(256), 0, st, xb, yb, bb, cb, cs, dtv, S0, Gst,
+                           R, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+    else
+        hipLaunchKernelGGL(dg::decay_grad_kernel<64>, dim3(nitems), dim3(256), 0, st, xb, yb, bb, cb, cs, dtv, S0, Gst,
+                           R, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

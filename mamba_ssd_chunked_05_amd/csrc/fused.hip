@@ -79,12 +79,12 @@ struct TileBase {
     const float *dt, *cs;
 };
 
-// dt_head: distance between consecutive heads in the dt/cs arrays
+// hx: heads of the x rows; dt_head: distance between consecutive heads in the dt/cs arrays
 template <int N, int HPW>
-__device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int H, int G, int64_t dt_head, int tid) {
+__device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int hx, int G, int64_t dt_head, int tid) {
     constexpr int BS = Strides<N>::BS, CS = Strides<N>::CS;
     const int xr = tid >> 3, xc = (tid & 7) * 8;
-    a.xo = (uint32_t)(xr * H * P + xc) * 2u;
+    a.xo = (uint32_t)(xr * hx * P + xc) * 2u;
     a.xl = xr * XS + xc;
     const int br = tid / (N / 8), bc = (tid % (N / 8)) * 8;
     a.bo = (uint32_t)(br * G * N + bc) * 2u;
@@ -94,14 +94,15 @@ __device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int H, int G, i
     a.dto = (uint32_t)((hh < HPW ? hh : 0) * dt_head + r);
 }
 
-// The tiles of the sub-chunk starting at token tbase of batch row b (heads h0.., group g);
-// dt0 / cs0 point at this chunk's first position of head h0 and sub is the sub-chunk index.
+// The tiles of the sub-chunk starting at token tbase of batch row b (x heads xh0.. of hx per row,
+// group g); dt0 / cs0 point at this chunk's first position of the workgroup's first head and sub is the
+// sub-chunk index.
 template <bool WITH_C>
 __device__ __forceinline__ TileBase tile_base(const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
-                                              int64_t dt0, int64_t b, int64_t L, int H, int G, int N, int h0, int g,
+                                              int64_t dt0, int64_t b, int64_t L, int hx, int G, int N, int xh0, int g,
                                               int64_t tbase, int sub) {
     TileBase t;
-    t.x = x + ((b * L + tbase) * H + h0) * (int64_t)P;
+    t.x = x + ((b * L + tbase) * hx + xh0) * (int64_t)P;
     t.b = B + ((b * L + tbase) * G + g) * (int64_t)N;
     t.c = WITH_C ? C + ((b * L + tbase) * G + g) * (int64_t)N : nullptr;
     t.dt = ds.dt_t + dt0 + (int64_t)QS * sub;
@@ -112,9 +113,9 @@ __device__ __forceinline__ TileBase tile_base(const bf16* x, const bf16* B, cons
 // Load one sub-chunk into registers; rows past the sequence end read as zero (rows = L - tile start).
 template <int N, int HPW, bool WITH_C>
 __device__ __forceinline__ void chunk_load(ChunkRegs<N, HPW, WITH_C>& rg, const ChunkAddr<N, HPW>& a,
-                                           const TileBase& t, int64_t rows, int H, int G, int tid) {
+                                           const TileBase& t, int64_t rows, int hx, int G, int tid) {
     constexpr int RPI = BRows<N>::RPI;
-    const uint32_t HP_ = (uint32_t)(H * P), GN = (uint32_t)(G * N);
+    const uint32_t HP_ = (uint32_t)(hx * P), GN = (uint32_t)(G * N);
     if (tid < 64 * HPW) {  // dt_t and cs cover every position of the chunk (zero-padded past L)
         rg.dt = t.dt[a.dto];
         rg.cs = t.cs[a.dto];
@@ -203,7 +204,7 @@ template <int N, int HPW, bool FWD>
 __global__ void __launch_bounds__(256, 2)
 chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, const bf16* __restrict__ C,
                        DtSrc ds, const float* __restrict__ start, const float* __restrict__ D, bf16* __restrict__ y, int64_t L,
-                       int H, int G, int Q, int64_t nC, uint32_t nitems) {
+                       int H, int G, int Q, int64_t nC, uint32_t nitems, XMap xm) {
     constexpr int NT = N / 16, NK = N / 32;
     constexpr int BS = Strides<N>::BS, CS = Strides<N>::CS;
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -245,11 +246,12 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     const int64_t nsubT = (L + QS - 1) / QS;
     const int64_t dt_head = FWD ? nsubT * QS : nC * Q;  // dt/cs distance between heads
     const int64_t dt0 = FWD ? ((b * H + h0) * nsubT + c * (Q / QS)) * QS : ((b * H + h0) * nC + c) * Q;
+    const int xh0 = h0 / xm.div * xm.mul;  // the x heads of this head pair
     ChunkAddr<N, HPW> ad;
-    chunk_addr<N, HPW>(ad, H, G, dt_head, tid);
+    chunk_addr<N, HPW>(ad, xm.hx, G, dt_head, tid);
     ChunkRegs<N, HPW, true> rg;
-    chunk_load<N, HPW, true>(rg, ad, tile_base<true>(x, B, C, ds, dt0, b, L, H, G, N, h0, g, t0, 0), L - t0, H, G,
-                             tid);
+    chunk_load<N, HPW, true>(rg, ad, tile_base<true>(x, B, C, ds, dt0, b, L, xm.hx, G, N, xh0, g, t0, 0), L - t0,
+                             xm.hx, G, tid);
     // this thread's output element offset within a sub-chunk's y tile (row l16, columns 16w + 4g4 ..)
     const uint32_t yo = (uint32_t)(l16 * H * P + 16 * w + 4 * g4);
 
@@ -261,8 +263,9 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
         __syncthreads();
         if (sc + 1 < nsub) {
             const int64_t t1 = tbase + QS;
-            chunk_load<N, HPW, true>(rg, ad, tile_base<true>(x, B, C, ds, dt0, b, L, H, G, N, h0, g, t1, sc + 1),
-                                     L - t1, H, G, tid);
+            chunk_load<N, HPW, true>(rg, ad,
+                                     tile_base<true>(x, B, C, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc + 1),
+                                     L - t1, xm.hx, G, tid);
         }
 
         // ---- phase 1: C.B^T tiles, decayed per head -> LDS in fragment order ----------------
@@ -467,7 +470,8 @@ __device__ __forceinline__ void state_store(bf16* xs, bf16* bsm, float* ww, cons
 template <int N, int HPW, bool FWD>
 __global__ void __launch_bounds__(256, 2)
 chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, DtSrc ds, float* __restrict__ states,
-                        float* __restrict__ totals, int64_t L, int H, int G, int Q, int64_t nC, uint32_t nitems) {
+                        float* __restrict__ totals, int64_t L, int H, int G, int Q, int64_t nC, uint32_t nitems,
+                        XMap xm) {
     constexpr int NT = N / 16;
     constexpr int BS = Strides<N>::BS;
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -498,13 +502,15 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     const int64_t dt0 = FWD ? ((b * H + h0) * nsubT + c * (Q / QS)) * QS : ((b * H + h0) * nC + c) * Q;
     float after = 0.0f, tot = 0.0f, cs_end = 0.0f;
     if (!FWD && tid < 64 * HPW) cs_end = ds.cs[dt0 + (int64_t)(tid >> 6) * dt_head + (Q - 1)];
+    const int xh0 = h0 / xm.div * xm.mul;  // the x heads of this head pair
     ChunkAddr<N, HPW> ad;
-    chunk_addr<N, HPW>(ad, H, G, dt_head, tid);
+    chunk_addr<N, HPW>(ad, xm.hx, G, dt_head, tid);
     ChunkRegs<N, HPW, false> rg;
     {
         const int64_t tl = t0 + (int64_t)(nsub - 1) * QS;
-        chunk_load<N, HPW, false>(rg, ad, tile_base<false>(x, B, nullptr, ds, dt0, b, L, H, G, N, h0, g, tl, nsub - 1),
-                                  L - tl, H, G, tid);
+        chunk_load<N, HPW, false>(rg, ad,
+                                  tile_base<false>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, tl, nsub - 1),
+                                  L - tl, xm.hx, G, tid);
     }
 
     for (int sc = nsub - 1; sc >= 0; --sc) {
@@ -514,8 +520,8 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
         if (sc > 0) {
             const int64_t t1 = t0 + (int64_t)(sc - 1) * QS;
             chunk_load<N, HPW, false>(rg, ad,
-                                      tile_base<false>(x, B, nullptr, ds, dt0, b, L, H, G, N, h0, g, t1, sc - 1),
-                                      L - t1, H, G, tid);
+                                      tile_base<false>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc - 1),
+                                      L - t1, xm.hx, G, tid);
         }
 
 #pragma unroll
@@ -626,7 +632,7 @@ __global__ void __launch_bounds__(256) subchunk_decay_kernel(DtFront fe, const b
 
 template <int N, int HPW, bool FWD>
 hipError_t launch_state_fast(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
-                             float* totals, hipStream_t st) {
+                             float* totals, const XMap& xm, hipStream_t st) {
     const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
     if (nitems == 0) return hipSuccess;
     const size_t lds = sizeof(AggLds<N, HPW>);
@@ -634,13 +640,13 @@ hipError_t launch_state_fast(const Shape& s, const bf16* x, const bf16* B, const
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, ds, states,
-                       totals, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+                       totals, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
     return hipGetLastError();
 }
 
 template <int N, int HPW, bool FWD>
 hipError_t launch_scan_fast(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
-                            const float* start, const float* D, bf16* y, hipStream_t st) {
+                            const float* start, const float* D, bf16* y, const XMap& xm, hipStream_t st) {
     const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
     if (nitems == 0) return hipSuccess;
     const size_t lds = sizeof(ScanLds<N, HPW>);
@@ -648,7 +654,7 @@ hipError_t launch_scan_fast(const Shape& s, const bf16* x, const bf16* B, const 
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, C, ds, start,
-                       D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+                       D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
     return hipGetLastError();
 }
 
@@ -663,10 +669,10 @@ hipError_t scan_wide(const Shape& s, const bf16* x, const bf16* B, const bf16* C
 // dispatch over (N, heads per workgroup)
 template <bool FWD>
 hipError_t state_dispatch(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
-                          float* totals, hipStream_t st);
+                          float* totals, hipStream_t st, const XMap* xm = nullptr);
 template <bool FWD>
 hipError_t scan_dispatch(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
-                         const float* start, const float* D, bf16* y, hipStream_t st);
+                         const float* start, const float* D, bf16* y, hipStream_t st, const XMap* xm = nullptr);
 
 }  // namespace fz
 
@@ -715,40 +721,46 @@ namespace fz {
 
 template <bool FWD>
 hipError_t state_dispatch(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
-                          float* totals, hipStream_t st) {
+                          float* totals, hipStream_t st, const XMap* xm) {
     if (s.N >= 256) return state_wide<FWD>(s, x, B, ds, states, totals, st);
+    const XMap id{(int)s.H, 1, 1};
+    const XMap& m = xm ? *xm : id;
     const bool pair = fast_hpw(s) == 2;
     if (s.N == 128)
-        return pair ? launch_state_fast<128, 2, FWD>(s, x, B, ds, states, totals, st)
-                    : launch_state_fast<128, 1, FWD>(s, x, B, ds, states, totals, st);
-    return pair ? launch_state_fast<64, 2, FWD>(s, x, B, ds, states, totals, st)
-                : launch_state_fast<64, 1, FWD>(s, x, B, ds, states, totals, st);
+        return pair ? launch_state_fast<128, 2, FWD>(s, x, B, ds, states, totals, m, st)
+                    : launch_state_fast<128, 1, FWD>(s, x, B, ds, states, totals, m, st);
+    return pair ? launch_state_fast<64, 2, FWD>(s, x, B, ds, states, totals, m, st)
+                : launch_state_fast<64, 1, FWD>(s, x, B, ds, states, totals, m, st);
 }
 
 template <bool FWD>
 hipError_t scan_dispatch(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
-                         const float* start, const float* D, bf16* y, hipStream_t st) {
+                         const float* start, const float* D, bf16* y, hipStream_t st, const XMap* xm) {
     if (s.N >= 256) return scan_wide<FWD>(s, x, B, C, ds, start, D, y, st);
+    const XMap id{(int)s.H, 1, 1};
+    const XMap& m = xm ? *xm : id;
     const bool pair = fast_hpw(s) == 2;
     if (s.N == 128)
-        return pair ? launch_scan_fast<128, 2, FWD>(s, x, B, C, ds, start, D, y, st)
-                    : launch_scan_fast<128, 1, FWD>(s, x, B, C, ds, start, D, y, st);
-    return pair ? launch_scan_fast<64, 2, FWD>(s, x, B, C, ds, start, D, y, st)
-                : launch_scan_fast<64, 1, FWD>(s, x, B, C, ds, start, D, y, st);
+        return pair ? launch_scan_fast<128, 2, FWD>(s, x, B, C, ds, start, D, y, m, st)
+                    : launch_scan_fast<128, 1, FWD>(s, x, B, C, ds, start, D, y, m, st);
+    return pair ? launch_scan_fast<64, 2, FWD>(s, x, B, C, ds, start, D, y, m, st)
+                : launch_scan_fast<64, 1, FWD>(s, x, B, C, ds, start, D, y, m, st);
 }
 
 }  // namespace fz
 
 hipError_t launch_chunk_state_fast(const Shape& s, const void* x, const void* B, const float* dt_t, const float* cs,
-                                   float* states, hipStream_t st) {
+                                   float* states, hipStream_t st, const XMap* xm) {
     const fz::DtSrc ds{dt_t, cs};
-    return fz::state_dispatch<false>(s, (const bf16*)x, (const bf16*)B, ds, states, nullptr, st);
+    return fz::state_dispatch<false>(s, (const bf16*)x, (const bf16*)B, ds, states, nullptr, st, xm);
 }
 
 hipError_t launch_chunk_scan_fast(const Shape& s, const void* x, const void* B, const void* C, const float* dt_t,
-                                  const float* cs, const float* start, const float* D, void* y, hipStream_t st) {
+                                  const float* cs, const float* start, const float* D, void* y, hipStream_t st,
+                                  const XMap* xm) {
     const fz::DtSrc ds{dt_t, cs};
-    return fz::scan_dispatch<false>(s, (const bf16*)x, (const bf16*)B, (const bf16*)C, ds, start, D, (bf16*)y, st);
+    return fz::scan_dispatch<false>(s, (const bf16*)x, (const bf16*)B, (const bf16*)C, ds, start, D, (bf16*)y, st,
+                                    xm);
 }
 
 FastFwdLayout fast_forward_layout(const Shape& s) {

@@ -45,14 +45,22 @@ bool step_multi_on_chip(const Shape& s);
 hipError_t launch_step_multi(const Shape& s, const DtFront& fe, float* state, const void* x, const void* dt,
                              const float* A, const void* B, const void* C, const float* D, void* y, hipStream_t st);
 
+// Where the fast kernels read x: rows of hx heads, and the head pair starting at head h0 reads the x heads
+// h0 / div * mul and the next one.  The identity is {H, 1, 1}.  The backward's transposed scans run
+// 2H half-heads (the two 64-column halves of each head) whose x is B or C of the head's group:
+// {2G, 2 H / G, 2}.
+struct XMap {
+    int hx, div, mul;
+};
 // Fast chunk-state / chunk-scan kernels (bf16, headdim 64, dstate 64 or 128, chunk a multiple of 64).
 bool fast_chunk_supported(const Shape& s);
 int fast_forward_chunk(const Shape& s);   // chunk size the forward uses on the fast path
 int fast_heads_per_wg(const Shape& s);
 hipError_t launch_chunk_state_fast(const Shape& s, const void* x, const void* B, const float* dt_t, const float* cs,
-                                   float* states, hipStream_t st);
+                                   float* states, hipStream_t st, const XMap* xm = nullptr);
 hipError_t launch_chunk_scan_fast(const Shape& s, const void* x, const void* B, const void* C, const float* dt_t,
-                                  const float* cs, const float* start, const float* D, void* y, hipStream_t st);
+                                  const float* cs, const float* start, const float* D, void* y, hipStream_t st,
+                                  const XMap* xm = nullptr);
 
 // The forward on the fast path: the decay arrays restart at every 64-token
 // sub-chunk (one coalesced pass over dt), the chunk states also yield each
@@ -89,8 +97,20 @@ hipError_t launch_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, in
 // inputs.  Byte offsets of the workspace pieces (all 256-byte aligned).
 struct BackwardLayout {
     size_t xr, dyr, Cr, Br, drev, dfwd, dt_t, cs, states, u_r, v_r, w, G0, dfT, h0T, finT, fscr, q, dlam, dxy,
-        dA_part, dD_part, total;
+        dA_part, dD_part, states_b, R, d2, A2, dt2, cs2, total;
+    int64_t Qt;  // chunk of the half-head transposed scans (local flow)
+    int64_t Lr;  // rows of the time-reversed copies (the sequence, front-padded to whole chunks when local)
+    bool local;  // the decay gradient is formed chunk by chunk (decay_grad.hip)
 };
+// The chunk-local decay gradient (decay_grad.hip): bf16 io, headdim 64, dstate 64 or 128, chunk 64 or 128
+// (a multiple of 64 for the fast chunk kernels that supply its states, at most 128 for its tiles).
+bool decay_grad_supported(const Shape& s);
+// R (b, H, L): R_k = a_k <G_k, S_{k-1}> from the forward chunk cumsum arrays (cs, dt), the forward
+// chunk-start states S0 (b, nC, H, P, N) and the reversed adjoint scan's chunk-start states Gst (same
+// layout, reversed chunk order).
+hipError_t launch_decay_grad(const Shape& s, const void* x, const void* dy, const void* B, const void* C,
+                             const float* cs, const float* dtv, const float* S0, const float* Gst, float* R,
+                             hipStream_t st);
 BackwardLayout backward_layout(const Shape& s);
 hipError_t launch_backward(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
                            const void* C, const float* D, const float* h0, const void* dy, const float* dfinal,

@@ -81,6 +81,30 @@ def test_backward_stress(gpu_ssd, mode):
     _check(ref, got, "f32", tol_dA=2e-2 if mode == "extreme" else None)
 
 
+# bf16 io, headdim 64, dstate 64 or 128, chunk 64 or 128: the decay gradient is formed chunk by chunk and the
+# transposed scans run in bf16 compute.  One chunk shorter than the chunk size, a length that is a whole
+# number of chunks (no padding of the reversed copies), chunk 64, groups, with and without h0 and dfinal.
+LOCAL = [
+    (1, 40, 2, 64, 64, 1, "bf16", 64, True),
+    (2, 256, 4, 64, 128, 2, "bf16", 128, True),
+    (1, 300, 2, 64, 128, 1, "bf16", 64, False),
+    (2, 450, 6, 64, 64, 3, "bf16", 0, True),
+]
+
+
+@pytest.mark.parametrize("case", LOCAL, ids=_ids)
+def test_backward_local(gpu_ssd, case):
+    ref, got = _grads(305, case)
+    _check(ref, got, "bf16")
+
+
+@pytest.mark.parametrize("mode", ["long_memory", "extreme", "zero"])
+def test_backward_local_stress(gpu_ssd, mode):
+    """The chunk-local decay gradient under long memory, huge steps and zero steps (bf16 io)."""
+    ref, got = _grads(306, (1, 700, 4, 64, 64, 1, "bf16", 128, True), dt_mode=mode)
+    _check(ref, got, "bf16")
+
+
 def test_backward_without_D(gpu_ssd):
     ref, got = _grads(302, (2, 200, 4, 16, 32, 2, "f32", 64, True), with_D=False)
     assert got["dD"] is None
