@@ -139,6 +139,23 @@ __device__ __forceinline__ void load8_f32(const bf16* p, float out[8]) {
 }
 
 // ---------------------------------------------------------------------------
+// cross-lane sums with data-parallel moves (no trip through the LDS unit)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// the sum over each row of 16 lanes, left in every lane of the row: lane swaps inside quads
+// (quad_perm [1,0,3,2] and [2,3,0,1]), then rotations by 4 and 8 inside the row
+__device__ __forceinline__ float row16_sum(float v) {
+    v = dpp_add<0xB1>(v);
+    v = dpp_add<0x4E>(v);
+    v = dpp_add<0x124>(v);
+    return dpp_add<0x128>(v);
+}
+
+// ---------------------------------------------------------------------------
 // workgroup -> XCD-contiguous work mapping.  Workgroups are dispatched
 // round-robin over the 8 XCDs (id % 8); this bijection gives every XCD a
 // contiguous range of logical work items so that neighbours (e.g. the heads

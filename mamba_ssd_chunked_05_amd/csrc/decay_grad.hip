@@ -34,9 +34,13 @@ constexpr int P = 64;
 constexpr int QMAX = 128;
 constexpr int XS = P + 16;  // x / dy row stride (bf16): 16-byte fragment reads of 16 rows
 
+template <int N>
 struct Lds {
+    static constexpr int NS = N + 16;  // B / C row stride (bf16)
     bf16 xs[QMAX * XS];
     bf16 ys[QMAX * XS];   // dy
+    bf16 bs[QMAX * NS];
+    bf16 cs[QMAX * NS];
     float lw[QMAX];       // in-chunk cumulative log2 decay (flat past the sequence end)
     float dtw[QMAX];      // dt (zero past the sequence end)
     float rowsum[QMAX];
@@ -59,11 +63,7 @@ __device__ __forceinline__ uint4 ldr(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-__device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
+__device__ __forceinline__ float sum16(float v) { return row16_sum(v); }
 
 // 8 fp32 values -> hi and lo bf16 fragments
 __device__ __forceinline__ void split8(const float4& a, const float4& b, Frag<bf16>& hi, Frag<bf16>& lo) {
@@ -82,12 +82,12 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, Frag<bf
 // the adjoint G_{c1+1} of the token after the chunk (dfinal for the last chunk), which enters decayed
 // by that token's factor 2^(cs of the next chunk's first position).
 //
-// Wavefront w holds rows 16 w .. 16 w + 15 of S0 and of Gam in registers (hi + lo bf16 fragments, read
-// once), so it forms the state terms for those 16 of the P output columns over every token of the
-// chunk; the four wavefronts' parts meet in LDS.  x and dy of the head sit in LDS; B and C, shared by
-// the heads of a group, are read as MFMA fragments straight from the cache.
+// Eight wavefronts.  Wavefront w < 4 holds rows 16 w .. 16 w + 15 of S0, wavefront 4 + w the same rows
+// of Gam, in registers (hi + lo bf16 fragments, read once): each forms its state term for those 16 of
+// the P output columns over every token of the chunk, and the four parts of each term meet in LDS.
+// x, dy, B and C of the chunk sit in LDS; all eight share the tiles of M.
 template <int N>
-__global__ void __launch_bounds__(256) decay_grad_kernel(const bf16* __restrict__ x, const bf16* __restrict__ dy,
+__global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict__ x, const bf16* __restrict__ dy,
                                                          const bf16* __restrict__ B, const bf16* __restrict__ C,
                                                          const float* __restrict__ cs,
                                                          const float* __restrict__ dtv,
@@ -95,8 +95,8 @@ __global__ void __launch_bounds__(256) decay_grad_kernel(const bf16* __restrict_
                                                          const float* __restrict__ Gst, float* __restrict__ R,
                                                          int64_t L, int H, int G, int Q, int64_t nC,
                                                          uint32_t nitems) {
-    constexpr int NK = N / 32;
-    __shared__ Lds sm;
+    constexpr int NK = N / 32, NS = Lds<N>::NS;
+    __shared__ Lds<N> sm;
     const uint32_t item = xcd_remap(blockIdx.x, nitems);
     const int h = (int)(item % (uint32_t)H);
     const int64_t c = (item / (uint32_t)H) % (uint32_t)nC;
@@ -104,32 +104,43 @@ __global__ void __launch_bounds__(256) decay_grad_kernel(const bf16* __restrict_
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pt = w & 3;          // this wavefront's 16 state rows
+    const bool gam_half = w >= 4;  // S0 (T2) or Gam (T3)
     const int QT = Q / 16;
     const int64_t c0 = c * Q;
     const int valid = (int)(L - c0 < Q ? L - c0 : Q);  // tokens of this chunk inside the sequence
 
-    // ---- loads: x and dy pieces (zero past the sequence end), this wavefront's state rows -----------
-    const int64_t HP = (int64_t)H * P;
+    // ---- loads: x, dy, B, C pieces (zero past the sequence end), this wavefront's state rows --------
+    const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N;
     const auto rx = rows_rsrc(x + ((b * L + c0) * H + h) * (int64_t)P, HP, valid, P);
     const auto ry = rows_rsrc(dy + ((b * L + c0) * H + h) * (int64_t)P, HP, valid, P);
-    constexpr int KX = QMAX * (P / 8) / 256;  // x (and dy) pieces per thread at the largest chunk
-    uint4 vx[KX], vy[KX];
+    const auto rb = rows_rsrc(B + ((b * L + c0) * G + g) * (int64_t)N, GN, valid, N);
+    const auto rc = rows_rsrc(C + ((b * L + c0) * G + g) * (int64_t)N, GN, valid, N);
+    constexpr int KX = QMAX * (P / 8) / 512, KB = QMAX * (N / 8) / 512;  // pieces per thread, largest chunk
+    uint4 vx[KX], vy[KX], vb[KB], vc[KB];
     const int xr0 = tid >> 3, xc = (tid & 7) * 8;
+    const int br0 = tid / (N / 8), bc = (tid % (N / 8)) * 8;
+    constexpr int BR = 512 / (N / 8);  // B rows per pass of 512 threads
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
-        const uint32_t off = (uint32_t)(((int64_t)(xr0 + 32 * k) * HP + xc) * 2);
+        const uint32_t off = (uint32_t)(((int64_t)(xr0 + 64 * k) * HP + xc) * 2);
         vx[k] = ldr(rx, off);
         vy[k] = ldr(ry, off);
     }
-    const float* S0c = S0 + ((b * nC + c) * H + h) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 8 * g4;
-    const float* Gc = Gst + ((b * nC + (nC - 1 - c)) * H + h) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 8 * g4;
-    float4 sa[NK][2], ga[NK][2];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        const uint32_t off = (uint32_t)(((int64_t)(br0 + BR * k) * GN + bc) * 2);
+        vb[k] = ldr(rb, off);
+        vc[k] = ldr(rc, off);
+    }
+    const float* S0c = S0 + ((b * nC + c) * H + h) * (int64_t)P * N + (int64_t)(16 * pt + l16) * N + 8 * g4;
+    const float* Gc = Gst + ((b * nC + (nC - 1 - c)) * H + h) * (int64_t)P * N + (int64_t)(16 * pt + l16) * N + 8 * g4;
+    const float* Mine = gam_half ? Gc : S0c;
+    float4 sa[NK][2];
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
-        sa[ks][0] = *reinterpret_cast<const float4*>(S0c + 32 * ks);
-        sa[ks][1] = *reinterpret_cast<const float4*>(S0c + 32 * ks + 4);
-        ga[ks][0] = *reinterpret_cast<const float4*>(Gc + 32 * ks);
-        ga[ks][1] = *reinterpret_cast<const float4*>(Gc + 32 * ks + 4);
+        sa[ks][0] = *reinterpret_cast<const float4*>(Mine + 32 * ks);
+        sa[ks][1] = *reinterpret_cast<const float4*>(Mine + 32 * ks + 4);
     }
     const int64_t base = ((b * H + h) * nC + c) * Q;
     if (tid < Q) {
@@ -142,81 +153,68 @@ __global__ void __launch_bounds__(256) decay_grad_kernel(const bf16* __restrict_
     }
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
-        if (xr0 + 32 * k < Q) {
-            *reinterpret_cast<uint4*>(&sm.xs[(xr0 + 32 * k) * XS + xc]) = vx[k];
-            *reinterpret_cast<uint4*>(&sm.ys[(xr0 + 32 * k) * XS + xc]) = vy[k];
+        if (xr0 + 64 * k < Q) {
+            *reinterpret_cast<uint4*>(&sm.xs[(xr0 + 64 * k) * XS + xc]) = vx[k];
+            *reinterpret_cast<uint4*>(&sm.ys[(xr0 + 64 * k) * XS + xc]) = vy[k];
         }
     }
-    // T1 part over this lane's state values, and the hi / lo fragments
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        if (br0 + BR * k < Q) {
+            *reinterpret_cast<uint4*>(&sm.bs[(br0 + BR * k) * NS + bc]) = vb[k];
+            *reinterpret_cast<uint4*>(&sm.cs[(br0 + BR * k) * NS + bc]) = vc[k];
+        }
+    }
+    // T1 part: the S0 wavefronts read the matching Gam rows for the dot product only
     float dot = 0.0f;
-    Frag<bf16> sh[NK], sl[NK], gh[NK], gl[NK];
+    if (!gam_half) {
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const float4 u = sa[ks][q], v = ga[ks][q];
-            dot = fmaf(u.x, v.x, fmaf(u.y, v.y, fmaf(u.z, v.z, fmaf(u.w, v.w, dot))));
+        for (int ks = 0; ks < NK; ++ks) {
+            const float4 v0 = *reinterpret_cast<const float4*>(Gc + 32 * ks);
+            const float4 v1 = *reinterpret_cast<const float4*>(Gc + 32 * ks + 4);
+            const float4 u0 = sa[ks][0], u1 = sa[ks][1];
+            dot = fmaf(u0.x, v0.x, fmaf(u0.y, v0.y, fmaf(u0.z, v0.z, fmaf(u0.w, v0.w, dot))));
+            dot = fmaf(u1.x, v1.x, fmaf(u1.y, v1.y, fmaf(u1.z, v1.z, fmaf(u1.w, v1.w, dot))));
         }
-        split8(sa[ks][0], sa[ks][1], sh[ks], sl[ks]);
-        split8(ga[ks][0], ga[ks][1], gh[ks], gl[ks]);
-    }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-    if (lane == 0) sm.red[w] = dot;
+        for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+        if (lane == 0) sm.red[w] = dot;
+    }
+    Frag<bf16> sh[NK], sl[NK];
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) split8(sa[ks][0], sa[ks][1], sh[ks], sl[ks]);
     __syncthreads();
 
-    // B and C rows of this chunk (group g), read as fragments from the cache; rows past the end read zero
-    const int64_t GN = (int64_t)G * N;
-    const auto rb = rows_rsrc(B + ((b * L + c0) * G + g) * (int64_t)N, GN, valid, N);
-    const auto rc = rows_rsrc(C + ((b * L + c0) * G + g) * (int64_t)N, GN, valid, N);
-    auto frag_bc = [&](__amdgpu_buffer_rsrc_t r, int row, int ks) {
-        Frag<bf16> f;
-        const uint4 v = ldr(r, (uint32_t)(((int64_t)row * GN + 32 * ks + 8 * g4) * 2));
-        f.v = __builtin_bit_cast(bf16x8, v);
-        return f;
-    };
-
-    // ---- T2 and T3 for this wavefront's 16 output columns p = 16 w + l16, every token tile -------------
-    for (int it = 0; it < QT; ++it) {
-        Frag<bf16> cf[NK], bf[NK];
+    // ---- T2 (C with S0, read out by dy) or T3 (B with Gam, read out by x) for p = 16 pt + l16 ----------
+    {
+        const bf16* A = gam_half ? sm.bs : sm.cs;
+        const bf16* Dm = gam_half ? sm.xs : sm.ys;
+        float* out = gam_half ? sm.s3 : sm.s2;
+        for (int it = 0; it < QT; ++it) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NK; ++ks) {
-            cf[ks] = frag_bc(rc, 16 * it + l16, ks);
-            bf[ks] = frag_bc(rb, 16 * it + l16, ks);
-        }
-        f32x4 a2 = {0.f, 0.f, 0.f, 0.f}, a3 = {0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks < NK; ++ks) {
+                Frag<bf16> a;
+                frag_load8<bf16>(a, &A[(16 * it + l16) * NS + 32 * ks + 8 * g4]);
+                mma(acc, a, sh[ks]);
+                mma(acc, a, sl[ks]);
+            }
+            // acc[r] = (St A_t)_p for t = 16 it + 4 g4 + r
 #pragma unroll
-        for (int ks = 0; ks < NK; ++ks) {
-            mma(a2, cf[ks], sh[ks]);
-            mma(a2, cf[ks], sl[ks]);
-            mma(a3, bf[ks], gh[ks]);
-            mma(a3, bf[ks], gl[ks]);
-        }
-        // a2[r] = (S0 C_t)_p, a3[r] = (Gam B_t)_p for t = 16 it + 4 g4 + r, p = 16 w + l16
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * it + 4 * g4 + r;
-            const float v2 = sum16(static_cast<float>(sm.ys[t * XS + 16 * w + l16]) * a2[r]);
-            const float v3 = sum16(static_cast<float>(sm.xs[t * XS + 16 * w + l16]) * a3[r]);
-            if (l16 == 0) {
-                atomicAdd(&sm.s2[t], v2);
-                atomicAdd(&sm.s3[t], v3);
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * it + 4 * g4 + r;
+                const float v = sum16(static_cast<float>(Dm[t * XS + 16 * pt + l16]) * acc[r]);
+                if (l16 == 0) atomicAdd(&out[t], v);
             }
         }
     }
 
     // ---- T4: the strictly lower triangle of M, tile by tile, into row and column sums -------------
     const int ntiles = QT * (QT + 1) / 2;
-    for (int tt = w; tt < ntiles; tt += 4) {
+    for (int tt = w; tt < ntiles; tt += 8) {
         int it = 0;
         while ((it + 1) * (it + 2) / 2 <= tt) ++it;
         const int jt = tt - it * (it + 1) / 2;
-        Frag<bf16> cf[NK], bf[NK];
-#pragma unroll
-        for (int ks = 0; ks < NK; ++ks) {
-            cf[ks] = frag_bc(rc, 16 * it + l16, ks);
-            bf[ks] = frag_bc(rb, 16 * jt + l16, ks);
-        }
         f32x4 ad = {0.f, 0.f, 0.f, 0.f}, ac = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < P / 32; ++ks) {
@@ -226,7 +224,12 @@ __global__ void __launch_bounds__(256) decay_grad_kernel(const bf16* __restrict_
             mma(ad, a, bo);
         }
 #pragma unroll
-        for (int ks = 0; ks < NK; ++ks) mma(ac, cf[ks], bf[ks]);
+        for (int ks = 0; ks < NK; ++ks) {
+            Frag<bf16> a, bo;
+            frag_load8<bf16>(a, &sm.cs[(16 * it + l16) * NS + 32 * ks + 8 * g4]);
+            frag_load8<bf16>(bo, &sm.bs[(16 * jt + l16) * NS + 32 * ks + 8 * g4]);
+            mma(ac, a, bo);
+        }
         const int j = 16 * jt + l16;
         const float lj = sm.lw[j], dj = sm.dtw[j];
         float colp = 0.0f;
@@ -296,10 +299,10 @@ hipError_t launch_decay_grad(const Shape& s, const void* x, const void* dy, cons
     if (nitems == 0) return hipSuccess;
     const bf16 *xb = (const bf16*)x, *yb = (const bf16*)dy, *bb = (const bf16*)B, *cb = (const bf16*)C;
     if (s.N == 128)
-        hipLaunchKernelGGL(dg::decay_grad_kernel<128>, dim3(nitems), dim3(256), 0, st, xb, yb, bb, cb, cs, dtv, S0, Gst,
+        hipLaunchKernelGGL(dg::decay_grad_kernel<128>, dim3(nitems), dim3(512), 0, st, xb, yb, bb, cb, cs, dtv, S0, Gst,
                            R, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
     else
-        hipLaunchKernelGGL(dg::decay_grad_kernel<64>, dim3(nitems), dim3(256), 0, st, xb, yb, bb, cb, cs, dtv, S0, Gst,
+        hipLaunchKernelGGL(dg::decay_grad_kernel<64>, dim3(nitems), dim3(512), 0, st, xb, yb, bb, cb, cs, dtv, S0, Gst,
                            R, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
     return hipGetLastError();
 }

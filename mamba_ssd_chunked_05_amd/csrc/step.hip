@@ -131,11 +131,6 @@ __device__ __forceinline__ void load4(const float* p, float* f) {
 
 constexpr int kStepK = 4;  // float4 of state per thread in step_lane_kernel
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
 // Sum over each aligned group of N4 lanes, left in every lane of the group: lane swaps inside quads
 // and rotations inside 16-lane rows (data-parallel moves, no trip through the LDS unit), then
 // cross-lane shuffles between rows.
@@ -378,21 +373,6 @@ struct MultiBlock {
         }
     }
 };
-
-// Sum over the 16 lanes of a DPP row, returned in every lane of the row:
-// quad_perm [1,0,3,2] and [2,3,0,1] sum each quad, row_half_mirror pairs the
-// two quads of each half row, row_mirror pairs the two half rows.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-    v += dpp_mov<0x141>(v);  // row_half_mirror
-    v += dpp_mov<0x140>(v);  // row_mirror
-    return v;
-}
 
 template <class T, int RT, int CT>
 __global__ void __launch_bounds__(256) step_multi_kernel(DtFront fe, float* __restrict__ state, const T* __restrict__ x,
