@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
-PEAK_FP32_MFMA_TFLOPS = 157.3  # dense fp32 MFMA (the backward's scans run in fp32)
+PEAK_FP32_MFMA_TFLOPS = 157.3  # dense fp32 MFMA (the backward's scans with fp32 inputs)
 # backward FLOP per token-head in its recurrence form: state recompute (3PN), adjoint update (3PN) and
 # the four contractions G.B, G^T.x, S^T.dy and <G, S> (2PN each)
 BWD_FLOP_PER_TOKEN_HEAD_PN = 14
@@ -66,20 +66,31 @@ def backward_section(ssd, torch, dev, timed, args, cfg, x, dt, A, B, C, D, token
     bwd_ms = timed(bwd, max(3, args.steps // 4))
     bflop = BWD_FLOP_PER_TOKEN_HEAD_PN * P * N * tokens * H
     btf = bflop / (bwd_ms / 1e3) / 1e12
+    # bf16 inputs run on the bf16 MFMA kernels (the decay gradient chunk by chunk); fp32 inputs on fp32 MFMA
+    peak = PEAK_BF16_TFLOPS if tdt == torch.bfloat16 else PEAK_FP32_MFMA_TFLOPS
+    es = x.element_size()
+    # minimum bytes: x, dy, dt read and dx, ddt written per token-head; B, C read and dB, dC written per
+    # token-group; the final-state gradient and dh0
+    min_bytes = b * L * (H * (3 * P * es + 2 * es) + 4 * G * N * es) + 2 * b * H * P * N * 4
     out = {
         "workload": f"{args.workload}: ssd_backward b={b} L={L} H={H} P={P} N={N} G={G} {cfg['dtype']} io, "
                     f"every gradient (dx, ddt, dA, dB, dC, dD, dh0), final-state gradient given",
         "ms_per_call": bwd_ms,
         "tokens_per_s": tokens / (bwd_ms / 1e3),
         "workspace_bytes": int(bws.numel()),
-        "roofline": {"kernel": "ssd_backward (whole call: three chunked scans, fp32 where the decay gradients "
-                               "need it, and the combine kernels)",
-                     "bound": "mfma", "achieved": btf, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": btf / PEAK_FP32_MFMA_TFLOPS,
-                     "flop_per_token_head": BWD_FLOP_PER_TOKEN_HEAD_PN * P * N},
+        "roofline": {"kernel": "ssd_backward (whole call: the adjoint and two transposed chunked scans, the "
+                               "chunk-local decay gradient, the combine kernels)",
+                     "bound": "mfma", "achieved": btf, "peak": peak, "unit": "TFLOP/s",
+                     "frac": btf / peak,
+                     "flop_per_token_head": BWD_FLOP_PER_TOKEN_HEAD_PN * P * N,
+                     "flop_count": "recurrence form: state recompute 3PN, adjoint 3PN, G.B, G^T.x, S^T.dy, <G,S> "
+                                   "2PN each, per token-head",
+                     "hbm_frac_min_bytes": min_bytes / (bwd_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                     "min_bytes_per_call": min_bytes},
     }
     log(f"backward: {bwd_ms:.3f} ms/call, {tokens / (bwd_ms / 1e3) / 1e6:.1f} M tok/s, {btf:.1f} TFLOP/s "
-        f"(recurrence-form count) against the fp32 MFMA peak")
+        f"(recurrence-form count, {btf / peak:.3f} of the {'bf16' if peak == PEAK_BF16_TFLOPS else 'fp32'} "
+        f"MFMA peak), {min_bytes / (bwd_ms / 1e3) / 1e9:.0f} GB/s on the minimum bytes")
     del gdy, gdf, bws
     torch.cuda.empty_cache()
     return out

@@ -674,7 +674,9 @@ BackwardLayout backward_layout(const Shape& s) {
     };
     f.xr = take(RLHP / 4 * sz), f.dyr = take(RLHP / 4 * sz), f.Cr = take(RLGN * sz), f.Br = take(RLGN * sz);
     f.drev = take(RLH), f.dfwd = take(BLH), f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST);
-    f.u_r = take(RLHP), f.v_r = take(RLHN), f.w = take(BLHN);
+    // the scans' outputs: bf16 in the local flow (u always comes from the bf16 kernels there), fp32 otherwise
+    const size_t osz = f.local ? 2 : 4;
+    f.u_r = take(RLHP / 4 * osz), f.v_r = take(RLHN / 4 * osz), f.w = take(BLHN / 4 * osz);
     f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS), f.fscr = take(HS);
     f.q = take(BLH), f.dlam = take(f.local ? 0 : BLH), f.dxy = take(BLH), f.dA_part = take(BH8), f.dD_part = take(BH8);
     f.states_b = take(f.local ? ST : 0), f.R = take(f.local ? BLH : 0);
