@@ -178,8 +178,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
                 }
             }
         }
+        // wavefront sums: each 16-lane row by DPP moves, then the four rows
+        sq = row16_sum(sq);
+        sw = row16_sum(sw);
+        sxy = row16_sum(sxy);
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
+        for (int off = 16; off < 64; off <<= 1) {
             sq += __shfl_xor(sq, off, 64);
             sw += __shfl_xor(sw, off, 64);
             sxy += __shfl_xor(sxy, off, 64);
