@@ -263,10 +263,15 @@ ssd_status ssd_step_multi_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, fl
  * and dh0 may be NULL (not written).  dims->chunk is the chunk of the
  * internal scans: 0 for the library's choice, else a multiple of 16 up to 512
  * whose fp32 tiles fit LDS.  Supported: dstate <= 256 besides the forward's
- * limits (SSD_ERR_UNSUPPORTED otherwise).  workspace:
+ * limits (SSD_ERR_UNSUPPORTED otherwise).  bf16 inputs with headdim 64,
+ * dstate 64 or 128 and chunk 64 or 128 (the library's choice) form the decay
+ * gradient chunk by chunk and run the transposed scans on the bf16 chunk
+ * kernels; other inputs run fp32 scans.  workspace:
  * ssd_backward_workspace_bytes(dims) bytes, 256-byte aligned (about
- * (2 s + 4) P + 8 N + 4 P N / chunk bytes per token-head, s = the io element
- * size); no output may overlap an input, another output or the workspace.
+ * (2 s + 4) P + 8 N + 4 P N / chunk bytes per token-head with fp32 scans, s =
+ * the io element size, and about 6 P + 4 N + 8 P N / chunk with the chunked
+ * decay gradient); no output may overlap an input, another output or the
+ * workspace.
  */
 size_t ssd_backward_workspace_bytes(const ssd_dims* dims);
 ssd_status ssd_backward(const ssd_dims* dims, const void* x, const void* dt, const float* A,

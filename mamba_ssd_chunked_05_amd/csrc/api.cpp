@@ -504,8 +504,10 @@ ssd_status ssd_step_multi(const ssd_dims* dims, float* state, const void* x, con
 // ---------------------------------------------------------------------------
 // backward pass
 // ---------------------------------------------------------------------------
-// The backward runs three fp32 scans on the generic chunk kernels: the adjoint (headdim P, dstate N)
-// and two transposed ones (headdim N, dstate P, one group per head).  The chunk must suit both.
+// The backward runs three scans: the adjoint (headdim P, dstate N) and two transposed ones (headdim N,
+// dstate P, one group per head).  Whatever path runs them (the fp32 generic kernels, or for bf16 inputs
+// with headdim 64 the chunk-local decay gradient and the bf16 chunk kernels), the chunk must suit the fp32
+// generic tiles, which every shape can fall back to.
 static bool backward_chunk_ok(const ssd::Shape& s, int64_t Q) {
     if (Q % 16 || Q < 16 || Q > 512) return false;
     ssd::Shape a = s, t = s;
