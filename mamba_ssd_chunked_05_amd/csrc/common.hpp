@@ -168,4 +168,15 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t id, uint32_t n) {
     return x * q + (x < rem ? x : rem) + k;
 }
 
+// The same XCD ranges walked from their end.  An output kernel that follows a chunk-state kernel over the
+// same items starts with the items that kernel ran last, whose x and B rows are then the most likely to
+// still sit in the memory-side cache.
+__device__ __forceinline__ uint32_t xcd_remap_rev(uint32_t id, uint32_t n) {
+    const uint32_t nx = 8;
+    uint32_t q = n / nx, rem = n % nx;
+    uint32_t x = id % nx, k = id / nx;
+    const uint32_t cnt = q + (x < rem ? 1u : 0u);  // items of XCD x
+    return x * q + (x < rem ? x : rem) + (cnt - 1u - k);
+}
+
 }  // namespace ssd

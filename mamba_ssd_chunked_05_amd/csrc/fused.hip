@@ -211,7 +211,7 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     ScanLds<N, HPW>& sm = *reinterpret_cast<ScanLds<N, HPW>*>(smem_raw);
 
     const int HP = H / HPW;
-    const uint32_t item = xcd_remap(blockIdx.x, nitems);
+    const uint32_t item = xcd_remap_rev(blockIdx.x, nitems);
     const int hp = (int)(item % (uint32_t)HP);
     const int64_t c = (item / (uint32_t)HP) % (uint32_t)nC;
     const int64_t b = item / ((uint32_t)HP * (uint32_t)nC);
