@@ -271,7 +271,8 @@ ssd_status ssd_step_multi_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, fl
  * (2 s + 4) P + 8 N + 4 P N / chunk bytes per token-head with fp32 scans, s =
  * the io element size, and about 6 P + 4 N + 8 P N / chunk with the chunked
  * decay gradient); no output may overlap an input, another output or the
- * workspace.
+ * workspace.  x, B, C, dy, dx, dB, dC, h0, dfinal and dh0 must be 16-byte
+ * aligned (SSD_ERR_UNSUPPORTED otherwise).
  */
 size_t ssd_backward_workspace_bytes(const ssd_dims* dims);
 ssd_status ssd_backward(const ssd_dims* dims, const void* x, const void* dt, const float* A,

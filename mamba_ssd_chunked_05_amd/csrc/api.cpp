@@ -576,6 +576,7 @@ ssd_status ssd_backward(const ssd_dims* dims, const void* x, const void* dt, con
             sdA{dA, z.A, "dA"}, sdB{dB, z.bc, "dB"}, sdC{dC, z.bc, "dC"}, sdD{dD, dD ? z.A : 0, "dD"},
             sdh0{dh0, dh0 ? z.hstate : 0, "dh0"}, sws{workspace, need, "workspace"};
         for (const Span& p : {sx, sdt, sA, sB, sC, sdy, sdx, sddt, sdA, sdB, sdC}) SSD_TRY(need_ptr(p));
+        SSD_TRY(need_align16({sx, sB, sC, sdy, sdx, sdB, sdC, sh0, sdf, sdh0}));
         if (s.b > 0 && s.L > 0) {
             if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
             if (workspace_bytes < need)

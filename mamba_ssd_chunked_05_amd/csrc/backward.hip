@@ -216,6 +216,120 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
     }
 }
 
+// NV consecutive bf16 (8 or 16 bytes) as floats
+template <int NV>
+__device__ __forceinline__ void ld_bf16(const bf16* p, float* o) {
+    if constexpr (NV == 8) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = static_cast<float>(v[i]);
+    } else {
+        static_assert(NV == 4, "4 or 8 values");
+        const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = static_cast<float>(v[i]);
+    }
+}
+
+// The combine of the chunk-local flow (bf16, headdim 64, dstate N = 64 or 128, H / G a multiple of 4), one
+// workgroup per (b, t): the quantities of four heads at once per wavefront, 16 lanes per head.  Wavefront
+// wv takes the head quads k = wv, wv + 4, ..., lane row r (lane / 16) head 4k + r; a lane covers
+// p = 4 l16 .. 4 l16 + 3 (8-byte accesses of u, dy, x, dx) and n = (N / 16) l16 .. (16-byte or 8-byte
+// accesses of v, w), so every row of u, v, w, dy, x and dx is read or written by one contiguous access per
+// wavefront.  A quad never straddles a group; the group sums of d v and w collect in registers per lane,
+// are added over the four lane rows when the group changes, and meet the other wavefronts' in LDS.
+template <int N>
+__global__ void __launch_bounds__(256) combine_quad_kernel(const bf16* __restrict__ dy, const bf16* __restrict__ x,
+                                                           const bf16* __restrict__ dt, const bf16* __restrict__ B,
+                                                           const float* __restrict__ D, const bf16* __restrict__ u_r,
+                                                           const bf16* __restrict__ v_r, const bf16* __restrict__ w,
+                                                           bf16* __restrict__ dx, bf16* __restrict__ dB,
+                                                           bf16* __restrict__ dC, float* __restrict__ q,
+                                                           float* __restrict__ dxy, int64_t L, int64_t Lr, int H,
+                                                           int G) {
+    constexpr int P = 64, NV = N / 16;
+    extern __shared__ float lds[];
+    float* pB = lds;             // [4][G][N] per-wavefront partial dB
+    float* pC = pB + 4 * G * N;  // [4][G][N] per-wavefront partial dC
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane >> 4, l16 = lane & 15;
+    const int64_t bt = blockIdx.x;  // b * L + t
+    const int64_t bb = bt / L, t = bt % L;
+    const int64_t btr = bb * Lr + (Lr - 1 - t);
+    const int hpg = H / G, nq = H / 4;
+    for (int e = tid; e < 8 * G * N; e += 256) lds[e] = 0.0f;
+    __syncthreads();
+    float ab[NV], ac[NV], bv[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) ab[k] = ac[k] = 0.0f;
+    int gcur = -1;
+    auto flush = [&]() {  // wavefront-uniform: every lane takes part in the row sums
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            ab[k] += __shfl_xor(ab[k], 16, 64);
+            ab[k] += __shfl_xor(ab[k], 32, 64);
+            ac[k] += __shfl_xor(ac[k], 16, 64);
+            ac[k] += __shfl_xor(ac[k], 32, 64);
+        }
+        if (r == 0) {
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                pB[(wv * G + gcur) * N + NV * l16 + k] = ab[k];
+                pC[(wv * G + gcur) * N + NV * l16 + k] = ac[k];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NV; ++k) ab[k] = ac[k] = 0.0f;
+    };
+    for (int qd = wv; qd < nq; qd += 4) {
+        const int g = 4 * qd / hpg;  // the same for the quad's four heads
+        if (g != gcur) {
+            if (gcur >= 0) flush();
+            gcur = g;
+            ld_bf16<NV>(B + (bt * G + g) * N + NV * l16, bv);
+        }
+        const int h = 4 * qd + r;
+        float uu[4], gy[4], xx[4], vv[NV], ww[NV];
+        ld_bf16<4>(u_r + (btr * H + h) * P + 4 * l16, uu);
+        ld_bf16<4>(dy + (bt * H + h) * P + 4 * l16, gy);
+        ld_bf16<4>(x + (bt * H + h) * P + 4 * l16, xx);
+        ld_bf16<NV>(v_r + (btr * H + h) * N + NV * l16, vv);
+        ld_bf16<NV>(w + (bt * H + h) * N + NV * l16, ww);
+        const float d = static_cast<float>(dt[bt * H + h]), Dh = D ? D[h] : 0.0f;
+        bf16x4 o;
+        float sxy = 0.0f, sq = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[i] = static_cast<bf16>(fmaf(d, uu[i], Dh * gy[i]));
+            sxy = fmaf(gy[i], xx[i], sxy);
+        }
+        *reinterpret_cast<bf16x4*>(dx + (bt * H + h) * P + 4 * l16) = o;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            sq = fmaf(vv[k], bv[k], sq);
+            ab[k] = fmaf(d, vv[k], ab[k]);
+            ac[k] += ww[k];
+        }
+        sq = row16_sum(sq);
+        sxy = row16_sum(sxy);
+        if (l16 == 0) {
+            q[(bb * H + h) * L + t] = sq;
+            dxy[(bb * H + h) * L + t] = sxy;
+        }
+    }
+    if (gcur >= 0) flush();
+    __syncthreads();
+    for (int e = tid; e < G * N; e += 256) {
+        float sb = 0.0f, sc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            sb += pB[k * G * N + e];
+            sc += pC[k * G * N + e];
+        }
+        dB[bt * G * N + e] = static_cast<bf16>(sb);
+        dC[bt * G * N + e] = static_cast<bf16>(sc);
+    }
+}
+
 // the combine kernel with LDS slices for the group sums when they fit, else the two-pass form
 template <class T, class U, class V>
 hipError_t launch_combine(const void* dy, const void* x, const void* dt, const void* B, const void* C,
@@ -529,8 +643,22 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     BWD_CHECK(launch_state_passing(sh, states, cs2, h0 ? h0T : nullptr, finT, st));
     BWD_CHECK(launch_chunk_scan_fast(sh, B, x, dy, dt2, cs2, states, nullptr, w, st, &xm));
 
-    BWD_CHECK((launch_combine<T, bf16, bf16>(dy, x, dt, B, C, D, u_r, v_r, w, dx, dB, dC, q, nullptr, dxy, b, L, Lr, H,
-                                             P, N, G, st)));
+    if (P == 64 && (N == 64 || N == 128) && hpg % 4 == 0 && (size_t)8 * G * N * 4 <= 64 * 1024) {
+        const size_t lds = (size_t)8 * G * N * 4;
+        const bf16 *dyb = static_cast<const bf16*>(dy), *xb = static_cast<const bf16*>(x);
+        const bf16 *dtb = static_cast<const bf16*>(dt), *Bb = static_cast<const bf16*>(B);
+        bf16 *dxb = static_cast<bf16*>(dx), *dBb = static_cast<bf16*>(dB), *dCb = static_cast<bf16*>(dC);
+        if (N == 128)
+            hipLaunchKernelGGL(combine_quad_kernel<128>, dim3((unsigned)(b * L)), dim3(256), lds, st, dyb, xb, dtb, Bb, D,
+                               u_r, v_r, w, dxb, dBb, dCb, q, dxy, L, Lr, H, G);
+        else
+            hipLaunchKernelGGL(combine_quad_kernel<64>, dim3((unsigned)(b * L)), dim3(256), lds, st, dyb, xb, dtb, Bb, D,
+                               u_r, v_r, w, dxb, dBb, dCb, q, dxy, L, Lr, H, G);
+        BWD_CHECK(hipGetLastError());
+    } else {
+        BWD_CHECK((launch_combine<T, bf16, bf16>(dy, x, dt, B, C, D, u_r, v_r, w, dx, dB, dC, q, nullptr, dxy, b, L, Lr,
+                                                 H, P, N, G, st)));
+    }
     hipLaunchKernelGGL(finish_kernel<T>, dim3((unsigned)H, (unsigned)b), dim3(256), 0, st, q, R, dxy,
                        static_cast<const T*>(dt), A, static_cast<T*>(ddt), dA_part, dD_part, L, H);
     BWD_CHECK(hipGetLastError());

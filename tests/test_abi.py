@@ -371,5 +371,7 @@ def test_backward_validates_pointers_and_workspace():
     assert _bwd(d, ws=ws, ws_bytes=need, dx=_p(64)) == ALIAS  # dx over x
     assert _bwd(d, ws=ws, ws_bytes=need, dB=_p((6 << 30) + 64)) == ALIAS  # dB over dx
     assert _bwd(d, ws=_p(5 << 30), ws_bytes=need) == ALIAS  # workspace over dy
+    assert _bwd(d, ws=ws, ws_bytes=need, dy=_p((5 << 30) + 8)) == UNSUP  # dy not 16-byte aligned
+    assert _bwd(d, ws=ws, ws_bytes=need, dB=_p((9 << 30) + 4)) == UNSUP  # dB not 16-byte aligned
     # no rows: nothing to validate against the workspace
     assert lib.ssd_backward_workspace_bytes(ctypes.byref(_d(b=0))) >= 0
