@@ -531,9 +531,10 @@ hipError_t scan_in(const Shape& s, int in_io, int xrep, const void* xin, const v
 
 // The backward with the decay gradient formed chunk by chunk (decay_grad.hip), for bf16 io with headdim
 // 64 and dstate 64 or 128.  The decay gradient then needs no long suffix sum, so the transposed scans
-// (c) and (d), which only feed dB, dC and q, run in bf16 compute.  The reversed copies are front-padded
-// to whole chunks, so that every reversed chunk is a forward chunk read backwards and the adjoint
-// scan's chunk-start states are the adjoints entering the forward chunks.
+// (c) and (d), which only feed dB, dC and q, run in bf16 compute.  The reversed scans read the inputs in
+// place, backwards (XMap::rows), over Lr tokens: the sequence front-padded to whole chunks (the padding
+// reads as zero), so that every reversed chunk is a forward chunk read backwards and the adjoint scan's
+// chunk-start states are the adjoints entering the forward chunks.
 hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, const void* dt, const float* A,
                      const void* B, const void* C, const float* D, const float* h0, const void* dy,
                      const float* dfinal, void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0,
@@ -542,8 +543,6 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     const int64_t b = s.b, L = s.L, Lr = f.Lr, pad = f.Lr - s.L;
     const int H = (int)s.H, P = (int)s.P, N = (int)s.N, G = (int)s.G;
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-    T *xr = reinterpret_cast<T*>(ws + f.xr), *dyr = reinterpret_cast<T*>(ws + f.dyr);
-    T *Cr = reinterpret_cast<T*>(ws + f.Cr), *Br = reinterpret_cast<T*>(ws + f.Br);
     float *drev = F(f.drev), *dfwd = F(f.dfwd), *dt_t = F(f.dt_t), *cs = F(f.cs);
     float *states = F(f.states), *states_b = F(f.states_b), *R = F(f.R), *G0 = F(f.G0), *dfT = F(f.dfT);
     float *h0T = F(f.h0T), *finT = F(f.finT), *fscr = F(f.fscr), *q = F(f.q), *dxy = F(f.dxy);
@@ -556,10 +555,6 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
         e = (expr);                    \
         if (e != hipSuccess) return e; \
     } while (0)
-    BWD_CHECK((copy<T, T>(x, xr, b, L, H, P, 1, true, pad, st)));
-    BWD_CHECK((copy<T, T>(dy, dyr, b, L, H, P, 1, true, pad, st)));
-    BWD_CHECK((copy<T, T>(C, Cr, b, L, G, N, 1, true, pad, st)));
-    BWD_CHECK((copy<T, T>(B, Br, b, L, G, N, 1, true, pad, st)));
     hipLaunchKernelGGL(steps_kernel<T>, grid1(b * Lr * H), dim3(256), 0, st, static_cast<const T*>(dt), drev, dfwd, L,
                        pad, H, b * Lr * H);
     BWD_CHECK(hipGetLastError());
@@ -588,12 +583,16 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
                        b * H * s.nC * s.Q);
     BWD_CHECK(hipGetLastError());
     // (b) the adjoint: u (dx), its final value G0 (dh0) and the chunk-start adjoints kept in states_b
-    BWD_CHECK(scan(sr16, dyr, Cr, Br, dt_t, cs, states_b, dfinal, G0, u_r, st));
+    const XMap xb{H, 1, 1, L};  // dy, C and B read backwards
+    BWD_CHECK(launch_chunk_state_fast(sr16, dy, C, dt_t, cs, states_b, st, &xb));
+    BWD_CHECK(launch_state_passing(sr16, states_b, cs, dfinal, G0, st));
+    BWD_CHECK(launch_chunk_scan_fast(sr16, dy, C, B, dt_t, cs, states_b, nullptr, u_r, st, &xb));
     // (c) G^T read out through x: v (dB, q), on the fast chunk kernels as nh H heads of headdim 64 (nh = N / 64:
     // at dstate 128 each head splits into two half-heads, the two halves of the state's N rows, which form
     // one head pair) whose x is (that half of) B or C of the head's group
     const int nh = N / 64;
-    const XMap xm{nh * G, nh * hpg, nh};
+    const XMap xm{nh * G, nh * hpg, nh, 0};  // (d): forwards
+    const XMap xmr{nh * G, nh * hpg, nh, L};  // (c): backwards
     Shape sh = sT16;
     sh.H = nh * H;
     sh.P = 64;
@@ -619,9 +618,9 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     hipLaunchKernelGGL(ones_kernel, grid1(b * sh.H * sh.nC * sh.Q), dim3(256), 0, st, dt2, Lr, (int)sh.Q, sh.nC,
                        b * sh.H * sh.nC * sh.Q);
     BWD_CHECK(hipGetLastError());
-    BWD_CHECK(launch_chunk_state_fast(sh, Cr, dyr, dt2, cs2, states, st, &xm));
+    BWD_CHECK(launch_chunk_state_fast(sh, C, dy, dt2, cs2, states, st, &xmr));
     BWD_CHECK(launch_state_passing(sh, states, cs2, dfT, fscr, st));
-    BWD_CHECK(launch_chunk_scan_fast(sh, Cr, dyr, xr, dt2, cs2, states, nullptr, v_r, st, &xm));
+    BWD_CHECK(launch_chunk_scan_fast(sh, C, dy, x, dt2, cs2, states, nullptr, v_r, st, &xmr));
     // forward direction: the chunk-start states S0 (hi/lo chunk states, fp32 pass), then the decay gradient
     BWD_CHECK(launch_chunk_cumsum(sf, none, dfwd, A, dt_t, cs, st));
     BWD_CHECK(launch_chunk_state(s16, x, B, dt_t, cs, states, st));
@@ -804,7 +803,10 @@ BackwardLayout backward_layout(const Shape& s) {
         o += a256(bytes);
         return at;
     };
-    f.xr = take(RLHP / 4 * sz), f.dyr = take(RLHP / 4 * sz), f.Cr = take(RLGN * sz), f.Br = take(RLGN * sz);
+    // the time-reversed copies of the fp32-scan flow (the local flow reads the inputs backwards in place)
+    const size_t cp = f.local ? 0 : 1;
+    f.xr = take(cp * RLHP / 4 * sz), f.dyr = take(cp * RLHP / 4 * sz), f.Cr = take(cp * RLGN * sz);
+    f.Br = take(cp * RLGN * sz);
     f.drev = take(RLH), f.dfwd = take(BLH), f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST);
     // the scans' outputs: bf16 in the local flow (u always comes from the bf16 kernels there), fp32 otherwise
     const size_t osz = f.local ? 2 : 4;

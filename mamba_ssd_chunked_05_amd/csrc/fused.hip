@@ -77,17 +77,20 @@ struct BRows {
 struct TileBase {
     const bf16 *x, *b, *c;
     const float *dt, *cs;
+    int64_t rows;  // rows of the tile inside the inputs, from the resource's start
 };
 
-// hx: heads of the x rows; dt_head: distance between consecutive heads in the dt/cs arrays
-template <int N, int HPW>
+// hx: heads of the x rows; dt_head: distance between consecutive heads in the dt/cs arrays.
+// REV: the tile's rows run backwards from its last input row (the resource starts at the lowest one), so
+// tile row r sits 63 - r rows above the resource's start; the later pieces of a thread step downwards.
+template <int N, int HPW, bool REV = false>
 __device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int hx, int G, int64_t dt_head, int tid) {
     constexpr int BS = Strides<N>::BS, CS = Strides<N>::CS;
     const int xr = tid >> 3, xc = (tid & 7) * 8;
-    a.xo = (uint32_t)(xr * hx * P + xc) * 2u;
+    a.xo = (uint32_t)((REV ? QS - 1 - xr : xr) * hx * P + xc) * 2u;
     a.xl = xr * XS + xc;
     const int br = tid / (N / 8), bc = (tid % (N / 8)) * 8;
-    a.bo = (uint32_t)(br * G * N + bc) * 2u;
+    a.bo = (uint32_t)((REV ? QS - 1 - br : br) * G * N + bc) * 2u;
     a.bl = br * BS + bc;
     a.cl = br * CS + bc;
     const int hh = tid >> 6, r = tid & 63;
@@ -96,40 +99,46 @@ __device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int hx, int G, 
 
 // The tiles of the sub-chunk starting at token tbase of batch row b (x heads xh0.. of hx per row,
 // group g); dt0 / cs0 point at this chunk's first position of the workgroup's first head and sub is the
-// sub-chunk index.
-template <bool WITH_C>
+// sub-chunk index.  REV: the inputs hold Lin rows per batch row in forward time, token t is input row
+// L - 1 - t, so the tile covers input rows L - 64 - tbase (its last token, the resource's start) up to
+// L - 1 - tbase, of which those below Lin exist (L a multiple of 64).
+template <bool WITH_C, bool REV = false>
 __device__ __forceinline__ TileBase tile_base(const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
                                               int64_t dt0, int64_t b, int64_t L, int hx, int G, int N, int xh0, int g,
-                                              int64_t tbase, int sub) {
+                                              int64_t tbase, int sub, int64_t Lin = 0) {
     TileBase t;
-    t.x = x + ((b * L + tbase) * hx + xh0) * (int64_t)P;
-    t.b = B + ((b * L + tbase) * G + g) * (int64_t)N;
-    t.c = WITH_C ? C + ((b * L + tbase) * G + g) * (int64_t)N : nullptr;
+    const int64_t r0 = REV ? b * Lin + (L - QS - tbase) : b * L + tbase;  // the resource's first row
+    t.x = x + (r0 * hx + xh0) * (int64_t)P;
+    t.b = B + (r0 * G + g) * (int64_t)N;
+    t.c = WITH_C ? C + (r0 * G + g) * (int64_t)N : nullptr;
+    t.rows = REV ? Lin - (L - QS - tbase) : L - tbase;
     t.dt = ds.dt_t + dt0 + (int64_t)QS * sub;
     t.cs = ds.cs + dt0 + (int64_t)QS * sub;
     return t;
 }
 
-// Load one sub-chunk into registers; rows past the sequence end read as zero (rows = L - tile start).
-template <int N, int HPW, bool WITH_C>
+// Load one sub-chunk into registers; rows past the inputs' end read as zero (t.rows from the resource's
+// start).  REV (offsets from chunk_addr<REV>): a thread's later pieces lie 32 or RPI rows lower.
+template <int N, int HPW, bool WITH_C, bool REV = false>
 __device__ __forceinline__ void chunk_load(ChunkRegs<N, HPW, WITH_C>& rg, const ChunkAddr<N, HPW>& a,
-                                           const TileBase& t, int64_t rows, int hx, int G, int tid) {
+                                           const TileBase& t, int hx, int G, int tid) {
     constexpr int RPI = BRows<N>::RPI;
     const uint32_t HP_ = (uint32_t)(hx * P), GN = (uint32_t)(G * N);
     if (tid < 64 * HPW) {  // dt_t and cs cover every position of the chunk (zero-padded past L)
         rg.dt = t.dt[a.dto];
         rg.cs = t.cs[a.dto];
     }
-    const auto rx = tile_rsrc(t.x, HP_, rows, HPW * P);
-    const auto rb = tile_rsrc(t.b, GN, rows, N);
+    const auto rx = tile_rsrc(t.x, HP_, t.rows, HPW * P);
+    const auto rb = tile_rsrc(t.b, GN, t.rows, N);
 #pragma unroll
-    for (int k = 0; k < 2 * HPW; ++k) rg.x[k] = ldbuf(rx, a.xo + ((k & 1) * 32 * HP_ + (k >> 1) * P) * 2u);
+    for (int k = 0; k < 2 * HPW; ++k)
+        rg.x[k] = ldbuf(rx, (REV ? a.xo - (k & 1) * 32 * HP_ * 2u : a.xo + (k & 1) * 32 * HP_ * 2u) + (k >> 1) * P * 2u);
 #pragma unroll
-    for (int k = 0; k < N / 32; ++k) rg.b[k] = ldbuf(rb, a.bo + k * RPI * GN * 2u);
+    for (int k = 0; k < N / 32; ++k) rg.b[k] = ldbuf(rb, REV ? a.bo - k * RPI * GN * 2u : a.bo + k * RPI * GN * 2u);
     if (WITH_C) {
-        const auto rc = tile_rsrc(t.c, GN, rows, N);
+        const auto rc = tile_rsrc(t.c, GN, t.rows, N);
 #pragma unroll
-        for (int k = 0; k < N / 32; ++k) rg.c[k] = ldbuf(rc, a.bo + k * RPI * GN * 2u);
+        for (int k = 0; k < N / 32; ++k) rg.c[k] = ldbuf(rc, REV ? a.bo - k * RPI * GN * 2u : a.bo + k * RPI * GN * 2u);
     }
 }
 
@@ -200,7 +209,8 @@ struct ScanLds {
 
 
 // FWD: the forward's variant, reading sub-chunk-local decay arrays (subchunk_decay_kernel).
-template <int N, int HPW, bool FWD>
+// REV: the inputs are walked backwards (XMap::rows).
+template <int N, int HPW, bool FWD, bool REV = false>
 __global__ void __launch_bounds__(256, 2)
 chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, const bf16* __restrict__ C,
                        DtSrc ds, const float* __restrict__ start, const float* __restrict__ D, bf16* __restrict__ y, int64_t L,
@@ -248,10 +258,10 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     const int64_t dt0 = FWD ? ((b * H + h0) * nsubT + c * (Q / QS)) * QS : ((b * H + h0) * nC + c) * Q;
     const int xh0 = h0 / xm.div * xm.mul;  // the x heads of this head pair
     ChunkAddr<N, HPW> ad;
-    chunk_addr<N, HPW>(ad, xm.hx, G, dt_head, tid);
+    chunk_addr<N, HPW, REV>(ad, xm.hx, G, dt_head, tid);
     ChunkRegs<N, HPW, true> rg;
-    chunk_load<N, HPW, true>(rg, ad, tile_base<true>(x, B, C, ds, dt0, b, L, xm.hx, G, N, xh0, g, t0, 0), L - t0,
-                             xm.hx, G, tid);
+    chunk_load<N, HPW, true, REV>(rg, ad, tile_base<true, REV>(x, B, C, ds, dt0, b, L, xm.hx, G, N, xh0, g, t0, 0, xm.rows),
+                                  xm.hx, G, tid);
     // this thread's output element offset within a sub-chunk's y tile (row l16, columns 16w + 4g4 ..)
     const uint32_t yo = (uint32_t)(l16 * H * P + 16 * w + 4 * g4);
 
@@ -263,9 +273,9 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
         __syncthreads();
         if (sc + 1 < nsub) {
             const int64_t t1 = tbase + QS;
-            chunk_load<N, HPW, true>(rg, ad,
-                                     tile_base<true>(x, B, C, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc + 1),
-                                     L - t1, xm.hx, G, tid);
+            chunk_load<N, HPW, true, REV>(
+                rg, ad, tile_base<true, REV>(x, B, C, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc + 1, xm.rows), xm.hx,
+                G, tid);
         }
 
         // ---- phase 1: C.B^T tiles, decayed per head -> LDS in fragment order ----------------
@@ -466,8 +476,8 @@ __device__ __forceinline__ void state_store(bf16* xs, bf16* bsm, float* ww, cons
 // the last to the first, which makes each sub-chunk's distance to the chunk's end known when its
 // weights are formed.
 // FWD: the forward's variant -- reads sub-chunk-local decay arrays and also writes each chunk's total
-// log2 decay to totals (b, H, nC).
-template <int N, int HPW, bool FWD>
+// log2 decay to totals (b, H, nC).  REV: the inputs are walked backwards (XMap::rows).
+template <int N, int HPW, bool FWD, bool REV = false>
 __global__ void __launch_bounds__(256, 2)
 chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, DtSrc ds, float* __restrict__ states,
                         float* __restrict__ totals, int64_t L, int H, int G, int Q, int64_t nC, uint32_t nitems,
@@ -504,13 +514,13 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     if (!FWD && tid < 64 * HPW) cs_end = ds.cs[dt0 + (int64_t)(tid >> 6) * dt_head + (Q - 1)];
     const int xh0 = h0 / xm.div * xm.mul;  // the x heads of this head pair
     ChunkAddr<N, HPW> ad;
-    chunk_addr<N, HPW>(ad, xm.hx, G, dt_head, tid);
+    chunk_addr<N, HPW, REV>(ad, xm.hx, G, dt_head, tid);
     ChunkRegs<N, HPW, false> rg;
     {
         const int64_t tl = t0 + (int64_t)(nsub - 1) * QS;
-        chunk_load<N, HPW, false>(rg, ad,
-                                  tile_base<false>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, tl, nsub - 1),
-                                  L - tl, xm.hx, G, tid);
+        chunk_load<N, HPW, false, REV>(
+            rg, ad, tile_base<false, REV>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, tl, nsub - 1, xm.rows),
+            xm.hx, G, tid);
     }
 
     for (int sc = nsub - 1; sc >= 0; --sc) {
@@ -519,9 +529,9 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
         __syncthreads();
         if (sc > 0) {
             const int64_t t1 = t0 + (int64_t)(sc - 1) * QS;
-            chunk_load<N, HPW, false>(rg, ad,
-                                      tile_base<false>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc - 1),
-                                      L - t1, xm.hx, G, tid);
+            chunk_load<N, HPW, false, REV>(
+                rg, ad, tile_base<false, REV>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc - 1, xm.rows),
+                xm.hx, G, tid);
         }
 
 #pragma unroll
@@ -630,17 +640,28 @@ __global__ void __launch_bounds__(256) subchunk_decay_kernel(DtFront fe, const b
     }
 }
 
+// Reading the inputs backwards (XMap::rows > 0) is a variant of the staged kernels only; it needs whole
+// 64-token tiles (L a multiple of 64) so that every tile's first input row lies inside the batch row.
+inline bool rev_ok(const Shape& s, const XMap& xm) { return xm.rows >= 0 && xm.rows <= s.L && s.L % QS == 0; }
+
 template <int N, int HPW, bool FWD>
 hipError_t launch_state_fast(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
                              float* totals, const XMap& xm, hipStream_t st) {
     const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
     if (nitems == 0) return hipSuccess;
     const size_t lds = sizeof(AggLds<N, HPW>);
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_fast_kernel<N, HPW, FWD>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const bool rev = !FWD && xm.rows > 0;
+    if (rev && !rev_ok(s, xm)) return hipErrorInvalidValue;
+    const void* fn = rev ? (const void*)chunk_state_fast_kernel<N, HPW, false, true>
+                         : (const void*)chunk_state_fast_kernel<N, HPW, FWD>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, ds, states,
-                       totals, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
+    if (rev)
+        hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW, false, true>), dim3(nitems), dim3(256), lds, st, x, B, ds,
+                           states, totals, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
+    else
+        hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, ds, states,
+                           totals, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
     return hipGetLastError();
 }
 
@@ -650,11 +671,18 @@ hipError_t launch_scan_fast(const Shape& s, const bf16* x, const bf16* B, const 
     const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
     if (nitems == 0) return hipSuccess;
     const size_t lds = sizeof(ScanLds<N, HPW>);
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_scan_fast_kernel<N, HPW, FWD>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const bool rev = !FWD && xm.rows > 0;
+    if (rev && !rev_ok(s, xm)) return hipErrorInvalidValue;
+    const void* fn = rev ? (const void*)chunk_scan_fast_kernel<N, HPW, false, true>
+                         : (const void*)chunk_scan_fast_kernel<N, HPW, FWD>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, C, ds, start,
-                       D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
+    if (rev)
+        hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, false, true>), dim3(nitems), dim3(256), lds, st, x, B, C, ds,
+                           start, D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
+    else
+        hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, C, ds, start,
+                           D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
     return hipGetLastError();
 }
 
@@ -722,8 +750,11 @@ namespace fz {
 template <bool FWD>
 hipError_t state_dispatch(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
                           float* totals, hipStream_t st, const XMap* xm) {
-    if (s.N >= 256) return state_wide<FWD>(s, x, B, ds, states, totals, st);
-    const XMap id{(int)s.H, 1, 1};
+    if (s.N >= 256) {
+        if (xm) return hipErrorInvalidValue;  // the wide kernels read x in place, forwards
+        return state_wide<FWD>(s, x, B, ds, states, totals, st);
+    }
+    const XMap id{(int)s.H, 1, 1, 0};
     const XMap& m = xm ? *xm : id;
     const bool pair = fast_hpw(s) == 2;
     if (s.N == 128)
@@ -736,8 +767,11 @@ hipError_t state_dispatch(const Shape& s, const bf16* x, const bf16* B, const Dt
 template <bool FWD>
 hipError_t scan_dispatch(const Shape& s, const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
                          const float* start, const float* D, bf16* y, hipStream_t st, const XMap* xm) {
-    if (s.N >= 256) return scan_wide<FWD>(s, x, B, C, ds, start, D, y, st);
-    const XMap id{(int)s.H, 1, 1};
+    if (s.N >= 256) {
+        if (xm) return hipErrorInvalidValue;  // the wide kernels read x in place, forwards
+        return scan_wide<FWD>(s, x, B, C, ds, start, D, y, st);
+    }
+    const XMap id{(int)s.H, 1, 1, 0};
     const XMap& m = xm ? *xm : id;
     const bool pair = fast_hpw(s) == 2;
     if (s.N == 128)

@@ -48,9 +48,12 @@ hipError_t launch_step_multi(const Shape& s, const DtFront& fe, float* state, co
 // Where the fast kernels read x: rows of hx heads, and the head pair starting at head h0 reads the x heads
 // h0 / div * mul and the next one.  The identity is {H, 1, 1}.  The backward's transposed scans run
 // 2H half-heads (the two 64-column halves of each head) whose x is B or C of the head's group:
-// {2G, 2 H / G, 2}.
+// {2G, 2 H / G, 2}.  rows > 0 (chunk state and chunk scan only, L a multiple of 64): the inputs x, B and
+// C hold `rows` tokens per batch row in forward time and the kernels walk them backwards -- their token
+// t (of L) is input row L - 1 - t, and the tokens t < L - rows (past the inputs' start) read as zero.
 struct XMap {
     int hx, div, mul;
+    int64_t rows;
 };
 // Fast chunk-state / chunk-scan kernels (bf16, headdim 64, dstate 64 or 128, chunk a multiple of 64).
 bool fast_chunk_supported(const Shape& s);
