@@ -105,7 +105,8 @@ __global__ void __launch_bounds__(256) dup_kernel(const float* __restrict__ in, 
 // ranges, so a wavefront meets each group once) and are flushed to a per-wavefront LDS slice.
 // Without SLICES (LDS too small for them) the group sums re-read v and w in a second pass.
 // u_r and v_r have Lr rows per batch row (time-reversed, behind Lr - L rows of padding); dlam may be
-// NULL (the chunk-local decay gradient does not use it).
+// NULL (the chunk-local decay gradient does not use it).  With u_r NULL dx is not written (the adjoint
+// scan wrote it), and with vrev 0 v_r is in forward time (L rows per batch row).
 template <class T, class U, class V, bool SLICES>
 __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, const T* __restrict__ x,
                                                       const T* __restrict__ dt, const T* __restrict__ B,
@@ -114,7 +115,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
                                                       const V* __restrict__ w, T* __restrict__ dx,
                                                       T* __restrict__ dB, T* __restrict__ dC, float* __restrict__ q,
                                                       float* __restrict__ dlam, float* __restrict__ dxy, int64_t L,
-                                                      int64_t Lr, int H, int P, int N, int G) {
+                                                      int64_t Lr, int H, int P, int N, int G, int vrev) {
     extern __shared__ float lds[];
     float* sB = lds;                // [G][N]
     float* sC = sB + G * N;         // [G][N]
@@ -124,7 +125,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bt = blockIdx.x;  // b * L + t
     const int64_t bb = bt / L, t = bt % L;
-    const int64_t btr = bb * Lr + (Lr - 1 - t);
+    const int64_t btr = bb * Lr + (Lr - 1 - t), btv = vrev ? btr : bt;
     const int hpg = H / G;
     for (int e = tid; e < G * N; e += 256) {
         sB[e] = to_f32(B[bt * G * N + e]);
@@ -162,14 +163,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
         for (int p = lane; p < P; p += 64) {
             const int64_t o = (bt * H + h) * P + p;
             const float gy = to_f32(dy[o]);
-            dx[o] = from_f32<T>(fmaf(d, to_f32(u_r[(btr * H + h) * P + p]), Dh * gy));
+            if (u_r) dx[o] = from_f32<T>(fmaf(d, to_f32(u_r[(btr * H + h) * P + p]), Dh * gy));
             sxy = fmaf(gy, to_f32(x[o]), sxy);
         }
 #pragma unroll
         for (int k = 0; k < kMaxNL; ++k) {
             const int n = lane + 64 * k;
             if (n < N) {
-                const float vv = to_f32(v_r[(btr * H + h) * N + n]), ww = to_f32(w[(bt * H + h) * N + n]);
+                const float vv = to_f32(v_r[(btv * H + h) * N + n]), ww = to_f32(w[(bt * H + h) * N + n]);
                 sq = fmaf(vv, sB[g * N + n], sq);
                 sw = fmaf(ww, sC[g * N + n], sw);
                 if (SLICES) {
@@ -207,7 +208,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
         } else {
             const int g = e / N, n = e % N;
             for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
-                sb = fmaf(sdt[h], to_f32(v_r[(btr * H + h) * N + n]), sb);
+                sb = fmaf(sdt[h], to_f32(v_r[(btv * H + h) * N + n]), sb);
                 sc += to_f32(w[(bt * H + h) * N + n]);
             }
         }
@@ -231,78 +232,59 @@ __device__ __forceinline__ void ld_bf16(const bf16* p, float* o) {
     }
 }
 
-// The combine of the chunk-local flow (bf16, headdim 64, dstate N = 64 or 128, H / G a multiple of 4), one
-// workgroup per (b, t): the quantities of four heads at once per wavefront, 16 lanes per head.  Wavefront
+// The combine of the chunk-local flow (bf16, headdim 64, dstate N = 64 or 128, H a multiple of 4), one
+// workgroup per (b, t), after the adjoint scan has written dx itself: per head q = v . B and dy . x, per
+// group dB = sum_h dt v and dC = sum_h w.  Four heads at once per wavefront, 16 lanes per head: wavefront
 // wv takes the head quads k = wv, wv + 4, ..., lane row r (lane / 16) head 4k + r; a lane covers
-// p = 4 l16 .. 4 l16 + 3 (8-byte accesses of u, dy, x, dx) and n = (N / 16) l16 .. (16-byte or 8-byte
-// accesses of v, w), so every row of u, v, w, dy, x and dx is read or written by one contiguous access per
-// wavefront.  A quad never straddles a group; the group sums of d v and w collect in registers per lane,
-// are added over the four lane rows when the group changes, and meet the other wavefronts' in LDS.
+// p = 4 l16 .. 4 l16 + 3 (8-byte accesses of dy, x) and n = (N / 16) l16 .. (16- or 8-byte accesses of
+// v, w), so every row of v, w, dy and x is read by one contiguous access per wavefront.  The group sums
+// collect in registers per lane and land, per (wavefront, lane row), in an LDS slice when the row's group
+// changes; the slices are added in a fixed order at the end.
 template <int N>
 __global__ void __launch_bounds__(256) combine_quad_kernel(const bf16* __restrict__ dy, const bf16* __restrict__ x,
                                                            const bf16* __restrict__ dt, const bf16* __restrict__ B,
-                                                           const float* __restrict__ D, const bf16* __restrict__ u_r,
-                                                           const bf16* __restrict__ v_r, const bf16* __restrict__ w,
-                                                           bf16* __restrict__ dx, bf16* __restrict__ dB,
-                                                           bf16* __restrict__ dC, float* __restrict__ q,
-                                                           float* __restrict__ dxy, int64_t L, int64_t Lr, int H,
-                                                           int G) {
+                                                           const bf16* __restrict__ v, const bf16* __restrict__ w,
+                                                           bf16* __restrict__ dB, bf16* __restrict__ dC,
+                                                           float* __restrict__ q, float* __restrict__ dxy, int64_t L,
+                                                           int H, int G) {
     constexpr int P = 64, NV = N / 16;
     extern __shared__ float lds[];
-    float* pB = lds;             // [4][G][N] per-wavefront partial dB
-    float* pC = pB + 4 * G * N;  // [4][G][N] per-wavefront partial dC
+    float* pB = lds;              // [16][G][N] per-(wavefront, lane row) partial dB
+    float* pC = pB + 16 * G * N;  // [16][G][N] per-(wavefront, lane row) partial dC
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane >> 4, l16 = lane & 15;
+    const int slot = 4 * wv + r;
     const int64_t bt = blockIdx.x;  // b * L + t
     const int64_t bb = bt / L, t = bt % L;
-    const int64_t btr = bb * Lr + (Lr - 1 - t);
     const int hpg = H / G, nq = H / 4;
-    for (int e = tid; e < 8 * G * N; e += 256) lds[e] = 0.0f;
+    for (int e = tid; e < 32 * G * N; e += 256) lds[e] = 0.0f;
     __syncthreads();
     float ab[NV], ac[NV], bv[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) ab[k] = ac[k] = 0.0f;
     int gcur = -1;
-    auto flush = [&]() {  // wavefront-uniform: every lane takes part in the row sums
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            ab[k] += __shfl_xor(ab[k], 16, 64);
-            ab[k] += __shfl_xor(ab[k], 32, 64);
-            ac[k] += __shfl_xor(ac[k], 16, 64);
-            ac[k] += __shfl_xor(ac[k], 32, 64);
-        }
-        if (r == 0) {
-#pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                pB[(wv * G + gcur) * N + NV * l16 + k] = ab[k];
-                pC[(wv * G + gcur) * N + NV * l16 + k] = ac[k];
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < NV; ++k) ab[k] = ac[k] = 0.0f;
-    };
     for (int qd = wv; qd < nq; qd += 4) {
-        const int g = 4 * qd / hpg;  // the same for the quad's four heads
-        if (g != gcur) {
-            if (gcur >= 0) flush();
+        const int h = 4 * qd + r, g = h / hpg;
+        if (g != gcur) {  // the same in each lane row
+            if (gcur >= 0) {
+#pragma unroll
+                for (int k = 0; k < NV; ++k) {
+                    pB[(slot * G + gcur) * N + NV * l16 + k] = ab[k];
+                    pC[(slot * G + gcur) * N + NV * l16 + k] = ac[k];
+                    ab[k] = ac[k] = 0.0f;
+                }
+            }
             gcur = g;
             ld_bf16<NV>(B + (bt * G + g) * N + NV * l16, bv);
         }
-        const int h = 4 * qd + r;
-        float uu[4], gy[4], xx[4], vv[NV], ww[NV];
-        ld_bf16<4>(u_r + (btr * H + h) * P + 4 * l16, uu);
+        float gy[4], xx[4], vv[NV], ww[NV];
         ld_bf16<4>(dy + (bt * H + h) * P + 4 * l16, gy);
         ld_bf16<4>(x + (bt * H + h) * P + 4 * l16, xx);
-        ld_bf16<NV>(v_r + (btr * H + h) * N + NV * l16, vv);
+        ld_bf16<NV>(v + (bt * H + h) * N + NV * l16, vv);
         ld_bf16<NV>(w + (bt * H + h) * N + NV * l16, ww);
-        const float d = static_cast<float>(dt[bt * H + h]), Dh = D ? D[h] : 0.0f;
-        bf16x4 o;
+        const float d = static_cast<float>(dt[bt * H + h]);
         float sxy = 0.0f, sq = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            o[i] = static_cast<bf16>(fmaf(d, uu[i], Dh * gy[i]));
-            sxy = fmaf(gy[i], xx[i], sxy);
-        }
-        *reinterpret_cast<bf16x4*>(dx + (bt * H + h) * P + 4 * l16) = o;
+        for (int i = 0; i < 4; ++i) sxy = fmaf(gy[i], xx[i], sxy);
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             sq = fmaf(vv[k], bv[k], sq);
@@ -316,12 +298,18 @@ __global__ void __launch_bounds__(256) combine_quad_kernel(const bf16* __restric
             dxy[(bb * H + h) * L + t] = sxy;
         }
     }
-    if (gcur >= 0) flush();
+    if (gcur >= 0) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            pB[(slot * G + gcur) * N + NV * l16 + k] = ab[k];
+            pC[(slot * G + gcur) * N + NV * l16 + k] = ac[k];
+        }
+    }
     __syncthreads();
     for (int e = tid; e < G * N; e += 256) {
         float sb = 0.0f, sc = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 16; ++k) {
             sb += pB[k * G * N + e];
             sc += pC[k * G * N + e];
         }
@@ -335,7 +323,7 @@ template <class T, class U, class V>
 hipError_t launch_combine(const void* dy, const void* x, const void* dt, const void* B, const void* C,
                           const float* D, const U* u_r, const V* v_r, const V* w, void* dx, void* dB,
                           void* dC, float* q, float* dlam, float* dxy, int64_t b, int64_t L, int64_t Lr, int H, int P,
-                          int N, int G, hipStream_t st) {
+                          int N, int G, hipStream_t st, bool vrev = true) {
     const size_t base = (size_t)(2 * G * N + H) * 4, sliced = base + (size_t)8 * G * N * 4;
     const bool slices = sliced <= 160 * 1024;
     const size_t lds = slices ? sliced : base;
@@ -347,12 +335,12 @@ hipError_t launch_combine(const void* dy, const void* x, const void* dt, const v
         hipLaunchKernelGGL((combine_kernel<T, U, V, true>), dim3((unsigned)(b * L)), dim3(256), lds, st,
                            static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
                            static_cast<const T*>(B), static_cast<const T*>(C), D, u_r, v_r, w, static_cast<T*>(dx),
-                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, Lr, H, P, N, G);
+                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, Lr, H, P, N, G, vrev ? 1 : 0);
     else
         hipLaunchKernelGGL((combine_kernel<T, U, V, false>), dim3((unsigned)(b * L)), dim3(256), lds, st,
                            static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
                            static_cast<const T*>(B), static_cast<const T*>(C), D, u_r, v_r, w, static_cast<T*>(dx),
-                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, Lr, H, P, N, G);
+                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, Lr, H, P, N, G, vrev ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -546,7 +534,7 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     float *drev = F(f.drev), *dfwd = F(f.dfwd), *dt_t = F(f.dt_t), *cs = F(f.cs);
     float *states = F(f.states), *states_b = F(f.states_b), *R = F(f.R), *G0 = F(f.G0), *dfT = F(f.dfT);
     float *h0T = F(f.h0T), *finT = F(f.finT), *fscr = F(f.fscr), *q = F(f.q), *dxy = F(f.dxy);
-    T *u_r = reinterpret_cast<T*>(ws + f.u_r), *v_r = reinterpret_cast<T*>(ws + f.v_r), *w = reinterpret_cast<T*>(ws + f.w);
+    T *v_r = reinterpret_cast<T*>(ws + f.v_r), *w = reinterpret_cast<T*>(ws + f.w);
     double *dA_part = reinterpret_cast<double*>(ws + f.dA_part), *dD_part = reinterpret_cast<double*>(ws + f.dD_part);
     const int64_t PN = (int64_t)P * N;
     hipError_t e;
@@ -582,17 +570,18 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     hipLaunchKernelGGL(ones_kernel, grid1(b * H * s.nC * s.Q), dim3(256), 0, st, dt_t, Lr, (int)s.Q, s.nC,
                        b * H * s.nC * s.Q);
     BWD_CHECK(hipGetLastError());
-    // (b) the adjoint: u (dx), its final value G0 (dh0) and the chunk-start adjoints kept in states_b
-    const XMap xb{H, 1, 1, L};  // dy, C and B read backwards
+    // (b) the adjoint: dx = dt u + D dy written by the scan itself (u = G B, dt as the output row scale, D
+    // on the x-role dy), its final value G0 (dh0) and the chunk-start adjoints kept in states_b
+    const XMap xb{H, 1, 1, L, dt};  // dy, C and B read backwards, dx written forwards
     BWD_CHECK(launch_chunk_state_fast(sr16, dy, C, dt_t, cs, states_b, st, &xb));
     BWD_CHECK(launch_state_passing(sr16, states_b, cs, dfinal, G0, st));
-    BWD_CHECK(launch_chunk_scan_fast(sr16, dy, C, B, dt_t, cs, states_b, nullptr, u_r, st, &xb));
+    BWD_CHECK(launch_chunk_scan_fast(sr16, dy, C, B, dt_t, cs, states_b, D, dx, st, &xb));
     // (c) G^T read out through x: v (dB, q), on the fast chunk kernels as nh H heads of headdim 64 (nh = N / 64:
     // at dstate 128 each head splits into two half-heads, the two halves of the state's N rows, which form
     // one head pair) whose x is (that half of) B or C of the head's group
     const int nh = N / 64;
-    const XMap xm{nh * G, nh * hpg, nh, 0};  // (d): forwards
-    const XMap xmr{nh * G, nh * hpg, nh, L};  // (c): backwards
+    const XMap xm{nh * G, nh * hpg, nh, 0, nullptr};   // (d): forwards
+    const XMap xmr{nh * G, nh * hpg, nh, L, nullptr};  // (c): read backwards, v written forwards
     Shape sh = sT16;
     sh.H = nh * H;
     sh.P = 64;
@@ -642,21 +631,21 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     BWD_CHECK(launch_state_passing(sh, states, cs2, h0 ? h0T : nullptr, finT, st));
     BWD_CHECK(launch_chunk_scan_fast(sh, B, x, dy, dt2, cs2, states, nullptr, w, st, &xm));
 
-    if (P == 64 && (N == 64 || N == 128) && hpg % 4 == 0 && (size_t)8 * G * N * 4 <= 64 * 1024) {
-        const size_t lds = (size_t)8 * G * N * 4;
-        const bf16 *dyb = static_cast<const bf16*>(dy), *xb = static_cast<const bf16*>(x);
+    const size_t lq = (size_t)32 * G * N * 4;  // the quad combine's LDS slices
+    if (P == 64 && (N == 64 || N == 128) && H % 4 == 0 && lq <= 64 * 1024) {
+        const bf16 *dyb = static_cast<const bf16*>(dy), *xb2 = static_cast<const bf16*>(x);
         const bf16 *dtb = static_cast<const bf16*>(dt), *Bb = static_cast<const bf16*>(B);
-        bf16 *dxb = static_cast<bf16*>(dx), *dBb = static_cast<bf16*>(dB), *dCb = static_cast<bf16*>(dC);
+        bf16 *dBb = static_cast<bf16*>(dB), *dCb = static_cast<bf16*>(dC);
         if (N == 128)
-            hipLaunchKernelGGL(combine_quad_kernel<128>, dim3((unsigned)(b * L)), dim3(256), lds, st, dyb, xb, dtb, Bb, D,
-                               u_r, v_r, w, dxb, dBb, dCb, q, dxy, L, Lr, H, G);
+            hipLaunchKernelGGL(combine_quad_kernel<128>, dim3((unsigned)(b * L)), dim3(256), lq, st, dyb, xb2, dtb, Bb,
+                               v_r, w, dBb, dCb, q, dxy, L, H, G);
         else
-            hipLaunchKernelGGL(combine_quad_kernel<64>, dim3((unsigned)(b * L)), dim3(256), lds, st, dyb, xb, dtb, Bb, D,
-                               u_r, v_r, w, dxb, dBb, dCb, q, dxy, L, Lr, H, G);
+            hipLaunchKernelGGL(combine_quad_kernel<64>, dim3((unsigned)(b * L)), dim3(256), lq, st, dyb, xb2, dtb, Bb,
+                               v_r, w, dBb, dCb, q, dxy, L, H, G);
         BWD_CHECK(hipGetLastError());
     } else {
-        BWD_CHECK((launch_combine<T, bf16, bf16>(dy, x, dt, B, C, D, u_r, v_r, w, dx, dB, dC, q, nullptr, dxy, b, L, Lr,
-                                                 H, P, N, G, st)));
+        BWD_CHECK((launch_combine<T, bf16, bf16>(dy, x, dt, B, C, D, nullptr, v_r, w, dx, dB, dC, q, nullptr, dxy, b, L,
+                                                 L, H, P, N, G, st, false)));
     }
     hipLaunchKernelGGL(finish_kernel<T>, dim3((unsigned)H, (unsigned)b), dim3(256), 0, st, q, R, dxy,
                        static_cast<const T*>(dt), A, static_cast<T*>(ddt), dA_part, dD_part, L, H);
@@ -810,7 +799,9 @@ BackwardLayout backward_layout(const Shape& s) {
     f.drev = take(RLH), f.dfwd = take(BLH), f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST);
     // the scans' outputs: bf16 in the local flow (u always comes from the bf16 kernels there), fp32 otherwise
     const size_t osz = f.local ? 2 : 4;
-    f.u_r = take(RLHP / 4 * osz), f.v_r = take(RLHN / 4 * osz), f.w = take(BLHN / 4 * osz);
+    // (the local flow: the adjoint scan writes dx itself, and v is written in forward time)
+    f.u_r = take(f.local ? 0 : RLHP / 4 * osz), f.v_r = take((f.local ? BLHN : RLHN) / 4 * osz);
+    f.w = take(BLHN / 4 * osz);
     f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS), f.fscr = take(HS);
     f.q = take(BLH), f.dlam = take(f.local ? 0 : BLH), f.dxy = take(BLH), f.dA_part = take(BH8), f.dD_part = take(BH8);
     f.states_b = take(f.local ? ST : 0), f.R = take(f.local ? BLH : 0);

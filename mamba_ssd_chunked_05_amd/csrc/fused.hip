@@ -54,6 +54,7 @@ struct ChunkRegs {
     uint4 c[WITH_C ? N / 32 : 1];
     float dt;   // dt_t of token (tid & 63) of head (tid >> 6), threads < 64 * HPW
     float cs;   // chunk cumulative log2 decay of that token
+    float rs;   // its output row scale (reversed walk with a row scale only)
 };
 
 // Per-thread staging offsets within one sub-chunk tile, in bytes from the tile's first element (32-bit: a
@@ -204,6 +205,7 @@ struct ScanLds {
     float dtw[HPW * QS];            // dt
     float ww[HPW * QS];             // 2^(l_63 - l_j) dt_j
     float ec[HPW * 4 * QS];         // separable decay factors of the off-diagonal tiles (chunk_store)
+    float rs[HPW * QS];             // output row scales (reversed walk with a row scale)
     float alpha[4];                 // 2^(l_63) per head
 };
 
@@ -262,6 +264,15 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     ChunkRegs<N, HPW, true> rg;
     chunk_load<N, HPW, true, REV>(rg, ad, tile_base<true, REV>(x, B, C, ds, dt0, b, L, xm.hx, G, N, xh0, g, t0, 0, xm.rows),
                                   xm.hx, G, tid);
+    // reversed walk: the output row scale of token (tid & 63) of head (tid >> 6), at input row L - 1 - t
+    const bf16* rsrc = REV ? static_cast<const bf16*>(xm.rowscale) : nullptr;
+    auto load_rs = [&](int64_t tb) {
+        if (REV && rsrc && tid < 64 * HPW) {
+            const int64_t f = L - 1 - (tb + (tid & 63));
+            rg.rs = f < xm.rows ? static_cast<float>(rsrc[(b * xm.rows + f) * H + h0 + (tid >> 6)]) : 0.0f;
+        }
+    };
+    load_rs(t0);
     // this thread's output element offset within a sub-chunk's y tile (row l16, columns 16w + 4g4 ..)
     const uint32_t yo = (uint32_t)(l16 * H * P + 16 * w + 4 * g4);
 
@@ -270,12 +281,14 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
         __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
         chunk_store<N, HPW, true, FWD>(sm.xs, sm.bs, sm.cs, sm.lw, sm.dtw, sm.ww, sm.ec, sm.alpha, rg, ad, cs_prev,
                                        tot, tid);
+        if (REV && rsrc && tid < 64 * HPW) sm.rs[tid] = rg.rs;
         __syncthreads();
         if (sc + 1 < nsub) {
             const int64_t t1 = tbase + QS;
             chunk_load<N, HPW, true, REV>(
                 rg, ad, tile_base<true, REV>(x, B, C, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc + 1, xm.rows), xm.hx,
                 G, tid);
+            load_rs(t1);
         }
 
         // ---- phase 1: C.B^T tiles, decayed per head -> LDS in fragment order ----------------
@@ -305,7 +318,7 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float v = gacc[r] * fast_exp2(fminf(li - lj[r], 0.0f)) * dj[r];
-                        m[r] = (j0 + r <= i ? v : 0.0f) + (j0 + r == i ? Dh[hh] : 0.0f);
+                        m[r] = (j0 + r <= i ? v : 0.0f) + (!REV && j0 + r == i ? Dh[hh] : 0.0f);
                     }
                 } else {  // below the diagonal: the separable factors of chunk_store
                     const float er = sm.ec[(hh * 4) * QS + i];
@@ -375,7 +388,20 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
                     mma(acc[hh], xf[js][hh], bo);
                 }
             }
-            if (full || tbase + i < L) {
+            if (REV) {  // forward rows: y = s (C.S + in-chunk term) + D x, nothing for the padding tokens
+                const int64_t f = L - 1 - (tbase + i);
+                if (f < xm.rows) {
+#pragma unroll
+                    for (int hh = 0; hh < HPW; ++hh) {
+                        const float s = rsrc ? sm.rs[hh * QS + i] : 1.0f;
+                        const bf16x4 xv = *reinterpret_cast<const bf16x4*>(&sm.xs[(hh * QS + i) * XS + 16 * w + 4 * g4]);
+                        bf16x4 o;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) o[r] = static_cast<bf16>(fmaf(s, acc[hh][r], Dh[hh] * static_cast<float>(xv[r])));
+                        *reinterpret_cast<bf16x4*>(y + ((b * xm.rows + f) * H + h0 + hh) * (int64_t)P + 16 * w + 4 * g4) = o;
+                    }
+                }
+            } else if (full || tbase + i < L) {
 #pragma unroll
                 for (int hh = 0; hh < HPW; ++hh) {
                     bf16x4 o;

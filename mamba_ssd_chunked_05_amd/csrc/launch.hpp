@@ -51,9 +51,13 @@ hipError_t launch_step_multi(const Shape& s, const DtFront& fe, float* state, co
 // {2G, 2 H / G, 2}.  rows > 0 (chunk state and chunk scan only, L a multiple of 64): the inputs x, B and
 // C hold `rows` tokens per batch row in forward time and the kernels walk them backwards -- their token
 // t (of L) is input row L - 1 - t, and the tokens t < L - rows (past the inputs' start) read as zero.
+// The chunk scan then writes its output in forward time too (`rows` rows per batch row, nothing for the
+// padding tokens), as y = s * (C.S + in-chunk term) + D x with s = rowscale[b, row, h] (an io-dtype
+// (b, rows, H) array, e.g. the step dt) or 1 when rowscale is NULL.
 struct XMap {
     int hx, div, mul;
     int64_t rows;
+    const void* rowscale;
 };
 // Fast chunk-state / chunk-scan kernels (bf16, headdim 64, dstate 64 or 128, chunk a multiple of 64).
 bool fast_chunk_supported(const Shape& s);
