@@ -468,6 +468,84 @@ __global__ void __launch_bounds__(256) finish_kernel(const float* __restrict__ q
     }
 }
 
+// The same over a tile of kFinTok tokens and every head, one workgroup per (b, tile), with per-tile
+// partial sums: q, R and dxy ((b, H, L)) are read along the tokens and dt, ddt ((b, L, H)) along the heads,
+// both coalesced, through an LDS tile [4][H][kFinTok + 1].
+constexpr int kFinTok = 32;
+
+template <class T>
+__global__ void __launch_bounds__(256) finish_tile_kernel(const float* __restrict__ q, const float* __restrict__ R,
+                                                          const float* __restrict__ dxy, const T* __restrict__ dt,
+                                                          const float* __restrict__ A, T* __restrict__ ddt,
+                                                          double* __restrict__ dA_part, double* __restrict__ dD_part,
+                                                          int64_t L, int H, int64_t ntile) {
+    constexpr int TS = kFinTok + 1;
+    extern __shared__ float lds[];
+    float *Rl = lds, *ql = Rl + H * TS, *xl = ql + H * TS, *dl = xl + H * TS;
+    const int tid = threadIdx.x;
+    const int64_t tile = blockIdx.x, bb = blockIdx.y, t0 = tile * kFinTok;
+    for (int e = tid; e < H * kFinTok; e += 256) {
+        const int h = e / kFinTok, tt = e % kFinTok;
+        const int64_t t = t0 + tt, o = (bb * H + h) * L + t;
+        const bool in = t < L;
+        Rl[h * TS + tt] = in ? R[o] : 0.0f;
+        ql[h * TS + tt] = in ? q[o] : 0.0f;
+        xl[h * TS + tt] = in ? dxy[o] : 0.0f;
+    }
+    __syncthreads();
+    for (int e = tid; e < H * kFinTok; e += 256) {
+        const int tt = e / H, h = e % H;
+        const int64_t t = t0 + tt;
+        float d = 0.0f;
+        if (t < L) {
+            const int64_t o = (bb * L + t) * H + h;
+            const float r = Rl[h * TS + tt];
+            ddt[o] = from_f32<T>((float)((double)A[h] * r + (double)ql[h * TS + tt]));
+            d = to_f32(dt[o]);
+        }
+        dl[h * TS + tt] = d;
+    }
+    __syncthreads();
+    for (int h = tid; h < H; h += 256) {
+        double da = 0.0, dd = 0.0;
+        for (int tt = 0; tt < kFinTok; ++tt) {
+            da += (double)dl[h * TS + tt] * (double)Rl[h * TS + tt];
+            dd += (double)xl[h * TS + tt];
+        }
+        dA_part[(bb * ntile + tile) * H + h] = da;
+        dD_part[(bb * ntile + tile) * H + h] = dd;
+    }
+}
+
+// dA[h], dD[h]: sums of the rows partial sums, one workgroup per head (fp64)
+__global__ void __launch_bounds__(256) reduce_rows_kernel(const double* __restrict__ dA_part,
+                                                          const double* __restrict__ dD_part, float* __restrict__ dA,
+                                                          float* __restrict__ dD, int64_t rows, int H) {
+    __shared__ double red[2][256];
+    const int tid = threadIdx.x, h = blockIdx.x;
+    double sa = 0.0, sd = 0.0;
+    for (int64_t r = tid; r < rows; r += 256) {
+        sa += dA_part[r * H + h];
+        sd += dD_part[r * H + h];
+    }
+    red[0][tid] = sa;
+    red[1][tid] = sd;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) {
+            red[0][tid] += red[0][tid + s];
+            red[1][tid] += red[1][tid + s];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        dA[h] = (float)red[0][0];
+        if (dD) dD[h] = (float)red[1][0];
+    }
+}
+
+inline size_t finish_tile_lds(int H) { return (size_t)4 * H * (kFinTok + 1) * 4; }
+
 template <class T>
 __global__ void __launch_bounds__(256) dh0_kernel(const float* __restrict__ G0, const T* __restrict__ dt,
                                                   const float* __restrict__ A, const float* __restrict__ dfinal,
@@ -647,10 +725,20 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
         BWD_CHECK((launch_combine<T, bf16, bf16>(dy, x, dt, B, C, D, nullptr, v_r, w, dx, dB, dC, q, nullptr, dxy, b, L,
                                                  L, H, P, N, G, st, false)));
     }
-    hipLaunchKernelGGL(finish_kernel<T>, dim3((unsigned)H, (unsigned)b), dim3(256), 0, st, q, R, dxy,
-                       static_cast<const T*>(dt), A, static_cast<T*>(ddt), dA_part, dD_part, L, H);
-    BWD_CHECK(hipGetLastError());
-    hipLaunchKernelGGL(reduce_kernel, grid1(H), dim3(256), 0, st, dA_part, dD_part, dA, dD, b, H);
+    if (finish_tile_lds(H) <= 64 * 1024) {
+        const int64_t ntile = (L + kFinTok - 1) / kFinTok;
+        hipLaunchKernelGGL(finish_tile_kernel<T>, dim3((unsigned)ntile, (unsigned)b), dim3(256), finish_tile_lds(H),
+                           st, q, R, dxy, static_cast<const T*>(dt), A, static_cast<T*>(ddt), dA_part, dD_part, L, H,
+                           ntile);
+        BWD_CHECK(hipGetLastError());
+        hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)H), dim3(256), 0, st, dA_part, dD_part, dA, dD,
+                           b * ntile, H);
+    } else {
+        hipLaunchKernelGGL(finish_kernel<T>, dim3((unsigned)H, (unsigned)b), dim3(256), 0, st, q, R, dxy,
+                           static_cast<const T*>(dt), A, static_cast<T*>(ddt), dA_part, dD_part, L, H);
+        BWD_CHECK(hipGetLastError());
+        hipLaunchKernelGGL(reduce_kernel, grid1(H), dim3(256), 0, st, dA_part, dD_part, dA, dD, b, H);
+    }
     BWD_CHECK(hipGetLastError());
     if (dh0) {
         hipLaunchKernelGGL(dh0_kernel<T>, grid1(b * H * PN), dim3(256), 0, st, G0, static_cast<const T*>(dt), A,
@@ -803,7 +891,9 @@ BackwardLayout backward_layout(const Shape& s) {
     f.u_r = take(f.local ? 0 : RLHP / 4 * osz), f.v_r = take((f.local ? BLHN : RLHN) / 4 * osz);
     f.w = take(BLHN / 4 * osz);
     f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS), f.fscr = take(HS);
-    f.q = take(BLH), f.dlam = take(f.local ? 0 : BLH), f.dxy = take(BLH), f.dA_part = take(BH8), f.dD_part = take(BH8);
+    // per-(b, head) partial sums of dA and dD; per (b, 32-token tile, head) in the local flow
+    const size_t PART = f.local ? (size_t)(s.b * ((s.L + 31) / 32) * s.H) * 8 : BH8;
+    f.q = take(BLH), f.dlam = take(f.local ? 0 : BLH), f.dxy = take(BLH), f.dA_part = take(PART), f.dD_part = take(PART);
     f.states_b = take(f.local ? ST : 0), f.R = take(f.local ? BLH : 0);
     // the half-head transposed scans (local flow): per half-head steps, A, and chunk cumsum arrays at their chunk
     f.Qt = f.local ? transposed_chunk(s) : 0;
