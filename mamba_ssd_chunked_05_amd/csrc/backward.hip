@@ -88,16 +88,6 @@ __global__ void __launch_bounds__(256) ones_kernel(float* __restrict__ dt_t, int
     dt_t[i] = pos < L ? 1.0f : 0.0f;
 }
 
-// out[i, 2h + k] = in[i, h] (k = 0, 1): per-head values for the two half-heads of every head
-__global__ void __launch_bounds__(256) dup_kernel(const float* __restrict__ in, float* __restrict__ out, int H,
-                                                  int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    const int64_t r = i / (2 * H);
-    const int h2 = (int)(i % (2 * H));
-    out[i] = in[r * H + (h2 >> 1)];
-}
-
 // One workgroup per (b, t), all heads: dx = dt u + D dy; per head q = v . B (= x^T G B), d lambda =
 // C . w - dt q and dy . x; per group dB = sum_h dt v and dC = sum_h w.  Wavefront wv takes heads
 // wv, wv + 4, ... (lanes over p and n) and reads each element of u, v, w once: the group sums
@@ -595,25 +585,68 @@ hipError_t scan_in(const Shape& s, int in_io, int xrep, const void* xin, const v
     return launch_chunk_scan_in(s, in_io, xrep, xin, Bin, Cin, dt_t, cs, states, nullptr, y, st);
 }
 
+// dh0 = a_0 G_0 from the transposed adjoint of a transposed scan's final state G0T (b, (N / 64) H, 64, P):
+// element (p, n) of head h sits at half-head h (N / 64) + n / 64, row n % 64; with no tokens dh0 = dfinal
+template <class T>
+__global__ void __launch_bounds__(256) dh0_tr_kernel(const float* __restrict__ G0T, const T* __restrict__ dt,
+                                                     const float* __restrict__ A, const float* __restrict__ dfinal,
+                                                     float* __restrict__ dh0, int64_t L, int H, int P, int N,
+                                                     int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int nn = (int)(i % N);
+    const int p = (int)((i / N) % P);
+    const int64_t bh = i / ((int64_t)P * N);
+    const int h = (int)(bh % H);
+    const int64_t bb = bh / H;
+    if (L == 0) {
+        dh0[i] = dfinal ? dfinal[i] : 0.0f;
+        return;
+    }
+    const float g = G0T[((bh * (N / 64) + nn / 64) * 64 + nn % 64) * P + p];
+    dh0[i] = fast_exp2(to_f32(dt[(bb * L) * H + h]) * A[h] * kLog2e) * g;
+}
+
 // The backward with the decay gradient formed chunk by chunk (decay_grad.hip), for bf16 io with headdim
 // 64 and dstate 64 or 128.  The decay gradient then needs no long suffix sum, so the transposed scans
-// (c) and (d), which only feed dB, dC and q, run in bf16 compute.  The reversed scans read the inputs in
-// place, backwards (XMap::rows), over Lr tokens: the sequence front-padded to whole chunks (the padding
-// reads as zero), so that every reversed chunk is a forward chunk read backwards and the adjoint scan's
-// chunk-start states are the adjoints entering the forward chunks.
+// (c) and (d), which only feed dB, dC and q, run in bf16 compute.  Every scan reads the inputs in place
+// and uses sub-chunk-local decay arrays (exact in-chunk decays at any chunk length).  The reversed scans
+// walk the inputs backwards (XMap::rows) over Lr tokens, the sequence front-padded to whole backward
+// chunks of Q tokens (the padding reads as zero), so that every reversed Q-chunk is a forward Q-chunk read
+// backwards.  The decay gradient needs, at every Q-chunk, the forward state entering it (S0) and the
+// adjoint entering it from the next one: both are stored every Q tokens by kernels that carry the state
+// in registers at the transposed scans' large chunk (hi/lo state updates), started from the transposed
+// scans' chunk-start states -- no Q-chunk local states and no pass over them.
 hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, const void* dt, const float* A,
                      const void* B, const void* C, const float* D, const float* h0, const void* dy,
                      const float* dfinal, void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0,
                      char* ws, hipStream_t st) {
     using T = bf16;
-    const int64_t b = s.b, L = s.L, Lr = f.Lr, pad = f.Lr - s.L;
+    const int64_t b = s.b, L = s.L, Lr = f.Lr;
     const int H = (int)s.H, P = (int)s.P, N = (int)s.N, G = (int)s.G;
+    const int nh = N / 64, H2 = nh * H, hpg = H / G;
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-    float *drev = F(f.drev), *dfwd = F(f.dfwd), *dt_t = F(f.dt_t), *cs = F(f.cs);
-    float *states = F(f.states), *states_b = F(f.states_b), *R = F(f.R), *G0 = F(f.G0), *dfT = F(f.dfT);
-    float *h0T = F(f.h0T), *finT = F(f.finT), *fscr = F(f.fscr), *q = F(f.q), *dxy = F(f.dxy);
-    T *v_r = reinterpret_cast<T*>(ws + f.v_r), *w = reinterpret_cast<T*>(ws + f.w);
+    float *dt_t = F(f.dt_t), *cs = F(f.cs), *states = F(f.states), *states_b = F(f.states_b), *R = F(f.R);
+    float *G0T = F(f.G0), *dfT = F(f.dfT), *h0T = F(f.h0T), *finT = F(f.finT), *q = F(f.q), *dxy = F(f.dxy);
+    float *totals = F(f.totals), *stT = F(f.stT);
+    T *v = reinterpret_cast<T*>(ws + f.v_r), *w = reinterpret_cast<T*>(ws + f.w);
     double *dA_part = reinterpret_cast<double*>(ws + f.dA_part), *dD_part = reinterpret_cast<double*>(ws + f.dD_part);
+    // the sub-chunk-local decay arrays (dtl, lw pairs): reversed per head (b), reversed per half-head (c),
+    // forwards per half-head (d), forwards per head (S0); the per-head and per-half-head ones coincide at N = 64
+    // (a pair for k heads over n sub-chunks: dtl, then lw, each b k n 64 floats; local_decay_floats sizes them)
+    const int64_t nsr = Lr / 64, nsf = (L + 63) / 64;
+    float* at = F(f.sub);
+    auto pair = [&](int64_t heads, int64_t nsub) {
+        float* p = at;
+        at += 2 * b * heads * nsub * 64;
+        return p;
+    };
+    float* rl = pair(H, nsr);
+    float* rh = nh == 2 ? pair(H2, nsr) : rl;
+    float* fh = pair(H2, nsf);
+    float* ff = nh == 2 ? pair(H, nsf) : fh;
+    auto dtl = [](float* p) { return p; };
+    auto lwp = [](float* p, int64_t heads, int64_t nsub, int64_t bb) { return p + bb * heads * nsub * 64; };
     const int64_t PN = (int64_t)P * N;
     hipError_t e;
 #define BWD_CHECK(expr)                \
@@ -621,93 +654,71 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
         e = (expr);                    \
         if (e != hipSuccess) return e; \
     } while (0)
-    hipLaunchKernelGGL(steps_kernel<T>, grid1(b * Lr * H), dim3(256), 0, st, static_cast<const T*>(dt), drev, dfwd, L,
-                       pad, H, b * Lr * H);
-    BWD_CHECK(hipGetLastError());
     hipLaunchKernelGGL(transpose_kernel, grid1(b * H * PN), dim3(256), 0, st, dfinal, dfT, P, N, b * H * PN);
     BWD_CHECK(hipGetLastError());
     hipLaunchKernelGGL(transpose_kernel, grid1(b * H * PN), dim3(256), 0, st, h0, h0T, P, N, b * H * PN);
     BWD_CHECK(hipGetLastError());
 
-    const DtFront none{nullptr, 0, 0, 0, 0.0f, 0.0f};
-    Shape sf = s;  // the forward direction: decay arrays from fp32 steps, bf16 chunk kernels
-    sf.io = 0;
-    Shape s16 = s;
-    Shape sr = s;  // the reversed direction over Lr tokens (nC chunks, as forwards)
-    sr.L = Lr;
-    sr.io = 0;
-    Shape sr16 = sr;
-    sr16.io = 1;
-    Shape sT16 = s;  // the transposed scans: headdim N, dstate P, one group per head, bf16 compute
-    sT16.P = N;
-    sT16.N = P;
-    sT16.G = H;
-    const int hpg = H / G;
-    // reversed direction: decay steps d', input step 1
-    BWD_CHECK(launch_chunk_cumsum(sr, none, drev, A, dt_t, cs, st));
-    hipLaunchKernelGGL(ones_kernel, grid1(b * H * s.nC * s.Q), dim3(256), 0, st, dt_t, Lr, (int)s.Q, s.nC,
-                       b * H * s.nC * s.Q);
-    BWD_CHECK(hipGetLastError());
-    // (b) the adjoint: dx = dt u + D dy written by the scan itself (u = G B, dt as the output row scale, D
-    // on the x-role dy), its final value G0 (dh0) and the chunk-start adjoints kept in states_b
-    const XMap xb{H, 1, 1, L, dt};  // dy, C and B read backwards, dx written forwards
-    BWD_CHECK(launch_chunk_state_fast(sr16, dy, C, dt_t, cs, states_b, st, &xb));
-    BWD_CHECK(launch_state_passing(sr16, states_b, cs, dfinal, G0, st));
-    BWD_CHECK(launch_chunk_scan_fast(sr16, dy, C, B, dt_t, cs, states_b, D, dx, st, &xb));
-    // (c) G^T read out through x: v (dB, q), on the fast chunk kernels as nh H heads of headdim 64 (nh = N / 64:
-    // at dstate 128 each head splits into two half-heads, the two halves of the state's N rows, which form
-    // one head pair) whose x is (that half of) B or C of the head's group
-    const int nh = N / 64;
-    const XMap xm{nh * G, nh * hpg, nh, 0, nullptr};   // (d): forwards
-    const XMap xmr{nh * G, nh * hpg, nh, L, nullptr};  // (c): read backwards, v written forwards
-    Shape sh = sT16;
-    sh.H = nh * H;
+    Shape sk = s;  // decay-array shapes: (b, tokens, kernel heads)
+    sk.L = Lr;
+    BWD_CHECK(launch_subchunk_decay_bwd(sk, dt, A, dtl(rl), lwp(rl, H, nsr, b), L, 1, true, true, st));
+    if (nh == 2) {
+        sk.H = H2;
+        BWD_CHECK(launch_subchunk_decay_bwd(sk, dt, A, dtl(rh), lwp(rh, H2, nsr, b), L, 2, true, true, st));
+    }
+    sk.L = L;
+    sk.H = H2;
+    BWD_CHECK(launch_subchunk_decay_bwd(sk, dt, A, dtl(fh), lwp(fh, H2, nsf, b), L, nh, false, false, st));
+    if (nh == 2) {
+        sk.H = H;
+        BWD_CHECK(launch_subchunk_decay_bwd(sk, dt, A, dtl(ff), lwp(ff, H, nsf, b), L, 1, false, false, st));
+    }
+
+    // (c) G^T read out through x: v (dB, q), as H2 half-heads of headdim 64 (at dstate 128 each head splits
+    // into the two halves of the state's N rows, which form one head pair) whose x is (that half of) C of
+    // the head's group; reversed, written forwards.  Its chunk-start states seed the adjoint scan (b) and
+    // its final state is the adjoint at the first token (dh0).
+    Shape sh = s;
+    sh.H = H2;
     sh.P = 64;
     sh.N = P;
     sh.G = H;
     sh.L = Lr;
     sh.Q = f.Qt;
     sh.nC = (Lr + f.Qt - 1) / f.Qt;
-    Shape shf = sh;  // their decay arrays come from fp32 steps
-    shf.io = 0;
-    float *d2 = F(f.d2), *A2 = F(f.A2), *dt2 = F(f.dt2), *cs2 = F(f.cs2);
-    const float* Ah = A;  // A and the steps per (half-)head
-    const float* drh = drev;
-    if (nh == 2) {
-        hipLaunchKernelGGL(dup_kernel, grid1(2 * H), dim3(256), 0, st, A, A2, H, (int64_t)2 * H);
-        BWD_CHECK(hipGetLastError());
-        hipLaunchKernelGGL(dup_kernel, grid1(b * Lr * 2 * H), dim3(256), 0, st, drev, d2, H, b * Lr * 2 * H);
-        BWD_CHECK(hipGetLastError());
-        Ah = A2;
-        drh = d2;
-    }
-    BWD_CHECK(launch_chunk_cumsum(shf, none, drh, Ah, dt2, cs2, st));
-    hipLaunchKernelGGL(ones_kernel, grid1(b * sh.H * sh.nC * sh.Q), dim3(256), 0, st, dt2, Lr, (int)sh.Q, sh.nC,
-                       b * sh.H * sh.nC * sh.Q);
-    BWD_CHECK(hipGetLastError());
-    BWD_CHECK(launch_chunk_state_fast(sh, C, dy, dt2, cs2, states, st, &xmr));
-    BWD_CHECK(launch_state_passing(sh, states, cs2, dfT, fscr, st));
-    BWD_CHECK(launch_chunk_scan_fast(sh, C, dy, x, dt2, cs2, states, nullptr, v_r, st, &xmr));
-    // forward direction: the chunk-start states S0 (hi/lo chunk states, fp32 pass), then the decay gradient
-    BWD_CHECK(launch_chunk_cumsum(sf, none, dfwd, A, dt_t, cs, st));
-    BWD_CHECK(launch_chunk_state(s16, x, B, dt_t, cs, states, st));
-    BWD_CHECK(launch_state_passing(s16, states, cs, h0, fscr, st));
-    BWD_CHECK(launch_decay_grad(s16, x, dy, B, C, cs, dt_t, states, states_b, R, st));
-    // (d) S^T read out through dy: w (dC), as half-heads like (c), forwards in time
+    Shape s1 = sh;  // the pass over the chunk totals: a chunk of "length 1" in its indexing
+    s1.Q = 1;
+    const XMap xmr{nh * G, nh * hpg, nh, L, nullptr, nullptr, 0, 0};
+    BWD_CHECK(launch_chunk_state_sub(sh, C, dy, dtl(rh), lwp(rh, H2, nsr, b), stT, totals, st, &xmr));
+    BWD_CHECK(launch_state_passing(s1, stT, totals, dfT, G0T, st));
+    BWD_CHECK(launch_chunk_scan_sub(sh, C, dy, x, dtl(rh), lwp(rh, H2, nsr, b), stT, nullptr, v, st, &xmr));
+    // (b) the adjoint G read out through B: dx = dt u + D dy written by the scan itself (u = G B, dt as the
+    // output row scale, D on the x-role dy), started from (c)'s states and storing the adjoint entering
+    // every Q-chunk in states_b
+    Shape sb = s;
+    sb.L = Lr;
+    sb.Q = f.Qt;
+    sb.nC = sh.nC;
+    const XMap xb{H, 1, 1, L, dt, states_b, (int)s.Q, 1};
+    BWD_CHECK(launch_chunk_scan_sub(sb, dy, C, B, dtl(rl), lwp(rl, H, nsr, b), stT, D, dx, st, &xb));
+    // (d) S^T read out through dy: w (dC), as half-heads like (c), forwards in time; its chunk-start states
+    // seed the walk that stores the forward state entering every Q-chunk (S0)
     sh.L = L;
     sh.nC = (L + f.Qt - 1) / f.Qt;
-    shf = sh;
-    shf.io = 0;
-    const float* dfh = dfwd;
-    if (nh == 2) {
-        hipLaunchKernelGGL(dup_kernel, grid1(b * L * 2 * H), dim3(256), 0, st, dfwd, d2, H, b * L * 2 * H);
-        BWD_CHECK(hipGetLastError());
-        dfh = d2;
-    }
-    BWD_CHECK(launch_chunk_cumsum(shf, none, dfh, Ah, dt2, cs2, st));
-    BWD_CHECK(launch_chunk_state_fast(sh, B, x, dt2, cs2, states, st, &xm));
-    BWD_CHECK(launch_state_passing(sh, states, cs2, h0 ? h0T : nullptr, finT, st));
-    BWD_CHECK(launch_chunk_scan_fast(sh, B, x, dy, dt2, cs2, states, nullptr, w, st, &xm));
+    s1 = sh;
+    s1.Q = 1;
+    const XMap xm{nh * G, nh * hpg, nh, 0, nullptr, nullptr, 0, 0};
+    BWD_CHECK(launch_chunk_state_sub(sh, B, x, dtl(fh), lwp(fh, H2, nsf, b), stT, totals, st, &xm));
+    BWD_CHECK(launch_state_passing(s1, stT, totals, h0 ? h0T : nullptr, finT, st));
+    BWD_CHECK(launch_chunk_scan_sub(sh, B, x, dy, dtl(fh), lwp(fh, H2, nsf, b), stT, nullptr, w, st, &xm));
+    Shape sw = s;
+    sw.Q = f.Qt;
+    sw.nC = sh.nC;
+    const XMap xw{H, 1, 1, 0, nullptr, states, (int)s.Q, 1};
+    BWD_CHECK(launch_chunk_walk(sw, x, B, dtl(ff), lwp(ff, H, nsf, b), stT, st, xw));
+    // the decay gradient, chunk by chunk at Q, from its chunk cumsum arrays and the stored states
+    BWD_CHECK(launch_chunk_cumsum(s, DtFront{nullptr, 0, 0, 0, 0.0f, 0.0f}, dt, A, dt_t, cs, st));
+    BWD_CHECK(launch_decay_grad(s, x, dy, B, C, cs, dt_t, states, states_b, R, st));
 
     const size_t lq = (size_t)32 * G * N * 4;  // the quad combine's LDS slices
     if (P == 64 && (N == 64 || N == 128) && H % 4 == 0 && lq <= 64 * 1024) {
@@ -716,13 +727,13 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
         bf16 *dBb = static_cast<bf16*>(dB), *dCb = static_cast<bf16*>(dC);
         if (N == 128)
             hipLaunchKernelGGL(combine_quad_kernel<128>, dim3((unsigned)(b * L)), dim3(256), lq, st, dyb, xb2, dtb, Bb,
-                               v_r, w, dBb, dCb, q, dxy, L, H, G);
+                               v, w, dBb, dCb, q, dxy, L, H, G);
         else
             hipLaunchKernelGGL(combine_quad_kernel<64>, dim3((unsigned)(b * L)), dim3(256), lq, st, dyb, xb2, dtb, Bb,
-                               v_r, w, dBb, dCb, q, dxy, L, H, G);
+                               v, w, dBb, dCb, q, dxy, L, H, G);
         BWD_CHECK(hipGetLastError());
     } else {
-        BWD_CHECK((launch_combine<T, bf16, bf16>(dy, x, dt, B, C, D, nullptr, v_r, w, dx, dB, dC, q, nullptr, dxy, b, L,
+        BWD_CHECK((launch_combine<T, bf16, bf16>(dy, x, dt, B, C, D, nullptr, v, w, dx, dB, dC, q, nullptr, dxy, b, L,
                                                  L, H, P, N, G, st, false)));
     }
     if (finish_tile_lds(H) <= 64 * 1024) {
@@ -741,10 +752,11 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     }
     BWD_CHECK(hipGetLastError());
     if (dh0) {
-        hipLaunchKernelGGL(dh0_kernel<T>, grid1(b * H * PN), dim3(256), 0, st, G0, static_cast<const T*>(dt), A,
-                           dfinal, dh0, L, H, PN, b * H * PN);
+        hipLaunchKernelGGL(dh0_tr_kernel<T>, grid1(b * H * PN), dim3(256), 0, st, G0T, static_cast<const T*>(dt), A,
+                           dfinal, dh0, L, H, P, N, b * H * PN);
         BWD_CHECK(hipGetLastError());
     }
+    (void)H2;
 #undef BWD_CHECK
     return hipSuccess;
 }
@@ -865,43 +877,44 @@ BackwardLayout backward_layout(const Shape& s) {
     auto a256 = [](size_t v) { return (v + 255) / 256 * 256; };
     BackwardLayout f{};
     f.local = decay_grad_supported(s);
-    f.Lr = f.local ? s.nC * s.Q : s.L;  // the reversed copies: front-padded to whole chunks when local
-    const size_t sz = s.io == 1 ? 2 : 4;  // the reversed copies keep the input dtype
-    const size_t BLHP = (size_t)(s.b * s.L * s.H * s.P) * 4, BLHN = (size_t)(s.b * s.L * s.H * s.N) * 4;
-    const size_t RLHP = (size_t)(s.b * f.Lr * s.H * s.P) * 4, RLHN = (size_t)(s.b * f.Lr * s.H * s.N) * 4;
-    const size_t RLGN = (size_t)(s.b * f.Lr * s.G * s.N), BLH = (size_t)(s.b * s.L * s.H) * 4;
-    const size_t RLH = (size_t)(s.b * f.Lr * s.H) * 4;
+    f.Lr = f.local ? s.nC * s.Q : s.L;  // the reversed walks: front-padded to whole chunks when local
+    const size_t BLHN = (size_t)(s.b * s.L * s.H * s.N) * 4, BLH = (size_t)(s.b * s.L * s.H) * 4;
     const size_t CS = (size_t)(s.b * s.H * s.nC * s.Q) * 4, ST = (size_t)(s.b * s.nC * s.H * s.P * s.N) * 4;
     const size_t HS = (size_t)(s.b * s.H * s.P * s.N) * 4, BH8 = (size_t)(s.b * s.H) * 8;
-    (void)BLHP;
     size_t o = 0;
     auto take = [&](size_t bytes) {
         const size_t at = o;
         o += a256(bytes);
         return at;
     };
-    // the time-reversed copies of the fp32-scan flow (the local flow reads the inputs backwards in place)
-    const size_t cp = f.local ? 0 : 1;
-    f.xr = take(cp * RLHP / 4 * sz), f.dyr = take(cp * RLHP / 4 * sz), f.Cr = take(cp * RLGN * sz);
-    f.Br = take(cp * RLGN * sz);
-    f.drev = take(RLH), f.dfwd = take(BLH), f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST);
-    // the scans' outputs: bf16 in the local flow (u always comes from the bf16 kernels there), fp32 otherwise
-    const size_t osz = f.local ? 2 : 4;
-    // (the local flow: the adjoint scan writes dx itself, and v is written in forward time)
-    f.u_r = take(f.local ? 0 : RLHP / 4 * osz), f.v_r = take((f.local ? BLHN : RLHN) / 4 * osz);
-    f.w = take(BLHN / 4 * osz);
-    f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS), f.fscr = take(HS);
-    // per-(b, head) partial sums of dA and dD; per (b, 32-token tile, head) in the local flow
-    const size_t PART = f.local ? (size_t)(s.b * ((s.L + 31) / 32) * s.H) * 8 : BH8;
-    f.q = take(BLH), f.dlam = take(f.local ? 0 : BLH), f.dxy = take(BLH), f.dA_part = take(PART), f.dD_part = take(PART);
-    f.states_b = take(f.local ? ST : 0), f.R = take(f.local ? BLH : 0);
-    // the half-head transposed scans (local flow): per half-head steps, A, and chunk cumsum arrays at their chunk
-    f.Qt = f.local ? transposed_chunk(s) : 0;
-    const int64_t nct = f.local ? (f.Lr + f.Qt - 1) / f.Qt : 0;
-    const int64_t nhh = s.N / 64 * s.H;  // heads of the transposed scans
-    f.d2 = take(f.local ? (size_t)(s.b * f.Lr * nhh) * 4 : 0), f.A2 = take(f.local ? (size_t)nhh * 4 : 0);
-    f.dt2 = take(f.local ? (size_t)(s.b * nhh * nct * f.Qt) * 4 : 0);
-    f.cs2 = take(f.local ? (size_t)(s.b * nhh * nct * f.Qt) * 4 : 0);
+    if (f.local) {
+        // chunk cumsum arrays and the stored states at the backward's chunk Q, the scans' bf16 outputs v and
+        // w (forward time), the transposed final states, per-token q, dy.x and R, per-tile partial sums
+        f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST), f.states_b = take(ST);
+        f.v_r = take(BLHN / 2), f.w = take(BLHN / 2);
+        f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS);
+        f.q = take(BLH), f.dxy = take(BLH), f.R = take(BLH);
+        const size_t PART = (size_t)(s.b * ((s.L + 31) / 32) * s.H) * 8;
+        f.dA_part = take(PART), f.dD_part = take(PART);
+        // the large-chunk scans: sub-chunk-local decay arrays (reversed per head and per half-head, forwards
+        // per half-head and per head), chunk totals and chunk-start states (transposed, per half-head)
+        f.Qt = transposed_chunk(s);
+        const int64_t nh = s.N / 64, H2 = nh * s.H, nsr = f.Lr / 64, nsf = (s.L + 63) / 64;
+        const int64_t heads_r = s.H + (nh == 2 ? H2 : 0), heads_f = H2 + (nh == 2 ? s.H : 0);
+        f.sub = take((size_t)(2 * s.b * 64 * (heads_r * nsr + heads_f * nsf)) * 4);
+        const int64_t nct = (f.Lr + f.Qt - 1) / f.Qt;  // at least the forward chunk count (L <= Lr)
+        f.totals = take((size_t)(s.b * H2 * nct) * 4);
+        f.stT = take((size_t)(s.b * nct * s.H * s.N * s.P) * 4);
+    } else {
+        const size_t sz = s.io == 1 ? 2 : 4;  // the reversed copies keep the input dtype
+        const size_t RLHP = (size_t)(s.b * f.Lr * s.H * s.P) * 4, RLHN = (size_t)(s.b * f.Lr * s.H * s.N) * 4;
+        const size_t RLGN = (size_t)(s.b * f.Lr * s.G * s.N), RLH = (size_t)(s.b * f.Lr * s.H) * 4;
+        f.xr = take(RLHP / 4 * sz), f.dyr = take(RLHP / 4 * sz), f.Cr = take(RLGN * sz), f.Br = take(RLGN * sz);
+        f.drev = take(RLH), f.dfwd = take(BLH), f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST);
+        f.u_r = take(RLHP), f.v_r = take(RLHN), f.w = take(BLHN);
+        f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS), f.fscr = take(HS);
+        f.q = take(BLH), f.dlam = take(BLH), f.dxy = take(BLH), f.dA_part = take(BH8), f.dD_part = take(BH8);
+    }
     f.total = o;
     return f;
 }

@@ -210,9 +210,10 @@ struct ScanLds {
 };
 
 
-// FWD: the forward's variant, reading sub-chunk-local decay arrays (subchunk_decay_kernel).
-// REV: the inputs are walked backwards (XMap::rows).
-template <int N, int HPW, bool FWD, bool REV = false>
+// FWD: sub-chunk-local decay arrays (subchunk_decay_kernel), as the forward reads them.
+// REV (with FWD): the inputs are walked backwards and the output written forwards (XMap::rows); TAP
+// (with REV): the carried state is stored every XMap::tapq positions, with a hi/lo state update.
+template <int N, int HPW, bool FWD, bool REV = false, bool TAP = false>
 __global__ void __launch_bounds__(256, 2)
 chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, const bf16* __restrict__ C,
                        DtSrc ds, const float* __restrict__ start, const float* __restrict__ D, bf16* __restrict__ y, int64_t L,
@@ -241,12 +242,26 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
 
     // carried state per head, transposed: st[hh][nt] holds S[p = 16w + l16][n = 16nt + 4g4 + r]
     f32x4 st[HPW][NT];
+    if (REV && xm.start_tr) {  // a transposed scan's states: element (p, n) of head h at half-head n / 64, row n % 64
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-        const float* S0 =
-            start + ((b * nC + c) * H + h0 + hh) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 4 * g4;
+        for (int hh = 0; hh < HPW; ++hh) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) st[hh][nt] = *reinterpret_cast<const f32x4*>(S0 + 16 * nt);
+            for (int nt = 0; nt < NT; ++nt) {
+                const int n = 16 * nt + 4 * g4;
+                const float* S0 = start + (((b * nC + c) * H + h0 + hh) * (N / 64) + n / 64) * (int64_t)64 * P +
+                                  (int64_t)(n % 64) * P + 16 * w + l16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[hh][nt][r] = S0[r * P];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+            const float* S0 =
+                start + ((b * nC + c) * H + h0 + hh) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 4 * g4;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) st[hh][nt] = *reinterpret_cast<const f32x4*>(S0 + 16 * nt);
+        }
     }
     // tiles above the diagonal that pair with a diagonal tile in a 32-wide K step stay zero
     for (int e = tid; e < HPW * 256; e += 256) {
@@ -278,6 +293,15 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
 
     for (int sc = 0; sc < nsub; ++sc) {
         const int64_t tbase = t0 + (int64_t)sc * QS;
+        if (TAP && tbase % xm.tapq == 0) {  // the state entering this position
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh) {
+                float* out = xm.tap + ((b * ((L + xm.tapq - 1) / xm.tapq) + tbase / xm.tapq) * H + h0 + hh) * (int64_t)P * N +
+                             (int64_t)(16 * w + l16) * N + 4 * g4;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(out + 16 * nt) = st[hh][nt];
+            }
+        }
         __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
         chunk_store<N, HPW, true, FWD>(sm.xs, sm.bs, sm.cs, sm.lw, sm.dtw, sm.ww, sm.ec, sm.alpha, rg, ad, cs_prev,
                                        tot, tid);
@@ -432,14 +456,20 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             // token slots of this K step: 32ks + 4g4 + r (slots 0..3) and 32ks + 16 + 4g4 + r (slots 4..7)
-            Frag<bf16> xw[HPW];
+            Frag<bf16> xw[HPW], xl[TAP ? HPW : 1];
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
                 const float* wv = &sm.ww[hh * QS + 32 * ks + 4 * g4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    xw[hh].v[r] = static_cast<bf16>(static_cast<float>(xf[ks][hh].v[r]) * wv[r]);
-                    xw[hh].v[4 + r] = static_cast<bf16>(static_cast<float>(xf[ks][hh].v[4 + r]) * wv[16 + r]);
+                    const float v0 = static_cast<float>(xf[ks][hh].v[r]) * wv[r];
+                    const float v1 = static_cast<float>(xf[ks][hh].v[4 + r]) * wv[16 + r];
+                    xw[hh].v[r] = static_cast<bf16>(v0);
+                    xw[hh].v[4 + r] = static_cast<bf16>(v1);
+                    if (TAP) {
+                        xl[hh].v[r] = static_cast<bf16>(v0 - static_cast<float>(xw[hh].v[r]));
+                        xl[hh].v[4 + r] = static_cast<bf16>(v1 - static_cast<float>(xw[hh].v[4 + r]));
+                    }
                 }
             }
             Frag<bf16> a[NT];  // every B^T fragment of this K step in flight before the products
@@ -451,7 +481,10 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-                for (int hh = 0; hh < HPW; ++hh) mma(st[hh][nt], a[nt], xw[hh]);
+                for (int hh = 0; hh < HPW; ++hh) {
+                    mma(st[hh][nt], a[nt], xw[hh]);
+                    if (TAP) mma(st[hh][nt], a[nt], xl[TAP ? hh : 0]);
+                }
             }
         }
     }
@@ -607,6 +640,148 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
 }
 
 // ---------------------------------------------------------------------------
+// chunk walk: the states entering every tapq-th position, from the chunk-start states
+// ---------------------------------------------------------------------------
+template <int N, int HPW>
+struct WalkLds {
+    bf16 xs[HPW * QS * XS];
+    bf16 bs[QS * Strides<N>::BS];
+    float lw[HPW * QS];
+    float dtw[HPW * QS];
+    float ww[HPW * QS];
+    float alpha[4];
+};
+
+// Per (b, chunk, head pair): carry the fp32 state from the chunk-start state over the chunk's 64-token
+// sub-chunks, S <- 2^(l_63) S + B^T (w x) with w_j = 2^(l_63 - l_j) dt_j and the scaled operand split into
+// hi + lo bf16, and store it (XMap::tap) at every position that is a multiple of XMap::tapq: the
+// chunk-start states of a tapq-chunking with neither chunk-local states nor a pass over them.  Reads
+// sub-chunk-local decay arrays (subchunk_decay_kernel); XMap::start_tr as for the chunk scan.
+template <int N, int HPW>
+__global__ void __launch_bounds__(256, 2)
+chunk_walk_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, DtSrc ds, const float* __restrict__ start,
+                       int64_t L, int H, int G, int Q, int64_t nC, uint32_t nitems, XMap xm) {
+    constexpr int NT = N / 16;
+    constexpr int BS = Strides<N>::BS;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    WalkLds<N, HPW>& sm = *reinterpret_cast<WalkLds<N, HPW>*>(smem_raw);
+
+    const int HP = H / HPW;
+    const uint32_t item = xcd_remap(blockIdx.x, nitems);
+    const int hp = (int)(item % (uint32_t)HP);
+    const int64_t c = (item / (uint32_t)HP) % (uint32_t)nC;
+    const int64_t b = item / ((uint32_t)HP * (uint32_t)nC);
+    const int h0 = hp * HPW;
+    const int g = h0 / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, in a scalar register
+    const int64_t t0 = c * Q;
+    const int64_t t_end = t0 + Q < L ? t0 + Q : L;
+    const int nsub = (int)((t_end - t0 + QS - 1) / QS);
+    float cs_prev = 0.0f, tot = 0.0f;
+
+    f32x4 st[HPW][NT];  // st[hh][nt] holds S[p = 16w + l16][n = 16nt + 4g4 + r]
+    if (xm.start_tr) {
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int n = 16 * nt + 4 * g4;
+                const float* S0 = start + (((b * nC + c) * H + h0 + hh) * (N / 64) + n / 64) * (int64_t)64 * P +
+                                  (int64_t)(n % 64) * P + 16 * w + l16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[hh][nt][r] = S0[r * P];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+            const float* S0 =
+                start + ((b * nC + c) * H + h0 + hh) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 4 * g4;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) st[hh][nt] = *reinterpret_cast<const f32x4*>(S0 + 16 * nt);
+        }
+    }
+
+    const int64_t nsubT = (L + QS - 1) / QS;
+    const int64_t dt_head = nsubT * QS;
+    const int64_t dt0 = ((b * H + h0) * nsubT + c * (Q / QS)) * QS;
+    const int64_t ntap = (L + xm.tapq - 1) / xm.tapq;
+    const int xh0 = h0 / xm.div * xm.mul;
+    ChunkAddr<N, HPW> ad;
+    chunk_addr<N, HPW>(ad, xm.hx, G, dt_head, tid);
+    ChunkRegs<N, HPW, false> rg;
+    chunk_load<N, HPW, false>(rg, ad, tile_base<false>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, t0, 0), xm.hx,
+                              G, tid);
+
+    for (int sc = 0; sc < nsub; ++sc) {
+        const int64_t tbase = t0 + (int64_t)sc * QS;
+        if (tbase % xm.tapq == 0) {  // the state entering this position
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh) {
+                float* out = xm.tap + ((b * ntap + tbase / xm.tapq) * H + h0 + hh) * (int64_t)P * N +
+                             (int64_t)(16 * w + l16) * N + 4 * g4;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(out + 16 * nt) = st[hh][nt];
+            }
+        }
+        __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
+        chunk_store<N, HPW, false, true>(sm.xs, sm.bs, nullptr, sm.lw, sm.dtw, sm.ww, nullptr, sm.alpha, rg, ad,
+                                         cs_prev, tot, tid);
+        __syncthreads();
+        if (sc + 1 < nsub) {
+            const int64_t t1 = tbase + QS;
+            chunk_load<N, HPW, false>(
+                rg, ad, tile_base<false>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc + 1), xm.hx, G, tid);
+        }
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+            const float alpha = sm.alpha[hh];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[hh][nt][r] *= alpha;
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            Frag<bf16> xh[HPW], xl[HPW];
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh) {
+                const bf16* xt = &sm.xs[hh * QS * XS];
+                const bf16x4 lo4 = tr_read(xt, 32 * ks + 4 * g4, 16 * w, XS, l16);
+                const bf16x4 hi4 = tr_read(xt, 32 * ks + 16 + 4 * g4, 16 * w, XS, l16);
+                const float* wv = &sm.ww[hh * QS + 32 * ks + 4 * g4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float v0 = static_cast<float>(lo4[r]) * wv[r];
+                    const float v1 = static_cast<float>(hi4[r]) * wv[16 + r];
+                    const bf16 h0v = static_cast<bf16>(v0), h1v = static_cast<bf16>(v1);
+                    xh[hh].v[r] = h0v;
+                    xh[hh].v[4 + r] = h1v;
+                    xl[hh].v[r] = static_cast<bf16>(v0 - static_cast<float>(h0v));
+                    xl[hh].v[4 + r] = static_cast<bf16>(v1 - static_cast<float>(h1v));
+                }
+            }
+            Frag<bf16> a[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                a[nt].v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * nt, BS, l16),
+                                tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * nt, BS, l16));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                for (int hh = 0; hh < HPW; ++hh) {
+                    mma(st[hh][nt], a[nt], xh[hh]);
+                    mma(st[hh][nt], a[nt], xl[hh]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // the forward's decay arrays: for every 64-token sub-chunk and head,
 //   dtl[b,h,s,i] = dt[b, 64s+i, h],   lw[b,h,s,i] = log2(e) sum_{k<=i} dt[b,64s+k,h] A[h]
 // (dt after the front-end: the input step in dtl, the decay step in lw)
@@ -616,10 +791,21 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
 // ---------------------------------------------------------------------------
 constexpr int kDecayHB = 64;  // heads per LDS block
 
+// Steps of the backward's scans (BWD): kernel head h reads dt head h / hdiv of a (b, Ls, H / hdiv) array
+// (the half-heads of a transposed scan share their head's steps and A); with rev the kernel's token t
+// (of L) takes the decay step of dt row L - t -- the reversed adjoint recurrence applies the decay of the
+// token after t, so the first real token (t = L - Ls) and the padding before it take none -- and with
+// unit the input step is 1.  Without BWD: the forward's arrays (Ls = L, hdiv = 1, no rev, no unit).
+struct DecaySrc {
+    int64_t Ls;
+    int hdiv, rev, unit;
+};
+
+template <bool BWD>
 __global__ void __launch_bounds__(256) subchunk_decay_kernel(DtFront fe, const bf16* __restrict__ dt,
                                                              const float* __restrict__ A, float* __restrict__ dtl,
                                                              float* __restrict__ lw, int64_t L, int H,
-                                                             uint32_t nitems) {
+                                                             uint32_t nitems, DecaySrc src) {
     __shared__ float blk[QS][kDecayHB + 1];
     __shared__ bool vok[QS][kDecayHB + 1];  // position inside the sequence
     const int64_t nsubT = (L + QS - 1) / QS;
@@ -628,6 +814,7 @@ __global__ void __launch_bounds__(256) subchunk_decay_kernel(DtFront fe, const b
     const int64_t b = item / (uint64_t)nsubT;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int64_t t0 = sub * QS;
+    const int Hs = BWD ? H / src.hdiv : H;
     for (int hb = 0; hb < H; hb += kDecayHB) {
         const int nh = H - hb < kDecayHB ? H - hb : kDecayHB;
         __syncthreads();
@@ -636,23 +823,32 @@ __global__ void __launch_bounds__(256) subchunk_decay_kernel(DtFront fe, const b
 #pragma unroll
         for (int k = 0; k < KL; ++k) {
             const int e = tid + 256 * k, t = e / kDecayHB, hh = e % kDecayHB;
-            const bool ok = hh < nh && t0 + t < L;  // load a valid element regardless, then select
-            v[k] = dt[ok ? (b * L + t0 + t) * H + hb + hh : 0];
+            bool ok = hh < nh && t0 + t < L;  // load a valid element regardless, then select
+            int64_t row = t0 + t;
+            int hs = hb + hh;
+            if (BWD) {
+                row = src.rev ? L - (t0 + t) : t0 + t;
+                ok = ok && row < src.Ls;
+                hs = (hb + hh) / src.hdiv;
+            }
+            v[k] = dt[ok ? (b * (BWD ? src.Ls : L) + row) * Hs + hs : 0];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < KL; ++k) {
             const int e = tid + 256 * k, t = e / kDecayHB, hh = e % kDecayHB;
-            const bool ok = hh < nh && t0 + t < L;
+            bool ok = hh < nh && t0 + t < L;
+            if (BWD) ok = ok && (src.rev ? L - (t0 + t) : t0 + t) < src.Ls;
             blk[t][hh] = ok ? to_f32(v[k]) : 0.0f;
             vok[t][hh] = ok;
         }
         __syncthreads();
         for (int hh = w; hh < nh; hh += 4) {
             const int h = hb + hh;
-            const float ah = A[h];
+            const float ah = A[BWD ? h / src.hdiv : h];
             float dec = 0.0f, d = 0.0f;  // decay and input steps; zero past L
             if (vok[lane][hh]) dt_front(fe, h, ah, blk[lane][hh], dec, d);
+            if (BWD && src.unit) d = t0 + lane < L ? 1.0f : 0.0f;
             float incl = dec * ah;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -666,9 +862,12 @@ __global__ void __launch_bounds__(256) subchunk_decay_kernel(DtFront fe, const b
     }
 }
 
-// Reading the inputs backwards (XMap::rows > 0) is a variant of the staged kernels only; it needs whole
-// 64-token tiles (L a multiple of 64) so that every tile's first input row lies inside the batch row.
+// Reading the inputs backwards (XMap::rows > 0) is a variant of the kernels with sub-chunk-local decay
+// arrays (FWD); it needs whole 64-token tiles (L a multiple of 64) so that every tile's first input row
+// lies inside the batch row.  Taps need the reversed scan (the chunk walk has its own kernel) and a
+// spacing that is a multiple of the sub-chunk (every tap position starts a sub-chunk).
 inline bool rev_ok(const Shape& s, const XMap& xm) { return xm.rows >= 0 && xm.rows <= s.L && s.L % QS == 0; }
+inline bool tap_ok(const Shape& s, const XMap& xm) { return xm.tapq > 0 && xm.tapq % QS == 0 && s.Q % QS == 0; }
 
 template <int N, int HPW, bool FWD>
 hipError_t launch_state_fast(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
@@ -676,14 +875,14 @@ hipError_t launch_state_fast(const Shape& s, const bf16* x, const bf16* B, const
     const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
     if (nitems == 0) return hipSuccess;
     const size_t lds = sizeof(AggLds<N, HPW>);
-    const bool rev = !FWD && xm.rows > 0;
-    if (rev && !rev_ok(s, xm)) return hipErrorInvalidValue;
-    const void* fn = rev ? (const void*)chunk_state_fast_kernel<N, HPW, false, true>
+    const bool rev = xm.rows > 0;
+    if (rev && (!FWD || !rev_ok(s, xm))) return hipErrorInvalidValue;
+    const void* fn = rev ? (const void*)chunk_state_fast_kernel<N, HPW, true, true>
                          : (const void*)chunk_state_fast_kernel<N, HPW, FWD>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     if (rev)
-        hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW, false, true>), dim3(nitems), dim3(256), lds, st, x, B, ds,
+        hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW, true, true>), dim3(nitems), dim3(256), lds, st, x, B, ds,
                            states, totals, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
     else
         hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, ds, states,
@@ -697,18 +896,39 @@ hipError_t launch_scan_fast(const Shape& s, const bf16* x, const bf16* B, const 
     const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
     if (nitems == 0) return hipSuccess;
     const size_t lds = sizeof(ScanLds<N, HPW>);
-    const bool rev = !FWD && xm.rows > 0;
-    if (rev && !rev_ok(s, xm)) return hipErrorInvalidValue;
-    const void* fn = rev ? (const void*)chunk_scan_fast_kernel<N, HPW, false, true>
-                         : (const void*)chunk_scan_fast_kernel<N, HPW, FWD>;
+    const bool rev = xm.rows > 0, tap = xm.tap != nullptr;
+    if (rev && (!FWD || !rev_ok(s, xm))) return hipErrorInvalidValue;
+    if (tap && (!rev || !tap_ok(s, xm))) return hipErrorInvalidValue;
+    if (xm.start_tr && !rev) return hipErrorInvalidValue;
+    const void* fn = tap   ? (const void*)chunk_scan_fast_kernel<N, HPW, true, true, true>
+                     : rev ? (const void*)chunk_scan_fast_kernel<N, HPW, true, true, false>
+                           : (const void*)chunk_scan_fast_kernel<N, HPW, FWD>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    if (rev)
-        hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, false, true>), dim3(nitems), dim3(256), lds, st, x, B, C, ds,
-                           start, D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
+    if (tap)
+        hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, true, true, true>), dim3(nitems), dim3(256), lds, st, x, B,
+                           C, ds, start, D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
+    else if (rev)
+        hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, true, true, false>), dim3(nitems), dim3(256), lds, st, x, B,
+                           C, ds, start, D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
     else
         hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, C, ds, start,
                            D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
+    return hipGetLastError();
+}
+
+template <int N, int HPW>
+hipError_t launch_walk_fast(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, const float* start,
+                            const XMap& xm, hipStream_t st) {
+    const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
+    if (nitems == 0) return hipSuccess;
+    if (!xm.tap || !tap_ok(s, xm) || xm.rows != 0) return hipErrorInvalidValue;
+    const size_t lds = sizeof(WalkLds<N, HPW>);
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_walk_fast_kernel<N, HPW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_walk_fast_kernel<N, HPW>), dim3(nitems), dim3(256), lds, st, x, B, ds, start, s.L,
+                       (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
     return hipGetLastError();
 }
 
@@ -823,6 +1043,46 @@ hipError_t launch_chunk_scan_fast(const Shape& s, const void* x, const void* B, 
                                     xm);
 }
 
+hipError_t launch_chunk_state_sub(const Shape& s, const void* x, const void* B, const float* dtl, const float* lw,
+                                  float* states, float* totals, hipStream_t st, const XMap* xm) {
+    if (s.N >= 256) return hipErrorInvalidValue;
+    const fz::DtSrc ds{dtl, lw};
+    return fz::state_dispatch<true>(s, (const bf16*)x, (const bf16*)B, ds, states, totals, st, xm);
+}
+
+hipError_t launch_chunk_scan_sub(const Shape& s, const void* x, const void* B, const void* C, const float* dtl,
+                                 const float* lw, const float* start, const float* D, void* y, hipStream_t st,
+                                 const XMap* xm) {
+    if (s.N >= 256) return hipErrorInvalidValue;
+    const fz::DtSrc ds{dtl, lw};
+    return fz::scan_dispatch<true>(s, (const bf16*)x, (const bf16*)B, (const bf16*)C, ds, start, D, (bf16*)y, st, xm);
+}
+
+hipError_t launch_chunk_walk(const Shape& s, const void* x, const void* B, const float* dtl, const float* lw,
+                             const float* start, hipStream_t st, const XMap& xm) {
+    const fz::DtSrc ds{dtl, lw};
+    const bf16 *xb = (const bf16*)x, *bb = (const bf16*)B;
+    const bool pair = fast_hpw(s) == 2;
+    if (s.N == 128)
+        return pair ? fz::launch_walk_fast<128, 2>(s, xb, bb, ds, start, xm, st)
+                    : fz::launch_walk_fast<128, 1>(s, xb, bb, ds, start, xm, st);
+    if (s.N == 64)
+        return pair ? fz::launch_walk_fast<64, 2>(s, xb, bb, ds, start, xm, st)
+                    : fz::launch_walk_fast<64, 1>(s, xb, bb, ds, start, xm, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_subchunk_decay_bwd(const Shape& s, const void* dt, const float* A, float* dtl, float* lw, int64_t Ls,
+                                     int hdiv, bool rev, bool unit, hipStream_t st) {
+    const uint32_t ndec = (uint32_t)(s.b * ((s.L + fz::QS - 1) / fz::QS));
+    if (ndec == 0) return hipSuccess;
+    if (hdiv < 1 || s.H % hdiv) return hipErrorInvalidValue;
+    const DtFront none{nullptr, 0, 0, 0, 0.0f, 0.0f};
+    hipLaunchKernelGGL(fz::subchunk_decay_kernel<true>, dim3(ndec), dim3(256), 0, st, none, (const bf16*)dt, A, dtl, lw,
+                       s.L, (int)s.H, ndec, fz::DecaySrc{Ls, hdiv, rev ? 1 : 0, unit ? 1 : 0});
+    return hipGetLastError();
+}
+
 FastFwdLayout fast_forward_layout(const Shape& s) {
     auto a256 = [](size_t v) { return (v + 255) / 256 * 256; };
     FastFwdLayout f;
@@ -847,8 +1107,8 @@ hipError_t launch_forward_fast(const Shape& s, const DtFront& fe, const void* x,
     float* totals = reinterpret_cast<float*>(ws + f.totals);
     const bf16 *xb = (const bf16*)x, *bb = (const bf16*)B, *cb = (const bf16*)C;
     const uint32_t ndec = (uint32_t)(s.b * ((s.L + fz::QS - 1) / fz::QS));
-    hipLaunchKernelGGL(fz::subchunk_decay_kernel, dim3(ndec), dim3(256), 0, st, fe, (const bf16*)dt, A, dtl, lw,
-                       s.L, (int)s.H, ndec);
+    hipLaunchKernelGGL(fz::subchunk_decay_kernel<false>, dim3(ndec), dim3(256), 0, st, fe, (const bf16*)dt, A, dtl,
+                       lw, s.L, (int)s.H, ndec, fz::DecaySrc{s.L, 1, 0, 0});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const fz::DtSrc ds{dtl, lw};

@@ -54,11 +54,34 @@ hipError_t launch_step_multi(const Shape& s, const DtFront& fe, float* state, co
 // The chunk scan then writes its output in forward time too (`rows` rows per batch row, nothing for the
 // padding tokens), as y = s * (C.S + in-chunk term) + D x with s = rowscale[b, row, h] (an io-dtype
 // (b, rows, H) array, e.g. the step dt) or 1 when rowscale is NULL.
+// tap (chunk scan with rows > 0, and the chunk walk): the fp32 state the kernel carries is also stored
+// at every position that is a multiple of tapq (the state entering it), as (b, L / tapq, H, P, N), and
+// the state update then splits its scaled operand into hi + lo bf16 (fp32-level states).  start_tr: the
+// chunk-start states are those of a transposed scan, (b, nC, (N / 64) H, 64, P).
 struct XMap {
     int hx, div, mul;
     int64_t rows;
     const void* rowscale;
+    float* tap;
+    int tapq;
+    int start_tr;
 };
+// The backward's chunk kernels over sub-chunk-local decay arrays (dtl, lw: (b, H, ceil(L / 64), 64), from
+// launch_subchunk_decay_bwd), with the reading options of XMap; the chunk state also writes each chunk's
+// total log2 decay (b, H, nC) for the state pass (run with Q = 1 over those totals).  dstate 64 or 128.
+hipError_t launch_chunk_state_sub(const Shape& s, const void* x, const void* B, const float* dtl, const float* lw,
+                                  float* states, float* totals, hipStream_t st, const XMap* xm);
+hipError_t launch_chunk_scan_sub(const Shape& s, const void* x, const void* B, const void* C, const float* dtl,
+                                 const float* lw, const float* start, const float* D, void* y, hipStream_t st,
+                                 const XMap* xm);
+// The states entering every xm.tapq-th position (xm.tap), walked from the chunk-start states.
+hipError_t launch_chunk_walk(const Shape& s, const void* x, const void* B, const float* dtl, const float* lw,
+                             const float* start, hipStream_t st, const XMap& xm);
+// Sub-chunk-local decay arrays for s.H kernel heads over s.L tokens from a bf16 dt of (b, Ls, H / hdiv):
+// kernel head h takes dt head h / hdiv and A[h / hdiv]; rev: token t takes the decay step of dt row
+// s.L - t (none where that row is past the end); unit: the input step is 1.
+hipError_t launch_subchunk_decay_bwd(const Shape& s, const void* dt, const float* A, float* dtl, float* lw, int64_t Ls,
+                                     int hdiv, bool rev, bool unit, hipStream_t st);
 // Fast chunk-state / chunk-scan kernels (bf16, headdim 64, dstate 64 or 128, chunk a multiple of 64).
 bool fast_chunk_supported(const Shape& s);
 int fast_forward_chunk(const Shape& s);   // chunk size the forward uses on the fast path
@@ -104,7 +127,7 @@ hipError_t launch_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, in
 // inputs.  Byte offsets of the workspace pieces (all 256-byte aligned).
 struct BackwardLayout {
     size_t xr, dyr, Cr, Br, drev, dfwd, dt_t, cs, states, u_r, v_r, w, G0, dfT, h0T, finT, fscr, q, dlam, dxy,
-        dA_part, dD_part, states_b, R, d2, A2, dt2, cs2, total;
+        dA_part, dD_part, states_b, R, sub, totals, stT, total;
     int64_t Qt;  // chunk of the half-head transposed scans (local flow)
     int64_t Lr;  // rows of the time-reversed copies (the sequence, front-padded to whole chunks when local)
     bool local;  // the decay gradient is formed chunk by chunk (decay_grad.hip)
