@@ -222,22 +222,19 @@ __device__ __forceinline__ void ld_bf16(const bf16* p, float* o) {
     }
 }
 
-// The combine of the chunk-local flow (bf16, headdim 64, dstate N = 64 or 128, H a multiple of 4), one
-// workgroup per (b, t), after the adjoint scan has written dx itself: per head q = v . B and dy . x, per
+// The combine of the chunk-local flow (bf16, dstate N = 64 or 128, H a multiple of 4), one workgroup per
+// (b, t), after the adjoint scan has written dx and the decay gradient dy . x: per head q = v . B, per
 // group dB = sum_h dt v and dC = sum_h w.  Four heads at once per wavefront, 16 lanes per head: wavefront
 // wv takes the head quads k = wv, wv + 4, ..., lane row r (lane / 16) head 4k + r; a lane covers
-// p = 4 l16 .. 4 l16 + 3 (8-byte accesses of dy, x) and n = (N / 16) l16 .. (16- or 8-byte accesses of
-// v, w), so every row of v, w, dy and x is read by one contiguous access per wavefront.  The group sums
-// collect in registers per lane and land, per (wavefront, lane row), in an LDS slice when the row's group
-// changes; the slices are added in a fixed order at the end.
+// n = (N / 16) l16 .. (16- or 8-byte accesses), so every row of v and w is read by one contiguous access
+// per wavefront.  The group sums collect in registers per lane and land, per (wavefront, lane row), in an
+// LDS slice when the row's group changes; the slices are added in a fixed order at the end.
 template <int N>
-__global__ void __launch_bounds__(256) combine_quad_kernel(const bf16* __restrict__ dy, const bf16* __restrict__ x,
-                                                           const bf16* __restrict__ dt, const bf16* __restrict__ B,
+__global__ void __launch_bounds__(256) combine_quad_kernel(const bf16* __restrict__ dt, const bf16* __restrict__ B,
                                                            const bf16* __restrict__ v, const bf16* __restrict__ w,
                                                            bf16* __restrict__ dB, bf16* __restrict__ dC,
-                                                           float* __restrict__ q, float* __restrict__ dxy, int64_t L,
-                                                           int H, int G) {
-    constexpr int P = 64, NV = N / 16;
+                                                           float* __restrict__ q, int64_t L, int H, int G) {
+    constexpr int NV = N / 16;
     extern __shared__ float lds[];
     float* pB = lds;              // [16][G][N] per-(wavefront, lane row) partial dB
     float* pC = pB + 16 * G * N;  // [16][G][N] per-(wavefront, lane row) partial dC
@@ -266,15 +263,11 @@ __global__ void __launch_bounds__(256) combine_quad_kernel(const bf16* __restric
             gcur = g;
             ld_bf16<NV>(B + (bt * G + g) * N + NV * l16, bv);
         }
-        float gy[4], xx[4], vv[NV], ww[NV];
-        ld_bf16<4>(dy + (bt * H + h) * P + 4 * l16, gy);
-        ld_bf16<4>(x + (bt * H + h) * P + 4 * l16, xx);
+        float vv[NV], ww[NV];
         ld_bf16<NV>(v + (bt * H + h) * N + NV * l16, vv);
         ld_bf16<NV>(w + (bt * H + h) * N + NV * l16, ww);
         const float d = static_cast<float>(dt[bt * H + h]);
-        float sxy = 0.0f, sq = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sxy = fmaf(gy[i], xx[i], sxy);
+        float sq = 0.0f;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             sq = fmaf(vv[k], bv[k], sq);
@@ -282,11 +275,7 @@ __global__ void __launch_bounds__(256) combine_quad_kernel(const bf16* __restric
             ac[k] += ww[k];
         }
         sq = row16_sum(sq);
-        sxy = row16_sum(sxy);
-        if (l16 == 0) {
-            q[(bb * H + h) * L + t] = sq;
-            dxy[(bb * H + h) * L + t] = sxy;
-        }
+        if (l16 == 0) q[(bb * H + h) * L + t] = sq;
     }
     if (gcur >= 0) {
 #pragma unroll
@@ -718,19 +707,18 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     BWD_CHECK(launch_chunk_walk(sw, x, B, dtl(ff), lwp(ff, H, nsf, b), stT, st, xw));
     // the decay gradient, chunk by chunk at Q, from its chunk cumsum arrays and the stored states
     BWD_CHECK(launch_chunk_cumsum(s, DtFront{nullptr, 0, 0, 0, 0.0f, 0.0f}, dt, A, dt_t, cs, st));
-    BWD_CHECK(launch_decay_grad(s, x, dy, B, C, cs, dt_t, states, states_b, R, st));
+    BWD_CHECK(launch_decay_grad(s, x, dy, B, C, cs, dt_t, states, states_b, R, dxy, st));
 
     const size_t lq = (size_t)32 * G * N * 4;  // the quad combine's LDS slices
     if (P == 64 && (N == 64 || N == 128) && H % 4 == 0 && lq <= 64 * 1024) {
-        const bf16 *dyb = static_cast<const bf16*>(dy), *xb2 = static_cast<const bf16*>(x);
         const bf16 *dtb = static_cast<const bf16*>(dt), *Bb = static_cast<const bf16*>(B);
         bf16 *dBb = static_cast<bf16*>(dB), *dCb = static_cast<bf16*>(dC);
         if (N == 128)
-            hipLaunchKernelGGL(combine_quad_kernel<128>, dim3((unsigned)(b * L)), dim3(256), lq, st, dyb, xb2, dtb, Bb,
-                               v, w, dBb, dCb, q, dxy, L, H, G);
+            hipLaunchKernelGGL(combine_quad_kernel<128>, dim3((unsigned)(b * L)), dim3(256), lq, st, dtb, Bb, v, w, dBb,
+                               dCb, q, L, H, G);
         else
-            hipLaunchKernelGGL(combine_quad_kernel<64>, dim3((unsigned)(b * L)), dim3(256), lq, st, dyb, xb2, dtb, Bb,
-                               v, w, dBb, dCb, q, dxy, L, H, G);
+            hipLaunchKernelGGL(combine_quad_kernel<64>, dim3((unsigned)(b * L)), dim3(256), lq, st, dtb, Bb, v, w, dBb,
+                               dCb, q, L, H, G);
         BWD_CHECK(hipGetLastError());
     } else {
         BWD_CHECK((launch_combine<T, bf16, bf16>(dy, x, dt, B, C, D, nullptr, v, w, dx, dB, dC, q, nullptr, dxy, b, L,

@@ -76,7 +76,7 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, Frag<bf
     }
 }
 
-// R (b, H, L) fp32.  cs / dtv: the forward chunk cumsum arrays (b, H, nC, Q) (log2 units; dt, zero past
+// R and dxy (dy_t . x_t, for dD) (b, H, L) fp32.  cs / dtv: the forward chunk cumsum arrays (b, H, nC, Q) (log2 units; dt, zero past
 // L); S0: forward chunk-start states (b, nC, H, P, N); Gst: the reversed adjoint scan's chunk-start
 // states (b, nC, H, P, N) in reversed chunk order, so forward chunk c reads reversed chunk nC - 1 - c:
 // the adjoint G_{c1+1} of the token after the chunk (dfinal for the last chunk), which enters decayed
@@ -93,8 +93,8 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
                                                          const float* __restrict__ dtv,
                                                          const float* __restrict__ S0,
                                                          const float* __restrict__ Gst, float* __restrict__ R,
-                                                         int64_t L, int H, int G, int Q, int64_t nC,
-                                                         uint32_t nitems) {
+                                                         float* __restrict__ dxy, int64_t L, int H, int G, int Q,
+                                                         int64_t nC, uint32_t nitems) {
     constexpr int NK = N / 32, NS = Lds<N>::NS;
     __shared__ Lds<N> sm;
     const uint32_t item = xcd_remap(blockIdx.x, nitems);
@@ -184,6 +184,22 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) split8(sa[ks][0], sa[ks][1], sh[ks], sl[ks]);
     __syncthreads();
+
+    // ---- dy_t . x_t per token (for dD): four threads per token, 16 columns each -------------------
+    if (tid < 4 * Q) {
+        const int t = tid >> 2, p0 = (tid & 3) * 16;
+        float sxy = 0.0f;
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.ys[t * XS + p0 + 8 * h8]);
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(&sm.xs[t * XS + p0 + 8 * h8]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sxy = fmaf(static_cast<float>(a[e]), static_cast<float>(v[e]), sxy);
+        }
+        sxy = dpp_add<0xB1>(sxy);  // the four threads of the token: quad_perm [1,0,3,2], then [2,3,0,1]
+        sxy = dpp_add<0x4E>(sxy);
+        if ((tid & 3) == 0 && t < valid) dxy[(b * H + h) * L + c0 + t] = sxy;
+    }
 
     // ---- T2 (C with S0, read out by dy) or T3 (B with Gam, read out by x) for p = 16 pt + l16 ----------
     {
@@ -293,17 +309,17 @@ bool decay_grad_supported(const Shape& s) {
 }
 
 hipError_t launch_decay_grad(const Shape& s, const void* x, const void* dy, const void* B, const void* C,
-                             const float* cs, const float* dtv, const float* S0, const float* Gst, float* R,
+                             const float* cs, const float* dtv, const float* S0, const float* Gst, float* R, float* dxy,
                              hipStream_t st) {
     const uint32_t nitems = (uint32_t)(s.b * s.nC * s.H);
     if (nitems == 0) return hipSuccess;
     const bf16 *xb = (const bf16*)x, *yb = (const bf16*)dy, *bb = (const bf16*)B, *cb = (const bf16*)C;
     if (s.N == 128)
         hipLaunchKernelGGL(dg::decay_grad_kernel<128>, dim3(nitems), dim3(512), 0, st, xb, yb, bb, cb, cs, dtv, S0, Gst,
-                           R, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+                           R, dxy, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
     else
         hipLaunchKernelGGL(dg::decay_grad_kernel<64>, dim3(nitems), dim3(512), 0, st, xb, yb, bb, cb, cs, dtv, S0, Gst,
-                           R, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+                           R, dxy, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
     return hipGetLastError();
 }
 

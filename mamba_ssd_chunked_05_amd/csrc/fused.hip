@@ -456,34 +456,59 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             // token slots of this K step: 32ks + 4g4 + r (slots 0..3) and 32ks + 16 + 4g4 + r (slots 4..7)
-            Frag<bf16> xw[HPW], xl[TAP ? HPW : 1];
+            if constexpr (TAP) {  // hi + lo scaled operand; the B^T fragments in two halves (fewer live registers)
+                Frag<bf16> xw[HPW], xl[HPW];
 #pragma unroll
-            for (int hh = 0; hh < HPW; ++hh) {
-                const float* wv = &sm.ww[hh * QS + 32 * ks + 4 * g4];
+                for (int hh = 0; hh < HPW; ++hh) {
+                    const float* wv = &sm.ww[hh * QS + 32 * ks + 4 * g4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v0 = static_cast<float>(xf[ks][hh].v[r]) * wv[r];
-                    const float v1 = static_cast<float>(xf[ks][hh].v[4 + r]) * wv[16 + r];
-                    xw[hh].v[r] = static_cast<bf16>(v0);
-                    xw[hh].v[4 + r] = static_cast<bf16>(v1);
-                    if (TAP) {
+                    for (int r = 0; r < 4; ++r) {
+                        const float v0 = static_cast<float>(xf[ks][hh].v[r]) * wv[r];
+                        const float v1 = static_cast<float>(xf[ks][hh].v[4 + r]) * wv[16 + r];
+                        xw[hh].v[r] = static_cast<bf16>(v0);
+                        xw[hh].v[4 + r] = static_cast<bf16>(v1);
                         xl[hh].v[r] = static_cast<bf16>(v0 - static_cast<float>(xw[hh].v[r]));
                         xl[hh].v[4 + r] = static_cast<bf16>(v1 - static_cast<float>(xw[hh].v[4 + r]));
                     }
                 }
-            }
-            Frag<bf16> a[NT];  // every B^T fragment of this K step in flight before the products
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                a[nt].v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * nt, BS, l16),
-                                tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * nt, BS, l16));
-            __builtin_amdgcn_sched_barrier(0);
+                for (int nb = 0; nb < NT; nb += NT / 2) {
+                    Frag<bf16> a[NT / 2];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
+                    for (int q = 0; q < NT / 2; ++q)
+                        a[q].v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * (nb + q), BS, l16),
+                                       tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * (nb + q), BS, l16));
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int q = 0; q < NT / 2; ++q) {
+#pragma unroll
+                        for (int hh = 0; hh < HPW; ++hh) {
+                            mma(st[hh][nb + q], a[q], xw[hh]);
+                            mma(st[hh][nb + q], a[q], xl[hh]);
+                        }
+                    }
+                }
+            } else {
+                Frag<bf16> xw[HPW];
 #pragma unroll
                 for (int hh = 0; hh < HPW; ++hh) {
-                    mma(st[hh][nt], a[nt], xw[hh]);
-                    if (TAP) mma(st[hh][nt], a[nt], xl[TAP ? hh : 0]);
+                    const float* wv = &sm.ww[hh * QS + 32 * ks + 4 * g4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        xw[hh].v[r] = static_cast<bf16>(static_cast<float>(xf[ks][hh].v[r]) * wv[r]);
+                        xw[hh].v[4 + r] = static_cast<bf16>(static_cast<float>(xf[ks][hh].v[4 + r]) * wv[16 + r]);
+                    }
+                }
+                Frag<bf16> a[NT];  // every B^T fragment of this K step in flight before the products
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    a[nt].v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * nt, BS, l16),
+                                    tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * nt, BS, l16));
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                    for (int hh = 0; hh < HPW; ++hh) mma(st[hh][nt], a[nt], xw[hh]);
                 }
             }
         }

@@ -139,7 +139,7 @@ bool decay_grad_supported(const Shape& s);
 // chunk-start states S0 (b, nC, H, P, N) and the reversed adjoint scan's chunk-start states Gst (same
 // layout, reversed chunk order).
 hipError_t launch_decay_grad(const Shape& s, const void* x, const void* dy, const void* B, const void* C,
-                             const float* cs, const float* dtv, const float* S0, const float* Gst, float* R,
+                             const float* cs, const float* dtv, const float* S0, const float* Gst, float* R, float* dxy,
                              hipStream_t st);
 BackwardLayout backward_layout(const Shape& s);
 hipError_t launch_backward(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
