@@ -155,6 +155,39 @@ __device__ __forceinline__ float row16_sum(float v) {
     return dpp_add<0x128>(v);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Four row sums at once: lane l16 of each row of 16 ends with the sum over the row of v[l16 / 4].  Each
+// exchange halves the values a lane keeps: with lane l16 ^ 8 (rotation by 8 inside the row) it keeps
+// v[2 b3 + 0, 1], with the mirrored lane of its half row (7 - l16 % 8, the opposite bit 2) it keeps
+// v[2 b3 + b2] (b3, b2: bits 3 and 2 of l16); the quad then holds four partial sums of the same value.
+__device__ __forceinline__ float row16_sum4(float v0, float v1, float v2, float v3, int l16) {
+    const bool b3 = (l16 & 8) != 0, b2 = (l16 & 4) != 0;
+    float k0 = b3 ? v2 : v0, k1 = b3 ? v3 : v1;
+    k0 += dpp_mov<0x128>(b3 ? v0 : v2);
+    k1 += dpp_mov<0x128>(b3 ? v1 : v3);
+    float m = b2 ? k1 : k0;
+    m += dpp_mov<0x141>(b2 ? k0 : k1);
+    m = dpp_add<0xB1>(m);
+    return dpp_add<0x4E>(m);
+}
+
+// inclusive prefix sum over the 64 lanes of a wavefront with data-parallel moves: shifts by 1, 2, 4 and
+// 8 lanes inside each row of 16 (a lane with no source adds zero), then each row's last value added to
+// the rows after it (row broadcasts of lanes 15 and 31)
+__device__ __forceinline__ float wave_incl_scan(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return v;
+}
+
 // ---------------------------------------------------------------------------
 // workgroup -> XCD-contiguous work mapping.  Workgroups are dispatched
 // round-robin over the 8 XCDs (id % 8); this bijection gives every XCD a

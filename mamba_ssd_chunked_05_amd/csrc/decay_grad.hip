@@ -63,7 +63,6 @@ __device__ __forceinline__ uint4 ldr(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-__device__ __forceinline__ float sum16(float v) { return row16_sum(v); }
 
 // 8 fp32 values -> hi and lo bf16 fragments
 __device__ __forceinline__ void split8(const float4& a, const float4& b, Frag<bf16>& hi, Frag<bf16>& lo) {
@@ -215,13 +214,12 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
                 mma(acc, a, sh[ks]);
                 mma(acc, a, sl[ks]);
             }
-            // acc[r] = (St A_t)_p for t = 16 it + 4 g4 + r
+            // acc[r] = (St A_t)_p for t = 16 it + 4 g4 + r; the four sums over p land in lanes l16 = 4 r
+            float v[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * it + 4 * g4 + r;
-                const float v = sum16(static_cast<float>(Dm[t * XS + 16 * pt + l16]) * acc[r]);
-                if (l16 == 0) atomicAdd(&out[t], v);
-            }
+            for (int r = 0; r < 4; ++r) v[r] = static_cast<float>(Dm[(16 * it + 4 * g4 + r) * XS + 16 * pt + l16]) * acc[r];
+            const float vs = row16_sum4(v[0], v[1], v[2], v[3], l16);
+            if ((l16 & 3) == 0) atomicAdd(&out[16 * it + 4 * g4 + (l16 >> 2)], vs);
         }
     }
 
@@ -248,16 +246,16 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
         }
         const int j = 16 * jt + l16;
         const float lj = sm.lw[j], dj = sm.dtw[j];
-        float colp = 0.0f;
+        float colp = 0.0f, m[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * it + 4 * g4 + r;
             // j < t only; the exponent is capped at 0 so no masked lane forms an infinity
-            const float m = j < t ? ad[r] * ac[r] * fast_exp2(fminf(sm.lw[t] - lj, 0.0f)) * dj : 0.0f;
-            colp += m;
-            const float rs = sum16(m);
-            if (l16 == 0) atomicAdd(&sm.rowsum[t], rs);
+            m[r] = j < t ? ad[r] * ac[r] * fast_exp2(fminf(sm.lw[t] - lj, 0.0f)) * dj : 0.0f;
+            colp += m[r];
         }
+        const float rs = row16_sum4(m[0], m[1], m[2], m[3], l16);  // row t = 16 it + 4 g4 + l16 / 4
+        if ((l16 & 3) == 0) atomicAdd(&sm.rowsum[16 * it + 4 * g4 + (l16 >> 2)], rs);
         colp += __shfl_xor(colp, 16, 64);
         colp += __shfl_xor(colp, 32, 64);
         if (g4 == 0) atomicAdd(&sm.colsum[j], colp);
@@ -280,15 +278,9 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
             a4[q] = in ? sm.colsum[k] - sm.rowsum[k] : 0.0f;
         }
         // inclusive prefix sums over k of the pair sums, then per position
-        float p2 = a2[0] + a2[1], p3 = a3[0] + a3[1], p4 = a4[0] + a4[1];
-        float tot2 = p2;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float u2 = __shfl_up(p2, off, 64), u3 = __shfl_up(p3, off, 64), u4 = __shfl_up(p4, off, 64);
-            if (lane >= off) p2 += u2, p3 += u3, p4 += u4;
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) tot2 += __shfl_xor(tot2, off, 64);
+        const float p2 = wave_incl_scan(a2[0] + a2[1]), p3 = wave_incl_scan(a3[0] + a3[1]);
+        const float p4 = wave_incl_scan(a4[0] + a4[1]);
+        const float tot2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p2), 63));  // the whole sum
         // exclusive prefix before this lane's pair
         const float e2 = p2 - (a2[0] + a2[1]), e3 = p3 - (a3[0] + a3[1]), e4 = p4 - (a4[0] + a4[1]);
         float* Rh = R + (b * H + h) * L + c0;
