@@ -269,7 +269,7 @@ ssd_status ssd_step_multi_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, fl
  * kernels; other inputs run fp32 scans.  workspace:
  * ssd_backward_workspace_bytes(dims) bytes, 256-byte aligned (about
  * (2 s + 4) P + 8 N + 4 P N / chunk bytes per token-head with fp32 scans, s =
- * the io element size, and about 6 P + 4 N + 8 P N / chunk with the chunked
+ * the io element size, and about 4 N + 8 P N / chunk + 70 with the chunked
  * decay gradient); no output may overlap an input, another output or the
  * workspace.  x, B, C, dy, dx, dB, dC, h0, dfinal and dh0 must be 16-byte
  * aligned (SSD_ERR_UNSUPPORTED otherwise).

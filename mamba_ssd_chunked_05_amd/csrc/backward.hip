@@ -16,11 +16,13 @@
 // differences: d lambda_t = C_t . w_t - dt_t x_t^T G_t B_t (+ <dfinal, S_L-1>
 // at the last token), then
 //   ddt_k = x_k^T G_k B_k + A sum_{t>=k} d lambda_t,  dA = sum_k dt_k sum_{t>=k} d lambda_t.
-// The scans run in fp32 (the generic chunk kernels with fp32 MFMA); they read
-// the inputs in place in forward time, and time-reversed copies (in the input
-// dtype) that this file builds for the reversed scans.  The transposed scans'
-// x-role input is B or C of the head's group, read through the kernels' x-head
-// map rather than copied per head.
+// Two flows.  bf16 inputs with headdim 64 and dstate 64 or 128 (run_local) form
+// the decay gradients chunk by chunk (decay_grad.hip) and run every scan on the
+// fast bf16 chunk kernels, reading the inputs in place (backwards for the
+// reversed scans).  Other inputs (run) use the generic chunk kernels in fp32
+// with fp64 suffix sums of d lambda, on time-reversed copies of the inputs that
+// this file builds.  The transposed scans' x-role input is B or C of the head's
+// group, read through the kernels' x-head map rather than copied per head.
 #include "common.hpp"
 #include "launch.hpp"
 
