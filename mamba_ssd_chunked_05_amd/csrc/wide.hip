@@ -17,7 +17,8 @@
 // (dstate 256) run four wavefronts; wavefront w carries the fp32 state rows
 // p = 16w .. 16w + 15 for all N columns in registers (N/4 values per lane).
 // chunk_scan_wide8_kernel (dstate 512) runs eight, each with one p-tile and
-// one half of the state columns.
+// one half of the state columns; chunk_state_wide32_kernel (dstate 512) holds
+// the state transposed in 32 x 32 tiles for the 32 x 32 x 16 MFMA.
 // Staging of the next block (or the next sub-chunk) runs one step ahead in
 // registers.  Layout and fragment conventions are those of fused.hip.
 #include "common.hpp"
@@ -765,11 +766,209 @@ chunk_state_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     if (FWD && tid == 0) totals[(b * H + h) * nC + c] = tot;
 }
 
+// ---------------------------------------------------------------------------
+// the same chunk-local states on 32 x 32 x 16 MFMAs.  The state is held transposed, S^T (n x p), in 32 x 32
+// accumulator tiles: wavefront w owns p-tile w % 2 (32 rows of p) and state half w / 2 (N/2 columns of n),
+// N/64 tiles.  Lane l of a 32 x 32 x 16 product holds operand row (A) or column (B) l % 32 and K positions
+// 8 (l / 32) .. + 7; accumulator slot i of lane l is row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32.
+// The A operand B^T (n x tokens) and the B operand w x (tokens x p) come from transpose reads of the
+// natural-layout tiles with the same token order (16-lane group g reads tokens 16 ks + 8 (g / 2) ..), so
+// one operand fetch serves twice the products of the 16 x 16 x 32 form and every B column is read by two
+// wavefronts instead of four.  Each pass stages one 128-column block per half.
+// ---------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void mma32(f32x16& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+
+struct Wide32Lds {
+    bf16 xs[QS * XS];
+    bf16 bs[2][QS * WBS];  // this pass's block of each half
+    uint4 xf[4][4][2][64];  // per wavefront, K step, hi / lo: the scaled operand in fragment order
+    float ww[QS];           // 2^(l_end - l_j) dt_j
+};
+
+struct Wide32Regs {
+    uint4 x[2];
+    uint4 b[8];  // the pass's two blocks: half tid / 128, rows (tid % 128) / 16 + 8 k, columns 8 (tid % 16)
+    float dt, cs;
+};
+
+template <int N, bool FWD>
+__global__ void __launch_bounds__(256, 2)
+chunk_state_wide32_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, DtSrc ds, float* __restrict__ states,
+                          float* __restrict__ totals, int64_t L, int H, int G, int Q, int64_t nC, uint32_t nitems) {
+    constexpr int NH = N / 2, NPASS = NH / WB, NTW = NH / 32;  // state half, passes, 32-wide tiles per wavefront
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Wide32Lds& sm = *reinterpret_cast<Wide32Lds*>(smem_raw);
+
+    const uint32_t item = xcd_remap(blockIdx.x, nitems);
+    const int h = (int)(item % (uint32_t)H);
+    const int64_t c = (item / (uint32_t)H) % (uint32_t)nC;
+    const int64_t b = item / ((uint32_t)H * (uint32_t)nC);
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pt = w & 1, nh = w >> 1;  // p-tile and state half of this wavefront
+    const int64_t t0 = c * Q;
+    const int64_t t_end = t0 + Q < L ? t0 + Q : L;
+    const int nsub = (int)((t_end - t0 + QS - 1) / QS);
+    const int64_t nsubT = (L + QS - 1) / QS;
+
+    f32x16 st[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[t][i] = 0.0f;
+
+    WideSrc src;
+    src.x = x, src.B = B, src.C = nullptr, src.ds = ds, src.b = b, src.L = L, src.H = H, src.G = G, src.N = N,
+    src.h = h, src.g = g;
+    src.dt0 = FWD ? ((b * H + h) * nsubT + c * (Q / QS)) * QS : ((b * H + h) * nC + c) * Q;
+    float after = 0.0f, tot = 0.0f, cs_end = 0.0f;
+    if (!FWD && tid < 64) cs_end = ds.cs[src.dt0 + (Q - 1)];
+    WideAddr ad;
+    wide_addr(ad, src, tid);
+    // the B pieces of this thread: half bh, rows br + 8 k, columns 8 (tid % 16) of the half's block q
+    const int bh = tid >> 7, br = (tid & 127) >> 4, bc = (tid & 15) * 8;
+    const int64_t GN = (int64_t)G * N;
+    const uint32_t bo = (uint32_t)((br * GN + bh * NH + bc) * 2);
+    auto load_b = [&](Wide32Regs& rg, int64_t tb, int q) {
+        const auto rb = tile_rsrc(B + ((b * L + tb) * G + g) * (int64_t)N, GN, L - tb, N);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rg.b[k] = ldbuf(rb, bo + (uint32_t)((8 * k * GN + WB * q) * 2));
+    };
+    auto load_x = [&](Wide32Regs& rg, int64_t tb, int sub) {
+        const int64_t HP_ = (int64_t)H * P;
+        const auto r = tile_rsrc(x + ((b * L + tb) * H + h) * (int64_t)P, HP_, L - tb, P);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) rg.x[k] = ldbuf(r, ad.xo + (uint32_t)(32 * k * HP_ * 2));
+        if (tid < 64) {
+            rg.dt = ds.dt_t[src.dt0 + (int64_t)QS * sub + tid];
+            rg.cs = ds.cs[src.dt0 + (int64_t)QS * sub + tid];
+        }
+    };
+    auto store_b = [&](const Wide32Regs& rg) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) *reinterpret_cast<uint4*>(&sm.bs[bh][(br + 8 * k) * WBS + bc]) = rg.b[k];
+    };
+    Wide32Regs rg;
+    {
+        const int64_t tl = t0 + (int64_t)(nsub - 1) * QS;
+        load_x(rg, tl, nsub - 1);
+        load_b(rg, tl, 0);
+    }
+    // transpose-read coordinates of this lane: token rows 16 ks + 8 (grp / 2) (+ 4), columns 16 (grp % 2) ..
+    const int krow = 8 * (grp >> 1), kcol = 16 * (grp & 1);
+
+    for (int sc = nsub - 1; sc >= 0; --sc) {
+        const int64_t tbase = t0 + (int64_t)sc * QS;
+        const bool more = sc > 0;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4*>(sm.xs + (ad.xr + 32 * k) * XS + ad.xc) = rg.x[k];
+        if (tid < 64) {
+            float e;  // log2 decay from this token to the chunk's end
+            if (FWD) {
+                const float last = __shfl(rg.cs, 63, 64);
+                e = after + (last - rg.cs);
+                after += last;
+                tot += last;
+            } else {
+                e = cs_end - rg.cs;
+            }
+            sm.ww[tid] = fast_exp2(e) * rg.dt;
+        }
+        store_b(rg);
+        __syncthreads();
+        if (more) load_x(rg, tbase - QS, sc - 1);
+        if (NPASS > 1)
+            load_b(rg, tbase, 1);
+        else if (more)
+            load_b(rg, tbase - QS, 0);
+
+        // the scaled operand w x of p-tile pt, hi + lo, for the four 16-token K steps, parked in this
+        // wavefront's LDS slot in fragment order (fewer live registers through the passes)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x4 v0 = tr_read(sm.xs, 16 * ks + krow, 32 * pt + kcol, XS, l16);
+            const bf16x4 v1 = tr_read(sm.xs, 16 * ks + krow + 4, 32 * pt + kcol, XS, l16);
+            const float* wv = &sm.ww[16 * ks + krow];
+            Frag<bf16> xh, xl;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float a0 = static_cast<float>(v0[r]) * wv[r];
+                const float a1 = static_cast<float>(v1[r]) * wv[4 + r];
+                const bf16 h0v = static_cast<bf16>(a0), h1v = static_cast<bf16>(a1);
+                xh.v[r] = h0v;
+                xh.v[4 + r] = h1v;
+                xl.v[r] = static_cast<bf16>(a0 - static_cast<float>(h0v));
+                xl.v[4 + r] = static_cast<bf16>(a1 - static_cast<float>(h1v));
+            }
+            *reinterpret_cast<bf16x8*>(&sm.xf[w][ks][0][lane]) = xh.v;
+            *reinterpret_cast<bf16x8*>(&sm.xf[w][ks][1][lane]) = xl.v;
+        }
+#pragma unroll
+        for (int q = 0; q < NPASS; ++q) {
+            if (q > 0) {
+                __syncthreads();
+                store_b(rg);
+                __syncthreads();
+                if (q + 1 < NPASS)
+                    load_b(rg, tbase, q + 1);
+                else if (more)
+                    load_b(rg, tbase - QS, 0);
+            }
+            const bf16* bsb = sm.bs[nh];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                Frag<bf16> xh, xl;
+                xh.v = *reinterpret_cast<const bf16x8*>(&sm.xf[w][ks][0][lane]);
+                xl.v = *reinterpret_cast<const bf16x8*>(&sm.xf[w][ks][1][lane]);
+#pragma unroll
+                for (int t = 0; t < WB / 32; ++t) {
+                    Frag<bf16> a;
+                    a.v = pack8(tr_read(bsb, 16 * ks + krow, 32 * t + kcol, WBS, l16),
+                                tr_read(bsb, 16 * ks + krow + 4, 32 * t + kcol, WBS, l16));
+                    mma32(st[q * (WB / 32) + t], a, xh);
+                    mma32(st[q * (WB / 32) + t], a, xl);
+                }
+            }
+        }
+    }
+    // a ragged last chunk ends at position Q-1 all the same: its padded tokens have dt = 0 and decay 1
+    float* out = states + ((b * nC + c) * H + h) * (int64_t)P * N + (int64_t)(32 * pt + (lane & 31)) * N + nh * NH +
+                 4 * (lane >> 5);
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 v = {st[t][4 * i4], st[t][4 * i4 + 1], st[t][4 * i4 + 2], st[t][4 * i4 + 3]};
+            *reinterpret_cast<f32x4*>(out + 32 * t + 8 * i4) = v;
+        }
+    }
+    if (FWD && tid == 0) totals[(b * H + h) * nC + c] = tot;
+}
+
 template <int N, bool FWD>
 hipError_t launch_state_wide(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, float* states,
                              float* totals, hipStream_t st) {
     const uint32_t nitems = (uint32_t)(s.b * s.nC * s.H);
     if (nitems == 0) return hipSuccess;
+    // dstate 512: the 32 x 32 x 16 form (64K-token forward 1.09-1.10 against 1.11-1.12 ms on two boxes, 4.18
+    // against 4.21 ms at 256K: half the MFMA issues and operand reads, little time, so the kernel is bound by
+    // neither).  dstate 256 keeps the 16 x 16 x 32 form: the 32 x 32 one's LDS (80 KB) halves its residency
+    // and measured 0.59 against 0.57 ms (2.21 against 2.06 ms at 256K).
+    if constexpr (N >= 512) {
+        const size_t lds = sizeof(Wide32Lds);
+        hipError_t e = hipFuncSetAttribute((const void*)chunk_state_wide32_kernel<N, FWD>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((chunk_state_wide32_kernel<N, FWD>), dim3(nitems), dim3(256), lds, st, x, B, ds, states,
+                           totals, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+        return hipGetLastError();
+    }
     const size_t lds = sizeof(WideAggLds);
     hipError_t e = hipFuncSetAttribute((const void*)chunk_state_wide_kernel<N, FWD>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
