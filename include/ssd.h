@@ -263,14 +263,15 @@ ssd_status ssd_step_multi_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, fl
  * and dh0 may be NULL (not written).  dims->chunk is the chunk of the
  * internal scans: 0 for the library's choice, else a multiple of 16 up to 512
  * whose fp32 tiles fit LDS.  Supported: dstate <= 256 besides the forward's
- * limits (SSD_ERR_UNSUPPORTED otherwise).  bf16 inputs with headdim 64,
- * dstate 64 or 128 and chunk 64 or 128 (the library's choice) form the decay
- * gradient chunk by chunk and run the transposed scans on the bf16 chunk
- * kernels; other inputs run fp32 scans.  workspace:
- * ssd_backward_workspace_bytes(dims) bytes, 256-byte aligned (about
- * (2 s + 4) P + 8 N + 4 P N / chunk bytes per token-head with fp32 scans, s =
- * the io element size, and about 4 N + 8 P N / chunk + 70 with the chunked
- * decay gradient); no output may overlap an input, another output or the
+ * limits (SSD_ERR_UNSUPPORTED otherwise).  The decay gradient is formed chunk
+ * by chunk from each chunk's starting state and adjoint.  bf16 inputs with
+ * headdim 64, dstate 64 or 128 and chunk 64 or 128 (the library's choice) run
+ * every scan on the bf16 chunk kernels; other inputs run fp32 scans.
+ * workspace: ssd_backward_workspace_bytes(dims) bytes, 256-byte aligned
+ * (about (2 s + 4) P + 8 N + 2 s N G / H + 8 P N / chunk + 30 bytes per
+ * token-head with fp32 scans, s = the io element size, and about 4 N + 8 P N /
+ * chunk + 70 on the bf16 chunk kernels); no output may overlap an input,
+ * another output or the
  * workspace.  x, B, C, dy, dx, dB, dC, h0, dfinal and dh0 must be 16-byte
  * aligned (SSD_ERR_UNSUPPORTED otherwise).
  */

@@ -16,13 +16,16 @@
 // differences: d lambda_t = C_t . w_t - dt_t x_t^T G_t B_t (+ <dfinal, S_L-1>
 // at the last token), then
 //   ddt_k = x_k^T G_k B_k + A sum_{t>=k} d lambda_t,  dA = sum_k dt_k sum_{t>=k} d lambda_t.
-// Two flows.  bf16 inputs with headdim 64 and dstate 64 or 128 (run_local) form
-// the decay gradients chunk by chunk (decay_grad.hip) and run every scan on the
-// fast bf16 chunk kernels, reading the inputs in place (backwards for the
-// reversed scans).  Other inputs (run) use the generic chunk kernels in fp32
-// with fp64 suffix sums of d lambda, on time-reversed copies of the inputs that
-// this file builds.  The transposed scans' x-role input is B or C of the head's
-// group, read through the kernels' x-head map rather than copied per head.
+// Both flows form the decay gradient chunk by chunk, R_k = a_k <G_k, S_{k-1}>
+// expanded over each chunk from its chunk-start state and adjoint (no long suffix
+// sum of d lambda, whose terms nearly cancel).  bf16 inputs with headdim 64 and
+// dstate 64 or 128 (run_local) use decay_grad.hip and run every scan on the fast
+// bf16 chunk kernels, reading the inputs in place (backwards for the reversed
+// scans).  Other inputs (run) use the generic chunk kernels in fp32 on
+// time-reversed copies of the inputs that this file builds, and a plain fp32
+// form of the decay gradient.  The transposed scans' x-role input is B or C of
+// the head's group, read through the kernels' x-head map rather than copied per
+// head.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -90,28 +93,27 @@ __global__ void __launch_bounds__(256) ones_kernel(float* __restrict__ dt_t, int
     dt_t[i] = pos < L ? 1.0f : 0.0f;
 }
 
-// One workgroup per (b, t), all heads: dx = dt u + D dy; per head q = v . B (= x^T G B), d lambda =
-// C . w - dt q and dy . x; per group dB = sum_h dt v and dC = sum_h w.  Wavefront wv takes heads
+// One workgroup per (b, t), all heads: dx = dt u + D dy; per head q = v . B (= x^T G B) and dy . x; per
+// group dB = sum_h dt v and dC = sum_h w.  Wavefront wv takes heads
 // wv, wv + 4, ... (lanes over p and n) and reads each element of u, v, w once: the group sums
 // accumulate in registers while the heads stay in one group (heads are grouped in contiguous
 // ranges, so a wavefront meets each group once) and are flushed to a per-wavefront LDS slice.
 // Without SLICES (LDS too small for them) the group sums re-read v and w in a second pass.
-// u_r and v_r have Lr rows per batch row (time-reversed, behind Lr - L rows of padding); dlam may be
-// NULL (the chunk-local decay gradient does not use it).  With u_r NULL dx is not written (the adjoint
-// scan wrote it), and with vrev 0 v_r is in forward time (L rows per batch row).
+// u_r and v_r have Lr rows per batch row (time-reversed, behind Lr - L rows of padding).  With u_r NULL
+// dx is not written (the adjoint scan wrote it), and with vrev 0 v_r is in forward time (L rows per
+// batch row).
 template <class T, class U, class V, bool SLICES>
 __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, const T* __restrict__ x,
                                                       const T* __restrict__ dt, const T* __restrict__ B,
-                                                      const T* __restrict__ C, const float* __restrict__ D,
+                                                      const float* __restrict__ D,
                                                       const U* __restrict__ u_r, const V* __restrict__ v_r,
                                                       const V* __restrict__ w, T* __restrict__ dx,
                                                       T* __restrict__ dB, T* __restrict__ dC, float* __restrict__ q,
-                                                      float* __restrict__ dlam, float* __restrict__ dxy, int64_t L,
-                                                      int64_t Lr, int H, int P, int N, int G, int vrev) {
+                                                      float* __restrict__ dxy, int64_t L, int64_t Lr, int H, int P,
+                                                      int N, int G, int vrev) {
     extern __shared__ float lds[];
     float* sB = lds;                // [G][N]
-    float* sC = sB + G * N;         // [G][N]
-    float* sdt = sC + G * N;        // [H]
+    float* sdt = sB + G * N;        // [H]
     float* pB = sdt + H;            // [4][G][N] per-wavefront partial dB
     float* pC = pB + 4 * G * N;     // [4][G][N] per-wavefront partial dC
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -119,10 +121,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
     const int64_t bb = bt / L, t = bt % L;
     const int64_t btr = bb * Lr + (Lr - 1 - t), btv = vrev ? btr : bt;
     const int hpg = H / G;
-    for (int e = tid; e < G * N; e += 256) {
-        sB[e] = to_f32(B[bt * G * N + e]);
-        sC[e] = to_f32(C[bt * G * N + e]);
-    }
+    for (int e = tid; e < G * N; e += 256) sB[e] = to_f32(B[bt * G * N + e]);
     if (SLICES)
         for (int e = tid; e < 8 * G * N; e += 256) pB[e] = 0.0f;  // pB and pC
     for (int h = tid; h < H; h += 256) sdt[h] = to_f32(dt[bt * H + h]);
@@ -151,7 +150,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
             gcur = g;
         }
         const float d = sdt[h], Dh = D ? D[h] : 0.0f;
-        float sxy = 0.0f, sq = 0.0f, sw = 0.0f;
+        float sxy = 0.0f, sq = 0.0f;
         for (int p = lane; p < P; p += 64) {
             const int64_t o = (bt * H + h) * P + p;
             const float gy = to_f32(dy[o]);
@@ -164,7 +163,6 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
             if (n < N) {
                 const float vv = to_f32(v_r[(btv * H + h) * N + n]), ww = to_f32(w[(bt * H + h) * N + n]);
                 sq = fmaf(vv, sB[g * N + n], sq);
-                sw = fmaf(ww, sC[g * N + n], sw);
                 if (SLICES) {
                     ab[k] = fmaf(d, vv, ab[k]);
                     ac[k] += ww;
@@ -173,17 +171,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ dy, 
         }
         // wavefront sums: each 16-lane row by DPP moves, then the four rows
         sq = row16_sum(sq);
-        sw = row16_sum(sw);
         sxy = row16_sum(sxy);
 #pragma unroll
         for (int off = 16; off < 64; off <<= 1) {
             sq += __shfl_xor(sq, off, 64);
-            sw += __shfl_xor(sw, off, 64);
             sxy += __shfl_xor(sxy, off, 64);
         }
         if (lane == 0) {
             q[(bb * H + h) * L + t] = sq;
-            if (dlam) dlam[(bb * H + h) * L + t] = sw - d * sq;
             dxy[(bb * H + h) * L + t] = sxy;
         }
     }
@@ -301,11 +296,10 @@ __global__ void __launch_bounds__(256) combine_quad_kernel(const bf16* __restric
 
 // the combine kernel with LDS slices for the group sums when they fit, else the two-pass form
 template <class T, class U, class V>
-hipError_t launch_combine(const void* dy, const void* x, const void* dt, const void* B, const void* C,
-                          const float* D, const U* u_r, const V* v_r, const V* w, void* dx, void* dB,
-                          void* dC, float* q, float* dlam, float* dxy, int64_t b, int64_t L, int64_t Lr, int H, int P,
-                          int N, int G, hipStream_t st, bool vrev = true) {
-    const size_t base = (size_t)(2 * G * N + H) * 4, sliced = base + (size_t)8 * G * N * 4;
+hipError_t launch_combine(const void* dy, const void* x, const void* dt, const void* B, const float* D, const U* u_r,
+                          const V* v_r, const V* w, void* dx, void* dB, void* dC, float* q, float* dxy, int64_t b,
+                          int64_t L, int64_t Lr, int H, int P, int N, int G, hipStream_t st, bool vrev = true) {
+    const size_t base = (size_t)(G * N + H) * 4, sliced = base + (size_t)8 * G * N * 4;
     const bool slices = sliced <= 160 * 1024;
     const size_t lds = slices ? sliced : base;
     const void* fn =
@@ -315,89 +309,123 @@ hipError_t launch_combine(const void* dy, const void* x, const void* dt, const v
     if (slices)
         hipLaunchKernelGGL((combine_kernel<T, U, V, true>), dim3((unsigned)(b * L)), dim3(256), lds, st,
                            static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
-                           static_cast<const T*>(B), static_cast<const T*>(C), D, u_r, v_r, w, static_cast<T*>(dx),
-                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, Lr, H, P, N, G, vrev ? 1 : 0);
+                           static_cast<const T*>(B), D, u_r, v_r, w, static_cast<T*>(dx), static_cast<T*>(dB),
+                           static_cast<T*>(dC), q, dxy, L, Lr, H, P, N, G, vrev ? 1 : 0);
     else
         hipLaunchKernelGGL((combine_kernel<T, U, V, false>), dim3((unsigned)(b * L)), dim3(256), lds, st,
                            static_cast<const T*>(dy), static_cast<const T*>(x), static_cast<const T*>(dt),
-                           static_cast<const T*>(B), static_cast<const T*>(C), D, u_r, v_r, w, static_cast<T*>(dx),
-                           static_cast<T*>(dB), static_cast<T*>(dC), q, dlam, dxy, L, Lr, H, P, N, G, vrev ? 1 : 0);
+                           static_cast<const T*>(B), D, u_r, v_r, w, static_cast<T*>(dx), static_cast<T*>(dB),
+                           static_cast<T*>(dC), q, dxy, L, Lr, H, P, N, G, vrev ? 1 : 0);
     return hipGetLastError();
 }
 
-// per (b, h): the final-state term, suffix sums R_k = sum_{t>=k} d lambda_t (fp64), ddt, and the
-// (b, h) parts of dA = sum_k dt_k R_k and dD = sum_t dy_t . x_t
+// The chunk-local decay gradient for the fp32 flow (any headdim, dstate and chunk up to 512), the same four
+// terms as decay_grad.hip, R_k = T1 + T2_k + T3_k + T4_k, in plain fp32 loops; one workgroup per (head,
+// chunk, b).  The in-chunk cumulative log2 decay is formed here in fp64 from dt, so the decay between any
+// two tokens of the chunk is exact to fp32 rounding however large the chunk's total.  S0T: the forward
+// transposed scan's chunk-start states (b, nC, H, N, P); Gst: the adjoint scan's chunk-start states
+// (b, nC, H, P, N) in reversed chunk order (its walk front-padded to whole chunks), entering decayed by
+// the next chunk's first token; the last chunk's is dfinal.
 template <class T>
-__global__ void __launch_bounds__(256) suffix_kernel(const float* __restrict__ dlam, const float* __restrict__ q,
-                                                     const float* __restrict__ dxy, const T* __restrict__ dt,
-                                                     const float* __restrict__ A,
-                                                     const float* __restrict__ dfinal, const float* __restrict__ finT,
-                                                     T* __restrict__ ddt, double* __restrict__ dA_part,
-                                                     double* __restrict__ dD_part, int64_t L, int H, int P, int N) {
-    __shared__ double red[256];
-    const int tid = threadIdx.x;
-    const int h = blockIdx.x;
-    const int64_t bb = blockIdx.y;
-    const int64_t bh = bb * H + h;
-    const float Ah = A[h];
-    // <dfinal, S_{L-1}>: the loss's dependence on the last log-decay through the final state
-    double fterm = 0.0;
-    if (dfinal) {
-        const int64_t PN = (int64_t)P * N;
-        for (int64_t e = tid; e < PN; e += 256) {
-            const int p = (int)(e / N), n = (int)(e % N);
-            fterm += (double)dfinal[bh * PN + e] * (double)finT[(bh * N + n) * P + p];
+__global__ void __launch_bounds__(256) decay_grad_plain_kernel(const T* __restrict__ x, const T* __restrict__ dy,
+                                                               const T* __restrict__ B, const T* __restrict__ C,
+                                                               const T* __restrict__ dt, const float* __restrict__ A,
+                                                               const float* __restrict__ S0T,
+                                                               const float* __restrict__ Gst, float* __restrict__ R,
+                                                               int64_t L, int H, int P, int N, int G, int Q,
+                                                               int64_t nC) {
+    extern __shared__ double dsm[];
+    double* lw = dsm;          // [Q] in-chunk cumulative log2 decay, fp64 (flat past the sequence end)
+    double* t2 = lw + Q;       // [Q] T2 suffix sums
+    double* red = t2 + Q;      // [256]
+    float* dtw = reinterpret_cast<float*>(red + 256);  // [Q]
+    float *s2 = dtw + Q, *s3 = s2 + Q, *rowsum = s3 + Q, *colsum = rowsum + Q;
+    const int tid = threadIdx.x, h = blockIdx.x;
+    const int64_t c = blockIdx.y, bb = blockIdx.z;
+    const int g = h / (H / G);
+    const int64_t c0 = c * Q;
+    const int valid = (int)(L - c0 < Q ? L - c0 : Q);
+    const double al = (double)A[h] * 1.4426950408889634;  // A log2 e
+    for (int t = tid; t < Q; t += 256) {
+        dtw[t] = t < valid ? to_f32(dt[(bb * L + c0 + t) * H + h]) : 0.0f;
+        s2[t] = s3[t] = rowsum[t] = colsum[t] = 0.0f;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double acc = 0.0;
+        for (int t = 0; t < Q; ++t) {
+            acc += al * (double)dtw[t];
+            lw[t] = acc;
         }
     }
-    red[tid] = fterm;
+    // T1's dot <Gam, S0> in fp64
+    const int64_t PN = (int64_t)P * N, HP = (int64_t)H * P, GN = (int64_t)G * N;
+    const float* S0c = S0T + ((bb * nC + c) * H + h) * PN;           // [n][p]
+    const float* Gc = Gst + ((bb * nC + (nC - 1 - c)) * H + h) * PN;  // [p][n]
+    double dot = 0.0;
+    for (int64_t e = tid; e < PN; e += 256) dot += (double)Gc[e] * (double)S0c[(e % N) * P + e / N];
+    red[tid] = dot;
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
         if (tid < s) red[tid] += red[tid + s];
         __syncthreads();
     }
-    fterm = red[0];
-    __syncthreads();
-    // thread tid owns tokens [t0, t1)
-    const int64_t per = (L + 255) / 256;
-    const int64_t t0 = tid * per < L ? tid * per : L, t1 = t0 + per < L ? t0 + per : L;
-    const float* dl = dlam + bh * L;
-    double loc = 0.0;
-    for (int64_t t = t0; t < t1; ++t) loc += (double)dl[t] + (t == L - 1 ? fterm : 0.0);
-    // exclusive suffix over the threads after this one
-    red[tid] = loc;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const double add = tid + off < 256 ? red[tid + off] : 0.0;
-        __syncthreads();
-        red[tid] += add;
-        __syncthreads();
+    const double tdot = red[0];
+    // s2_t = dy_t . (S0 C_t) and s3_t = x_t . (Gam B_t), one (token, p) per step
+    for (int e = tid; e < valid * P; e += 256) {
+        const int t = e / P, p = e % P;
+        const T* Ct = C + (bb * L + c0 + t) * GN + (int64_t)g * N;
+        const T* Bt = B + (bb * L + c0 + t) * GN + (int64_t)g * N;
+        float u = 0.0f, v = 0.0f;
+        for (int n = 0; n < N; ++n) {
+            u = fmaf(S0c[(int64_t)n * P + p], to_f32(Ct[n]), u);
+            v = fmaf(Gc[(int64_t)p * N + n], to_f32(Bt[n]), v);
+        }
+        const int64_t o = (bb * L + c0 + t) * HP + (int64_t)h * P + p;
+        atomicAdd(&s2[t], to_f32(dy[o]) * u);
+        atomicAdd(&s3[t], to_f32(x[o]) * v);
     }
-    double R = red[tid] - loc;  // sum over later threads' tokens
-    double da = 0.0, dd = 0.0;
-    for (int64_t t = t1 - 1; t >= t0; --t) {
-        R += (double)dl[t] + (t == L - 1 ? fterm : 0.0);
-        const float d = to_f32(dt[(bb * L + t) * H + h]);
-        ddt[(bb * L + t) * H + h] = from_f32<T>((float)((double)Ah * R + (double)q[bh * L + t]));
-        da += (double)d * R;
-        dd += (double)dxy[bh * L + t];
+    // T4: M_tj = (dy_t . x_j)(C_t . B_j) 2^(l_t - l_j) dt_j over the pairs j < t, into row and column sums
+    const int npair = valid * (valid - 1) / 2;
+    for (int e = tid; e < npair; e += 256) {
+        int t = (int)((1.0 + sqrt(1.0 + 8.0 * (double)e)) * 0.5);  // pair e = t (t - 1) / 2 + j
+        while (t * (t - 1) / 2 > e) --t;
+        while ((t + 1) * t / 2 <= e) ++t;
+        const int j = e - t * (t - 1) / 2;
+        const T* yt = dy + (bb * L + c0 + t) * HP + (int64_t)h * P;
+        const T* xj = x + (bb * L + c0 + j) * HP + (int64_t)h * P;
+        const T* Ct = C + (bb * L + c0 + t) * GN + (int64_t)g * N;
+        const T* Bj = B + (bb * L + c0 + j) * GN + (int64_t)g * N;
+        float yx = 0.0f, cb = 0.0f;
+        for (int p = 0; p < P; ++p) yx = fmaf(to_f32(yt[p]), to_f32(xj[p]), yx);
+        for (int n = 0; n < N; ++n) cb = fmaf(to_f32(Ct[n]), to_f32(Bj[n]), cb);
+        const float m = yx * cb * exp2f((float)(lw[t] - lw[j])) * dtw[j];
+        atomicAdd(&rowsum[t], m);
+        atomicAdd(&colsum[j], m);
     }
     __syncthreads();
-    red[tid] = da;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) red[tid] += red[tid + s];
-        __syncthreads();
+    // R_k = T1 + T2_k + T3_k + T4_k, in fp64 over the chunk's positions
+    if (tid == 0) {
+        const double lend = lw[Q - 1];
+        // the adjoint enters decayed by the next token's factor (none after the sequence's end)
+        const double gam = c + 1 < nC ? exp2(al * (double)to_f32(dt[(bb * L + c0 + Q) * H + h])) : 1.0;
+        const double T1 = exp2(lend) * gam * tdot;
+        double suf = 0.0;
+        for (int k = valid - 1; k >= 0; --k) {
+            suf += exp2(lw[k]) * (double)s2[k];
+            t2[k] = suf;
+        }
+        double pre3 = 0.0, pre4 = 0.0;
+        float* Rh = R + (bb * H + h) * L + c0;
+        for (int k = 0; k < valid; ++k) {
+            Rh[k] = (float)(T1 + t2[k] + pre3 + pre4);
+            pre3 += (double)dtw[k] * exp2(lend - lw[k]) * gam * (double)s3[k];
+            pre4 += (double)colsum[k] - (double)rowsum[k];
+        }
     }
-    if (tid == 0) dA_part[bh] = red[0];
-    __syncthreads();
-    red[tid] = dd;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) red[tid] += red[tid + s];
-        __syncthreads();
-    }
-    if (tid == 0) dD_part[bh] = red[0];
 }
+
+inline size_t decay_grad_plain_lds(int Q) { return (size_t)(2 * Q + 256) * 8 + (size_t)5 * Q * 4; }
 
 // dA[h], dD[h]: sums over the batch rows
 __global__ void __launch_bounds__(256) reduce_kernel(const double* __restrict__ dA_part, const double* __restrict__ dD_part,
@@ -723,8 +751,8 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
                                dCb, q, L, H, G);
         BWD_CHECK(hipGetLastError());
     } else {
-        BWD_CHECK((launch_combine<T, bf16, bf16>(dy, x, dt, B, C, D, nullptr, v, w, dx, dB, dC, q, nullptr, dxy, b, L,
-                                                 L, H, P, N, G, st, false)));
+        BWD_CHECK((launch_combine<T, bf16, bf16>(dy, x, dt, B, D, nullptr, v, w, dx, dB, dC, q, dxy, b, L, L, H, P, N,
+                                                 G, st, false)));
     }
     if (finish_tile_lds(H) <= 64 * 1024) {
         const int64_t ntile = (L + kFinTok - 1) / kFinTok;
@@ -755,14 +783,15 @@ template <class T>
 hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const void* dt, const float* A,
                const void* B, const void* C, const float* D, const float* h0, const void* dy, const float* dfinal,
                void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0, char* ws, hipStream_t st) {
-    const int64_t b = s.b, L = s.L;
+    const int64_t b = s.b, L = s.L, Lr = f.Lr, pad = f.Lr - s.L;
     const int H = (int)s.H, P = (int)s.P, N = (int)s.N, G = (int)s.G;
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
     T *xr = reinterpret_cast<T*>(ws + f.xr), *dyr = reinterpret_cast<T*>(ws + f.dyr);
     T *Cr = reinterpret_cast<T*>(ws + f.Cr), *Br = reinterpret_cast<T*>(ws + f.Br);
     float *drev = F(f.drev), *dfwd = F(f.dfwd), *dt_t = F(f.dt_t), *cs = F(f.cs);
-    float *states = F(f.states), *u_r = F(f.u_r), *v_r = F(f.v_r), *w = F(f.w), *G0 = F(f.G0), *dfT = F(f.dfT);
-    float *h0T = F(f.h0T), *finT = F(f.finT), *fscr = F(f.fscr), *q = F(f.q), *dlam = F(f.dlam), *dxy = F(f.dxy);
+    float *states = F(f.states), *states_b = F(f.states_b), *u_r = F(f.u_r), *v_r = F(f.v_r), *w = F(f.w);
+    float *G0 = F(f.G0), *dfT = F(f.dfT), *h0T = F(f.h0T), *finT = F(f.finT), *fscr = F(f.fscr), *q = F(f.q);
+    float *dxy = F(f.dxy), *R = F(f.R);
     double *dA_part = reinterpret_cast<double*>(ws + f.dA_part), *dD_part = reinterpret_cast<double*>(ws + f.dD_part);
     const int64_t PN = (int64_t)P * N;
     const int io = sizeof(T) == 2 ? 1 : 0;
@@ -784,13 +813,14 @@ hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const voi
         }
         return hipSuccess;
     }
-    // time-reversed copies for the reversed scans, in the input dtype
-    BWD_CHECK((copy<T, T>(x, xr, b, L, H, P, 1, true, 0, st)));
-    BWD_CHECK((copy<T, T>(dy, dyr, b, L, H, P, 1, true, 0, st)));
-    BWD_CHECK((copy<T, T>(C, Cr, b, L, G, N, 1, true, 0, st)));
-    BWD_CHECK((copy<T, T>(B, Br, b, L, G, N, 1, true, 0, st)));
-    hipLaunchKernelGGL(steps_kernel<T>, grid1(b * L * H), dim3(256), 0, st, static_cast<const T*>(dt), drev, dfwd, L,
-                       (int64_t)0, H, b * L * H);
+    // time-reversed copies for the reversed scans, in the input dtype, front-padded to whole chunks so that
+    // every reversed chunk is a forward chunk read backwards
+    BWD_CHECK((copy<T, T>(x, xr, b, L, H, P, 1, true, pad, st)));
+    BWD_CHECK((copy<T, T>(dy, dyr, b, L, H, P, 1, true, pad, st)));
+    BWD_CHECK((copy<T, T>(C, Cr, b, L, G, N, 1, true, pad, st)));
+    BWD_CHECK((copy<T, T>(B, Br, b, L, G, N, 1, true, pad, st)));
+    hipLaunchKernelGGL(steps_kernel<T>, grid1(b * Lr * H), dim3(256), 0, st, static_cast<const T*>(dt), drev, dfwd, L,
+                       pad, H, b * Lr * H);
     BWD_CHECK(hipGetLastError());
     hipLaunchKernelGGL(transpose_kernel, grid1(b * H * PN), dim3(256), 0, st, dfinal, dfT, P, N, b * H * PN);
     BWD_CHECK(hipGetLastError());
@@ -798,44 +828,57 @@ hipError_t run(const Shape& s, const BackwardLayout& f, const void* x, const voi
     BWD_CHECK(hipGetLastError());
 
     const DtFront none{nullptr, 0, 0, 0, 0.0f, 0.0f};
-    Shape sb = s;  // the adjoint scan: headdim P, dstate N, G groups, fp32 compute
+    Shape sb = s;  // the adjoint scan: headdim P, dstate N, G groups, fp32 compute, over Lr reversed tokens
     sb.io = 0;
-    Shape sT = s;  // the transposed scans: headdim N, dstate P, one group per head, fp32 compute
-    sT.io = 0;
+    sb.L = Lr;
+    Shape sT = sb;  // the transposed scans: headdim N, dstate P, one group per head
     sT.P = N;
     sT.N = P;
     sT.G = H;
     const int hpg = H / G;  // the transposed scans' x-role (B or C) is shared by the heads of a group
     // reversed scans (b) and (c): decay steps d', input step 1
     BWD_CHECK(launch_chunk_cumsum(sb, none, drev, A, dt_t, cs, st));
-    hipLaunchKernelGGL(ones_kernel, grid1(b * H * s.nC * s.Q), dim3(256), 0, st, dt_t, L, (int)s.Q, s.nC,
+    hipLaunchKernelGGL(ones_kernel, grid1(b * H * s.nC * s.Q), dim3(256), 0, st, dt_t, Lr, (int)s.Q, s.nC,
                        b * H * s.nC * s.Q);
     BWD_CHECK(hipGetLastError());
-    // (b) on the bf16 chunk kernels when the shape allows: only dx (bf16 accuracy) and the final
-    // adjoint (fp32, hi + lo split chunk states) come from it; the decay gradients use (c) and (d)
-    Shape s16 = s;
+    // (b) on the bf16 chunk kernels when the shape allows: dx (bf16 accuracy), and the final adjoint and the
+    // chunk-start adjoints (fp32, hi + lo split chunk states) for the decay gradient
+    Shape s16 = sb;
     s16.io = 1;
     const bool fastb = io == 1 && fast_chunk_supported(s16);
     if (fastb)
-        BWD_CHECK(scan(s16, dyr, Cr, Br, dt_t, cs, states, dfinal, G0, u_r, st));
+        BWD_CHECK(scan(s16, dyr, Cr, Br, dt_t, cs, states_b, dfinal, G0, u_r, st));
     else
-        BWD_CHECK(scan_in(sb, io, 1, dyr, Cr, Br, dt_t, cs, states, dfinal, G0, u_r, st));
+        BWD_CHECK(scan_in(sb, io, 1, dyr, Cr, Br, dt_t, cs, states_b, dfinal, G0, u_r, st));
     // (c): x-role C of the head's group, B-role dy, read out through x (all reversed)
     BWD_CHECK(scan_in(sT, io, hpg, Cr, dyr, xr, dt_t, cs, states, dfT, fscr, v_r, st));
-    // forward transposed scan (d): decay and input step dt; x-role B, B-role x, read out through dy
-    BWD_CHECK(launch_chunk_cumsum(sb, none, dfwd, A, dt_t, cs, st));
-    BWD_CHECK(scan_in(sT, io, hpg, B, x, dy, dt_t, cs, states, h0 ? h0T : nullptr, finT, w, st));
+    // forward transposed scan (d): decay and input step dt; x-role B, B-role x, read out through dy; its
+    // chunk-start states (S0 transposed) stay in `states` for the decay gradient
+    Shape sf = s;
+    sf.io = 0;
+    Shape sTf = sT;
+    sTf.L = L;
+    BWD_CHECK(launch_chunk_cumsum(sf, none, dfwd, A, dt_t, cs, st));
+    BWD_CHECK(scan_in(sTf, io, hpg, B, x, dy, dt_t, cs, states, h0 ? h0T : nullptr, finT, w, st));
 
-    // combine
+    // combine: dx, dB, dC, q and dy . x
     if (fastb)
-        BWD_CHECK((launch_combine<T, bf16, float>(dy, x, dt, B, C, D, reinterpret_cast<const bf16*>(u_r), v_r, w, dx, dB,
-                                                  dC, q, dlam, dxy, b, L, L, H, P, N, G, st)));
+        BWD_CHECK((launch_combine<T, bf16, float>(dy, x, dt, B, D, reinterpret_cast<const bf16*>(u_r), v_r, w, dx, dB,
+                                                  dC, q, dxy, b, L, Lr, H, P, N, G, st)));
     else
-        BWD_CHECK((launch_combine<T, float, float>(dy, x, dt, B, C, D, u_r, v_r, w, dx, dB, dC, q, dlam, dxy, b, L, L, H,
-                                                   P, N, G, st)));
-    hipLaunchKernelGGL(suffix_kernel<T>, dim3((unsigned)H, (unsigned)b), dim3(256), 0, st, dlam, q, dxy,
-                       static_cast<const T*>(dt), A, dfinal, finT, static_cast<T*>(ddt), dA_part, dD_part, L, H, P,
-                       N);
+        BWD_CHECK((launch_combine<T, float, float>(dy, x, dt, B, D, u_r, v_r, w, dx, dB, dC, q, dxy, b, L, Lr, H, P,
+                                                   N, G, st)));
+    // the decay gradient chunk by chunk, then ddt, dA, dD
+    const size_t lds = decay_grad_plain_lds((int)s.Q);
+    BWD_CHECK(hipFuncSetAttribute((const void*)decay_grad_plain_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds));
+    hipLaunchKernelGGL(decay_grad_plain_kernel<T>, dim3((unsigned)H, (unsigned)s.nC, (unsigned)b), dim3(256), lds, st,
+                       static_cast<const T*>(x), static_cast<const T*>(dy), static_cast<const T*>(B),
+                       static_cast<const T*>(C), static_cast<const T*>(dt), A, states, states_b, R, L, H, P, N, G,
+                       (int)s.Q, s.nC);
+    BWD_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(finish_kernel<T>, dim3((unsigned)H, (unsigned)b), dim3(256), 0, st, q, R, dxy,
+                       static_cast<const T*>(dt), A, static_cast<T*>(ddt), dA_part, dD_part, L, H);
     BWD_CHECK(hipGetLastError());
     hipLaunchKernelGGL(reduce_kernel, grid1(H), dim3(256), 0, st, dA_part, dD_part, dA, dD, b, H);
     BWD_CHECK(hipGetLastError());
@@ -867,7 +910,7 @@ BackwardLayout backward_layout(const Shape& s) {
     auto a256 = [](size_t v) { return (v + 255) / 256 * 256; };
     BackwardLayout f{};
     f.local = decay_grad_supported(s);
-    f.Lr = f.local ? s.nC * s.Q : s.L;  // the reversed walks: front-padded to whole chunks when local
+    f.Lr = s.nC * s.Q;  // the reversed walks: front-padded to whole chunks
     const size_t BLHN = (size_t)(s.b * s.L * s.H * s.N) * 4, BLH = (size_t)(s.b * s.L * s.H) * 4;
     const size_t CS = (size_t)(s.b * s.H * s.nC * s.Q) * 4, ST = (size_t)(s.b * s.nC * s.H * s.P * s.N) * 4;
     const size_t HS = (size_t)(s.b * s.H * s.P * s.N) * 4, BH8 = (size_t)(s.b * s.H) * 8;
@@ -901,9 +944,9 @@ BackwardLayout backward_layout(const Shape& s) {
         const size_t RLGN = (size_t)(s.b * f.Lr * s.G * s.N), RLH = (size_t)(s.b * f.Lr * s.H) * 4;
         f.xr = take(RLHP / 4 * sz), f.dyr = take(RLHP / 4 * sz), f.Cr = take(RLGN * sz), f.Br = take(RLGN * sz);
         f.drev = take(RLH), f.dfwd = take(BLH), f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST);
-        f.u_r = take(RLHP), f.v_r = take(RLHN), f.w = take(BLHN);
+        f.u_r = take(RLHP), f.v_r = take(RLHN), f.w = take(BLHN), f.states_b = take(ST);
         f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS), f.fscr = take(HS);
-        f.q = take(BLH), f.dlam = take(BLH), f.dxy = take(BLH), f.dA_part = take(BH8), f.dD_part = take(BH8);
+        f.q = take(BLH), f.dxy = take(BLH), f.R = take(BLH), f.dA_part = take(BH8), f.dD_part = take(BH8);
     }
     f.total = o;
     return f;

@@ -126,7 +126,7 @@ hipError_t launch_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, in
 // Backward pass (backward.hip): three fp32 chunked scans on converted copies of the
 // inputs.  Byte offsets of the workspace pieces (all 256-byte aligned).
 struct BackwardLayout {
-    size_t xr, dyr, Cr, Br, drev, dfwd, dt_t, cs, states, u_r, v_r, w, G0, dfT, h0T, finT, fscr, q, dlam, dxy,
+    size_t xr, dyr, Cr, Br, drev, dfwd, dt_t, cs, states, u_r, v_r, w, G0, dfT, h0T, finT, fscr, q, dxy,
         dA_part, dD_part, states_b, R, sub, totals, stT, total;
     int64_t Qt;  // chunk of the half-head transposed scans (local flow)
     int64_t Lr;  // rows of the time-reversed copies (the sequence, front-padded to whole chunks when local)
