@@ -737,7 +737,7 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     BWD_CHECK(launch_chunk_walk(sw, x, B, dtl(ff), lwp(ff, H, nsf, b), stT, st, xw));
     // the decay gradient, chunk by chunk at Q, from its chunk cumsum arrays and the stored states
     BWD_CHECK(launch_chunk_cumsum(s, DtFront{nullptr, 0, 0, 0, 0.0f, 0.0f}, dt, A, dt_t, cs, st));
-    BWD_CHECK(launch_decay_grad(s, x, dy, B, C, cs, dt_t, states, states_b, R, dxy, st));
+    BWD_CHECK(launch_decay_grad(s, x, dy, B, C, cs, dt_t, states, states_b, F(f.cbt), R, dxy, st));
 
     const size_t lq = (size_t)32 * G * N * 4;  // the quad combine's LDS slices
     if (P == 64 && (N == 64 || N == 128) && H % 4 == 0 && lq <= 64 * 1024) {
@@ -938,6 +938,7 @@ BackwardLayout backward_layout(const Shape& s) {
         const int64_t nct = (f.Lr + f.Qt - 1) / f.Qt;  // at least the forward chunk count (L <= Lr)
         f.totals = take((size_t)(s.b * H2 * nct) * 4);
         f.stT = take((size_t)(s.b * nct * s.H * s.N * s.P) * 4);
+        f.cbt = take(decay_grad_tile_bytes(s));  // the chunks' C . B tiles
     } else {
         const size_t sz = s.io == 1 ? 2 : 4;  // the reversed copies keep the input dtype
         const size_t RLHP = (size_t)(s.b * f.Lr * s.H * s.P) * 4, RLHN = (size_t)(s.b * f.Lr * s.H * s.N) * 4;

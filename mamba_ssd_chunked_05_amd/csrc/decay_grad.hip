@@ -22,8 +22,9 @@
 // no longer needs fp32 scans: dy . x and C . B are exact bf16 products with
 // fp32 accumulation, and S0 and Gam enter the MFMA split into hi + lo bf16.
 //
-// One workgroup (four wavefronts) per (b, chunk, head); headdim 64, dstate 64
-// or 128, chunk 64 or 128.
+// T4's C . B factor does not depend on the head: a small kernel forms its tiles once per (b, chunk, group)
+// and every head of the group reads them.  The per-head kernel then keeps only x, dy and one B-or-C tile
+// in LDS (under half of a CU's), so two of its workgroups share each CU.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -32,23 +33,17 @@ namespace dg {
 
 constexpr int P = 64;
 constexpr int QMAX = 128;
-constexpr int XS = P + 16;  // x / dy row stride (bf16): 16-byte fragment reads of 16 rows
+constexpr int XS = P + 8;  // x / dy row stride (bf16): 16-byte fragment reads of 16 rows hit distinct banks
 
-template <int N>
-struct Lds {
-    static constexpr int NS = N + 16;  // B / C row stride (bf16)
-    bf16 xs[QMAX * XS];
-    bf16 ys[QMAX * XS];   // dy
-    bf16 bs[QMAX * NS];
-    bf16 cs[QMAX * NS];
-    float lw[QMAX];       // in-chunk cumulative log2 decay (flat past the sequence end)
-    float dtw[QMAX];      // dt (zero past the sequence end)
-    float rowsum[QMAX];
-    float colsum[QMAX];
-    float s2[QMAX];       // dy_t . (S0 C_t), before the factor 2^(l_t)
-    float s3[QMAX];       // x_j . (Gam B_j), before dt_j 2^(l_c1 - l_j)
-    float red[4];
-};
+// tiles on and below the diagonal of a chunk's Q x Q matrix, 16 x 16 each
+__host__ __device__ constexpr int tri_tiles(int Q) { return (Q / 16) * (Q / 16 + 1) / 2; }
+
+// tile tt -> (it, jt), jt <= it, tt = it (it + 1) / 2 + jt
+__device__ __forceinline__ void tri_index(int tt, int& it, int& jt) {
+    it = 0;
+    while ((it + 1) * (it + 2) / 2 <= tt) ++it;
+    jt = tt - it * (it + 1) / 2;
+}
 
 // a buffer resource over rows [0, rows) of a row-major bf16 tile (row_stride elements apart, row_len
 // elements read per row); rows past it read zero
@@ -63,7 +58,6 @@ __device__ __forceinline__ uint4 ldr(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-
 // 8 fp32 values -> hi and lo bf16 fragments
 __device__ __forceinline__ void split8(const float4& a, const float4& b, Frag<bf16>& hi, Frag<bf16>& lo) {
     const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -75,21 +69,118 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, Frag<bf
     }
 }
 
-// R and dxy (dy_t . x_t, for dD) (b, H, L) fp32.  cs / dtv: the forward chunk cumsum arrays (b, H, nC, Q) (log2 units; dt, zero past
-// L); S0: forward chunk-start states (b, nC, H, P, N); Gst: the reversed adjoint scan's chunk-start
-// states (b, nC, H, P, N) in reversed chunk order, so forward chunk c reads reversed chunk nC - 1 - c:
-// the adjoint G_{c1+1} of the token after the chunk (dfinal for the last chunk), which enters decayed
-// by that token's factor 2^(cs of the next chunk's first position).
+// C_t . B_j over the tiles on and below the diagonal of each (b, chunk, group), as exact bf16 products
+// with fp32 accumulation.  cbt: (b, nC, G, tri_tiles(Q), 256) fp32, tile tt = it (it + 1) / 2 + jt in the
+// accumulator order: float 4 l + r of a tile is row 16 it + 4 (l / 16) + r, column 16 jt + l % 16 (rows
+// past the sequence end are zero).  One workgroup of four wavefronts per item; B and C of the chunk in LDS.
+template <int N>
+__global__ void __launch_bounds__(256) cb_tiles_kernel(const bf16* __restrict__ B, const bf16* __restrict__ C,
+                                                       float* __restrict__ cbt, int64_t L, int G, int Q, int64_t nC,
+                                                       uint32_t nitems) {
+    constexpr int NK = N / 32, NS = N + 8;
+    __shared__ bf16 bs[QMAX * NS];
+    __shared__ bf16 cs[QMAX * NS];
+    const uint32_t item = xcd_remap(blockIdx.x, nitems);  // (b nC + c) G + g
+    const int g = (int)(item % (uint32_t)G);
+    const int64_t c = (item / (uint32_t)G) % (uint32_t)nC;
+    const int64_t b = item / ((uint32_t)G * (uint32_t)nC);
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t c0 = c * Q, GN = (int64_t)G * N;
+    const int valid = (int)(L - c0 < Q ? L - c0 : Q);
+    const auto rb = rows_rsrc(B + ((b * L + c0) * G + g) * (int64_t)N, GN, valid, N);
+    const auto rc = rows_rsrc(C + ((b * L + c0) * G + g) * (int64_t)N, GN, valid, N);
+    constexpr int KB = QMAX * (N / 8) / 256, BR = 256 / (N / 8);  // pieces per thread; rows per pass
+    const int r0 = tid / (N / 8), col = (tid % (N / 8)) * 8;
+    uint4 vb[KB], vc[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        const uint32_t off = (uint32_t)(((int64_t)(r0 + BR * k) * GN + col) * 2);
+        vb[k] = ldr(rb, off);
+        vc[k] = ldr(rc, off);
+    }
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        if (r0 + BR * k < Q) {
+            *reinterpret_cast<uint4*>(&bs[(r0 + BR * k) * NS + col]) = vb[k];
+            *reinterpret_cast<uint4*>(&cs[(r0 + BR * k) * NS + col]) = vc[k];
+        }
+    }
+    __syncthreads();
+    const int ntiles = tri_tiles(Q);
+    float* out = cbt + (int64_t)item * ntiles * 256 + lane * 4;
+    for (int tt = w; tt < ntiles; tt += 4) {
+        int it, jt;
+        tri_index(tt, it, jt);
+        f32x4 ac = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+            Frag<bf16> a, bo;
+            frag_load8<bf16>(a, &cs[(16 * it + l16) * NS + 32 * ks + 8 * g4]);
+            frag_load8<bf16>(bo, &bs[(16 * jt + l16) * NS + 32 * ks + 8 * g4]);
+            mma(ac, a, bo);
+        }
+        *reinterpret_cast<float4*>(out + tt * 256) = make_float4(ac[0], ac[1], ac[2], ac[3]);
+    }
+}
+
+template <int N>
+struct Lds {
+    static constexpr int NS = N + 8;  // B / C row stride (bf16)
+    bf16 xs[QMAX * XS];
+    bf16 ys[QMAX * XS];   // dy
+    bf16 bc[QMAX * NS];   // C while T2 runs, then B for T3
+    float lw[QMAX];       // in-chunk cumulative log2 decay (flat past the sequence end)
+    float dtw[QMAX];      // dt (zero past the sequence end)
+    float rowsum[QMAX];
+    float colsum[QMAX];
+    float s2[QMAX];       // dy_t . (S0 C_t), before the factor 2^(l_t)
+    float s3[QMAX];       // x_j . (Gam B_j), before dt_j 2^(l_c1 - l_j)
+    float red[4];
+};
+
+// T2 (C with S0, read out by dy) or T3 (B with Gam, read out by x) for the state rows p = 16 pt + l16 and
+// the token tiles it = half, half + 2, ...: the sum over p of D_tp (St A_t)_p into out[t]
+template <int N>
+__device__ __forceinline__ void state_term(const bf16* A, const bf16* Dm, float* out, const Frag<bf16> (&sh)[N / 32],
+                                           const Frag<bf16> (&sl)[N / 32], int pt, int half, int QT, int l16, int g4) {
+    constexpr int NK = N / 32, NS = Lds<N>::NS;
+    for (int it = half; it < QT; it += 2) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+            Frag<bf16> a;
+            frag_load8<bf16>(a, &A[(16 * it + l16) * NS + 32 * ks + 8 * g4]);
+            mma(acc, a, sh[ks]);
+            mma(acc, a, sl[ks]);
+        }
+        // acc[r] = (St A_t)_p for t = 16 it + 4 g4 + r; the four sums over p land in lanes l16 = 4 r
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = static_cast<float>(Dm[(16 * it + 4 * g4 + r) * XS + 16 * pt + l16]) * acc[r];
+        const float vs = row16_sum4(v[0], v[1], v[2], v[3], l16);
+        if ((l16 & 3) == 0) atomicAdd(&out[16 * it + 4 * g4 + (l16 >> 2)], vs);
+    }
+}
+
+// R and dxy (dy_t . x_t, for dD) (b, H, L) fp32.  cs / dtv: the forward chunk cumsum arrays (b, H, nC, Q)
+// (log2 units; dt, zero past L); cbt: cb_tiles_kernel's C . B tiles; S0: forward chunk-start states
+// (b, nC, H, P, N); Gst: the reversed adjoint scan's chunk-start states (b, nC, H, P, N) in reversed chunk
+// order, so forward chunk c reads reversed chunk nC - 1 - c: the adjoint G_{c1+1} of the token after the
+// chunk (dfinal for the last chunk), which enters decayed by that token's factor 2^(cs of the next chunk's
+// first position).
 //
-// Eight wavefronts.  Wavefront w < 4 holds rows 16 w .. 16 w + 15 of S0, wavefront 4 + w the same rows
-// of Gam, in registers (hi + lo bf16 fragments, read once): each forms its state term for those 16 of
-// the P output columns over every token of the chunk, and the four parts of each term meet in LDS.
-// x, dy, B and C of the chunk sit in LDS; all eight share the tiles of M.
+// Eight wavefronts; wavefront w holds rows 16 (w % 4) .. + 15 of both S0 and Gam in registers (hi + lo
+// bf16 fragments, read once) and forms T2, then T3, for those 16 of the P output columns over every other
+// 16-token tile of the chunk (w / 4 picks which); the parts of each term meet in LDS.  x and dy of the
+// chunk sit in LDS, and one tile that holds C for T2 and is then refilled with B for T3.  All eight share
+// the tiles of M, whose C . B factor comes from cbt.
 template <int N>
 __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict__ x, const bf16* __restrict__ dy,
                                                          const bf16* __restrict__ B, const bf16* __restrict__ C,
                                                          const float* __restrict__ cs,
                                                          const float* __restrict__ dtv,
+                                                         const float* __restrict__ cbt,
                                                          const float* __restrict__ S0,
                                                          const float* __restrict__ Gst, float* __restrict__ R,
                                                          float* __restrict__ dxy, int64_t L, int H, int G, int Q,
@@ -103,13 +194,14 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pt = w & 3;          // this wavefront's 16 state rows
-    const bool gam_half = w >= 4;  // S0 (T2) or Gam (T3)
+    const int pt = w & 3;    // this wavefront's 16 state rows
+    const int half = w >> 2; // its token tiles in T2 and T3
     const int QT = Q / 16;
     const int64_t c0 = c * Q;
     const int valid = (int)(L - c0 < Q ? L - c0 : Q);  // tokens of this chunk inside the sequence
 
-    // ---- loads: x, dy, B, C pieces (zero past the sequence end), this wavefront's state rows --------
+    // ---- loads: x, dy and C pieces into LDS, B pieces held for T3 (zero past the sequence end), this
+    // wavefront's rows of S0 and Gam ----------------------------------------------------------------------
     const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N;
     const auto rx = rows_rsrc(x + ((b * L + c0) * H + h) * (int64_t)P, HP, valid, P);
     const auto ry = rows_rsrc(dy + ((b * L + c0) * H + h) * (int64_t)P, HP, valid, P);
@@ -127,19 +219,16 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
         vy[k] = ldr(ry, off);
     }
 #pragma unroll
-    for (int k = 0; k < KB; ++k) {
-        const uint32_t off = (uint32_t)(((int64_t)(br0 + BR * k) * GN + bc) * 2);
-        vb[k] = ldr(rb, off);
-        vc[k] = ldr(rc, off);
-    }
+    for (int k = 0; k < KB; ++k) vc[k] = ldr(rc, (uint32_t)(((int64_t)(br0 + BR * k) * GN + bc) * 2));
     const float* S0c = S0 + ((b * nC + c) * H + h) * (int64_t)P * N + (int64_t)(16 * pt + l16) * N + 8 * g4;
     const float* Gc = Gst + ((b * nC + (nC - 1 - c)) * H + h) * (int64_t)P * N + (int64_t)(16 * pt + l16) * N + 8 * g4;
-    const float* Mine = gam_half ? Gc : S0c;
-    float4 sa[NK][2];
+    float4 sa[NK][2], ga[NK][2];
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
-        sa[ks][0] = *reinterpret_cast<const float4*>(Mine + 32 * ks);
-        sa[ks][1] = *reinterpret_cast<const float4*>(Mine + 32 * ks + 4);
+        sa[ks][0] = *reinterpret_cast<const float4*>(S0c + 32 * ks);
+        sa[ks][1] = *reinterpret_cast<const float4*>(S0c + 32 * ks + 4);
+        ga[ks][0] = *reinterpret_cast<const float4*>(Gc + 32 * ks);
+        ga[ks][1] = *reinterpret_cast<const float4*>(Gc + 32 * ks + 4);
     }
     const int64_t base = ((b * H + h) * nC + c) * Q;
     if (tid < Q) {
@@ -158,30 +247,29 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
         }
     }
 #pragma unroll
-    for (int k = 0; k < KB; ++k) {
-        if (br0 + BR * k < Q) {
-            *reinterpret_cast<uint4*>(&sm.bs[(br0 + BR * k) * NS + bc]) = vb[k];
-            *reinterpret_cast<uint4*>(&sm.cs[(br0 + BR * k) * NS + bc]) = vc[k];
-        }
-    }
-    // T1 part: the S0 wavefronts read the matching Gam rows for the dot product only
-    float dot = 0.0f;
-    if (!gam_half) {
+    for (int k = 0; k < KB; ++k)
+        if (br0 + BR * k < Q) *reinterpret_cast<uint4*>(&sm.bc[(br0 + BR * k) * NS + bc]) = vc[k];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) vb[k] = ldr(rb, (uint32_t)(((int64_t)(br0 + BR * k) * GN + bc) * 2));
+    // T1 part: <S0, Gam> over this wavefront's rows (one wavefront per row block)
+    if (half == 0) {
+        float dot = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < NK; ++ks) {
-            const float4 v0 = *reinterpret_cast<const float4*>(Gc + 32 * ks);
-            const float4 v1 = *reinterpret_cast<const float4*>(Gc + 32 * ks + 4);
-            const float4 u0 = sa[ks][0], u1 = sa[ks][1];
+            const float4 v0 = ga[ks][0], v1 = ga[ks][1], u0 = sa[ks][0], u1 = sa[ks][1];
             dot = fmaf(u0.x, v0.x, fmaf(u0.y, v0.y, fmaf(u0.z, v0.z, fmaf(u0.w, v0.w, dot))));
             dot = fmaf(u1.x, v1.x, fmaf(u1.y, v1.y, fmaf(u1.z, v1.z, fmaf(u1.w, v1.w, dot))));
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-        if (lane == 0) sm.red[w] = dot;
+        if (lane == 0) sm.red[pt] = dot;
     }
-    Frag<bf16> sh[NK], sl[NK];
+    Frag<bf16> sh[NK], sl[NK], gh[NK], gl[NK];
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) split8(sa[ks][0], sa[ks][1], sh[ks], sl[ks]);
+    for (int ks = 0; ks < NK; ++ks) {
+        split8(sa[ks][0], sa[ks][1], sh[ks], sl[ks]);
+        split8(ga[ks][0], ga[ks][1], gh[ks], gl[ks]);
+    }
     __syncthreads();
 
     // ---- dy_t . x_t per token (for dD): four threads per token, 16 columns each -------------------
@@ -200,36 +288,23 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
         if ((tid & 3) == 0 && t < valid) dxy[(b * H + h) * L + c0 + t] = sxy;
     }
 
-    // ---- T2 (C with S0, read out by dy) or T3 (B with Gam, read out by x) for p = 16 pt + l16 ----------
-    {
-        const bf16* A = gam_half ? sm.bs : sm.cs;
-        const bf16* Dm = gam_half ? sm.xs : sm.ys;
-        float* out = gam_half ? sm.s3 : sm.s2;
-        for (int it = 0; it < QT; ++it) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- T2 from the C tile; then the tile is refilled with B and T3 formed --------------------------
+    state_term<N>(sm.bc, sm.ys, sm.s2, sh, sl, pt, half, QT, l16, g4);
+    __syncthreads();
 #pragma unroll
-            for (int ks = 0; ks < NK; ++ks) {
-                Frag<bf16> a;
-                frag_load8<bf16>(a, &A[(16 * it + l16) * NS + 32 * ks + 8 * g4]);
-                mma(acc, a, sh[ks]);
-                mma(acc, a, sl[ks]);
-            }
-            // acc[r] = (St A_t)_p for t = 16 it + 4 g4 + r; the four sums over p land in lanes l16 = 4 r
-            float v[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = static_cast<float>(Dm[(16 * it + 4 * g4 + r) * XS + 16 * pt + l16]) * acc[r];
-            const float vs = row16_sum4(v[0], v[1], v[2], v[3], l16);
-            if ((l16 & 3) == 0) atomicAdd(&out[16 * it + 4 * g4 + (l16 >> 2)], vs);
-        }
-    }
+    for (int k = 0; k < KB; ++k)
+        if (br0 + BR * k < Q) *reinterpret_cast<uint4*>(&sm.bc[(br0 + BR * k) * NS + bc]) = vb[k];
+    __syncthreads();
+    state_term<N>(sm.bc, sm.xs, sm.s3, gh, gl, pt, half, QT, l16, g4);
 
     // ---- T4: the strictly lower triangle of M, tile by tile, into row and column sums -------------
-    const int ntiles = QT * (QT + 1) / 2;
+    const int ntiles = tri_tiles(Q);
+    const float* cbi = cbt + ((b * nC + c) * G + g) * (int64_t)ntiles * 256 + lane * 4;
     for (int tt = w; tt < ntiles; tt += 8) {
-        int it = 0;
-        while ((it + 1) * (it + 2) / 2 <= tt) ++it;
-        const int jt = tt - it * (it + 1) / 2;
-        f32x4 ad = {0.f, 0.f, 0.f, 0.f}, ac = {0.f, 0.f, 0.f, 0.f};
+        int it, jt;
+        tri_index(tt, it, jt);
+        const float4 cb = *reinterpret_cast<const float4*>(cbi + tt * 256);
+        f32x4 ad = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < P / 32; ++ks) {
             Frag<bf16> a, bo;
@@ -237,13 +312,7 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
             frag_load8<bf16>(bo, &sm.xs[(16 * jt + l16) * XS + 32 * ks + 8 * g4]);
             mma(ad, a, bo);
         }
-#pragma unroll
-        for (int ks = 0; ks < NK; ++ks) {
-            Frag<bf16> a, bo;
-            frag_load8<bf16>(a, &sm.cs[(16 * it + l16) * NS + 32 * ks + 8 * g4]);
-            frag_load8<bf16>(bo, &sm.bs[(16 * jt + l16) * NS + 32 * ks + 8 * g4]);
-            mma(ac, a, bo);
-        }
+        const float ac[4] = {cb.x, cb.y, cb.z, cb.w};
         const int j = 16 * jt + l16;
         const float lj = sm.lw[j], dj = sm.dtw[j];
         float colp = 0.0f, m[4];
@@ -261,7 +330,6 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
         if (g4 == 0) atomicAdd(&sm.colsum[j], colp);
     }
     __syncthreads();
-
     // ---- R_k = T1 + T2_k + T3_k + T4_k: one wavefront, two positions per lane ---------------------
     if (w == 0) {
         const float lend = sm.lw[Q - 1];
@@ -300,18 +368,27 @@ bool decay_grad_supported(const Shape& s) {
     return s.io == 1 && s.P == 64 && (s.N == 64 || s.N == 128) && (s.Q == 64 || s.Q == dg::QMAX);
 }
 
+size_t decay_grad_tile_bytes(const Shape& s) {
+    return (size_t)(s.b * s.nC * s.G) * dg::tri_tiles((int)s.Q) * 256 * sizeof(float);
+}
+
 hipError_t launch_decay_grad(const Shape& s, const void* x, const void* dy, const void* B, const void* C,
-                             const float* cs, const float* dtv, const float* S0, const float* Gst, float* R, float* dxy,
-                             hipStream_t st) {
-    const uint32_t nitems = (uint32_t)(s.b * s.nC * s.H);
+                             const float* cs, const float* dtv, const float* S0, const float* Gst, float* cbt,
+                             float* R, float* dxy, hipStream_t st) {
+    const uint32_t nitems = (uint32_t)(s.b * s.nC * s.H), ncb = (uint32_t)(s.b * s.nC * s.G);
     if (nitems == 0) return hipSuccess;
     const bf16 *xb = (const bf16*)x, *yb = (const bf16*)dy, *bb = (const bf16*)B, *cb = (const bf16*)C;
-    if (s.N == 128)
-        hipLaunchKernelGGL(dg::decay_grad_kernel<128>, dim3(nitems), dim3(512), 0, st, xb, yb, bb, cb, cs, dtv, S0, Gst,
-                           R, dxy, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
-    else
-        hipLaunchKernelGGL(dg::decay_grad_kernel<64>, dim3(nitems), dim3(512), 0, st, xb, yb, bb, cb, cs, dtv, S0, Gst,
-                           R, dxy, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+    if (s.N == 128) {
+        hipLaunchKernelGGL(dg::cb_tiles_kernel<128>, dim3(ncb), dim3(256), 0, st, bb, cb, cbt, s.L, (int)s.G, (int)s.Q,
+                           s.nC, ncb);
+        hipLaunchKernelGGL(dg::decay_grad_kernel<128>, dim3(nitems), dim3(512), 0, st, xb, yb, bb, cb, cs, dtv, cbt, S0,
+                           Gst, R, dxy, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+    } else {
+        hipLaunchKernelGGL(dg::cb_tiles_kernel<64>, dim3(ncb), dim3(256), 0, st, bb, cb, cbt, s.L, (int)s.G, (int)s.Q,
+                           s.nC, ncb);
+        hipLaunchKernelGGL(dg::decay_grad_kernel<64>, dim3(nitems), dim3(512), 0, st, xb, yb, bb, cb, cs, dtv, cbt, S0,
+                           Gst, R, dxy, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+    }
     return hipGetLastError();
 }
 

@@ -127,7 +127,7 @@ hipError_t launch_selective_scan(int64_t b, int64_t L, int64_t Dc, int64_t N, in
 // inputs.  Byte offsets of the workspace pieces (all 256-byte aligned).
 struct BackwardLayout {
     size_t xr, dyr, Cr, Br, drev, dfwd, dt_t, cs, states, u_r, v_r, w, G0, dfT, h0T, finT, fscr, q, dxy,
-        dA_part, dD_part, states_b, R, sub, totals, stT, total;
+        dA_part, dD_part, states_b, R, sub, totals, stT, cbt, total;
     int64_t Qt;  // chunk of the half-head transposed scans (local flow)
     int64_t Lr;  // rows of the time-reversed copies (the sequence, front-padded to whole chunks when local)
     bool local;  // the decay gradient is formed chunk by chunk (decay_grad.hip)
@@ -137,10 +137,12 @@ struct BackwardLayout {
 bool decay_grad_supported(const Shape& s);
 // R (b, H, L): R_k = a_k <G_k, S_{k-1}> from the forward chunk cumsum arrays (cs, dt), the forward
 // chunk-start states S0 (b, nC, H, P, N) and the reversed adjoint scan's chunk-start states Gst (same
-// layout, reversed chunk order).
+// layout, reversed chunk order); dxy (b, H, L) = dy_t . x_t.  cbt: scratch of decay_grad_tile_bytes(s)
+// bytes for the chunks' C . B tiles (shared by the heads of a group).
+size_t decay_grad_tile_bytes(const Shape& s);
 hipError_t launch_decay_grad(const Shape& s, const void* x, const void* dy, const void* B, const void* C,
-                             const float* cs, const float* dtv, const float* S0, const float* Gst, float* R, float* dxy,
-                             hipStream_t st);
+                             const float* cs, const float* dtv, const float* S0, const float* Gst, float* cbt,
+                             float* R, float* dxy, hipStream_t st);
 BackwardLayout backward_layout(const Shape& s);
 hipError_t launch_backward(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
                            const void* C, const float* D, const float* h0, const void* dy, const float* dfinal,
