@@ -38,11 +38,14 @@ constexpr int XS = P + 8;  // x / dy row stride (bf16): 16-byte fragment reads o
 // tiles on and below the diagonal of a chunk's Q x Q matrix, 16 x 16 each
 __host__ __device__ constexpr int tri_tiles(int Q) { return (Q / 16) * (Q / 16 + 1) / 2; }
 
-// tile tt -> (it, jt), jt <= it, tt = it (it + 1) / 2 + jt
-__device__ __forceinline__ void tri_index(int tt, int& it, int& jt) {
-    it = 0;
-    while ((it + 1) * (it + 2) / 2 <= tt) ++it;
-    jt = tt - it * (it + 1) / 2;
+// column-major order of those tiles: column jt holds rows it = jt .. QT - 1 and starts at tile col_start(jt)
+__host__ __device__ constexpr int col_start(int QT, int jt) { return jt * QT - jt * (jt - 1) / 2; }
+
+// tile k -> (it, jt)
+__device__ __forceinline__ void col_index(int k, int QT, int& it, int& jt) {
+    jt = 0;
+    while (col_start(QT, jt + 1) <= k) ++jt;
+    it = jt + (k - col_start(QT, jt));
 }
 
 // a buffer resource over rows [0, rows) of a row-major bf16 tile (row_stride elements apart, row_len
@@ -70,9 +73,9 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, Frag<bf
 }
 
 // C_t . B_j over the tiles on and below the diagonal of each (b, chunk, group), as exact bf16 products
-// with fp32 accumulation.  cbt: (b, nC, G, tri_tiles(Q), 256) fp32, tile tt = it (it + 1) / 2 + jt in the
-// accumulator order: float 4 l + r of a tile is row 16 it + 4 (l / 16) + r, column 16 jt + l % 16 (rows
-// past the sequence end are zero).  One workgroup of four wavefronts per item; B and C of the chunk in LDS.
+// with fp32 accumulation.  cbt: (b, nC, G, tri_tiles(Q), 256) fp32, tiles in column-major order (col_index),
+// each in the accumulator order: float 4 l + r of tile (it, jt) is row 16 it + 4 (l / 16) + r, column
+// 16 jt + l % 16 (rows past the sequence end are zero).  One workgroup of four wavefronts per item; B and C of the chunk in LDS.
 template <int N>
 __global__ void __launch_bounds__(256) cb_tiles_kernel(const bf16* __restrict__ B, const bf16* __restrict__ C,
                                                        float* __restrict__ cbt, int64_t L, int G, int Q, int64_t nC,
@@ -109,9 +112,9 @@ __global__ void __launch_bounds__(256) cb_tiles_kernel(const bf16* __restrict__ 
     __syncthreads();
     const int ntiles = tri_tiles(Q);
     float* out = cbt + (int64_t)item * ntiles * 256 + lane * 4;
-    for (int tt = w; tt < ntiles; tt += 4) {
+    for (int k = w; k < ntiles; k += 4) {
         int it, jt;
-        tri_index(tt, it, jt);
+        col_index(k, Q / 16, it, jt);
         f32x4 ac = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NK; ++ks) {
@@ -120,12 +123,12 @@ __global__ void __launch_bounds__(256) cb_tiles_kernel(const bf16* __restrict__ 
             frag_load8<bf16>(bo, &bs[(16 * jt + l16) * NS + 32 * ks + 8 * g4]);
             mma(ac, a, bo);
         }
-        *reinterpret_cast<float4*>(out + tt * 256) = make_float4(ac[0], ac[1], ac[2], ac[3]);
+        *reinterpret_cast<float4*>(out + k * 256) = make_float4(ac[0], ac[1], ac[2], ac[3]);
     }
 }
 
 template <int N>
-struct Lds {
+struct alignas(16) Lds {
     static constexpr int NS = N + 8;  // B / C row stride (bf16)
     bf16 xs[QMAX * XS];
     bf16 ys[QMAX * XS];   // dy
@@ -290,6 +293,16 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
 
     // ---- T2 from the C tile; then the tile is refilled with B and T3 formed --------------------------
     state_term<N>(sm.bc, sm.ys, sm.s2, sh, sl, pt, half, QT, l16, g4);
+    // this wavefront's run of C . B tiles of M (tiles k0 .. k1 - 1 in column-major order), fetched while
+    // T3 runs into the registers that S0's fragments held
+    const int ntiles = tri_tiles(Q);
+    const int k0 = w * ntiles / 8, k1 = (w + 1) * ntiles / 8;
+    const float* cbi = cbt + (((b * nC + c) * G + g) * (int64_t)ntiles + k0) * 256 + lane * 4;
+    constexpr int KT = (tri_tiles(QMAX) + 7) / 8;
+    float4 cbv[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+        cbv[k] = k0 + k < k1 ? *reinterpret_cast<const float4*>(cbi + k * 256) : make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < KB; ++k)
@@ -297,39 +310,61 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
     __syncthreads();
     state_term<N>(sm.bc, sm.xs, sm.s3, gh, gl, pt, half, QT, l16, g4);
 
-    // ---- T4: the strictly lower triangle of M, tile by tile, into row and column sums -------------
-    const int ntiles = tri_tiles(Q);
-    const float* cbi = cbt + ((b * nC + c) * G + g) * (int64_t)ntiles * 256 + lane * 4;
-    for (int tt = w; tt < ntiles; tt += 8) {
-        int it, jt;
-        tri_index(tt, it, jt);
-        const float4 cb = *reinterpret_cast<const float4*>(cbi + tt * 256);
-        f32x4 ad = {0.f, 0.f, 0.f, 0.f};
+    // ---- T4: the strictly lower triangle of M, tile by tile, into row and column sums.  Down a column of
+    // tiles the x fragments, the column's decay and dt stay in registers and the column sums accumulate
+    // there; each tile's four row sums take one LDS atomic. ------------------------------------------------
+    {
+        int jt = -1;
+        Frag<bf16> xf[P / 32];
+        float lj = 0.0f, dj = 0.0f, colp = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < P / 32; ++ks) {
-            Frag<bf16> a, bo;
-            frag_load8<bf16>(a, &sm.ys[(16 * it + l16) * XS + 32 * ks + 8 * g4]);
-            frag_load8<bf16>(bo, &sm.xs[(16 * jt + l16) * XS + 32 * ks + 8 * g4]);
-            mma(ad, a, bo);
-        }
-        const float ac[4] = {cb.x, cb.y, cb.z, cb.w};
-        const int j = 16 * jt + l16;
-        const float lj = sm.lw[j], dj = sm.dtw[j];
-        float colp = 0.0f, m[4];
+        for (int kk = 0; kk < KT; ++kk) {
+            const int k = k0 + kk;
+            if (k >= k1) break;
+            int it, jn;
+            col_index(k, QT, it, jn);
+            if (jn != jt) {
+                if (jt >= 0) {
+                    colp += __shfl_xor(colp, 16, 64);
+                    colp += __shfl_xor(colp, 32, 64);
+                    if (g4 == 0) atomicAdd(&sm.colsum[16 * jt + l16], colp);
+                }
+                jt = jn;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * it + 4 * g4 + r;
-            // j < t only; the exponent is capped at 0 so no masked lane forms an infinity
-            m[r] = j < t ? ad[r] * ac[r] * fast_exp2(fminf(sm.lw[t] - lj, 0.0f)) * dj : 0.0f;
-            colp += m[r];
+                for (int ks = 0; ks < P / 32; ++ks) frag_load8<bf16>(xf[ks], &sm.xs[(16 * jt + l16) * XS + 32 * ks + 8 * g4]);
+                lj = sm.lw[16 * jt + l16];
+                dj = sm.dtw[16 * jt + l16];
+                colp = 0.0f;
+            }
+            f32x4 ad = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < P / 32; ++ks) {
+                Frag<bf16> a;
+                frag_load8<bf16>(a, &sm.ys[(16 * it + l16) * XS + 32 * ks + 8 * g4]);
+                mma(ad, a, xf[ks]);
+            }
+            const float4 cb = cbv[kk];
+            const float4 lt = *reinterpret_cast<const float4*>(&sm.lw[16 * it + 4 * g4]);
+            const float ac[4] = {cb.x, cb.y, cb.z, cb.w}, lr[4] = {lt.x, lt.y, lt.z, lt.w};
+            const int j = 16 * jt + l16;
+            float m[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // j < t only; the exponent is capped at 0 so no masked lane forms an infinity
+                m[r] = j < 16 * it + 4 * g4 + r ? ad[r] * ac[r] * fast_exp2(fminf(lr[r] - lj, 0.0f)) * dj : 0.0f;
+                colp += m[r];
+            }
+            const float rs = row16_sum4(m[0], m[1], m[2], m[3], l16);  // row t = 16 it + 4 g4 + l16 / 4
+            if ((l16 & 3) == 0) atomicAdd(&sm.rowsum[16 * it + 4 * g4 + (l16 >> 2)], rs);
         }
-        const float rs = row16_sum4(m[0], m[1], m[2], m[3], l16);  // row t = 16 it + 4 g4 + l16 / 4
-        if ((l16 & 3) == 0) atomicAdd(&sm.rowsum[16 * it + 4 * g4 + (l16 >> 2)], rs);
-        colp += __shfl_xor(colp, 16, 64);
-        colp += __shfl_xor(colp, 32, 64);
-        if (g4 == 0) atomicAdd(&sm.colsum[j], colp);
+        if (jt >= 0) {
+            colp += __shfl_xor(colp, 16, 64);
+            colp += __shfl_xor(colp, 32, 64);
+            if (g4 == 0) atomicAdd(&sm.colsum[16 * jt + l16], colp);
+        }
     }
     __syncthreads();
+
     // ---- R_k = T1 + T2_k + T3_k + T4_k: one wavefront, two positions per lane ---------------------
     if (w == 0) {
         const float lend = sm.lw[Q - 1];
