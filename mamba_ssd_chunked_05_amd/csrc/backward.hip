@@ -240,8 +240,11 @@ __global__ void __launch_bounds__(256) combine_quad_kernel(const bf16* __restric
     const int64_t bt = blockIdx.x;  // b * L + t
     const int64_t bb = bt / L, t = bt % L;
     const int hpg = H / G, nq = H / 4;
-    for (int e = tid; e < 32 * G * N; e += 256) lds[e] = 0.0f;
-    __syncthreads();
+    // with one group and every (wavefront, lane row) slot holding heads, every slot writes its partial sums
+    if (!(G == 1 && nq >= 4)) {
+        for (int e = tid; e < 32 * G * N; e += 256) lds[e] = 0.0f;
+        __syncthreads();
+    }
     float ab[NV], ac[NV], bv[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) ab[k] = ac[k] = 0.0f;
