@@ -636,9 +636,10 @@ __global__ void __launch_bounds__(256) dh0_tr_kernel(const float* __restrict__ G
 // walk the inputs backwards (XMap::rows) over Lr tokens, the sequence front-padded to whole backward
 // chunks of Q tokens (the padding reads as zero), so that every reversed Q-chunk is a forward Q-chunk read
 // backwards.  The decay gradient needs, at every Q-chunk, the forward state entering it (S0) and the
-// adjoint entering it from the next one: both are stored every Q tokens by kernels that carry the state
-// in registers at the transposed scans' large chunk (hi/lo state updates), started from the transposed
-// scans' chunk-start states -- no Q-chunk local states and no pass over them.
+// adjoint entering it from the next one: both are stored every Q tokens by scans that carry that state in
+// registers at the transposed scans' large chunk (hi/lo state updates) -- the adjoint scan (b), and the
+// forward transposed scan (d), whose state is S^T and is stored back in (P, N) layout -- so there are
+// no Q-chunk local states and no pass over them.
 hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, const void* dt, const float* A,
                      const void* B, const void* C, const float* D, const float* h0, const void* dy,
                      const float* dfinal, void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0,
@@ -654,8 +655,8 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     T *v = reinterpret_cast<T*>(ws + f.v_r), *w = reinterpret_cast<T*>(ws + f.w);
     double *dA_part = reinterpret_cast<double*>(ws + f.dA_part), *dD_part = reinterpret_cast<double*>(ws + f.dD_part);
     // the sub-chunk-local decay arrays (dtl, lw pairs): reversed per head (b), reversed per half-head (c),
-    // forwards per half-head (d), forwards per head (S0); the per-head and per-half-head ones coincide at N = 64
-    // (a pair for k heads over n sub-chunks: dtl, then lw, each b k n 64 floats; local_decay_floats sizes them)
+    // forwards per half-head (d); the per-head and per-half-head ones coincide at N = 64
+    // (a pair for k heads over n sub-chunks: dtl, then lw, each b k n 64 floats; backward_layout sizes them)
     const int64_t nsr = Lr / 64, nsf = (L + 63) / 64;
     float* at = F(f.sub);
     auto pair = [&](int64_t heads, int64_t nsub) {
@@ -666,7 +667,6 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     float* rl = pair(H, nsr);
     float* rh = nh == 2 ? pair(H2, nsr) : rl;
     float* fh = pair(H2, nsf);
-    float* ff = nh == 2 ? pair(H, nsf) : fh;
     auto dtl = [](float* p) { return p; };
     auto lwp = [](float* p, int64_t heads, int64_t nsub, int64_t bb) { return p + bb * heads * nsub * 64; };
     const int64_t PN = (int64_t)P * N;
@@ -691,10 +691,6 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     sk.L = L;
     sk.H = H2;
     BWD_CHECK(launch_subchunk_decay_bwd(sk, dt, A, dtl(fh), lwp(fh, H2, nsf, b), L, nh, false, false, st));
-    if (nh == 2) {
-        sk.H = H;
-        BWD_CHECK(launch_subchunk_decay_bwd(sk, dt, A, dtl(ff), lwp(ff, H, nsf, b), L, 1, false, false, st));
-    }
 
     // (c) G^T read out through x: v (dB, q), as H2 half-heads of headdim 64 (at dstate 128 each head splits
     // into the two halves of the state's N rows, which form one head pair) whose x is (that half of) C of
@@ -710,7 +706,7 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     sh.nC = (Lr + f.Qt - 1) / f.Qt;
     Shape s1 = sh;  // the pass over the chunk totals: a chunk of "length 1" in its indexing
     s1.Q = 1;
-    const XMap xmr{nh * G, nh * hpg, nh, L, nullptr, nullptr, 0, 0};
+    const XMap xmr{nh * G, nh * hpg, nh, L, nullptr, nullptr, 0, 0, 0};
     BWD_CHECK(launch_chunk_state_sub(sh, C, dy, dtl(rh), lwp(rh, H2, nsr, b), stT, totals, st, &xmr));
     BWD_CHECK(launch_state_passing(s1, stT, totals, dfT, G0T, st));
     BWD_CHECK(launch_chunk_scan_sub(sh, C, dy, x, dtl(rh), lwp(rh, H2, nsr, b), stT, nullptr, v, st, &xmr));
@@ -721,23 +717,19 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     sb.L = Lr;
     sb.Q = f.Qt;
     sb.nC = sh.nC;
-    const XMap xb{H, 1, 1, L, dt, states_b, (int)s.Q, 1};
+    const XMap xb{H, 1, 1, L, dt, states_b, (int)s.Q, 1, 0};
     BWD_CHECK(launch_chunk_scan_sub(sb, dy, C, B, dtl(rl), lwp(rl, H, nsr, b), stT, D, dx, st, &xb));
-    // (d) S^T read out through dy: w (dC), as half-heads like (c), forwards in time; its chunk-start states
-    // seed the walk that stores the forward state entering every Q-chunk (S0)
+    // (d) S^T read out through dy: w (dC), as half-heads like (c), forwards in time; it also stores the
+    // forward state entering every Q-chunk (S0), back in the heads' (P, N) layout
     sh.L = L;
     sh.nC = (L + f.Qt - 1) / f.Qt;
     s1 = sh;
     s1.Q = 1;
-    const XMap xm{nh * G, nh * hpg, nh, 0, nullptr, nullptr, 0, 0};
+    const XMap xm{nh * G, nh * hpg, nh, 0, nullptr, nullptr, 0, 0, 0};
+    const XMap xmt{nh * G, nh * hpg, nh, 0, nullptr, states, (int)s.Q, 0, nh};
     BWD_CHECK(launch_chunk_state_sub(sh, B, x, dtl(fh), lwp(fh, H2, nsf, b), stT, totals, st, &xm));
     BWD_CHECK(launch_state_passing(s1, stT, totals, h0 ? h0T : nullptr, finT, st));
-    BWD_CHECK(launch_chunk_scan_sub(sh, B, x, dy, dtl(fh), lwp(fh, H2, nsf, b), stT, nullptr, w, st, &xm));
-    Shape sw = s;
-    sw.Q = f.Qt;
-    sw.nC = sh.nC;
-    const XMap xw{H, 1, 1, 0, nullptr, states, (int)s.Q, 1};
-    BWD_CHECK(launch_chunk_walk(sw, x, B, dtl(ff), lwp(ff, H, nsf, b), stT, st, xw));
+    BWD_CHECK(launch_chunk_scan_sub(sh, B, x, dy, dtl(fh), lwp(fh, H2, nsf, b), stT, nullptr, w, st, &xmt));
     // the decay gradient, chunk by chunk at Q, from its chunk cumsum arrays and the stored states
     BWD_CHECK(launch_chunk_cumsum(s, DtFront{nullptr, 0, 0, 0, 0.0f, 0.0f}, dt, A, dt_t, cs, st));
     BWD_CHECK(launch_decay_grad(s, x, dy, B, C, cs, dt_t, states, states_b, F(f.cbt), R, dxy, st));
@@ -936,7 +928,7 @@ BackwardLayout backward_layout(const Shape& s) {
         // per half-head and per head), chunk totals and chunk-start states (transposed, per half-head)
         f.Qt = transposed_chunk(s);
         const int64_t nh = s.N / 64, H2 = nh * s.H, nsr = f.Lr / 64, nsf = (s.L + 63) / 64;
-        const int64_t heads_r = s.H + (nh == 2 ? H2 : 0), heads_f = H2 + (nh == 2 ? s.H : 0);
+        const int64_t heads_r = s.H + (nh == 2 ? H2 : 0), heads_f = H2;
         f.sub = take((size_t)(2 * s.b * 64 * (heads_r * nsr + heads_f * nsf)) * 4);
         const int64_t nct = (f.Lr + f.Qt - 1) / f.Qt;  // at least the forward chunk count (L <= Lr)
         f.totals = take((size_t)(s.b * H2 * nct) * 4);

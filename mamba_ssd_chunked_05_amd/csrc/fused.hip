@@ -212,8 +212,9 @@ struct ScanLds {
 
 // FWD: sub-chunk-local decay arrays (subchunk_decay_kernel), as the forward reads them.
 // REV (with FWD): the inputs are walked backwards and the output written forwards (XMap::rows); TAP
-// (with REV): the carried state is stored every XMap::tapq positions, with a hi/lo state update.
-template <int N, int HPW, bool FWD, bool REV = false, bool TAP = false>
+// (with FWD): the carried state is stored every XMap::tapq positions, with a hi/lo state update; TTR
+// (with TAP): it is a transposed scan's state, stored back in its heads' layout (XMap::tap_tr).
+template <int N, int HPW, bool FWD, bool REV = false, bool TAP = false, bool TTR = false>
 __global__ void __launch_bounds__(256, 2)
 chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, const bf16* __restrict__ C,
                        DtSrc ds, const float* __restrict__ start, const float* __restrict__ D, bf16* __restrict__ y, int64_t L,
@@ -294,12 +295,25 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     for (int sc = 0; sc < nsub; ++sc) {
         const int64_t tbase = t0 + (int64_t)sc * QS;
         if (TAP && tbase % xm.tapq == 0) {  // the state entering this position
+            const int64_t tk = b * ((L + xm.tapq - 1) / xm.tapq) + tbase / xm.tapq;
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
-                float* out = xm.tap + ((b * ((L + xm.tapq - 1) / xm.tapq) + tbase / xm.tapq) * H + h0 + hh) * (int64_t)P * N +
-                             (int64_t)(16 * w + l16) * N + 4 * g4;
+                if constexpr (TTR) {  // a transposed scan's state, back in its head's (dstate x headdim) layout
+                    // (dword stores, 64 contiguous bytes per 16 lanes; a quad-lane transpose to 16-byte stores
+                    // measured slower)
+                    const int nh = xm.tap_tr, h2 = h0 + hh;
+                    float* out = xm.tap + (tk * (H / nh) + h2 / nh) * (int64_t)N * (64 * nh) + 64 * (h2 % nh) +
+                                 16 * w + l16;
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(out + 16 * nt) = st[hh][nt];
+                    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) out[(int64_t)(16 * nt + 4 * g4 + r) * (64 * nh)] = st[hh][nt][r];
+                    }
+                } else {
+                    float* out = xm.tap + (tk * H + h0 + hh) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 4 * g4;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(out + 16 * nt) = st[hh][nt];
+                }
             }
         }
         __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
@@ -665,148 +679,6 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
 }
 
 // ---------------------------------------------------------------------------
-// chunk walk: the states entering every tapq-th position, from the chunk-start states
-// ---------------------------------------------------------------------------
-template <int N, int HPW>
-struct WalkLds {
-    bf16 xs[HPW * QS * XS];
-    bf16 bs[QS * Strides<N>::BS];
-    float lw[HPW * QS];
-    float dtw[HPW * QS];
-    float ww[HPW * QS];
-    float alpha[4];
-};
-
-// Per (b, chunk, head pair): carry the fp32 state from the chunk-start state over the chunk's 64-token
-// sub-chunks, S <- 2^(l_63) S + B^T (w x) with w_j = 2^(l_63 - l_j) dt_j and the scaled operand split into
-// hi + lo bf16, and store it (XMap::tap) at every position that is a multiple of XMap::tapq: the
-// chunk-start states of a tapq-chunking with neither chunk-local states nor a pass over them.  Reads
-// sub-chunk-local decay arrays (subchunk_decay_kernel); XMap::start_tr as for the chunk scan.
-template <int N, int HPW>
-__global__ void __launch_bounds__(256, 2)
-chunk_walk_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, DtSrc ds, const float* __restrict__ start,
-                       int64_t L, int H, int G, int Q, int64_t nC, uint32_t nitems, XMap xm) {
-    constexpr int NT = N / 16;
-    constexpr int BS = Strides<N>::BS;
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    WalkLds<N, HPW>& sm = *reinterpret_cast<WalkLds<N, HPW>*>(smem_raw);
-
-    const int HP = H / HPW;
-    const uint32_t item = xcd_remap(blockIdx.x, nitems);
-    const int hp = (int)(item % (uint32_t)HP);
-    const int64_t c = (item / (uint32_t)HP) % (uint32_t)nC;
-    const int64_t b = item / ((uint32_t)HP * (uint32_t)nC);
-    const int h0 = hp * HPW;
-    const int g = h0 / (H / G);
-    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, in a scalar register
-    const int64_t t0 = c * Q;
-    const int64_t t_end = t0 + Q < L ? t0 + Q : L;
-    const int nsub = (int)((t_end - t0 + QS - 1) / QS);
-    float cs_prev = 0.0f, tot = 0.0f;
-
-    f32x4 st[HPW][NT];  // st[hh][nt] holds S[p = 16w + l16][n = 16nt + 4g4 + r]
-    if (xm.start_tr) {
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int n = 16 * nt + 4 * g4;
-                const float* S0 = start + (((b * nC + c) * H + h0 + hh) * (N / 64) + n / 64) * (int64_t)64 * P +
-                                  (int64_t)(n % 64) * P + 16 * w + l16;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) st[hh][nt][r] = S0[r * P];
-            }
-        }
-    } else {
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-            const float* S0 =
-                start + ((b * nC + c) * H + h0 + hh) * (int64_t)P * N + (int64_t)(16 * w + l16) * N + 4 * g4;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) st[hh][nt] = *reinterpret_cast<const f32x4*>(S0 + 16 * nt);
-        }
-    }
-
-    const int64_t nsubT = (L + QS - 1) / QS;
-    const int64_t dt_head = nsubT * QS;
-    const int64_t dt0 = ((b * H + h0) * nsubT + c * (Q / QS)) * QS;
-    const int64_t ntap = (L + xm.tapq - 1) / xm.tapq;
-    const int xh0 = h0 / xm.div * xm.mul;
-    ChunkAddr<N, HPW> ad;
-    chunk_addr<N, HPW>(ad, xm.hx, G, dt_head, tid);
-    ChunkRegs<N, HPW, false> rg;
-    chunk_load<N, HPW, false>(rg, ad, tile_base<false>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, t0, 0), xm.hx,
-                              G, tid);
-
-    for (int sc = 0; sc < nsub; ++sc) {
-        const int64_t tbase = t0 + (int64_t)sc * QS;
-        if (tbase % xm.tapq == 0) {  // the state entering this position
-#pragma unroll
-            for (int hh = 0; hh < HPW; ++hh) {
-                float* out = xm.tap + ((b * ntap + tbase / xm.tapq) * H + h0 + hh) * (int64_t)P * N +
-                             (int64_t)(16 * w + l16) * N + 4 * g4;
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(out + 16 * nt) = st[hh][nt];
-            }
-        }
-        __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
-        chunk_store<N, HPW, false, true>(sm.xs, sm.bs, nullptr, sm.lw, sm.dtw, sm.ww, nullptr, sm.alpha, rg, ad,
-                                         cs_prev, tot, tid);
-        __syncthreads();
-        if (sc + 1 < nsub) {
-            const int64_t t1 = tbase + QS;
-            chunk_load<N, HPW, false>(
-                rg, ad, tile_base<false>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc + 1), xm.hx, G, tid);
-        }
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-            const float alpha = sm.alpha[hh];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) st[hh][nt][r] *= alpha;
-            }
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            Frag<bf16> xh[HPW], xl[HPW];
-#pragma unroll
-            for (int hh = 0; hh < HPW; ++hh) {
-                const bf16* xt = &sm.xs[hh * QS * XS];
-                const bf16x4 lo4 = tr_read(xt, 32 * ks + 4 * g4, 16 * w, XS, l16);
-                const bf16x4 hi4 = tr_read(xt, 32 * ks + 16 + 4 * g4, 16 * w, XS, l16);
-                const float* wv = &sm.ww[hh * QS + 32 * ks + 4 * g4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v0 = static_cast<float>(lo4[r]) * wv[r];
-                    const float v1 = static_cast<float>(hi4[r]) * wv[16 + r];
-                    const bf16 h0v = static_cast<bf16>(v0), h1v = static_cast<bf16>(v1);
-                    xh[hh].v[r] = h0v;
-                    xh[hh].v[4 + r] = h1v;
-                    xl[hh].v[r] = static_cast<bf16>(v0 - static_cast<float>(h0v));
-                    xl[hh].v[4 + r] = static_cast<bf16>(v1 - static_cast<float>(h1v));
-                }
-            }
-            Frag<bf16> a[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                a[nt].v = pack8(tr_read(sm.bs, 32 * ks + 4 * g4, 16 * nt, BS, l16),
-                                tr_read(sm.bs, 32 * ks + 16 + 4 * g4, 16 * nt, BS, l16));
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-                for (int hh = 0; hh < HPW; ++hh) {
-                    mma(st[hh][nt], a[nt], xh[hh]);
-                    mma(st[hh][nt], a[nt], xl[hh]);
-                }
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // the forward's decay arrays: for every 64-token sub-chunk and head,
 //   dtl[b,h,s,i] = dt[b, 64s+i, h],   lw[b,h,s,i] = log2(e) sum_{k<=i} dt[b,64s+k,h] A[h]
 // (dt after the front-end: the input step in dtl, the decay step in lw)
@@ -889,8 +761,8 @@ __global__ void __launch_bounds__(256) subchunk_decay_kernel(DtFront fe, const b
 
 // Reading the inputs backwards (XMap::rows > 0) is a variant of the kernels with sub-chunk-local decay
 // arrays (FWD); it needs whole 64-token tiles (L a multiple of 64) so that every tile's first input row
-// lies inside the batch row.  Taps need the reversed scan (the chunk walk has its own kernel) and a
-// spacing that is a multiple of the sub-chunk (every tap position starts a sub-chunk).
+// lies inside the batch row.  Taps need a spacing that is a multiple of the sub-chunk (every tap position
+// starts a sub-chunk).
 inline bool rev_ok(const Shape& s, const XMap& xm) { return xm.rows >= 0 && xm.rows <= s.L && s.L % QS == 0; }
 inline bool tap_ok(const Shape& s, const XMap& xm) { return xm.tapq > 0 && xm.tapq % QS == 0 && s.Q % QS == 0; }
 
@@ -923,37 +795,28 @@ hipError_t launch_scan_fast(const Shape& s, const bf16* x, const bf16* B, const 
     const size_t lds = sizeof(ScanLds<N, HPW>);
     const bool rev = xm.rows > 0, tap = xm.tap != nullptr;
     if (rev && (!FWD || !rev_ok(s, xm))) return hipErrorInvalidValue;
-    if (tap && (!rev || !tap_ok(s, xm))) return hipErrorInvalidValue;
+    if (tap && (!FWD || !tap_ok(s, xm))) return hipErrorInvalidValue;
+    if (tap && (xm.tap_tr != 0) == rev) return hipErrorInvalidValue;  // taps: reversed, or transposed forwards
+    if (xm.tap_tr && (!tap || xm.tap_tr > 2 || s.H % xm.tap_tr != 0)) return hipErrorInvalidValue;
     if (xm.start_tr && !rev) return hipErrorInvalidValue;
-    const void* fn = tap   ? (const void*)chunk_scan_fast_kernel<N, HPW, true, true, true>
+    const void* fn = tap   ? (rev ? (const void*)chunk_scan_fast_kernel<N, HPW, true, true, true>
+                                  : (const void*)chunk_scan_fast_kernel<N, HPW, true, false, true, true>)
                      : rev ? (const void*)chunk_scan_fast_kernel<N, HPW, true, true, false>
                            : (const void*)chunk_scan_fast_kernel<N, HPW, FWD>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    if (tap)
+    if (tap && rev)
         hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, true, true, true>), dim3(nitems), dim3(256), lds, st, x, B,
                            C, ds, start, D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
+    else if (tap)
+        hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, true, false, true, true>), dim3(nitems), dim3(256), lds, st,
+                           x, B, C, ds, start, D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
     else if (rev)
         hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, true, true, false>), dim3(nitems), dim3(256), lds, st, x, B,
                            C, ds, start, D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
     else
         hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, C, ds, start,
                            D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
-    return hipGetLastError();
-}
-
-template <int N, int HPW>
-hipError_t launch_walk_fast(const Shape& s, const bf16* x, const bf16* B, const DtSrc& ds, const float* start,
-                            const XMap& xm, hipStream_t st) {
-    const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
-    if (nitems == 0) return hipSuccess;
-    if (!xm.tap || !tap_ok(s, xm) || xm.rows != 0) return hipErrorInvalidValue;
-    const size_t lds = sizeof(WalkLds<N, HPW>);
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_walk_fast_kernel<N, HPW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_walk_fast_kernel<N, HPW>), dim3(nitems), dim3(256), lds, st, x, B, ds, start, s.L,
-                       (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
     return hipGetLastError();
 }
 
@@ -1081,20 +944,6 @@ hipError_t launch_chunk_scan_sub(const Shape& s, const void* x, const void* B, c
     if (s.N >= 256) return hipErrorInvalidValue;
     const fz::DtSrc ds{dtl, lw};
     return fz::scan_dispatch<true>(s, (const bf16*)x, (const bf16*)B, (const bf16*)C, ds, start, D, (bf16*)y, st, xm);
-}
-
-hipError_t launch_chunk_walk(const Shape& s, const void* x, const void* B, const float* dtl, const float* lw,
-                             const float* start, hipStream_t st, const XMap& xm) {
-    const fz::DtSrc ds{dtl, lw};
-    const bf16 *xb = (const bf16*)x, *bb = (const bf16*)B;
-    const bool pair = fast_hpw(s) == 2;
-    if (s.N == 128)
-        return pair ? fz::launch_walk_fast<128, 2>(s, xb, bb, ds, start, xm, st)
-                    : fz::launch_walk_fast<128, 1>(s, xb, bb, ds, start, xm, st);
-    if (s.N == 64)
-        return pair ? fz::launch_walk_fast<64, 2>(s, xb, bb, ds, start, xm, st)
-                    : fz::launch_walk_fast<64, 1>(s, xb, bb, ds, start, xm, st);
-    return hipErrorInvalidValue;
 }
 
 hipError_t launch_subchunk_decay_bwd(const Shape& s, const void* dt, const float* A, float* dtl, float* lw, int64_t Ls,

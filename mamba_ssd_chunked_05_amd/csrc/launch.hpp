@@ -54,10 +54,13 @@ hipError_t launch_step_multi(const Shape& s, const DtFront& fe, float* state, co
 // The chunk scan then writes its output in forward time too (`rows` rows per batch row, nothing for the
 // padding tokens), as y = s * (C.S + in-chunk term) + D x with s = rowscale[b, row, h] (an io-dtype
 // (b, rows, H) array, e.g. the step dt) or 1 when rowscale is NULL.
-// tap (chunk scan with rows > 0, and the chunk walk): the fp32 state the kernel carries is also stored
+// tap (chunk scan over sub-chunk-local decay arrays): the fp32 state the kernel carries is also stored
 // at every position that is a multiple of tapq (the state entering it), as (b, L / tapq, H, P, N), and
-// the state update then splits its scaled operand into hi + lo bf16 (fp32-level states).  start_tr: the
-// chunk-start states are those of a transposed scan, (b, nC, (N / 64) H, 64, P).
+// the state update then splits its scaled operand into hi + lo bf16 (fp32-level states).  tap_tr > 0:
+// the scan is a transposed one with tap_tr half-heads per head, and its taps go to the original heads'
+// layout (b, L / tapq, H / tap_tr, N, 64 tap_tr): kernel head h2's state row i and column j become element
+// (j, 64 (h2 % tap_tr) + i) of head h2 / tap_tr.  start_tr: the chunk-start states are those of a
+// transposed scan, (b, nC, (N / 64) H, 64, P).
 struct XMap {
     int hx, div, mul;
     int64_t rows;
@@ -65,6 +68,7 @@ struct XMap {
     float* tap;
     int tapq;
     int start_tr;
+    int tap_tr;
 };
 // The backward's chunk kernels over sub-chunk-local decay arrays (dtl, lw: (b, H, ceil(L / 64), 64), from
 // launch_subchunk_decay_bwd), with the reading options of XMap; the chunk state also writes each chunk's
@@ -74,9 +78,6 @@ hipError_t launch_chunk_state_sub(const Shape& s, const void* x, const void* B, 
 hipError_t launch_chunk_scan_sub(const Shape& s, const void* x, const void* B, const void* C, const float* dtl,
                                  const float* lw, const float* start, const float* D, void* y, hipStream_t st,
                                  const XMap* xm);
-// The states entering every xm.tapq-th position (xm.tap), walked from the chunk-start states.
-hipError_t launch_chunk_walk(const Shape& s, const void* x, const void* B, const float* dtl, const float* lw,
-                             const float* start, hipStream_t st, const XMap& xm);
 // Sub-chunk-local decay arrays for s.H kernel heads over s.L tokens from a bf16 dt of (b, Ls, H / hdiv):
 // kernel head h takes dt head h / hdiv and A[h / hdiv]; rev: token t takes the decay step of dt row
 // s.L - t (none where that row is past the end); unit: the input step is 1.
