@@ -78,13 +78,15 @@ struct BRows {
 struct TileBase {
     const bf16 *x, *b, *c;
     const float *dt, *cs;
-    int64_t rows;  // rows of the tile inside the inputs, from the resource's start
+    const bf16* rdt;  // raw dt (DtSrc::raw): the sub-chunk's first row, this workgroup's first head
+    int64_t rows;     // rows of the tile inside the inputs, from the resource's start
 };
 
 // hx: heads of the x rows; dt_head: distance between consecutive heads in the dt/cs arrays.
 // REV: the tile's rows run backwards from its last input row (the resource starts at the lowest one), so
 // tile row r sits 63 - r rows above the resource's start; the later pieces of a thread step downwards.
-template <int N, int HPW, bool REV = false>
+// RAW: dt_head is the row length of the raw dt (its heads), and a thread's dt element is token r, head hh.
+template <int N, int HPW, bool REV = false, bool RAW = false>
 __device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int hx, int G, int64_t dt_head, int tid) {
     constexpr int BS = Strides<N>::BS, CS = Strides<N>::CS;
     const int xr = tid >> 3, xc = (tid & 7) * 8;
@@ -95,7 +97,7 @@ __device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int hx, int G, 
     a.bl = br * BS + bc;
     a.cl = br * CS + bc;
     const int hh = tid >> 6, r = tid & 63;
-    a.dto = (uint32_t)((hh < HPW ? hh : 0) * dt_head + r);
+    a.dto = RAW ? (uint32_t)(r * dt_head + (hh < HPW ? hh : 0)) : (uint32_t)((hh < HPW ? hh : 0) * dt_head + r);
 }
 
 // The tiles of the sub-chunk starting at token tbase of batch row b (x heads xh0.. of hx per row,
@@ -103,7 +105,7 @@ __device__ __forceinline__ void chunk_addr(ChunkAddr<N, HPW>& a, int hx, int G, 
 // sub-chunk index.  REV: the inputs hold Lin rows per batch row in forward time, token t is input row
 // L - 1 - t, so the tile covers input rows L - 64 - tbase (its last token, the resource's start) up to
 // L - 1 - tbase, of which those below Lin exist (L a multiple of 64).
-template <bool WITH_C, bool REV = false>
+template <bool WITH_C, bool REV = false, bool RAW = false>
 __device__ __forceinline__ TileBase tile_base(const bf16* x, const bf16* B, const bf16* C, const DtSrc& ds,
                                               int64_t dt0, int64_t b, int64_t L, int hx, int G, int N, int xh0, int g,
                                               int64_t tbase, int sub, int64_t Lin = 0) {
@@ -113,21 +115,34 @@ __device__ __forceinline__ TileBase tile_base(const bf16* x, const bf16* B, cons
     t.b = B + (r0 * G + g) * (int64_t)N;
     t.c = WITH_C ? C + (r0 * G + g) * (int64_t)N : nullptr;
     t.rows = REV ? Lin - (L - QS - tbase) : L - tbase;
-    t.dt = ds.dt_t + dt0 + (int64_t)QS * sub;
-    t.cs = ds.cs + dt0 + (int64_t)QS * sub;
+    if constexpr (RAW) {  // dt0: the raw element of token 0 of this batch row and the workgroup's first head
+        t.rdt = ds.raw + dt0 + tbase * (int64_t)ds.H;
+        t.dt = t.cs = nullptr;
+    } else {
+        t.rdt = nullptr;
+        t.dt = ds.dt_t + dt0 + (int64_t)QS * sub;
+        t.cs = ds.cs + dt0 + (int64_t)QS * sub;
+    }
     return t;
 }
 
 // Load one sub-chunk into registers; rows past the inputs' end read as zero (t.rows from the resource's
 // start).  REV (offsets from chunk_addr<REV>): a thread's later pieces lie 32 or RPI rows lower.
-template <int N, int HPW, bool WITH_C, bool REV = false>
+// RAW: rg.dt is the raw step and rg.cs flags a token inside the sequence.
+template <int N, int HPW, bool WITH_C, bool REV = false, bool RAW = false>
 __device__ __forceinline__ void chunk_load(ChunkRegs<N, HPW, WITH_C>& rg, const ChunkAddr<N, HPW>& a,
                                            const TileBase& t, int hx, int G, int tid) {
     constexpr int RPI = BRows<N>::RPI;
     const uint32_t HP_ = (uint32_t)(hx * P), GN = (uint32_t)(G * N);
-    if (tid < 64 * HPW) {  // dt_t and cs cover every position of the chunk (zero-padded past L)
-        rg.dt = t.dt[a.dto];
-        rg.cs = t.cs[a.dto];
+    if (tid < 64 * HPW) {
+        if (RAW) {
+            const bool in = (tid & 63) < t.rows;
+            rg.dt = in ? to_f32(t.rdt[a.dto]) : 0.0f;
+            rg.cs = in ? 1.0f : 0.0f;
+        } else {  // dt_t and cs cover every position of the chunk (zero-padded past L)
+            rg.dt = t.dt[a.dto];
+            rg.cs = t.cs[a.dto];
+        }
     }
     const auto rx = tile_rsrc(t.x, HP_, t.rows, HPW * P);
     const auto rb = tile_rsrc(t.b, GN, t.rows, N);
@@ -154,10 +169,13 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<N, HPW, WITH_C>& rg, const 
 //   ec[0][i]  = 2^(l_i - l_(16 (i / 16)))      (<= 1: i at or after its block start)
 //   ec[it][j] = 2^(l_(16 it) - l_j) dt_j       (<= dt_j for j < 16 it, the only ones used)
 // so those tiles need no exponential; the diagonal tiles form 2^(l_i - l_j) directly.
-template <int N, int HPW, bool WITH_C, bool FWD>
+// RAW (with FWD): rg holds the raw step (chunk_load<RAW>); the front-end fe with A[h] = ah gives the input
+// and decay steps, and a wavefront scan of the decay steps the sub-chunk's cumulative decay.
+template <int N, int HPW, bool WITH_C, bool FWD, bool RAW = false>
 __device__ __forceinline__ void chunk_store(bf16* xs, bf16* bsm, bf16* csm, float* lw, float* dtw, float* ww,
                                             float* ec, float* alpha, const ChunkRegs<N, HPW, WITH_C>& rg,
-                                            const ChunkAddr<N, HPW>& a, float& cs_prev, float& tot, int tid) {
+                                            const ChunkAddr<N, HPW>& a, float& cs_prev, float& tot, int tid,
+                                            const DtFront* fe = nullptr, int h = 0, float ah = 0.0f) {
     constexpr int RPI = BRows<N>::RPI, BS = Strides<N>::BS, CS = Strides<N>::CS;
 #pragma unroll
     for (int k = 0; k < 2 * HPW; ++k)
@@ -169,9 +187,14 @@ __device__ __forceinline__ void chunk_store(bf16* xs, bf16* bsm, bf16* csm, floa
     }
     if (tid < 64 * HPW) {
         const int hh = tid >> 6, lane = tid & 63;
-        const float d = rg.dt;
+        float d = rg.dt;
         float incl;  // cumulative log2 decay inside the sub-chunk
-        if (FWD) {
+        if (RAW) {
+            float dec = 0.0f, inp = 0.0f;  // zero past the sequence end
+            if (rg.cs != 0.0f) dt_front(*fe, h, ah, rg.dt, dec, inp);
+            d = inp;
+            incl = wave_incl_scan(dec * ah) * kLog2e;
+        } else if (FWD) {
             incl = rg.cs;
         } else {
             incl = rg.cs - cs_prev;
@@ -213,8 +236,9 @@ struct ScanLds {
 // FWD: sub-chunk-local decay arrays (subchunk_decay_kernel), as the forward reads them.
 // REV (with FWD): the inputs are walked backwards and the output written forwards (XMap::rows); TAP
 // (with FWD): the carried state is stored every XMap::tapq positions, with a hi/lo state update; TTR
-// (with TAP): it is a transposed scan's state, stored back in its heads' layout (XMap::tap_tr).
-template <int N, int HPW, bool FWD, bool REV = false, bool TAP = false, bool TTR = false>
+// (with TAP): it is a transposed scan's state, stored back in its heads' layout (XMap::tap_tr).  RAW (with
+// FWD, forwards, no taps): the decays come from the raw dt (DtSrc::raw), formed per sub-chunk in registers.
+template <int N, int HPW, bool FWD, bool REV = false, bool TAP = false, bool TTR = false, bool RAW = false>
 __global__ void __launch_bounds__(256, 2)
 chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, const bf16* __restrict__ C,
                        DtSrc ds, const float* __restrict__ start, const float* __restrict__ D, bf16* __restrict__ y, int64_t L,
@@ -233,6 +257,7 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     const int g = h0 / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, in a scalar register
+    static_assert(!RAW || (FWD && !REV && !TAP), "raw decays: the forward's scan only");
     float Dh[HPW];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) Dh[hh] = D ? D[h0 + hh] : 0.0f;
@@ -272,13 +297,17 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
     }
 
     const int64_t nsubT = (L + QS - 1) / QS;
-    const int64_t dt_head = FWD ? nsubT * QS : nC * Q;  // dt/cs distance between heads
-    const int64_t dt0 = FWD ? ((b * H + h0) * nsubT + c * (Q / QS)) * QS : ((b * H + h0) * nC + c) * Q;
+    // dt/cs distance between heads (RAW: the raw dt's row length) and this chunk's first element
+    const int64_t dt_head = RAW ? (int64_t)ds.H : FWD ? nsubT * QS : nC * Q;
+    const int64_t dt0 = RAW   ? b * L * ds.H + h0
+                        : FWD ? ((b * H + h0) * nsubT + c * (Q / QS)) * QS
+                              : ((b * H + h0) * nC + c) * Q;
+    const float ah = RAW && tid < 64 * HPW ? ds.A[h0 + (tid >> 6)] : 0.0f;  // A of this thread's head
     const int xh0 = h0 / xm.div * xm.mul;  // the x heads of this head pair
     ChunkAddr<N, HPW> ad;
-    chunk_addr<N, HPW, REV>(ad, xm.hx, G, dt_head, tid);
+    chunk_addr<N, HPW, REV, RAW>(ad, xm.hx, G, dt_head, tid);
     ChunkRegs<N, HPW, true> rg;
-    chunk_load<N, HPW, true, REV>(rg, ad, tile_base<true, REV>(x, B, C, ds, dt0, b, L, xm.hx, G, N, xh0, g, t0, 0, xm.rows),
+    chunk_load<N, HPW, true, REV, RAW>(rg, ad, tile_base<true, REV, RAW>(x, B, C, ds, dt0, b, L, xm.hx, G, N, xh0, g, t0, 0, xm.rows),
                                   xm.hx, G, tid);
     // reversed walk: the output row scale of token (tid & 63) of head (tid >> 6), at input row L - 1 - t
     const bf16* rsrc = REV ? static_cast<const bf16*>(xm.rowscale) : nullptr;
@@ -317,14 +346,14 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
             }
         }
         __syncthreads();  // the previous sub-chunk's readers are done with the LDS tiles
-        chunk_store<N, HPW, true, FWD>(sm.xs, sm.bs, sm.cs, sm.lw, sm.dtw, sm.ww, sm.ec, sm.alpha, rg, ad, cs_prev,
-                                       tot, tid);
+        chunk_store<N, HPW, true, FWD, RAW>(sm.xs, sm.bs, sm.cs, sm.lw, sm.dtw, sm.ww, sm.ec, sm.alpha, rg, ad,
+                                            cs_prev, tot, tid, &ds.fe, h0 + (tid >> 6), ah);
         if (REV && rsrc && tid < 64 * HPW) sm.rs[tid] = rg.rs;
         __syncthreads();
         if (sc + 1 < nsub) {
             const int64_t t1 = tbase + QS;
-            chunk_load<N, HPW, true, REV>(
-                rg, ad, tile_base<true, REV>(x, B, C, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc + 1, xm.rows), xm.hx,
+            chunk_load<N, HPW, true, REV, RAW>(
+                rg, ad, tile_base<true, REV, RAW>(x, B, C, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc + 1, xm.rows), xm.hx,
                 G, tid);
             load_rs(t1);
         }
@@ -544,10 +573,11 @@ struct AggLds {
 // walked from the last, `after` holds the log2 decay from this sub-chunk's end to the chunk's end and
 // tot accumulates the chunk's total.  Otherwise cs is cumulative over the chunk and cs_end is its
 // value at the chunk's last position (flat past the sequence end, where dt is zero).
-template <int N, int HPW, bool FWD>
+// RAW (with FWD): the steps and the sub-chunk's cumulative decay from the raw dt, as in chunk_store.
+template <int N, int HPW, bool FWD, bool RAW = false>
 __device__ __forceinline__ void state_store(bf16* xs, bf16* bsm, float* ww, const ChunkRegs<N, HPW, false>& rg,
                                             const ChunkAddr<N, HPW>& a, float& after, float cs_end, float& tot,
-                                            int tid) {
+                                            int tid, const DtFront* fe = nullptr, int h = 0, float ah = 0.0f) {
     constexpr int RPI = BRows<N>::RPI, BS = Strides<N>::BS;
 #pragma unroll
     for (int k = 0; k < 2 * HPW; ++k)
@@ -555,16 +585,23 @@ __device__ __forceinline__ void state_store(bf16* xs, bf16* bsm, float* ww, cons
 #pragma unroll
     for (int k = 0; k < N / 32; ++k) *reinterpret_cast<uint4*>(bsm + a.bl + k * RPI * BS) = rg.b[k];
     if (tid < 64 * HPW) {
+        float cs = rg.cs, d = rg.dt;
+        if (RAW) {
+            float dec = 0.0f, inp = 0.0f;  // zero past the sequence end
+            if (rg.cs != 0.0f) dt_front(*fe, h, ah, rg.dt, dec, inp);
+            d = inp;
+            cs = wave_incl_scan(dec * ah) * kLog2e;
+        }
         float e;  // log2 decay from this token to the chunk's end
         if (FWD) {
-            const float last = __shfl(rg.cs, 63, 64);
-            e = after + (last - rg.cs);
+            const float last = __shfl(cs, 63, 64);
+            e = after + (last - cs);
             after += last;
             tot += last;
         } else {
-            e = cs_end - rg.cs;
+            e = cs_end - cs;
         }
-        ww[(tid >> 6) * QS + (tid & 63)] = fast_exp2(e) * rg.dt;
+        ww[(tid >> 6) * QS + (tid & 63)] = fast_exp2(e) * d;
     }
 }
 
@@ -574,8 +611,9 @@ __device__ __forceinline__ void state_store(bf16* xs, bf16* bsm, float* ww, cons
 // the last to the first, which makes each sub-chunk's distance to the chunk's end known when its
 // weights are formed.
 // FWD: the forward's variant -- reads sub-chunk-local decay arrays and also writes each chunk's total
-// log2 decay to totals (b, H, nC).  REV: the inputs are walked backwards (XMap::rows).
-template <int N, int HPW, bool FWD, bool REV = false>
+// log2 decay to totals (b, H, nC).  REV: the inputs are walked backwards (XMap::rows).  RAW (with FWD,
+// forwards): the decays come from the raw dt (DtSrc::raw), formed per sub-chunk in registers.
+template <int N, int HPW, bool FWD, bool REV = false, bool RAW = false>
 __global__ void __launch_bounds__(256, 2)
 chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, DtSrc ds, float* __restrict__ states,
                         float* __restrict__ totals, int64_t L, int H, int G, int Q, int64_t nC, uint32_t nitems,
@@ -606,29 +644,35 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
     }
 
     const int64_t nsubT = (L + QS - 1) / QS;
-    const int64_t dt_head = FWD ? nsubT * QS : nC * Q;  // dt/cs distance between heads
-    const int64_t dt0 = FWD ? ((b * H + h0) * nsubT + c * (Q / QS)) * QS : ((b * H + h0) * nC + c) * Q;
+    static_assert(!RAW || (FWD && !REV), "raw decays: the forward's chunk state only");
+    // dt/cs distance between heads (RAW: the raw dt's row length) and this chunk's first element
+    const int64_t dt_head = RAW ? (int64_t)ds.H : FWD ? nsubT * QS : nC * Q;
+    const int64_t dt0 = RAW   ? b * L * ds.H + h0
+                        : FWD ? ((b * H + h0) * nsubT + c * (Q / QS)) * QS
+                              : ((b * H + h0) * nC + c) * Q;
+    const float ah = RAW && tid < 64 * HPW ? ds.A[h0 + (tid >> 6)] : 0.0f;  // A of this thread's head
     float after = 0.0f, tot = 0.0f, cs_end = 0.0f;
     if (!FWD && tid < 64 * HPW) cs_end = ds.cs[dt0 + (int64_t)(tid >> 6) * dt_head + (Q - 1)];
     const int xh0 = h0 / xm.div * xm.mul;  // the x heads of this head pair
     ChunkAddr<N, HPW> ad;
-    chunk_addr<N, HPW, REV>(ad, xm.hx, G, dt_head, tid);
+    chunk_addr<N, HPW, REV, RAW>(ad, xm.hx, G, dt_head, tid);
     ChunkRegs<N, HPW, false> rg;
     {
         const int64_t tl = t0 + (int64_t)(nsub - 1) * QS;
-        chunk_load<N, HPW, false, REV>(
-            rg, ad, tile_base<false, REV>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, tl, nsub - 1, xm.rows),
+        chunk_load<N, HPW, false, REV, RAW>(
+            rg, ad, tile_base<false, REV, RAW>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, tl, nsub - 1, xm.rows),
             xm.hx, G, tid);
     }
 
     for (int sc = nsub - 1; sc >= 0; --sc) {
         __syncthreads();
-        state_store<N, HPW, FWD>(sm.xs, sm.bs, sm.ww, rg, ad, after, cs_end, tot, tid);
+        state_store<N, HPW, FWD, RAW>(sm.xs, sm.bs, sm.ww, rg, ad, after, cs_end, tot, tid, &ds.fe, h0 + (tid >> 6),
+                                      ah);
         __syncthreads();
         if (sc > 0) {
             const int64_t t1 = t0 + (int64_t)(sc - 1) * QS;
-            chunk_load<N, HPW, false, REV>(
-                rg, ad, tile_base<false, REV>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc - 1, xm.rows),
+            chunk_load<N, HPW, false, REV, RAW>(
+                rg, ad, tile_base<false, REV, RAW>(x, B, nullptr, ds, dt0, b, L, xm.hx, G, N, xh0, g, t1, sc - 1, xm.rows),
                 xm.hx, G, tid);
         }
 
@@ -772,15 +816,20 @@ hipError_t launch_state_fast(const Shape& s, const bf16* x, const bf16* B, const
     const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
     if (nitems == 0) return hipSuccess;
     const size_t lds = sizeof(AggLds<N, HPW>);
-    const bool rev = xm.rows > 0;
+    const bool rev = xm.rows > 0, raw = ds.raw != nullptr;
     if (rev && (!FWD || !rev_ok(s, xm))) return hipErrorInvalidValue;
-    const void* fn = rev ? (const void*)chunk_state_fast_kernel<N, HPW, true, true>
-                         : (const void*)chunk_state_fast_kernel<N, HPW, FWD>;
+    if (raw && (!FWD || rev)) return hipErrorInvalidValue;
+    const void* fn = rev   ? (const void*)chunk_state_fast_kernel<N, HPW, true, true>
+                     : raw ? (const void*)chunk_state_fast_kernel<N, HPW, true, false, true>
+                           : (const void*)chunk_state_fast_kernel<N, HPW, FWD>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     if (rev)
         hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW, true, true>), dim3(nitems), dim3(256), lds, st, x, B, ds,
                            states, totals, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
+    else if (raw)
+        hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW, true, false, true>), dim3(nitems), dim3(256), lds, st, x,
+                           B, ds, states, totals, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
     else
         hipLaunchKernelGGL((chunk_state_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, ds, states,
                            totals, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
@@ -793,8 +842,9 @@ hipError_t launch_scan_fast(const Shape& s, const bf16* x, const bf16* B, const 
     const uint32_t nitems = (uint32_t)(s.b * s.nC * (s.H / HPW));
     if (nitems == 0) return hipSuccess;
     const size_t lds = sizeof(ScanLds<N, HPW>);
-    const bool rev = xm.rows > 0, tap = xm.tap != nullptr;
+    const bool rev = xm.rows > 0, tap = xm.tap != nullptr, raw = ds.raw != nullptr;
     if (rev && (!FWD || !rev_ok(s, xm))) return hipErrorInvalidValue;
+    if (raw && (!FWD || rev || tap || xm.start_tr)) return hipErrorInvalidValue;
     if (tap && (!FWD || !tap_ok(s, xm))) return hipErrorInvalidValue;
     if (tap && (xm.tap_tr != 0) == rev) return hipErrorInvalidValue;  // taps: reversed, or transposed forwards
     if (xm.tap_tr && (!tap || xm.tap_tr > 2 || s.H % xm.tap_tr != 0)) return hipErrorInvalidValue;
@@ -802,6 +852,7 @@ hipError_t launch_scan_fast(const Shape& s, const bf16* x, const bf16* B, const 
     const void* fn = tap   ? (rev ? (const void*)chunk_scan_fast_kernel<N, HPW, true, true, true>
                                   : (const void*)chunk_scan_fast_kernel<N, HPW, true, false, true, true>)
                      : rev ? (const void*)chunk_scan_fast_kernel<N, HPW, true, true, false>
+                     : raw ? (const void*)chunk_scan_fast_kernel<N, HPW, true, false, false, false, true>
                            : (const void*)chunk_scan_fast_kernel<N, HPW, FWD>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -814,6 +865,9 @@ hipError_t launch_scan_fast(const Shape& s, const bf16* x, const bf16* B, const 
     else if (rev)
         hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, true, true, false>), dim3(nitems), dim3(256), lds, st, x, B,
                            C, ds, start, D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
+    else if (raw)
+        hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, true, false, false, false, true>), dim3(nitems), dim3(256),
+                           lds, st, x, B, C, ds, start, D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
     else
         hipLaunchKernelGGL((chunk_scan_fast_kernel<N, HPW, FWD>), dim3(nitems), dim3(256), lds, st, x, B, C, ds, start,
                            D, y, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems, xm);
@@ -957,10 +1011,18 @@ hipError_t launch_subchunk_decay_bwd(const Shape& s, const void* dt, const float
     return hipGetLastError();
 }
 
+// The chunk kernels form the decays from the raw dt themselves at dstate <= 128 when the forward is short
+// (at most 2^20 token-heads): that saves the decay pass's launch, which dominates there (2.7B heads at
+// 1K and 4K tokens: 40.6 and 73.4 against 48.5 and 81.5 us; the 130M shape: 56.9 against 59.9 us), while
+// on long inputs the pass is cheaper than the in-kernel work (2.7B heads at 64K tokens: 0.763 against
+// 0.753 ms).
+static bool forward_raw_decay(const Shape& s) { return s.N <= 128 && s.b * s.L * s.H <= ((int64_t)1 << 20); }
+
 FastFwdLayout fast_forward_layout(const Shape& s) {
     auto a256 = [](size_t v) { return (v + 255) / 256 * 256; };
     FastFwdLayout f;
-    const size_t pos = (size_t)(s.b * s.H * ((s.L + fz::QS - 1) / fz::QS) * fz::QS) * 4;
+    // the decay pass's arrays unless the chunk kernels form the decays themselves
+    const size_t pos = forward_raw_decay(s) ? 0 : (size_t)(s.b * s.H * ((s.L + fz::QS - 1) / fz::QS) * fz::QS) * 4;
     f.dtl = 0;
     f.lw = a256(pos);
     f.states = f.lw + a256(pos);
@@ -980,12 +1042,17 @@ hipError_t launch_forward_fast(const Shape& s, const DtFront& fe, const void* x,
     float* states = reinterpret_cast<float*>(ws + f.states);
     float* totals = reinterpret_cast<float*>(ws + f.totals);
     const bf16 *xb = (const bf16*)x, *bb = (const bf16*)B, *cb = (const bf16*)C;
-    const uint32_t ndec = (uint32_t)(s.b * ((s.L + fz::QS - 1) / fz::QS));
-    hipLaunchKernelGGL(fz::subchunk_decay_kernel<false>, dim3(ndec), dim3(256), 0, st, fe, (const bf16*)dt, A, dtl,
-                       lw, s.L, (int)s.H, ndec, fz::DecaySrc{s.L, 1, 0, 0});
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const fz::DtSrc ds{dtl, lw};
+    fz::DtSrc ds{dtl, lw};
+    hipError_t e;
+    if (forward_raw_decay(s)) {
+        ds = fz::DtSrc{nullptr, nullptr, (const bf16*)dt, A, fe, (int)s.H};
+    } else {
+        const uint32_t ndec = (uint32_t)(s.b * ((s.L + fz::QS - 1) / fz::QS));
+        hipLaunchKernelGGL(fz::subchunk_decay_kernel<false>, dim3(ndec), dim3(256), 0, st, fe, (const bf16*)dt, A,
+                           dtl, lw, s.L, (int)s.H, ndec, fz::DecaySrc{s.L, 1, 0, 0});
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     e = fz::state_dispatch<true>(s, xb, bb, ds, states, totals, st);
     if (e != hipSuccess) return e;
     // the pass reads one total per chunk: a chunk of "length 1" in its indexing

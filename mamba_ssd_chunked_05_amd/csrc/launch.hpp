@@ -93,11 +93,11 @@ hipError_t launch_chunk_scan_fast(const Shape& s, const void* x, const void* B, 
                                   const float* cs, const float* start, const float* D, void* y, hipStream_t st,
                                   const XMap* xm = nullptr);
 
-// The forward on the fast path: the decay arrays restart at every 64-token
-// sub-chunk (one coalesced pass over dt), the chunk states also yield each
-// chunk's total decay, the state pass runs over those totals, then the output
-// kernel.  Workspace byte offsets: dt and decay (b, H, ceil(L/64), 64), chunk
-// states (b, nC, H, P, N), chunk totals (b, H, nC), all fp32.
+// The forward on the fast path: the decays restart at every 64-token sub-chunk (one coalesced pass over
+// dt writes them, or, for short inputs at dstate <= 128, the chunk kernels form them from dt themselves),
+// the chunk states also yield each chunk's total decay, the state pass runs over those totals, then the
+// output kernel.  Workspace byte offsets: dt and decay (b, H, ceil(L/64), 64; empty when the kernels form
+// them), chunk states (b, nC, H, P, N), chunk totals (b, H, nC), all fp32.
 struct FastFwdLayout {
     size_t dtl, lw, states, totals, total;
 };

@@ -3,6 +3,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace ssd {
 namespace fz {
@@ -60,10 +61,16 @@ __device__ __forceinline__ uint4 ldbuf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 
 // dt (fp32) and the cumulative log2 decay: over the chunk for the staged calls,
-// restarting at every 64-token sub-chunk in the forward.
+// restarting at every 64-token sub-chunk in the forward.  raw (the forward at dstate <= 128): no
+// arrays -- the kernels read the step dt (b, L, H) bf16 themselves (rows of H elements), apply the
+// front-end fe and A, and form each sub-chunk's cumulative decay in registers.
 struct DtSrc {
     const float* dt_t;
     const float* cs;
+    const bf16* raw = nullptr;
+    const float* A = nullptr;
+    DtFront fe{nullptr, 0, 0, 0, 0.0f, 0.0f};
+    int H = 0;
 };
 
 }  // namespace fz
