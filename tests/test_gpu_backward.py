@@ -107,6 +107,40 @@ def test_backward_local_stress(gpu_ssd, mode):
     _check(ref, got, "bf16")
 
 
+def test_backward_in_a_graph(gpu_ssd):
+    """A backward call (the bf16 chunk-kernel path: some twenty launches on the caller's stream) captured in one
+    graph replays to the oracle's gradients, replay after replay, with eager work between replays.  (Its LDS
+    atomics add in no fixed order, so replays are compared with the oracle, not bit by bit.)"""
+    case = (1, 517, 4, 64, 128, 1, "bf16", 0, True)
+    b, L, H, P, N, G, dtype, chunk, _ = case
+    fi = make_forward_inputs(b, L, H, P, N, G, dtype, 311, h0_std=0.4)
+    rng = np.random.default_rng(318)
+    from synth import round_to
+
+    dy = round_to(rng.standard_normal(fi.x.shape), dtype)
+    dfinal = round_to(rng.standard_normal((b, H, P, N)), "f32")
+    ref = oracle.backward(fi.x, fi.dt, fi.A, fi.B, fi.C, fi.D, fi.h0, dy, dfinal)
+    args = (dev(fi.x, dtype), dev(fi.dt, dtype), dev(fi.A), dev(fi.B, dtype), dev(fi.C, dtype), dev(fi.D),
+            dev(fi.h0), dev(dy, dtype), dev(dfinal))
+    nbytes = ssd_mod.backward_workspace_bytes(args[0], args[3])
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=args[0].device)
+    eager = ssd_mod.backward(*args, workspace=ws)
+    torch.cuda.synchronize()
+    _check(ref, {k: (None if v is None else host(v)) for k, v in eager.items()}, "bf16")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = ssd_mod.backward(*args, workspace=ws)
+    for rep in range(3):
+        for v in out.values():
+            if v is not None:
+                v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _check(ref, {k: (None if v is None else host(v)) for k, v in out.items()}, "bf16")
+        _ = (eager["dx"].float() * 2).sum().item()  # eager work between replays
+
+
 def test_backward_without_D(gpu_ssd):
     ref, got = _grads(302, (2, 200, 4, 16, 32, 2, "f32", 64, True), with_D=False)
     assert got["dD"] is None
