@@ -649,7 +649,7 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     const int H = (int)s.H, P = (int)s.P, N = (int)s.N, G = (int)s.G;
     const int nh = N / 64, H2 = nh * H, hpg = H / G;
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-    float *dt_t = F(f.dt_t), *cs = F(f.cs), *states = F(f.states), *states_b = F(f.states_b), *R = F(f.R);
+    float *states = F(f.states), *states_b = F(f.states_b), *R = F(f.R);
     float *G0T = F(f.G0), *dfT = F(f.dfT), *h0T = F(f.h0T), *finT = F(f.finT), *q = F(f.q), *dxy = F(f.dxy);
     float *totals = F(f.totals), *stT = F(f.stT);
     T *v = reinterpret_cast<T*>(ws + f.v_r), *w = reinterpret_cast<T*>(ws + f.w);
@@ -730,9 +730,8 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     BWD_CHECK(launch_chunk_state_sub(sh, B, x, dtl(fh), lwp(fh, H2, nsf, b), stT, totals, st, &xm));
     BWD_CHECK(launch_state_passing(s1, stT, totals, h0 ? h0T : nullptr, finT, st));
     BWD_CHECK(launch_chunk_scan_sub(sh, B, x, dy, dtl(fh), lwp(fh, H2, nsf, b), stT, nullptr, w, st, &xmt));
-    // the decay gradient, chunk by chunk at Q, from its chunk cumsum arrays and the stored states
-    BWD_CHECK(launch_chunk_cumsum(s, DtFront{nullptr, 0, 0, 0, 0.0f, 0.0f}, dt, A, dt_t, cs, st));
-    BWD_CHECK(launch_decay_grad(s, x, dy, B, C, cs, dt_t, states, states_b, F(f.cbt), R, dxy, st));
+    // the decay gradient, chunk by chunk at Q, from the steps and the stored states
+    BWD_CHECK(launch_decay_grad(s, x, dy, B, C, dt, A, states, states_b, F(f.cbt), R, dxy, st));
 
     const size_t lq = (size_t)32 * G * N * 4;  // the quad combine's LDS slices
     if (P == 64 && (N == 64 || N == 128) && H % 4 == 0 && lq <= 64 * 1024) {
@@ -916,9 +915,9 @@ BackwardLayout backward_layout(const Shape& s) {
         return at;
     };
     if (f.local) {
-        // chunk cumsum arrays and the stored states at the backward's chunk Q, the scans' bf16 outputs v and
-        // w (forward time), the transposed final states, per-token q, dy.x and R, per-tile partial sums
-        f.dt_t = take(CS), f.cs = take(CS), f.states = take(ST), f.states_b = take(ST);
+        // the stored states at the backward's chunk Q, the scans' bf16 outputs v and w (forward time), the
+        // transposed final states, per-token q, dy.x and R, per-tile partial sums
+        f.states = take(ST), f.states_b = take(ST);
         f.v_r = take(BLHN / 2), f.w = take(BLHN / 2);
         f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS);
         f.q = take(BLH), f.dxy = take(BLH), f.R = take(BLH);

@@ -166,8 +166,10 @@ __device__ __forceinline__ void state_term(const bf16* A, const bf16* Dm, float*
     }
 }
 
-// R and dxy (dy_t . x_t, for dD) (b, H, L) fp32.  cs / dtv: the forward chunk cumsum arrays (b, H, nC, Q)
-// (log2 units; dt, zero past L); cbt: cb_tiles_kernel's C . B tiles; S0: forward chunk-start states
+// R and dxy (dy_t . x_t, for dD) (b, H, L) fp32.  dt (b, L, H) bf16 and A give the chunk's decays: dt of
+// each token (zero past L) and the in-chunk cumulative log2 decay, from a wavefront scan of dt A per 64
+// tokens (at chunk 128 the second wavefront adds the first's total once both are in LDS); cbt:
+// cb_tiles_kernel's C . B tiles; S0: forward chunk-start states
 // (b, nC, H, P, N); Gst: the reversed adjoint scan's chunk-start states (b, nC, H, P, N) in reversed chunk
 // order, so forward chunk c reads reversed chunk nC - 1 - c: the adjoint G_{c1+1} of the token after the
 // chunk (dfinal for the last chunk), which enters decayed by that token's factor 2^(cs of the next chunk's
@@ -181,8 +183,8 @@ __device__ __forceinline__ void state_term(const bf16* A, const bf16* Dm, float*
 template <int N>
 __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict__ x, const bf16* __restrict__ dy,
                                                          const bf16* __restrict__ B, const bf16* __restrict__ C,
-                                                         const float* __restrict__ cs,
-                                                         const float* __restrict__ dtv,
+                                                         const bf16* __restrict__ dt,
+                                                         const float* __restrict__ A,
                                                          const float* __restrict__ cbt,
                                                          const float* __restrict__ S0,
                                                          const float* __restrict__ Gst, float* __restrict__ R,
@@ -233,10 +235,11 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
         ga[ks][0] = *reinterpret_cast<const float4*>(Gc + 32 * ks);
         ga[ks][1] = *reinterpret_cast<const float4*>(Gc + 32 * ks + 4);
     }
-    const int64_t base = ((b * H + h) * nC + c) * Q;
-    if (tid < Q) {
-        sm.lw[tid] = cs[base + tid];
-        sm.dtw[tid] = dtv[base + tid];
+    const float ah = A[h];
+    if (tid < Q) {  // whole wavefronts (Q is 64 or 128)
+        const float dv = c0 + tid < L ? static_cast<float>(dt[(b * L + c0 + tid) * H + h]) : 0.0f;
+        sm.lw[tid] = wave_incl_scan(dv * ah) * kLog2e;  // the second wavefront's part still lacks the first's total
+        sm.dtw[tid] = dv;
         sm.rowsum[tid] = 0.0f;
         sm.colsum[tid] = 0.0f;
         sm.s2[tid] = 0.0f;
@@ -274,6 +277,7 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
         split8(ga[ks][0], ga[ks][1], gh[ks], gl[ks]);
     }
     __syncthreads();
+    if (w == 1 && tid < Q) sm.lw[tid] += sm.lw[63];  // read again only after the barriers before T4
 
     // ---- dy_t . x_t per token (for dD): four threads per token, 16 columns each -------------------
     if (tid < 4 * Q) {
@@ -369,7 +373,7 @@ __global__ void __launch_bounds__(512) decay_grad_kernel(const bf16* __restrict_
     if (w == 0) {
         const float lend = sm.lw[Q - 1];
         // the adjoint enters decayed by the next token's factor (none after the sequence's end)
-        const float gam = c + 1 < nC ? fast_exp2(cs[((b * H + h) * nC + c + 1) * Q]) : 1.0f;
+        const float gam = c + 1 < nC ? fast_exp2(static_cast<float>(dt[(b * L + c0 + Q) * H + h]) * ah * kLog2e) : 1.0f;
         const float T1 = fast_exp2(lend) * gam * (sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]);
         float a2[2], a3[2], a4[2];
 #pragma unroll
@@ -408,21 +412,22 @@ size_t decay_grad_tile_bytes(const Shape& s) {
 }
 
 hipError_t launch_decay_grad(const Shape& s, const void* x, const void* dy, const void* B, const void* C,
-                             const float* cs, const float* dtv, const float* S0, const float* Gst, float* cbt,
-                             float* R, float* dxy, hipStream_t st) {
+                             const void* dt, const float* A, const float* S0, const float* Gst, float* cbt, float* R,
+                             float* dxy, hipStream_t st) {
     const uint32_t nitems = (uint32_t)(s.b * s.nC * s.H), ncb = (uint32_t)(s.b * s.nC * s.G);
     if (nitems == 0) return hipSuccess;
-    const bf16 *xb = (const bf16*)x, *yb = (const bf16*)dy, *bb = (const bf16*)B, *cb = (const bf16*)C;
+    const bf16 *xb = (const bf16*)x, *yb = (const bf16*)dy, *bb = (const bf16*)B, *cb = (const bf16*)C,
+               *dtb = (const bf16*)dt;
     if (s.N == 128) {
         hipLaunchKernelGGL(dg::cb_tiles_kernel<128>, dim3(ncb), dim3(256), 0, st, bb, cb, cbt, s.L, (int)s.G, (int)s.Q,
                            s.nC, ncb);
-        hipLaunchKernelGGL(dg::decay_grad_kernel<128>, dim3(nitems), dim3(512), 0, st, xb, yb, bb, cb, cs, dtv, cbt, S0,
-                           Gst, R, dxy, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+        hipLaunchKernelGGL(dg::decay_grad_kernel<128>, dim3(nitems), dim3(512), 0, st, xb, yb, bb, cb, dtb, A, cbt,
+                           S0, Gst, R, dxy, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
     } else {
         hipLaunchKernelGGL(dg::cb_tiles_kernel<64>, dim3(ncb), dim3(256), 0, st, bb, cb, cbt, s.L, (int)s.G, (int)s.Q,
                            s.nC, ncb);
-        hipLaunchKernelGGL(dg::decay_grad_kernel<64>, dim3(nitems), dim3(512), 0, st, xb, yb, bb, cb, cs, dtv, cbt, S0,
-                           Gst, R, dxy, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
+        hipLaunchKernelGGL(dg::decay_grad_kernel<64>, dim3(nitems), dim3(512), 0, st, xb, yb, bb, cb, dtb, A, cbt,
+                           S0, Gst, R, dxy, s.L, (int)s.H, (int)s.G, (int)s.Q, s.nC, nitems);
     }
     return hipGetLastError();
 }

@@ -136,14 +136,14 @@ struct BackwardLayout {
 // The chunk-local decay gradient (decay_grad.hip): bf16 io, headdim 64, dstate 64 or 128, chunk 64 or 128
 // (a multiple of 64 for the fast chunk kernels that supply its states, at most 128 for its tiles).
 bool decay_grad_supported(const Shape& s);
-// R (b, H, L): R_k = a_k <G_k, S_{k-1}> from the forward chunk cumsum arrays (cs, dt), the forward
-// chunk-start states S0 (b, nC, H, P, N) and the reversed adjoint scan's chunk-start states Gst (same
-// layout, reversed chunk order); dxy (b, H, L) = dy_t . x_t.  cbt: scratch of decay_grad_tile_bytes(s)
-// bytes for the chunks' C . B tiles (shared by the heads of a group).
+// R (b, H, L): R_k = a_k <G_k, S_{k-1}> from the step dt (b, L, H) bf16 and A (the chunks' decays are
+// formed in the kernel), the forward chunk-start states S0 (b, nC, H, P, N) and the reversed adjoint
+// scan's chunk-start states Gst (same layout, reversed chunk order); dxy (b, H, L) = dy_t . x_t.  cbt:
+// scratch of decay_grad_tile_bytes(s) bytes for the chunks' C . B tiles (shared by the heads of a group).
 size_t decay_grad_tile_bytes(const Shape& s);
 hipError_t launch_decay_grad(const Shape& s, const void* x, const void* dy, const void* B, const void* C,
-                             const float* cs, const float* dtv, const float* S0, const float* Gst, float* cbt,
-                             float* R, float* dxy, hipStream_t st);
+                             const void* dt, const float* A, const float* S0, const float* Gst, float* cbt, float* R,
+                             float* dxy, hipStream_t st);
 BackwardLayout backward_layout(const Shape& s);
 hipError_t launch_backward(const Shape& s, const void* x, const void* dt, const float* A, const void* B,
                            const void* C, const float* D, const float* h0, const void* dy, const float* dfinal,
