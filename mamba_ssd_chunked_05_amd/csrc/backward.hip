@@ -681,16 +681,14 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     hipLaunchKernelGGL(transpose_kernel, grid1(b * H * PN), dim3(256), 0, st, h0, h0T, P, N, b * H * PN);
     BWD_CHECK(hipGetLastError());
 
-    Shape sk = s;  // decay-array shapes: (b, tokens, kernel heads)
-    sk.L = Lr;
-    BWD_CHECK(launch_subchunk_decay_bwd(sk, dt, A, dtl(rl), lwp(rl, H, nsr, b), L, 1, true, true, st));
-    if (nh == 2) {
-        sk.H = H2;
-        BWD_CHECK(launch_subchunk_decay_bwd(sk, dt, A, dtl(rh), lwp(rh, H2, nsr, b), L, 2, true, true, st));
-    }
-    sk.L = L;
-    sk.H = H2;
-    BWD_CHECK(launch_subchunk_decay_bwd(sk, dt, A, dtl(fh), lwp(fh, H2, nsf, b), L, nh, false, false, st));
+    // the decay arrays in one launch: reversed per head (b), reversed per half-head (c), forwards per
+    // half-head (d) (at N = 64 the half-heads are the heads and the second set is the first)
+    DecaySet sets[3];
+    int nsets = 0;
+    sets[nsets++] = DecaySet{dtl(rl), lwp(rl, H, nsr, b), b, Lr, L, H, 1, true, true};
+    if (nh == 2) sets[nsets++] = DecaySet{dtl(rh), lwp(rh, H2, nsr, b), b, Lr, L, H2, 2, true, true};
+    sets[nsets++] = DecaySet{dtl(fh), lwp(fh, H2, nsf, b), b, L, L, H2, nh, false, false};
+    BWD_CHECK(launch_subchunk_decay_bwd_sets(sets, nsets, dt, A, st));
 
     // (c) G^T read out through x: v (dB, q), as H2 half-heads of headdim 64 (at dstate 128 each head splits
     // into the two halves of the state's N rows, which form one head pair) whose x is (that half of) C of

@@ -743,14 +743,14 @@ struct DecaySrc {
 };
 
 template <bool BWD>
-__global__ void __launch_bounds__(256) subchunk_decay_kernel(DtFront fe, const bf16* __restrict__ dt,
-                                                             const float* __restrict__ A, float* __restrict__ dtl,
-                                                             float* __restrict__ lw, int64_t L, int H,
-                                                             uint32_t nitems, DecaySrc src) {
+__device__ __forceinline__ void subchunk_decay_body(const DtFront& fe, const bf16* __restrict__ dt,
+                                                    const float* __restrict__ A, float* __restrict__ dtl,
+                                                    float* __restrict__ lw, int64_t L, int H, uint32_t nitems,
+                                                    const DecaySrc& src, uint32_t block) {
     __shared__ float blk[QS][kDecayHB + 1];
     __shared__ bool vok[QS][kDecayHB + 1];  // position inside the sequence
     const int64_t nsubT = (L + QS - 1) / QS;
-    const uint32_t item = xcd_remap(blockIdx.x, nitems);
+    const uint32_t item = xcd_remap(block, nitems);
     const int64_t sub = item % (uint64_t)nsubT;
     const int64_t b = item / (uint64_t)nsubT;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -801,6 +801,34 @@ __global__ void __launch_bounds__(256) subchunk_decay_kernel(DtFront fe, const b
             lw[o] = incl * kLog2e;
         }
     }
+}
+
+template <bool BWD>
+__global__ void __launch_bounds__(256) subchunk_decay_kernel(DtFront fe, const bf16* __restrict__ dt,
+                                                             const float* __restrict__ A, float* __restrict__ dtl,
+                                                             float* __restrict__ lw, int64_t L, int H,
+                                                             uint32_t nitems, DecaySrc src) {
+    subchunk_decay_body<BWD>(fe, dt, A, dtl, lw, L, H, nitems, src, blockIdx.x);
+}
+
+// several sets of the backward's decay arrays in one launch: set blockIdx.y, workgroups past its count idle
+struct DecayJob {
+    float *dtl, *lw;
+    int64_t L;
+    int H;
+    uint32_t nitems;
+    DecaySrc src;
+};
+struct DecayJobs {
+    DecayJob j[3];
+};
+
+__global__ void __launch_bounds__(256) subchunk_decay_jobs_kernel(const bf16* __restrict__ dt, const float* __restrict__ A,
+                                                                  DecayJobs jobs) {
+    const DecayJob& jb = jobs.j[blockIdx.y];
+    if (blockIdx.x >= jb.nitems) return;
+    const DtFront none{nullptr, 0, 0, 0, 0.0f, 0.0f};
+    subchunk_decay_body<true>(none, dt, A, jb.dtl, jb.lw, jb.L, jb.H, jb.nitems, jb.src, blockIdx.x);
 }
 
 // Reading the inputs backwards (XMap::rows > 0) is a variant of the kernels with sub-chunk-local decay
@@ -1000,14 +1028,21 @@ hipError_t launch_chunk_scan_sub(const Shape& s, const void* x, const void* B, c
     return fz::scan_dispatch<true>(s, (const bf16*)x, (const bf16*)B, (const bf16*)C, ds, start, D, (bf16*)y, st, xm);
 }
 
-hipError_t launch_subchunk_decay_bwd(const Shape& s, const void* dt, const float* A, float* dtl, float* lw, int64_t Ls,
-                                     int hdiv, bool rev, bool unit, hipStream_t st) {
-    const uint32_t ndec = (uint32_t)(s.b * ((s.L + fz::QS - 1) / fz::QS));
-    if (ndec == 0) return hipSuccess;
-    if (hdiv < 1 || s.H % hdiv) return hipErrorInvalidValue;
-    const DtFront none{nullptr, 0, 0, 0, 0.0f, 0.0f};
-    hipLaunchKernelGGL(fz::subchunk_decay_kernel<true>, dim3(ndec), dim3(256), 0, st, none, (const bf16*)dt, A, dtl, lw,
-                       s.L, (int)s.H, ndec, fz::DecaySrc{Ls, hdiv, rev ? 1 : 0, unit ? 1 : 0});
+hipError_t launch_subchunk_decay_bwd_sets(const DecaySet* sets, int nsets, const void* dt, const float* A,
+                                          hipStream_t st) {
+    if (nsets < 1 || nsets > 3) return hipErrorInvalidValue;
+    fz::DecayJobs jobs{};
+    uint32_t gx = 0;
+    for (int k = 0; k < nsets; ++k) {
+        const DecaySet& d = sets[k];
+        if (d.hdiv < 1 || d.H % d.hdiv) return hipErrorInvalidValue;
+        const uint32_t n = (uint32_t)(d.b * ((d.L + fz::QS - 1) / fz::QS));
+        jobs.j[k] = fz::DecayJob{d.dtl, d.lw, d.L, d.H, n, fz::DecaySrc{d.Ls, d.hdiv, d.rev ? 1 : 0, d.unit ? 1 : 0}};
+        gx = n > gx ? n : gx;
+    }
+    if (gx == 0) return hipSuccess;
+    hipLaunchKernelGGL(fz::subchunk_decay_jobs_kernel, dim3(gx, (unsigned)nsets), dim3(256), 0, st, (const bf16*)dt, A,
+                       jobs);
     return hipGetLastError();
 }
 

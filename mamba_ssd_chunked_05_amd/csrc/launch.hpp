@@ -78,11 +78,18 @@ hipError_t launch_chunk_state_sub(const Shape& s, const void* x, const void* B, 
 hipError_t launch_chunk_scan_sub(const Shape& s, const void* x, const void* B, const void* C, const float* dtl,
                                  const float* lw, const float* start, const float* D, void* y, hipStream_t st,
                                  const XMap* xm);
-// Sub-chunk-local decay arrays for s.H kernel heads over s.L tokens from a bf16 dt of (b, Ls, H / hdiv):
-// kernel head h takes dt head h / hdiv and A[h / hdiv]; rev: token t takes the decay step of dt row
-// s.L - t (none where that row is past the end); unit: the input step is 1.
-hipError_t launch_subchunk_decay_bwd(const Shape& s, const void* dt, const float* A, float* dtl, float* lw, int64_t Ls,
-                                     int hdiv, bool rev, bool unit, hipStream_t st);
+// Up to three sets of sub-chunk-local decay arrays in one launch.  A set covers H kernel heads over L
+// tokens (b batch rows) from a bf16 dt of (b, Ls, H / hdiv): kernel head h takes dt head h / hdiv and
+// A[h / hdiv]; rev: token t takes the decay step of dt row L - t (none where that row is past the end);
+// unit: the input step is 1.
+struct DecaySet {
+    float *dtl, *lw;
+    int64_t b, L, Ls;
+    int H, hdiv;
+    bool rev, unit;
+};
+hipError_t launch_subchunk_decay_bwd_sets(const DecaySet* sets, int nsets, const void* dt, const float* A,
+                                          hipStream_t st);
 // Fast chunk-state / chunk-scan kernels (bf16, headdim 64, dstate 64 or 128, chunk a multiple of 64).
 bool fast_chunk_supported(const Shape& s);
 int fast_forward_chunk(const Shape& s);   // chunk size the forward uses on the fast path
