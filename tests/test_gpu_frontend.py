@@ -71,6 +71,22 @@ def test_forward_frontend(gpu_ssd, shape, mode):
         assert rel_l2(plain["final"], ref["final"]) > 1e-2
 
 
+def test_forward_frontend_long(gpu_ssd):
+    """Above 2^20 token-heads the fast forward keeps its decay pass (the front-end applied there) instead of
+    forming the decays in the chunk kernels: every front-end option at once, against the oracle on every head."""
+    b, L, H, P, N, G, dtype, chunk = 1, 8256, 128, 64, 64, 2, "bf16", 0  # 1,056,768 token-heads
+    mode = "all"
+    fi = make_forward_inputs(b, L, H, P, N, G, dtype, 155, h0_std=0.3)
+    raw, bias = _raw_dt(fi, mode, dtype, 156)
+    dec, inp = _oracle_steps(raw, fi.A, bias, mode)
+    ref = oracle.forward(fi.x, dec, fi.A, fi.B, fi.C, fi.D, fi.h0, dt_in=inp)
+    y, fin = gpu_ssd.forward(dev(fi.x, dtype), dev(raw, dtype), dev(fi.A), dev(fi.B, dtype), dev(fi.C, dtype),
+                             dev(fi.D), dev(fi.h0), chunk=chunk, frontend=_frontend(mode, bias))
+    torch.cuda.synchronize()
+    assert_close_y(host(y), ref["y"], dtype)
+    assert_close_state(host(fin), ref["final"])
+
+
 @pytest.mark.parametrize("mode", list(MODES))
 def test_cumsum_frontend(gpu_ssd, mode):
     fi = make_forward_inputs(2, 200, 5, 16, 16, 1, "f32", 152)
