@@ -269,8 +269,10 @@ ssd_status ssd_step_multi_ex(const ssd_dims* dims, const ssd_dt_frontend* fe, fl
  * every scan on the bf16 chunk kernels; other inputs run fp32 scans.
  * workspace: ssd_backward_workspace_bytes(dims) bytes, 256-byte aligned
  * (about (2 s + 4) P + 8 N + 2 s N G / H + 8 P N / chunk + 30 bytes per
- * token-head with fp32 scans, s = the io element size, and about 4 N + 8 P N /
- * chunk + 2.5 chunk G / H + 70 on the bf16 chunk kernels); no output may
+ * token-head with fp32 scans, s = the io element size; on the bf16 chunk
+ * kernels about max(2 N, 4 P N / chunk) + 4 P N / chunk + 2.5 chunk G / H +
+ * 70 when H is a multiple of 4 and G N <= 1024, else 4 N + 8 P N / chunk +
+ * 2.5 chunk G / H + 70); no output may
  * overlap an input, another output or the workspace.  x, B, C, dy, dx, dB,
  * dC, h0, dfinal and dh0 must be 16-byte aligned (SSD_ERR_UNSUPPORTED
  * otherwise).

@@ -220,21 +220,20 @@ __device__ __forceinline__ void ld_bf16(const bf16* p, float* o) {
 }
 
 // The combine of the chunk-local flow (bf16, dstate N = 64 or 128, H a multiple of 4), one workgroup per
-// (b, t), after the adjoint scan has written dx and the decay gradient dy . x: per head q = v . B, per
-// group dB = sum_h dt v and dC = sum_h w.  Four heads at once per wavefront, 16 lanes per head: wavefront
-// wv takes the head quads k = wv, wv + 4, ..., lane row r (lane / 16) head 4k + r; a lane covers
-// n = (N / 16) l16 .. (16- or 8-byte accesses), so every row of v and w is read by one contiguous access
-// per wavefront.  The group sums collect in registers per lane and land, per (wavefront, lane row), in an
-// LDS slice when the row's group changes; the slices are added in a fixed order at the end.
-template <int N>
+// (b, t), in two halves that run apart: DB, after the adjoint readout v: per head q = v . B and per group
+// dB = sum_h dt v; else, after the forward readout w: per group dC = sum_h w.  Four heads at once per
+// wavefront, 16 lanes per head: wavefront wv takes the head quads k = wv, wv + 4, ..., lane row r (lane /
+// 16) head 4k + r; a lane covers n = (N / 16) l16 .. (16- or 8-byte accesses), so every row of v or w is
+// read by one contiguous access per wavefront.  The group sums collect in registers per lane and land, per
+// (wavefront, lane row), in an LDS slice when the row's group changes; the slices are added in a fixed
+// order at the end.
+template <int N, bool DB>
 __global__ void __launch_bounds__(256) combine_quad_kernel(const bf16* __restrict__ dt, const bf16* __restrict__ B,
-                                                           const bf16* __restrict__ v, const bf16* __restrict__ w,
-                                                           bf16* __restrict__ dB, bf16* __restrict__ dC,
+                                                           const bf16* __restrict__ vw, bf16* __restrict__ dBC,
                                                            float* __restrict__ q, int64_t L, int H, int G) {
     constexpr int NV = N / 16;
     extern __shared__ float lds[];
-    float* pB = lds;              // [16][G][N] per-(wavefront, lane row) partial dB
-    float* pC = pB + 16 * G * N;  // [16][G][N] per-(wavefront, lane row) partial dC
+    float* pS = lds;  // [16][G][N] per-(wavefront, lane row) partial dB or dC
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane >> 4, l16 = lane & 15;
     const int slot = 4 * wv + r;
     const int64_t bt = blockIdx.x;  // b * L + t
@@ -242,12 +241,12 @@ __global__ void __launch_bounds__(256) combine_quad_kernel(const bf16* __restric
     const int hpg = H / G, nq = H / 4;
     // with one group and every (wavefront, lane row) slot holding heads, every slot writes its partial sums
     if (!(G == 1 && nq >= 4)) {
-        for (int e = tid; e < 32 * G * N; e += 256) lds[e] = 0.0f;
+        for (int e = tid; e < 16 * G * N; e += 256) lds[e] = 0.0f;
         __syncthreads();
     }
-    float ab[NV], ac[NV], bv[NV];
+    float acc[NV], bv[NV];
 #pragma unroll
-    for (int k = 0; k < NV; ++k) ab[k] = ac[k] = 0.0f;
+    for (int k = 0; k < NV; ++k) acc[k] = 0.0f;
     int gcur = -1;
     for (int qd = wv; qd < nq; qd += 4) {
         const int h = 4 * qd + r, g = h / hpg;
@@ -255,45 +254,40 @@ __global__ void __launch_bounds__(256) combine_quad_kernel(const bf16* __restric
             if (gcur >= 0) {
 #pragma unroll
                 for (int k = 0; k < NV; ++k) {
-                    pB[(slot * G + gcur) * N + NV * l16 + k] = ab[k];
-                    pC[(slot * G + gcur) * N + NV * l16 + k] = ac[k];
-                    ab[k] = ac[k] = 0.0f;
+                    pS[(slot * G + gcur) * N + NV * l16 + k] = acc[k];
+                    acc[k] = 0.0f;
                 }
             }
             gcur = g;
-            ld_bf16<NV>(B + (bt * G + g) * N + NV * l16, bv);
+            if constexpr (DB) ld_bf16<NV>(B + (bt * G + g) * N + NV * l16, bv);
         }
-        float vv[NV], ww[NV];
-        ld_bf16<NV>(v + (bt * H + h) * N + NV * l16, vv);
-        ld_bf16<NV>(w + (bt * H + h) * N + NV * l16, ww);
-        const float d = static_cast<float>(dt[bt * H + h]);
-        float sq = 0.0f;
+        float vv[NV];
+        ld_bf16<NV>(vw + (bt * H + h) * N + NV * l16, vv);
+        if constexpr (DB) {
+            const float d = static_cast<float>(dt[bt * H + h]);
+            float sq = 0.0f;
 #pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            sq = fmaf(vv[k], bv[k], sq);
-            ab[k] = fmaf(d, vv[k], ab[k]);
-            ac[k] += ww[k];
+            for (int k = 0; k < NV; ++k) {
+                sq = fmaf(vv[k], bv[k], sq);
+                acc[k] = fmaf(d, vv[k], acc[k]);
+            }
+            sq = row16_sum(sq);
+            if (l16 == 0) q[(bb * H + h) * L + t] = sq;
+        } else {
+#pragma unroll
+            for (int k = 0; k < NV; ++k) acc[k] += vv[k];
         }
-        sq = row16_sum(sq);
-        if (l16 == 0) q[(bb * H + h) * L + t] = sq;
     }
     if (gcur >= 0) {
 #pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            pB[(slot * G + gcur) * N + NV * l16 + k] = ab[k];
-            pC[(slot * G + gcur) * N + NV * l16 + k] = ac[k];
-        }
+        for (int k = 0; k < NV; ++k) pS[(slot * G + gcur) * N + NV * l16 + k] = acc[k];
     }
     __syncthreads();
     for (int e = tid; e < G * N; e += 256) {
-        float sb = 0.0f, sc = 0.0f;
+        float sum = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            sb += pB[k * G * N + e];
-            sc += pC[k * G * N + e];
-        }
-        dB[bt * G * N + e] = static_cast<bf16>(sb);
-        dC[bt * G * N + e] = static_cast<bf16>(sc);
+        for (int k = 0; k < 16; ++k) sum += pS[k * G * N + e];
+        dBC[bt * G * N + e] = static_cast<bf16>(sum);
     }
 }
 
@@ -640,6 +634,18 @@ __global__ void __launch_bounds__(256) dh0_tr_kernel(const float* __restrict__ G
 // registers at the transposed scans' large chunk (hi/lo state updates) -- the adjoint scan (b), and the
 // forward transposed scan (d), whose state is S^T and is stored back in (P, N) layout -- so there are
 // no Q-chunk local states and no pass over them.
+}  // namespace bwd
+
+// The local flow's combine in two halves (dC after the forward readout, dB and q after the adjoint one):
+// headdim 64, dstate 64 or 128, H a multiple of 4, and one LDS slice set per (wavefront, lane row) and
+// group within 64 KB.
+static size_t quad_combine_lds(const Shape& s) { return (size_t)16 * s.G * s.N * 4; }
+static bool quad_combine(const Shape& s) {
+    return s.P == 64 && (s.N == 64 || s.N == 128) && s.H % 4 == 0 && quad_combine_lds(s) <= 64 * 1024;
+}
+
+namespace bwd {
+
 hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, const void* dt, const float* A,
                      const void* B, const void* C, const float* D, const float* h0, const void* dy,
                      const float* dfinal, void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0,
@@ -690,24 +696,60 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     sets[nsets++] = DecaySet{dtl(fh), lwp(fh, H2, nsf, b), b, L, L, H2, nh, false, false};
     BWD_CHECK(launch_subchunk_decay_bwd_sets(sets, nsets, dt, A, st));
 
-    // (c) G^T read out through x: v (dB, q), as H2 half-heads of headdim 64 (at dstate 128 each head splits
-    // into the two halves of the state's N rows, which form one head pair) whose x is (that half of) C of
-    // the head's group; reversed, written forwards.  Its chunk-start states seed the adjoint scan (b) and
-    // its final state is the adjoint at the first token (dh0).
+    // The half-head scans (c) and (d): H2 half-heads of headdim 64 (at dstate 128 each head splits into the
+    // two halves of the state's N rows, which form one head pair) whose x is (that half of) B or C of the
+    // head's group.
     Shape sh = s;
     sh.H = H2;
     sh.P = 64;
     sh.N = P;
     sh.G = H;
-    sh.L = Lr;
+    Shape s1;  // the pass over the chunk totals: a chunk of "length 1" in its indexing
+    const bool split = quad_combine(s);
+    const bf16 *dtb = static_cast<const bf16*>(dt), *Bb = static_cast<const bf16*>(B);
+    const unsigned nbt = (unsigned)(b * L);
+    const size_t lq = quad_combine_lds(s);
+    // (d) S^T read out through dy: w (dC), forwards in time; it also stores the forward state entering every
+    // Q-chunk (S0), back in the heads' (P, N) layout.  With the split combine, dC is summed at once and w's
+    // memory then serves v and the adjoint's states.
+    sh.L = L;
     sh.Q = f.Qt;
+    sh.nC = (L + f.Qt - 1) / f.Qt;
+    s1 = sh;
+    s1.Q = 1;
+    const XMap xm{nh * G, nh * hpg, nh, 0, nullptr, nullptr, 0, 0, 0};
+    const XMap xmt{nh * G, nh * hpg, nh, 0, nullptr, states, (int)s.Q, 0, nh};
+    BWD_CHECK(launch_chunk_state_sub(sh, B, x, dtl(fh), lwp(fh, H2, nsf, b), stT, totals, st, &xm));
+    BWD_CHECK(launch_state_passing(s1, stT, totals, h0 ? h0T : nullptr, finT, st));
+    BWD_CHECK(launch_chunk_scan_sub(sh, B, x, dy, dtl(fh), lwp(fh, H2, nsf, b), stT, nullptr, w, st, &xmt));
+    if (split) {
+        if (N == 128)
+            hipLaunchKernelGGL((combine_quad_kernel<128, false>), dim3(nbt), dim3(256), lq, st, dtb, Bb, w,
+                               static_cast<bf16*>(dC), q, L, H, G);
+        else
+            hipLaunchKernelGGL((combine_quad_kernel<64, false>), dim3(nbt), dim3(256), lq, st, dtb, Bb, w,
+                               static_cast<bf16*>(dC), q, L, H, G);
+        BWD_CHECK(hipGetLastError());
+    }
+    // (c) G^T read out through x: v (dB, q), reversed, written forwards.  Its chunk-start states seed the
+    // adjoint scan (b) and its final state is the adjoint at the first token (dh0).
+    sh.L = Lr;
     sh.nC = (Lr + f.Qt - 1) / f.Qt;
-    Shape s1 = sh;  // the pass over the chunk totals: a chunk of "length 1" in its indexing
+    s1 = sh;
     s1.Q = 1;
     const XMap xmr{nh * G, nh * hpg, nh, L, nullptr, nullptr, 0, 0, 0};
     BWD_CHECK(launch_chunk_state_sub(sh, C, dy, dtl(rh), lwp(rh, H2, nsr, b), stT, totals, st, &xmr));
     BWD_CHECK(launch_state_passing(s1, stT, totals, dfT, G0T, st));
     BWD_CHECK(launch_chunk_scan_sub(sh, C, dy, x, dtl(rh), lwp(rh, H2, nsr, b), stT, nullptr, v, st, &xmr));
+    if (split) {
+        if (N == 128)
+            hipLaunchKernelGGL((combine_quad_kernel<128, true>), dim3(nbt), dim3(256), lq, st, dtb, Bb, v,
+                               static_cast<bf16*>(dB), q, L, H, G);
+        else
+            hipLaunchKernelGGL((combine_quad_kernel<64, true>), dim3(nbt), dim3(256), lq, st, dtb, Bb, v,
+                               static_cast<bf16*>(dB), q, L, H, G);
+        BWD_CHECK(hipGetLastError());
+    }
     // (b) the adjoint G read out through B: dx = dt u + D dy written by the scan itself (u = G B, dt as the
     // output row scale, D on the x-role dy), started from (c)'s states and storing the adjoint entering
     // every Q-chunk in states_b
@@ -717,35 +759,11 @@ hipError_t run_local(const Shape& s, const BackwardLayout& f, const void* x, con
     sb.nC = sh.nC;
     const XMap xb{H, 1, 1, L, dt, states_b, (int)s.Q, 1, 0};
     BWD_CHECK(launch_chunk_scan_sub(sb, dy, C, B, dtl(rl), lwp(rl, H, nsr, b), stT, D, dx, st, &xb));
-    // (d) S^T read out through dy: w (dC), as half-heads like (c), forwards in time; it also stores the
-    // forward state entering every Q-chunk (S0), back in the heads' (P, N) layout
-    sh.L = L;
-    sh.nC = (L + f.Qt - 1) / f.Qt;
-    s1 = sh;
-    s1.Q = 1;
-    const XMap xm{nh * G, nh * hpg, nh, 0, nullptr, nullptr, 0, 0, 0};
-    const XMap xmt{nh * G, nh * hpg, nh, 0, nullptr, states, (int)s.Q, 0, nh};
-    BWD_CHECK(launch_chunk_state_sub(sh, B, x, dtl(fh), lwp(fh, H2, nsf, b), stT, totals, st, &xm));
-    BWD_CHECK(launch_state_passing(s1, stT, totals, h0 ? h0T : nullptr, finT, st));
-    BWD_CHECK(launch_chunk_scan_sub(sh, B, x, dy, dtl(fh), lwp(fh, H2, nsf, b), stT, nullptr, w, st, &xmt));
     // the decay gradient, chunk by chunk at Q, from the steps and the stored states
     BWD_CHECK(launch_decay_grad(s, x, dy, B, C, dt, A, states, states_b, F(f.cbt), R, dxy, st));
-
-    const size_t lq = (size_t)32 * G * N * 4;  // the quad combine's LDS slices
-    if (P == 64 && (N == 64 || N == 128) && H % 4 == 0 && lq <= 64 * 1024) {
-        const bf16 *dtb = static_cast<const bf16*>(dt), *Bb = static_cast<const bf16*>(B);
-        bf16 *dBb = static_cast<bf16*>(dB), *dCb = static_cast<bf16*>(dC);
-        if (N == 128)
-            hipLaunchKernelGGL(combine_quad_kernel<128>, dim3((unsigned)(b * L)), dim3(256), lq, st, dtb, Bb, v, w, dBb,
-                               dCb, q, L, H, G);
-        else
-            hipLaunchKernelGGL(combine_quad_kernel<64>, dim3((unsigned)(b * L)), dim3(256), lq, st, dtb, Bb, v, w, dBb,
-                               dCb, q, L, H, G);
-        BWD_CHECK(hipGetLastError());
-    } else {
+    if (!split)
         BWD_CHECK((launch_combine<T, bf16, bf16>(dy, x, dt, B, D, nullptr, v, w, dx, dB, dC, q, dxy, b, L, L, H, P, N,
                                                  G, st, false)));
-    }
     if (finish_tile_lds(H) <= 64 * 1024) {
         const int64_t ntile = (L + kFinTok - 1) / kFinTok;
         hipLaunchKernelGGL(finish_tile_kernel<T>, dim3((unsigned)ntile, (unsigned)b), dim3(256), finish_tile_lds(H),
@@ -915,8 +933,15 @@ BackwardLayout backward_layout(const Shape& s) {
     if (f.local) {
         // the stored states at the backward's chunk Q, the scans' bf16 outputs v and w (forward time), the
         // transposed final states, per-token q, dy.x and R, per-tile partial sums
-        f.states = take(ST), f.states_b = take(ST);
-        f.v_r = take(BLHN / 2), f.w = take(BLHN / 2);
+        if (quad_combine(s)) {
+            // the combine runs in halves, so w (read for dC before (c) runs), then v (read for dB before (b)
+            // runs), then the adjoint's states take turns in one region
+            f.states = take(ST);
+            f.v_r = f.w = f.states_b = take(std::max(ST, BLHN / 2));
+        } else {
+            f.states = take(ST), f.states_b = take(ST);
+            f.v_r = take(BLHN / 2), f.w = take(BLHN / 2);
+        }
         f.G0 = take(HS), f.dfT = take(HS), f.h0T = take(HS), f.finT = take(HS);
         f.q = take(BLH), f.dxy = take(BLH), f.R = take(BLH);
         const size_t PART = (size_t)(s.b * ((s.L + 31) / 32) * s.H) * 8;
