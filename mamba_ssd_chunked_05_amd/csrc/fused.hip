@@ -487,19 +487,35 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
         }
 
         // ---- phase 3: S <- 2^(l_63) S + B^T (w x) ---------------------------------------------
+        // With taps the state's decay is applied inside the first K step (ahead of it, the reversed
+        // dstate-128 scan spilled registers).
+        auto decay_state = [&]() {
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-            const float alpha = sm.alpha[hh];
+            for (int hh = 0; hh < HPW; ++hh) {
+                const float alpha = sm.alpha[hh];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
+                for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) st[hh][nt][r] *= alpha;
+                    for (int r = 0; r < 4; ++r) st[hh][nt][r] *= alpha;
+                }
+            }
+        };
+        if constexpr (!TAP) {  // (the same loop as decay_state, written out: the call form compiles differently)
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh) {
+                const float alpha = sm.alpha[hh];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) st[hh][nt][r] *= alpha;
+                }
             }
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             // token slots of this K step: 32ks + 4g4 + r (slots 0..3) and 32ks + 16 + 4g4 + r (slots 4..7)
             if constexpr (TAP) {  // hi + lo scaled operand; the B^T fragments in two halves (fewer live registers)
+                if (ks == 0) decay_state();
                 Frag<bf16> xw[HPW], xl[HPW];
 #pragma unroll
                 for (int hh = 0; hh < HPW; ++hh) {
