@@ -84,13 +84,14 @@ def test_backward_stress(gpu_ssd, mode):
 # bf16 io, headdim 64, dstate 64 or 128, chunk 64 or 128: the decay gradient is formed chunk by chunk and the
 # transposed scans run in bf16 compute.  One chunk shorter than the chunk size, a length that is a whole
 # number of chunks (no front padding of the reversed walks), chunk 64, groups, an odd number of heads per
-# group, with and without h0 and dfinal.
+# group, one head per group with 64 KB of combine slices, with and without h0 and dfinal.
 LOCAL = [
     (1, 40, 2, 64, 64, 1, "bf16", 64, True),
     (2, 256, 4, 64, 128, 2, "bf16", 128, True),
     (1, 300, 2, 64, 128, 1, "bf16", 64, False),
     (2, 450, 6, 64, 64, 3, "bf16", 0, True),
     (1, 333, 3, 64, 128, 1, "bf16", 128, True),  # three heads per group: one head per workgroup, generic combine
+    (1, 200, 8, 64, 128, 8, "bf16", 128, True),  # eight groups at dstate 128: the two-half combine's widest slices
 ]
 
 
