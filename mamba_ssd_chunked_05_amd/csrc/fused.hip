@@ -520,15 +520,15 @@ chunk_scan_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, c
 #pragma unroll
                 for (int hh = 0; hh < HPW; ++hh) {
                     const float* wv = &sm.ww[hh * QS + 32 * ks + 4 * g4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float v0 = static_cast<float>(xf[ks][hh].v[r]) * wv[r];
-                        const float v1 = static_cast<float>(xf[ks][hh].v[4 + r]) * wv[16 + r];
-                        xw[hh].v[r] = static_cast<bf16>(v0);
-                        xw[hh].v[4 + r] = static_cast<bf16>(v1);
-                        xl[hh].v[r] = static_cast<bf16>(v0 - static_cast<float>(xw[hh].v[r]));
-                        xl[hh].v[4 + r] = static_cast<bf16>(v1 - static_cast<float>(xw[hh].v[4 + r]));
-                    }
+                    const f32x4 w0 = {wv[0], wv[1], wv[2], wv[3]}, w1 = {wv[16], wv[17], wv[18], wv[19]};
+                    const bf16x4 x0 = {xf[ks][hh].v[0], xf[ks][hh].v[1], xf[ks][hh].v[2], xf[ks][hh].v[3]};
+                    const bf16x4 x1 = {xf[ks][hh].v[4], xf[ks][hh].v[5], xf[ks][hh].v[6], xf[ks][hh].v[7]};
+                    const f32x4 v0 = __builtin_convertvector(x0, f32x4) * w0;
+                    const f32x4 v1 = __builtin_convertvector(x1, f32x4) * w1;
+                    const bf16x4 h0 = __builtin_convertvector(v0, bf16x4), h1 = __builtin_convertvector(v1, bf16x4);
+                    xw[hh].v = pack8(h0, h1);
+                    xl[hh].v = pack8(__builtin_convertvector(v0 - bf16x4_to_f32(h0), bf16x4),
+                                     __builtin_convertvector(v1 - bf16x4_to_f32(h1), bf16x4));
                 }
 #pragma unroll
                 for (int nb = 0; nb < NT; nb += NT / 2) {
@@ -701,16 +701,13 @@ chunk_state_fast_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
                 const bf16x4 lo4 = tr_read(xt, 32 * ks + 4 * g4, 16 * w, XS, l16);
                 const bf16x4 hi4 = tr_read(xt, 32 * ks + 16 + 4 * g4, 16 * w, XS, l16);
                 const float* wv = &sm.ww[hh * QS + 32 * ks + 4 * g4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v0 = static_cast<float>(lo4[r]) * wv[r];
-                    const float v1 = static_cast<float>(hi4[r]) * wv[16 + r];
-                    const bf16 h0v = static_cast<bf16>(v0), h1v = static_cast<bf16>(v1);
-                    xh[hh].v[r] = h0v;
-                    xh[hh].v[4 + r] = h1v;
-                    xl[hh].v[r] = static_cast<bf16>(v0 - static_cast<float>(h0v));
-                    xl[hh].v[4 + r] = static_cast<bf16>(v1 - static_cast<float>(h1v));
-                }
+                const f32x4 w0 = {wv[0], wv[1], wv[2], wv[3]}, w1 = {wv[16], wv[17], wv[18], wv[19]};
+                const f32x4 v0 = __builtin_convertvector(lo4, f32x4) * w0;
+                const f32x4 v1 = __builtin_convertvector(hi4, f32x4) * w1;
+                const bf16x4 h0 = __builtin_convertvector(v0, bf16x4), h1 = __builtin_convertvector(v1, bf16x4);
+                xh[hh].v = pack8(h0, h1);
+                xl[hh].v = pack8(__builtin_convertvector(v0 - bf16x4_to_f32(h0), bf16x4),
+                                 __builtin_convertvector(v1 - bf16x4_to_f32(h1), bf16x4));
             }
             Frag<bf16> a[NT];  // every B^T fragment of this K step in flight before the products
 #pragma unroll

@@ -32,6 +32,14 @@ __device__ __forceinline__ bf16x8 pack8(const bf16x4& a, const bf16x4& b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// four bf16 as floats, read from their packed halves (a shift or a mask each), so that a value rounded
+// to bf16 in a pair is not rounded again on its own to recover it
+__device__ __forceinline__ f32x4 bf16x4_to_f32(const bf16x4& h) {
+    const uint2 u = __builtin_bit_cast(uint2, h);
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+}
+
 __device__ __forceinline__ bf16x4 cvt4(const f32x4& v) {
     bf16x4 r;
     r[0] = static_cast<bf16>(v[0]);
