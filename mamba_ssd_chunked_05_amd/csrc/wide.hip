@@ -724,16 +724,14 @@ chunk_state_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B, 
             const bf16x4 lo4 = tr_read(sm.xs, 32 * ks + 4 * g4, 16 * w, XS, l16);
             const bf16x4 hi4 = tr_read(sm.xs, 32 * ks + 16 + 4 * g4, 16 * w, XS, l16);
             const float* wv = &sm.ww[32 * ks + 4 * g4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float v0 = static_cast<float>(lo4[r]) * wv[r];
-                const float v1 = static_cast<float>(hi4[r]) * wv[16 + r];
-                const bf16 h0v = static_cast<bf16>(v0), h1v = static_cast<bf16>(v1);
-                xh[ks].v[r] = h0v;
-                xh[ks].v[4 + r] = h1v;
-                xl[ks].v[r] = static_cast<bf16>(v0 - static_cast<float>(h0v));
-                xl[ks].v[4 + r] = static_cast<bf16>(v1 - static_cast<float>(h1v));
-            }
+            // four values at a time; the hi part is read back from its packed pair
+            const f32x4 w0 = {wv[0], wv[1], wv[2], wv[3]}, w1 = {wv[16], wv[17], wv[18], wv[19]};
+            const f32x4 v0 = __builtin_convertvector(lo4, f32x4) * w0;
+            const f32x4 v1 = __builtin_convertvector(hi4, f32x4) * w1;
+            const bf16x4 h0 = __builtin_convertvector(v0, bf16x4), h1 = __builtin_convertvector(v1, bf16x4);
+            xh[ks].v = pack8(h0, h1);
+            xl[ks].v = pack8(__builtin_convertvector(v0 - bf16x4_to_f32(h0), bf16x4),
+                             __builtin_convertvector(v1 - bf16x4_to_f32(h1), bf16x4));
         }
 #pragma unroll
         for (int nb = 0; nb < NBLK; ++nb) {
@@ -896,16 +894,14 @@ chunk_state_wide32_kernel(const bf16* __restrict__ x, const bf16* __restrict__ B
             const bf16x4 v1 = tr_read(sm.xs, 16 * ks + krow + 4, 32 * pt + kcol, XS, l16);
             const float* wv = &sm.ww[16 * ks + krow];
             Frag<bf16> xh, xl;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float a0 = static_cast<float>(v0[r]) * wv[r];
-                const float a1 = static_cast<float>(v1[r]) * wv[4 + r];
-                const bf16 h0v = static_cast<bf16>(a0), h1v = static_cast<bf16>(a1);
-                xh.v[r] = h0v;
-                xh.v[4 + r] = h1v;
-                xl.v[r] = static_cast<bf16>(a0 - static_cast<float>(h0v));
-                xl.v[4 + r] = static_cast<bf16>(a1 - static_cast<float>(h1v));
-            }
+            // four values at a time; the hi part is read back from its packed pair
+            const f32x4 w0 = {wv[0], wv[1], wv[2], wv[3]}, w1 = {wv[4], wv[5], wv[6], wv[7]};
+            const f32x4 a0 = __builtin_convertvector(v0, f32x4) * w0;
+            const f32x4 a1 = __builtin_convertvector(v1, f32x4) * w1;
+            const bf16x4 h0 = __builtin_convertvector(a0, bf16x4), h1 = __builtin_convertvector(a1, bf16x4);
+            xh.v = pack8(h0, h1);
+            xl.v = pack8(__builtin_convertvector(a0 - bf16x4_to_f32(h0), bf16x4),
+                         __builtin_convertvector(a1 - bf16x4_to_f32(h1), bf16x4));
             *reinterpret_cast<bf16x8*>(&sm.xf[w][ks][0][lane]) = xh.v;
             *reinterpret_cast<bf16x8*>(&sm.xf[w][ks][1][lane]) = xl.v;
         }
