@@ -803,12 +803,7 @@ __device__ __forceinline__ void subchunk_decay_body(const DtFront& fe, const bf1
             float dec = 0.0f, d = 0.0f;  // decay and input steps; zero past L
             if (vok[lane][hh]) dt_front(fe, h, ah, blk[lane][hh], dec, d);
             if (BWD && src.unit) d = t0 + lane < L ? 1.0f : 0.0f;
-            float incl = dec * ah;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float up = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += up;
-            }
+            const float incl = wave_incl_scan(dec * ah);  // DPP steps, no LDS permutes
             const int64_t o = ((b * H + h) * nsubT + sub) * QS + lane;
             dtl[o] = d;
             lw[o] = incl * kLog2e;
