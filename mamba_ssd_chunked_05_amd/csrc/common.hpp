@@ -178,6 +178,18 @@ __device__ __forceinline__ float row16_sum4(float v0, float v1, float v2, float 
 // inclusive prefix sum over the 64 lanes of a wavefront with data-parallel moves: shifts by 1, 2, 4 and
 // 8 lanes inside each row of 16 (a lane with no source adds zero), then each row's last value added to
 // the rows after it (row broadcasts of lanes 15 and 31)
+// the value lane `src` (a constant) holds, in a scalar register: a lane read, no LDS permute; every lane of
+// the wavefront must hold a valid value there
+__device__ __forceinline__ float lane_read(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+// the value the first lane of this lane's 16-lane row holds
+__device__ __forceinline__ float row_first(float v, int lane) {
+    const float r0 = lane_read(v, 0), r1 = lane_read(v, 16), r2 = lane_read(v, 32), r3 = lane_read(v, 48);
+    const int g = lane >> 4;
+    return g < 2 ? (g == 0 ? r0 : r1) : (g == 2 ? r2 : r3);
+}
+
 __device__ __forceinline__ float wave_incl_scan(float v) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));

@@ -198,18 +198,18 @@ __device__ __forceinline__ void chunk_store(bf16* xs, bf16* bsm, bf16* csm, floa
             incl = rg.cs;
         } else {
             incl = rg.cs - cs_prev;
-            cs_prev = __shfl(rg.cs, 63, 64);
+            cs_prev = lane_read(rg.cs, 63);
         }
-        const float last = __shfl(incl, 63, 64);
+        const float last = lane_read(incl, 63);
         tot += last;
         lw[hh * QS + lane] = incl;
         dtw[hh * QS + lane] = d;
         ww[hh * QS + lane] = fast_exp2(last - incl) * d;
         if (ec) {
-            ec[(hh * 4) * QS + lane] = fast_exp2(incl - __shfl(incl, lane & ~15, 64));
+            ec[(hh * 4) * QS + lane] = fast_exp2(incl - row_first(incl, lane));
 #pragma unroll
             for (int it = 1; it < 4; ++it)
-                ec[(hh * 4 + it) * QS + lane] = fast_exp2(fminf(__shfl(incl, 16 * it, 64) - incl, 0.0f)) * d;
+                ec[(hh * 4 + it) * QS + lane] = fast_exp2(fminf(lane_read(incl, 16 * it) - incl, 0.0f)) * d;
         }
         if (lane == 0) alpha[hh] = fast_exp2(last);
     }
@@ -610,7 +610,7 @@ __device__ __forceinline__ void state_store(bf16* xs, bf16* bsm, float* ww, cons
         }
         float e;  // log2 decay from this token to the chunk's end
         if (FWD) {
-            const float last = __shfl(cs, 63, 64);
+            const float last = lane_read(cs, 63);
             e = after + (last - cs);
             after += last;
             tot += last;
